@@ -1,0 +1,163 @@
+"""fp64 CPU oracle for Transformer-based linear attention (test infrastructure).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product path (the HIP library
+and its Python binding) never does.  It shares no code with the HIP path.
+
+The arithmetic lives in ``la_oracle.c`` (plain C, fp64).  This module only
+builds it with gcc, loads it with ctypes and marshals numpy arrays.  See the
+header of ``la_oracle.c`` for what is computed and which passage of the pages
+each step follows ("Transformer Based Linear Attention with Optimized GPU
+Kernel Implementation": TL;DR and Figure 1 caption on the sciencestack.ai page;
+the reordering and state-update pseudocode in section 2 of the cloud.baidu.com
+article).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "la_oracle.c")
+_LIB = os.path.join(_HERE, "liblaoracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile la_oracle.c with gcc (no fast-math, OpenMP over heads)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+               "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Wextra",
+               "-o", tmp, _SRC]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _bind(lib):
+    dp = ctypes.POINTER(ctypes.c_double)
+    i64 = ctypes.c_int64
+    for name in ("la_oracle_forward_direct", "la_oracle_forward_state"):
+        f = getattr(lib, name)
+        f.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64, ctypes.c_int]
+        f.restype = None
+    for name in ("la_oracle_backward_direct", "la_oracle_backward_state"):
+        f = getattr(lib, name)
+        f.argtypes = [dp, dp, dp, dp, dp, dp, dp, i64, i64, i64, i64,
+                      ctypes.c_int]
+        f.restype = None
+    lib.la_oracle_max_threads.argtypes = []
+    lib.la_oracle_max_threads.restype = ctypes.c_int
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        _lib = _bind(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _c64(x) -> np.ndarray:
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    if a.ndim != 4:
+        raise ValueError("expected a [B,H,N,D] array, got shape %r" % (a.shape,))
+    return a
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _check(*arrs):
+    shape = arrs[0].shape
+    for a in arrs[1:]:
+        if a.shape != shape:
+            raise ValueError("shape mismatch %r vs %r" % (a.shape, shape))
+    return shape
+
+
+def _forward(name, q, k, v, causal, lib=None):
+    q, k, v = _c64(q), _c64(k), _c64(v)
+    B, H, N, D = _check(q, k, v)
+    o = np.empty_like(q)
+    den = np.empty((B, H, N), dtype=np.float64)
+    getattr(lib or _load(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(den),
+                           B, H, N, D, int(bool(causal)))
+    return o, den
+
+
+def _backward(name, q, k, v, g, causal, lib=None):
+    q, k, v, g = _c64(q), _c64(k), _c64(v), _c64(g)
+    B, H, N, D = _check(q, k, v, g)
+    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+    getattr(lib or _load(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(dq),
+                           _ptr(dk), _ptr(dv), B, H, N, D, int(bool(causal)))
+    return dq, dk, dv
+
+
+def forward_direct(q, k, v, causal=False):
+    """O(N^2 D) definition: returns (O, den) as fp64 arrays."""
+    return _forward("la_oracle_forward_direct", q, k, v, causal)
+
+
+def forward_state(q, k, v, causal=False):
+    """O(N D^2) state form (reordered products / token recurrence)."""
+    return _forward("la_oracle_forward_state", q, k, v, causal)
+
+
+def backward_direct(q, k, v, g, causal=False):
+    """O(N^2 D) analytical gradients: returns (dQ, dK, dV)."""
+    return _backward("la_oracle_backward_direct", q, k, v, g, causal)
+
+
+def backward_state(q, k, v, g, causal=False):
+    """O(N D^2) gradients through the forward and gradient states."""
+    return _backward("la_oracle_backward_state", q, k, v, g, causal)
+
+
+def max_threads() -> int:
+    return int(_load().la_oracle_max_threads())
+
+
+class Variant:
+    """The same API bound to another build of la_oracle.c (used by the test
+    that plants mistakes in a copy of the oracle source to show that the pins
+    catch them)."""
+
+    def __init__(self, so_path):
+        self._lib = _bind(ctypes.CDLL(so_path))
+
+    def forward_direct(self, q, k, v, causal=False):
+        return _forward("la_oracle_forward_direct", q, k, v, causal, self._lib)
+
+    def forward_state(self, q, k, v, causal=False):
+        return _forward("la_oracle_forward_state", q, k, v, causal, self._lib)
+
+    def backward_direct(self, q, k, v, g, causal=False):
+        return _backward("la_oracle_backward_direct", q, k, v, g, causal, self._lib)
+
+    def backward_state(self, q, k, v, g, causal=False):
+        return _backward("la_oracle_backward_state", q, k, v, g, causal, self._lib)
+
+
+def build_variant(src_text: str, out_dir: str) -> "Variant":
+    """Compile C source text (a modified copy of la_oracle.c) and bind it."""
+    src = os.path.join(out_dir, "variant.c")
+    so = os.path.join(out_dir, "libvariant.so")
+    with open(src, "w") as f:
+        f.write(src_text)
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+                    "-ffp-contract=off", "-w", "-o", so, src], check=True)
+    return Variant(so)
+
+
+def source_text() -> str:
+    with open(_SRC) as f:
+        return f.read()
