@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Throughput of one Transformer-based linear-attention head-batch, forward +
+backward, on one MI355X.
+
+A step is one la_forward (saving its state) plus one la_backward over the
+same resident inputs: every row of the hot path (state reduction, apply and
+normalise, the backward prologue, dQ, the gradient-state reduction, dK and
+dV).  Default workload: B=4, H=16, N=4096, D=128, fp32 storage,
+non-causal, i.i.d. N(0,1)/sqrt(D) inputs (dO unscaled) drawn on the GPU
+from the shared seeded generator.
+
+Output: one JSON line on stdout.  `value` is tokens/s = B*N per step / step
+time over K timed steps bracketed by device synchronisation.  `roofline`
+gives the dominant kernel's achieved rate from per-launch HIP events (a
+second timed pass in which the library records caller-owned events around
+every launch), against the MI355X fp32-MFMA or HBM peak.  `cpu_baseline`
+times the fp64 CPU oracle on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LA fwd+bwd tokens/s at B4 H16 D128 N4096; % of binding HBM/FLOP roofline"
+PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix (= fp32 vector) peak
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+KERNEL_SOURCES = [os.path.join(ROOT, "linear_attention_transformer_amd", "csrc", f)
+                  for f in ("la_kernels.hpp", "la_api.hip")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(kernel: str, BH: int, N: int, D: int, s: int, fused_bwd_q: bool):
+    """(flops, bytes) per launch that the method itself requires (rows a2..a7
+    of the hot path); recomputation and scans count as overhead."""
+    nd, ndd = BH * N * D, BH * N * D * D
+    table = {
+        "state_local": (2 * ndd, 2 * nd * s),            # S = K^T V, z, u
+        "forward": (2 * ndd, 2 * nd * s),                # Q S, normalise, write O
+        "bwd_q": ((4 if fused_bwd_q else 2) * ndd, 3 * nd * s),  # dQ (+ dS = Q^T A)
+        "grad_state_local": (2 * ndd, 2 * nd * s),       # dS when not fused
+        "bwd_kv": (4 * ndd, 4 * nd * s),                 # dK, dV
+        "state_scan": (0, 0),
+    }
+    return table.get(kernel, (0, 0))
+
+
+def cpu_baseline(q, k, v, g, causal):
+    import oracle
+    from linear_attention_transformer_amd.inputs import as_f64_numpy
+    B, H, N, D = q.shape
+    BH = B * H
+    # about 5-15 s of oracle work on a 16-core host: the whole workload at the
+    # default size, proportionally fewer heads for larger N * D^2
+    heads = max(1, min(BH, round(BH * (4096 * 128 * 128) / (N * D * D))))
+    sel = lambda t: t.reshape(BH, N, D)[:heads].unsqueeze(0)
+    a = [as_f64_numpy(sel(x)) for x in (q, k, v, g)]
+    oracle.build(force=False)
+    t0 = time.perf_counter()
+    oracle.forward_state(a[0], a[1], a[2], causal)
+    oracle.backward_state(*a, causal)
+    dt = time.perf_counter() - t0
+    tokens = B * N * heads / BH
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": "fp64 C oracle (state form, OpenMP over heads), one forward+"
+                      "backward of %d of the %d heads at N=%d D=%d, %.2f s; value "
+                      "scaled to the workload's B*N tokens" % (heads, BH, N, D, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--dtype", choices=("fp32", "bf16"), default="fp32",
+                    help="storage dtype of Q, K, V, O and gradients (arithmetic is fp32)")
+    ap.add_argument("--causal", type=int, choices=(0, 1), default=0)
+    ap.add_argument("--B", type=int, default=4)
+    ap.add_argument("--H", type=int, default=16)
+    ap.add_argument("--N", type=int, default=4096)
+    ap.add_argument("--D", type=int, default=128)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures the linear-attention hot path on one GPU "
+              "(heads shard across GPUs with no communication); --gpus %d is not "
+              "supported" % max(args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import linear_attention_transformer_amd as la
+    from linear_attention_transformer_amd.inputs import make_inputs
+    if not os.path.exists(la.LIB_PATH):
+        from linear_attention_transformer_amd import build as hip_build
+        hip_build.build()
+    la.load_library()
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, H, N, D, causal = args.B, args.H, args.N, args.D, bool(args.causal)
+    dt = torch.float32 if args.dtype == "fp32" else torch.bfloat16
+    s = 4 if args.dtype == "fp32" else 2
+    print("bench: B=%d H=%d N=%d D=%d %s causal=%d steps=%d warmup=%d"
+          % (B, H, N, D, args.dtype, causal, args.steps, args.warmup), file=sys.stderr, flush=True)
+    q, k, v, g = make_inputs(B, H, N, D, dtype=dt, seed=0, device=dev, draw_device=dev)
+    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+    ws = la.alloc_workspace(B, H, N, D, causal, dev)
+    st = torch.empty(max(la.state_size(B, H, N, D, causal) // 4, 4), dtype=torch.float32,
+                     device=dev)
+
+    def step(tf=None, tb=None):
+        la.forward(q, k, v, causal, out=o, state_out=st, workspace=ws, trace=tf)
+        la.backward(q, k, v, g, causal, state=st, outs=(dq, dk, dv), workspace=ws, trace=tb)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region 1: the headline, nothing but the K steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = e0.elapsed_time(e1) / args.steps
+    tokens_per_s = B * N / (ms * 1e-3)
+    print("bench: %.3f ms/step (wall %.3f ms/step), %.1f M tokens/s"
+          % (ms, wall * 1e3 / args.steps, tokens_per_s / 1e6), file=sys.stderr, flush=True)
+
+    # timed region 2: the same K steps with per-launch events
+    traces = [(la.KernelTrace(dev), la.KernelTrace(dev)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for tf, tb in traces:
+        step(tf, tb)
+    t1.record()
+    torch.cuda.synchronize()
+    traced_ms = t0.elapsed_time(t1) / args.steps
+    per_kernel = {}
+    for tf, tb in traces:
+        for tr in (tf, tb):
+            for name, t in zip(tr.names(), tr.times_ms()):
+                per_kernel.setdefault(name, []).append(t)
+    launches = {n: len(v) // args.steps for n, v in per_kernel.items()}
+    avg_us = {n: 1e3 * sum(v) / len(v) for n, v in per_kernel.items()}
+    step_us = {n: avg_us[n] * launches[n] for n in avg_us}
+    dom = max(step_us, key=step_us.get)
+    fused = D != 256
+    flops, nbytes = algorithmic(dom, B * H, N, D, s, fused)
+    t_dom = avg_us[dom] * 1e-6
+    ridge = PEAK_FP32_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if nbytes and flops / nbytes < ridge:
+        bound, achieved, peak, unit = "hbm", nbytes / t_dom / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        bound, achieved, peak, unit = "mfma", flops / t_dom / 1e12, PEAK_FP32_MFMA_TFLOPS, "TFLOP/s"
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        key = "%s B%d H%d N%d D%d %s causal=%d" % (dom, B, H, N, D, args.dtype, int(causal))
+        ent = tr.get("entries", {}).get(key)
+        if ent and tr.get("kernel_source_hash") == kernel_source_hash():
+            traffic = ent["bytes_per_launch"]
+    roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom,
+                "kernel_avg_us": round(avg_us[dom], 2),
+                "algorithmic_per_launch": {"flops": flops, "bytes": nbytes}}
+    total_flops = 12 * B * H * N * D * D
+    total_bytes = 11 * B * H * N * D * s
+    step_floor_us = 1e6 * max(total_flops / (PEAK_FP32_MFMA_TFLOPS * 1e12),
+                              total_bytes / (PEAK_HBM_GBS * 1e9))
+    print("bench: per-kernel us/launch " + ", ".join("%s=%.1f" % kv for kv in avg_us.items()),
+          file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(q, k, v, g, causal)
+        print("bench: cpu baseline %.3g tokens/s on %d threads" % (cpu["value"], cpu["cores"]),
+              file=sys.stderr, flush=True)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "LA forward+backward, B=%d H=%d N=%d D=%d, %s storage, %s"
+                               % (B, H, N, D, args.dtype, "causal" if causal else "non-causal"),
+                   "B": B, "H": H, "N": N, "D": D, "causal": causal, "storage": args.dtype,
+                   "global_batch": B, "seq_len": N},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "step_roofline": {"floor_us": round(step_floor_us, 1),
+                          "frac": round(step_floor_us / (ms * 1e3), 4)},
+        "kernels_us_per_launch": {n: round(t, 2) for n, t in avg_us.items()},
+        "traced_ms_per_step": round(traced_ms, 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,152 @@
+/*
+ * la.h -- C ABI of the MI355X (gfx950) linear-attention library
+ * (built as linear_attention_transformer_amd/liblinattn.so).
+ *
+ * Operation (one head-batch of Transformer-based linear attention, from the
+ * pages about "Transformer Based Linear Attention with Optimized GPU Kernel
+ * Implementation": TL;DR and Figure 1 caption on the sciencestack.ai page,
+ * and the product reordering / state-update pseudocode of section 2 of the
+ * cloud.baidu.com article).  For every head independently, with rows
+ * q_i, k_j, v_j of D values and J(i) = all j (non-causal) or j <= i (causal):
+ *
+ *     w_ij  = 1 + q_i . k_j              constant term + linear term
+ *     den_i = sum_{j in J(i)} w_ij        normalisation
+ *     o_i   = sum_{j in J(i)} w_ij v_j / den_i
+ *
+ * evaluated in O(N D^2) time through the D x D state S = sum k v^T and the
+ * D-vectors z = sum k, u = sum v (prefix sums when causal).  The backward
+ * pass returns the analytical gradients of L = sum_i dO_i . o_i:
+ *
+ *     a_i = dO_i / den_i,  c_i = a_i . o_i
+ *     dQ_i = sum_{j in J(i)} (a_i . v_j - c_i) k_j
+ *     dK_j = sum_{i: j in J(i)} (a_i . v_j - c_i) q_i
+ *     dV_j = sum_{i: j in J(i)} w_ij a_i
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors Q, K, V, O, dO, dQ, dK, dV are DEVICE pointers with layout
+ *    [B, H, N, D], contiguous, element type `dtype` (fp32 or bf16).  All
+ *    arithmetic is fp32; bf16 outputs are rounded to nearest even.
+ *  - The caller owns (allocates and frees) every buffer, including the
+ *    workspace and the saved state.  The library never allocates memory.
+ *  - Outputs are overwritten, never accumulated into.
+ *  - Device pointers must be 16-byte aligned (LA_ERR_ALIGN otherwise).
+ *  - Outputs must not overlap any input or each other (LA_ERR_ALIAS).
+ *  - B, H, N >= 0, B*H <= 2^22, N <= 2^24 (LA_ERR_SHAPE otherwise).
+ *    B*H*N == 0 is a no-op returning LA_OK.
+ *    D must be one of 16, 32, 64, 128, 256 (LA_ERR_UNSUPPORTED otherwise).
+ *  - All arguments are validated on the host before anything is enqueued;
+ *    on any error nothing is launched.
+ *  - Kernels are enqueued on `stream` (a hipStream_t; NULL = default
+ *    stream).  The call does not synchronise.  A failed launch returns
+ *    LA_ERR_HIP; faults inside kernels surface at the caller's next
+ *    synchronisation.
+ *  - Results are deterministic: the same inputs give bit-identical outputs
+ *    on every call (fixed-order reductions, no floating-point atomics).
+ *  - The library keeps no mutable global state; concurrent calls on
+ *    different streams must use different workspaces.
+ */
+#ifndef LA_H
+#define LA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LA_OK = 0,
+    LA_ERR_NULL = 1,        /* a required pointer is NULL */
+    LA_ERR_SHAPE = 2,       /* negative size, or sizes overflow int64 */
+    LA_ERR_DTYPE = 3,       /* dtype is not LA_FP32 / LA_BF16 */
+    LA_ERR_UNSUPPORTED = 4, /* D not in {16,32,64,128,256}, or causal not 0/1 */
+    LA_ERR_WORKSPACE = 5,   /* workspace smaller than la_workspace_size() */
+    LA_ERR_ALIAS = 6,       /* an output overlaps an input or another output */
+    LA_ERR_ALIGN = 7,       /* a device pointer is not 16-byte aligned */
+    LA_ERR_HIP = 8          /* a HIP launch failed */
+} la_status;
+
+typedef enum { LA_FP32 = 0, LA_BF16 = 1 } la_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *la_status_string(int status);
+
+/* Bytes of device workspace that la_forward and la_backward need for this
+ * problem (the same bound covers both passes).  0 when B*H*N == 0. */
+size_t la_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D,
+                         int causal);
+
+/* Bytes of the state the forward pass can save for the backward pass:
+ * the reduced key-value state (S, z, u) of every head, and in the causal
+ * case one exclusive prefix of it per sequence segment.  fp32. */
+size_t la_state_size(int64_t B, int64_t H, int64_t N, int64_t D, int causal);
+
+/* Number of sequence segments each head is split into (diagnostic). */
+int64_t la_num_segments(int64_t B, int64_t H, int64_t N, int64_t D,
+                        int causal);
+
+/*
+ * Forward pass.
+ *   Q, K, V   : inputs [B,H,N,D] of `dtype`.
+ *   O         : output [B,H,N,D] of `dtype`.
+ *   den_out   : optional output [B,H,N] fp32, the denominators den_i
+ *               (NULL = not written).
+ *   state_out : optional output of la_state_size() bytes; when given, the
+ *               state needed by la_backward is saved there (NULL = not saved).
+ *   ws        : device workspace of ws_bytes >= la_workspace_size() bytes
+ *               (its contents on entry are ignored).
+ */
+int la_forward(const void *Q, const void *K, const void *V, void *O,
+               int64_t B, int64_t H, int64_t N, int64_t D, int causal,
+               int dtype, float *den_out, void *state_out, void *ws,
+               size_t ws_bytes, void *stream);
+
+/*
+ * Backward pass.
+ *   Q, K, V, dO : inputs [B,H,N,D] of `dtype` (dO = dL/dO).
+ *   dQ, dK, dV  : outputs [B,H,N,D] of `dtype`.
+ *   state_in    : optional; the state_out written by la_forward on the same
+ *                 Q/K/V and sizes.  NULL = recompute it from K and V.
+ *   ws          : device workspace of ws_bytes >= la_workspace_size() bytes.
+ */
+int la_backward(const void *Q, const void *K, const void *V, const void *dO,
+                void *dQ, void *dK, void *dV, int64_t B, int64_t H,
+                int64_t N, int64_t D, int causal, int dtype,
+                const void *state_in, void *ws, size_t ws_bytes,
+                void *stream);
+
+/*
+ * Kernel-level timing (benchmarks, profilers).  Same arguments and behaviour
+ * as la_forward / la_backward, plus:
+ *   events     : NULL, or n_events hipEvent_t handles created by the caller
+ *                (as void*).  Before the i-th kernel launch of the call the
+ *                library records events[2i] on `stream`, after it
+ *                events[2i+1], for every i with 2i+1 < n_events.
+ *   n_launched : optional out, the number of kernels the call launched.
+ *   names      : optional out array of n_events/2 entries; names[i] is set
+ *                to a static string naming the i-th kernel ("state_local",
+ *                "state_scan", "forward", "bwd_q", "grad_state_local",
+ *                "bwd_kv").
+ * Events are recorded only when all arguments are valid.  The library
+ * never creates, synchronises or destroys the events.
+ */
+int la_forward_traced(const void *Q, const void *K, const void *V, void *O,
+                      int64_t B, int64_t H, int64_t N, int64_t D, int causal,
+                      int dtype, float *den_out, void *state_out, void *ws,
+                      size_t ws_bytes, void *stream, void *const *events,
+                      int n_events, int *n_launched, const char **names);
+
+int la_backward_traced(const void *Q, const void *K, const void *V,
+                       const void *dO, void *dQ, void *dK, void *dV, int64_t B,
+                       int64_t H, int64_t N, int64_t D, int causal, int dtype,
+                       const void *state_in, void *ws, size_t ws_bytes,
+                       void *stream, void *const *events, int n_events,
+                       int *n_launched, const char **names);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LA_H */

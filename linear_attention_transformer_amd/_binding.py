@@ -1,0 +1,218 @@
+"""ctypes binding of liblinattn.so (C ABI in include/la.h).
+
+Argument marshalling only: every step of the forward and backward pass runs
+in the HIP kernels of the library.  PyTorch provides device memory and the
+current stream.  There is no CPU fallback: if the library is missing or a
+tensor is not on the GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblinattn.so")
+
+LA_FP32, LA_BF16 = 0, 1
+STATUS = {0: "LA_OK", 1: "LA_ERR_NULL", 2: "LA_ERR_SHAPE", 3: "LA_ERR_DTYPE",
+          4: "LA_ERR_UNSUPPORTED", 5: "LA_ERR_WORKSPACE", 6: "LA_ERR_ALIAS",
+          7: "LA_ERR_ALIGN", 8: "LA_ERR_HIP"}
+SUPPORTED_D = (16, 32, 64, 128, 256)
+
+_lib = None
+
+
+class LAError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__("%s failed: %s" % (what, status_string(code)))
+
+
+def load_library():
+    """Load liblinattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            "HIP library %s is not built; run __graft_entry__.build() "
+            "(or python -m linear_attention_transformer_amd.build)" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp, sz, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.la_status_string.argtypes = [ci]
+    lib.la_status_string.restype = ctypes.c_char_p
+    lib.la_workspace_size.argtypes = [i64, i64, i64, i64, ci]
+    lib.la_workspace_size.restype = sz
+    lib.la_state_size.argtypes = [i64, i64, i64, i64, ci]
+    lib.la_state_size.restype = sz
+    lib.la_num_segments.argtypes = [i64, i64, i64, i64, ci]
+    lib.la_num_segments.restype = i64
+    lib.la_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ci, ci, vp, vp,
+                               vp, sz, vp]
+    lib.la_forward.restype = ci
+    lib.la_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ci,
+                                ci, vp, vp, sz, vp]
+    lib.la_backward.restype = ci
+    ev, ip, cpp = ctypes.c_void_p, ctypes.POINTER(ci), ctypes.POINTER(ctypes.c_char_p)
+    lib.la_forward_traced.argtypes = lib.la_forward.argtypes + [ev, ci, ip, cpp]
+    lib.la_forward_traced.restype = ci
+    lib.la_backward_traced.argtypes = lib.la_backward.argtypes + [ev, ci, ip, cpp]
+    lib.la_backward_traced.restype = ci
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load_library().la_status_string(int(code)).decode()
+
+
+def workspace_size(B, H, N, D, causal=False) -> int:
+    return int(load_library().la_workspace_size(B, H, N, D, int(bool(causal))))
+
+
+def state_size(B, H, N, D, causal=False) -> int:
+    return int(load_library().la_state_size(B, H, N, D, int(bool(causal))))
+
+
+def num_segments(B, H, N, D, causal=False) -> int:
+    return int(load_library().la_num_segments(B, H, N, D, int(bool(causal))))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return LA_FP32
+    if t.dtype == torch.bfloat16:
+        return LA_BF16
+    raise TypeError("linear attention supports float32 and bfloat16 storage, got %s"
+                    % t.dtype)
+
+
+def _check(*ts: torch.Tensor):
+    t0 = ts[0]
+    if t0.dim() != 4:
+        raise ValueError("expected [B, H, N, D] tensors, got shape %s" % (tuple(t0.shape),))
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("linear attention runs on the GPU only; got a %s tensor"
+                             % t.device)
+        if t.shape != t0.shape or t.dtype != t0.dtype or t.device != t0.device:
+            raise ValueError("q, k, v (and dO) must share shape, dtype and device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, H, N, D]")
+    return tuple(t0.shape), _dtype_code(t0)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+class KernelTrace:
+    """Caller-owned HIP events that the library records around each of its
+    kernel launches in one call (see la_forward_traced in include/la.h)."""
+
+    def __init__(self, device, max_launches: int = 8):
+        self.max_launches = max_launches
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * max_launches)]
+        stream = torch.cuda.current_stream(device)
+        for e in self.events:      # torch creates the HIP event on first record
+            e.record(stream)
+        self._handles = (ctypes.c_void_p * len(self.events))(
+            *[ctypes.c_void_p(e.cuda_event) for e in self.events])
+        self._names = (ctypes.c_char_p * max_launches)()
+        self._n = ctypes.c_int(0)
+
+    def args(self):
+        return (ctypes.cast(self._handles, ctypes.c_void_p), len(self.events),
+                ctypes.byref(self._n), self._names)
+
+    def names(self):
+        return [self._names[i].decode() for i in range(min(self._n.value, self.max_launches))]
+
+    def times_ms(self):
+        """Per-launch durations (call after the stream has been synchronised)."""
+        return [self.events[2 * i].elapsed_time(self.events[2 * i + 1])
+                for i in range(min(self._n.value, self.max_launches))]
+
+
+def alloc_workspace(B, H, N, D, causal, device) -> torch.Tensor:
+    return torch.empty(max(workspace_size(B, H, N, D, causal), 16), dtype=torch.uint8,
+                       device=device)
+
+
+def forward(q, k, v, causal: bool = False, *, return_den: bool = False,
+            save_state: bool = False, out=None, state_out=None, workspace=None,
+            trace: KernelTrace = None):
+    """O = LA(q, k, v).  Returns (O, den or None, state or None).
+
+    ``state_out`` (a float32 CUDA tensor of state_size() bytes) receives the
+    saved state; ``save_state=True`` allocates one."""
+    (B, H, N, D), dt = _check(q, k, v)
+    lib = load_library()
+    c = int(bool(causal))
+    o = torch.empty_like(q) if out is None else out
+    den = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_den else None
+    state = state_out
+    if state is None and save_state:
+        state = torch.empty(max(state_size(B, H, N, D, causal) // 4, 4),
+                            dtype=torch.float32, device=q.device)
+    ws = alloc_workspace(B, H, N, D, causal, q.device) if workspace is None else workspace
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, D, c, dt, _ptr(den), _ptr(state),
+            _ptr(ws), ws.numel(), _stream(q.device))
+    if trace is None:
+        rc = lib.la_forward(*args)
+    else:
+        rc = lib.la_forward_traced(*args, *trace.args())
+    if rc != 0:
+        raise LAError(rc, "la_forward")
+    return o, den, state
+
+
+def backward(q, k, v, do, causal: bool = False, *, state=None, outs=None,
+             workspace=None, trace: KernelTrace = None):
+    """Returns (dQ, dK, dV) for the upstream gradient do."""
+    (B, H, N, D), dt = _check(q, k, v, do)
+    lib = load_library()
+    c = int(bool(causal))
+    if outs is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    else:
+        dq, dk, dv = outs
+    ws = alloc_workspace(B, H, N, D, causal, q.device) if workspace is None else workspace
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, D,
+            c, dt, _ptr(state), _ptr(ws), ws.numel(), _stream(q.device))
+    if trace is None:
+        rc = lib.la_backward(*args)
+    else:
+        rc = lib.la_backward_traced(*args, *trace.args())
+    if rc != 0:
+        raise LAError(rc, "la_backward")
+    return dq, dk, dv
+
+
+class LinearAttention(torch.autograd.Function):
+    """Autograd wrapper: saves q, k, v and the forward's key-value state
+    (O(D^2) per head, plus one per segment when causal)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, causal=False):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        o, _, state = forward(q, k, v, causal, save_state=True)
+        ctx.save_for_backward(q, k, v, state)
+        ctx.causal = causal
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, state = ctx.saved_tensors
+        dq, dk, dv = backward(q, k, v, do.contiguous(), ctx.causal, state=state)
+        return dq, dk, dv, None
+
+
+def linear_attention(q, k, v, causal: bool = False):
+    return LinearAttention.apply(q, k, v, causal)

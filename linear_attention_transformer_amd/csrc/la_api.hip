@@ -1,0 +1,459 @@
+// la_api.hip -- C ABI of the linear-attention library (declared in
+// include/la.h): argument validation, segment planning, workspace layout and
+// kernel dispatch.  See la_kernels.hpp for the method and its sources.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+
+#include "la.h"
+#include "la_kernels.hpp"
+
+namespace {
+
+using namespace la;
+
+// Segments are multiples of 64 rows (every chunk size divides 64).  The
+// plan aims at >= 512 workgroups per launch (two per CU on 256 CUs) by
+// splitting each head's sequence into segments.
+constexpr int64_t kSegAlign = 64;
+constexpr int64_t kTargetWorkgroups = 512;
+
+struct Plan {
+    int64_t BH, N, D, PS, nseg, seg_len;
+    int causal;
+};
+
+bool supported_d(int64_t D)
+{
+    return D == 16 || D == 32 || D == 64 || D == 128 || D == 256;
+}
+
+Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int causal)
+{
+    Plan p;
+    p.BH = B * H;
+    p.N = N;
+    p.D = D;
+    p.PS = D * D + 2 * D;
+    p.causal = causal;
+    const int64_t nchunks = std::max<int64_t>((N + kSegAlign - 1) / kSegAlign, 1);
+    const int64_t want =
+        p.BH >= kTargetWorkgroups ? 1 : (kTargetWorkgroups + p.BH - 1) / std::max<int64_t>(p.BH, 1);
+    const int64_t ns = std::min(want, nchunks);
+    const int64_t per = (nchunks + ns - 1) / ns;
+    p.seg_len = per * kSegAlign;
+    p.nseg = std::max<int64_t>((N + p.seg_len - 1) / p.seg_len, 1);
+    return p;
+}
+
+// workspace regions, in floats, each rounded up to 64 floats (256 bytes)
+struct Layout {
+    int64_t part, tot, gpart, gtot, cbuf, total;
+};
+
+int64_t up64(int64_t x) { return (x + 63) / 64 * 64; }
+
+Layout make_layout(const Plan &p)
+{
+    Layout l;
+    int64_t off = 0;
+    l.part = off;
+    off += up64(p.BH * p.nseg * p.PS);
+    l.tot = off;
+    off += up64(p.BH * p.PS);
+    l.gpart = off;
+    off += up64(p.BH * p.nseg * p.PS);
+    l.gtot = off;
+    off += up64(p.BH * p.PS);
+    l.cbuf = off;
+    off += up64(p.BH * p.N * 2);
+    l.total = off;
+    return l;
+}
+
+int64_t state_floats(const Plan &p) { return p.BH * (p.causal ? p.nseg : 1) * p.PS; }
+
+int check_sizes(int64_t B, int64_t H, int64_t N, int64_t D, int causal)
+{
+    if (causal != 0 && causal != 1)
+        return LA_ERR_UNSUPPORTED;
+    if (B < 0 || H < 0 || N < 0)
+        return LA_ERR_SHAPE;
+    if (!supported_d(D))
+        return LA_ERR_UNSUPPORTED;
+    int64_t t;
+    if (__builtin_mul_overflow(B, H, &t) || __builtin_mul_overflow(t, N, &t) ||
+        __builtin_mul_overflow(t, D, &t) || __builtin_mul_overflow(t, (int64_t)16, &t))
+        return LA_ERR_SHAPE;
+    // keeps every grid below 2^31 workgroups and row counts exact in fp32
+    if (B * H > (int64_t)1 << 22 || N > (int64_t)1 << 24)
+        return LA_ERR_SHAPE;
+    return LA_OK;
+}
+
+struct Range {
+    const char *p;
+    size_t n;
+};
+
+bool overlap(const Range &a, const Range &b)
+{
+    if (a.p == nullptr || b.p == nullptr || a.n == 0 || b.n == 0)
+        return false;
+    return a.p < b.p + b.n && b.p < a.p + a.n;
+}
+
+bool aliased(const Range *outs, int nout, const Range *ins, int nin)
+{
+    for (int i = 0; i < nout; ++i) {
+        for (int j = 0; j < nin; ++j)
+            if (overlap(outs[i], ins[j]))
+                return true;
+        for (int j = i + 1; j < nout; ++j)
+            if (overlap(outs[i], outs[j]))
+                return true;
+    }
+    return false;
+}
+
+bool misaligned(const void *p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u); }
+
+int launched()
+{
+    return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+// Optional per-launch timing: caller-owned hipEvents recorded around each
+// kernel launch (events[2i] before, events[2i+1] after launch i).
+struct Tracer {
+    void *const *ev;
+    int nev;
+    int n;
+    const char **names;
+};
+
+template <class F>
+int traced(Tracer *t, hipStream_t s, const char *name, F &&launch)
+{
+    const bool rec = t != nullptr && t->ev != nullptr && 2 * t->n + 1 < t->nev;
+    if (rec && hipEventRecord(static_cast<hipEvent_t>(t->ev[2 * t->n]), s) != hipSuccess)
+        return LA_ERR_HIP;
+    launch();
+    const int rc = launched();
+    if (rec && hipEventRecord(static_cast<hipEvent_t>(t->ev[2 * t->n + 1]), s) != hipSuccess)
+        return LA_ERR_HIP;
+    if (t != nullptr) {
+        if (t->names != nullptr && 2 * t->n + 1 < t->nev)
+            t->names[t->n] = name;
+        ++t->n;
+    }
+    return rc;
+}
+
+int scan(float *part, float *out, const Plan &p, int mode, hipStream_t s, Tracer *t)
+{
+    const int64_t bph = (p.PS + 255) / 256;
+    return traced(t, s, "state_scan", [&] {
+        k_state_scan<<<dim3((unsigned)(p.BH * bph)), dim3(256), 0, s>>>(
+            part, out, (int)p.nseg, p.PS, bph, mode);
+    });
+}
+
+template <class ST, int D>
+int state_of_kv(const void *K, const void *V, float *part, float *tot, const Plan &p,
+                hipStream_t s, Tracer *t)
+{
+    typedef Cfg<D, DefCS<D>::value> C;
+    typedef typename ST::T T;
+    const dim3 grid((unsigned)(p.nseg * p.BH * C::CS));
+    int rc = traced(t, s, "state_local", [&] {
+        k_state_local<ST, D><<<grid, dim3(C::NT), 0, s>>>(
+            static_cast<const T *>(K), static_cast<const T *>(V), part, p.N, p.seg_len,
+            (int)p.nseg);
+    });
+    if (rc != LA_OK)
+        return rc;
+    return p.causal ? scan(part, nullptr, p, 1, s, t) : scan(part, tot, p, 0, s, t);
+}
+
+template <class ST, int D>
+int run_forward(const void *Q, const void *K, const void *V, void *O, float *den_out,
+                void *state_out, float *ws, const Plan &p, hipStream_t s, Tracer *t)
+{
+    typedef Cfg<D, DefCS<D>::value> C;
+    typedef typename ST::T T;
+    const Layout l = make_layout(p);
+    float *rec;
+    int rc;
+    if (p.causal) {
+        rec = state_out ? static_cast<float *>(state_out) : ws + l.part;
+        rc = state_of_kv<ST, D>(K, V, rec, nullptr, p, s, t);
+    } else {
+        rec = state_out ? static_cast<float *>(state_out) : ws + l.tot;
+        rc = state_of_kv<ST, D>(K, V, ws + l.part, rec, p, s, t);
+    }
+    if (rc != LA_OK)
+        return rc;
+    const dim3 grid((unsigned)(p.nseg * p.BH * C::CS));
+    return traced(t, s, "forward", [&] {
+        if (p.causal)
+            k_forward<ST, D, true><<<grid, dim3(C::NT), 0, s>>>(
+                static_cast<const T *>(Q), static_cast<const T *>(K),
+                static_cast<const T *>(V), static_cast<T *>(O), den_out, rec, p.N,
+                p.seg_len, (int)p.nseg);
+        else
+            k_forward<ST, D, false><<<grid, dim3(C::NT), 0, s>>>(
+                static_cast<const T *>(Q), static_cast<const T *>(K),
+                static_cast<const T *>(V), static_cast<T *>(O), den_out, rec, p.N,
+                p.seg_len, (int)p.nseg);
+    });
+}
+
+template <class ST, int D, bool CAUSAL>
+int run_backward_t(const void *Q, const void *K, const void *V, const void *G, void *dQ,
+                   void *dK, void *dV, const void *state_in, float *ws, const Plan &p,
+                   hipStream_t s, Tracer *t)
+{
+    typedef Cfg<D, DefCS<D>::value> C;
+    typedef Cfg<D, 1> CQ;
+    typedef typename ST::T T;
+    constexpr bool FUSE = (D != 256);
+    const Layout l = make_layout(p);
+    const float *fstate;
+    int rc;
+    if (state_in) {
+        fstate = static_cast<const float *>(state_in);
+    } else {
+        rc = state_of_kv<ST, D>(K, V, ws + l.part, ws + l.tot, p, s, t);
+        if (rc != LA_OK)
+            return rc;
+        fstate = CAUSAL ? ws + l.part : ws + l.tot;
+    }
+    float *gpart = ws + l.gpart, *cbuf = ws + l.cbuf;
+    const T *q = static_cast<const T *>(Q), *k = static_cast<const T *>(K),
+            *v = static_cast<const T *>(V), *g = static_cast<const T *>(G);
+    rc = traced(t, s, "bwd_q", [&] {
+        k_bwd_q<ST, D, CAUSAL, FUSE><<<dim3((unsigned)(p.nseg * p.BH)), dim3(CQ::NT), 0, s>>>(
+            q, k, v, g, static_cast<T *>(dQ), fstate, gpart, cbuf, p.N, p.seg_len,
+            (int)p.nseg);
+    });
+    if (rc != LA_OK)
+        return rc;
+    const dim3 grid((unsigned)(p.nseg * p.BH * C::CS));
+    if constexpr (!FUSE) {
+        rc = traced(t, s, "grad_state_local", [&] {
+            k_grad_state_local<ST, D><<<grid, dim3(C::NT), 0, s>>>(q, g, cbuf, gpart, p.N,
+                                                                   p.seg_len, (int)p.nseg);
+        });
+        if (rc != LA_OK)
+            return rc;
+    }
+    const float *gstate;
+    if (CAUSAL) {
+        rc = scan(gpart, nullptr, p, 2, s, t);
+        gstate = gpart;
+    } else {
+        rc = scan(gpart, ws + l.gtot, p, 0, s, t);
+        gstate = ws + l.gtot;
+    }
+    if (rc != LA_OK)
+        return rc;
+    return traced(t, s, "bwd_kv", [&] {
+        k_bwd_kv<ST, D, CAUSAL><<<grid, dim3(C::NT), 0, s>>>(
+            q, k, v, g, static_cast<T *>(dK), static_cast<T *>(dV), gstate, cbuf, p.N,
+            p.seg_len, (int)p.nseg);
+    });
+}
+
+template <class ST, int D>
+int run_backward(const void *Q, const void *K, const void *V, const void *G, void *dQ,
+                 void *dK, void *dV, const void *state_in, float *ws, const Plan &p,
+                 hipStream_t s, Tracer *t)
+{
+    if (p.causal)
+        return run_backward_t<ST, D, true>(Q, K, V, G, dQ, dK, dV, state_in, ws, p, s, t);
+    return run_backward_t<ST, D, false>(Q, K, V, G, dQ, dK, dV, state_in, ws, p, s, t);
+}
+
+template <class ST>
+int dispatch_forward(const void *Q, const void *K, const void *V, void *O, float *den,
+                     void *st, float *ws, const Plan &p, hipStream_t s, Tracer *t)
+{
+    switch (p.D) {
+    case 16: return run_forward<ST, 16>(Q, K, V, O, den, st, ws, p, s, t);
+    case 32: return run_forward<ST, 32>(Q, K, V, O, den, st, ws, p, s, t);
+    case 64: return run_forward<ST, 64>(Q, K, V, O, den, st, ws, p, s, t);
+    case 128: return run_forward<ST, 128>(Q, K, V, O, den, st, ws, p, s, t);
+    case 256: return run_forward<ST, 256>(Q, K, V, O, den, st, ws, p, s, t);
+    default: return LA_ERR_UNSUPPORTED;
+    }
+}
+
+template <class ST>
+int dispatch_backward(const void *Q, const void *K, const void *V, const void *G, void *dQ,
+                      void *dK, void *dV, const void *st, float *ws, const Plan &p,
+                      hipStream_t s, Tracer *t)
+{
+    switch (p.D) {
+    case 16: return run_backward<ST, 16>(Q, K, V, G, dQ, dK, dV, st, ws, p, s, t);
+    case 32: return run_backward<ST, 32>(Q, K, V, G, dQ, dK, dV, st, ws, p, s, t);
+    case 64: return run_backward<ST, 64>(Q, K, V, G, dQ, dK, dV, st, ws, p, s, t);
+    case 128: return run_backward<ST, 128>(Q, K, V, G, dQ, dK, dV, st, ws, p, s, t);
+    case 256: return run_backward<ST, 256>(Q, K, V, G, dQ, dK, dV, st, ws, p, s, t);
+    default: return LA_ERR_UNSUPPORTED;
+    }
+}
+
+size_t elem_size(int dtype) { return dtype == LA_BF16 ? 2 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+const char *la_status_string(int status)
+{
+    switch (status) {
+    case LA_OK: return "LA_OK";
+    case LA_ERR_NULL: return "LA_ERR_NULL: a required pointer is NULL";
+    case LA_ERR_SHAPE: return "LA_ERR_SHAPE: negative or too large size";
+    case LA_ERR_DTYPE: return "LA_ERR_DTYPE: dtype must be LA_FP32 or LA_BF16";
+    case LA_ERR_UNSUPPORTED:
+        return "LA_ERR_UNSUPPORTED: D must be 16, 32, 64, 128 or 256 and causal 0 or 1";
+    case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE: workspace too small";
+    case LA_ERR_ALIAS: return "LA_ERR_ALIAS: an output overlaps an input or another output";
+    case LA_ERR_ALIGN: return "LA_ERR_ALIGN: device pointers must be 16-byte aligned";
+    case LA_ERR_HIP: return "LA_ERR_HIP: a HIP launch failed";
+    default: return "unknown la_status";
+    }
+}
+
+int64_t la_num_segments(int64_t B, int64_t H, int64_t N, int64_t D, int causal)
+{
+    if (check_sizes(B, H, N, D, causal) != LA_OK)
+        return 0;
+    return make_plan(B, H, N, D, causal).nseg;
+}
+
+size_t la_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D, int causal)
+{
+    if (check_sizes(B, H, N, D, causal) != LA_OK || B * H * N == 0)
+        return 0;
+    return (size_t)make_layout(make_plan(B, H, N, D, causal)).total * sizeof(float);
+}
+
+size_t la_state_size(int64_t B, int64_t H, int64_t N, int64_t D, int causal)
+{
+    if (check_sizes(B, H, N, D, causal) != LA_OK || B * H * N == 0)
+        return 0;
+    return (size_t)state_floats(make_plan(B, H, N, D, causal)) * sizeof(float);
+}
+
+int la_forward_traced(const void *Q, const void *K, const void *V, void *O, int64_t B,
+                      int64_t H, int64_t N, int64_t D, int causal, int dtype, float *den_out,
+                      void *state_out, void *ws, size_t ws_bytes, void *stream,
+                      void *const *events, int n_events, int *n_launched, const char **names)
+{
+    if (n_launched)
+        *n_launched = 0;
+    if (dtype != LA_FP32 && dtype != LA_BF16)
+        return LA_ERR_DTYPE;
+    int rc = check_sizes(B, H, N, D, causal);
+    if (rc != LA_OK)
+        return rc;
+    if (B * H * N == 0)
+        return LA_OK;
+    if (!Q || !K || !V || !O || !ws)
+        return LA_ERR_NULL;
+    const Plan p = make_plan(B, H, N, D, causal);
+    const size_t need = (size_t)make_layout(p).total * sizeof(float);
+    if (ws_bytes < need)
+        return LA_ERR_WORKSPACE;
+    if (misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(O) ||
+        misaligned(den_out) || misaligned(state_out) || misaligned(ws))
+        return LA_ERR_ALIGN;
+    const size_t tb = (size_t)(B * H * N * D) * elem_size(dtype);
+    const Range ins[3] = {{(const char *)Q, tb}, {(const char *)K, tb}, {(const char *)V, tb}};
+    const Range outs[4] = {
+        {(const char *)O, tb},
+        {(const char *)den_out, (size_t)(B * H * N) * sizeof(float)},
+        {(const char *)state_out, (size_t)state_floats(p) * sizeof(float)},
+        {(const char *)ws, need}};
+    if (aliased(outs, 4, ins, 3))
+        return LA_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float *w = static_cast<float *>(ws);
+    Tracer t{events, events ? n_events : 0, 0, names};
+    rc = (dtype == LA_FP32)
+             ? dispatch_forward<StF32>(Q, K, V, O, den_out, state_out, w, p, s, &t)
+             : dispatch_forward<StBF16>(Q, K, V, O, den_out, state_out, w, p, s, &t);
+    if (n_launched)
+        *n_launched = t.n;
+    return rc;
+}
+
+int la_forward(const void *Q, const void *K, const void *V, void *O, int64_t B, int64_t H,
+               int64_t N, int64_t D, int causal, int dtype, float *den_out, void *state_out,
+               void *ws, size_t ws_bytes, void *stream)
+{
+    return la_forward_traced(Q, K, V, O, B, H, N, D, causal, dtype, den_out, state_out, ws,
+                             ws_bytes, stream, nullptr, 0, nullptr, nullptr);
+}
+
+int la_backward_traced(const void *Q, const void *K, const void *V, const void *dO, void *dQ,
+                       void *dK, void *dV, int64_t B, int64_t H, int64_t N, int64_t D,
+                       int causal, int dtype, const void *state_in, void *ws, size_t ws_bytes,
+                       void *stream, void *const *events, int n_events, int *n_launched,
+                       const char **names)
+{
+    if (n_launched)
+        *n_launched = 0;
+    if (dtype != LA_FP32 && dtype != LA_BF16)
+        return LA_ERR_DTYPE;
+    int rc = check_sizes(B, H, N, D, causal);
+    if (rc != LA_OK)
+        return rc;
+    if (B * H * N == 0)
+        return LA_OK;
+    if (!Q || !K || !V || !dO || !dQ || !dK || !dV || !ws)
+        return LA_ERR_NULL;
+    const Plan p = make_plan(B, H, N, D, causal);
+    const size_t need = (size_t)make_layout(p).total * sizeof(float);
+    if (ws_bytes < need)
+        return LA_ERR_WORKSPACE;
+    if (misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(dO) ||
+        misaligned(dQ) || misaligned(dK) || misaligned(dV) || misaligned(state_in) ||
+        misaligned(ws))
+        return LA_ERR_ALIGN;
+    const size_t tb = (size_t)(B * H * N * D) * elem_size(dtype);
+    const Range ins[5] = {{(const char *)Q, tb},
+                          {(const char *)K, tb},
+                          {(const char *)V, tb},
+                          {(const char *)dO, tb},
+                          {(const char *)state_in, (size_t)state_floats(p) * sizeof(float)}};
+    const Range outs[4] = {
+        {(const char *)dQ, tb}, {(const char *)dK, tb}, {(const char *)dV, tb},
+        {(const char *)ws, need}};
+    if (aliased(outs, 4, ins, 5))
+        return LA_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float *w = static_cast<float *>(ws);
+    Tracer t{events, events ? n_events : 0, 0, names};
+    rc = (dtype == LA_FP32)
+             ? dispatch_backward<StF32>(Q, K, V, dO, dQ, dK, dV, state_in, w, p, s, &t)
+             : dispatch_backward<StBF16>(Q, K, V, dO, dQ, dK, dV, state_in, w, p, s, &t);
+    if (n_launched)
+        *n_launched = t.n;
+    return rc;
+}
+
+int la_backward(const void *Q, const void *K, const void *V, const void *dO, void *dQ,
+                void *dK, void *dV, int64_t B, int64_t H, int64_t N, int64_t D, int causal,
+                int dtype, const void *state_in, void *ws, size_t ws_bytes, void *stream)
+{
+    return la_backward_traced(Q, K, V, dO, dQ, dK, dV, B, H, N, D, causal, dtype, state_in, ws,
+                              ws_bytes, stream, nullptr, 0, nullptr, nullptr);
+}
+
+}  // extern "C"

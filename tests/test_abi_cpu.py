@@ -1,0 +1,118 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+that include/la.h declares, and rejects bad arguments on the host before any
+launch.  The argument-validation cases pass host addresses as stand-ins for
+device pointers, so they only run where no GPU is visible (a validation bug
+there could otherwise launch a kernel on them)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import linear_attention_transformer_amd as la
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "la.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_[a-z_]+)\s*\(", text)))
+
+
+def test_library_built_and_loads():
+    assert os.path.exists(la.LIB_PATH)
+    la.load_library()
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"la_forward", "la_backward", "la_workspace_size", "la_state_size",
+            "la_status_string", "la_num_segments"} <= set(names)
+    lib = ctypes.CDLL(la.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", la.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (la_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_status_strings():
+    for code, name in la.STATUS.items():
+        assert la.status_string(code).startswith(name)
+    assert la.status_string(99) == "unknown la_status"
+
+
+def test_sizes():
+    B, H, N, D = 4, 16, 4096, 128
+    ns = la.num_segments(B, H, N, D)
+    assert ns == 8
+    ps = D * D + 2 * D
+    assert la.state_size(B, H, N, D, False) == B * H * ps * 4
+    assert la.state_size(B, H, N, D, True) == B * H * ns * ps * 4
+    ws = la.workspace_size(B, H, N, D, True)
+    # workspace is O(B H (segments D^2 + N)): far below one [B,H,N,D] tensor
+    # once N >> D; here it must stay below the four fp32 inputs
+    assert 0 < ws < 4 * B * H * N * D * 4
+    assert la.workspace_size(0, 16, 4096, 128) == 0
+    assert la.workspace_size(4, 16, 4096, 48) == 0       # unsupported D
+    assert la.workspace_size(4, 16, -1, 128) == 0
+    # segments grow with N, never exceed the 64-row chunks
+    for n in (1, 63, 64, 65, 1000, 131072):
+        s = la.num_segments(1, 1, n, 64)
+        assert 1 <= s <= max(1, (n + 63) // 64)
+
+
+needs_no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
+                                  reason="host-only validation with stand-in pointers")
+
+
+@needs_no_gpu
+def test_host_validation_rejects_before_launch():
+    lib = la.load_library()
+    buf = (ctypes.c_char * (1 << 20))()
+    base = ctypes.addressof(buf)
+    a16 = (base + 15) & ~15
+    P = lambda off=0: ctypes.c_void_p(a16 + off)
+    B, H, N, D = 1, 2, 8, 16
+    ws = la.workspace_size(B, H, N, D, False)
+    tb = B * H * N * D * 4
+    f = lib.la_forward
+    # dtype, causal, sizes, D
+    assert f(P(), P(tb), P(2 * tb), P(3 * tb), B, H, N, D, 0, 7, None, None, P(4 * tb), ws, None) == 3
+    assert f(P(), P(tb), P(2 * tb), P(3 * tb), B, H, N, D, 2, 0, None, None, P(4 * tb), ws, None) == 4
+    assert f(P(), P(tb), P(2 * tb), P(3 * tb), B, H, -1, D, 0, 0, None, None, P(4 * tb), ws, None) == 2
+    assert f(P(), P(tb), P(2 * tb), P(3 * tb), B, H, N, 6, 0, 0, None, None, P(4 * tb), ws, None) == 4
+    assert f(P(), P(tb), P(2 * tb), P(3 * tb), 1 << 40, 1 << 40, N, D, 0, 0, None, None,
+             P(4 * tb), ws, None) == 2
+    # empty problem is a no-op even with NULL pointers
+    assert f(None, None, None, None, B, H, 0, D, 0, 0, None, None, None, 0, None) == 0
+    # NULL, workspace, alignment, aliasing
+    assert f(None, P(tb), P(2 * tb), P(3 * tb), B, H, N, D, 0, 0, None, None, P(4 * tb), ws, None) == 1
+    assert f(P(), P(tb), P(2 * tb), P(3 * tb), B, H, N, D, 0, 0, None, None, P(4 * tb), ws - 4, None) == 5
+    assert f(P(4), P(tb), P(2 * tb), P(3 * tb), B, H, N, D, 0, 0, None, None, P(4 * tb), ws, None) == 7
+    assert f(P(), P(tb), P(2 * tb), P(0), B, H, N, D, 0, 0, None, None, P(4 * tb), ws, None) == 6
+    assert f(P(), P(tb), P(2 * tb), P(3 * tb), B, H, N, D, 0, 0, None, None, P(3 * tb), ws, None) == 6
+    assert f(P(), P(tb), P(2 * tb), P(3 * tb), B, H, N, D, 0, 0, ctypes.c_void_p(a16 + 3 * tb + 16),
+             None, P(4 * tb), ws, None) == 6
+    g = lib.la_backward
+    args = lambda q, gw: (P(q), P(tb), P(2 * tb), P(3 * tb), P(4 * tb), P(5 * tb), P(6 * tb),
+                          B, H, N, D, 0, 0, None, P(7 * tb), gw)
+    assert g(*args(0, ws - 16), None) == 5
+    assert g(*args(8, ws), None) == 7
+    assert g(P(), P(tb), P(2 * tb), P(3 * tb), P(4 * tb), P(4 * tb), P(6 * tb), B, H, N, D, 0, 0,
+             None, P(7 * tb), ws, None) == 6
+    assert g(P(), P(tb), P(2 * tb), P(3 * tb), P(4 * tb), P(5 * tb), P(6 * tb), B, H, N, D, 0, 0,
+             P(4 * tb), P(7 * tb), ws, None) == 6
+    assert g(P(), P(tb), P(2 * tb), None, P(4 * tb), P(5 * tb), P(6 * tb), B, H, N, D, 0, 0,
+             None, P(7 * tb), ws, None) == 1
+
+
+def test_python_side_refuses_cpu_tensors():
+    q = torch.zeros(1, 1, 4, 16)
+    with pytest.raises(ValueError):
+        la.forward(q, q, q)
