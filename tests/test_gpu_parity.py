@@ -226,10 +226,10 @@ def test_validation_errors_on_device():
     with pytest.raises(m.LAError) as e:
         m.forward(q, k, v, False, out=q)          # output aliases an input
     assert e.value.code == 6
-    big = torch.zeros(1, 2, 65 * 64 + 1, device=DEV)
-    mis = big[1:].view(1, 2, 65, 64)[:, :, :64]    # 4-byte offset
+    big = torch.zeros(2 * 65 * 64, device=DEV)
+    strided = big.view(1, 2, 65, 64)[:, :, :64]
     with pytest.raises(ValueError):
-        m.forward(mis, k, v)                      # not contiguous
+        m.forward(strided, k, v)                  # not contiguous
     flat = torch.zeros(2 * 64 * 64 + 1, device=DEV)
     mis = flat[1:].view(1, 2, 64, 64)
     with pytest.raises(m.LAError) as e:
