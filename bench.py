@@ -170,7 +170,7 @@ def main():
     avg_us = {n: 1e3 * sum(v) / len(v) for n, v in per_kernel.items()}
     step_us = {n: avg_us[n] * launches[n] for n in avg_us}
     dom = max(step_us, key=step_us.get)
-    fused = D != 256
+    fused = "grad_state_local" not in per_kernel   # dQ kernel also reduces dS
     flops, nbytes = algorithmic(dom, B * H, N, D, s, fused)
     t_dom = avg_us[dom] * 1e-6
     ridge = PEAK_FP32_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)

@@ -9,6 +9,7 @@
 
 #include "la.h"
 #include "la_kernels.hpp"
+#include "la_kernels_nc.hpp"
 
 namespace {
 
@@ -161,18 +162,40 @@ int scan(float *part, float *out, const Plan &p, int mode, hipStream_t s, Tracer
     });
 }
 
+// the non-causal fast path (la_kernels_nc.hpp) covers 32 <= D <= 128
+template <int D>
+constexpr bool nc_path()
+{
+    return D >= 32 && D <= 128;
+}
+
 template <class ST, int D>
 int state_of_kv(const void *K, const void *V, float *part, float *tot, const Plan &p,
                 hipStream_t s, Tracer *t)
 {
     typedef Cfg<D, DefCS<D>::value> C;
     typedef typename ST::T T;
-    const dim3 grid((unsigned)(p.nseg * p.BH * C::CS));
-    int rc = traced(t, s, "state_local", [&] {
-        k_state_local<ST, D><<<grid, dim3(C::NT), 0, s>>>(
-            static_cast<const T *>(K), static_cast<const T *>(V), part, p.N, p.seg_len,
-            (int)p.nseg);
-    });
+    int rc = LA_OK;
+    bool done = false;
+    if constexpr (nc_path<D>()) {
+        if (!p.causal) {
+            rc = traced(t, s, "state_local", [&] {
+                nc::k_reduce_nc<ST, D, false><<<dim3((unsigned)(p.nseg * p.BH)),
+                                                dim3(nc::kReduceThreads), 0, s>>>(
+                    static_cast<const T *>(K), static_cast<const T *>(V), nullptr, part, p.N,
+                    p.seg_len, (int)p.nseg);
+            });
+            done = true;
+        }
+    }
+    if (!done) {
+        const dim3 grid((unsigned)(p.nseg * p.BH * C::CS));
+        rc = traced(t, s, "state_local", [&] {
+            k_state_local<ST, D><<<grid, dim3(C::NT), 0, s>>>(
+                static_cast<const T *>(K), static_cast<const T *>(V), part, p.N, p.seg_len,
+                (int)p.nseg);
+        });
+    }
     if (rc != LA_OK)
         return rc;
     return p.causal ? scan(part, nullptr, p, 1, s, t) : scan(part, tot, p, 0, s, t);
@@ -196,6 +219,15 @@ int run_forward(const void *Q, const void *K, const void *V, void *O, float *den
     }
     if (rc != LA_OK)
         return rc;
+    if constexpr (nc_path<D>()) {
+        if (!p.causal)
+            return traced(t, s, "forward", [&] {
+                nc::k_apply_nc<ST, D, 0><<<dim3((unsigned)(p.nseg * p.BH)),
+                                           dim3(nc::kApplyThreads), 0, s>>>(
+                    static_cast<const T *>(Q), nullptr, static_cast<T *>(O), nullptr, den_out,
+                    nullptr, rec, p.N, p.seg_len, (int)p.nseg);
+            });
+    }
     const dim3 grid((unsigned)(p.nseg * p.BH * C::CS));
     return traced(t, s, "forward", [&] {
         if (p.causal)
@@ -234,6 +266,30 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
     float *gpart = ws + l.gpart, *cbuf = ws + l.cbuf;
     const T *q = static_cast<const T *>(Q), *k = static_cast<const T *>(K),
             *v = static_cast<const T *>(V), *g = static_cast<const T *>(G);
+    if constexpr (!CAUSAL && nc_path<D>()) {
+        const dim3 g1((unsigned)(p.nseg * p.BH));
+        rc = traced(t, s, "bwd_q", [&] {
+            nc::k_apply_nc<ST, D, 1><<<g1, dim3(nc::kApplyThreads), 0, s>>>(
+                g, q, static_cast<T *>(dQ), nullptr, nullptr, cbuf, fstate, p.N, p.seg_len,
+                (int)p.nseg);
+        });
+        if (rc != LA_OK)
+            return rc;
+        rc = traced(t, s, "grad_state_local", [&] {
+            nc::k_reduce_nc<ST, D, true><<<g1, dim3(nc::kReduceThreads), 0, s>>>(
+                q, g, cbuf, gpart, p.N, p.seg_len, (int)p.nseg);
+        });
+        if (rc != LA_OK)
+            return rc;
+        if ((rc = scan(gpart, ws + l.gtot, p, 0, s, t)) != LA_OK)
+            return rc;
+        return traced(t, s, "bwd_kv", [&] {
+            nc::k_apply_nc<ST, D, 2><<<dim3((unsigned)(2 * p.nseg * p.BH)),
+                                       dim3(nc::kApplyThreads), 0, s>>>(
+                v, k, static_cast<T *>(dK), static_cast<T *>(dV), nullptr, nullptr,
+                ws + l.gtot, p.N, p.seg_len, (int)p.nseg);
+        });
+    }
     rc = traced(t, s, "bwd_q", [&] {
         k_bwd_q<ST, D, CAUSAL, FUSE><<<dim3((unsigned)(p.nseg * p.BH)), dim3(CQ::NT), 0, s>>>(
             q, k, v, g, static_cast<T *>(dQ), fstate, gpart, cbuf, p.N, p.seg_len,
