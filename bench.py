@@ -33,8 +33,19 @@ METRIC = "LA fwd+bwd tokens/s at B4 H16 D128 N4096; % of binding HBM/FLOP roofli
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix (= fp32 vector) peak
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 KERNEL_SOURCES = [os.path.join(ROOT, "linear_attention_transformer_amd", "csrc", f)
-                  for f in ("la_kernels.hpp", "la_api.hip")]
+                  for f in ("la_kernels.hpp", "la_kernels_nc.hpp", "la_api.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COPY_MIB = 256                  # plain streaming kernel: reads and writes this much
+
+# device kernel (demangled name) -> launch name the library's tracer reports
+KERNEL_NAMES = [
+    (r"k_reduce_nc<[^>]*, (true|1)>|k_grad_state_local<", "grad_state_local"),
+    (r"k_reduce_nc<|k_state_local<", "state_local"),
+    (r"k_apply_nc<[^>]*, 0>|k_forward<", "forward"),
+    (r"k_apply_nc<[^>]*, 1>|k_bwd_q<", "bwd_q"),
+    (r"k_apply_nc<[^>]*, 2>|k_bwd_kv<", "bwd_kv"),
+    (r"k_state_scan", "state_scan"),
+]
 
 
 def kernel_source_hash() -> str:
@@ -60,6 +71,100 @@ def algorithmic(kernel: str, BH: int, N: int, D: int, s: int, fused_bwd_q: bool)
     return table.get(kernel, (0, 0))
 
 
+def launch_name(kernel: str):
+    import re
+    for pat, name in KERNEL_NAMES:
+        if re.search(pat, kernel):
+            return name
+    return None
+
+
+def workload_key(kernel, B, H, N, D, dtype, causal):
+    return "%s B%d H%d N%d D%d %s causal=%d" % (kernel, B, H, N, D, dtype, int(causal))
+
+
+def pmc_summary(fetch_dir, write_dir, args):
+    """Per-launch HBM traffic of the library's kernels from two rocprofv3
+    --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per
+    dispatch).  Each counter is scaled by what it reads for the copy kernel
+    the same run launches (COPY_MIB read and COPY_MIB written), so the
+    figures are bytes.  Merges the entries into profiles/traffic.json and
+    prints a markdown table."""
+    import csv
+    import glob
+
+    def load(d, counter):
+        per, calib = {}, []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                val = float(r["Counter_Value"])
+                if "neg_kernel" in r["Kernel_Name"]:
+                    calib.append(val)
+                name = launch_name(r["Kernel_Name"]) if "la::" in r["Kernel_Name"] else None
+                if name:
+                    per.setdefault(name, []).append(val)
+        if not calib:
+            sys.exit("bench.py: no copy-kernel dispatch with %s under %s" % (counter, d))
+        return {n: sum(v) / len(v) for n, v in per.items()}, sum(calib) / len(calib), \
+            {n: len(v) for n, v in per.items()}
+
+    fetch, fcal, count = load(fetch_dir, "FETCH_SIZE")
+    write, wcal, _ = load(write_dir, "WRITE_SIZE")
+    copy_bytes = COPY_MIB << 20
+    fs, wsc = copy_bytes / (fcal * 1024), copy_bytes / (wcal * 1024)
+    doc = {"entries": {}}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            doc = json.load(f)
+    if doc.get("kernel_source_hash") != kernel_source_hash():
+        doc = {"entries": {}}
+    doc["kernel_source_hash"] = kernel_source_hash()
+    doc["calibration"] = {"copy_bytes_each_way": copy_bytes, "fetch_kib": fcal,
+                          "write_kib": wcal, "fetch_scale": fs, "write_scale": wsc}
+    s = 4 if args.dtype == "fp32" else 2
+    print("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB | write MB "
+          "| traffic MB | algorithmic MB |")
+    print("|---|---|---|---|---|---|---|---|")
+    for name in sorted(fetch):
+        rd, wr = fetch[name] * 1024 * fs, write.get(name, 0.0) * 1024 * wsc
+        key = workload_key(name, args.B, args.H, args.N, args.D, args.dtype, args.causal)
+        doc["entries"][key] = {"bytes_per_launch": round(rd + wr), "read_bytes": round(rd),
+                               "write_bytes": round(wr)}
+        alg = algorithmic(name, args.B * args.H, args.N, args.D, s,
+                          "grad_state_local" not in fetch)[1]
+        print("| %s | %d | %.0f | %.0f | %.1f | %.1f | %.1f | %.1f |"
+              % (name, count[name], fetch[name], write.get(name, 0.0), rd / 1e6, wr / 1e6,
+                 (rd + wr) / 1e6, alg / 1e6))
+    print("\ncalibration: copy kernel of %d MiB each way read FETCH_SIZE %.0f KiB, "
+          "WRITE_SIZE %.0f KiB -> scales %.3f, %.3f" % (COPY_MIB, fcal, wcal, fs, wsc))
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(doc, f, indent=1, sort_keys=True)
+
+
+def copy_reference(dev):
+    """Bandwidth of a plain streaming kernel (torch.neg over COPY_MIB fp32,
+    read once and written once): the achievable-HBM reference, and the
+    calibration dispatch for the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = (COPY_MIB << 20) // 4
+    src = torch.zeros(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    reps = 5
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps * 1e-3
+    del src, dst
+    return 2 * (COPY_MIB << 20) / t / 1e9
+
+
 def cpu_baseline(q, k, v, g, causal):
     import oracle
     from linear_attention_transformer_amd.inputs import as_f64_numpy
@@ -71,16 +176,20 @@ def cpu_baseline(q, k, v, g, causal):
     sel = lambda t: t.reshape(BH, N, D)[:heads].unsqueeze(0)
     a = [as_f64_numpy(sel(x)) for x in (q, k, v, g)]
     oracle.build(force=False)
-    t0 = time.perf_counter()
-    oracle.forward_state(a[0], a[1], a[2], causal)
-    oracle.backward_state(*a, causal)
-    dt = time.perf_counter() - t0
+    times = []
+    while len(times) < 3 and sum(times) < 10.0:   # median of up to 3 runs, ~10 s
+        t0 = time.perf_counter()
+        oracle.forward_state(a[0], a[1], a[2], causal)
+        oracle.backward_state(*a, causal)
+        times.append(time.perf_counter() - t0)
+    dt = sorted(times)[len(times) // 2]
     tokens = B * N * heads / BH
     return {"value": tokens / dt, "unit": "tokens/s", "cores": oracle.max_threads(),
             "kind": "oracle",
-            "sample": "fp64 C oracle (state form, OpenMP over heads), one forward+"
-                      "backward of %d of the %d heads at N=%d D=%d, %.2f s; value "
-                      "scaled to the workload's B*N tokens" % (heads, BH, N, D, dt)}
+            "sample": "fp64 C oracle (state form, OpenMP over heads), forward+backward "
+                      "of %d of the %d heads at N=%d D=%d; median of %d runs, %.2f s "
+                      "each; value scaled to the workload's B*N tokens"
+                      % (heads, BH, N, D, len(times), dt)}
 
 
 def main():
@@ -97,7 +206,14 @@ def main():
     ap.add_argument("--N", type=int, default=4096)
     ap.add_argument("--D", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs of this script (FETCH_SIZE, "
+                         "WRITE_SIZE) for the given workload into profiles/traffic.json; "
+                         "no GPU work")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -135,6 +251,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    copy_gbs = copy_reference(dev)
 
     # timed region 1: the headline, nothing but the K steps
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -182,7 +299,7 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        key = "%s B%d H%d N%d D%d %s causal=%d" % (dom, B, H, N, D, args.dtype, int(causal))
+        key = workload_key(dom, B, H, N, D, args.dtype, causal)
         ent = tr.get("entries", {}).get(key)
         if ent and tr.get("kernel_source_hash") == kernel_source_hash():
             traffic = ent["bytes_per_launch"]
@@ -226,6 +343,7 @@ def main():
                           "frac": round(step_floor_us / (ms * 1e3), 4)},
         "kernels_us_per_launch": {n: round(t, 2) for n, t in avg_us.items()},
         "traced_ms_per_step": round(traced_ms, 4),
+        "hbm_copy_GBs": round(copy_gbs, 1),
     }
     print(json.dumps(line), flush=True)
 
