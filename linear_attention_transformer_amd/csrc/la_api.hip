@@ -225,7 +225,7 @@ int run_forward(const void *Q, const void *K, const void *V, void *O, float *den
                 nc::k_apply_nc<ST, D, 0><<<dim3((unsigned)(p.nseg * p.BH)),
                                            dim3(nc::kApplyThreads), 0, s>>>(
                     static_cast<const T *>(Q), nullptr, static_cast<T *>(O), nullptr, den_out,
-                    nullptr, rec, p.N, p.seg_len, (int)p.nseg);
+                    rec, p.N, p.seg_len, (int)p.nseg);
             });
     }
     const dim3 grid((unsigned)(p.nseg * p.BH * C::CS));
@@ -268,16 +268,10 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
             *v = static_cast<const T *>(V), *g = static_cast<const T *>(G);
     if constexpr (!CAUSAL && nc_path<D>()) {
         const dim3 g1((unsigned)(p.nseg * p.BH));
+        // dQ and the segment's gradient record in one pass
         rc = traced(t, s, "bwd_q", [&] {
-            nc::k_apply_nc<ST, D, 1><<<g1, dim3(nc::kApplyThreads), 0, s>>>(
-                g, q, static_cast<T *>(dQ), nullptr, nullptr, cbuf, fstate, p.N, p.seg_len,
-                (int)p.nseg);
-        });
-        if (rc != LA_OK)
-            return rc;
-        rc = traced(t, s, "grad_state_local", [&] {
-            nc::k_reduce_nc<ST, D, true><<<g1, dim3(nc::kReduceThreads), 0, s>>>(
-                q, g, cbuf, gpart, p.N, p.seg_len, (int)p.nseg);
+            nc::k_bwd_q_nc<ST, D><<<g1, dim3(512), 0, s>>>(
+                g, q, static_cast<T *>(dQ), gpart, fstate, p.N, p.seg_len, (int)p.nseg);
         });
         if (rc != LA_OK)
             return rc;
@@ -286,8 +280,8 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
         return traced(t, s, "bwd_kv", [&] {
             nc::k_apply_nc<ST, D, 2><<<dim3((unsigned)(2 * p.nseg * p.BH)),
                                        dim3(nc::kApplyThreads), 0, s>>>(
-                v, k, static_cast<T *>(dK), static_cast<T *>(dV), nullptr, nullptr,
-                ws + l.gtot, p.N, p.seg_len, (int)p.nseg);
+                v, k, static_cast<T *>(dK), static_cast<T *>(dV), nullptr, ws + l.gtot, p.N,
+                p.seg_len, (int)p.nseg);
         });
     }
     rc = traced(t, s, "bwd_q", [&] {

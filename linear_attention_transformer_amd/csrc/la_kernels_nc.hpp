@@ -105,6 +105,17 @@ __device__ __forceinline__ f16v zero16()
     return z;
 }
 
+// Wait until every global load issued so far has returned.  Called once,
+// before a loop whose body reads registers loaded ahead of it: otherwise the
+// compiler keeps those loads pending across the loop's back edge and waits
+// on them inside the loop, which also drains the loop's own prefetches.
+__device__ __forceinline__ void drain_loads()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0); expcnt, lgkmcnt not waited on
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // VW consecutive elements at p, widened to fp32 into o[0..VW)
 template <class ST, int VW>
 __device__ __forceinline__ void load_vec(const typename ST::T *p, float *o)
@@ -329,13 +340,11 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce_nc(
 // A is the MFMA left operand applied to each row x_i of X:
 // KIND 0 forward : A = S^T;  o_i = (u + A q_i) / (N + q_i.z);
 //                  X = Q.  den_out[i] = N + q_i.z (optional).
-// KIND 1 dQ      : A = S;  a_i = g_i / den_i, y_i = A a_i,
-//                  c_i = (a_i.u + q_i.y_i) / den_i, dq_i = y_i - c_i z;
-//                  X = dO, X2 = Q; cbuf[i] = (c_i, 1/den_i).
 // KIND 2 dK | dV : blockIdx parity 0: A = dS, X = V, dk_j = A v_j - r;
 //                  parity 1: A = dS^T, X2 = K, dv_j = A k_j + t.
 // rec: total record of the head: Mat[D][D], vec1[D], vec2[D] =
-//      (S, z, u) for KIND 0/1 and (dS, r, t) for KIND 2.
+//      (S, z, u) for KIND 0 and (dS, r, t) for KIND 2.
+// (dQ is k_bwd_q_nc below.)
 //
 // The workgroup's waves split the output columns into 32-column blocks
 // (and, for D < 128, the rows into row groups).  Each wave keeps its block
@@ -346,21 +355,26 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce_nc(
 // from there: column n = tile row j, k-block kb = columns kb*8 .. kb*8+7
 // (lane half h reads 4*h .. 4*h+3 as one 16-byte LDS read feeding four
 // MFMAs).  The accumulator returns 4 groups of 4 consecutive output columns
-// per lane (16-byte stores).  The normalisation is linear, so per-row
-// scalars are applied in the epilogue; row sums over all columns (q.z, and
-// for dQ also dO.u and q.y) are formed per column block and exchanged
-// through LDS at the same barrier.  Rows past the end of the segment are
-// staged as zeros and not stored.
+// per lane (16-byte stores).  Rows past the end of the segment are staged
+// as zeros and not stored.
+//
+// The round loop is software-pipelined so that the MFMA chain of a round
+// runs with the other work in its shadow: the stores of the previous
+// round's rows are issued between its k-blocks, and in the forward q_j.z
+// is accumulated from the very operands the MFMAs consume (lane half h sees
+// half of row j's columns; the halves are added after the loop), so the
+// normalisation needs no exchange between waves.
 template <class ST, int D, int KIND>
 __global__ __launch_bounds__(kApplyThreads) void k_apply_nc(
     const typename ST::T *__restrict__ X, const typename ST::T *__restrict__ X2,
     typename ST::T *__restrict__ Out, typename ST::T *__restrict__ Out2,
-    float *__restrict__ den_out, float *__restrict__ cbuf, const float *__restrict__ rec,
-    int64_t N, int64_t seg_len, int nseg)
+    float *__restrict__ den_out, const float *__restrict__ rec, int64_t N, int64_t seg_len,
+    int nseg)
 {
     typedef typename ST::T T;
     typedef IO<ST> io;
     static_assert(D >= 32, "32-column output blocks");
+    static_assert(KIND == 0 || KIND == 2, "forward or dK | dV");
     constexpr int KB = D / 8;                // k-blocks of 8
     constexpr int NWAVE = kApplyThreads / 64;
     constexpr int NCB = D / 32;              // column blocks
@@ -373,7 +387,7 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_nc(
     constexpr int PER = TR * CPR / kApplyThreads;  // chunks per thread per round
     static_assert(TR * CPR % kApplyThreads == 0, "staging split");
     __shared__ __attribute__((aligned(16))) float xs[2][TR * LDX];
-    __shared__ float xch[2][NRG][NCB][32][3];  // per-row partial sums of the blocks
+    __shared__ __attribute__((aligned(16))) float vz[KIND == 0 ? D : 4];  // z
 
     const int sub = (KIND == 2) ? (int)(blockIdx.x & 1) : 0;
     const int64_t b = (KIND == 2) ? (blockIdx.x >> 1) : blockIdx.x;
@@ -388,7 +402,6 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_nc(
     const bool colread = (KIND == 0) || (KIND == 2 && sub == 1);
 
     const T *xh = ((KIND == 2 && sub == 1) ? X2 : X) + hoff;
-    const T *qh = (KIND == 1) ? X2 + hoff : nullptr;
     T *oh = ((KIND == 2 && sub == 1) ? Out2 : Out) + hoff;
 
     // staging: thread's chunk p of a round covers row (tid + p*NT) / CPR,
@@ -439,83 +452,94 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_nc(
                 am[kb][r] = v[r];
         }
     }
-    // epilogue vector at the lane's output columns 32*cb + 8*q + 4*h + (0..3)
+    // epilogue vector at the lane's output columns 32*cb + 8*q + 4*h + (0..3):
+    // u (forward), -r (dK) or t (dV)
     f4 ev[4];
     {
         const float *vec = st + D * D + ((KIND == 0 || (KIND == 2 && sub == 1)) ? D : 0);
+        const float sgn = (KIND == 2 && sub == 0) ? -1.f : 1.f;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            ev[q] = *reinterpret_cast<const f4 *>(vec + 32 * cb + 8 * q + 4 * h);
+            ev[q] = sgn * *reinterpret_cast<const f4 *>(vec + 32 * cb + 8 * q + 4 * h);
     }
-    // second vector at the same columns: z (forward, for q.z) or u (dQ, for dO.u)
-    f4 ew[4];
-    if constexpr (KIND == 0 || KIND == 1) {
-        const float *vec = st + D * D + (KIND == 0 ? 0 : D);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            ew[q] = *reinterpret_cast<const f4 *>(vec + 32 * cb + 8 * q + 4 * h);
-    }
+    if constexpr (KIND == 0)
+        for (int e = tid; e < D; e += kApplyThreads)
+            vz[e] = st[D * D + e];
     stage_round(0, beg);
+    drain_loads();
     if (nrounds > 1)
         fetch_round(beg + TR);
     __syncthreads();
 
+    // the previous round's output rows, stored during the next round
+    f4 pend[4];
+    int64_t prow = 0;
+    bool pok = false;
+    auto store_pending = [&](int q) {
+        if (pok)
+            io::store4(oh + prow * D + 32 * cb + 8 * q + 4 * h, pend[q]);
+    };
+
     for (int64_t round = 0; round < nrounds; ++round) {
         const int buf = (int)(round & 1);
-        const int64_t t0 = beg + round * TR + 32 * rg;  // this row group's tile
         const float *xt = &xs[buf][(32 * rg + j) * LDX + 4 * h];
-        f4 qv[4];
-        if constexpr (KIND == 1) {
-            int64_t r = t0 + j;
-            r = r < end ? r : end - 1;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                qv[q] = io::load4(qh + r * D + 32 * cb + 8 * q + 4 * h);
-        }
-
         f16v acc = zero16();
-        // LDS operand one k-block ahead of the MFMAs; the scheduling barrier
+        float qz = 0.f;
+        // LDS operands one k-block ahead of the MFMAs; the scheduling barrier
         // per k-block stops the compiler from hoisting every read of the tile
-        f4 xn = *reinterpret_cast<const f4 *>(xt);
+        f4 xn = *reinterpret_cast<const f4 *>(xt), zn;
+        // z is the same every round: an opaque offset keeps its reads inside
+        // the loop (hoisted, they would hold D/2 registers for the whole loop)
+        int zo = 4 * h;
+        asm volatile("" : "+v"(zo));
+        if constexpr (KIND == 0)
+            zn = *reinterpret_cast<const f4 *>(&vz[zo]);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const f4 x = xn;
-            if (kb + 1 < KB)
+            f4 z;
+            if constexpr (KIND == 0)
+                z = zn;
+            if (kb + 1 < KB) {
                 xn = *reinterpret_cast<const f4 *>(xt + (kb + 1) * 8);
+                if constexpr (KIND == 0)
+                    zn = *reinterpret_cast<const f4 *>(&vz[zo + (kb + 1) * 8]);
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 acc = mma32(am[kb][r], x[r], acc);
+            if constexpr (KIND == 0) {
+                qz += dot4(x, z);
+                // keep the sum here: sunk below the loop, it would keep every
+                // k-block's operands alive until the end of the round
+                asm volatile("" : "+v"(qz));
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (kb == q * (KB / 4))
+                    store_pending(q);
             __builtin_amdgcn_sched_barrier(0);
         }
 
-        const int64_t row = t0 + j;
-        const bool ok = row < end;
-        float c = 0.f, inv = 0.f;
-        if constexpr (KIND == 0 || KIND == 1) {
-            // partial row sums over this block's 32 columns, exchanged below:
-            // forward: q.z;  dQ: dO.u, q.z, q.(S dO)
-            const float *xr = &xs[buf][(32 * rg + j) * LDX + 32 * cb + 4 * h];
-            float p0 = 0.f, p1 = 0.f, p2 = 0.f;
+        const int64_t row = beg + round * TR + 32 * rg + j;
+        if constexpr (KIND == 0) {
+            qz += __shfl_xor(qz, 32, 64);
+            const float den = (float)N + qz;
+            const float inv = 1.f / den;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                p0 += dot4(*reinterpret_cast<const f4 *>(xr + 8 * q), ew[q]);
-            if constexpr (KIND == 1) {
+                pend[q] = f4{(acc[4 * q] + ev[q][0]) * inv, (acc[4 * q + 1] + ev[q][1]) * inv,
+                             (acc[4 * q + 2] + ev[q][2]) * inv, (acc[4 * q + 3] + ev[q][3]) * inv};
+            if (den_out != nullptr && row < end && h == 0 && cb == 0)
+                den_out[bh * N + row] = den;
+        } else {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    p1 += dot4(qv[q], ev[q]);
-                    p2 += qv[q][0] * acc[4 * q] + qv[q][1] * acc[4 * q + 1] +
-                          qv[q][2] * acc[4 * q + 2] + qv[q][3] * acc[4 * q + 3];
-                }
-            }
-            p0 += __shfl_xor(p0, 32, 64);
-            p1 += __shfl_xor(p1, 32, 64);
-            p2 += __shfl_xor(p2, 32, 64);
-            if (h == 0) {
-                xch[buf][rg][cb][j][0] = p0;
-                xch[buf][rg][cb][j][1] = p1;
-                xch[buf][rg][cb][j][2] = p2;
-            }
+            for (int q = 0; q < 4; ++q)
+                pend[q] = f4{acc[4 * q] + ev[q][0], acc[4 * q + 1] + ev[q][1],
+                             acc[4 * q + 2] + ev[q][2], acc[4 * q + 3] + ev[q][3]};
         }
+        prow = row;
+        pok = row < end;
         // stage the next round (its buffer was last read before the previous
         // barrier) and fetch the one after
         if (round + 1 < nrounds) {
@@ -524,52 +548,300 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_nc(
                 fetch_round(beg + (round + 2) * TR);
         }
         __syncthreads();
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        store_pending(q);
+}
 
-        if constexpr (KIND == 0) {
-            float qz = 0.f;
+// ============================================================ dQ + gradient record
+// One pass over a segment's rows of Q and dO that produces dQ (as KIND 1 of
+// k_apply_nc) and the segment's gradient record [dS | r | t] (as
+// k_reduce_nc<GRAD = true>) without a second read of Q and dO:
+//   a_i = g_i / den_i,  den_i = N + q_i.z,  y_i = S a_i,
+//   c_i = (a_i.u + q_i.y_i) / den_i,  dq_i = y_i - c_i z,
+//   dS = sum_i q_i a_i^T,  r = sum_i c_i q_i,  t = sum_i a_i.
+// The workgroup has two roles of four waves each, so that no wave holds both
+// a D x D slice of S (the dQ product) and one of dS (the reduction):
+//   role 0 (waves 0-3): the dQ rows, exactly as k_apply_nc KIND 1;
+//   role 1 (waves 4-7): dS[:, 32*cb ..] over the round's rows, with
+//                       a_i formed from its own den_i; r needs c_i, which
+//                       role 0 hands over through LDS one round later.
+// Both roles stage the rows (Q and dO, fp32, double-buffered) together and
+// meet at one barrier per round.
+template <class ST, int D>
+__global__ __launch_bounds__(512) void k_bwd_q_nc(
+    const typename ST::T *__restrict__ G, const typename ST::T *__restrict__ Q,
+    typename ST::T *__restrict__ dQ, float *__restrict__ part_out,
+    const float *__restrict__ rec, int64_t N, int64_t seg_len, int nseg)
+{
+    typedef typename ST::T T;
+    typedef IO<ST> io;
+    static_assert(D >= 32, "32-column output blocks");
+    constexpr int NT = 512;
+    constexpr int KB = D / 8;
+    constexpr int NCB = D / 32;
+    constexpr int NRG = 4 / NCB;
+    constexpr int TR = 32 * NRG;
+    constexpr int LDX = D + 4;
+    constexpr int VEC = 16 / sizeof(T);
+    constexpr int CPR = D / VEC;
+    constexpr int PER = TR * CPR / NT;
+    static_assert(PER >= 1 && TR * CPR % NT == 0, "staging split");
+    __shared__ __attribute__((aligned(16))) float xs[2][TR * LDX];  // dO rows
+    __shared__ __attribute__((aligned(16))) float qs[2][TR * LDX];  // Q rows
+    __shared__ __attribute__((aligned(16))) float vl[2 * D];        // z | u
+    __shared__ float xch[2][NRG][NCB][32][2];  // dO.u and q.(S dO) partials
+    __shared__ float cx[2][NRG][32];           // c_i of the round's rows
+
+    const int64_t bh = blockIdx.x / nseg;
+    const int seg = (int)(blockIdx.x % nseg);
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, j = lane & 31, h = lane >> 5;
+    const int role = w >> 2, cb = (w & 3) % NCB, rg = (w & 3) / NCB;
+    const int64_t beg = (int64_t)seg * seg_len;
+    const int64_t end = (beg + seg_len < N) ? beg + seg_len : N;
+    const int64_t hoff = bh * N * D;
+    const float *st = rec + bh * (int64_t)(D * D + 2 * D);
+    const T *gh = G + hoff, *qh = Q + hoff;
+    T *oh = dQ + hoff;
+
+    uint4 sg[PER], sq[PER];
+    auto fetch_round = [&](int64_t r0) {
 #pragma unroll
-            for (int c2 = 0; c2 < NCB; ++c2)
-                qz += xch[buf][rg][c2][j][0];
-            const float den = (float)N + qz;
-            inv = 1.f / den;
+        for (int p = 0; p < PER; ++p) {
+            const int c = tid + p * NT;
+            int64_t row = r0 + c / CPR;
+            row = row < end ? row : end - 1;  // valid address; zeroed when staged
+            sg[p] = *reinterpret_cast<const uint4 *>(gh + row * D + VEC * (c % CPR));
+            sq[p] = *reinterpret_cast<const uint4 *>(qh + row * D + VEC * (c % CPR));
+        }
+    };
+    auto stage_one = [&](float *lds, const uint4 &src, int c, bool ok) {
+        float v[VEC];
+        if constexpr (VEC == 4)
+            StF32::widen(src, v);
+        else
+            StBF16::widen(src, v);
+        float *dst = lds + (c / CPR) * LDX + VEC * (c % CPR);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f4 o = {(acc[4 * q] + ev[q][0]) * inv, (acc[4 * q + 1] + ev[q][1]) * inv,
-                              (acc[4 * q + 2] + ev[q][2]) * inv, (acc[4 * q + 3] + ev[q][3]) * inv};
-                if (ok)
-                    io::store4(oh + row * D + 32 * cb + 8 * q + 4 * h, o);
+        for (int x = 0; x < VEC; x += 4)
+            *reinterpret_cast<f4 *>(dst + x) =
+                ok ? f4{v[x], v[x + 1], v[x + 2], v[x + 3]} : f4{0.f, 0.f, 0.f, 0.f};
+    };
+    auto stage_round = [&](int buf, int64_t r0) {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int c = tid + p * NT;
+            const bool ok = r0 + c / CPR < end;
+            stage_one(xs[buf], sg[p], c, ok);
+            stage_one(qs[buf], sq[p], c, ok);
+        }
+    };
+    // den of row j of this wave's tile in full (lane half h sums half the
+    // columns): the same value in both halves
+    auto inv_den = [&](int buf) {
+        const float *qr = &qs[buf][(32 * rg + j) * LDX + (D / 2) * h];
+        float qz = 0.f;
+#pragma unroll
+        for (int x = 0; x < D / 2; x += 4)
+            qz += dot4(*reinterpret_cast<const f4 *>(qr + x),
+                       *reinterpret_cast<const f4 *>(&vl[(D / 2) * h + x]));
+        qz += __shfl_xor(qz, 32, 64);
+        return 1.f / ((float)N + qz);
+    };
+
+    const int64_t nrounds = (end - beg + TR - 1) / TR;
+    fetch_round(beg);
+    for (int e = tid; e < 2 * D; e += NT)
+        vl[e] = st[D * D + e];
+    // role 0's block of S: am[kb][r] = S[32*cb + j][kb*8 + 4*h + r] (loaded
+    // by every wave so that the registers are set on every path; dead in
+    // role 1)
+    float am[KB][4];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        const f4 v = *reinterpret_cast<const f4 *>(st + (32 * cb + j) * D + kb * 8 + 4 * h);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            am[kb][r] = v[r];
+    }
+    stage_round(0, beg);
+    drain_loads();
+    if (nrounds > 1)
+        fetch_round(beg + TR);
+    __syncthreads();
+
+    f16v gacc[NCB];
+    float racc = 0.f, tacc = 0.f;
+    float qcur[16], qprev[16];
+    if (role == 0) {
+        for (int64_t round = 0; round < nrounds; ++round) {
+            const int buf = (int)(round & 1);
+            const int64_t row = beg + round * TR + 32 * rg + j;
+            const float *xt = &xs[buf][(32 * rg + j) * LDX + 4 * h];
+            f16v acc = zero16();
+            f4 xn = *reinterpret_cast<const f4 *>(xt);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const f4 x = xn;
+                if (kb + 1 < KB)
+                    xn = *reinterpret_cast<const f4 *>(xt + (kb + 1) * 8);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc = mma32(am[kb][r], x[r], acc);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            if (den_out != nullptr && ok && h == 0 && cb == 0)
-                den_out[bh * N + row] = den;
-        } else if constexpr (KIND == 1) {
-            float rz = 0.f, qz = 0.f, qy = 0.f;
+            const float inv = inv_den(buf);
+            // partial dO.u and q.(S dO) over this block's columns
+            {
+                const float *xr = &xs[buf][(32 * rg + j) * LDX + 32 * cb + 4 * h];
+                const float *qr = &qs[buf][(32 * rg + j) * LDX + 32 * cb + 4 * h];
+                float p0 = 0.f, p2 = 0.f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f4 qv = *reinterpret_cast<const f4 *>(qr + 8 * q);
+                    p0 += dot4(*reinterpret_cast<const f4 *>(xr + 8 * q),
+                               *reinterpret_cast<const f4 *>(&vl[D + 32 * cb + 8 * q + 4 * h]));
+                    p2 += qv[0] * acc[4 * q] + qv[1] * acc[4 * q + 1] + qv[2] * acc[4 * q + 2] +
+                          qv[3] * acc[4 * q + 3];
+                }
+                p0 += __shfl_xor(p0, 32, 64);
+                p2 += __shfl_xor(p2, 32, 64);
+                if (h == 0) {
+                    xch[buf][rg][cb][j][0] = p0;
+                    xch[buf][rg][cb][j][1] = p2;
+                }
+            }
+            if (round + 1 < nrounds) {
+                stage_round(buf ^ 1, beg + (round + 1) * TR);
+                if (round + 2 < nrounds)
+                    fetch_round(beg + (round + 2) * TR);
+            }
+            __syncthreads();
+            float rz = 0.f, qy = 0.f;
 #pragma unroll
             for (int c2 = 0; c2 < NCB; ++c2) {
                 rz += xch[buf][rg][c2][j][0];
-                qz += xch[buf][rg][c2][j][1];
-                qy += xch[buf][rg][c2][j][2];
+                qy += xch[buf][rg][c2][j][1];
             }
-            inv = 1.f / ((float)N + qz);
-            c = (rz + qy) * inv * inv;  // (a.u + q.y_true) / den
+            const float c = (rz + qy) * inv * inv;  // (a.u + q.y_true) / den
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const f4 o = {acc[4 * q] * inv - c * ev[q][0], acc[4 * q + 1] * inv - c * ev[q][1],
-                              acc[4 * q + 2] * inv - c * ev[q][2],
-                              acc[4 * q + 3] * inv - c * ev[q][3]};
-                if (ok)
+                const f4 z = *reinterpret_cast<const f4 *>(&vl[32 * cb + 8 * q + 4 * h]);
+                const f4 o = {acc[4 * q] * inv - c * z[0], acc[4 * q + 1] * inv - c * z[1],
+                              acc[4 * q + 2] * inv - c * z[2], acc[4 * q + 3] * inv - c * z[3]};
+                if (row < end)
                     io::store4(oh + row * D + 32 * cb + 8 * q + 4 * h, o);
             }
-            if (ok && h == 0 && cb == 0)
-                reinterpret_cast<float2 *>(cbuf)[bh * N + row] = float2{c, inv};
-        } else {
-            const float sgn = (sub == 0) ? -1.f : 1.f;
+            if (cb == 0 && h == 0)
+                cx[buf][rg][j] = c;
+        }
+    } else {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f4 o = {acc[4 * q] + sgn * ev[q][0], acc[4 * q + 1] + sgn * ev[q][1],
-                              acc[4 * q + 2] + sgn * ev[q][2], acc[4 * q + 3] + sgn * ev[q][3]};
-                if (ok)
-                    io::store4(oh + row * D + 32 * cb + 8 * q + 4 * h, o);
+        for (int t = 0; t < NCB; ++t)
+            gacc[t] = zero16();
+        for (int64_t round = 0; round < nrounds; ++round) {
+            const int buf = (int)(round & 1);
+            const float inv = inv_den(buf);
+            // dS[:, block cb] += Q^T A over the tile's rows (k = row; rows
+            // 2kk + h per MFMA step), operands one step ahead
+            const float *qt = &qs[buf][(32 * rg + h) * LDX + j];
+            const float *gt = &xs[buf][(32 * rg + h) * LDX + 32 * cb + j];
+            float an[NCB], gn = gt[0];
+#pragma unroll
+            for (int t = 0; t < NCB; ++t)
+                an[t] = qt[32 * t];
+#pragma unroll
+            for (int kk = 0; kk < 16; ++kk) {
+                float a[NCB];
+#pragma unroll
+                for (int t = 0; t < NCB; ++t)
+                    a[t] = an[t];
+                const float g = gn;
+                if (kk + 1 < 16) {
+                    gn = gt[(2 * kk + 2) * LDX];
+#pragma unroll
+                    for (int t = 0; t < NCB; ++t)
+                        an[t] = qt[(2 * kk + 2) * LDX + 32 * t];
+                }
+                const float i0 = __int_as_float(
+                    __builtin_amdgcn_readlane(__float_as_int(inv), 2 * kk));
+                const float i1 = __int_as_float(
+                    __builtin_amdgcn_readlane(__float_as_int(inv), 2 * kk + 1));
+                const float bv = g * (h ? i1 : i0);
+                tacc += bv;
+#pragma unroll
+                for (int t = 0; t < NCB; ++t)
+                    gacc[t] = mma32(a[t], bv, gacc[t]);
+                qcur[kk] = qt[2 * kk * LDX + 32 * cb];
+                __builtin_amdgcn_sched_barrier(0);
             }
+            if (round + 1 < nrounds) {
+                stage_round(buf ^ 1, beg + (round + 1) * TR);
+                if (round + 2 < nrounds)
+                    fetch_round(beg + (round + 2) * TR);
+            }
+            __syncthreads();
+            // r += c_i q_i over the previous round's rows (c_i arrived in LDS
+            // from role 0 before this barrier)
+            if (round > 0) {
+#pragma unroll
+                for (int kk = 0; kk < 16; ++kk)
+                    racc += cx[buf ^ 1][rg][2 * kk + h] * qprev[kk];
+            }
+#pragma unroll
+            for (int kk = 0; kk < 16; ++kk)
+                qprev[kk] = qcur[kk];
+        }
+    }
+    __syncthreads();  // the last round's c_i is in LDS; staging buffers are free
+
+    constexpr int PW = NCB * 16 * 64 + 64;  // floats per handing wave
+    static_assert((NRG - 1) * NCB * PW <= 2 * TR * LDX, "merge space");
+    float *red = &xs[0][0];
+    if (role == 1) {
+        if (nrounds > 0) {
+            const int lb = (int)((nrounds - 1) & 1);
+#pragma unroll
+            for (int kk = 0; kk < 16; ++kk)
+                racc += cx[lb][rg][2 * kk + h] * qprev[kk];
+        }
+        racc += __shfl_xor(racc, 32, 64);
+        tacc += __shfl_xor(tacc, 32, 64);
+        if (NRG > 1 && rg > 0) {
+            float *dst = red + ((rg - 1) * NCB + cb) * PW;
+#pragma unroll
+            for (int t = 0; t < NCB; ++t)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    dst[(t * 16 + i) * 64 + lane] = gacc[t][i];
+            if (h == 0) {
+                dst[NCB * 16 * 64 + j] = racc;
+                dst[NCB * 16 * 64 + 32 + j] = tacc;
+            }
+        }
+    }
+    __syncthreads();
+    if (role == 1 && rg == 0) {
+        for (int o = 1; o < NRG; ++o) {
+            const float *src = red + ((o - 1) * NCB + cb) * PW;
+#pragma unroll
+            for (int t = 0; t < NCB; ++t)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    gacc[t][i] += src[(t * 16 + i) * 64 + lane];
+            racc += src[NCB * 16 * 64 + j];
+            tacc += src[NCB * 16 * 64 + 32 + j];
+        }
+        float *out = part_out + (bh * nseg + seg) * (int64_t)(D * D + 2 * D);
+#pragma unroll
+        for (int t = 0; t < NCB; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                out[(32 * t + 8 * (i / 4) + 4 * h + (i % 4)) * D + 32 * cb + j] = gacc[t][i];
+        if (h == 0) {
+            out[D * D + 32 * cb + j] = racc;
+            out[D * D + D + 32 * cb + j] = tacc;
         }
     }
 }
