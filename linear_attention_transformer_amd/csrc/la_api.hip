@@ -178,15 +178,13 @@ int state_of_kv(const void *K, const void *V, float *part, float *tot, const Pla
     int rc = LA_OK;
     bool done = false;
     if constexpr (nc_path<D>()) {
-        if (!p.causal) {
-            rc = traced(t, s, "state_local", [&] {
-                nc::k_reduce_nc<ST, D, false><<<dim3((unsigned)(p.nseg * p.BH)),
-                                                dim3(nc::kReduceThreads), 0, s>>>(
-                    static_cast<const T *>(K), static_cast<const T *>(V), nullptr, part, p.N,
-                    p.seg_len, (int)p.nseg);
-            });
-            done = true;
-        }
+        rc = traced(t, s, "state_local", [&] {
+            nc::k_reduce_nc<ST, D, false><<<dim3((unsigned)(p.nseg * p.BH)),
+                                            dim3(nc::kReduceThreads), 0, s>>>(
+                static_cast<const T *>(K), static_cast<const T *>(V), nullptr, part, p.N,
+                p.seg_len, (int)p.nseg);
+        });
+        done = true;
     }
     if (!done) {
         const dim3 grid((unsigned)(p.nseg * p.BH * C::CS));
@@ -227,6 +225,12 @@ int run_forward(const void *Q, const void *K, const void *V, void *O, float *den
                     static_cast<const T *>(Q), nullptr, static_cast<T *>(O), nullptr, den_out,
                     rec, p.N, p.seg_len, (int)p.nseg);
             });
+        return traced(t, s, "forward", [&] {
+            nc::k_fwd_causal<ST, D><<<dim3((unsigned)(p.nseg * p.BH)), dim3(64 * (D / 32)), 0,
+                                      s>>>(
+                static_cast<const T *>(Q), static_cast<const T *>(K), static_cast<const T *>(V),
+                static_cast<T *>(O), den_out, rec, p.N, p.seg_len, (int)p.nseg);
+        });
     }
     const dim3 grid((unsigned)(p.nseg * p.BH * C::CS));
     return traced(t, s, "forward", [&] {
