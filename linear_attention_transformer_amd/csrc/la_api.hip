@@ -10,6 +10,7 @@
 #include "la.h"
 #include "la_kernels.hpp"
 #include "la_kernels_nc.hpp"
+#include "la_kernels_causal.hpp"
 
 namespace {
 
@@ -226,7 +227,7 @@ int run_forward(const void *Q, const void *K, const void *V, void *O, float *den
                     rec, p.N, p.seg_len, (int)p.nseg);
             });
         return traced(t, s, "forward", [&] {
-            nc::k_fwd_causal<ST, D><<<dim3((unsigned)(p.nseg * p.BH)), dim3(64 * (D / 32)), 0,
+            cz::k_fwd_causal<ST, D><<<dim3((unsigned)(p.nseg * p.BH)), dim3(cz::threads<D>()), 0,
                                       s>>>(
                 static_cast<const T *>(Q), static_cast<const T *>(K), static_cast<const T *>(V),
                 static_cast<T *>(O), den_out, rec, p.N, p.seg_len, (int)p.nseg);
@@ -270,6 +271,29 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
     float *gpart = ws + l.gpart, *cbuf = ws + l.cbuf;
     const T *q = static_cast<const T *>(Q), *k = static_cast<const T *>(K),
             *v = static_cast<const T *>(V), *g = static_cast<const T *>(G);
+    if constexpr (CAUSAL && nc_path<D>()) {
+        const dim3 g1((unsigned)(p.nseg * p.BH)), nt(cz::threads<D>());
+        // dQ and (c_i, 1/den_i), chunk by chunk from the saved prefix records
+        rc = traced(t, s, "bwd_q", [&] {
+            cz::k_bwd_q_causal<ST, D><<<g1, nt, 0, s>>>(q, k, v, g, static_cast<T *>(dQ), cbuf,
+                                                        fstate, p.N, p.seg_len, (int)p.nseg);
+        });
+        if (rc != LA_OK)
+            return rc;
+        rc = traced(t, s, "grad_state_local", [&] {
+            nc::k_reduce_nc<ST, D, true><<<g1, dim3(nc::kReduceThreads), 0, s>>>(
+                q, g, cbuf, gpart, p.N, p.seg_len, (int)p.nseg);
+        });
+        if (rc != LA_OK)
+            return rc;
+        if ((rc = scan(gpart, nullptr, p, 2, s, t)) != LA_OK)  // exclusive suffix
+            return rc;
+        return traced(t, s, "bwd_kv", [&] {
+            cz::k_bwd_kv_causal<ST, D><<<dim3((unsigned)(2 * p.nseg * p.BH)), nt, 0, s>>>(
+                q, k, v, g, static_cast<T *>(dK), static_cast<T *>(dV), cbuf, gpart, p.N,
+                p.seg_len, (int)p.nseg);
+        });
+    }
     if constexpr (!CAUSAL && nc_path<D>()) {
         const dim3 g1((unsigned)(p.nseg * p.BH));
         // dQ and the segment's gradient record in one pass

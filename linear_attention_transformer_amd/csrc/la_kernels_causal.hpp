@@ -1,0 +1,696 @@
+// la_kernels_causal.hpp -- causal linear attention for 32 <= D <= 128 on gfx950.
+//
+// Same method as la_kernels.hpp, causal mask j <= i (pages about
+// "Transformer Based Linear Attention with Optimized GPU Kernel
+// Implementation": sciencestack.ai TL;DR and Figure 1 caption; the
+// token-by-token state growth of the cloud.baidu.com article, section 2).
+// Each head's sequence is cut into segments (one workgroup each) and each
+// segment into chunks of C = 32 rows, processed in order.  A segment starts
+// from the record of everything before it (forward, dQ: the exclusive prefix
+// of the per-segment state records) or after it (dK, dV: the exclusive
+// suffix of the gradient records).  For every chunk:
+//   - the running state is applied to the chunk's rows (an MFMA product
+//     over D, as in the non-causal kernels);
+//   - the masked in-chunk block is formed densely: each wave contributes the
+//     share of a C x C product (Q K^T or dO V^T) over its 32 columns of D,
+//     the shares meet in LDS, and the block is applied with one more MFMA
+//     over the chunk's rows;
+//   - the running state is updated by the chunk (an MFMA over its rows).
+//
+// Wave cb of a workgroup owns output columns 32 cb .. 32 cb + 31 and the
+// matching D x 32 slice of the running state, held as four (D / 32) MFMA
+// accumulators st[t][i] <-> state[32 t + 8 (i / 4) + 4 h + i % 4][32 cb + j]
+// (or its transpose).  With v_mfma_f32_32x32x2_f32 (lane l = 32 h + j
+// supplies A[m = j][k = h] and B[k = h][n = j]; accumulator element i sits
+// at row 8 (i / 4) + 4 h + i % 4, column j) that is exactly the A operand
+// of the apply at k-block kb, step r: st[kb / 4][4 (kb % 4) + r].  So the
+// state is applied and updated in place without leaving the registers.
+//
+// Rows are staged in LDS as fp32 from a register prefetch of the next chunk.
+// Three barriers per chunk: after the shares are written (B1), after the
+// last read of the chunk's rows (B2) and after the next chunk is staged
+// (B3).  Tensors read only before B1 are restaged right after it, so at most
+// two tensors' prefetch registers are live at a time.
+#pragma once
+
+#include "la_kernels_nc.hpp"
+
+namespace la {
+namespace cz {
+
+using nc::dot4;
+using nc::drain_loads;
+using nc::f16v;
+using nc::IO;
+using nc::mma32;
+using nc::zero16;
+
+constexpr int kC = 32;  // rows per chunk
+
+template <int D>
+constexpr int threads() { return 64 * (D / 32); }
+
+// Rows r0 .. r0 + kC - 1 of one head's [N, D] tensor: fetched into registers
+// by the NT threads of the workgroup (16-byte loads; rows clamped below
+// `end` so that every address is valid), then written to LDS as fp32 with
+// the rows at or past `end` zeroed.
+template <class ST, int D, int NT>
+struct Rows {
+    typedef typename ST::T T;
+    static constexpr int VEC = 16 / sizeof(T);
+    static constexpr int CPR = D / VEC;
+    static constexpr int PER = kC * CPR / NT;
+    static constexpr int LDX = D + 4;
+    static_assert(PER >= 1 && kC * CPR % NT == 0, "staging split");
+    uint4 r[PER];
+
+    __device__ __forceinline__ void fetch(const T *src, int64_t r0, int64_t end, int tid)
+    {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int c = tid + p * NT;
+            int64_t row = r0 + c / CPR;
+            row = row < end ? row : end - 1;
+            r[p] = *reinterpret_cast<const uint4 *>(src + row * D + VEC * (c % CPR));
+        }
+    }
+    __device__ __forceinline__ void stage(float *lds, int64_t r0, int64_t end, int tid) const
+    {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int c = tid + p * NT;
+            const bool ok = r0 + c / CPR < end;
+            float v[VEC];
+            if constexpr (VEC == 4)
+                StF32::widen(r[p], v);
+            else
+                StBF16::widen(r[p], v);
+            float *dst = lds + (c / CPR) * LDX + VEC * (c % CPR);
+#pragma unroll
+            for (int x = 0; x < VEC; x += 4)
+                *reinterpret_cast<f4 *>(dst + x) =
+                    ok ? f4{v[x], v[x + 1], v[x + 2], v[x + 3]} : f4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+};
+
+// this wave's share of X_c Y_c^T over columns 32 cb .. 32 cb + 31 of D,
+// written to sh[i * WP + jj] (i: row of X, jj: row of Y)
+template <int D>
+__device__ __forceinline__ void share_xyT(const float *xs, const float *ys, float *sh, int cb,
+                                          int j, int h)
+{
+    constexpr int LDX = D + 4, WP = kC + 1;
+    f16v a = zero16();
+    const float *xa = xs + j * LDX + 32 * cb + 4 * h;
+    const float *ya = ys + j * LDX + 32 * cb + 4 * h;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        const f4 x = *reinterpret_cast<const f4 *>(xa + 8 * kb);
+        const f4 y = *reinterpret_cast<const f4 *>(ya + 8 * kb);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            a = mma32(x[r], y[r], a);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+        sh[(8 * (e / 4) + 4 * h + (e % 4)) * WP + j] = a[e];
+}
+
+// ============================================================ forward
+// o_i = (u + S^T q_i + sum_{j in c, j <= i} (1 + q_i.k_j) v_j) / den_i,
+// den_i = t0 + q_i.z + sum_{j in c, j <= i} (1 + q_i.k_j), with (S, z, u)
+// over the rows before the chunk (t0 = its first row); then
+// (S, z, u) += (K_c^T V_c, sum k, sum v).  st[t] = S[32t.., 32cb..].
+template <class ST, int D>
+__global__ __launch_bounds__(threads<D>()) void k_fwd_causal(
+    const typename ST::T *__restrict__ Q, const typename ST::T *__restrict__ K,
+    const typename ST::T *__restrict__ V, typename ST::T *__restrict__ O,
+    float *__restrict__ den_out, const float *__restrict__ rec, int64_t N, int64_t seg_len,
+    int nseg)
+{
+    typedef typename ST::T T;
+    typedef IO<ST> io;
+    static_assert(D >= 32 && D <= 128, "32-column blocks, state in registers");
+    constexpr int NCB = D / 32, NT = threads<D>(), KB = D / 8, LDX = D + 4, WP = kC + 1;
+    __shared__ __attribute__((aligned(16))) float qs[kC * LDX];
+    __shared__ __attribute__((aligned(16))) float ks[kC * LDX];
+    __shared__ __attribute__((aligned(16))) float vs[kC * LDX];
+    __shared__ float wx[NCB][kC * WP];
+    __shared__ __attribute__((aligned(16))) float vz[D];
+    __shared__ __attribute__((aligned(16))) float vu[D];
+
+    const int64_t bh = blockIdx.x / nseg;
+    const int seg = (int)(blockIdx.x % nseg);
+    const int tid = threadIdx.x, cb = tid >> 6, lane = tid & 63, j = lane & 31, h = lane >> 5;
+    const int64_t beg = (int64_t)seg * seg_len;
+    const int64_t end = (beg + seg_len < N) ? beg + seg_len : N;
+    const int64_t hoff = bh * N * D;
+    const float *st = rec + (bh * nseg + seg) * (int64_t)(D * D + 2 * D);
+    const T *qh = Q + hoff, *kh = K + hoff, *vh = V + hoff;
+    T *oh = O + hoff;
+
+    Rows<ST, D, NT> rq, rk, rv;
+    const int64_t nrounds = (end - beg + kC - 1) / kC;
+    rq.fetch(qh, beg, end, tid);
+    rk.fetch(kh, beg, end, tid);
+    rv.fetch(vh, beg, end, tid);
+    f16v sacc[NCB];
+#pragma unroll
+    for (int t = 0; t < NCB; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            sacc[t][i] = st[(32 * t + 8 * (i / 4) + 4 * h + (i % 4)) * D + 32 * cb + j];
+    for (int e = tid; e < D; e += NT) {
+        vz[e] = st[D * D + e];
+        vu[e] = st[D * D + D + e];
+    }
+    rq.stage(qs, beg, end, tid);
+    rk.stage(ks, beg, end, tid);
+    rv.stage(vs, beg, end, tid);
+    drain_loads();
+    if (nrounds > 1)
+        rq.fetch(qh, beg + kC, end, tid);
+    __syncthreads();
+
+    f4 pend[4];
+    int64_t prow = 0;
+    bool pok = false;
+    auto store_pending = [&](int q) {
+        if (pok)
+            io::store4(oh + prow * D + 32 * cb + 8 * q + 4 * h, pend[q]);
+    };
+
+    for (int64_t round = 0; round < nrounds; ++round) {
+        const int64_t t0 = beg + round * kC;
+        const bool more = round + 1 < nrounds;
+        // (1) the prefix state applied to the chunk's queries, and q.z
+        f16v acc = zero16();
+        float qz = 0.f;
+        {
+            const float *xt = &qs[j * LDX + 4 * h];
+            int zo = 4 * h;
+            asm volatile("" : "+v"(zo));  // z changes per chunk: keep its reads here
+            f4 xn = *reinterpret_cast<const f4 *>(xt);
+            f4 zn = *reinterpret_cast<const f4 *>(&vz[zo]);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const f4 x = xn, z = zn;
+                if (kb + 1 < KB) {
+                    xn = *reinterpret_cast<const f4 *>(xt + (kb + 1) * 8);
+                    zn = *reinterpret_cast<const f4 *>(&vz[zo + (kb + 1) * 8]);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc = mma32(sacc[kb / 4][4 * (kb % 4) + r], x[r], acc);
+                qz += dot4(x, z);
+                asm volatile("" : "+v"(qz));  // accumulate here, not after the loop
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (kb == q * (KB / 4))
+                        store_pending(q);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // (2) this wave's share of Q_c K_c^T
+        share_xyT<D>(qs, ks, wx[cb], cb, j, h);
+        __syncthreads();  // B1
+        if (more) {
+            rq.stage(qs, t0 + kC, end, tid);
+            rk.fetch(kh, t0 + kC, end, tid);
+            rv.fetch(vh, t0 + kC, end, tid);
+        }
+        // (3) in-chunk term (key rows jr = 2kk + h of the MFMA step) and the
+        // state update
+        float rs = 0.f, zc = 0.f, uc = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < kC / 2; ++kk) {
+            const int jr = 2 * kk + h;
+            const float vb = vs[jr * LDX + 32 * cb + j];
+            float wsum = 0.f;
+#pragma unroll
+            for (int p = 0; p < NCB; ++p)
+                wsum += wx[p][j * WP + jr];
+            const float wm = (jr <= j) ? 1.f + wsum : 0.f;
+            rs += wm;
+            acc = mma32(vb, wm, acc);
+#pragma unroll
+            for (int t = 0; t < NCB; ++t) {
+                const float kt = ks[jr * LDX + 32 * t + j];
+                sacc[t] = mma32(kt, vb, sacc[t]);
+                if (t == cb)
+                    zc += kt;
+            }
+            uc += vb;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        rs += __shfl_xor(rs, 32, 64);
+        zc += __shfl_xor(zc, 32, 64);
+        uc += __shfl_xor(uc, 32, 64);
+        qz += __shfl_xor(qz, 32, 64);
+        // (4) normalised rows of the chunk, stored during the next product
+        const float den = (float)t0 + qz + rs;
+        const float inv = 1.f / den;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f4 u = *reinterpret_cast<const f4 *>(&vu[32 * cb + 8 * q + 4 * h]);
+            pend[q] = f4{(acc[4 * q] + u[0]) * inv, (acc[4 * q + 1] + u[1]) * inv,
+                         (acc[4 * q + 2] + u[2]) * inv, (acc[4 * q + 3] + u[3]) * inv};
+        }
+        prow = t0 + j;
+        pok = prow < end;
+        if (den_out != nullptr && pok && h == 0 && cb == 0)
+            den_out[bh * N + prow] = den;
+        __syncthreads();  // B2
+        if (h == 0) {
+            vz[32 * cb + j] += zc;
+            vu[32 * cb + j] += uc;
+        }
+        if (more) {
+            rk.stage(ks, t0 + kC, end, tid);
+            rv.stage(vs, t0 + kC, end, tid);
+            if (round + 2 < nrounds)
+                rq.fetch(qh, t0 + 2 * kC, end, tid);
+        }
+        __syncthreads();  // B3
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        store_pending(q);
+}
+
+// ============================================================ dQ
+// With (S, z, u) over the rows before the chunk and, for row i of it,
+//   W_ij = 1 + q_i.k_j, GV_ij = g_i.v_j (j in the chunk, j <= i),
+//   den_i = t0 + q_i.z + sum_j W_ij,  y_i = S g_i,
+//   c_i = (g_i.u + q_i.y_i + sum_j W_ij GV_ij) / den_i^2   (= a_i.o_i),
+//   dq_i = (y_i + sum_j (GV_ij - c_i den_i) k_j) / den_i - c_i z,
+// (S a_i - c_i z plus the in-chunk sum of (a_i.v_j - c_i) k_j), and
+// cbuf[i] = (c_i, 1 / den_i) for the gradient record and the dK | dV pass.
+// The product runs over S's rows: st[t] = S^T[32t.., 32cb..].
+template <class ST, int D>
+__global__ __launch_bounds__(threads<D>()) void k_bwd_q_causal(
+    const typename ST::T *__restrict__ Q, const typename ST::T *__restrict__ K,
+    const typename ST::T *__restrict__ V, const typename ST::T *__restrict__ G,
+    typename ST::T *__restrict__ dQ, float *__restrict__ cbuf, const float *__restrict__ rec,
+    int64_t N, int64_t seg_len, int nseg)
+{
+    typedef typename ST::T T;
+    typedef IO<ST> io;
+    static_assert(D >= 32 && D <= 128, "32-column blocks, state in registers");
+    constexpr int NCB = D / 32, NT = threads<D>(), KB = D / 8, LDX = D + 4, WP = kC + 1;
+    __shared__ __attribute__((aligned(16))) float qs[kC * LDX];
+    __shared__ __attribute__((aligned(16))) float ks[kC * LDX];
+    __shared__ __attribute__((aligned(16))) float vs[kC * LDX];
+    __shared__ __attribute__((aligned(16))) float gs[kC * LDX];
+    __shared__ float wx[NCB][kC * WP];  // shares of Q_c K_c^T
+    __shared__ float gx[NCB][kC * WP];  // shares of G_c V_c^T
+    __shared__ float xq[NCB][kC];       // shares of q_i.y_i
+    __shared__ __attribute__((aligned(16))) float vz[D];
+    __shared__ __attribute__((aligned(16))) float vu[D];
+
+    const int64_t bh = blockIdx.x / nseg;
+    const int seg = (int)(blockIdx.x % nseg);
+    const int tid = threadIdx.x, cb = tid >> 6, lane = tid & 63, j = lane & 31, h = lane >> 5;
+    const int64_t beg = (int64_t)seg * seg_len;
+    const int64_t end = (beg + seg_len < N) ? beg + seg_len : N;
+    const int64_t hoff = bh * N * D;
+    const float *st = rec + (bh * nseg + seg) * (int64_t)(D * D + 2 * D);
+    const T *qh = Q + hoff, *kh = K + hoff, *vh = V + hoff, *gh = G + hoff;
+    T *oh = dQ + hoff;
+
+    Rows<ST, D, NT> rq, rk, rv, rg;
+    const int64_t nrounds = (end - beg + kC - 1) / kC;
+    rq.fetch(qh, beg, end, tid);
+    rk.fetch(kh, beg, end, tid);
+    rv.fetch(vh, beg, end, tid);
+    rg.fetch(gh, beg, end, tid);
+    // sacc[t][i] = S[32cb + j][32t + 8(i/4) + 4h + i%4]
+    f16v sacc[NCB];
+#pragma unroll
+    for (int t = 0; t < NCB; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f4 v = *reinterpret_cast<const f4 *>(st + (32 * cb + j) * D + 32 * t + 8 * q +
+                                                       4 * h);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sacc[t][4 * q + r] = v[r];
+        }
+    for (int e = tid; e < D; e += NT) {
+        vz[e] = st[D * D + e];
+        vu[e] = st[D * D + D + e];
+    }
+    rq.stage(qs, beg, end, tid);
+    rk.stage(ks, beg, end, tid);
+    rv.stage(vs, beg, end, tid);
+    rg.stage(gs, beg, end, tid);
+    drain_loads();
+    if (nrounds > 1) {
+        rq.fetch(qh, beg + kC, end, tid);
+        rg.fetch(gh, beg + kC, end, tid);
+    }
+    __syncthreads();
+
+    f4 pend[4];
+    int64_t prow = 0;
+    bool pok = false;
+    auto store_pending = [&](int q) {
+        if (pok)
+            io::store4(oh + prow * D + 32 * cb + 8 * q + 4 * h, pend[q]);
+    };
+
+    for (int64_t round = 0; round < nrounds; ++round) {
+        const int64_t t0 = beg + round * kC;
+        const bool more = round + 1 < nrounds;
+        // (1) y = S g for the chunk's rows, with g.u and q.z
+        f16v acc = zero16();
+        float gu = 0.f, qz = 0.f;
+        {
+            const float *xt = &gs[j * LDX + 4 * h];
+            const float *qt = &qs[j * LDX + 4 * h];
+            int vo = 4 * h;
+            asm volatile("" : "+v"(vo));  // z and u change per chunk
+            f4 xn = *reinterpret_cast<const f4 *>(xt);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const f4 x = xn;
+                if (kb + 1 < KB)
+                    xn = *reinterpret_cast<const f4 *>(xt + (kb + 1) * 8);
+                const f4 qv = *reinterpret_cast<const f4 *>(qt + kb * 8);
+                const f4 z = *reinterpret_cast<const f4 *>(&vz[vo + kb * 8]);
+                const f4 u = *reinterpret_cast<const f4 *>(&vu[vo + kb * 8]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc = mma32(sacc[kb / 4][4 * (kb % 4) + r], x[r], acc);
+                gu += dot4(x, u);
+                qz += dot4(qv, z);
+                asm volatile("" : "+v"(gu), "+v"(qz));
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (kb == q * (KB / 4))
+                        store_pending(q);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // (2) shares of Q_c K_c^T, G_c V_c^T and q.y over this wave's columns
+        share_xyT<D>(qs, ks, wx[cb], cb, j, h);
+        share_xyT<D>(gs, vs, gx[cb], cb, j, h);
+        {
+            float p = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f4 qv = *reinterpret_cast<const f4 *>(&qs[j * LDX + 32 * cb + 8 * q + 4 * h]);
+                p += qv[0] * acc[4 * q] + qv[1] * acc[4 * q + 1] + qv[2] * acc[4 * q + 2] +
+                     qv[3] * acc[4 * q + 3];
+            }
+            p += __shfl_xor(p, 32, 64);
+            if (h == 0)
+                xq[cb][j] = p;
+        }
+        __syncthreads();  // B1
+        if (more) {
+            rq.stage(qs, t0 + kC, end, tid);
+            rg.stage(gs, t0 + kC, end, tid);
+            rk.fetch(kh, t0 + kC, end, tid);
+            rv.fetch(vh, t0 + kC, end, tid);
+        }
+        // (3) den, c, then the in-chunk term and the state update (key rows
+        // jr = 2kk + h of the MFMA step)
+        float gvk[kC / 2];
+        float rs = 0.f, cw = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < kC / 2; ++kk) {
+            const int jr = 2 * kk + h;
+            float w = 0.f, gv = 0.f;
+#pragma unroll
+            for (int p = 0; p < NCB; ++p) {
+                w += wx[p][j * WP + jr];
+                gv += gx[p][j * WP + jr];
+            }
+            const bool m = jr <= j;
+            const float wm = m ? 1.f + w : 0.f;
+            rs += wm;
+            cw += wm * gv;
+            gvk[kk] = m ? gv : 0.f;
+        }
+        rs += __shfl_xor(rs, 32, 64);
+        cw += __shfl_xor(cw, 32, 64);
+        gu += __shfl_xor(gu, 32, 64);
+        qz += __shfl_xor(qz, 32, 64);
+        float qy = 0.f;
+#pragma unroll
+        for (int p = 0; p < NCB; ++p)
+            qy += xq[p][j];
+        const float den = (float)t0 + qz + rs;
+        const float inv = 1.f / den;
+        const float c = (gu + qy + cw) * inv * inv;
+        const float cden = c * den;
+        float zc = 0.f, uc = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < kC / 2; ++kk) {
+            const int jr = 2 * kk + h;
+            const float kv = ks[jr * LDX + 32 * cb + j];
+            const float pm = (jr <= j) ? gvk[kk] - cden : 0.f;
+            acc = mma32(kv, pm, acc);
+#pragma unroll
+            for (int t = 0; t < NCB; ++t) {
+                const float vt = vs[jr * LDX + 32 * t + j];
+                sacc[t] = mma32(vt, kv, sacc[t]);
+                if (t == cb)
+                    uc += vt;
+            }
+            zc += kv;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        zc += __shfl_xor(zc, 32, 64);
+        uc += __shfl_xor(uc, 32, 64);
+        // (4) dq rows (z of the rows before the chunk), stored during the next
+        // product
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f4 z = *reinterpret_cast<const f4 *>(&vz[32 * cb + 8 * q + 4 * h]);
+            pend[q] = f4{acc[4 * q] * inv - c * z[0], acc[4 * q + 1] * inv - c * z[1],
+                         acc[4 * q + 2] * inv - c * z[2], acc[4 * q + 3] * inv - c * z[3]};
+        }
+        prow = t0 + j;
+        pok = prow < end;
+        if (pok && h == 0 && cb == 0)
+            reinterpret_cast<float2 *>(cbuf)[bh * N + prow] = float2{c, inv};
+        __syncthreads();  // B2
+        if (h == 0) {
+            vz[32 * cb + j] += zc;
+            vu[32 * cb + j] += uc;
+        }
+        if (more) {
+            rk.stage(ks, t0 + kC, end, tid);
+            rv.stage(vs, t0 + kC, end, tid);
+            if (round + 2 < nrounds) {
+                rq.fetch(qh, t0 + 2 * kC, end, tid);
+                rg.fetch(gh, t0 + 2 * kC, end, tid);
+            }
+        }
+        __syncthreads();  // B3
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        store_pending(q);
+}
+
+// ============================================================ dK | dV
+// Chunks in reverse order.  With (R, r, t) = (sum q a^T, sum c q, sum a) over
+// the rows after the chunk and, for row j of it (i in the chunk, i >= j),
+//   dk_j = R v_j - r + sum_i (a_i.v_j - c_i) q_i,
+//   dv_j = t + R^T k_j + sum_i (1 + q_i.k_j) a_i,
+// a_i = g_i / den_i and (c_i, 1 / den_i) from cbuf; then (R, r, t) += the
+// chunk's rows.  Workgroup parity 0 computes dK (st[t] = R^T[32t.., 32cb..],
+// shares of G_c V_c^T), parity 1 computes dV (st[t] = R[32t.., 32cb..],
+// shares of Q_c K_c^T).
+template <class ST, int D>
+__global__ __launch_bounds__(threads<D>()) void k_bwd_kv_causal(
+    const typename ST::T *__restrict__ Q, const typename ST::T *__restrict__ K,
+    const typename ST::T *__restrict__ V, const typename ST::T *__restrict__ G,
+    typename ST::T *__restrict__ dK, typename ST::T *__restrict__ dV,
+    const float *__restrict__ cbuf, const float *__restrict__ rec, int64_t N, int64_t seg_len,
+    int nseg)
+{
+    typedef typename ST::T T;
+    typedef IO<ST> io;
+    static_assert(D >= 32 && D <= 128, "32-column blocks, state in registers");
+    constexpr int NCB = D / 32, NT = threads<D>(), KB = D / 8, LDX = D + 4, WP = kC + 1;
+    __shared__ __attribute__((aligned(16))) float xs[kC * LDX];  // V (dK) or K (dV)
+    __shared__ __attribute__((aligned(16))) float qs[kC * LDX];
+    __shared__ __attribute__((aligned(16))) float gs[kC * LDX];
+    __shared__ float sh[NCB][kC * WP];
+    __shared__ float cs[kC], is[kC];  // c_i, 1/den_i of the chunk's rows
+    __shared__ __attribute__((aligned(16))) float vr[D];  // r (dK) or t (dV)
+
+    const int par = (int)(blockIdx.x & 1);
+    const int64_t b = blockIdx.x >> 1;
+    const int64_t bh = b / nseg;
+    const int seg = (int)(b % nseg);
+    const int tid = threadIdx.x, cb = tid >> 6, lane = tid & 63, j = lane & 31, h = lane >> 5;
+    const int64_t beg = (int64_t)seg * seg_len;
+    const int64_t end = (beg + seg_len < N) ? beg + seg_len : N;
+    const int64_t hoff = bh * N * D;
+    const float *st = rec + (bh * nseg + seg) * (int64_t)(D * D + 2 * D);
+    const T *xh = (par == 0 ? V : K) + hoff, *qh = Q + hoff, *gh = G + hoff;
+    T *oh = (par == 0 ? dK : dV) + hoff;
+    const float2 *ch = reinterpret_cast<const float2 *>(cbuf) + bh * N;
+
+    Rows<ST, D, NT> rx, rq, rg;
+    float2 rc = float2{0.f, 0.f};
+    auto fetch_c = [&](int64_t r0) {
+        if (tid < kC) {
+            int64_t row = r0 + tid;
+            row = row < end ? row : end - 1;
+            rc = ch[row];
+        }
+    };
+    auto stage_c = [&](int64_t r0) {
+        if (tid < kC) {
+            const bool ok = r0 + tid < end;
+            cs[tid] = ok ? rc.x : 0.f;
+            is[tid] = ok ? rc.y : 0.f;
+        }
+    };
+    const int64_t nrounds = (end - beg + kC - 1) / kC;
+    const int64_t last = beg + (nrounds - 1) * kC;  // first row of the last chunk
+    rx.fetch(xh, last, end, tid);
+    rq.fetch(qh, last, end, tid);
+    rg.fetch(gh, last, end, tid);
+    fetch_c(last);
+    // parity 0: sacc[t][i] = R[32cb + j][32t + 8(i/4) + 4h + i%4]
+    // parity 1: sacc[t][i] = R[32t + 8(i/4) + 4h + i%4][32cb + j]
+    f16v sacc[NCB];
+#pragma unroll
+    for (int t = 0; t < NCB; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int a = 32 * t + 8 * (i / 4) + 4 * h + (i % 4), o = 32 * cb + j;
+            sacc[t][i] = (par == 0) ? st[o * D + a] : st[a * D + o];
+        }
+    for (int e = tid; e < D; e += NT)
+        vr[e] = st[D * D + (par == 0 ? 0 : D) + e];
+    rx.stage(xs, last, end, tid);
+    rq.stage(qs, last, end, tid);
+    rg.stage(gs, last, end, tid);
+    stage_c(last);
+    drain_loads();
+    if (nrounds > 1)
+        rx.fetch(xh, last - kC, end, tid);
+    __syncthreads();
+
+    f4 pend[4];
+    int64_t prow = 0;
+    bool pok = false;
+    auto store_pending = [&](int q) {
+        if (pok)
+            io::store4(oh + prow * D + 32 * cb + 8 * q + 4 * h, pend[q]);
+    };
+
+    for (int64_t round = 0; round < nrounds; ++round) {
+        const int64_t t0 = last - round * kC;
+        const bool more = round + 1 < nrounds;
+        // (1) the suffix state applied to the chunk's rows of V (dK) or K (dV)
+        f16v acc = zero16();
+        {
+            const float *xt = &xs[j * LDX + 4 * h];
+            f4 xn = *reinterpret_cast<const f4 *>(xt);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const f4 x = xn;
+                if (kb + 1 < KB)
+                    xn = *reinterpret_cast<const f4 *>(xt + (kb + 1) * 8);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc = mma32(sacc[kb / 4][4 * (kb % 4) + r], x[r], acc);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (kb == q * (KB / 4))
+                        store_pending(q);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // (2) shares: G_c V_c^T (dK; xs holds V) or Q_c K_c^T (dV; xs holds K)
+        if (par == 0)
+            share_xyT<D>(gs, xs, sh[cb], cb, j, h);
+        else
+            share_xyT<D>(qs, xs, sh[cb], cb, j, h);
+        __syncthreads();  // B1
+        if (more) {
+            rx.stage(xs, t0 - kC, end, tid);
+            rq.fetch(qh, t0 - kC, end, tid);
+            rg.fetch(gh, t0 - kC, end, tid);
+            fetch_c(t0 - kC);
+        }
+        // (3) in-chunk term over query rows ir = 2kk + h >= j, and the state
+        // update
+        float vc = 0.f;
+        if (par == 0) {
+#pragma unroll
+            for (int kk = 0; kk < kC / 2; ++kk) {
+                const int ir = 2 * kk + h;
+                float s = 0.f;
+#pragma unroll
+                for (int p = 0; p < NCB; ++p)
+                    s += sh[p][ir * WP + j];
+                const float ci = cs[ir], ii = is[ir];
+                const float pm = (ir >= j) ? s * ii - ci : 0.f;
+                const float qb = qs[ir * LDX + 32 * cb + j];
+                acc = mma32(qb, pm, acc);
+#pragma unroll
+                for (int t = 0; t < NCB; ++t)
+                    sacc[t] = mma32(gs[ir * LDX + 32 * t + j] * ii, qb, sacc[t]);
+                vc += ci * qb;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < kC / 2; ++kk) {
+                const int ir = 2 * kk + h;
+                float s = 0.f;
+#pragma unroll
+                for (int p = 0; p < NCB; ++p)
+                    s += sh[p][ir * WP + j];
+                const float wm = (ir >= j) ? 1.f + s : 0.f;
+                const float ab = gs[ir * LDX + 32 * cb + j] * is[ir];
+                acc = mma32(ab, wm, acc);
+#pragma unroll
+                for (int t = 0; t < NCB; ++t)
+                    sacc[t] = mma32(qs[ir * LDX + 32 * t + j], ab, sacc[t]);
+                vc += ab;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        vc += __shfl_xor(vc, 32, 64);
+        // (4) rows of dK (- r) or dV (+ t) with the vector of the rows after
+        // the chunk
+        const float sg = (par == 0) ? -1.f : 1.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f4 v = *reinterpret_cast<const f4 *>(&vr[32 * cb + 8 * q + 4 * h]);
+            pend[q] = f4{acc[4 * q] + sg * v[0], acc[4 * q + 1] + sg * v[1],
+                         acc[4 * q + 2] + sg * v[2], acc[4 * q + 3] + sg * v[3]};
+        }
+        prow = t0 + j;
+        pok = prow < end;
+        __syncthreads();  // B2
+        if (h == 0)
+            vr[32 * cb + j] += vc;
+        if (more) {
+            rq.stage(qs, t0 - kC, end, tid);
+            rg.stage(gs, t0 - kC, end, tid);
+            stage_c(t0 - kC);
+            if (round + 2 < nrounds)
+                rx.fetch(xh, t0 - 2 * kC, end, tid);
+        }
+        __syncthreads();  // B3
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        store_pending(q);
+}
+
+}  // namespace cz
+}  // namespace la

@@ -554,232 +554,6 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_nc(
         store_pending(q);
 }
 
-// ============================================================ causal forward
-// O for the causal mask, one workgroup per (head, segment), chunks of C = 32
-// rows in order.  The segment starts from the exclusive prefix record of its
-// head (S, z, u over the rows before it); per chunk c with rows t0 ..:
-//   o_i = (u + S^T q_i + sum_{j in c, j <= i} (1 + q_i.k_j) v_j) / den_i,
-//   den_i = t0 + q_i.z + sum_{j in c, j <= i} (1 + q_i.k_j),
-// and then (S, z, u) += (K_c^T V_c, sum k, sum v).
-// Wave cb (one per 32-column block) keeps its column block of the running S
-// as MFMA accumulators, sacc[t][i] = S[32t + 8(i/4) + 4h + i%4][32 cb + j],
-// which is also the A-operand layout of the product S^T q (k-block kb,
-// step r <-> tile kb/4, element 4(kb%4) + r), so the state is updated and
-// applied in place.  Per chunk:
-//   (1) acc = S^T-block . Q_c^T, with q_i.z formed from the same operands;
-//   (2) the wave's share of Q_c K_c^T (its 32 columns of D) to LDS;
-//   barrier;
-//   (3) W = sum of the shares, masked (j <= i) with the constant added;
-//       acc += V_c-block^T . W^T (row sums of W go to den) and
-//       sacc += K_c^T . V_c-block;
-//   (4) o rows; stored during the next chunk's product.
-// Q_c, K_c, V_c are staged in LDS (fp32) from a register prefetch of the
-// next chunk; the staging area is refilled between two more barriers.
-template <class ST, int D>
-__global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal(
-    const typename ST::T *__restrict__ Q, const typename ST::T *__restrict__ K,
-    const typename ST::T *__restrict__ V, typename ST::T *__restrict__ O,
-    float *__restrict__ den_out, const float *__restrict__ rec, int64_t N, int64_t seg_len,
-    int nseg)
-{
-    typedef typename ST::T T;
-    typedef IO<ST> io;
-    static_assert(D >= 32 && D <= 128, "32-column blocks, state in registers");
-    constexpr int NCB = D / 32;
-    constexpr int NT = 64 * NCB;
-    constexpr int KB = D / 8;
-    constexpr int C = 32;
-    constexpr int LDX = D + 4;
-    constexpr int WP = C + 1;
-    constexpr int VEC = 16 / sizeof(T);
-    constexpr int CPR = D / VEC;
-    constexpr int PER = C * CPR / NT;
-    static_assert(PER >= 1 && C * CPR % NT == 0, "staging split");
-    __shared__ __attribute__((aligned(16))) float qs[C * LDX];
-    __shared__ __attribute__((aligned(16))) float ks[C * LDX];
-    __shared__ __attribute__((aligned(16))) float vs[C * LDX];
-    __shared__ float wx[NCB][C * WP];  // per-wave shares of Q_c K_c^T
-    __shared__ __attribute__((aligned(16))) float vz[D];
-    __shared__ __attribute__((aligned(16))) float vu[D];
-
-    const int64_t bh = blockIdx.x / nseg;
-    const int seg = (int)(blockIdx.x % nseg);
-    const int tid = threadIdx.x, cb = tid >> 6, lane = tid & 63, j = lane & 31, h = lane >> 5;
-    const int64_t beg = (int64_t)seg * seg_len;
-    const int64_t end = (beg + seg_len < N) ? beg + seg_len : N;
-    const int64_t hoff = bh * N * D;
-    const float *st = rec + (bh * nseg + seg) * (int64_t)(D * D + 2 * D);
-    const T *qh = Q + hoff, *kh = K + hoff, *vh = V + hoff;
-    T *oh = O + hoff;
-
-    uint4 sq[PER], sk[PER], sv[PER];
-    auto fetch = [&](int64_t r0) {
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int c = tid + p * NT;
-            int64_t row = r0 + c / CPR;
-            row = row < end ? row : end - 1;  // valid address; zeroed when staged
-            const int64_t off = row * D + VEC * (c % CPR);
-            sq[p] = *reinterpret_cast<const uint4 *>(qh + off);
-            sk[p] = *reinterpret_cast<const uint4 *>(kh + off);
-            sv[p] = *reinterpret_cast<const uint4 *>(vh + off);
-        }
-    };
-    auto stage_one = [&](float *lds, const uint4 &src, int c, bool ok) {
-        float v[VEC];
-        if constexpr (VEC == 4)
-            StF32::widen(src, v);
-        else
-            StBF16::widen(src, v);
-        float *dst = lds + (c / CPR) * LDX + VEC * (c % CPR);
-#pragma unroll
-        for (int x = 0; x < VEC; x += 4)
-            *reinterpret_cast<f4 *>(dst + x) =
-                ok ? f4{v[x], v[x + 1], v[x + 2], v[x + 3]} : f4{0.f, 0.f, 0.f, 0.f};
-    };
-    auto stage = [&](int64_t r0) {
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int c = tid + p * NT;
-            const bool ok = r0 + c / CPR < end;
-            stage_one(qs, sq[p], c, ok);
-            stage_one(ks, sk[p], c, ok);
-            stage_one(vs, sv[p], c, ok);
-        }
-    };
-
-    const int64_t nrounds = (end - beg + C - 1) / C;
-    fetch(beg);
-    f16v sacc[NCB];
-#pragma unroll
-    for (int t = 0; t < NCB; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            sacc[t][i] = st[(32 * t + 8 * (i / 4) + 4 * h + (i % 4)) * D + 32 * cb + j];
-    for (int e = tid; e < D; e += NT) {
-        vz[e] = st[D * D + e];
-        vu[e] = st[D * D + D + e];
-    }
-    stage(beg);
-    drain_loads();
-    if (nrounds > 1)
-        fetch(beg + C);
-    __syncthreads();
-
-    f4 pend[4];
-    int64_t prow = 0;
-    bool pok = false;
-    auto store_pending = [&](int q) {
-        if (pok)
-            io::store4(oh + prow * D + 32 * cb + 8 * q + 4 * h, pend[q]);
-    };
-
-    for (int64_t round = 0; round < nrounds; ++round) {
-        const int64_t t0 = beg + round * C;
-        // (1) the prefix state applied to the chunk's queries, and q.z
-        f16v acc = zero16();
-        float qz = 0.f;
-        {
-            const float *xt = &qs[j * LDX + 4 * h];
-            int zo = 4 * h;
-            asm volatile("" : "+v"(zo));
-            f4 xn = *reinterpret_cast<const f4 *>(xt);
-            f4 zn = *reinterpret_cast<const f4 *>(&vz[zo]);
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const f4 x = xn, z = zn;
-                if (kb + 1 < KB) {
-                    xn = *reinterpret_cast<const f4 *>(xt + (kb + 1) * 8);
-                    zn = *reinterpret_cast<const f4 *>(&vz[zo + (kb + 1) * 8]);
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc = mma32(sacc[kb / 4][4 * (kb % 4) + r], x[r], acc);
-                qz += dot4(x, z);
-                asm volatile("" : "+v"(qz));
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (kb == q * (KB / 4))
-                        store_pending(q);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        // (2) this wave's share of Q_c K_c^T: wacc[e] = W[8(e/4)+4h+e%4][j]
-        {
-            f16v wacc = zero16();
-            const float *qa = &qs[j * LDX + 32 * cb + 4 * h];
-            const float *ka = &ks[j * LDX + 32 * cb + 4 * h];
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const f4 a = *reinterpret_cast<const f4 *>(qa + 8 * kb);
-                const f4 b = *reinterpret_cast<const f4 *>(ka + 8 * kb);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    wacc = mma32(a[r], b[r], wacc);
-            }
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                wx[cb][(8 * (e / 4) + 4 * h + (e % 4)) * WP + j] = wacc[e];
-        }
-        __syncthreads();
-        // (3) in-chunk term (key rows jr = 2kk + h of the MFMA step) and the
-        // state update
-        float rs = 0.f, zc = 0.f, uc = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-            const int jr = 2 * kk + h;
-            const float vb = vs[jr * LDX + 32 * cb + j];
-            float wsum = 0.f;
-#pragma unroll
-            for (int p = 0; p < NCB; ++p)
-                wsum += wx[p][j * WP + jr];
-            const float wm = (jr <= j) ? 1.f + wsum : 0.f;
-            rs += wm;
-            acc = mma32(vb, wm, acc);
-#pragma unroll
-            for (int t = 0; t < NCB; ++t) {
-                const float kt = ks[jr * LDX + 32 * t + j];
-                sacc[t] = mma32(kt, vb, sacc[t]);
-                if (t == cb)
-                    zc += kt;
-            }
-            uc += vb;
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        rs += __shfl_xor(rs, 32, 64);
-        zc += __shfl_xor(zc, 32, 64);
-        uc += __shfl_xor(uc, 32, 64);
-        qz += __shfl_xor(qz, 32, 64);
-        // (4) normalised rows of the chunk
-        const float den = (float)t0 + qz + rs;
-        const float inv = 1.f / den;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const f4 u = *reinterpret_cast<const f4 *>(&vu[32 * cb + 8 * q + 4 * h]);
-            pend[q] = f4{(acc[4 * q] + u[0]) * inv, (acc[4 * q + 1] + u[1]) * inv,
-                         (acc[4 * q + 2] + u[2]) * inv, (acc[4 * q + 3] + u[3]) * inv};
-        }
-        prow = t0 + j;
-        pok = prow < end;
-        if (den_out != nullptr && pok && h == 0 && cb == 0)
-            den_out[bh * N + prow] = den;
-        __syncthreads();  // every read of this chunk's LDS data is done
-        if (h == 0) {
-            vz[32 * cb + j] += zc;
-            vu[32 * cb + j] += uc;
-        }
-        if (round + 1 < nrounds) {
-            stage(t0 + C);
-            if (round + 2 < nrounds)
-                fetch(t0 + 2 * C);
-        }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        store_pending(q);
-}
-
 // ============================================================ dQ + gradient record
 // One pass over a segment's rows of Q and dO that produces dQ (as KIND 1 of
 // k_apply_nc) and the segment's gradient record [dS | r | t] (as
