@@ -28,6 +28,10 @@ def build(verbose: bool = False) -> str:
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
            "-shared", "-Wall", "-I", os.path.join(ROOT, "include"),
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # MFMA accumulators in VGPRs: the running states of the causal
+           # kernels are both accumulators and A operands, and the AGPR form
+           # would keep a copy of them in each register file
+           "-mllvm", "-amdgpu-mfma-vgpr-form",
            "-o", tmp, SRC]
     res = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass warns that it does not know the device feature; drop that

@@ -46,14 +46,18 @@ using nc::mma32;
 using nc::zero16;
 
 constexpr int kC = 32;  // rows per chunk
+// word 3 of a raw buffer resource descriptor on gfx9-family GPUs (gfx950
+// included): 32-bit data format, no swizzle, zero returned out of range
+constexpr int kBufferWord3 = 0x00020000;
 
 template <int D>
 constexpr int threads() { return 64 * (D / 32); }
 
 // Rows r0 .. r0 + kC - 1 of one head's [N, D] tensor: fetched into registers
-// by the NT threads of the workgroup (16-byte loads; rows clamped below
-// `end` so that every address is valid), then written to LDS as fp32 with
-// the rows at or past `end` zeroed.
+// by the NT threads of the workgroup with 16-byte buffer loads through a
+// descriptor that covers only the chunk's valid rows (base = row r0, range
+// = the rows before `end`), so loads past the end return zeros and every
+// access stays inside the tensor; then written to LDS as fp32.
 template <class ST, int D, int NT>
 struct Rows {
     typedef typename ST::T T;
@@ -66,20 +70,22 @@ struct Rows {
 
     __device__ __forceinline__ void fetch(const T *src, int64_t r0, int64_t end, int tid)
     {
+        const int rows = (int)(end - r0 < kC ? end - r0 : kC);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<T *>(src + r0 * D), (short)0, rows * (int)(D * sizeof(T)), kBufferWord3);
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
             const int c = tid + p * NT;
-            int64_t row = r0 + c / CPR;
-            row = row < end ? row : end - 1;
-            r[p] = *reinterpret_cast<const uint4 *>(src + row * D + VEC * (c % CPR));
+            r[p] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                           rs, (c / CPR) * (int)(D * sizeof(T)) + 16 * (c % CPR), 0, 0));
         }
     }
-    __device__ __forceinline__ void stage(float *lds, int64_t r0, int64_t end, int tid) const
+    __device__ __forceinline__ void stage(float *lds, int tid) const
     {
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
             const int c = tid + p * NT;
-            const bool ok = r0 + c / CPR < end;
             float v[VEC];
             if constexpr (VEC == 4)
                 StF32::widen(r[p], v);
@@ -88,8 +94,7 @@ struct Rows {
             float *dst = lds + (c / CPR) * LDX + VEC * (c % CPR);
 #pragma unroll
             for (int x = 0; x < VEC; x += 4)
-                *reinterpret_cast<f4 *>(dst + x) =
-                    ok ? f4{v[x], v[x + 1], v[x + 2], v[x + 3]} : f4{0.f, 0.f, 0.f, 0.f};
+                *reinterpret_cast<f4 *>(dst + x) = f4{v[x], v[x + 1], v[x + 2], v[x + 3]};
         }
     }
 };
@@ -165,9 +170,9 @@ __global__ __launch_bounds__(threads<D>()) void k_fwd_causal(
         vz[e] = st[D * D + e];
         vu[e] = st[D * D + D + e];
     }
-    rq.stage(qs, beg, end, tid);
-    rk.stage(ks, beg, end, tid);
-    rv.stage(vs, beg, end, tid);
+    rq.stage(qs, tid);
+    rk.stage(ks, tid);
+    rv.stage(vs, tid);
     drain_loads();
     if (nrounds > 1)
         rq.fetch(qh, beg + kC, end, tid);
@@ -216,7 +221,7 @@ __global__ __launch_bounds__(threads<D>()) void k_fwd_causal(
         share_xyT<D>(qs, ks, wx[cb], cb, j, h);
         __syncthreads();  // B1
         if (more) {
-            rq.stage(qs, t0 + kC, end, tid);
+            rq.stage(qs, tid);
             rk.fetch(kh, t0 + kC, end, tid);
             rv.fetch(vh, t0 + kC, end, tid);
         }
@@ -267,8 +272,8 @@ __global__ __launch_bounds__(threads<D>()) void k_fwd_causal(
             vu[32 * cb + j] += uc;
         }
         if (more) {
-            rk.stage(ks, t0 + kC, end, tid);
-            rv.stage(vs, t0 + kC, end, tid);
+            rk.stage(ks, tid);
+            rv.stage(vs, tid);
             if (round + 2 < nrounds)
                 rq.fetch(qh, t0 + 2 * kC, end, tid);
         }
@@ -341,10 +346,10 @@ __global__ __launch_bounds__(threads<D>()) void k_bwd_q_causal(
         vz[e] = st[D * D + e];
         vu[e] = st[D * D + D + e];
     }
-    rq.stage(qs, beg, end, tid);
-    rk.stage(ks, beg, end, tid);
-    rv.stage(vs, beg, end, tid);
-    rg.stage(gs, beg, end, tid);
+    rq.stage(qs, tid);
+    rk.stage(ks, tid);
+    rv.stage(vs, tid);
+    rg.stage(gs, tid);
     drain_loads();
     if (nrounds > 1) {
         rq.fetch(qh, beg + kC, end, tid);
@@ -410,8 +415,8 @@ __global__ __launch_bounds__(threads<D>()) void k_bwd_q_causal(
         }
         __syncthreads();  // B1
         if (more) {
-            rq.stage(qs, t0 + kC, end, tid);
-            rg.stage(gs, t0 + kC, end, tid);
+            rq.stage(qs, tid);
+            rg.stage(gs, tid);
             rk.fetch(kh, t0 + kC, end, tid);
             rv.fetch(vh, t0 + kC, end, tid);
         }
@@ -483,8 +488,8 @@ __global__ __launch_bounds__(threads<D>()) void k_bwd_q_causal(
             vu[32 * cb + j] += uc;
         }
         if (more) {
-            rk.stage(ks, t0 + kC, end, tid);
-            rv.stage(vs, t0 + kC, end, tid);
+            rk.stage(ks, tid);
+            rv.stage(vs, tid);
             if (round + 2 < nrounds) {
                 rq.fetch(qh, t0 + 2 * kC, end, tid);
                 rg.fetch(gh, t0 + 2 * kC, end, tid);
@@ -506,26 +511,33 @@ __global__ __launch_bounds__(threads<D>()) void k_bwd_q_causal(
 // chunk's rows.  Workgroup parity 0 computes dK (st[t] = R^T[32t.., 32cb..],
 // shares of G_c V_c^T), parity 1 computes dV (st[t] = R[32t.., 32cb..],
 // shares of Q_c K_c^T).
-template <class ST, int D>
-__global__ __launch_bounds__(threads<D>()) void k_bwd_kv_causal(
+// LDS of the dK | dV pass
+template <int D>
+struct KvLds {
+    static constexpr int LDX = D + 4, WP = kC + 1, NCB = D / 32;
+    float xs[kC * LDX];    // V (dK) or K (dV)
+    float qs[kC * LDX];
+    float gs[kC * LDX];
+    float sh[NCB][kC * WP];
+    float cs[kC], is[kC];  // c_i, 1/den_i of the chunk's rows
+    float vr[D];           // r (dK) or t (dV)
+};
+
+template <class ST, int D, int PAR>
+__device__ __forceinline__ void kv_pass(
     const typename ST::T *__restrict__ Q, const typename ST::T *__restrict__ K,
     const typename ST::T *__restrict__ V, const typename ST::T *__restrict__ G,
     typename ST::T *__restrict__ dK, typename ST::T *__restrict__ dV,
     const float *__restrict__ cbuf, const float *__restrict__ rec, int64_t N, int64_t seg_len,
-    int nseg)
+    int nseg, KvLds<D> &L)
 {
     typedef typename ST::T T;
     typedef IO<ST> io;
     static_assert(D >= 32 && D <= 128, "32-column blocks, state in registers");
     constexpr int NCB = D / 32, NT = threads<D>(), KB = D / 8, LDX = D + 4, WP = kC + 1;
-    __shared__ __attribute__((aligned(16))) float xs[kC * LDX];  // V (dK) or K (dV)
-    __shared__ __attribute__((aligned(16))) float qs[kC * LDX];
-    __shared__ __attribute__((aligned(16))) float gs[kC * LDX];
-    __shared__ float sh[NCB][kC * WP];
-    __shared__ float cs[kC], is[kC];  // c_i, 1/den_i of the chunk's rows
-    __shared__ __attribute__((aligned(16))) float vr[D];  // r (dK) or t (dV)
+    float *xs = L.xs, *qs = L.qs, *gs = L.gs, *cs = L.cs, *is = L.is, *vr = L.vr;
+    auto &sh = L.sh;
 
-    const int par = (int)(blockIdx.x & 1);
     const int64_t b = blockIdx.x >> 1;
     const int64_t bh = b / nseg;
     const int seg = (int)(b % nseg);
@@ -534,8 +546,8 @@ __global__ __launch_bounds__(threads<D>()) void k_bwd_kv_causal(
     const int64_t end = (beg + seg_len < N) ? beg + seg_len : N;
     const int64_t hoff = bh * N * D;
     const float *st = rec + (bh * nseg + seg) * (int64_t)(D * D + 2 * D);
-    const T *xh = (par == 0 ? V : K) + hoff, *qh = Q + hoff, *gh = G + hoff;
-    T *oh = (par == 0 ? dK : dV) + hoff;
+    const T *xh = (PAR == 0 ? V : K) + hoff, *qh = Q + hoff, *gh = G + hoff;
+    T *oh = (PAR == 0 ? dK : dV) + hoff;
     const float2 *ch = reinterpret_cast<const float2 *>(cbuf) + bh * N;
 
     Rows<ST, D, NT> rx, rq, rg;
@@ -568,26 +580,19 @@ __global__ __launch_bounds__(threads<D>()) void k_bwd_kv_causal(
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int a = 32 * t + 8 * (i / 4) + 4 * h + (i % 4), o = 32 * cb + j;
-            sacc[t][i] = (par == 0) ? st[o * D + a] : st[a * D + o];
+            sacc[t][i] = (PAR == 0) ? st[o * D + a] : st[a * D + o];
         }
     for (int e = tid; e < D; e += NT)
-        vr[e] = st[D * D + (par == 0 ? 0 : D) + e];
-    rx.stage(xs, last, end, tid);
-    rq.stage(qs, last, end, tid);
-    rg.stage(gs, last, end, tid);
+        vr[e] = st[D * D + (PAR == 0 ? 0 : D) + e];
+    rx.stage(xs, tid);
+    rq.stage(qs, tid);
+    rg.stage(gs, tid);
     stage_c(last);
     drain_loads();
     if (nrounds > 1)
         rx.fetch(xh, last - kC, end, tid);
     __syncthreads();
 
-    f4 pend[4];
-    int64_t prow = 0;
-    bool pok = false;
-    auto store_pending = [&](int q) {
-        if (pok)
-            io::store4(oh + prow * D + 32 * cb + 8 * q + 4 * h, pend[q]);
-    };
 
     for (int64_t round = 0; round < nrounds; ++round) {
         const int64_t t0 = last - round * kC;
@@ -605,21 +610,17 @@ __global__ __launch_bounds__(threads<D>()) void k_bwd_kv_causal(
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     acc = mma32(sacc[kb / 4][4 * (kb % 4) + r], x[r], acc);
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (kb == q * (KB / 4))
-                        store_pending(q);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
         // (2) shares: G_c V_c^T (dK; xs holds V) or Q_c K_c^T (dV; xs holds K)
-        if (par == 0)
+        if constexpr (PAR == 0)
             share_xyT<D>(gs, xs, sh[cb], cb, j, h);
         else
             share_xyT<D>(qs, xs, sh[cb], cb, j, h);
         __syncthreads();  // B1
         if (more) {
-            rx.stage(xs, t0 - kC, end, tid);
+            rx.stage(xs, tid);
             rq.fetch(qh, t0 - kC, end, tid);
             rg.fetch(gh, t0 - kC, end, tid);
             fetch_c(t0 - kC);
@@ -627,7 +628,7 @@ __global__ __launch_bounds__(threads<D>()) void k_bwd_kv_causal(
         // (3) in-chunk term over query rows ir = 2kk + h >= j, and the state
         // update
         float vc = 0.f;
-        if (par == 0) {
+        if constexpr (PAR == 0) {
 #pragma unroll
             for (int kk = 0; kk < kC / 2; ++kk) {
                 const int ir = 2 * kk + h;
@@ -665,31 +666,44 @@ __global__ __launch_bounds__(threads<D>()) void k_bwd_kv_causal(
         }
         vc += __shfl_xor(vc, 32, 64);
         // (4) rows of dK (- r) or dV (+ t) with the vector of the rows after
-        // the chunk
-        const float sg = (par == 0) ? -1.f : 1.f;
+        // the chunk (stored here: the next chunk's product covers them)
+        const float sg = (PAR == 0) ? -1.f : 1.f;
+        if (t0 + j < end)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const f4 v = *reinterpret_cast<const f4 *>(&vr[32 * cb + 8 * q + 4 * h]);
-            pend[q] = f4{acc[4 * q] + sg * v[0], acc[4 * q + 1] + sg * v[1],
-                         acc[4 * q + 2] + sg * v[2], acc[4 * q + 3] + sg * v[3]};
-        }
-        prow = t0 + j;
-        pok = prow < end;
+            for (int q = 0; q < 4; ++q) {
+                const f4 v = *reinterpret_cast<const f4 *>(&vr[32 * cb + 8 * q + 4 * h]);
+                io::store4(oh + (t0 + j) * D + 32 * cb + 8 * q + 4 * h,
+                           f4{acc[4 * q] + sg * v[0], acc[4 * q + 1] + sg * v[1],
+                              acc[4 * q + 2] + sg * v[2], acc[4 * q + 3] + sg * v[3]});
+            }
         __syncthreads();  // B2
         if (h == 0)
             vr[32 * cb + j] += vc;
         if (more) {
-            rq.stage(qs, t0 - kC, end, tid);
-            rg.stage(gs, t0 - kC, end, tid);
+            rq.stage(qs, tid);
+            rg.stage(gs, tid);
             stage_c(t0 - kC);
             if (round + 2 < nrounds)
                 rx.fetch(xh, t0 - 2 * kC, end, tid);
         }
         __syncthreads();  // B3
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        store_pending(q);
+}
+
+
+template <class ST, int D>
+__global__ __launch_bounds__(threads<D>()) __attribute__((amdgpu_waves_per_eu(2))) void k_bwd_kv_causal(
+    const typename ST::T *__restrict__ Q, const typename ST::T *__restrict__ K,
+    const typename ST::T *__restrict__ V, const typename ST::T *__restrict__ G,
+    typename ST::T *__restrict__ dK, typename ST::T *__restrict__ dV,
+    const float *__restrict__ cbuf, const float *__restrict__ rec, int64_t N, int64_t seg_len,
+    int nseg)
+{
+    __shared__ __attribute__((aligned(16))) KvLds<D> lds;
+    if (blockIdx.x & 1)
+        kv_pass<ST, D, 1>(Q, K, V, G, dK, dV, cbuf, rec, N, seg_len, nseg, lds);
+    else
+        kv_pass<ST, D, 0>(Q, K, V, G, dK, dV, cbuf, rec, N, seg_len, nseg, lds);
 }
 
 }  // namespace cz
