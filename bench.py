@@ -33,7 +33,8 @@ METRIC = "LA fwd+bwd tokens/s at B4 H16 D128 N4096; % of binding HBM/FLOP roofli
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix (= fp32 vector) peak
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 KERNEL_SOURCES = [os.path.join(ROOT, "linear_attention_transformer_amd", "csrc", f)
-                  for f in ("la_kernels.hpp", "la_kernels_nc.hpp", "la_api.hip")]
+                  for f in ("la_kernels.hpp", "la_kernels_nc.hpp", "la_kernels_causal.hpp",
+                            "la_api.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_MIB = 256                  # plain streaming kernel: reads and writes this much
 
@@ -41,9 +42,9 @@ COPY_MIB = 256                  # plain streaming kernel: reads and writes this 
 KERNEL_NAMES = [
     (r"k_reduce_nc<[^>]*, (true|1)>|k_grad_state_local<", "grad_state_local"),
     (r"k_reduce_nc<|k_state_local<", "state_local"),
-    (r"k_apply_nc<[^>]*, 0>|k_forward<", "forward"),
-    (r"k_apply_nc<[^>]*, 1>|k_bwd_q<", "bwd_q"),
-    (r"k_apply_nc<[^>]*, 2>|k_bwd_kv<", "bwd_kv"),
+    (r"k_apply_nc<[^>]*, 0>|k_fwd_causal<|k_forward<", "forward"),
+    (r"k_bwd_q_nc<|k_bwd_q_causal<|k_bwd_q<", "bwd_q"),
+    (r"k_apply_nc<[^>]*, 2>|k_bwd_kv_causal<|k_bwd_kv<", "bwd_kv"),
     (r"k_state_scan", "state_scan"),
 ]
 
