@@ -6,11 +6,13 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <type_traits>
 
 #include "la.h"
 #include "la_kernels.hpp"
 #include "la_kernels_nc.hpp"
 #include "la_kernels_causal.hpp"
+#include "la_kernels_bf16.hpp"
 
 namespace {
 
@@ -180,10 +182,15 @@ int state_of_kv(const void *K, const void *V, float *part, float *tot, const Pla
     bool done = false;
     if constexpr (nc_path<D>()) {
         rc = traced(t, s, "state_local", [&] {
-            nc::k_reduce_nc<ST, D, false><<<dim3((unsigned)(p.nseg * p.BH)),
-                                            dim3(nc::kReduceThreads), 0, s>>>(
-                static_cast<const T *>(K), static_cast<const T *>(V), nullptr, part, p.N,
-                p.seg_len, (int)p.nseg);
+            if constexpr (std::is_same<ST, StBF16>::value)
+                bf::k_reduce_bf<D, false><<<dim3((unsigned)(p.nseg * p.BH)), dim3(256), 0, s>>>(
+                    static_cast<const T *>(K), static_cast<const T *>(V), nullptr, part, p.N,
+                    p.seg_len, (int)p.nseg);
+            else
+                nc::k_reduce_nc<ST, D, false><<<dim3((unsigned)(p.nseg * p.BH)),
+                                                dim3(nc::kReduceThreads), 0, s>>>(
+                    static_cast<const T *>(K), static_cast<const T *>(V), nullptr, part, p.N,
+                    p.seg_len, (int)p.nseg);
         });
         done = true;
     }
@@ -221,10 +228,16 @@ int run_forward(const void *Q, const void *K, const void *V, void *O, float *den
     if constexpr (nc_path<D>()) {
         if (!p.causal)
             return traced(t, s, "forward", [&] {
-                nc::k_apply_nc<ST, D, 0><<<dim3((unsigned)(p.nseg * p.BH)),
-                                           dim3(nc::kApplyThreads), 0, s>>>(
-                    static_cast<const T *>(Q), nullptr, static_cast<T *>(O), nullptr, den_out,
-                    rec, p.N, p.seg_len, (int)p.nseg);
+                if constexpr (std::is_same<ST, StBF16>::value)
+                    bf::k_apply_bf<D, 0><<<dim3((unsigned)(p.nseg * p.BH)),
+                                           dim3(bf::kApplyThreads), 0, s>>>(
+                        static_cast<const T *>(Q), nullptr, static_cast<T *>(O), nullptr,
+                        den_out, rec, p.N, p.seg_len, (int)p.nseg);
+                else
+                    nc::k_apply_nc<ST, D, 0><<<dim3((unsigned)(p.nseg * p.BH)),
+                                               dim3(nc::kApplyThreads), 0, s>>>(
+                        static_cast<const T *>(Q), nullptr, static_cast<T *>(O), nullptr,
+                        den_out, rec, p.N, p.seg_len, (int)p.nseg);
             });
         return traced(t, s, "forward", [&] {
             cz::k_fwd_causal<ST, D><<<dim3((unsigned)(p.nseg * p.BH)), dim3(cz::threads<D>()), 0,
@@ -281,8 +294,12 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
         if (rc != LA_OK)
             return rc;
         rc = traced(t, s, "grad_state_local", [&] {
-            nc::k_reduce_nc<ST, D, true><<<g1, dim3(nc::kReduceThreads), 0, s>>>(
-                q, g, cbuf, gpart, p.N, p.seg_len, (int)p.nseg);
+            if constexpr (std::is_same<ST, StBF16>::value)
+                bf::k_reduce_bf<D, true><<<g1, dim3(256), 0, s>>>(q, g, cbuf, gpart, p.N,
+                                                                p.seg_len, (int)p.nseg);
+            else
+                nc::k_reduce_nc<ST, D, true><<<g1, dim3(nc::kReduceThreads), 0, s>>>(
+                    q, g, cbuf, gpart, p.N, p.seg_len, (int)p.nseg);
         });
         if (rc != LA_OK)
             return rc;
@@ -306,10 +323,16 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
         if ((rc = scan(gpart, ws + l.gtot, p, 0, s, t)) != LA_OK)
             return rc;
         return traced(t, s, "bwd_kv", [&] {
-            nc::k_apply_nc<ST, D, 2><<<dim3((unsigned)(2 * p.nseg * p.BH)),
-                                       dim3(nc::kApplyThreads), 0, s>>>(
-                v, k, static_cast<T *>(dK), static_cast<T *>(dV), nullptr, ws + l.gtot, p.N,
-                p.seg_len, (int)p.nseg);
+            if constexpr (std::is_same<ST, StBF16>::value)
+                bf::k_apply_bf<D, 2><<<dim3((unsigned)(2 * p.nseg * p.BH)),
+                                       dim3(bf::kApplyThreads), 0, s>>>(
+                    v, k, static_cast<T *>(dK), static_cast<T *>(dV), nullptr, ws + l.gtot, p.N,
+                    p.seg_len, (int)p.nseg);
+            else
+                nc::k_apply_nc<ST, D, 2><<<dim3((unsigned)(2 * p.nseg * p.BH)),
+                                           dim3(nc::kApplyThreads), 0, s>>>(
+                    v, k, static_cast<T *>(dK), static_cast<T *>(dV), nullptr, ws + l.gtot, p.N,
+                    p.seg_len, (int)p.nseg);
         });
     }
     rc = traced(t, s, "bwd_q", [&] {

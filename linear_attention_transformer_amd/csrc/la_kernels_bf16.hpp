@@ -1,0 +1,478 @@
+// la_kernels_bf16.hpp -- bf16-storage kernels on the bf16 matrix cores of
+// gfx950 (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
+//
+// Same method and layout as la_kernels_nc.hpp (pages about "Transformer
+// Based Linear Attention with Optimized GPU Kernel Implementation":
+// sciencestack.ai TL;DR and Figure 1 caption; cloud.baidu.com article,
+// section 2).  With bf16 storage every row of Q, K, V and dO is exactly a
+// bf16 vector, so a product with it on the bf16 MFMA accumulates exact
+// products in fp32.  The other factor of the apply products is an fp32 state
+// (S, dS); it is carried as two bf16 terms, hi = bf16(x) and lo = bf16(x -
+// hi), which represent x to about 2^-17 relative, and each k-step issues two
+// MFMAs (hi, lo) against the same row operand.
+//
+// v_mfma_f32_32x32x16_bf16: lane l = 32 h + j supplies A[m = j][k = 8h ..
+// 8h + 7] and B[k = 8h .. 8h + 7][n = j] (8 bf16 each) and holds accumulator
+// element i at row 8 (i / 4) + 4 h + i % 4, column j -- the same output
+// layout as the fp32 32x32x2 form, so the epilogues are unchanged.
+#pragma once
+
+#include "la_kernels_nc.hpp"
+
+namespace la {
+namespace bf {
+
+using nc::dot4;
+using nc::drain_loads;
+using nc::f16v;
+using nc::zero16;
+
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f16v mma16(bf8 a, bf8 b, f16v c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// word 3 of a raw buffer resource descriptor on gfx9-family GPUs
+constexpr int kBufferWord3 = 0x00020000;
+
+// x = hi + lo with hi, lo bf16 (round to nearest even both times)
+__device__ __forceinline__ void split_bf16(float x, __bf16 &hi, __bf16 &lo)
+{
+    hi = (__bf16)x;
+    lo = (__bf16)(x - (float)hi);
+}
+
+// the 8 bf16 of b as fp32
+__device__ __forceinline__ void unpack8(bf8 b, float *o)
+{
+    const uint4 u = __builtin_bit_cast(uint4, b);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o[2 * i] = __uint_as_float(w[i] << 16);
+        o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+
+constexpr int kApplyThreads = 256;
+
+// ============================================================ apply
+// KIND 0 forward : A = S^T, o_i = (u + A q_i) / (N + q_i.z), X = Q;
+//                  den_out[i] = N + q_i.z (optional).
+// KIND 2 dK | dV : parity 0: A = dS, X = V, dk_j = A v_j - r;
+//                  parity 1: A = dS^T, X2 = K, dv_j = A k_j + t.
+// The structure is k_apply_nc's: waves own 32-column output blocks (and, for
+// D < 128, row groups), hold their block of A in registers (as hi/lo bf16
+// pairs: 8 per lane and k-step of 16), stage each round of rows in LDS
+// (raw bf16, double-buffered, one barrier per round), and read the B operand
+// as one 16-byte LDS read per k-step.  In the forward q_j.z is accumulated
+// from the same operands; stores of a round are issued during the next
+// round's MFMAs.  Rows are loaded through a per-round buffer descriptor that
+// covers only the rows before the segment end (zeros beyond it).
+template <int D, int KIND>
+__global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
+    const uint16_t *__restrict__ X, const uint16_t *__restrict__ X2, uint16_t *__restrict__ Out,
+    uint16_t *__restrict__ Out2, float *__restrict__ den_out, const float *__restrict__ rec,
+    int64_t N, int64_t seg_len, int nseg)
+{
+    typedef nc::IO<StBF16> io;
+    static_assert(D >= 32 && D <= 128, "32-column output blocks");
+    static_assert(KIND == 0 || KIND == 2, "forward or dK | dV");
+    constexpr int KS = D / 16;               // k-steps of 16
+    constexpr int NWAVE = kApplyThreads / 64;
+    constexpr int NCB = D / 32;
+    constexpr int NRG = NWAVE / NCB;
+    constexpr int TR = 32 * NRG;             // rows per round
+    constexpr int LDX = D + 8;               // LDS row pitch (bf16)
+    constexpr int CPR = D / 8;               // 16-byte chunks per row
+    constexpr int PER = TR * CPR / kApplyThreads;
+    static_assert(PER >= 1 && TR * CPR % kApplyThreads == 0, "staging split");
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][TR * LDX];
+    __shared__ __attribute__((aligned(16))) float vz[KIND == 0 ? D : 4];
+
+    const int sub = (KIND == 2) ? (int)(blockIdx.x & 1) : 0;
+    const int64_t b = (KIND == 2) ? (blockIdx.x >> 1) : blockIdx.x;
+    const int64_t bh = b / nseg;
+    const int seg = (int)(b % nseg);
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, j = lane & 31, h = lane >> 5;
+    const int cb = w % NCB, rg = w / NCB;
+    const int64_t beg = (int64_t)seg * seg_len;
+    const int64_t end = (beg + seg_len < N) ? beg + seg_len : N;
+    const int64_t hoff = bh * N * D;
+    const float *st = rec + bh * (int64_t)(D * D + 2 * D);
+    const bool colread = (KIND == 0) || (KIND == 2 && sub == 1);
+    const uint16_t *xh = ((KIND == 2 && sub == 1) ? X2 : X) + hoff;
+    uint16_t *oh = ((KIND == 2 && sub == 1) ? Out2 : Out) + hoff;
+
+    uint4 stg[PER];
+    auto fetch_round = [&](int64_t r0) {
+        const int rows = (int)(end - r0 < TR ? end - r0 : TR);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(xh + r0 * D), (short)0, rows * D * 2, kBufferWord3);
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int c = tid + p * kApplyThreads;
+            stg[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rs, (c / CPR) * D * 2 + 16 * (c % CPR), 0, 0));
+        }
+    };
+    auto stage_round = [&](int buf) {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int c = tid + p * kApplyThreads;
+            *reinterpret_cast<uint4 *>(&xs[buf][(c / CPR) * LDX + 8 * (c % CPR)]) = stg[p];
+        }
+    };
+
+    const int64_t nrounds = (end - beg + TR - 1) / TR;
+    fetch_round(beg);
+
+    // this wave's block of A as hi/lo bf16:
+    // a?[ks][s] = A[32 cb + j][16 ks + 8 h + s]
+    bf8 ahi[KS], alo[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        float v[8];
+        if (colread) {
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                v[s] = st[(16 * ks + 8 * h + s) * D + 32 * cb + j];
+        } else {
+            const f4 v0 = *reinterpret_cast<const f4 *>(st + (32 * cb + j) * D + 16 * ks + 8 * h);
+            const f4 v1 =
+                *reinterpret_cast<const f4 *>(st + (32 * cb + j) * D + 16 * ks + 8 * h + 4);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                v[s] = v0[s];
+                v[s + 4] = v1[s];
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            __bf16 hi, lo;
+            split_bf16(v[s], hi, lo);
+            ahi[ks][s] = hi;
+            alo[ks][s] = lo;
+        }
+    }
+    // epilogue vector at the lane's output columns 32*cb + 8*q + 4*h + (0..3):
+    // u (forward), -r (dK) or t (dV)
+    f4 ev[4];
+    {
+        const float *vec = st + D * D + ((KIND == 0 || (KIND == 2 && sub == 1)) ? D : 0);
+        const float sgn = (KIND == 2 && sub == 0) ? -1.f : 1.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            ev[q] = sgn * *reinterpret_cast<const f4 *>(vec + 32 * cb + 8 * q + 4 * h);
+    }
+    if constexpr (KIND == 0)
+        for (int e = tid; e < D; e += kApplyThreads)
+            vz[e] = st[D * D + e];
+    stage_round(0);
+    drain_loads();
+    if (nrounds > 1)
+        fetch_round(beg + TR);
+    __syncthreads();
+
+    f4 pend[4];
+    int64_t prow = 0;
+    bool pok = false;
+    auto store_pending = [&](int q) {
+        if (pok)
+            io::store4(oh + prow * D + 32 * cb + 8 * q + 4 * h, pend[q]);
+    };
+
+    for (int64_t round = 0; round < nrounds; ++round) {
+        const int buf = (int)(round & 1);
+        const uint16_t *xt = &xs[buf][(32 * rg + j) * LDX + 8 * h];
+        int zo = 8 * h;
+        asm volatile("" : "+v"(zo));  // z reads stay in the loop
+        f16v acc = zero16();
+        float qz = 0.f;
+        bf8 xn = *reinterpret_cast<const bf8 *>(xt);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf8 x = xn;
+            if (ks + 1 < KS)
+                xn = *reinterpret_cast<const bf8 *>(xt + 16 * (ks + 1));
+            acc = mma16(ahi[ks], x, acc);
+            acc = mma16(alo[ks], x, acc);
+            if constexpr (KIND == 0) {
+                float xf[8];
+                unpack8(x, xf);
+                const f4 z0 = *reinterpret_cast<const f4 *>(&vz[zo + 16 * ks]);
+                const f4 z1 = *reinterpret_cast<const f4 *>(&vz[zo + 16 * ks + 4]);
+                qz += dot4(f4{xf[0], xf[1], xf[2], xf[3]}, z0) +
+                      dot4(f4{xf[4], xf[5], xf[6], xf[7]}, z1);
+                asm volatile("" : "+v"(qz));
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (ks == (q * KS) / 4)
+                    store_pending(q);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        const int64_t row = beg + round * TR + 32 * rg + j;
+        if constexpr (KIND == 0) {
+            qz += __shfl_xor(qz, 32, 64);
+            const float den = (float)N + qz;
+            const float inv = 1.f / den;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                pend[q] = f4{(acc[4 * q] + ev[q][0]) * inv, (acc[4 * q + 1] + ev[q][1]) * inv,
+                             (acc[4 * q + 2] + ev[q][2]) * inv, (acc[4 * q + 3] + ev[q][3]) * inv};
+            if (den_out != nullptr && row < end && h == 0 && cb == 0)
+                den_out[bh * N + row] = den;
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                pend[q] = f4{acc[4 * q] + ev[q][0], acc[4 * q + 1] + ev[q][1],
+                             acc[4 * q + 2] + ev[q][2], acc[4 * q + 3] + ev[q][3]};
+        }
+        prow = row;
+        pok = row < end;
+        if (round + 1 < nrounds) {
+            stage_round(buf ^ 1);
+            if (round + 2 < nrounds)
+                fetch_round(beg + (round + 2) * TR);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        store_pending(q);
+}
+
+// ============================================================ reduction
+// Record (bh, seg) as k_reduce_nc writes it: Mat[D][D] = sum_t X[t]^T Y'[t],
+// cx = sum_t w_t X[t], cy = sum_t Y'[t] over the segment's rows, with
+//   forward  (GRAD = false): X = K, Y' = V, w = 1        -> S, z, u
+//   backward (GRAD = true) : X = Q, Y' = dO / den, w = c -> dS, r, t
+// and (c_t, 1/den_t) from cbuf.  The contraction runs over tokens, so both
+// MFMA operands need 8 consecutive tokens of one column per lane: each
+// round of TT = 64 rows is staged transposed in LDS (column-major, tokens
+// contiguous), each staging lane packing a pair of tokens into 32-bit
+// writes.  Y' of the backward is an fp32 product, kept as hi and lo bf16
+// planes (two MFMAs per step).  The column sums are accumulated by the
+// staging lanes across rounds and reduced across lanes once at the end.
+// Waves own 32x32 output tiles (D = 128: a 2 x 2 block each); for D = 32
+// the four waves split the k-steps of the single tile and add up in LDS.
+template <int D, bool GRAD>
+__global__ __launch_bounds__(256) void k_reduce_bf(
+    const uint16_t *__restrict__ X, const uint16_t *__restrict__ Y,
+    const float *__restrict__ cbuf, float *__restrict__ part, int64_t N, int64_t seg_len,
+    int nseg)
+{
+    static_assert(D >= 32 && D <= 128, "32x32 tiles");
+    constexpr int NT = 256, TT = 64;
+    constexpr int R2 = TT + 8;              // bf16 pitch of a transposed column
+    constexpr int NTILE1 = D / 32;          // tiles per dimension
+    constexpr int NTILE = NTILE1 * NTILE1;
+    constexpr int TPW1 = NTILE >= 4 ? NTILE1 / 2 : 1;  // tiles per wave per dimension
+    constexpr int WPT = NTILE >= 4 ? 1 : 4;           // waves sharing a tile (k split)
+    constexpr int CH = D / 8;               // 8-column chunks per row
+    constexpr int PC = (TT / 2) * CH;       // (token pair, chunk) items per round
+    constexpr int PER = (PC + NT - 1) / NT;
+    constexpr int NYP = GRAD ? 2 : 1;       // planes of Y'
+    __shared__ __attribute__((aligned(16))) uint16_t xT[D * R2];
+    __shared__ __attribute__((aligned(16))) uint16_t yT[NYP][D * R2];
+    __shared__ float red[WPT > 1 ? (WPT - 1) * 16 * 64 : 1];
+
+    const int64_t bh = blockIdx.x / nseg;
+    const int seg = (int)(blockIdx.x % nseg);
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, j = lane & 31, h = lane >> 5;
+    const int64_t beg = (int64_t)seg * seg_len;
+    const int64_t end = (beg + seg_len < N) ? beg + seg_len : N;
+    const int64_t hoff = bh * N * D;
+    const uint16_t *xh = X + hoff, *yh = Y + hoff;
+    const float2 *ch = GRAD ? reinterpret_cast<const float2 *>(cbuf) + bh * N : nullptr;
+    // output tiles of this wave
+    const int m0 = (NTILE >= 4) ? (w / 2) * 32 * TPW1 : 0;
+    const int n0 = (NTILE >= 4) ? (w % 2) * 32 * TPW1 : 0;
+    const int ksplit = (NTILE >= 4) ? 0 : w;  // D = 32: this wave's k-step
+
+    // staging items: q = tid + p * NT -> chunk q / (TT/2), token pair q % (TT/2)
+    uint4 sx[PER][2], sy[PER][2];
+    float2 scb[PER][2];
+    float cx[PER][8], cy[PER][8];
+#pragma unroll
+    for (int p = 0; p < PER; ++p)
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            cx[p][s] = cy[p][s] = 0.f;
+
+    auto fetch = [&](int64_t r0) {
+        const int rows = (int)(end - r0 < TT ? end - r0 : TT);
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(xh + r0 * D), (short)0, rows * D * 2, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(yh + r0 * D), (short)0, rows * D * 2, kBufferWord3);
+        __amdgpu_buffer_rsrc_t rc;
+        if constexpr (GRAD)
+            rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float2 *>(ch + r0), (short)0,
+                                                   rows * 8, kBufferWord3);
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int q = tid + p * NT;
+            if (PC % NT == 0 || q < PC) {
+                const int chunk = q / (TT / 2), pr = q % (TT / 2);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int off = (2 * pr + u) * D * 2 + 16 * chunk;
+                    sx[p][u] = __builtin_bit_cast(uint4,
+                                                  __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+                    sy[p][u] = __builtin_bit_cast(uint4,
+                                                  __builtin_amdgcn_raw_buffer_load_b128(ry, off, 0, 0));
+                    if constexpr (GRAD)
+                        scb[p][u] = __builtin_bit_cast(
+                            float2, __builtin_amdgcn_raw_buffer_load_b64(rc, (2 * pr + u) * 8, 0, 0));
+                }
+            }
+        }
+    };
+    auto stage = [&]() {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int q = tid + p * NT;
+            if (PC % NT == 0 || q < PC) {
+                const int chunk = q / (TT / 2), pr = q % (TT / 2);
+                float xv[2][8], yv[2][8];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    StBF16::widen(sx[p][u], xv[u]);
+                    StBF16::widen(sy[p][u], yv[u]);
+                }
+                const uint32_t *xw0 = reinterpret_cast<const uint32_t *>(&sx[p][0]);
+                const uint32_t *xw1 = reinterpret_cast<const uint32_t *>(&sx[p][1]);
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    // tokens 2 pr, 2 pr + 1 of column 8 chunk + s, packed
+                    const uint32_t lo0 = (s & 1) ? (xw0[s / 2] >> 16) : (xw0[s / 2] & 0xffffu);
+                    const uint32_t lo1 = (s & 1) ? (xw1[s / 2] >> 16) : (xw1[s / 2] & 0xffffu);
+                    *reinterpret_cast<uint32_t *>(&xT[(8 * chunk + s) * R2 + 2 * pr]) =
+                        lo0 | (lo1 << 16);
+                }
+                if constexpr (!GRAD) {
+                    const uint32_t *yw0 = reinterpret_cast<const uint32_t *>(&sy[p][0]);
+                    const uint32_t *yw1 = reinterpret_cast<const uint32_t *>(&sy[p][1]);
+#pragma unroll
+                    for (int s = 0; s < 8; ++s) {
+                        const uint32_t a0 = (s & 1) ? (yw0[s / 2] >> 16) : (yw0[s / 2] & 0xffffu);
+                        const uint32_t a1 = (s & 1) ? (yw1[s / 2] >> 16) : (yw1[s / 2] & 0xffffu);
+                        *reinterpret_cast<uint32_t *>(&yT[0][(8 * chunk + s) * R2 + 2 * pr]) =
+                            a0 | (a1 << 16);
+                        cx[p][s] += xv[0][s] + xv[1][s];
+                        cy[p][s] += yv[0][s] + yv[1][s];
+                    }
+                } else {
+#pragma unroll
+                    for (int s = 0; s < 8; ++s) {
+                        __bf16 h0, l0, h1, l1;
+                        const float a0 = yv[0][s] * scb[p][0].y, a1 = yv[1][s] * scb[p][1].y;
+                        split_bf16(a0, h0, l0);
+                        split_bf16(a1, h1, l1);
+                        *reinterpret_cast<uint32_t *>(&yT[0][(8 * chunk + s) * R2 + 2 * pr]) =
+                            (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                        *reinterpret_cast<uint32_t *>(&yT[1][(8 * chunk + s) * R2 + 2 * pr]) =
+                            (uint32_t)__builtin_bit_cast(uint16_t, l0) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+                        cx[p][s] += scb[p][0].x * xv[0][s] + scb[p][1].x * xv[1][s];
+                        cy[p][s] += a0 + a1;
+                    }
+                }
+            }
+        }
+    };
+
+    f16v acc[TPW1][TPW1];
+#pragma unroll
+    for (int a = 0; a < TPW1; ++a)
+#pragma unroll
+        for (int b = 0; b < TPW1; ++b)
+            acc[a][b] = zero16();
+
+    const int64_t nrounds = (end - beg + TT - 1) / TT;
+    fetch(beg);
+    for (int64_t round = 0; round < nrounds; ++round) {
+        __syncthreads();  // the previous round's operands have been read
+        stage();
+        if (round + 1 < nrounds)
+            fetch(beg + (round + 1) * TT);
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < TT / 16; ++kk) {
+            if (WPT > 1 && kk != ksplit)
+                continue;
+            bf8 av[TPW1], bv[TPW1][NYP];
+#pragma unroll
+            for (int a = 0; a < TPW1; ++a)
+                av[a] = *reinterpret_cast<const bf8 *>(&xT[(m0 + 32 * a + j) * R2 + 16 * kk + 8 * h]);
+#pragma unroll
+            for (int b = 0; b < TPW1; ++b)
+#pragma unroll
+                for (int y = 0; y < NYP; ++y)
+                    bv[b][y] = *reinterpret_cast<const bf8 *>(
+                        &yT[y][(n0 + 32 * b + j) * R2 + 16 * kk + 8 * h]);
+#pragma unroll
+            for (int a = 0; a < TPW1; ++a)
+#pragma unroll
+                for (int b = 0; b < TPW1; ++b)
+#pragma unroll
+                    for (int y = 0; y < NYP; ++y)
+                        acc[a][b] = mma16(av[a], bv[b][y], acc[a][b]);
+        }
+    }
+
+    float *out = part + (bh * nseg + seg) * (int64_t)(D * D + 2 * D);
+    if constexpr (WPT > 1) {
+        // D = 32: waves 1..3 hand their k-split partials to wave 0
+        if (w > 0)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                red[((w - 1) * 16 + i) * 64 + lane] = acc[0][0][i];
+        __syncthreads();
+        if (w == 0)
+            for (int o = 0; o < WPT - 1; ++o)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    acc[0][0][i] += red[(o * 16 + i) * 64 + lane];
+    }
+    if (WPT == 1 || w == 0) {
+#pragma unroll
+        for (int a = 0; a < TPW1; ++a)
+#pragma unroll
+            for (int b = 0; b < TPW1; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    out[(m0 + 32 * a + 8 * (i / 4) + 4 * h + (i % 4)) * D + n0 + 32 * b + j] =
+                        acc[a][b][i];
+    }
+    // column sums: the 32 lanes of a half-wave share one chunk of 8 columns
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+        const int q = tid + p * NT;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+#pragma unroll
+            for (int o = 1; o < 32; o <<= 1) {
+                cx[p][s] += __shfl_xor(cx[p][s], o, 64);
+                cy[p][s] += __shfl_xor(cy[p][s], o, 64);
+            }
+        }
+        if ((PC % NT == 0 || q < PC) && j == 0) {
+            const int chunk = q / (TT / 2);
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                out[D * D + 8 * chunk + s] = cx[p][s];
+                out[D * D + D + 8 * chunk + s] = cy[p][s];
+            }
+        }
+    }
+}
+
+}  // namespace bf
+}  // namespace la
