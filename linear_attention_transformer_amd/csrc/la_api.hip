@@ -232,7 +232,7 @@ int run_forward(const void *Q, const void *K, const void *V, void *O, float *den
                     bf::k_apply_bf<D, 0><<<dim3((unsigned)(p.nseg * p.BH)),
                                            dim3(bf::kApplyThreads), 0, s>>>(
                         static_cast<const T *>(Q), nullptr, static_cast<T *>(O), nullptr,
-                        den_out, rec, p.N, p.seg_len, (int)p.nseg);
+                        den_out, nullptr, rec, p.N, p.seg_len, (int)p.nseg);
                 else
                     nc::k_apply_nc<ST, D, 0><<<dim3((unsigned)(p.nseg * p.BH)),
                                                dim3(nc::kApplyThreads), 0, s>>>(
@@ -313,11 +313,27 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
     }
     if constexpr (!CAUSAL && nc_path<D>()) {
         const dim3 g1((unsigned)(p.nseg * p.BH));
-        // dQ and the segment's gradient record in one pass
-        rc = traced(t, s, "bwd_q", [&] {
-            nc::k_bwd_q_nc<ST, D><<<g1, dim3(512), 0, s>>>(
-                g, q, static_cast<T *>(dQ), gpart, fstate, p.N, p.seg_len, (int)p.nseg);
-        });
+        if constexpr (std::is_same<ST, StBF16>::value) {
+            // bf16 matrix cores: dQ with (c_i, 1/den_i), then the gradient
+            // records from a second (bf16, half-size) read of Q and dO
+            rc = traced(t, s, "bwd_q", [&] {
+                bf::k_apply_bf<D, 1><<<g1, dim3(bf::kApplyThreads), 0, s>>>(
+                    g, q, static_cast<T *>(dQ), nullptr, nullptr, cbuf, fstate, p.N, p.seg_len,
+                    (int)p.nseg);
+            });
+            if (rc != LA_OK)
+                return rc;
+            rc = traced(t, s, "grad_state_local", [&] {
+                bf::k_reduce_bf<D, true><<<g1, dim3(256), 0, s>>>(q, g, cbuf, gpart, p.N,
+                                                                p.seg_len, (int)p.nseg);
+            });
+        } else {
+            // dQ and the segment's gradient record in one pass over Q and dO
+            rc = traced(t, s, "bwd_q", [&] {
+                nc::k_bwd_q_nc<ST, D><<<g1, dim3(512), 0, s>>>(
+                    g, q, static_cast<T *>(dQ), gpart, fstate, p.N, p.seg_len, (int)p.nseg);
+            });
+        }
         if (rc != LA_OK)
             return rc;
         if ((rc = scan(gpart, ws + l.gtot, p, 0, s, t)) != LA_OK)
@@ -326,8 +342,8 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
             if constexpr (std::is_same<ST, StBF16>::value)
                 bf::k_apply_bf<D, 2><<<dim3((unsigned)(2 * p.nseg * p.BH)),
                                        dim3(bf::kApplyThreads), 0, s>>>(
-                    v, k, static_cast<T *>(dK), static_cast<T *>(dV), nullptr, ws + l.gtot, p.N,
-                    p.seg_len, (int)p.nseg);
+                    v, k, static_cast<T *>(dK), static_cast<T *>(dV), nullptr, nullptr,
+                    ws + l.gtot, p.N, p.seg_len, (int)p.nseg);
             else
                 nc::k_apply_nc<ST, D, 2><<<dim3((unsigned)(2 * p.nseg * p.BH)),
                                            dim3(nc::kApplyThreads), 0, s>>>(

@@ -61,6 +61,10 @@ constexpr int kApplyThreads = 256;
 // ============================================================ apply
 // KIND 0 forward : A = S^T, o_i = (u + A q_i) / (N + q_i.z), X = Q;
 //                  den_out[i] = N + q_i.z (optional).
+// KIND 1 dQ      : A = S, X = dO, X2 = Q: y_i = A g_i, den_i = N + q_i.z,
+//                  c_i = (g_i.u + q_i.y_i) / den_i^2, dq_i = y_i / den_i - c_i z;
+//                  cbuf[i] = (c_i, 1/den_i).  q_i.y_i is summed over the
+//                  waves' column blocks through LDS at the round's barrier.
 // KIND 2 dK | dV : parity 0: A = dS, X = V, dk_j = A v_j - r;
 //                  parity 1: A = dS^T, X2 = K, dv_j = A k_j + t.
 // The structure is k_apply_nc's: waves own 32-column output blocks (and, for
@@ -74,12 +78,12 @@ constexpr int kApplyThreads = 256;
 template <int D, int KIND>
 __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
     const uint16_t *__restrict__ X, const uint16_t *__restrict__ X2, uint16_t *__restrict__ Out,
-    uint16_t *__restrict__ Out2, float *__restrict__ den_out, const float *__restrict__ rec,
-    int64_t N, int64_t seg_len, int nseg)
+    uint16_t *__restrict__ Out2, float *__restrict__ den_out, float *__restrict__ cbuf,
+    const float *__restrict__ rec, int64_t N, int64_t seg_len, int nseg)
 {
     typedef nc::IO<StBF16> io;
     static_assert(D >= 32 && D <= 128, "32-column output blocks");
-    static_assert(KIND == 0 || KIND == 2, "forward or dK | dV");
+    static_assert(KIND >= 0 && KIND <= 2, "forward, dQ or dK | dV");
     constexpr int KS = D / 16;               // k-steps of 16
     constexpr int NWAVE = kApplyThreads / 64;
     constexpr int NCB = D / 32;
@@ -89,8 +93,12 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
     constexpr int CPR = D / 8;               // 16-byte chunks per row
     constexpr int PER = TR * CPR / kApplyThreads;
     static_assert(PER >= 1 && TR * CPR % kApplyThreads == 0, "staging split");
+    constexpr bool DQ = (KIND == 1);
     __shared__ __attribute__((aligned(16))) uint16_t xs[2][TR * LDX];
-    __shared__ __attribute__((aligned(16))) float vz[KIND == 0 ? D : 4];
+    __shared__ __attribute__((aligned(16))) uint16_t qs[DQ ? 2 : 1][DQ ? TR * LDX : 8];
+    __shared__ __attribute__((aligned(16))) float vz[KIND <= 1 ? D : 4];
+    __shared__ __attribute__((aligned(16))) float vu[DQ ? D : 4];
+    __shared__ float xch[DQ ? 2 : 1][NRG][NCB][32];
 
     const int sub = (KIND == 2) ? (int)(blockIdx.x & 1) : 0;
     const int64_t b = (KIND == 2) ? (blockIdx.x >> 1) : blockIdx.x;
@@ -104,18 +112,26 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
     const float *st = rec + bh * (int64_t)(D * D + 2 * D);
     const bool colread = (KIND == 0) || (KIND == 2 && sub == 1);
     const uint16_t *xh = ((KIND == 2 && sub == 1) ? X2 : X) + hoff;
+    const uint16_t *qh = DQ ? X2 + hoff : nullptr;
     uint16_t *oh = ((KIND == 2 && sub == 1) ? Out2 : Out) + hoff;
 
-    uint4 stg[PER];
+    uint4 stg[PER], stq[DQ ? PER : 1];
     auto fetch_round = [&](int64_t r0) {
         const int rows = (int)(end - r0 < TR ? end - r0 : TR);
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t *>(xh + r0 * D), (short)0, rows * D * 2, kBufferWord3);
+        __amdgpu_buffer_rsrc_t rq;
+        if constexpr (DQ)
+            rq = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(qh + r0 * D), (short)0,
+                                                   rows * D * 2, kBufferWord3);
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
             const int c = tid + p * kApplyThreads;
-            stg[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                   rs, (c / CPR) * D * 2 + 16 * (c % CPR), 0, 0));
+            const int off = (c / CPR) * D * 2 + 16 * (c % CPR);
+            stg[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+            if constexpr (DQ)
+                stq[p] =
+                    __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
         }
     };
     auto stage_round = [&](int buf) {
@@ -123,6 +139,8 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
         for (int p = 0; p < PER; ++p) {
             const int c = tid + p * kApplyThreads;
             *reinterpret_cast<uint4 *>(&xs[buf][(c / CPR) * LDX + 8 * (c % CPR)]) = stg[p];
+            if constexpr (DQ)
+                *reinterpret_cast<uint4 *>(&qs[buf][(c / CPR) * LDX + 8 * (c % CPR)]) = stq[p];
         }
     };
 
@@ -158,7 +176,7 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
         }
     }
     // epilogue vector at the lane's output columns 32*cb + 8*q + 4*h + (0..3):
-    // u (forward), -r (dK) or t (dV)
+    // u (forward), z (dQ), -r (dK) or t (dV)
     f4 ev[4];
     {
         const float *vec = st + D * D + ((KIND == 0 || (KIND == 2 && sub == 1)) ? D : 0);
@@ -167,9 +185,12 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
         for (int q = 0; q < 4; ++q)
             ev[q] = sgn * *reinterpret_cast<const f4 *>(vec + 32 * cb + 8 * q + 4 * h);
     }
-    if constexpr (KIND == 0)
-        for (int e = tid; e < D; e += kApplyThreads)
+    if constexpr (KIND <= 1)
+        for (int e = tid; e < D; e += kApplyThreads) {
             vz[e] = st[D * D + e];
+            if constexpr (DQ)
+                vu[e] = st[D * D + D + e];
+        }
     stage_round(0);
     drain_loads();
     if (nrounds > 1)
@@ -189,8 +210,9 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
         const uint16_t *xt = &xs[buf][(32 * rg + j) * LDX + 8 * h];
         int zo = 8 * h;
         asm volatile("" : "+v"(zo));  // z reads stay in the loop
+        const uint16_t *qt = DQ ? &qs[buf][(32 * rg + j) * LDX + 8 * h] : nullptr;
         f16v acc = zero16();
-        float qz = 0.f;
+        float qz = 0.f, gu = 0.f;
         bf8 xn = *reinterpret_cast<const bf8 *>(xt);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -207,6 +229,20 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
                 qz += dot4(f4{xf[0], xf[1], xf[2], xf[3]}, z0) +
                       dot4(f4{xf[4], xf[5], xf[6], xf[7]}, z1);
                 asm volatile("" : "+v"(qz));
+            } else if constexpr (DQ) {
+                // g.u from the operand, q.z from the same columns of q
+                float xf[8], qf[8];
+                unpack8(x, xf);
+                unpack8(*reinterpret_cast<const bf8 *>(qt + 16 * ks), qf);
+                const f4 z0 = *reinterpret_cast<const f4 *>(&vz[zo + 16 * ks]);
+                const f4 z1 = *reinterpret_cast<const f4 *>(&vz[zo + 16 * ks + 4]);
+                const f4 u0 = *reinterpret_cast<const f4 *>(&vu[zo + 16 * ks]);
+                const f4 u1 = *reinterpret_cast<const f4 *>(&vu[zo + 16 * ks + 4]);
+                qz += dot4(f4{qf[0], qf[1], qf[2], qf[3]}, z0) +
+                      dot4(f4{qf[4], qf[5], qf[6], qf[7]}, z1);
+                gu += dot4(f4{xf[0], xf[1], xf[2], xf[3]}, u0) +
+                      dot4(f4{xf[4], xf[5], xf[6], xf[7]}, u1);
+                asm volatile("" : "+v"(qz), "+v"(gu));
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -226,11 +262,26 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
                              (acc[4 * q + 2] + ev[q][2]) * inv, (acc[4 * q + 3] + ev[q][3]) * inv};
             if (den_out != nullptr && row < end && h == 0 && cb == 0)
                 den_out[bh * N + row] = den;
-        } else {
+        } else if constexpr (KIND == 2) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 pend[q] = f4{acc[4 * q] + ev[q][0], acc[4 * q + 1] + ev[q][1],
                              acc[4 * q + 2] + ev[q][2], acc[4 * q + 3] + ev[q][3]};
+        } else {
+            // q.y over this block's 32 output columns, summed across blocks below
+            const uint16_t *qr = &qs[buf][(32 * rg + j) * LDX + 32 * cb + 4 * h];
+            float p = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint2 u = *reinterpret_cast<const uint2 *>(qr + 8 * q);
+                p += __uint_as_float(u.x << 16) * acc[4 * q] +
+                     __uint_as_float(u.x & 0xffff0000u) * acc[4 * q + 1] +
+                     __uint_as_float(u.y << 16) * acc[4 * q + 2] +
+                     __uint_as_float(u.y & 0xffff0000u) * acc[4 * q + 3];
+            }
+            p += __shfl_xor(p, 32, 64);
+            if (h == 0)
+                xch[buf][rg][cb][j] = p;
         }
         prow = row;
         pok = row < end;
@@ -240,6 +291,23 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
                 fetch_round(beg + (round + 2) * TR);
         }
         __syncthreads();
+        if constexpr (DQ) {
+            float qy = 0.f;
+#pragma unroll
+            for (int c2 = 0; c2 < NCB; ++c2)
+                qy += xch[buf][rg][c2][j];
+            qz += __shfl_xor(qz, 32, 64);
+            gu += __shfl_xor(gu, 32, 64);
+            const float inv = 1.f / ((float)N + qz);
+            const float c = (gu + qy) * inv * inv;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                pend[q] = f4{acc[4 * q] * inv - c * ev[q][0], acc[4 * q + 1] * inv - c * ev[q][1],
+                             acc[4 * q + 2] * inv - c * ev[q][2],
+                             acc[4 * q + 3] * inv - c * ev[q][3]};
+            if (pok && h == 0 && cb == 0)
+                reinterpret_cast<float2 *>(cbuf)[bh * N + row] = float2{c, inv};
+        }
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q)
