@@ -99,6 +99,12 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
     __shared__ __attribute__((aligned(16))) float vz[KIND <= 1 ? D : 4];
     __shared__ __attribute__((aligned(16))) float vu[DQ ? D : 4];
     __shared__ float xch[DQ ? 2 : 1][NRG][NCB][32];
+    // output rows of a round (bf16), stored as whole rows by the workgroup
+    // LAG rounds later: the forward and dK | dV tiles are complete at the
+    // round's barrier, the dQ tile only after the next one
+    constexpr int LAG = DQ ? 2 : 1;
+    constexpr int OCH = TR * CPR / kApplyThreads;  // 16-byte output chunks per thread
+    __shared__ __attribute__((aligned(16))) uint16_t ot[2][TR * LDX];
 
     const int sub = (KIND == 2) ? (int)(blockIdx.x & 1) : 0;
     const int64_t b = (KIND == 2) ? (blockIdx.x >> 1) : blockIdx.x;
@@ -197,12 +203,24 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
         fetch_round(beg + TR);
     __syncthreads();
 
-    f4 pend[4];
-    int64_t prow = 0;
-    bool pok = false;
-    auto store_pending = [&](int q) {
-        if (pok)
-            io::store4(oh + prow * D + 32 * cb + 8 * q + 4 * h, pend[q]);
+    // this lane's 4 x 4 output values of a round into its tile
+    auto put_tile = [&](int tb, const f4 *o) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint2 r;
+            r.x = (uint32_t)StBF16::narrow(o[q][0]) | ((uint32_t)StBF16::narrow(o[q][1]) << 16);
+            r.y = (uint32_t)StBF16::narrow(o[q][2]) | ((uint32_t)StBF16::narrow(o[q][3]) << 16);
+            *reinterpret_cast<uint2 *>(&ot[tb][(32 * rg + j) * LDX + 32 * cb + 8 * q + 4 * h]) = r;
+        }
+    };
+    // chunk p of round rr's tile to global memory (16 bytes per lane;
+    // consecutive lanes cover consecutive 16-byte pieces of a row)
+    auto store_tile = [&](int64_t rr, int p) {
+        const int c = tid + p * kApplyThreads;
+        const int64_t grow = beg + rr * TR + c / CPR;
+        if (grow < end)
+            *reinterpret_cast<uint4 *>(oh + grow * D + 8 * (c % CPR)) =
+                *reinterpret_cast<const uint4 *>(&ot[(int)(rr & 1)][(c / CPR) * LDX + 8 * (c % CPR)]);
     };
 
     for (int64_t round = 0; round < nrounds; ++round) {
@@ -245,13 +263,14 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
                 asm volatile("" : "+v"(qz), "+v"(gu));
             }
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if (ks == (q * KS) / 4)
-                    store_pending(q);
+            for (int p = 0; p < OCH; ++p)
+                if (round >= LAG && ks == (p * KS) / OCH)
+                    store_tile(round - LAG, p);
             __builtin_amdgcn_sched_barrier(0);
         }
 
         const int64_t row = beg + round * TR + 32 * rg + j;
+        f4 pend[4];
         if constexpr (KIND == 0) {
             qz += __shfl_xor(qz, 32, 64);
             const float den = (float)N + qz;
@@ -262,11 +281,13 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
                              (acc[4 * q + 2] + ev[q][2]) * inv, (acc[4 * q + 3] + ev[q][3]) * inv};
             if (den_out != nullptr && row < end && h == 0 && cb == 0)
                 den_out[bh * N + row] = den;
+            put_tile(buf, pend);
         } else if constexpr (KIND == 2) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 pend[q] = f4{acc[4 * q] + ev[q][0], acc[4 * q + 1] + ev[q][1],
                              acc[4 * q + 2] + ev[q][2], acc[4 * q + 3] + ev[q][3]};
+            put_tile(buf, pend);
         } else {
             // q.y over this block's 32 output columns, summed across blocks below
             const uint16_t *qr = &qs[buf][(32 * rg + j) * LDX + 32 * cb + 4 * h];
@@ -283,8 +304,6 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
             if (h == 0)
                 xch[buf][rg][cb][j] = p;
         }
-        prow = row;
-        pok = row < end;
         if (round + 1 < nrounds) {
             stage_round(buf ^ 1);
             if (round + 2 < nrounds)
@@ -305,13 +324,16 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
                 pend[q] = f4{acc[4 * q] * inv - c * ev[q][0], acc[4 * q + 1] * inv - c * ev[q][1],
                              acc[4 * q + 2] * inv - c * ev[q][2],
                              acc[4 * q + 3] * inv - c * ev[q][3]};
-            if (pok && h == 0 && cb == 0)
+            if (row < end && h == 0 && cb == 0)
                 reinterpret_cast<float2 *>(cbuf)[bh * N + row] = float2{c, inv};
+            put_tile(buf, pend);
         }
     }
+    __syncthreads();
+    for (int64_t rr = nrounds - LAG < 0 ? 0 : nrounds - LAG; rr < nrounds; ++rr)
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-        store_pending(q);
+        for (int p = 0; p < OCH; ++p)
+            store_tile(rr, p);
 }
 
 // ============================================================ reduction
