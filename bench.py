@@ -31,9 +31,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "LA fwd+bwd tokens/s at B4 H16 D128 N4096; % of binding HBM/FLOP roofline"
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix (= fp32 vector) peak
+PEAK_BF16_MFMA_TFLOPS = 2516.6  # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 KERNEL_SOURCES = [os.path.join(ROOT, "linear_attention_transformer_amd", "csrc", f)
                   for f in ("la_kernels.hpp", "la_kernels_nc.hpp", "la_kernels_causal.hpp",
+                            "la_kernels_bf16.hpp",
                             "la_api.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_MIB = 256                  # plain streaming kernel: reads and writes this much
@@ -166,6 +168,46 @@ def copy_reference(dev):
     return 2 * (COPY_MIB << 20) / t / 1e9
 
 
+def uses_bf16_mfma(dtype, D, causal):
+    """Whether every kernel of the path computes on the bf16 matrix cores
+    (bf16 storage, 32 <= D <= 128, non-causal); otherwise fp32 matrix cores."""
+    return dtype == "bf16" and 32 <= D <= 128 and not causal
+
+
+def step_floor_us(B, H, N, D, s, bf16_mfma):
+    """Roofline time of one fwd+bwd step: algorithmic bytes at the HBM peak
+    against algorithmic flops at the matrix peak of the operand type."""
+    flops, nbytes = 12 * B * H * N * D * D, 11 * B * H * N * D * s
+    peak = PEAK_BF16_MFMA_TFLOPS if bf16_mfma else PEAK_FP32_MFMA_TFLOPS
+    return 1e6 * max(flops / (peak * 1e12), nbytes / (PEAK_HBM_GBS * 1e9))
+
+
+def time_variant(la, make_inputs, dev, B, H, N, D, dtype, causal, steps, warmup):
+    """ms per fwd+bwd step of another storage type / mask at the same shape
+    (same protocol as the headline: warm-up, then steps between two events)."""
+    import torch
+    q, k, v, g = make_inputs(B, H, N, D, dtype=dtype, seed=0, device=dev, draw_device=dev)
+    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+    ws = la.alloc_workspace(B, H, N, D, causal, dev)
+    st = torch.empty(max(la.state_size(B, H, N, D, causal) // 4, 4), dtype=torch.float32,
+                     device=dev)
+
+    def step():
+        la.forward(q, k, v, causal, out=o, state_out=st, workspace=ws)
+        la.backward(q, k, v, g, causal, state=st, outs=(dq, dk, dv), workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def cpu_baseline(q, k, v, g, causal):
     import oracle
     from linear_attention_transformer_amd.inputs import as_f64_numpy
@@ -207,6 +249,8 @@ def main():
     ap.add_argument("--N", type=int, default=4096)
     ap.add_argument("--D", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the other storage type / mask at the same shape")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs of this script (FETCH_SIZE, "
                          "WRITE_SIZE) for the given workload into profiles/traffic.json; "
@@ -291,11 +335,13 @@ def main():
     fused = "grad_state_local" not in per_kernel   # dQ kernel also reduces dS
     flops, nbytes = algorithmic(dom, B * H, N, D, s, fused)
     t_dom = avg_us[dom] * 1e-6
-    ridge = PEAK_FP32_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    bf16_mfma = uses_bf16_mfma(args.dtype, D, causal)
+    mpeak = PEAK_BF16_MFMA_TFLOPS if bf16_mfma else PEAK_FP32_MFMA_TFLOPS
+    ridge = mpeak * 1e12 / (PEAK_HBM_GBS * 1e9)
     if nbytes and flops / nbytes < ridge:
         bound, achieved, peak, unit = "hbm", nbytes / t_dom / 1e9, PEAK_HBM_GBS, "GB/s"
     else:
-        bound, achieved, peak, unit = "mfma", flops / t_dom / 1e12, PEAK_FP32_MFMA_TFLOPS, "TFLOP/s"
+        bound, achieved, peak, unit = "mfma", flops / t_dom / 1e12, mpeak, "TFLOP/s"
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -308,12 +354,30 @@ def main():
                 "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom,
                 "kernel_avg_us": round(avg_us[dom], 2),
                 "algorithmic_per_launch": {"flops": flops, "bytes": nbytes}}
-    total_flops = 12 * B * H * N * D * D
-    total_bytes = 11 * B * H * N * D * s
-    step_floor_us = 1e6 * max(total_flops / (PEAK_FP32_MFMA_TFLOPS * 1e12),
-                              total_bytes / (PEAK_HBM_GBS * 1e9))
+    floor_us = step_floor_us(B, H, N, D, s, bf16_mfma)
     print("bench: per-kernel us/launch " + ", ".join("%s=%.1f" % kv for kv in avg_us.items()),
           file=sys.stderr, flush=True)
+
+    # the other storage type and mask at the same shape, each timed like the
+    # headline (bf16 storage runs on the bf16 matrix cores for 32 <= D <= 128)
+    variants = {}
+    if not args.no_variants:
+        del o, dq, dk, dv, ws, st
+        torch.cuda.empty_cache()
+        for vdt in ("fp32", "bf16"):
+            for vc in (False, True):
+                if vdt == args.dtype and vc == causal:
+                    continue
+                tdt = torch.float32 if vdt == "fp32" else torch.bfloat16
+                vms = time_variant(la, make_inputs, dev, B, H, N, D, tdt, vc,
+                                   max(args.steps // 2, 5), 3)
+                vs = 4 if vdt == "fp32" else 2
+                fl = step_floor_us(B, H, N, D, vs, uses_bf16_mfma(vdt, D, vc))
+                variants["%s %s" % (vdt, "causal" if vc else "non-causal")] = {
+                    "ms_per_step": round(vms, 4), "tokens_per_s": round(B * N / (vms * 1e-3), 1),
+                    "step_floor_us": round(fl, 1), "step_frac": round(fl / (vms * 1e3), 4)}
+                print("bench: variant %s %s: %.3f ms/step" % (vdt, "causal" if vc else
+                      "non-causal", vms), file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -332,7 +396,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16" if bf16_mfma else "f32",
         "data": "synthetic",
         "config": {"workload": "LA forward+backward, B=%d H=%d N=%d D=%d, %s storage, %s"
                                % (B, H, N, D, args.dtype, "causal" if causal else "non-causal"),
@@ -340,11 +404,12 @@ def main():
                    "global_batch": B, "seq_len": N},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "step_roofline": {"floor_us": round(step_floor_us, 1),
-                          "frac": round(step_floor_us / (ms * 1e3), 4)},
+        "step_roofline": {"floor_us": round(floor_us, 1),
+                          "frac": round(floor_us / (ms * 1e3), 4)},
         "kernels_us_per_launch": {n: round(t, 2) for n, t in avg_us.items()},
         "traced_ms_per_step": round(traced_ms, 4),
         "hbm_copy_GBs": round(copy_gbs, 1),
+        "variants": variants,
     }
     print(json.dumps(line), flush=True)
 
