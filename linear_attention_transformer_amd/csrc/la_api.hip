@@ -240,10 +240,18 @@ int run_forward(const void *Q, const void *K, const void *V, void *O, float *den
                         den_out, rec, p.N, p.seg_len, (int)p.nseg);
             });
         return traced(t, s, "forward", [&] {
-            cz::k_fwd_causal<ST, D><<<dim3((unsigned)(p.nseg * p.BH)), dim3(cz::threads<D>()), 0,
-                                      s>>>(
-                static_cast<const T *>(Q), static_cast<const T *>(K), static_cast<const T *>(V),
-                static_cast<T *>(O), den_out, rec, p.N, p.seg_len, (int)p.nseg);
+            if constexpr (std::is_same<ST, StBF16>::value)
+                bf::k_fwd_causal_bf<D><<<dim3((unsigned)(p.nseg * p.BH)),
+                                         dim3(cz::threads<D>()), 0, s>>>(
+                    static_cast<const T *>(Q), static_cast<const T *>(K),
+                    static_cast<const T *>(V), static_cast<T *>(O), den_out, rec, p.N, p.seg_len,
+                    (int)p.nseg);
+            else
+                cz::k_fwd_causal<ST, D><<<dim3((unsigned)(p.nseg * p.BH)),
+                                          dim3(cz::threads<D>()), 0, s>>>(
+                    static_cast<const T *>(Q), static_cast<const T *>(K),
+                    static_cast<const T *>(V), static_cast<T *>(O), den_out, rec, p.N, p.seg_len,
+                    (int)p.nseg);
         });
     }
     const dim3 grid((unsigned)(p.nseg * p.BH * C::CS));

@@ -564,5 +564,319 @@ __global__ __launch_bounds__(256) void k_reduce_bf(
     }
 }
 
+// ============================================================ causal
+// The causal kernels of la_kernels_causal.hpp on the bf16 matrix cores, same
+// chunking (C = 32 rows) and state layout: wave cb holds its D x 32 slice of
+// the running state as fp32 accumulators st[t][i] <-> state[32 t + 8 (i/4) +
+// 4 h + i % 4][32 cb + j].  For the bf16 MFMA the k-slots of lane (j, h) at
+// k-step 2 t + p are taken as accumulator elements 8 p .. 8 p + 7 of st[t],
+// i.e. d = 32 t + 16 p + 4 h + {0..3, 8..11}; the state operand is their
+// hi/lo bf16 split (re-split every chunk, as the state changes), and the row
+// operand is the row's bf16 values at the same d (two 8-byte LDS reads).
+// Products over the chunk's tokens (the in-chunk block and the state update)
+// read 8 consecutive tokens of a column from transposed LDS tiles.
+
+constexpr int kCc = 32;            // rows per chunk
+constexpr int kRT = kCc + 8;       // bf16 pitch of a transposed column
+
+// the 8 bf16 of row r at d = d0 + {0..3, 8..11} (d0 = 32 t + 16 p + 4 h)
+__device__ __forceinline__ bf8 row_at(const uint16_t *row, int d0)
+{
+    const uint2 a = *reinterpret_cast<const uint2 *>(row + d0);
+    const uint2 b = *reinterpret_cast<const uint2 *>(row + d0 + 8);
+    return __builtin_bit_cast(bf8, uint4{a.x, a.y, b.x, b.y});
+}
+
+// hi/lo bf16 operands of accumulator elements 8p .. 8p + 7 of a
+__device__ __forceinline__ void split8(const f16v &a, int p, bf8 &hi, bf8 &lo)
+{
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        __bf16 x, y;
+        split_bf16(a[8 * p + s], x, y);
+        hi[s] = x;
+        lo[s] = y;
+    }
+}
+
+// Staging of one chunk: item q = tid (+ NT) covers token pair pr = q % 16
+// and 8-column chunk q / 16; loads two 16-byte pieces through a descriptor
+// limited to the chunk's valid rows (zeros past the end).
+template <int D, int NT>
+struct ChunkRows {
+    static constexpr int CH = D / 8;
+    static constexpr int PC = (kCc / 2) * CH;
+    static constexpr int PER = (PC + NT - 1) / NT;
+    static constexpr int LDX = D + 8;  // bf16 pitch of a natural row
+    uint4 r[PER][2];
+
+    __device__ __forceinline__ void fetch(const uint16_t *src, int64_t r0, int64_t end, int tid)
+    {
+        const int rows = (int)(end - r0 < kCc ? end - r0 : kCc);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(src + r0 * D), (short)0, rows * D * 2, kBufferWord3);
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int q = tid + p * NT;
+            if (PC % NT == 0 || q < PC) {
+                const int chunk = q / (kCc / 2), pr = q % (kCc / 2);
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+                    r[p][u] = __builtin_bit_cast(
+                        uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                   rs, (2 * pr + u) * D * 2 + 16 * chunk, 0, 0));
+            }
+        }
+    }
+    // natural rows [token][d]
+    __device__ __forceinline__ void stage_nat(uint16_t *lds, int tid) const
+    {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int q = tid + p * NT;
+            if (PC % NT == 0 || q < PC) {
+                const int chunk = q / (kCc / 2), pr = q % (kCc / 2);
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+                    *reinterpret_cast<uint4 *>(&lds[(2 * pr + u) * LDX + 8 * chunk]) = r[p][u];
+            }
+        }
+    }
+    // transposed [d][token], tokens 2 pr, 2 pr + 1 packed per 32-bit write
+    __device__ __forceinline__ void stage_tr(uint16_t *lds, int tid) const
+    {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int q = tid + p * NT;
+            if (PC % NT == 0 || q < PC) {
+                const int chunk = q / (kCc / 2), pr = q % (kCc / 2);
+                const uint32_t *w0 = reinterpret_cast<const uint32_t *>(&r[p][0]);
+                const uint32_t *w1 = reinterpret_cast<const uint32_t *>(&r[p][1]);
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const uint32_t a = (s & 1) ? (w0[s / 2] >> 16) : (w0[s / 2] & 0xffffu);
+                    const uint32_t b = (s & 1) ? (w1[s / 2] >> 16) : (w1[s / 2] & 0xffffu);
+                    *reinterpret_cast<uint32_t *>(&lds[(8 * chunk + s) * kRT + 2 * pr]) =
+                        a | (b << 16);
+                }
+            }
+        }
+    }
+};
+
+// 8 consecutive tokens (16 kk + 8 h ..) of column c of a transposed tile
+__device__ __forceinline__ bf8 col_at(const uint16_t *ldsT, int c, int kk, int h)
+{
+    return *reinterpret_cast<const bf8 *>(&ldsT[c * kRT + 16 * kk + 8 * h]);
+}
+
+// this wave's share of X_c Y_c^T over columns 32 cb .. 32 cb + 31 (natural
+// rows), written to sh[i * (kCc + 1) + jj]
+template <int D>
+__device__ __forceinline__ void share_bf(const uint16_t *xs, const uint16_t *ys, float *sh,
+                                         int cb, int j, int h)
+{
+    constexpr int LDX = D + 8, WP = kCc + 1;
+    f16v a = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const bf8 x = *reinterpret_cast<const bf8 *>(&xs[j * LDX + 32 * cb + 16 * ks + 8 * h]);
+        const bf8 y = *reinterpret_cast<const bf8 *>(&ys[j * LDX + 32 * cb + 16 * ks + 8 * h]);
+        a = mma16(x, y, a);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+        sh[(8 * (e / 4) + 4 * h + (e % 4)) * WP + j] = a[e];
+}
+
+// Forward (as cz::k_fwd_causal): per chunk (1) acc = S^T-block . Q_c^T and
+// q.z; (2) share of Q_c K_c^T; barrier; (3) acc += V_c-block^T . W^T with W
+// masked and the constant added (its row sums go to den), st += K_c^T .
+// V_c-block; (4) normalised rows.
+template <int D>
+__global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal_bf(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ den_out,
+    const float *__restrict__ rec, int64_t N, int64_t seg_len, int nseg)
+{
+    typedef nc::IO<StBF16> io;
+    static_assert(D >= 32 && D <= 128, "32-column blocks, state in registers");
+    constexpr int NCB = D / 32, NT = 64 * NCB, LDX = D + 8, WP = kCc + 1;
+    __shared__ __attribute__((aligned(16))) uint16_t qs[kCc * LDX];
+    __shared__ __attribute__((aligned(16))) uint16_t ks[kCc * LDX];
+    __shared__ __attribute__((aligned(16))) uint16_t kT[D * kRT];
+    __shared__ __attribute__((aligned(16))) uint16_t vT[D * kRT];
+    __shared__ float wx[NCB][kCc * WP];
+    __shared__ __attribute__((aligned(16))) float vz[D];
+    __shared__ __attribute__((aligned(16))) float vu[D];
+
+    const int64_t bh = blockIdx.x / nseg;
+    const int seg = (int)(blockIdx.x % nseg);
+    const int tid = threadIdx.x, cb = tid >> 6, lane = tid & 63, j = lane & 31, h = lane >> 5;
+    const int64_t beg = (int64_t)seg * seg_len;
+    const int64_t end = (beg + seg_len < N) ? beg + seg_len : N;
+    const int64_t hoff = bh * N * D;
+    const float *st = rec + (bh * nseg + seg) * (int64_t)(D * D + 2 * D);
+    const uint16_t *qh = Q + hoff, *kh = K + hoff, *vh = V + hoff;
+    uint16_t *oh = O + hoff;
+
+    ChunkRows<D, NT> rq, rk, rv;
+    const int64_t nrounds = (end - beg + kCc - 1) / kCc;
+    rq.fetch(qh, beg, end, tid);
+    rk.fetch(kh, beg, end, tid);
+    rv.fetch(vh, beg, end, tid);
+    f16v sacc[NCB];
+#pragma unroll
+    for (int t = 0; t < NCB; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            sacc[t][i] = st[(32 * t + 8 * (i / 4) + 4 * h + (i % 4)) * D + 32 * cb + j];
+    for (int e = tid; e < D; e += NT) {
+        vz[e] = st[D * D + e];
+        vu[e] = st[D * D + D + e];
+    }
+    rq.stage_nat(qs, tid);
+    rk.stage_nat(ks, tid);
+    rk.stage_tr(kT, tid);
+    rv.stage_tr(vT, tid);
+    drain_loads();
+    if (nrounds > 1)
+        rq.fetch(qh, beg + kCc, end, tid);
+    __syncthreads();
+
+    f4 pend[4];
+    int64_t prow = 0;
+    bool pok = false;
+    auto store_pending = [&](int q) {
+        if (pok)
+            io::store4(oh + prow * D + 32 * cb + 8 * q + 4 * h, pend[q]);
+    };
+
+    for (int64_t round = 0; round < nrounds; ++round) {
+        const int64_t t0 = beg + round * kCc;
+        const bool more = round + 1 < nrounds;
+        // (1) the prefix state applied to the chunk's queries, and q.z
+        f16v acc = zero16();
+        float qz = 0.f;
+        {
+            const uint16_t *qrow = &qs[j * LDX];
+            int zo = 4 * h;
+            asm volatile("" : "+v"(zo));  // z changes per chunk: keep its reads here
+#pragma unroll
+            for (int t = 0; t < NCB; ++t)
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    const int d0 = 32 * t + 16 * p;
+                    const bf8 x = row_at(qrow, d0 + 4 * h);
+                    bf8 ahi, alo;
+                    split8(sacc[t], p, ahi, alo);
+                    acc = mma16(ahi, x, acc);
+                    acc = mma16(alo, x, acc);
+                    float xf[8];
+                    unpack8(x, xf);
+                    const f4 z0 = *reinterpret_cast<const f4 *>(&vz[zo + d0]);
+                    const f4 z1 = *reinterpret_cast<const f4 *>(&vz[zo + d0 + 8]);
+                    qz += dot4(f4{xf[0], xf[1], xf[2], xf[3]}, z0) +
+                          dot4(f4{xf[4], xf[5], xf[6], xf[7]}, z1);
+                    asm volatile("" : "+v"(qz));
+                    if (t == 0 && p == 0) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            store_pending(q);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+        }
+        // (2) this wave's share of Q_c K_c^T
+        share_bf<D>(qs, ks, wx[cb], cb, j, h);
+        __syncthreads();  // B1
+        if (more)
+            rq.stage_nat(qs, tid);  // Q is read only before B1
+        if (more) {
+            rk.fetch(kh, t0 + kCc, end, tid);
+            rv.fetch(vh, t0 + kCc, end, tid);
+        }
+        // (3) in-chunk term over key rows 16 kk + 8 h .. and the state update
+        float rs = 0.f, zc = 0.f, uc = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < kCc / 16; ++kk) {
+            // W[j][16 kk + 8 h + s], masked, + 1
+            float wm[8];
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const int jr = 16 * kk + 8 * h + s;
+                float w = 0.f;
+#pragma unroll
+                for (int pp = 0; pp < NCB; ++pp)
+                    w += wx[pp][j * WP + jr];
+                wm[s] = (jr <= j) ? 1.f + w : 0.f;
+                rs += wm[s];
+            }
+            bf8 whi, wlo;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                __bf16 x, y;
+                split_bf16(wm[s], x, y);
+                whi[s] = x;
+                wlo[s] = y;
+            }
+            const bf8 vcol = col_at(vT, 32 * cb + j, kk, h);  // V[16kk+8h..][32cb+j]
+            acc = mma16(vcol, whi, acc);
+            acc = mma16(vcol, wlo, acc);
+#pragma unroll
+            for (int t = 0; t < NCB; ++t) {
+                const bf8 kcol = col_at(kT, 32 * t + j, kk, h);
+                sacc[t] = mma16(kcol, vcol, sacc[t]);
+                if (t == cb) {
+                    float kf[8];
+                    unpack8(kcol, kf);
+#pragma unroll
+                    for (int s = 0; s < 8; ++s)
+                        zc += kf[s];
+                }
+            }
+            float vf[8];
+            unpack8(vcol, vf);
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                uc += vf[s];
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        rs += __shfl_xor(rs, 32, 64);
+        zc += __shfl_xor(zc, 32, 64);
+        uc += __shfl_xor(uc, 32, 64);
+        qz += __shfl_xor(qz, 32, 64);
+        // (4) normalised rows of the chunk, stored during the next product
+        const float den = (float)t0 + qz + rs;
+        const float inv = 1.f / den;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f4 u = *reinterpret_cast<const f4 *>(&vu[32 * cb + 8 * q + 4 * h]);
+            pend[q] = f4{(acc[4 * q] + u[0]) * inv, (acc[4 * q + 1] + u[1]) * inv,
+                         (acc[4 * q + 2] + u[2]) * inv, (acc[4 * q + 3] + u[3]) * inv};
+        }
+        prow = t0 + j;
+        pok = prow < end;
+        if (den_out != nullptr && pok && h == 0 && cb == 0)
+            den_out[bh * N + prow] = den;
+        __syncthreads();  // B2
+        if (h == 0) {
+            vz[32 * cb + j] += zc;
+            vu[32 * cb + j] += uc;
+        }
+        if (more) {
+            rk.stage_nat(ks, tid);
+            rk.stage_tr(kT, tid);
+            rv.stage_tr(vT, tid);
+            if (round + 2 < nrounds)
+                rq.fetch(qh, t0 + 2 * kCc, end, tid);
+        }
+        __syncthreads();  // B3
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        store_pending(q);
+}
+
 }  // namespace bf
 }  // namespace la
