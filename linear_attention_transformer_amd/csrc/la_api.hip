@@ -296,8 +296,14 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
         const dim3 g1((unsigned)(p.nseg * p.BH)), nt(cz::threads<D>());
         // dQ and (c_i, 1/den_i), chunk by chunk from the saved prefix records
         rc = traced(t, s, "bwd_q", [&] {
-            cz::k_bwd_q_causal<ST, D><<<g1, nt, 0, s>>>(q, k, v, g, static_cast<T *>(dQ), cbuf,
-                                                        fstate, p.N, p.seg_len, (int)p.nseg);
+            if constexpr (std::is_same<ST, StBF16>::value)
+                bf::k_bwd_q_causal_bf<D><<<g1, nt, 0, s>>>(q, k, v, g, static_cast<T *>(dQ),
+                                                           cbuf, fstate, p.N, p.seg_len,
+                                                           (int)p.nseg);
+            else
+                cz::k_bwd_q_causal<ST, D><<<g1, nt, 0, s>>>(q, k, v, g, static_cast<T *>(dQ),
+                                                            cbuf, fstate, p.N, p.seg_len,
+                                                            (int)p.nseg);
         });
         if (rc != LA_OK)
             return rc;

@@ -878,5 +878,252 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal_bf(
         store_pending(q);
 }
 
+// dQ (as cz::k_bwd_q_causal): st[t] = S^T[32t.., 32cb..]; per chunk
+// (1) acc = S-block . G_c^T with g.u and q.z; (2) shares of Q_c K_c^T and
+// G_c V_c^T, q.y over the wave's columns; barrier; (3) den, c, then acc +=
+// K_c-block^T . P^T (P = GV - c den, masked) and st += V_c^T . K_c-block;
+// (4) dq rows and cbuf = (c, 1/den).
+template <int D>
+__global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const uint16_t *__restrict__ G, uint16_t *__restrict__ dQ,
+    float *__restrict__ cbuf, const float *__restrict__ rec, int64_t N, int64_t seg_len,
+    int nseg)
+{
+    typedef nc::IO<StBF16> io;
+    static_assert(D >= 32 && D <= 128, "32-column blocks, state in registers");
+    constexpr int NCB = D / 32, NT = 64 * NCB, LDX = D + 8, WP = kCc + 1;
+    __shared__ __attribute__((aligned(16))) uint16_t qs[kCc * LDX];
+    __shared__ __attribute__((aligned(16))) uint16_t gs[kCc * LDX];
+    __shared__ __attribute__((aligned(16))) uint16_t ks[kCc * LDX];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[kCc * LDX];
+    __shared__ __attribute__((aligned(16))) uint16_t kT[D * kRT];
+    __shared__ __attribute__((aligned(16))) uint16_t vT[D * kRT];
+    __shared__ float wx[NCB][kCc * WP];  // shares of Q_c K_c^T
+    __shared__ float gx[NCB][kCc * WP];  // shares of G_c V_c^T
+    __shared__ float xq[NCB][kCc];       // shares of q_i.y_i
+    __shared__ __attribute__((aligned(16))) float vz[D];
+    __shared__ __attribute__((aligned(16))) float vu[D];
+
+    const int64_t bh = blockIdx.x / nseg;
+    const int seg = (int)(blockIdx.x % nseg);
+    const int tid = threadIdx.x, cb = tid >> 6, lane = tid & 63, j = lane & 31, h = lane >> 5;
+    const int64_t beg = (int64_t)seg * seg_len;
+    const int64_t end = (beg + seg_len < N) ? beg + seg_len : N;
+    const int64_t hoff = bh * N * D;
+    const float *st = rec + (bh * nseg + seg) * (int64_t)(D * D + 2 * D);
+    const uint16_t *qh = Q + hoff, *kh = K + hoff, *vh = V + hoff, *gh = G + hoff;
+    uint16_t *oh = dQ + hoff;
+
+    ChunkRows<D, NT> rq, rg, rk, rv;
+    const int64_t nrounds = (end - beg + kCc - 1) / kCc;
+    rq.fetch(qh, beg, end, tid);
+    rg.fetch(gh, beg, end, tid);
+    rk.fetch(kh, beg, end, tid);
+    rv.fetch(vh, beg, end, tid);
+    // sacc[t][4q + r] = S[32cb + j][32t + 8q + 4h + r]
+    f16v sacc[NCB];
+#pragma unroll
+    for (int t = 0; t < NCB; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f4 v = *reinterpret_cast<const f4 *>(st + (32 * cb + j) * D + 32 * t + 8 * q +
+                                                       4 * h);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sacc[t][4 * q + r] = v[r];
+        }
+    for (int e = tid; e < D; e += NT) {
+        vz[e] = st[D * D + e];
+        vu[e] = st[D * D + D + e];
+    }
+    rq.stage_nat(qs, tid);
+    rg.stage_nat(gs, tid);
+    rk.stage_nat(ks, tid);
+    rk.stage_tr(kT, tid);
+    rv.stage_nat(vs, tid);
+    rv.stage_tr(vT, tid);
+    drain_loads();
+    if (nrounds > 1) {
+        rq.fetch(qh, beg + kCc, end, tid);
+        rg.fetch(gh, beg + kCc, end, tid);
+    }
+    __syncthreads();
+
+    f4 pend[4];
+    int64_t prow = 0;
+    bool pok = false;
+    auto store_pending = [&](int q) {
+        if (pok)
+            io::store4(oh + prow * D + 32 * cb + 8 * q + 4 * h, pend[q]);
+    };
+
+    for (int64_t round = 0; round < nrounds; ++round) {
+        const int64_t t0 = beg + round * kCc;
+        const bool more = round + 1 < nrounds;
+        // (1) y = S g for the chunk's rows, with g.u and q.z at the same columns
+        f16v acc = zero16();
+        float gu = 0.f, qz = 0.f;
+        {
+            const uint16_t *grow = &gs[j * LDX], *qrow = &qs[j * LDX];
+            int vo = 4 * h;
+            asm volatile("" : "+v"(vo));  // z and u change per chunk
+#pragma unroll
+            for (int t = 0; t < NCB; ++t)
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    const int d0 = 32 * t + 16 * p;
+                    const bf8 x = row_at(grow, d0 + 4 * h);
+                    bf8 ahi, alo;
+                    split8(sacc[t], p, ahi, alo);
+                    acc = mma16(ahi, x, acc);
+                    acc = mma16(alo, x, acc);
+                    float xf[8], qf[8];
+                    unpack8(x, xf);
+                    unpack8(row_at(qrow, d0 + 4 * h), qf);
+                    const f4 z0 = *reinterpret_cast<const f4 *>(&vz[vo + d0]);
+                    const f4 z1 = *reinterpret_cast<const f4 *>(&vz[vo + d0 + 8]);
+                    const f4 u0 = *reinterpret_cast<const f4 *>(&vu[vo + d0]);
+                    const f4 u1 = *reinterpret_cast<const f4 *>(&vu[vo + d0 + 8]);
+                    gu += dot4(f4{xf[0], xf[1], xf[2], xf[3]}, u0) +
+                          dot4(f4{xf[4], xf[5], xf[6], xf[7]}, u1);
+                    qz += dot4(f4{qf[0], qf[1], qf[2], qf[3]}, z0) +
+                          dot4(f4{qf[4], qf[5], qf[6], qf[7]}, z1);
+                    asm volatile("" : "+v"(gu), "+v"(qz));
+                    if (t == 0 && p == 0) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            store_pending(q);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+        }
+        // (2) shares of Q_c K_c^T, G_c V_c^T and q.y over this wave's columns
+        share_bf<D>(qs, ks, wx[cb], cb, j, h);
+        share_bf<D>(gs, vs, gx[cb], cb, j, h);
+        {
+            const uint16_t *qr = &qs[j * LDX + 32 * cb + 4 * h];
+            float pq = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint2 u = *reinterpret_cast<const uint2 *>(qr + 8 * q);
+                pq += __uint_as_float(u.x << 16) * acc[4 * q] +
+                      __uint_as_float(u.x & 0xffff0000u) * acc[4 * q + 1] +
+                      __uint_as_float(u.y << 16) * acc[4 * q + 2] +
+                      __uint_as_float(u.y & 0xffff0000u) * acc[4 * q + 3];
+            }
+            pq += __shfl_xor(pq, 32, 64);
+            if (h == 0)
+                xq[cb][j] = pq;
+        }
+        __syncthreads();  // B1
+        if (more) {
+            rq.stage_nat(qs, tid);  // Q and dO are read only before B1
+            rg.stage_nat(gs, tid);
+            rk.fetch(kh, t0 + kCc, end, tid);
+            rv.fetch(vh, t0 + kCc, end, tid);
+        }
+        // (3) den and c of row j, then the in-chunk term and the update over
+        // key rows 16 kk + 8 h + s
+        float gvk[kCc / 16][8];
+        float rs = 0.f, cw = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < kCc / 16; ++kk)
+#pragma unroll
+            for (int s2 = 0; s2 < 8; ++s2) {
+                const int jr = 16 * kk + 8 * h + s2;
+                float w = 0.f, gv = 0.f;
+#pragma unroll
+                for (int pp = 0; pp < NCB; ++pp) {
+                    w += wx[pp][j * WP + jr];
+                    gv += gx[pp][j * WP + jr];
+                }
+                const bool m = jr <= j;
+                const float wm = m ? 1.f + w : 0.f;
+                rs += wm;
+                cw += wm * gv;
+                gvk[kk][s2] = m ? gv : 0.f;
+            }
+        rs += __shfl_xor(rs, 32, 64);
+        cw += __shfl_xor(cw, 32, 64);
+        gu += __shfl_xor(gu, 32, 64);
+        qz += __shfl_xor(qz, 32, 64);
+        float qy = 0.f;
+#pragma unroll
+        for (int pp = 0; pp < NCB; ++pp)
+            qy += xq[pp][j];
+        const float den = (float)t0 + qz + rs;
+        const float inv = 1.f / den;
+        const float c = (gu + qy + cw) * inv * inv;
+        const float cden = c * den;
+        float zc = 0.f, uc = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < kCc / 16; ++kk) {
+            bf8 phi, plo;
+#pragma unroll
+            for (int s2 = 0; s2 < 8; ++s2) {
+                const int jr = 16 * kk + 8 * h + s2;
+                __bf16 x, y;
+                split_bf16((jr <= j) ? gvk[kk][s2] - cden : 0.f, x, y);
+                phi[s2] = x;
+                plo[s2] = y;
+            }
+            const bf8 kcol = col_at(kT, 32 * cb + j, kk, h);  // K[16kk+8h..][32cb+j]
+            acc = mma16(kcol, phi, acc);
+            acc = mma16(kcol, plo, acc);
+#pragma unroll
+            for (int t = 0; t < NCB; ++t) {
+                const bf8 vcol = col_at(vT, 32 * t + j, kk, h);
+                sacc[t] = mma16(vcol, kcol, sacc[t]);
+                if (t == cb) {
+                    float vf[8];
+                    unpack8(vcol, vf);
+#pragma unroll
+                    for (int s2 = 0; s2 < 8; ++s2)
+                        uc += vf[s2];
+                }
+            }
+            float kf[8];
+            unpack8(kcol, kf);
+#pragma unroll
+            for (int s2 = 0; s2 < 8; ++s2)
+                zc += kf[s2];
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        zc += __shfl_xor(zc, 32, 64);
+        uc += __shfl_xor(uc, 32, 64);
+        // (4) dq rows (z of the rows before the chunk)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f4 z = *reinterpret_cast<const f4 *>(&vz[32 * cb + 8 * q + 4 * h]);
+            pend[q] = f4{acc[4 * q] * inv - c * z[0], acc[4 * q + 1] * inv - c * z[1],
+                         acc[4 * q + 2] * inv - c * z[2], acc[4 * q + 3] * inv - c * z[3]};
+        }
+        prow = t0 + j;
+        pok = prow < end;
+        if (pok && h == 0 && cb == 0)
+            reinterpret_cast<float2 *>(cbuf)[bh * N + prow] = float2{c, inv};
+        __syncthreads();  // B2
+        if (h == 0) {
+            vz[32 * cb + j] += zc;
+            vu[32 * cb + j] += uc;
+        }
+        if (more) {
+            rk.stage_nat(ks, tid);
+            rk.stage_tr(kT, tid);
+            rv.stage_nat(vs, tid);
+            rv.stage_tr(vT, tid);
+            if (round + 2 < nrounds) {
+                rq.fetch(qh, t0 + 2 * kCc, end, tid);
+                rg.fetch(gh, t0 + 2 * kCc, end, tid);
+            }
+        }
+        __syncthreads();  // B3
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        store_pending(q);
+}
+
 }  // namespace bf
 }  // namespace la
