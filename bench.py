@@ -170,8 +170,8 @@ def copy_reference(dev):
 
 def uses_bf16_mfma(dtype, D, causal):
     """Whether every kernel of the path computes on the bf16 matrix cores
-    (bf16 storage, 32 <= D <= 128, non-causal); otherwise fp32 matrix cores."""
-    return dtype == "bf16" and 32 <= D <= 128 and not causal
+    (bf16 storage, 32 <= D <= 128, either mask); otherwise fp32 matrix cores."""
+    return dtype == "bf16" and 32 <= D <= 128
 
 
 def step_floor_us(B, H, N, D, s, bf16_mfma):

@@ -320,9 +320,14 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
         if ((rc = scan(gpart, nullptr, p, 2, s, t)) != LA_OK)  // exclusive suffix
             return rc;
         return traced(t, s, "bwd_kv", [&] {
-            cz::k_bwd_kv_causal<ST, D><<<dim3((unsigned)(2 * p.nseg * p.BH)), nt, 0, s>>>(
-                q, k, v, g, static_cast<T *>(dK), static_cast<T *>(dV), cbuf, gpart, p.N,
-                p.seg_len, (int)p.nseg);
+            if constexpr (std::is_same<ST, StBF16>::value)
+                bf::k_bwd_kv_causal_bf<D><<<dim3((unsigned)(2 * p.nseg * p.BH)), nt, 0, s>>>(
+                    q, k, v, g, static_cast<T *>(dK), static_cast<T *>(dV), cbuf, gpart, p.N,
+                    p.seg_len, (int)p.nseg);
+            else
+                cz::k_bwd_kv_causal<ST, D><<<dim3((unsigned)(2 * p.nseg * p.BH)), nt, 0, s>>>(
+                    q, k, v, g, static_cast<T *>(dK), static_cast<T *>(dV), cbuf, gpart, p.N,
+                    p.seg_len, (int)p.nseg);
         });
     }
     if constexpr (!CAUSAL && nc_path<D>()) {

@@ -664,6 +664,61 @@ struct ChunkRows {
     }
 };
 
+// (c_t, 1/den_t) of a chunk's rows for the staging items: item q covers
+// tokens 2 (q % 16) and 2 (q % 16) + 1; rows past the end read as zeros
+template <int D, int NT>
+struct ChunkCb {
+    static constexpr int PER = ChunkRows<D, NT>::PER, PC = ChunkRows<D, NT>::PC;
+    float2 r[PER][2];
+    __device__ __forceinline__ void fetch(const float2 *src, int64_t r0, int64_t end, int tid)
+    {
+        const int rows = (int)(end - r0 < kCc ? end - r0 : kCc);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float2 *>(src + r0), (short)0, rows * 8, kBufferWord3);
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int q = tid + p * NT;
+            if (PC % NT == 0 || q < PC) {
+                const int pr = q % (kCc / 2);
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+                    r[p][u] = __builtin_bit_cast(
+                        float2, __builtin_amdgcn_raw_buffer_load_b64(rs, (2 * pr + u) * 8, 0, 0));
+            }
+        }
+    }
+};
+
+// a_t = g_t / den_t of the staged dO rows, transposed, as hi and lo planes
+template <int D, int NT>
+__device__ __forceinline__ void stage_a_tr(const ChunkRows<D, NT> &rg, const ChunkCb<D, NT> &cb,
+                                           uint16_t *hiT, uint16_t *loT, int tid)
+{
+    typedef ChunkRows<D, NT> R;
+#pragma unroll
+    for (int p = 0; p < R::PER; ++p) {
+        const int q = tid + p * NT;
+        if (R::PC % NT == 0 || q < R::PC) {
+            const int chunk = q / (kCc / 2), pr = q % (kCc / 2);
+            float g0[8], g1[8];
+            StBF16::widen(rg.r[p][0], g0);
+            StBF16::widen(rg.r[p][1], g1);
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                __bf16 h0, l0, h1, l1;
+                split_bf16(g0[s] * cb.r[p][0].y, h0, l0);
+                split_bf16(g1[s] * cb.r[p][1].y, h1, l1);
+                *reinterpret_cast<uint32_t *>(&hiT[(8 * chunk + s) * kRT + 2 * pr]) =
+                    (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                    ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                *reinterpret_cast<uint32_t *>(&loT[(8 * chunk + s) * kRT + 2 * pr]) =
+                    (uint32_t)__builtin_bit_cast(uint16_t, l0) |
+                    ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+            }
+        }
+    }
+}
+
 // 8 consecutive tokens (16 kk + 8 h ..) of column c of a transposed tile
 __device__ __forceinline__ bf8 col_at(const uint16_t *ldsT, int c, int kk, int h)
 {
@@ -1123,6 +1178,210 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
 #pragma unroll
     for (int q = 0; q < 4; ++q)
         store_pending(q);
+}
+
+// dK | dV (as cz::k_bwd_kv_causal), chunks in reverse order with the running
+// suffix state (R, r, t).  Parity 0 (dK): st[t] = R^T[32t.., 32cb..];
+// acc = R-block . V_c^T + Q_c-block^T . P with P[i][j] = g_i.v_j / den_i -
+// c_i (i >= j), from shares of G_c V_c^T; R += Q_c^T A_c.  Parity 1 (dV):
+// st[t] = R[32t.., 32cb..]; acc = R^T-block . K_c^T + A_c-block^T . W with
+// W[i][j] = 1 + q_i.k_j (i >= j), from shares of Q_c K_c^T.  A_c = G_c /
+// den is formed at staging as transposed hi/lo planes.
+template <int D>
+struct KvBfLds {
+    static constexpr int LDX = D + 8, WP = kCc + 1, NCB = D / 32;
+    uint16_t xs[kCc * LDX];  // V (dK) or K (dV), natural
+    uint16_t ys[kCc * LDX];  // dO (dK) or Q (dV), natural
+    uint16_t qT[D * kRT];
+    uint16_t aT[2][D * kRT];  // a = dO / den, hi and lo
+    float sh[NCB][kCc * WP];
+    float cs[kCc], is[kCc];
+    float vr[D];  // r (dK) or t (dV)
+};
+
+template <int D, int PAR>
+__device__ __forceinline__ void kv_pass_bf(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const uint16_t *__restrict__ G, uint16_t *__restrict__ dK,
+    uint16_t *__restrict__ dV, const float *__restrict__ cbuf, const float *__restrict__ rec,
+    int64_t N, int64_t seg_len, int nseg, KvBfLds<D> &L)
+{
+    typedef nc::IO<StBF16> io;
+    constexpr int NCB = D / 32, NT = 64 * NCB, LDX = D + 8, WP = kCc + 1;
+    const int64_t b = blockIdx.x >> 1;
+    const int64_t bh = b / nseg;
+    const int seg = (int)(b % nseg);
+    const int tid = threadIdx.x, cb = tid >> 6, lane = tid & 63, j = lane & 31, h = lane >> 5;
+    const int64_t beg = (int64_t)seg * seg_len;
+    const int64_t end = (beg + seg_len < N) ? beg + seg_len : N;
+    const int64_t hoff = bh * N * D;
+    const float *st = rec + (bh * nseg + seg) * (int64_t)(D * D + 2 * D);
+    const uint16_t *xh = (PAR == 0 ? V : K) + hoff, *qh = Q + hoff, *gh = G + hoff;
+    uint16_t *oh = (PAR == 0 ? dK : dV) + hoff;
+    const float2 *ch = reinterpret_cast<const float2 *>(cbuf) + bh * N;
+
+    ChunkRows<D, NT> rx, rq, rg;
+    ChunkCb<D, NT> rc;
+    auto fetch = [&](int64_t r0) {
+        rx.fetch(xh, r0, end, tid);
+        rq.fetch(qh, r0, end, tid);
+        rg.fetch(gh, r0, end, tid);
+        rc.fetch(ch, r0, end, tid);
+    };
+    auto stage = [&](int64_t r0) {
+        rx.stage_nat(L.xs, tid);
+        if (PAR == 0)
+            rg.stage_nat(L.ys, tid);
+        else
+            rq.stage_nat(L.ys, tid);
+        rq.stage_tr(L.qT, tid);
+        stage_a_tr<D, NT>(rg, rc, L.aT[0], L.aT[1], tid);
+        // (c, 1/den) of the chunk's rows
+        if (tid < kCc) {
+            const bool ok = r0 + tid < end;
+            const float2 v = ok ? ch[r0 + tid] : float2{0.f, 0.f};
+            L.cs[tid] = v.x;
+            L.is[tid] = v.y;
+        }
+    };
+
+    const int64_t nrounds = (end - beg + kCc - 1) / kCc;
+    const int64_t last = beg + (nrounds - 1) * kCc;
+    fetch(last);
+    f16v sacc[NCB];
+#pragma unroll
+    for (int t = 0; t < NCB; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int a = 32 * t + 8 * (i / 4) + 4 * h + (i % 4), o = 32 * cb + j;
+            sacc[t][i] = (PAR == 0) ? st[o * D + a] : st[a * D + o];
+        }
+    for (int e = tid; e < D; e += NT)
+        L.vr[e] = st[D * D + (PAR == 0 ? 0 : D) + e];
+    stage(last);
+    drain_loads();
+    if (nrounds > 1)
+        fetch(last - kCc);
+    __syncthreads();
+
+    for (int64_t round = 0; round < nrounds; ++round) {
+        const int64_t t0 = last - round * kCc;
+        // (1) the suffix state applied to the chunk's rows of V (dK) or K (dV)
+        f16v acc = zero16();
+        {
+            const uint16_t *xrow = &L.xs[j * LDX];
+#pragma unroll
+            for (int t = 0; t < NCB; ++t)
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    const bf8 x = row_at(xrow, 32 * t + 16 * p + 4 * h);
+                    bf8 ahi, alo;
+                    split8(sacc[t], p, ahi, alo);
+                    acc = mma16(ahi, x, acc);
+                    acc = mma16(alo, x, acc);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+        }
+        // (2) shares: G_c V_c^T (dK) or Q_c K_c^T (dV)
+        share_bf<D>(L.ys, L.xs, L.sh[cb], cb, j, h);
+        __syncthreads();  // B1
+        // (3) in-chunk term over query rows ir = 16 kk + 8 h + s >= j, and the
+        // state update
+        float vc = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < kCc / 16; ++kk) {
+            float bm[8];
+#pragma unroll
+            for (int s2 = 0; s2 < 8; ++s2) {
+                const int ir = 16 * kk + 8 * h + s2;
+                float sv = 0.f;
+#pragma unroll
+                for (int pp = 0; pp < NCB; ++pp)
+                    sv += L.sh[pp][ir * WP + j];
+                if (PAR == 0)
+                    bm[s2] = (ir >= j) ? sv * L.is[ir] - L.cs[ir] : 0.f;
+                else
+                    bm[s2] = (ir >= j) ? 1.f + sv : 0.f;
+            }
+            bf8 bhi, blo;
+#pragma unroll
+            for (int s2 = 0; s2 < 8; ++s2) {
+                __bf16 x, y;
+                split_bf16(bm[s2], x, y);
+                bhi[s2] = x;
+                blo[s2] = y;
+            }
+            if constexpr (PAR == 0) {
+                const bf8 qcol = col_at(L.qT, 32 * cb + j, kk, h);  // Q[ir][32cb+j]
+                acc = mma16(qcol, bhi, acc);
+                acc = mma16(qcol, blo, acc);
+#pragma unroll
+                for (int t = 0; t < NCB; ++t) {
+                    sacc[t] = mma16(col_at(L.aT[0], 32 * t + j, kk, h), qcol, sacc[t]);
+                    sacc[t] = mma16(col_at(L.aT[1], 32 * t + j, kk, h), qcol, sacc[t]);
+                }
+                float qf[8];
+                unpack8(qcol, qf);
+#pragma unroll
+                for (int s2 = 0; s2 < 8; ++s2)
+                    vc += L.cs[16 * kk + 8 * h + s2] * qf[s2];
+            } else {
+                const bf8 ahi = col_at(L.aT[0], 32 * cb + j, kk, h);  // a[ir][32cb+j]
+                const bf8 alo = col_at(L.aT[1], 32 * cb + j, kk, h);
+                acc = mma16(ahi, bhi, acc);
+                acc = mma16(ahi, blo, acc);
+                acc = mma16(alo, bhi, acc);
+#pragma unroll
+                for (int t = 0; t < NCB; ++t) {
+                    const bf8 qcol = col_at(L.qT, 32 * t + j, kk, h);
+                    sacc[t] = mma16(qcol, ahi, sacc[t]);
+                    sacc[t] = mma16(qcol, alo, sacc[t]);
+                }
+                float af[8], lf[8];
+                unpack8(ahi, af);
+                unpack8(alo, lf);
+#pragma unroll
+                for (int s2 = 0; s2 < 8; ++s2)
+                    vc += af[s2] + lf[s2];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        vc += __shfl_xor(vc, 32, 64);
+        // (4) rows of dK (- r) or dV (+ t) with the vector of the rows after
+        // the chunk
+        const float sg = (PAR == 0) ? -1.f : 1.f;
+        if (t0 + j < end)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f4 v = *reinterpret_cast<const f4 *>(&L.vr[32 * cb + 8 * q + 4 * h]);
+                io::store4(oh + (t0 + j) * D + 32 * cb + 8 * q + 4 * h,
+                           f4{acc[4 * q] + sg * v[0], acc[4 * q + 1] + sg * v[1],
+                              acc[4 * q + 2] + sg * v[2], acc[4 * q + 3] + sg * v[3]});
+            }
+        __syncthreads();  // B2
+        if (h == 0)
+            L.vr[32 * cb + j] += vc;
+        if (round + 1 < nrounds) {
+            stage(t0 - kCc);
+            if (round + 2 < nrounds)
+                fetch(t0 - 2 * kCc);
+        }
+        __syncthreads();  // B3
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * (D / 32)) void k_bwd_kv_causal_bf(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const uint16_t *__restrict__ G, uint16_t *__restrict__ dK,
+    uint16_t *__restrict__ dV, const float *__restrict__ cbuf, const float *__restrict__ rec,
+    int64_t N, int64_t seg_len, int nseg)
+{
+    __shared__ __attribute__((aligned(16))) KvBfLds<D> lds;
+    if (blockIdx.x & 1)
+        kv_pass_bf<D, 1>(Q, K, V, G, dK, dV, cbuf, rec, N, seg_len, nseg, lds);
+    else
+        kv_pass_bf<D, 0>(Q, K, V, G, dK, dV, cbuf, rec, N, seg_len, nseg, lds);
 }
 
 }  // namespace bf
