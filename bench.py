@@ -296,6 +296,11 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # device memory of the step: the 8 I/O tensors plus the library's
+    # workspace and saved state (everything the caller allocates for it)
+    mem = {"peak_allocated": torch.cuda.max_memory_allocated(dev),
+           "io_tensors": 8 * q.numel() * q.element_size(),
+           "workspace": ws.numel(), "saved_state": st.numel() * 4}
     copy_gbs = copy_reference(dev)
 
     # timed region 1: the headline, nothing but the K steps
@@ -409,6 +414,7 @@ def main():
         "kernels_us_per_launch": {n: round(t, 2) for n, t in avg_us.items()},
         "traced_ms_per_step": round(traced_ms, 4),
         "hbm_copy_GBs": round(copy_gbs, 1),
+        "memory_bytes": mem,
         "variants": variants,
     }
     print(json.dumps(line), flush=True)
