@@ -97,10 +97,20 @@ def test_ragged_fp32(D, N, causal):
     compare(1, 2, N, D, torch.float32, causal, seed=N + D)
 
 
-@pytest.mark.parametrize("D", [16, 64, 128, 256])
+@pytest.mark.parametrize("D", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ragged_bf16(D, causal):
     compare(2, 1, 777, D, torch.bfloat16, causal, seed=3)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_long_segments_d128(causal, dtype):
+    """Two heads over a long ragged sequence at D=128: each segment spans
+    many staging rounds and chunks, and the last one ends mid-chunk."""
+    m = la()
+    assert m.num_segments(1, 2, 20001, 128) < (20001 + 63) // 64
+    compare(1, 2, 20001, 128, dtype, causal, seed=11)
 
 
 @pytest.mark.parametrize("causal", [False, True])
