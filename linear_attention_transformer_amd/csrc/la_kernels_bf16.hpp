@@ -725,18 +725,19 @@ __device__ __forceinline__ bf8 col_at(const uint16_t *ldsT, int c, int kk, int h
     return *reinterpret_cast<const bf8 *>(&ldsT[c * kRT + 16 * kk + 8 * h]);
 }
 
-// this wave's share of X_c Y_c^T over columns 32 cb .. 32 cb + 31 (natural
-// rows), written to sh[i * (kCc + 1) + jj]
+// X_c Y_c^T over all D columns (natural rows), written to sh[i * (kCc + 1) +
+// jj] by one wave: on the bf16 matrix cores the whole 32 x 32 block is D/16
+// MFMAs, cheaper than exchanging per-wave shares through LDS
 template <int D>
-__device__ __forceinline__ void share_bf(const uint16_t *xs, const uint16_t *ys, float *sh,
-                                         int cb, int j, int h)
+__device__ __forceinline__ void full_bf(const uint16_t *xs, const uint16_t *ys, float *sh,
+                                        int j, int h)
 {
     constexpr int LDX = D + 8, WP = kCc + 1;
     f16v a = zero16();
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        const bf8 x = *reinterpret_cast<const bf8 *>(&xs[j * LDX + 32 * cb + 16 * ks + 8 * h]);
-        const bf8 y = *reinterpret_cast<const bf8 *>(&ys[j * LDX + 32 * cb + 16 * ks + 8 * h]);
+    for (int ks = 0; ks < D / 16; ++ks) {
+        const bf8 x = *reinterpret_cast<const bf8 *>(&xs[j * LDX + 16 * ks + 8 * h]);
+        const bf8 y = *reinterpret_cast<const bf8 *>(&ys[j * LDX + 16 * ks + 8 * h]);
         a = mma16(x, y, a);
     }
 #pragma unroll
@@ -761,7 +762,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal_bf(
     __shared__ __attribute__((aligned(16))) uint16_t ks[kCc * LDX];
     __shared__ __attribute__((aligned(16))) uint16_t kT[D * kRT];
     __shared__ __attribute__((aligned(16))) uint16_t vT[D * kRT];
-    __shared__ float wx[NCB][kCc * WP];
+    __shared__ float wx[kCc * WP];  // Q_c K_c^T
     __shared__ __attribute__((aligned(16))) float vz[D];
     __shared__ __attribute__((aligned(16))) float vu[D];
 
@@ -842,8 +843,9 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal_bf(
                     __builtin_amdgcn_sched_barrier(0);
                 }
         }
-        // (2) this wave's share of Q_c K_c^T
-        share_bf<D>(qs, ks, wx[cb], cb, j, h);
+        // (2) Q_c K_c^T (one wave)
+        if (cb == 0)
+            full_bf<D>(qs, ks, wx, j, h);
         __syncthreads();  // B1
         if (more)
             rq.stage_nat(qs, tid);  // Q is read only before B1
@@ -860,11 +862,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal_bf(
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 const int jr = 16 * kk + 8 * h + s;
-                float w = 0.f;
-#pragma unroll
-                for (int pp = 0; pp < NCB; ++pp)
-                    w += wx[pp][j * WP + jr];
-                wm[s] = (jr <= j) ? 1.f + w : 0.f;
+                wm[s] = (jr <= j) ? 1.f + wx[j * WP + jr] : 0.f;
                 rs += wm[s];
             }
             bf8 whi, wlo;
@@ -954,8 +952,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
     __shared__ __attribute__((aligned(16))) uint16_t vs[kCc * LDX];
     __shared__ __attribute__((aligned(16))) uint16_t kT[D * kRT];
     __shared__ __attribute__((aligned(16))) uint16_t vT[D * kRT];
-    __shared__ float wx[NCB][kCc * WP];  // shares of Q_c K_c^T
-    __shared__ float gx[NCB][kCc * WP];  // shares of G_c V_c^T
+    __shared__ float wx[kCc * WP];       // Q_c K_c^T
+    __shared__ float gx[kCc * WP];       // G_c V_c^T
     __shared__ float xq[NCB][kCc];       // shares of q_i.y_i
     __shared__ __attribute__((aligned(16))) float vz[D];
     __shared__ __attribute__((aligned(16))) float vu[D];
@@ -1053,9 +1051,12 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
                     __builtin_amdgcn_sched_barrier(0);
                 }
         }
-        // (2) shares of Q_c K_c^T, G_c V_c^T and q.y over this wave's columns
-        share_bf<D>(qs, ks, wx[cb], cb, j, h);
-        share_bf<D>(gs, vs, gx[cb], cb, j, h);
+        // (2) Q_c K_c^T and G_c V_c^T (one wave each), q.y over this wave's
+        // columns
+        if (cb == 0)
+            full_bf<D>(qs, ks, wx, j, h);
+        if (cb == NCB - 1)
+            full_bf<D>(gs, vs, gx, j, h);
         {
             const uint16_t *qr = &qs[j * LDX + 32 * cb + 4 * h];
             float pq = 0.f;
@@ -1087,12 +1088,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
 #pragma unroll
             for (int s2 = 0; s2 < 8; ++s2) {
                 const int jr = 16 * kk + 8 * h + s2;
-                float w = 0.f, gv = 0.f;
-#pragma unroll
-                for (int pp = 0; pp < NCB; ++pp) {
-                    w += wx[pp][j * WP + jr];
-                    gv += gx[pp][j * WP + jr];
-                }
+                const float w = wx[j * WP + jr], gv = gx[j * WP + jr];
                 const bool m = jr <= j;
                 const float wm = m ? 1.f + w : 0.f;
                 rs += wm;
@@ -1194,7 +1190,7 @@ struct KvBfLds {
     uint16_t ys[kCc * LDX];  // dO (dK) or Q (dV), natural
     uint16_t qT[D * kRT];
     uint16_t aT[2][D * kRT];  // a = dO / den, hi and lo
-    float sh[NCB][kCc * WP];
+    float sh[kCc * WP];
     float cs[kCc], is[kCc];
     float vr[D];  // r (dK) or t (dV)
 };
@@ -1282,8 +1278,9 @@ __device__ __forceinline__ void kv_pass_bf(
                     __builtin_amdgcn_sched_barrier(0);
                 }
         }
-        // (2) shares: G_c V_c^T (dK) or Q_c K_c^T (dV)
-        share_bf<D>(L.ys, L.xs, L.sh[cb], cb, j, h);
+        // (2) G_c V_c^T (dK) or Q_c K_c^T (dV), one wave
+        if (cb == 0)
+            full_bf<D>(L.ys, L.xs, L.sh, j, h);
         __syncthreads();  // B1
         // (3) in-chunk term over query rows ir = 16 kk + 8 h + s >= j, and the
         // state update
@@ -1294,10 +1291,7 @@ __device__ __forceinline__ void kv_pass_bf(
 #pragma unroll
             for (int s2 = 0; s2 < 8; ++s2) {
                 const int ir = 16 * kk + 8 * h + s2;
-                float sv = 0.f;
-#pragma unroll
-                for (int pp = 0; pp < NCB; ++pp)
-                    sv += L.sh[pp][ir * WP + j];
+                const float sv = L.sh[ir * WP + j];
                 if (PAR == 0)
                     bm[s2] = (ir >= j) ? sv * L.is[ir] - L.cs[ir] : 0.f;
                 else
