@@ -158,7 +158,7 @@ int traced(Tracer *t, hipStream_t s, const char *name, F &&launch)
 
 int scan(float *part, float *out, const Plan &p, int mode, hipStream_t s, Tracer *t)
 {
-    const int64_t bph = (p.PS + 255) / 256;
+    const int64_t bph = (p.PS / 4 + 255) / 256;  // 4 floats per thread
     return traced(t, s, "state_scan", [&] {
         k_state_scan<<<dim3((unsigned)(p.BH * bph)), dim3(256), 0, s>>>(
             part, out, (int)p.nseg, p.PS, bph, mode);

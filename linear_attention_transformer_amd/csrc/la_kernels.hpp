@@ -503,31 +503,45 @@ __global__ __launch_bounds__(threads_for<D>()) void k_grad_state_local(
 //   mode 0: out[bh] = sum_s part[bh][s]
 //   mode 1: part[bh][s] <- sum_{s' < s} part[bh][s']   (in place)
 //   mode 2: part[bh][s] <- sum_{s' > s} part[bh][s']   (in place)
+// Each thread takes 4 consecutive floats of the record (records are PS =
+// D^2 + 2D floats, a multiple of 4, and 16-byte aligned); the segments'
+// loads of a batch are issued before any of them is added, in order.
 __global__ __launch_bounds__(256) void k_state_scan(float *__restrict__ part,
                                                     float *__restrict__ out, int nseg,
                                                     int64_t PS, int64_t blocks_per_head,
                                                     int mode)
 {
+    constexpr int BATCH = 8;
     const int64_t bh = blockIdx.x / blocks_per_head;
-    const int64_t e = (blockIdx.x % blocks_per_head) * 256 + threadIdx.x;
+    const int64_t e = 4 * ((blockIdx.x % blocks_per_head) * 256 + threadIdx.x);
     if (e >= PS)
         return;
-    float *p = part + bh * nseg * PS + e;
-    float run = 0.f;
+    f4 *p = reinterpret_cast<f4 *>(part + bh * nseg * PS + e);
+    const int64_t ps4 = PS / 4;
+    f4 run = {0.f, 0.f, 0.f, 0.f};
     if (mode == 0) {
-        for (int s = 0; s < nseg; ++s)
-            run += p[s * PS];
-        out[bh * PS + e] = run;
+        for (int s0 = 0; s0 < nseg; s0 += BATCH) {
+            f4 v[BATCH];
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b)
+                if (s0 + b < nseg)
+                    v[b] = p[(s0 + b) * ps4];
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b)
+                if (s0 + b < nseg)
+                    run += v[b];
+        }
+        *reinterpret_cast<f4 *>(out + bh * PS + e) = run;
     } else if (mode == 1) {
         for (int s = 0; s < nseg; ++s) {
-            const float v = p[s * PS];
-            p[s * PS] = run;
+            const f4 v = p[s * ps4];
+            p[s * ps4] = run;
             run += v;
         }
     } else {
         for (int s = nseg - 1; s >= 0; --s) {
-            const float v = p[s * PS];
-            p[s * PS] = run;
+            const f4 v = p[s * ps4];
+            p[s * ps4] = run;
             run += v;
         }
     }
