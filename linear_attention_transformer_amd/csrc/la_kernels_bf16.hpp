@@ -357,7 +357,9 @@ __global__ __launch_bounds__(256) void k_reduce_bf(
     int nseg)
 {
     static_assert(D >= 32 && D <= 128, "32x32 tiles");
-    constexpr int NT = 256, TT = 64;
+    // rows per round: 64, or 32 for the backward, whose staging also carries
+    // (c, 1/den) and the hi/lo planes (registers for one wave per SIMD more)
+    constexpr int NT = 256, TT = GRAD ? 32 : 64;
     constexpr int R2 = TT + 8;              // bf16 pitch of a transposed column
     constexpr int NTILE1 = D / 32;          // tiles per dimension
     constexpr int NTILE = NTILE1 * NTILE1;
@@ -541,19 +543,19 @@ __global__ __launch_bounds__(256) void k_reduce_bf(
                     out[(m0 + 32 * a + 8 * (i / 4) + 4 * h + (i % 4)) * D + n0 + 32 * b + j] =
                         acc[a][b][i];
     }
-    // column sums: the 32 lanes of a half-wave share one chunk of 8 columns
+    // column sums: the TT/2 consecutive lanes of a chunk hold its 8 columns
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
         const int q = tid + p * NT;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
 #pragma unroll
-            for (int o = 1; o < 32; o <<= 1) {
+            for (int o = 1; o < TT / 2; o <<= 1) {
                 cx[p][s] += __shfl_xor(cx[p][s], o, 64);
                 cy[p][s] += __shfl_xor(cy[p][s], o, 64);
             }
         }
-        if ((PC % NT == 0 || q < PC) && j == 0) {
+        if ((PC % NT == 0 || q < PC) && q % (TT / 2) == 0) {
             const int chunk = q / (TT / 2);
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
