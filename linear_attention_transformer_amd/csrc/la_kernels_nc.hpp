@@ -8,23 +8,20 @@
 //   k_reduce_nc : Mat = X^T Y over a segment of rows plus column sums.  The
 //                 contraction runs over tokens, which are the row index of
 //                 X and Y in memory, so MFMA operands are loaded straight
-//                 from global memory (16 consecutive columns of one row per
-//                 16 lanes) with a several-steps-deep register prefetch; no
-//                 LDS, no barriers in the loop.
-//   k_apply_nc  : out_i = epilogue(M-applied row i) for every row of a
-//                 segment.  The D x D matrix sits in LDS (loaded once per
-//                 workgroup), and each wave streams its own 16-row tiles
-//                 with no barrier.  The product is formed transposed
-//                 (out^T = M . X^T): the row tile is the MFMA B operand,
-//                 read from global as 16-byte vectors along the row, and
-//                 the result comes back as 4 consecutive columns of one
-//                 row per lane, so stores are 16-byte vectors too and every
-//                 per-row scalar (den_i, c_i) stays inside the lane.
+//                 from global memory (32 lanes per token row, consecutive
+//                 columns per lane) with a several-steps-deep register
+//                 prefetch; no LDS, no barriers in the loop.
+//   k_apply_nc  : out_i = epilogue(A x_i) for every row x_i of a segment
+//                 (forward: A = S^T; dK: A = dS; dV: A = dS^T).  Each wave
+//                 keeps a 32-column block of A in registers; the workgroup
+//                 stages 32-row tiles of X in LDS (double-buffered, one
+//                 barrier per round) and every wave reads its MFMA B operand
+//                 from there.
+//   k_bwd_q_nc  : dQ and the segment's gradient record in one pass over Q
+//                 and dO: one role of waves forms dQ as k_apply_nc does, the
+//                 other accumulates dS = Q^T A from the same staged tiles.
 //
-// MFMA: v_mfma_f32_16x16x4_f32.  Lane l = 16*lg + lr supplies A[m=lr][k=lg]
-// and B[k=lg][n=lr] and receives C[m=4*lg+r][n=lr], r = 0..3.  In the apply
-// kernel the four accumulator steps r use k = 4*lg + r inside a 16-block,
-// for which both operands are contiguous 16-byte reads.
+// MFMA: v_mfma_f32_32x32x2_f32 throughout (layout below).
 #pragma once
 
 #include "la_kernels.hpp"
