@@ -88,14 +88,18 @@ struct StBF16 {
             o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
         }
     }
-    // IEEE round-to-nearest-even to bfloat16; NaN stays a (quiet) NaN
+    // round-to-nearest-even to bfloat16 (gfx950 converts in hardware:
+    // v_cvt_pk_bf16_f32, two values per instruction; NaN stays NaN)
     __device__ static __forceinline__ T narrow(float x)
     {
-        uint32_t u = __float_as_uint(x);
-        if ((u & 0x7fffffffu) > 0x7f800000u)
-            return (uint16_t)((u >> 16) | 0x0040u);
-        u += 0x7fffu + ((u >> 16) & 1u);
-        return (uint16_t)(u >> 16);
+        return __builtin_bit_cast(uint16_t, (__bf16)x);
+    }
+    // a in the low half, b in the high half
+    __device__ static __forceinline__ uint32_t narrow2(float a, float b)
+    {
+        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+        const bf2 v = {(__bf16)a, (__bf16)b};
+        return __builtin_bit_cast(uint32_t, v);
     }
 };
 

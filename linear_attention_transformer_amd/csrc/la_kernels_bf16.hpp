@@ -60,7 +60,9 @@ constexpr int kApplyThreads = 256;
 
 // ============================================================ apply
 // KIND 0 forward : A = S^T, o_i = (u + A q_i) / (N + q_i.z), X = Q;
-//                  den_out[i] = N + q_i.z (optional).
+//                  den_out[i] = N + q_i.z (optional).  Each wave forms q_i.z
+//                  over its own 32 columns; the partials meet in LDS at the
+//                  round's barrier.
 // KIND 1 dQ      : A = S, X = dO, X2 = Q: y_i = A g_i, den_i = N + q_i.z,
 //                  c_i = (g_i.u + q_i.y_i) / den_i^2, dq_i = y_i / den_i - c_i z;
 //                  cbuf[i] = (c_i, 1/den_i).  q_i.y_i is summed over the
@@ -71,9 +73,8 @@ constexpr int kApplyThreads = 256;
 // D < 128, row groups), hold their block of A in registers (as hi/lo bf16
 // pairs: 8 per lane and k-step of 16), stage each round of rows in LDS
 // (raw bf16, double-buffered, one barrier per round), and read the B operand
-// as one 16-byte LDS read per k-step.  In the forward q_j.z is accumulated
-// from the same operands; stores of a round are issued during the next
-// round's MFMAs.  Rows are loaded through a per-round buffer descriptor that
+// as one 16-byte LDS read per k-step.  Stores of a round are issued during
+// a later round's MFMAs.  Rows are loaded through a per-round buffer descriptor that
 // covers only the rows before the segment end (zeros beyond it).
 template <int D, int KIND>
 __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
@@ -98,11 +99,14 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
     __shared__ __attribute__((aligned(16))) uint16_t qs[DQ ? 2 : 1][DQ ? TR * LDX : 8];
     __shared__ __attribute__((aligned(16))) float vz[KIND <= 1 ? D : 4];
     __shared__ __attribute__((aligned(16))) float vu[DQ ? D : 4];
-    __shared__ float xch[DQ ? 2 : 1][NRG][NCB][32];
+    // per-row sums over the column blocks (forward: q.z; dQ: q.y), one
+    // partial per wave, added up after the round's barrier
+    constexpr bool XCH = (KIND <= 1);
+    __shared__ float xch[XCH ? 2 : 1][NRG][NCB][32];
     // output rows of a round (bf16), stored as whole rows by the workgroup
-    // LAG rounds later: the forward and dK | dV tiles are complete at the
-    // round's barrier, the dQ tile only after the next one
-    constexpr int LAG = DQ ? 2 : 1;
+    // LAG rounds later: the dK | dV tile is complete at the round's barrier,
+    // the forward and dQ tiles (normalised after it) only at the next one
+    constexpr int LAG = XCH ? 2 : 1;
     constexpr int OCH = TR * CPR / kApplyThreads;  // 16-byte output chunks per thread
     __shared__ __attribute__((aligned(16))) uint16_t ot[2][TR * LDX];
 
@@ -208,8 +212,8 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             uint2 r;
-            r.x = (uint32_t)StBF16::narrow(o[q][0]) | ((uint32_t)StBF16::narrow(o[q][1]) << 16);
-            r.y = (uint32_t)StBF16::narrow(o[q][2]) | ((uint32_t)StBF16::narrow(o[q][3]) << 16);
+            r.x = StBF16::narrow2(o[q][0], o[q][1]);
+            r.y = StBF16::narrow2(o[q][2], o[q][3]);
             *reinterpret_cast<uint2 *>(&ot[tb][(32 * rg + j) * LDX + 32 * cb + 8 * q + 4 * h]) = r;
         }
     };
@@ -239,15 +243,7 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
                 xn = *reinterpret_cast<const bf8 *>(xt + 16 * (ks + 1));
             acc = mma16(ahi[ks], x, acc);
             acc = mma16(alo[ks], x, acc);
-            if constexpr (KIND == 0) {
-                float xf[8];
-                unpack8(x, xf);
-                const f4 z0 = *reinterpret_cast<const f4 *>(&vz[zo + 16 * ks]);
-                const f4 z1 = *reinterpret_cast<const f4 *>(&vz[zo + 16 * ks + 4]);
-                qz += dot4(f4{xf[0], xf[1], xf[2], xf[3]}, z0) +
-                      dot4(f4{xf[4], xf[5], xf[6], xf[7]}, z1);
-                asm volatile("" : "+v"(qz));
-            } else if constexpr (DQ) {
+            if constexpr (DQ) {
                 // g.u from the operand, q.z from the same columns of q
                 float xf[8], qf[8];
                 unpack8(x, xf);
@@ -272,16 +268,20 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
         const int64_t row = beg + round * TR + 32 * rg + j;
         f4 pend[4];
         if constexpr (KIND == 0) {
-            qz += __shfl_xor(qz, 32, 64);
-            const float den = (float)N + qz;
-            const float inv = 1.f / den;
+            // q.z over this block's 32 columns of q (lane half h: 16 of them)
+            const uint16_t *qr = &xs[buf][(32 * rg + j) * LDX + 32 * cb + 16 * h];
+            const float *zr = &vz[32 * cb + 16 * h];
+            float p = 0.f;
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                pend[q] = f4{(acc[4 * q] + ev[q][0]) * inv, (acc[4 * q + 1] + ev[q][1]) * inv,
-                             (acc[4 * q + 2] + ev[q][2]) * inv, (acc[4 * q + 3] + ev[q][3]) * inv};
-            if (den_out != nullptr && row < end && h == 0 && cb == 0)
-                den_out[bh * N + row] = den;
-            put_tile(buf, pend);
+            for (int e = 0; e < 16; e += 8) {
+                float xf[8];
+                unpack8(*reinterpret_cast<const bf8 *>(qr + e), xf);
+                p += dot4(f4{xf[0], xf[1], xf[2], xf[3]}, *reinterpret_cast<const f4 *>(zr + e)) +
+                     dot4(f4{xf[4], xf[5], xf[6], xf[7]}, *reinterpret_cast<const f4 *>(zr + e + 4));
+            }
+            p += __shfl_xor(p, 32, 64);
+            if (h == 0)
+                xch[buf][rg][cb][j] = p;
         } else if constexpr (KIND == 2) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -310,6 +310,21 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
                 fetch_round(beg + (round + 2) * TR);
         }
         __syncthreads();
+        if constexpr (KIND == 0) {
+            float qz = 0.f;
+#pragma unroll
+            for (int c2 = 0; c2 < NCB; ++c2)
+                qz += xch[buf][rg][c2][j];
+            const float den = (float)N + qz;
+            const float inv = 1.f / den;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                pend[q] = f4{(acc[4 * q] + ev[q][0]) * inv, (acc[4 * q + 1] + ev[q][1]) * inv,
+                             (acc[4 * q + 2] + ev[q][2]) * inv, (acc[4 * q + 3] + ev[q][3]) * inv};
+            if (den_out != nullptr && row < end && h == 0 && cb == 0)
+                den_out[bh * N + row] = den;
+            put_tile(buf, pend);
+        }
         if constexpr (DQ) {
             float qy = 0.f;
 #pragma unroll

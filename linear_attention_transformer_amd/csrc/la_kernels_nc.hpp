@@ -61,8 +61,8 @@ struct IO<StBF16> {
     __device__ static __forceinline__ void store4(uint16_t *p, f4 v)
     {
         uint2 r;
-        r.x = (uint32_t)StBF16::narrow(v[0]) | ((uint32_t)StBF16::narrow(v[1]) << 16);
-        r.y = (uint32_t)StBF16::narrow(v[2]) | ((uint32_t)StBF16::narrow(v[3]) << 16);
+        r.x = StBF16::narrow2(v[0], v[1]);
+        r.y = StBF16::narrow2(v[2], v[3]);
         *reinterpret_cast<uint2 *>(p) = r;
     }
 };
