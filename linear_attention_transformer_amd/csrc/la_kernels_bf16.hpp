@@ -65,8 +65,9 @@ constexpr int kApplyThreads = 256;
 //                  round's barrier.
 // KIND 1 dQ      : A = S, X = dO, X2 = Q: y_i = A g_i, den_i = N + q_i.z,
 //                  c_i = (g_i.u + q_i.y_i) / den_i^2, dq_i = y_i / den_i - c_i z;
-//                  cbuf[i] = (c_i, 1/den_i).  q_i.y_i is summed over the
-//                  waves' column blocks through LDS at the round's barrier.
+//                  cbuf[i] = (c_i, 1/den_i).  q_i.y_i, g_i.u and q_i.z are
+//                  formed per column block and summed through LDS at the
+//                  round's barrier.
 // KIND 2 dK | dV : parity 0: A = dS, X = V, dk_j = A v_j - r;
 //                  parity 1: A = dS^T, X2 = K, dv_j = A k_j + t.
 // The structure is k_apply_nc's: waves own 32-column output blocks (and, for
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
     // per-row sums over the column blocks (forward: q.z; dQ: q.y), one
     // partial per wave, added up after the round's barrier
     constexpr bool XCH = (KIND <= 1);
-    __shared__ float xch[XCH ? 2 : 1][NRG][NCB][32];
+    __shared__ float xch[XCH ? 2 : 1][NRG][NCB][32][DQ ? 2 : 1];
     // output rows of a round (bf16), stored as whole rows by the workgroup
     // LAG rounds later: the dK | dV tile is complete at the round's barrier,
     // the forward and dQ tiles (normalised after it) only at the next one
@@ -230,11 +231,7 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
     for (int64_t round = 0; round < nrounds; ++round) {
         const int buf = (int)(round & 1);
         const uint16_t *xt = &xs[buf][(32 * rg + j) * LDX + 8 * h];
-        int zo = 8 * h;
-        asm volatile("" : "+v"(zo));  // z reads stay in the loop
-        const uint16_t *qt = DQ ? &qs[buf][(32 * rg + j) * LDX + 8 * h] : nullptr;
         f16v acc = zero16();
-        float qz = 0.f, gu = 0.f;
         bf8 xn = *reinterpret_cast<const bf8 *>(xt);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -243,21 +240,6 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
                 xn = *reinterpret_cast<const bf8 *>(xt + 16 * (ks + 1));
             acc = mma16(ahi[ks], x, acc);
             acc = mma16(alo[ks], x, acc);
-            if constexpr (DQ) {
-                // g.u from the operand, q.z from the same columns of q
-                float xf[8], qf[8];
-                unpack8(x, xf);
-                unpack8(*reinterpret_cast<const bf8 *>(qt + 16 * ks), qf);
-                const f4 z0 = *reinterpret_cast<const f4 *>(&vz[zo + 16 * ks]);
-                const f4 z1 = *reinterpret_cast<const f4 *>(&vz[zo + 16 * ks + 4]);
-                const f4 u0 = *reinterpret_cast<const f4 *>(&vu[zo + 16 * ks]);
-                const f4 u1 = *reinterpret_cast<const f4 *>(&vu[zo + 16 * ks + 4]);
-                qz += dot4(f4{qf[0], qf[1], qf[2], qf[3]}, z0) +
-                      dot4(f4{qf[4], qf[5], qf[6], qf[7]}, z1);
-                gu += dot4(f4{xf[0], xf[1], xf[2], xf[3]}, u0) +
-                      dot4(f4{xf[4], xf[5], xf[6], xf[7]}, u1);
-                asm volatile("" : "+v"(qz), "+v"(gu));
-            }
 #pragma unroll
             for (int p = 0; p < OCH; ++p)
                 if (round >= LAG && ks == (p * KS) / OCH)
@@ -267,21 +249,24 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
 
         const int64_t row = beg + round * TR + 32 * rg + j;
         f4 pend[4];
-        if constexpr (KIND == 0) {
-            // q.z over this block's 32 columns of q (lane half h: 16 of them)
-            const uint16_t *qr = &xs[buf][(32 * rg + j) * LDX + 32 * cb + 16 * h];
-            const float *zr = &vz[32 * cb + 16 * h];
+        // a.b over this block's 32 columns of two staged rows (lane half h
+        // sums 16 of them; both halves get the total)
+        auto rowdot = [&](const uint16_t *a, const float *b) {
             float p = 0.f;
 #pragma unroll
             for (int e = 0; e < 16; e += 8) {
-                float xf[8];
-                unpack8(*reinterpret_cast<const bf8 *>(qr + e), xf);
-                p += dot4(f4{xf[0], xf[1], xf[2], xf[3]}, *reinterpret_cast<const f4 *>(zr + e)) +
-                     dot4(f4{xf[4], xf[5], xf[6], xf[7]}, *reinterpret_cast<const f4 *>(zr + e + 4));
+                float af[8];
+                unpack8(*reinterpret_cast<const bf8 *>(a + 32 * cb + 16 * h + e), af);
+                const float *br = b + 32 * cb + 16 * h + e;
+                p += dot4(f4{af[0], af[1], af[2], af[3]}, *reinterpret_cast<const f4 *>(br)) +
+                     dot4(f4{af[4], af[5], af[6], af[7]}, *reinterpret_cast<const f4 *>(br + 4));
             }
-            p += __shfl_xor(p, 32, 64);
+            return p + __shfl_xor(p, 32, 64);
+        };
+        if constexpr (KIND == 0) {
+            const float p = rowdot(&xs[buf][(32 * rg + j) * LDX], vz);  // q.z
             if (h == 0)
-                xch[buf][rg][cb][j] = p;
+                xch[buf][rg][cb][j][0] = p;
         } else if constexpr (KIND == 2) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -289,7 +274,8 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
                              acc[4 * q + 2] + ev[q][2], acc[4 * q + 3] + ev[q][3]};
             put_tile(buf, pend);
         } else {
-            // q.y over this block's 32 output columns, summed across blocks below
+            // q.y over this block's 32 output columns (y = S g in the
+            // accumulators), plus g.u and q.z over its 32 input columns
             const uint16_t *qr = &qs[buf][(32 * rg + j) * LDX + 32 * cb + 4 * h];
             float p = 0.f;
 #pragma unroll
@@ -301,8 +287,12 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
                      __uint_as_float(u.y & 0xffff0000u) * acc[4 * q + 3];
             }
             p += __shfl_xor(p, 32, 64);
-            if (h == 0)
-                xch[buf][rg][cb][j] = p;
+            p += rowdot(&xs[buf][(32 * rg + j) * LDX], vu);               // g.u
+            const float pz = rowdot(&qs[buf][(32 * rg + j) * LDX], vz);  // q.z
+            if (h == 0) {
+                xch[buf][rg][cb][j][0] = p;
+                xch[buf][rg][cb][j][DQ ? 1 : 0] = pz;
+            }
         }
         if (round + 1 < nrounds) {
             stage_round(buf ^ 1);
@@ -314,7 +304,7 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
             float qz = 0.f;
 #pragma unroll
             for (int c2 = 0; c2 < NCB; ++c2)
-                qz += xch[buf][rg][c2][j];
+                qz += xch[buf][rg][c2][j][0];
             const float den = (float)N + qz;
             const float inv = 1.f / den;
 #pragma unroll
@@ -326,14 +316,14 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
             put_tile(buf, pend);
         }
         if constexpr (DQ) {
-            float qy = 0.f;
+            float sy = 0.f, qz = 0.f;  // g.u + q.y and q.z
 #pragma unroll
-            for (int c2 = 0; c2 < NCB; ++c2)
-                qy += xch[buf][rg][c2][j];
-            qz += __shfl_xor(qz, 32, 64);
-            gu += __shfl_xor(gu, 32, 64);
+            for (int c2 = 0; c2 < NCB; ++c2) {
+                sy += xch[buf][rg][c2][j][0];
+                qz += xch[buf][rg][c2][j][DQ ? 1 : 0];
+            }
             const float inv = 1.f / ((float)N + qz);
-            const float c = (gu + qy) * inv * inv;
+            const float c = sy * inv * inv;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 pend[q] = f4{acc[4 * q] * inv - c * ev[q][0], acc[4 * q + 1] * inv - c * ev[q][1],
