@@ -436,35 +436,39 @@ __global__ __launch_bounds__(256) void k_reduce_bf(
             const int q = tid + p * NT;
             if (PC % NT == 0 || q < PC) {
                 const int chunk = q / (TT / 2), pr = q % (TT / 2);
-                float xv[2][8], yv[2][8];
+                // tokens 2 pr, 2 pr + 1 of column 8 chunk + s as one bf16 pair
+                auto pair = [&](const uint4 &t0, const uint4 &t1, int s) {
+                    const uint32_t w0 = reinterpret_cast<const uint32_t *>(&t0)[s / 2];
+                    const uint32_t w1 = reinterpret_cast<const uint32_t *>(&t1)[s / 2];
+                    return (s & 1) ? __builtin_amdgcn_perm(w1, w0, 0x07060302u)
+                                   : __builtin_amdgcn_perm(w1, w0, 0x05040100u);
+                };
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    StBF16::widen(sx[p][u], xv[u]);
-                    StBF16::widen(sy[p][u], yv[u]);
-                }
-                const uint32_t *xw0 = reinterpret_cast<const uint32_t *>(&sx[p][0]);
-                const uint32_t *xw1 = reinterpret_cast<const uint32_t *>(&sx[p][1]);
-#pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    // tokens 2 pr, 2 pr + 1 of column 8 chunk + s, packed
-                    const uint32_t lo0 = (s & 1) ? (xw0[s / 2] >> 16) : (xw0[s / 2] & 0xffffu);
-                    const uint32_t lo1 = (s & 1) ? (xw1[s / 2] >> 16) : (xw1[s / 2] & 0xffffu);
+                for (int s = 0; s < 8; ++s)
                     *reinterpret_cast<uint32_t *>(&xT[(8 * chunk + s) * R2 + 2 * pr]) =
-                        lo0 | (lo1 << 16);
-                }
+                        pair(sx[p][0], sx[p][1], s);
                 if constexpr (!GRAD) {
-                    const uint32_t *yw0 = reinterpret_cast<const uint32_t *>(&sy[p][0]);
-                    const uint32_t *yw1 = reinterpret_cast<const uint32_t *>(&sy[p][1]);
+                    // column sums from the same pairs: a two-term bf16 dot
+                    // product with (1, 1), exact products summed in fp32
+                    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+                    const bf2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
                     for (int s = 0; s < 8; ++s) {
-                        const uint32_t a0 = (s & 1) ? (yw0[s / 2] >> 16) : (yw0[s / 2] & 0xffffu);
-                        const uint32_t a1 = (s & 1) ? (yw1[s / 2] >> 16) : (yw1[s / 2] & 0xffffu);
-                        *reinterpret_cast<uint32_t *>(&yT[0][(8 * chunk + s) * R2 + 2 * pr]) =
-                            a0 | (a1 << 16);
-                        cx[p][s] += xv[0][s] + xv[1][s];
-                        cy[p][s] += yv[0][s] + yv[1][s];
+                        const uint32_t px = pair(sx[p][0], sx[p][1], s);
+                        const uint32_t py = pair(sy[p][0], sy[p][1], s);
+                        *reinterpret_cast<uint32_t *>(&yT[0][(8 * chunk + s) * R2 + 2 * pr]) = py;
+                        cx[p][s] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, px), ones,
+                                                                   cx[p][s], false);
+                        cy[p][s] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, py), ones,
+                                                                   cy[p][s], false);
                     }
                 } else {
+                    float xv[2][8], yv[2][8];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        StBF16::widen(sx[p][u], xv[u]);
+                        StBF16::widen(sy[p][u], yv[u]);
+                    }
 #pragma unroll
                     for (int s = 0; s < 8; ++s) {
                         __bf16 h0, l0, h1, l1;
