@@ -56,6 +56,29 @@ __device__ __forceinline__ void unpack8(bf8 b, float *o)
     }
 }
 
+// Element s of two 8 x bf16 vectors as one bf16 pair (t0's in the low half)
+__device__ __forceinline__ uint32_t pair_bf16(const uint4 &t0, const uint4 &t1, int s)
+{
+    const uint32_t w0 = reinterpret_cast<const uint32_t *>(&t0)[s / 2];
+    const uint32_t w1 = reinterpret_cast<const uint32_t *>(&t1)[s / 2];
+    return (s & 1) ? __builtin_amdgcn_perm(w1, w0, 0x07060302u)
+                   : __builtin_amdgcn_perm(w1, w0, 0x05040100u);
+}
+
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+
+// sum of the 8 bf16 of b, added to c (bf16 dot2 against (1, 1): the
+// products are exact, the sums fp32)
+__device__ __forceinline__ float sum8(bf8 b, float c)
+{
+    const uint4 u = __builtin_bit_cast(uint4, b);
+    const bf2 ones = {(__bf16)1.f, (__bf16)1.f};
+    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.x), ones, c, false);
+    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.y), ones, c, false);
+    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.z), ones, c, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.w), ones, c, false);
+}
+
 constexpr int kApplyThreads = 256;
 
 // ============================================================ apply
@@ -437,25 +460,18 @@ __global__ __launch_bounds__(256) void k_reduce_bf(
             if (PC % NT == 0 || q < PC) {
                 const int chunk = q / (TT / 2), pr = q % (TT / 2);
                 // tokens 2 pr, 2 pr + 1 of column 8 chunk + s as one bf16 pair
-                auto pair = [&](const uint4 &t0, const uint4 &t1, int s) {
-                    const uint32_t w0 = reinterpret_cast<const uint32_t *>(&t0)[s / 2];
-                    const uint32_t w1 = reinterpret_cast<const uint32_t *>(&t1)[s / 2];
-                    return (s & 1) ? __builtin_amdgcn_perm(w1, w0, 0x07060302u)
-                                   : __builtin_amdgcn_perm(w1, w0, 0x05040100u);
-                };
 #pragma unroll
                 for (int s = 0; s < 8; ++s)
                     *reinterpret_cast<uint32_t *>(&xT[(8 * chunk + s) * R2 + 2 * pr]) =
-                        pair(sx[p][0], sx[p][1], s);
+                        pair_bf16(sx[p][0], sx[p][1], s);
                 if constexpr (!GRAD) {
                     // column sums from the same pairs: a two-term bf16 dot
                     // product with (1, 1), exact products summed in fp32
-                    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
                     const bf2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
                     for (int s = 0; s < 8; ++s) {
-                        const uint32_t px = pair(sx[p][0], sx[p][1], s);
-                        const uint32_t py = pair(sy[p][0], sy[p][1], s);
+                        const uint32_t px = pair_bf16(sx[p][0], sx[p][1], s);
+                        const uint32_t py = pair_bf16(sy[p][0], sy[p][1], s);
                         *reinterpret_cast<uint32_t *>(&yT[0][(8 * chunk + s) * R2 + 2 * pr]) = py;
                         cx[p][s] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, px), ones,
                                                                    cx[p][s], false);
@@ -661,15 +677,10 @@ struct ChunkRows {
             const int q = tid + p * NT;
             if (PC % NT == 0 || q < PC) {
                 const int chunk = q / (kCc / 2), pr = q % (kCc / 2);
-                const uint32_t *w0 = reinterpret_cast<const uint32_t *>(&r[p][0]);
-                const uint32_t *w1 = reinterpret_cast<const uint32_t *>(&r[p][1]);
 #pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const uint32_t a = (s & 1) ? (w0[s / 2] >> 16) : (w0[s / 2] & 0xffffu);
-                    const uint32_t b = (s & 1) ? (w1[s / 2] >> 16) : (w1[s / 2] & 0xffffu);
+                for (int s = 0; s < 8; ++s)
                     *reinterpret_cast<uint32_t *>(&lds[(8 * chunk + s) * kRT + 2 * pr]) =
-                        a | (b << 16);
-                }
+                        pair_bf16(r[p][0], r[p][1], s);
             }
         }
     }
@@ -716,15 +727,15 @@ __device__ __forceinline__ void stage_a_tr(const ChunkRows<D, NT> &rg, const Chu
             StBF16::widen(rg.r[p][1], g1);
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                __bf16 h0, l0, h1, l1;
-                split_bf16(g0[s] * cb.r[p][0].y, h0, l0);
-                split_bf16(g1[s] * cb.r[p][1].y, h1, l1);
-                *reinterpret_cast<uint32_t *>(&hiT[(8 * chunk + s) * kRT + 2 * pr]) =
-                    (uint32_t)__builtin_bit_cast(uint16_t, h0) |
-                    ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                // tokens 2 pr, 2 pr + 1 of column 8 chunk + s: hi and lo pairs
+                const float a0 = g0[s] * cb.r[p][0].y, a1 = g1[s] * cb.r[p][1].y;
+                const bf2 hv = {(__bf16)a0, (__bf16)a1};
+                const uint32_t hw = __builtin_bit_cast(uint32_t, hv);
+                const bf2 lv = {(__bf16)(a0 - __uint_as_float(hw << 16)),
+                                (__bf16)(a1 - __uint_as_float(hw & 0xffff0000u))};
+                *reinterpret_cast<uint32_t *>(&hiT[(8 * chunk + s) * kRT + 2 * pr]) = hw;
                 *reinterpret_cast<uint32_t *>(&loT[(8 * chunk + s) * kRT + 2 * pr]) =
-                    (uint32_t)__builtin_bit_cast(uint16_t, l0) |
-                    ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+                    __builtin_bit_cast(uint32_t, lv);
             }
         }
     }
@@ -774,6 +785,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal_bf(
     __shared__ __attribute__((aligned(16))) uint16_t kT[D * kRT];
     __shared__ __attribute__((aligned(16))) uint16_t vT[D * kRT];
     __shared__ float wx[kCc * WP];  // Q_c K_c^T
+    __shared__ float qzx[NCB][kCc];  // q.z over each wave's 32 columns
     __shared__ __attribute__((aligned(16))) float vz[D];
     __shared__ __attribute__((aligned(16))) float vu[D];
 
@@ -822,13 +834,23 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal_bf(
     for (int64_t round = 0; round < nrounds; ++round) {
         const int64_t t0 = beg + round * kCc;
         const bool more = round + 1 < nrounds;
-        // (1) the prefix state applied to the chunk's queries, and q.z
+        // (1) the prefix state applied to the chunk's queries, and q.z over
+        // this wave's 32 columns (the partials meet in LDS at B1)
         f16v acc = zero16();
-        float qz = 0.f;
         {
             const uint16_t *qrow = &qs[j * LDX];
-            int zo = 4 * h;
-            asm volatile("" : "+v"(zo));  // z changes per chunk: keep its reads here
+            float p = 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; e += 8) {
+                float xf[8];
+                unpack8(*reinterpret_cast<const bf8 *>(qrow + 32 * cb + 16 * h + e), xf);
+                const float *zr = &vz[32 * cb + 16 * h + e];
+                p += dot4(f4{xf[0], xf[1], xf[2], xf[3]}, *reinterpret_cast<const f4 *>(zr)) +
+                     dot4(f4{xf[4], xf[5], xf[6], xf[7]}, *reinterpret_cast<const f4 *>(zr + 4));
+            }
+            p += __shfl_xor(p, 32, 64);
+            if (h == 0)
+                qzx[cb][j] = p;
 #pragma unroll
             for (int t = 0; t < NCB; ++t)
 #pragma unroll
@@ -839,13 +861,6 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal_bf(
                     split8(sacc[t], p, ahi, alo);
                     acc = mma16(ahi, x, acc);
                     acc = mma16(alo, x, acc);
-                    float xf[8];
-                    unpack8(x, xf);
-                    const f4 z0 = *reinterpret_cast<const f4 *>(&vz[zo + d0]);
-                    const f4 z1 = *reinterpret_cast<const f4 *>(&vz[zo + d0 + 8]);
-                    qz += dot4(f4{xf[0], xf[1], xf[2], xf[3]}, z0) +
-                          dot4(f4{xf[4], xf[5], xf[6], xf[7]}, z1);
-                    asm volatile("" : "+v"(qz));
                     if (t == 0 && p == 0) {
 #pragma unroll
                         for (int q = 0; q < 4; ++q)
@@ -891,25 +906,19 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal_bf(
             for (int t = 0; t < NCB; ++t) {
                 const bf8 kcol = col_at(kT, 32 * t + j, kk, h);
                 sacc[t] = mma16(kcol, vcol, sacc[t]);
-                if (t == cb) {
-                    float kf[8];
-                    unpack8(kcol, kf);
-#pragma unroll
-                    for (int s = 0; s < 8; ++s)
-                        zc += kf[s];
-                }
+                if (t == cb)
+                    zc = sum8(kcol, zc);
             }
-            float vf[8];
-            unpack8(vcol, vf);
-#pragma unroll
-            for (int s = 0; s < 8; ++s)
-                uc += vf[s];
+            uc = sum8(vcol, uc);
             __builtin_amdgcn_sched_barrier(0);
         }
         rs += __shfl_xor(rs, 32, 64);
         zc += __shfl_xor(zc, 32, 64);
         uc += __shfl_xor(uc, 32, 64);
-        qz += __shfl_xor(qz, 32, 64);
+        float qz = 0.f;
+#pragma unroll
+        for (int c2 = 0; c2 < NCB; ++c2)
+            qz += qzx[c2][j];
         // (4) normalised rows of the chunk, stored during the next product
         const float den = (float)t0 + qz + rs;
         const float inv = 1.f / den;
@@ -965,7 +974,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
     __shared__ __attribute__((aligned(16))) uint16_t vT[D * kRT];
     __shared__ float wx[kCc * WP];       // Q_c K_c^T
     __shared__ float gx[kCc * WP];       // G_c V_c^T
-    __shared__ float xq[NCB][kCc];       // shares of q_i.y_i
+    __shared__ float xq[NCB][kCc];       // shares of q_i.y_i + g_i.u
+    __shared__ float xz[NCB][kCc];       // shares of q_i.z
     __shared__ __attribute__((aligned(16))) float vz[D];
     __shared__ __attribute__((aligned(16))) float vu[D];
 
@@ -1025,13 +1035,23 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
     for (int64_t round = 0; round < nrounds; ++round) {
         const int64_t t0 = beg + round * kCc;
         const bool more = round + 1 < nrounds;
-        // (1) y = S g for the chunk's rows, with g.u and q.z at the same columns
+        // (1) y = S g for the chunk's rows; g.u and q.z over this wave's 32
+        // columns (the shares meet in LDS at B1)
         f16v acc = zero16();
         float gu = 0.f, qz = 0.f;
         {
             const uint16_t *grow = &gs[j * LDX], *qrow = &qs[j * LDX];
-            int vo = 4 * h;
-            asm volatile("" : "+v"(vo));  // z and u change per chunk
+#pragma unroll
+            for (int e = 0; e < 16; e += 8) {
+                const int d = 32 * cb + 16 * h + e;
+                float xf[8], qf[8];
+                unpack8(*reinterpret_cast<const bf8 *>(grow + d), xf);
+                unpack8(*reinterpret_cast<const bf8 *>(qrow + d), qf);
+                gu += dot4(f4{xf[0], xf[1], xf[2], xf[3]}, *reinterpret_cast<const f4 *>(&vu[d])) +
+                      dot4(f4{xf[4], xf[5], xf[6], xf[7]}, *reinterpret_cast<const f4 *>(&vu[d + 4]));
+                qz += dot4(f4{qf[0], qf[1], qf[2], qf[3]}, *reinterpret_cast<const f4 *>(&vz[d])) +
+                      dot4(f4{qf[4], qf[5], qf[6], qf[7]}, *reinterpret_cast<const f4 *>(&vz[d + 4]));
+            }
 #pragma unroll
             for (int t = 0; t < NCB; ++t)
 #pragma unroll
@@ -1042,18 +1062,6 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
                     split8(sacc[t], p, ahi, alo);
                     acc = mma16(ahi, x, acc);
                     acc = mma16(alo, x, acc);
-                    float xf[8], qf[8];
-                    unpack8(x, xf);
-                    unpack8(row_at(qrow, d0 + 4 * h), qf);
-                    const f4 z0 = *reinterpret_cast<const f4 *>(&vz[vo + d0]);
-                    const f4 z1 = *reinterpret_cast<const f4 *>(&vz[vo + d0 + 8]);
-                    const f4 u0 = *reinterpret_cast<const f4 *>(&vu[vo + d0]);
-                    const f4 u1 = *reinterpret_cast<const f4 *>(&vu[vo + d0 + 8]);
-                    gu += dot4(f4{xf[0], xf[1], xf[2], xf[3]}, u0) +
-                          dot4(f4{xf[4], xf[5], xf[6], xf[7]}, u1);
-                    qz += dot4(f4{qf[0], qf[1], qf[2], qf[3]}, z0) +
-                          dot4(f4{qf[4], qf[5], qf[6], qf[7]}, z1);
-                    asm volatile("" : "+v"(gu), "+v"(qz));
                     if (t == 0 && p == 0) {
 #pragma unroll
                         for (int q = 0; q < 4; ++q)
@@ -1079,9 +1087,13 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
                       __uint_as_float(u.y << 16) * acc[4 * q + 2] +
                       __uint_as_float(u.y & 0xffff0000u) * acc[4 * q + 3];
             }
+            pq += gu;
             pq += __shfl_xor(pq, 32, 64);
-            if (h == 0)
+            qz += __shfl_xor(qz, 32, 64);
+            if (h == 0) {
                 xq[cb][j] = pq;
+                xz[cb][j] = qz;
+            }
         }
         __syncthreads();  // B1
         if (more) {
@@ -1108,15 +1120,15 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
             }
         rs += __shfl_xor(rs, 32, 64);
         cw += __shfl_xor(cw, 32, 64);
-        gu += __shfl_xor(gu, 32, 64);
-        qz += __shfl_xor(qz, 32, 64);
-        float qy = 0.f;
+        float qyu = 0.f, qzs = 0.f;  // q.y + g.u and q.z over all columns
 #pragma unroll
-        for (int pp = 0; pp < NCB; ++pp)
-            qy += xq[pp][j];
-        const float den = (float)t0 + qz + rs;
+        for (int pp = 0; pp < NCB; ++pp) {
+            qyu += xq[pp][j];
+            qzs += xz[pp][j];
+        }
+        const float den = (float)t0 + qzs + rs;
         const float inv = 1.f / den;
-        const float c = (gu + qy + cw) * inv * inv;
+        const float c = (qyu + cw) * inv * inv;
         const float cden = c * den;
         float zc = 0.f, uc = 0.f;
 #pragma unroll
@@ -1137,19 +1149,10 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
             for (int t = 0; t < NCB; ++t) {
                 const bf8 vcol = col_at(vT, 32 * t + j, kk, h);
                 sacc[t] = mma16(vcol, kcol, sacc[t]);
-                if (t == cb) {
-                    float vf[8];
-                    unpack8(vcol, vf);
-#pragma unroll
-                    for (int s2 = 0; s2 < 8; ++s2)
-                        uc += vf[s2];
-                }
+                if (t == cb)
+                    uc = sum8(vcol, uc);
             }
-            float kf[8];
-            unpack8(kcol, kf);
-#pragma unroll
-            for (int s2 = 0; s2 < 8; ++s2)
-                zc += kf[s2];
+            zc = sum8(kcol, zc);
             __builtin_amdgcn_sched_barrier(0);
         }
         zc += __shfl_xor(zc, 32, 64);
@@ -1342,12 +1345,7 @@ __device__ __forceinline__ void kv_pass_bf(
                     sacc[t] = mma16(qcol, ahi, sacc[t]);
                     sacc[t] = mma16(qcol, alo, sacc[t]);
                 }
-                float af[8], lf[8];
-                unpack8(ahi, af);
-                unpack8(alo, lf);
-#pragma unroll
-                for (int s2 = 0; s2 < 8; ++s2)
-                    vc += af[s2] + lf[s2];
+                vc = sum8(alo, sum8(ahi, vc));
             }
             __builtin_amdgcn_sched_barrier(0);
         }
