@@ -357,10 +357,9 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce_nc(
 //
 // The round loop is software-pipelined so that the MFMA chain of a round
 // runs with the other work in its shadow: the stores of the previous
-// round's rows are issued between its k-blocks, and in the forward q_j.z
-// is accumulated from the very operands the MFMAs consume (lane half h sees
-// half of row j's columns; the halves are added after the loop), so the
-// normalisation needs no exchange between waves.
+// round's rows are issued between its k-blocks.  In the forward each wave
+// forms q_j.z over its own 32 columns of the staged row only; the partials
+// meet in LDS at the round's barrier, after which the rows are normalised.
 template <class ST, int D, int KIND>
 __global__ __launch_bounds__(kApplyThreads) void k_apply_nc(
     const typename ST::T *__restrict__ X, const typename ST::T *__restrict__ X2,
@@ -385,6 +384,9 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_nc(
     static_assert(TR * CPR % kApplyThreads == 0, "staging split");
     __shared__ __attribute__((aligned(16))) float xs[2][TR * LDX];
     __shared__ __attribute__((aligned(16))) float vz[KIND == 0 ? D : 4];  // z
+    // forward: q.z of each row over each wave's 32 columns (added up after
+    // the round's barrier)
+    __shared__ float xch[KIND == 0 ? 2 : 1][NRG][NCB][32];
 
     const int sub = (KIND == 2) ? (int)(blockIdx.x & 1) : 0;
     const int64_t b = (KIND == 2) ? (blockIdx.x >> 1) : blockIdx.x;
@@ -481,36 +483,17 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_nc(
         const int buf = (int)(round & 1);
         const float *xt = &xs[buf][(32 * rg + j) * LDX + 4 * h];
         f16v acc = zero16();
-        float qz = 0.f;
         // LDS operands one k-block ahead of the MFMAs; the scheduling barrier
         // per k-block stops the compiler from hoisting every read of the tile
-        f4 xn = *reinterpret_cast<const f4 *>(xt), zn;
-        // z is the same every round: an opaque offset keeps its reads inside
-        // the loop (hoisted, they would hold D/2 registers for the whole loop)
-        int zo = 4 * h;
-        asm volatile("" : "+v"(zo));
-        if constexpr (KIND == 0)
-            zn = *reinterpret_cast<const f4 *>(&vz[zo]);
+        f4 xn = *reinterpret_cast<const f4 *>(xt);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const f4 x = xn;
-            f4 z;
-            if constexpr (KIND == 0)
-                z = zn;
-            if (kb + 1 < KB) {
+            if (kb + 1 < KB)
                 xn = *reinterpret_cast<const f4 *>(xt + (kb + 1) * 8);
-                if constexpr (KIND == 0)
-                    zn = *reinterpret_cast<const f4 *>(&vz[zo + (kb + 1) * 8]);
-            }
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 acc = mma32(am[kb][r], x[r], acc);
-            if constexpr (KIND == 0) {
-                qz += dot4(x, z);
-                // keep the sum here: sunk below the loop, it would keep every
-                // k-block's operands alive until the end of the round
-                asm volatile("" : "+v"(qz));
-            }
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 if (kb == q * (KB / 4))
@@ -520,15 +503,16 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_nc(
 
         const int64_t row = beg + round * TR + 32 * rg + j;
         if constexpr (KIND == 0) {
-            qz += __shfl_xor(qz, 32, 64);
-            const float den = (float)N + qz;
-            const float inv = 1.f / den;
+            // q.z over this wave's 32 columns (lane half h: 16 of them)
+            const float *qr = &xs[buf][(32 * rg + j) * LDX + 32 * cb + 16 * h];
+            const float *zr = &vz[32 * cb + 16 * h];
+            float p = 0.f;
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                pend[q] = f4{(acc[4 * q] + ev[q][0]) * inv, (acc[4 * q + 1] + ev[q][1]) * inv,
-                             (acc[4 * q + 2] + ev[q][2]) * inv, (acc[4 * q + 3] + ev[q][3]) * inv};
-            if (den_out != nullptr && row < end && h == 0 && cb == 0)
-                den_out[bh * N + row] = den;
+            for (int e = 0; e < 16; e += 4)
+                p += dot4(*reinterpret_cast<const f4 *>(qr + e), *reinterpret_cast<const f4 *>(zr + e));
+            p += __shfl_xor(p, 32, 64);
+            if (h == 0)
+                xch[buf][rg][cb][j] = p;
         } else {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -545,6 +529,20 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_nc(
                 fetch_round(beg + (round + 2) * TR);
         }
         __syncthreads();
+        if constexpr (KIND == 0) {
+            float qz = 0.f;
+#pragma unroll
+            for (int c2 = 0; c2 < NCB; ++c2)
+                qz += xch[buf][rg][c2][j];
+            const float den = (float)N + qz;
+            const float inv = 1.f / den;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                pend[q] = f4{(acc[4 * q] + ev[q][0]) * inv, (acc[4 * q + 1] + ev[q][1]) * inv,
+                             (acc[4 * q + 2] + ev[q][2]) * inv, (acc[4 * q + 3] + ev[q][3]) * inv};
+            if (den_out != nullptr && row < end && h == 0 && cb == 0)
+                den_out[bh * N + row] = den;
+        }
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q)
