@@ -558,12 +558,14 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_nc(
 //   dS = sum_i q_i a_i^T,  r = sum_i c_i q_i,  t = sum_i a_i.
 // The workgroup has two roles of four waves each, so that no wave holds both
 // a D x D slice of S (the dQ product) and one of dS (the reduction):
-//   role 0 (waves 0-3): the dQ rows, exactly as k_apply_nc KIND 1;
+//   role 0 (waves 0-3): the dQ rows (y = S g as k_apply_nc applies its
+//                       state), normalised after the round's barrier;
 //   role 1 (waves 4-7): dS[:, 32*cb ..] over the round's rows, with
-//                       a_i formed from its own den_i; r needs c_i, which
-//                       role 0 hands over through LDS one round later.
-// Both roles stage the rows (Q and dO, fp32, double-buffered) together and
-// meet at one barrier per round.
+//                       a_i = g_i / den_i; r needs c_i, which role 0 hands
+//                       over through LDS one round later.
+// Both roles stage the rows (Q and dO, fp32, double-buffered) together,
+// forming 1/den_i of each staged row on the way, and meet at one barrier per
+// round.
 template <class ST, int D>
 __global__ __launch_bounds__(512) void k_bwd_q_nc(
     const typename ST::T *__restrict__ G, const typename ST::T *__restrict__ Q,
@@ -588,6 +590,7 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
     __shared__ __attribute__((aligned(16))) float vl[2 * D];        // z | u
     __shared__ float xch[2][NRG][NCB][32][2];  // dO.u and q.(S dO) partials
     __shared__ float cx[2][NRG][32];           // c_i of the round's rows
+    __shared__ float ivx[2][TR];               // 1/den_i of the round's rows
 
     const int64_t bh = blockIdx.x / nseg;
     const int seg = (int)(blockIdx.x % nseg);
@@ -611,38 +614,45 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
             sq[p] = *reinterpret_cast<const uint4 *>(qh + row * D + VEC * (c % CPR));
         }
     };
-    auto stage_one = [&](float *lds, const uint4 &src, int c, bool ok) {
-        float v[VEC];
+    // widened chunk to LDS (zeros for rows past the end); returns the values
+    auto stage_one = [&](float *lds, const uint4 &src, int c, bool ok, float (&v)[VEC]) {
         if constexpr (VEC == 4)
             StF32::widen(src, v);
         else
             StBF16::widen(src, v);
+#pragma unroll
+        for (int x = 0; x < VEC; ++x)
+            v[x] = ok ? v[x] : 0.f;
         float *dst = lds + (c / CPR) * LDX + VEC * (c % CPR);
 #pragma unroll
         for (int x = 0; x < VEC; x += 4)
-            *reinterpret_cast<f4 *>(dst + x) =
-                ok ? f4{v[x], v[x + 1], v[x + 2], v[x + 3]} : f4{0.f, 0.f, 0.f, 0.f};
+            *reinterpret_cast<f4 *>(dst + x) = f4{v[x], v[x + 1], v[x + 2], v[x + 3]};
     };
+    // Staging also forms den_i = N + q_i.z of every staged row, once per row:
+    // the CPR consecutive threads that stage a row add their chunks' dot
+    // products by shuffles (a row's chunks lie in one wave), and the row's
+    // first thread writes 1/den_i to LDS for both roles.
+    static_assert(CPR <= 64 && 64 % CPR == 0, "a staged row lies in one wave");
     auto stage_round = [&](int buf, int64_t r0) {
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
             const int c = tid + p * NT;
             const bool ok = r0 + c / CPR < end;
-            stage_one(xs[buf], sg[p], c, ok);
-            stage_one(qs[buf], sq[p], c, ok);
-        }
-    };
-    // den of row j of this wave's tile in full (lane half h sums half the
-    // columns): the same value in both halves
-    auto inv_den = [&](int buf) {
-        const float *qr = &qs[buf][(32 * rg + j) * LDX + (D / 2) * h];
-        float qz = 0.f;
+            float gv[VEC], qv[VEC];
+            stage_one(xs[buf], sg[p], c, ok, gv);
+            stage_one(qs[buf], sq[p], c, ok, qv);
+            const float *zc = &vl[VEC * (c % CPR)];
+            float pz = 0.f;
 #pragma unroll
-        for (int x = 0; x < D / 2; x += 4)
-            qz += dot4(*reinterpret_cast<const f4 *>(qr + x),
-                       *reinterpret_cast<const f4 *>(&vl[(D / 2) * h + x]));
-        qz += __shfl_xor(qz, 32, 64);
-        return 1.f / ((float)N + qz);
+            for (int x = 0; x < VEC; x += 4)
+                pz += dot4(f4{qv[x], qv[x + 1], qv[x + 2], qv[x + 3]},
+                           *reinterpret_cast<const f4 *>(zc + x));
+#pragma unroll
+            for (int o = 1; o < CPR; o <<= 1)
+                pz += __shfl_xor(pz, o, 64);
+            if (c % CPR == 0)
+                ivx[buf][c / CPR] = 1.f / ((float)N + pz);
+        }
     };
 
     const int64_t nrounds = (end - beg + TR - 1) / TR;
@@ -660,6 +670,7 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
         for (int r = 0; r < 4; ++r)
             am[kb][r] = v[r];
     }
+    __syncthreads();  // z in LDS before the first staging reads it
     stage_round(0, beg);
     drain_loads();
     if (nrounds > 1)
@@ -673,6 +684,8 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
         for (int64_t round = 0; round < nrounds; ++round) {
             const int buf = (int)(round & 1);
             const int64_t row = beg + round * TR + 32 * rg + j;
+            // (read before the barrier: the slot is restaged one round later)
+            const float inv = ivx[buf][32 * rg + j];
             const float *xt = &xs[buf][(32 * rg + j) * LDX + 4 * h];
             f16v acc = zero16();
             f4 xn = *reinterpret_cast<const f4 *>(xt);
@@ -686,7 +699,6 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
                     acc = mma32(am[kb][r], x[r], acc);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            const float inv = inv_den(buf);
             // partial dO.u and q.(S dO) over this block's columns
             {
                 const float *xr = &xs[buf][(32 * rg + j) * LDX + 32 * cb + 4 * h];
@@ -737,7 +749,7 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
             gacc[t] = zero16();
         for (int64_t round = 0; round < nrounds; ++round) {
             const int buf = (int)(round & 1);
-            const float inv = inv_den(buf);
+            const float inv = ivx[buf][32 * rg + j];
             // dS[:, block cb] += Q^T A over the tile's rows (k = row; rows
             // 2kk + h per MFMA step), operands one step ahead
             const float *qt = &qs[buf][(32 * rg + h) * LDX + j];
