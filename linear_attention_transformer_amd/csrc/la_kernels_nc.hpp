@@ -628,18 +628,17 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
         for (int x = 0; x < VEC; x += 4)
             *reinterpret_cast<f4 *>(dst + x) = f4{v[x], v[x + 1], v[x + 2], v[x + 3]};
     };
-    // Staging also forms den_i = N + q_i.z of every staged row, once per row:
-    // the CPR consecutive threads that stage a row add their chunks' dot
-    // products by shuffles (a row's chunks lie in one wave), and the row's
-    // first thread writes 1/den_i to LDS for both roles.
+    // Staging also forms den_i = N + q_i.z of every staged row, once per row
+    // (the CPR consecutive threads that stage a row add their chunks' dot
+    // products by shuffles: a row's chunks lie in one wave), stores the dO
+    // row already divided by it, a_i = g_i / den_i, and keeps 1/den_i in LDS.
     static_assert(CPR <= 64 && 64 % CPR == 0, "a staged row lies in one wave");
     auto stage_round = [&](int buf, int64_t r0) {
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
             const int c = tid + p * NT;
             const bool ok = r0 + c / CPR < end;
-            float gv[VEC], qv[VEC];
-            stage_one(xs[buf], sg[p], c, ok, gv);
+            float qv[VEC];
             stage_one(qs[buf], sq[p], c, ok, qv);
             const float *zc = &vl[VEC * (c % CPR)];
             float pz = 0.f;
@@ -650,8 +649,19 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
 #pragma unroll
             for (int o = 1; o < CPR; o <<= 1)
                 pz += __shfl_xor(pz, o, 64);
+            const float inv = 1.f / ((float)N + pz);
             if (c % CPR == 0)
-                ivx[buf][c / CPR] = 1.f / ((float)N + pz);
+                ivx[buf][c / CPR] = inv;
+            float gv[VEC];
+            if constexpr (VEC == 4)
+                StF32::widen(sg[p], gv);
+            else
+                StBF16::widen(sg[p], gv);
+            float *dst = xs[buf] + (c / CPR) * LDX + VEC * (c % CPR);
+#pragma unroll
+            for (int x = 0; x < VEC; x += 4)
+                *reinterpret_cast<f4 *>(dst + x) =
+                    ok ? f4{gv[x], gv[x + 1], gv[x + 2], gv[x + 3]} * inv : f4{0.f, 0.f, 0.f, 0.f};
         }
     };
 
@@ -699,7 +709,7 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
                     acc = mma32(am[kb][r], x[r], acc);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            // partial dO.u and q.(S dO) over this block's columns
+            // y' = S a in acc; partial a.u and q.y' over this block's columns
             {
                 const float *xr = &xs[buf][(32 * rg + j) * LDX + 32 * cb + 4 * h];
                 const float *qr = &qs[buf][(32 * rg + j) * LDX + 32 * cb + 4 * h];
@@ -731,12 +741,12 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
                 rz += xch[buf][rg][c2][j][0];
                 qy += xch[buf][rg][c2][j][1];
             }
-            const float c = (rz + qy) * inv * inv;  // (a.u + q.y_true) / den
+            const float c = (rz + qy) * inv;  // (a.u + q.S a) / den
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const f4 z = *reinterpret_cast<const f4 *>(&vl[32 * cb + 8 * q + 4 * h]);
-                const f4 o = {acc[4 * q] * inv - c * z[0], acc[4 * q + 1] * inv - c * z[1],
-                              acc[4 * q + 2] * inv - c * z[2], acc[4 * q + 3] * inv - c * z[3]};
+                const f4 o = {acc[4 * q] - c * z[0], acc[4 * q + 1] - c * z[1],
+                              acc[4 * q + 2] - c * z[2], acc[4 * q + 3] - c * z[3]};
                 if (row < end)
                     io::store4(oh + row * D + 32 * cb + 8 * q + 4 * h, o);
             }
@@ -749,38 +759,30 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
             gacc[t] = zero16();
         for (int64_t round = 0; round < nrounds; ++round) {
             const int buf = (int)(round & 1);
-            const float inv = ivx[buf][32 * rg + j];
             // dS[:, block cb] += Q^T A over the tile's rows (k = row; rows
-            // 2kk + h per MFMA step), operands one step ahead
-            const float *qt = &qs[buf][(32 * rg + h) * LDX + j];
+            // 2kk + h per MFMA step), operands one step ahead.  Lane j reads
+            // NCB consecutive columns NCB j .. of its q row as one vector:
+            // tile t takes column NCB j + t, so its output row m is dS row
+            // NCB m + t.
+            const float *qt = &qs[buf][(32 * rg + h) * LDX + NCB * j];
+            const float *qc = &qs[buf][(32 * rg + h) * LDX + 32 * cb + j];
             const float *gt = &xs[buf][(32 * rg + h) * LDX + 32 * cb + j];
-            float an[NCB], gn = gt[0];
-#pragma unroll
-            for (int t = 0; t < NCB; ++t)
-                an[t] = qt[32 * t];
+            typedef float fv __attribute__((ext_vector_type(NCB)));
+            fv an = *reinterpret_cast<const fv *>(qt);
+            float gn = gt[0];
 #pragma unroll
             for (int kk = 0; kk < 16; ++kk) {
-                float a[NCB];
-#pragma unroll
-                for (int t = 0; t < NCB; ++t)
-                    a[t] = an[t];
-                const float g = gn;
+                const fv a = an;
+                const float bv = gn;  // a_i = g_i / den_i, staged
                 if (kk + 1 < 16) {
                     gn = gt[(2 * kk + 2) * LDX];
-#pragma unroll
-                    for (int t = 0; t < NCB; ++t)
-                        an[t] = qt[(2 * kk + 2) * LDX + 32 * t];
+                    an = *reinterpret_cast<const fv *>(qt + (2 * kk + 2) * LDX);
                 }
-                const float i0 = __int_as_float(
-                    __builtin_amdgcn_readlane(__float_as_int(inv), 2 * kk));
-                const float i1 = __int_as_float(
-                    __builtin_amdgcn_readlane(__float_as_int(inv), 2 * kk + 1));
-                const float bv = g * (h ? i1 : i0);
                 tacc += bv;
 #pragma unroll
                 for (int t = 0; t < NCB; ++t)
                     gacc[t] = mma32(a[t], bv, gacc[t]);
-                qcur[kk] = qt[2 * kk * LDX + 32 * cb];
+                qcur[kk] = qc[2 * kk * LDX];
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (round + 1 < nrounds) {
@@ -845,7 +847,7 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
         for (int t = 0; t < NCB; ++t)
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                out[(32 * t + 8 * (i / 4) + 4 * h + (i % 4)) * D + 32 * cb + j] = gacc[t][i];
+                out[(NCB * (8 * (i / 4) + 4 * h + (i % 4)) + t) * D + 32 * cb + j] = gacc[t][i];
         if (h == 0) {
             out[D * D + 32 * cb + j] = racc;
             out[D * D + D + 32 * cb + j] = tacc;
