@@ -136,6 +136,31 @@ __device__ __forceinline__ void load_vec(const typename ST::T *p, float *o)
     }
 }
 
+// load_vec through a raw buffer descriptor (voffset per lane, soffset uniform)
+template <class ST, int VW>
+__device__ __forceinline__ void buf_load_vec(__amdgpu_buffer_rsrc_t rs, int vo, int so, float *o)
+{
+    if constexpr (sizeof(typename ST::T) == 4) {
+        if constexpr (VW == 2) {
+            const float2 x =
+                __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rs, vo, so, 0));
+            o[0] = x.x;
+            o[1] = x.y;
+        } else {
+            o[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, vo, so, 0));
+        }
+    } else {
+        if constexpr (VW == 2) {
+            const uint32_t x = __builtin_amdgcn_raw_buffer_load_b32(rs, vo, so, 0);
+            o[0] = __uint_as_float(x << 16);
+            o[1] = __uint_as_float(x & 0xffff0000u);
+        } else {
+            o[0] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, vo, so, 0)
+                                   << 16);
+        }
+    }
+}
+
 // ============================================================ reduction
 // Record (bh, seg): Mat[D][D] = sum_t X[t]^T Y'[t], cx[D] = sum_t w_t X[t],
 // cy[D] = sum_t Y'[t] over the rows t of the segment, where
@@ -178,6 +203,20 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce_nc(
     const T *xh = X + bh * N * D + m0 + VW * j;
     const T *yh = Y + bh * N * D + n0 + VW * j;
     const float2 *ch = GRAD ? reinterpret_cast<const float2 *>(cbuf) + bh * N : nullptr;
+    // The ring loads go through buffer descriptors over the segment's rows:
+    // the lane's offset is fixed and each step adds a uniform (scalar) one,
+    // and steps past the end read zeros.
+    const uint32_t rows = (uint32_t)(end - beg);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T *>(X + (bh * N + beg) * D), (short)0, (int)(rows * D * sizeof(T)), 0x00020000);
+    const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T *>(Y + (bh * N + beg) * D), (short)0, (int)(rows * D * sizeof(T)), 0x00020000);
+    __amdgpu_buffer_rsrc_t rcb;
+    if constexpr (GRAD)
+        rcb = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(cbuf + 2 * (bh * N + beg)),
+                                                (short)0, (int)(rows * 8), 0x00020000);
+    const int ox = (int)((h * D + m0 + VW * j) * sizeof(T));
+    const int oy = (int)((h * D + n0 + VW * j) * sizeof(T));
     const int64_t nsteps = (end - beg + 1) / 2;
 
     f16v acc[VW][VW];
@@ -192,17 +231,17 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce_nc(
         csx[a] = csy[a] = 0.f;
 
     float ra[U][VW], rb[U][VW], rc[U], rs[U];
-    // Prefetch ring over this wave's complete 2-token steps.  Addresses are
-    // clamped into the segment and no loaded value is masked: slots past the
-    // last step are fetched but never consumed, so nothing waits on a load
-    // before its use.  An odd last token is handled after the loop.
-    auto fetch = [&](int u, int64_t s) {
-        int64_t t = beg + 2 * s + h;
-        t = t < end ? t : end - 1;
-        load_vec<ST, VW>(xh + t * D, ra[u]);
-        load_vec<ST, VW>(yh + t * D, rb[u]);
+    // Prefetch ring over this wave's complete 2-token steps.  Slots past the
+    // last step are fetched (as zeros) but never consumed, so nothing waits on
+    // a load before its use.  An odd last token is handled after the loop.
+    auto fetch = [&](int u, int s) {
+        const int so = __builtin_amdgcn_readfirstlane(s) * (int)(2 * D * sizeof(T));
+        buf_load_vec<ST, VW>(rx, ox, so, ra[u]);
+        buf_load_vec<ST, VW>(ry, oy, so, rb[u]);
         if constexpr (GRAD) {
-            const float2 cs = ch[t];
+            const float2 cs = __builtin_bit_cast(
+                float2, __builtin_amdgcn_raw_buffer_load_b64(
+                            rcb, h * 8, __builtin_amdgcn_readfirstlane(s) * 16, 0));
             rc[u] = cs.x;
             rs[u] = cs.y;
         }
@@ -232,12 +271,12 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce_nc(
     const int full = mine / U;
 #pragma unroll
     for (int u = 0; u < U; ++u)
-        fetch(u, tsi + (int64_t)u * TS);
+        fetch(u, tsi + u * TS);
     for (int it = 0; it < full; ++it) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             consume(ra[u], rb[u], GRAD ? rc[u] : 1.f, GRAD ? rs[u] : 1.f);
-            fetch(u, tsi + ((int64_t)(it + 1) * U + u) * TS);
+            fetch(u, tsi + ((it + 1) * U + u) * TS);
             // keep step u's work and its refill together: the scheduler would
             // otherwise sink the refills to the end of the body and hoist the
             // column-sum adds of later steps, each forcing an early wait
