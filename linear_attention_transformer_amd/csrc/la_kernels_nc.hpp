@@ -444,14 +444,19 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_nc(
 
     // staging: thread's chunk p of a round covers row (tid + p*NT) / CPR,
     // columns VEC*((tid + p*NT) % CPR) ..
+    // rows load through a descriptor over the segment (rows past its end read
+    // zeros); the lane's offsets are fixed, the round's is a scalar
+    const __amdgpu_buffer_rsrc_t rsx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T *>(xh + beg * D), (short)0, (int)((end - beg) * D * sizeof(T)), 0x00020000);
     uint4 stg[PER];
     auto fetch_round = [&](int64_t r0) {
+        const int so = __builtin_amdgcn_readfirstlane((int)((r0 - beg) * D * sizeof(T)));
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
             const int c = tid + p * kApplyThreads;
-            int64_t row = r0 + c / CPR;
-            row = row < end ? row : end - 1;  // valid address; zeroed when staged
-            stg[p] = *reinterpret_cast<const uint4 *>(xh + row * D + VEC * (c % CPR));
+            stg[p] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                           rsx, (int)(((c / CPR) * D + VEC * (c % CPR)) * sizeof(T)), so, 0));
         }
     };
     auto stage_round = [&](int buf, int64_t r0) {
@@ -642,15 +647,22 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
     const T *gh = G + hoff, *qh = Q + hoff;
     T *oh = dQ + hoff;
 
+    // rows load through descriptors over the segment (rows past its end read
+    // zeros); the lane's offsets are fixed, the round's is a scalar
+    const int segb = (int)((end - beg) * D * sizeof(T));
+    const __amdgpu_buffer_rsrc_t rsg =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(gh + beg * D), (short)0, segb, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsq =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(qh + beg * D), (short)0, segb, 0x00020000);
     uint4 sg[PER], sq[PER];
     auto fetch_round = [&](int64_t r0) {
+        const int so = __builtin_amdgcn_readfirstlane((int)((r0 - beg) * D * sizeof(T)));
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
             const int c = tid + p * NT;
-            int64_t row = r0 + c / CPR;
-            row = row < end ? row : end - 1;  // valid address; zeroed when staged
-            sg[p] = *reinterpret_cast<const uint4 *>(gh + row * D + VEC * (c % CPR));
-            sq[p] = *reinterpret_cast<const uint4 *>(qh + row * D + VEC * (c % CPR));
+            const int vo = (int)(((c / CPR) * D + VEC * (c % CPR)) * sizeof(T));
+            sg[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsg, vo, so, 0));
+            sq[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsq, vo, so, 0));
         }
     };
     // widened chunk to LDS (zeros for rows past the end); returns the values
