@@ -459,11 +459,11 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_nc(
                            rsx, (int)(((c / CPR) * D + VEC * (c % CPR)) * sizeof(T)), so, 0));
         }
     };
-    auto stage_round = [&](int buf, int64_t r0) {
+    // (rows past the segment end were loaded as zeros)
+    auto stage_round = [&](int buf) {
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
             const int c = tid + p * kApplyThreads;
-            const bool ok = r0 + c / CPR < end;
             float v[VEC];
             if constexpr (VEC == 4)
                 StF32::widen(stg[p], v);
@@ -472,8 +472,7 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_nc(
             float *dst = &xs[buf][(c / CPR) * LDX + VEC * (c % CPR)];
 #pragma unroll
             for (int x = 0; x < VEC; x += 4)
-                *reinterpret_cast<f4 *>(dst + x) =
-                    ok ? f4{v[x], v[x + 1], v[x + 2], v[x + 3]} : f4{0.f, 0.f, 0.f, 0.f};
+                *reinterpret_cast<f4 *>(dst + x) = f4{v[x], v[x + 1], v[x + 2], v[x + 3]};
         }
     };
 
@@ -482,13 +481,15 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_nc(
 
     // this wave's block of A: am[kb][r] = A[32*cb + j][kb*8 + 4*h + r]
     float am[KB][4];
+    if (colread) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-        if (colread) {
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 am[kb][r] = st[(kb * 8 + 4 * h + r) * D + 32 * cb + j];
-        } else {
+    } else {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
             const f4 v = *reinterpret_cast<const f4 *>(st + (32 * cb + j) * D + kb * 8 + 4 * h);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
@@ -508,7 +509,7 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_nc(
     if constexpr (KIND == 0)
         for (int e = tid; e < D; e += kApplyThreads)
             vz[e] = st[D * D + e];
-    stage_round(0, beg);
+    stage_round(0);
     drain_loads();
     if (nrounds > 1)
         fetch_round(beg + TR);
@@ -568,7 +569,7 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_nc(
         // stage the next round (its buffer was last read before the previous
         // barrier) and fetch the one after
         if (round + 1 < nrounds) {
-            stage_round(buf ^ 1, beg + (round + 1) * TR);
+            stage_round(buf ^ 1);
             if (round + 2 < nrounds)
                 fetch_round(beg + (round + 2) * TR);
         }
@@ -665,15 +666,13 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
             sq[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsq, vo, so, 0));
         }
     };
-    // widened chunk to LDS (zeros for rows past the end); returns the values
-    auto stage_one = [&](float *lds, const uint4 &src, int c, bool ok, float (&v)[VEC]) {
+    // widened chunk to LDS (rows past the segment end were loaded as zeros);
+    // returns the values
+    auto stage_one = [&](float *lds, const uint4 &src, int c, float (&v)[VEC]) {
         if constexpr (VEC == 4)
             StF32::widen(src, v);
         else
             StBF16::widen(src, v);
-#pragma unroll
-        for (int x = 0; x < VEC; ++x)
-            v[x] = ok ? v[x] : 0.f;
         float *dst = lds + (c / CPR) * LDX + VEC * (c % CPR);
 #pragma unroll
         for (int x = 0; x < VEC; x += 4)
@@ -684,13 +683,12 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
     // products by shuffles: a row's chunks lie in one wave), stores the dO
     // row already divided by it, a_i = g_i / den_i, and keeps 1/den_i in LDS.
     static_assert(CPR <= 64 && 64 % CPR == 0, "a staged row lies in one wave");
-    auto stage_round = [&](int buf, int64_t r0) {
+    auto stage_round = [&](int buf) {
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
             const int c = tid + p * NT;
-            const bool ok = r0 + c / CPR < end;
             float qv[VEC];
-            stage_one(qs[buf], sq[p], c, ok, qv);
+            stage_one(qs[buf], sq[p], c, qv);
             const float *zc = &vl[VEC * (c % CPR)];
             float pz = 0.f;
 #pragma unroll
@@ -711,8 +709,7 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
             float *dst = xs[buf] + (c / CPR) * LDX + VEC * (c % CPR);
 #pragma unroll
             for (int x = 0; x < VEC; x += 4)
-                *reinterpret_cast<f4 *>(dst + x) =
-                    ok ? f4{gv[x], gv[x + 1], gv[x + 2], gv[x + 3]} * inv : f4{0.f, 0.f, 0.f, 0.f};
+                *reinterpret_cast<f4 *>(dst + x) = f4{gv[x], gv[x + 1], gv[x + 2], gv[x + 3]} * inv;
         }
     };
 
@@ -732,7 +729,7 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
             am[kb][r] = v[r];
     }
     __syncthreads();  // z in LDS before the first staging reads it
-    stage_round(0, beg);
+    stage_round(0);
     drain_loads();
     if (nrounds > 1)
         fetch_round(beg + TR);
@@ -781,7 +778,7 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
                 }
             }
             if (round + 1 < nrounds) {
-                stage_round(buf ^ 1, beg + (round + 1) * TR);
+                stage_round(buf ^ 1);
                 if (round + 2 < nrounds)
                     fetch_round(beg + (round + 2) * TR);
             }
@@ -837,7 +834,7 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (round + 1 < nrounds) {
-                stage_round(buf ^ 1, beg + (round + 1) * TR);
+                stage_round(buf ^ 1);
                 if (round + 2 < nrounds)
                     fetch_round(beg + (round + 2) * TR);
             }
