@@ -43,7 +43,9 @@
  *    synchronisation.
  *  - Results are deterministic: the same inputs give bit-identical outputs
  *    on every call (fixed-order reductions, no floating-point atomics).
- *  - The library keeps no mutable global state; concurrent calls on
+ *  - The library keeps no mutable global state apart from device facts it
+ *    caches on first use (the compute-unit count of each device and the
+ *    occupancy of a kernel, which size some launches); concurrent calls on
  *    different streams must use different workspaces.
  */
 #ifndef LA_H

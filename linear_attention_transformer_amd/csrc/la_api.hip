@@ -52,6 +52,50 @@ Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int causal)
     return p;
 }
 
+// Workgroups of `kern` (`threads` each) resident on the current device at
+// once: compute units x workgroups per unit.  Both factors are cached (the
+// compute-unit count per device, the occupancy per kernel); 0 if unknown.
+template <class K>
+int64_t resident_wgs(K kern, int threads)
+{
+    static int cus[64];
+    static int per_cu = -1;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 0;
+    if (cus[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cus[dev] = v;
+    }
+    if (per_cu < 0) {
+        int v = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kern, threads, 0) != hipSuccess)
+            return 0;
+        per_cu = v;
+    }
+    return (int64_t)per_cu * cus[dev];
+}
+
+// The plan re-segmented so that one pass of the kernel is a single batch of
+// resident workgroups (for a kernel whose workgroups hold one segment of one
+// head), never with more segments than the plan's (its workspace holds that
+// many records per head).
+Plan one_batch(const Plan &p, int64_t resident)
+{
+    Plan q = p;
+    const int64_t want = resident > 0 ? std::max<int64_t>(resident / std::max<int64_t>(p.BH, 1), 1)
+                                      : p.nseg;
+    if (want >= p.nseg)
+        return q;
+    const int64_t nchunks = std::max<int64_t>((p.N + kSegAlign - 1) / kSegAlign, 1);
+    const int64_t per = (nchunks + want - 1) / want;
+    q.seg_len = per * kSegAlign;
+    q.nseg = std::max<int64_t>((p.N + q.seg_len - 1) / q.seg_len, 1);
+    return q;
+}
+
 // workspace regions, in floats, each rounded up to 64 floats (256 bytes)
 struct Layout {
     int64_t part, tot, gpart, gtot, cbuf, total;
@@ -347,16 +391,23 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
                                                                 p.seg_len, (int)p.nseg);
             });
         } else {
-            // dQ and the segment's gradient record in one pass over Q and dO
+            // dQ and the segment's gradient record in one pass over Q and dO,
+            // its segments sized for one batch of resident workgroups
+            const Plan pq = one_batch(p, resident_wgs(nc::k_bwd_q_nc<ST, D>, 512));
             rc = traced(t, s, "bwd_q", [&] {
-                nc::k_bwd_q_nc<ST, D><<<g1, dim3(512), 0, s>>>(
-                    g, q, static_cast<T *>(dQ), gpart, fstate, p.N, p.seg_len, (int)p.nseg);
+                nc::k_bwd_q_nc<ST, D><<<dim3((unsigned)(pq.nseg * pq.BH)), dim3(512), 0, s>>>(
+                    g, q, static_cast<T *>(dQ), gpart, fstate, pq.N, pq.seg_len, (int)pq.nseg);
             });
+            if (rc != LA_OK)
+                return rc;
+            if ((rc = scan(gpart, ws + l.gtot, pq, 0, s, t)) != LA_OK)
+                return rc;
         }
         if (rc != LA_OK)
             return rc;
-        if ((rc = scan(gpart, ws + l.gtot, p, 0, s, t)) != LA_OK)
-            return rc;
+        if constexpr (std::is_same<ST, StBF16>::value)
+            if ((rc = scan(gpart, ws + l.gtot, p, 0, s, t)) != LA_OK)
+                return rc;
         return traced(t, s, "bwd_kv", [&] {
             if constexpr (std::is_same<ST, StBF16>::value)
                 bf::k_apply_bf<D, 2><<<dim3((unsigned)(2 * p.nseg * p.BH)),

@@ -106,7 +106,6 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
     uint16_t *__restrict__ Out2, float *__restrict__ den_out, float *__restrict__ cbuf,
     const float *__restrict__ rec, int64_t N, int64_t seg_len, int nseg)
 {
-    typedef nc::IO<StBF16> io;
     static_assert(D >= 32 && D <= 128, "32-column output blocks");
     static_assert(KIND >= 0 && KIND <= 2, "forward, dQ or dK | dV");
     constexpr int KS = D / 16;               // k-steps of 16

@@ -217,7 +217,6 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce_nc(
                                                 (short)0, (int)(rows * 8), 0x00020000);
     const int ox = (int)((h * D + m0 + VW * j) * sizeof(T));
     const int oy = (int)((h * D + n0 + VW * j) * sizeof(T));
-    const int64_t nsteps = (end - beg + 1) / 2;
 
     f16v acc[VW][VW];
 #pragma unroll
