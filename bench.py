@@ -10,7 +10,9 @@ non-causal, i.i.d. N(0,1)/sqrt(D) inputs (dO unscaled) drawn on the GPU
 from the shared seeded generator.
 
 Output: one JSON line on stdout.  `value` is tokens/s = B*N per step / step
-time over K timed steps bracketed by device synchronisation.  `roofline`
+time over K timed steps bracketed by device synchronisation, after W untimed
+warm-up steps (200 by default: the GPU reaches the clocks it holds under
+sustained load only after the first few tens of steps from idle).  `roofline`
 gives the dominant kernel's achieved rate from per-launch HIP events (a
 second timed pass in which the library records caller-owned events around
 every launch), against the MI355X fp32-MFMA or HBM peak.  `cpu_baseline`
@@ -240,8 +242,11 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    # the GPU raises its clocks over the first tens of steps after idle
+    # (measured: ~0.8 ms/step over the first 20 fp32 steps, ~0.50 ms/step
+    # from about step 60 on), so the untimed warm-up is long by default
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--dtype", choices=("fp32", "bf16"), default="fp32",
                     help="storage dtype of Q, K, V, O and gradients (arithmetic is fp32)")
     ap.add_argument("--causal", type=int, choices=(0, 1), default=0)
@@ -302,7 +307,6 @@ def main():
     mem = {"peak_allocated": torch.cuda.max_memory_allocated(dev),
            "io_tensors": 8 * q.numel() * q.element_size(),
            "workspace": ws.numel(), "saved_state": st.numel() * 4}
-    copy_gbs = copy_reference(dev)
 
     # timed region 1: the headline, nothing but the K steps
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -376,7 +380,7 @@ def main():
                     continue
                 tdt = torch.float32 if vdt == "fp32" else torch.bfloat16
                 vms = time_variant(la, make_inputs, dev, B, H, N, D, tdt, vc,
-                                   max(args.steps // 2, 5), 3)
+                                   max(args.steps // 2, 5), args.warmup)
                 vs = 4 if vdt == "fp32" else 2
                 fl = step_floor_us(B, H, N, D, vs, uses_bf16_mfma(vdt, D, vc))
                 variants["%s %s" % (vdt, "causal" if vc else "non-causal")] = {
@@ -384,6 +388,10 @@ def main():
                     "step_floor_us": round(fl, 1), "step_frac": round(fl / (vms * 1e3), 4)}
                 print("bench: variant %s %s: %.3f ms/step" % (vdt, "causal" if vc else
                       "non-causal", vms), file=sys.stderr, flush=True)
+
+    # the copy reference runs after every timed region: a burst of streaming
+    # traffic just before one would lower its clocks
+    copy_gbs = copy_reference(dev)
 
     cpu = None
     if not args.no_cpu_baseline:
