@@ -216,6 +216,16 @@ constexpr bool nc_path()
     return D >= 32 && D <= 128;
 }
 
+// fp32 storage at D = 256: the fast reduction (four 128 x 128 blocks per
+// segment) for both masks, the fast non-causal apply kernels (eight waves)
+// and a dQ pass without the dS role (the gradient record then comes from
+// the reduction)
+template <class ST, int D>
+constexpr bool wide_path()
+{
+    return std::is_same<ST, StF32>::value && D == 256;
+}
+
 template <class ST, int D>
 int state_of_kv(const void *K, const void *V, float *part, float *tot, const Plan &p,
                 hipStream_t s, Tracer *t)
@@ -224,17 +234,18 @@ int state_of_kv(const void *K, const void *V, float *part, float *tot, const Pla
     typedef typename ST::T T;
     int rc = LA_OK;
     bool done = false;
-    if constexpr (nc_path<D>()) {
+    if constexpr (nc_path<D>() || wide_path<ST, D>()) {
         rc = traced(t, s, "state_local", [&] {
             if constexpr (std::is_same<ST, StBF16>::value)
                 bf::k_reduce_bf<D, false><<<dim3((unsigned)(p.nseg * p.BH)), dim3(256), 0, s>>>(
                     static_cast<const T *>(K), static_cast<const T *>(V), nullptr, part, p.N,
                     p.seg_len, (int)p.nseg);
             else
-                nc::k_reduce_nc<ST, D, false><<<dim3((unsigned)(p.nseg * p.BH)),
-                                                dim3(nc::kReduceThreads), 0, s>>>(
-                    static_cast<const T *>(K), static_cast<const T *>(V), nullptr, part, p.N,
-                    p.seg_len, (int)p.nseg);
+                nc::k_reduce_nc<ST, D, false>
+                    <<<dim3((unsigned)(p.nseg * p.BH * nc::reduce_blocks<D>())),
+                       dim3(nc::kReduceThreads), 0, s>>>(
+                        static_cast<const T *>(K), static_cast<const T *>(V), nullptr, part, p.N,
+                        p.seg_len, (int)p.nseg);
         });
         done = true;
     }
@@ -297,6 +308,15 @@ int run_forward(const void *Q, const void *K, const void *V, void *O, float *den
                     static_cast<const T *>(V), static_cast<T *>(O), den_out, rec, p.N, p.seg_len,
                     (int)p.nseg);
         });
+    }
+    if constexpr (wide_path<ST, D>()) {
+        if (!p.causal)
+            return traced(t, s, "forward", [&] {
+                nc::k_apply_nc<ST, D, 0><<<dim3((unsigned)(p.nseg * p.BH)),
+                                           dim3(nc::apply_threads<D>()), 0, s>>>(
+                    static_cast<const T *>(Q), nullptr, static_cast<T *>(O), nullptr, den_out,
+                    rec, p.N, p.seg_len, (int)p.nseg);
+            });
     }
     const dim3 grid((unsigned)(p.nseg * p.BH * C::CS));
     return traced(t, s, "forward", [&] {
@@ -372,6 +392,33 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
                 cz::k_bwd_kv_causal<ST, D><<<dim3((unsigned)(2 * p.nseg * p.BH)), nt, 0, s>>>(
                     q, k, v, g, static_cast<T *>(dK), static_cast<T *>(dV), cbuf, gpart, p.N,
                     p.seg_len, (int)p.nseg);
+        });
+    }
+    if constexpr (!CAUSAL && wide_path<ST, D>()) {
+        // dQ and (c_i, 1/den_i); the gradient records by the fast reduction;
+        // dK | dV by the eight-wave apply kernel
+        const dim3 g1((unsigned)(p.nseg * p.BH));
+        rc = traced(t, s, "bwd_q", [&] {
+            nc::k_bwd_q_nc<ST, D, false><<<g1, dim3(512), 0, s>>>(
+                g, q, static_cast<T *>(dQ), cbuf, fstate, p.N, p.seg_len, (int)p.nseg);
+        });
+        if (rc != LA_OK)
+            return rc;
+        rc = traced(t, s, "grad_state_local", [&] {
+            nc::k_reduce_nc<ST, D, true>
+                <<<dim3((unsigned)(p.nseg * p.BH * nc::reduce_blocks<D>())),
+                   dim3(nc::kReduceThreads), 0, s>>>(q, g, cbuf, gpart, p.N, p.seg_len,
+                                                     (int)p.nseg);
+        });
+        if (rc != LA_OK)
+            return rc;
+        if ((rc = scan(gpart, ws + l.gtot, p, 0, s, t)) != LA_OK)
+            return rc;
+        return traced(t, s, "bwd_kv", [&] {
+            nc::k_apply_nc<ST, D, 2><<<dim3((unsigned)(2 * p.nseg * p.BH)),
+                                       dim3(nc::apply_threads<D>()), 0, s>>>(
+                v, k, static_cast<T *>(dK), static_cast<T *>(dV), nullptr, ws + l.gtot, p.N,
+                p.seg_len, (int)p.nseg);
         });
     }
     if constexpr (!CAUSAL && nc_path<D>()) {

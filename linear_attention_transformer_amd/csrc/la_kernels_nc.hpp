@@ -82,6 +82,12 @@ __device__ __forceinline__ float lg_sum(float v)
 
 constexpr int kReduceThreads = 256;
 constexpr int kApplyThreads = 256;
+// apply workgroups: four waves, or one wave per 32-column block when D > 128
+template <int D>
+constexpr int apply_threads()
+{
+    return D > 128 ? 64 * (D / 32) : kApplyThreads;
+}
 
 // v_mfma_f32_32x32x2_f32: lane l = 32*h + j supplies A[m=j][k=h] and
 // B[k=h][n=j] and holds accumulator element i at row 8*(i/4) + 4*h + i%4,
@@ -166,15 +172,23 @@ __device__ __forceinline__ void buf_load_vec(__amdgpu_buffer_rsrc_t rs, int vo, 
 // cy[D] = sum_t Y'[t] over the rows t of the segment, where
 //   forward  (GRAD = false): Y' = Y, w = 1          -> S, z, u
 //   backward (GRAD = true) : Y' = Y * inv_den_t, w = c_t  -> dS, r, t
-// with (c_t, inv_den_t) read from cbuf.  Waves own square output tiles
-// (TM x TM, TM = min(D, 64)); when there are fewer tiles than waves, the
-// waves of a tile split the token steps and add their partials in LDS.
+// with (c_t, inv_den_t) read from cbuf.  A workgroup forms one DB x DB block
+// of Mat (DB = min(D, 128); D = 256 takes 4 workgroups per segment, block
+// index fastest in blockIdx).  Waves own square output tiles (TM x TM,
+// TM = min(DB, 64)); when there are fewer tiles than waves, the waves of a
+// tile split the token steps and add their partials in LDS.
 //
 // One MFMA step covers two tokens (k = h).  Lane j loads VW = TM/32
 // consecutive columns of its token's row, so 32 lanes read 32*VW columns:
 // MFMA (ca, cb) pairs column m0 + VW*j + ca of X with column n0 + VW*j + cb
 // of Y, and accumulator (ca, cb) element i holds
 // Mat[m0 + VW*(8*(i/4) + 4*h + i%4) + ca][n0 + VW*j + cb].
+template <int D>
+constexpr int reduce_blocks()
+{
+    return D > 128 ? (D / 128) * (D / 128) : 1;
+}
+
 template <class ST, int D, bool GRAD>
 __global__ __launch_bounds__(kReduceThreads) void k_reduce_nc(
     const typename ST::T *__restrict__ X, const typename ST::T *__restrict__ Y,
@@ -183,8 +197,10 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce_nc(
 {
     typedef typename ST::T T;
     static_assert(D >= 32, "32x32 tiles");
-    constexpr int TM = D < 64 ? D : 64;
-    constexpr int NQ1 = D / TM;
+    constexpr int DB = D < 128 ? D : 128;  // this workgroup's block of Mat
+    constexpr int NB1 = D / DB;
+    constexpr int TM = DB < 64 ? DB : 64;
+    constexpr int NQ1 = DB / TM;
     constexpr int NQ = NQ1 * NQ1;
     constexpr int NWAVE = kReduceThreads / 64;
     static_assert(NQ <= NWAVE && NWAVE % NQ == 0, "tile split");
@@ -193,11 +209,13 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce_nc(
     constexpr int U = GRAD ? 16 : 24;  // prefetched steps (<= 48 loads in flight)
     __shared__ float red[(TS > 1) ? (TS - 1) * (TM * TM + 2 * TM) : 1];
 
-    const int64_t bh = blockIdx.x / nseg;
-    const int seg = (int)(blockIdx.x % nseg);
+    const int blk = (int)(blockIdx.x % (NB1 * NB1));
+    const int64_t bs = blockIdx.x / (NB1 * NB1);
+    const int64_t bh = bs / nseg;
+    const int seg = (int)(bs % nseg);
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, j = lane & 31, h = lane >> 5;
     const int quad = w % NQ, tsi = w / NQ;
-    const int m0 = (quad / NQ1) * TM, n0 = (quad % NQ1) * TM;
+    const int m0 = (blk / NB1) * DB + (quad / NQ1) * TM, n0 = (blk % NB1) * DB + (quad % NQ1) * TM;
     const int64_t beg = (int64_t)seg * seg_len;
     const int64_t end = (beg + seg_len < N) ? beg + seg_len : N;
     const T *xh = X + bh * N * D + m0 + VW * j;
@@ -399,7 +417,7 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce_nc(
 // forms q_j.z over its own 32 columns of the staged row only; the partials
 // meet in LDS at the round's barrier, after which the rows are normalised.
 template <class ST, int D, int KIND>
-__global__ __launch_bounds__(kApplyThreads) void k_apply_nc(
+__global__ __launch_bounds__(apply_threads<D>()) void k_apply_nc(
     const typename ST::T *__restrict__ X, const typename ST::T *__restrict__ X2,
     typename ST::T *__restrict__ Out, typename ST::T *__restrict__ Out2,
     float *__restrict__ den_out, const float *__restrict__ rec, int64_t N, int64_t seg_len,
@@ -409,8 +427,9 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_nc(
     typedef IO<ST> io;
     static_assert(D >= 32, "32-column output blocks");
     static_assert(KIND == 0 || KIND == 2, "forward or dK | dV");
+    constexpr int NT = apply_threads<D>();
     constexpr int KB = D / 8;                // k-blocks of 8
-    constexpr int NWAVE = kApplyThreads / 64;
+    constexpr int NWAVE = NT / 64;
     constexpr int NCB = D / 32;              // column blocks
     static_assert(NCB <= NWAVE && NWAVE % NCB == 0, "column split");
     constexpr int NRG = NWAVE / NCB;         // row groups
@@ -418,8 +437,8 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_nc(
     constexpr int LDX = D + 4;               // LDS row pitch (floats)
     constexpr int VEC = 16 / sizeof(T);      // elements per 16-byte load
     constexpr int CPR = D / VEC;             // 16-byte chunks per row
-    constexpr int PER = TR * CPR / kApplyThreads;  // chunks per thread per round
-    static_assert(TR * CPR % kApplyThreads == 0, "staging split");
+    constexpr int PER = TR * CPR / NT;  // chunks per thread per round
+    static_assert(TR * CPR % NT == 0, "staging split");
     __shared__ __attribute__((aligned(16))) float xs[2][TR * LDX];
     __shared__ __attribute__((aligned(16))) float vz[KIND == 0 ? D : 4];  // z
     // forward: q.z of each row over each wave's 32 columns (added up after
@@ -452,7 +471,7 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_nc(
         const int so = __builtin_amdgcn_readfirstlane((int)((r0 - beg) * D * sizeof(T)));
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
-            const int c = tid + p * kApplyThreads;
+            const int c = tid + p * NT;
             stg[p] = __builtin_bit_cast(
                 uint4, __builtin_amdgcn_raw_buffer_load_b128(
                            rsx, (int)(((c / CPR) * D + VEC * (c % CPR)) * sizeof(T)), so, 0));
@@ -462,7 +481,7 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_nc(
     auto stage_round = [&](int buf) {
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
-            const int c = tid + p * kApplyThreads;
+            const int c = tid + p * NT;
             float v[VEC];
             if constexpr (VEC == 4)
                 StF32::widen(stg[p], v);
@@ -506,7 +525,7 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_nc(
             ev[q] = sgn * *reinterpret_cast<const f4 *>(vec + 32 * cb + 8 * q + 4 * h);
     }
     if constexpr (KIND == 0)
-        for (int e = tid; e < D; e += kApplyThreads)
+        for (int e = tid; e < D; e += NT)
             vz[e] = st[D * D + e];
     stage_round(0);
     drain_loads();
@@ -609,8 +628,10 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_nc(
 //                       over through LDS one round later.
 // Both roles stage the rows (Q and dO, fp32, double-buffered) together,
 // forming 1/den_i of each staged row on the way, and meet at one barrier per
-// round.
-template <class ST, int D>
+// round.  With DS = false (D = 256, where a wave of either role needs 128
+// registers of state) the workgroup is eight dQ waves only, and it writes
+// (c_i, 1/den_i) to part_out (as cbuf) for k_reduce_nc<GRAD = true>.
+template <class ST, int D, bool DS = true>
 __global__ __launch_bounds__(512) void k_bwd_q_nc(
     const typename ST::T *__restrict__ G, const typename ST::T *__restrict__ Q,
     typename ST::T *__restrict__ dQ, float *__restrict__ part_out,
@@ -619,10 +640,14 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
     typedef typename ST::T T;
     typedef IO<ST> io;
     static_assert(D >= 32, "32-column output blocks");
-    constexpr int NT = 512;
     constexpr int KB = D / 8;
     constexpr int NCB = D / 32;
-    constexpr int NRG = 4 / NCB;
+    // waves of the dQ role: four next to four of the dS role, or (without
+    // the dS role, D = 256) one per column block
+    constexpr int NW0 = DS ? 4 : (NCB > 4 ? NCB : 4);
+    constexpr int NT = DS ? 512 : 64 * NW0;
+    static_assert(NT == 512 && NW0 % NCB == 0 && (!DS || NCB <= 4), "role layout");
+    constexpr int NRG = NW0 / NCB;
     constexpr int TR = 32 * NRG;
     constexpr int LDX = D + 4;
     constexpr int VEC = 16 / sizeof(T);
@@ -639,7 +664,8 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
     const int64_t bh = blockIdx.x / nseg;
     const int seg = (int)(blockIdx.x % nseg);
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, j = lane & 31, h = lane >> 5;
-    const int role = w >> 2, cb = (w & 3) % NCB, rg = (w & 3) / NCB;
+    const int role = DS ? (w >> 2) : 0, w0 = DS ? (w & 3) : w;
+    const int cb = w0 % NCB, rg = w0 / NCB;
     const int64_t beg = (int64_t)seg * seg_len;
     const int64_t end = (beg + seg_len < N) ? beg + seg_len : N;
     const int64_t hoff = bh * N * D;
@@ -797,10 +823,16 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
                 if (row < end)
                     io::store4(oh + row * D + 32 * cb + 8 * q + 4 * h, o);
             }
-            if (cb == 0 && h == 0)
-                cx[buf][rg][j] = c;
+            if constexpr (DS) {
+                if (cb == 0 && h == 0)
+                    cx[buf][rg][j] = c;
+            } else {
+                // (c_i, 1/den_i) for the separate gradient reduction
+                if (cb == 0 && h == 0 && row < end)
+                    reinterpret_cast<float2 *>(part_out)[bh * N + row] = float2{c, inv};
+            }
         }
-    } else {
+    } else if constexpr (DS) {
 #pragma unroll
         for (int t = 0; t < NCB; ++t)
             gacc[t] = zero16();
@@ -850,6 +882,8 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
                 qprev[kk] = qcur[kk];
         }
     }
+    if constexpr (!DS)
+        return;
     __syncthreads();  // the last round's c_i is in LDS; staging buffers are free
 
     constexpr int PW = NCB * 16 * 64 + 64;  // floats per handing wave
