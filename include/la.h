@@ -120,6 +120,97 @@ int la_backward(const void *Q, const void *K, const void *V, const void *dO,
                 void *stream);
 
 /*
+ * Sequences in pieces: carried state
+ * ----------------------------------
+ * The method keeps one running state (S, z, u) and a token count, grown
+ * token by token in the state-update pseudocode of section 2 of the
+ * cloud.baidu.com article, so a long sequence can be processed piece by
+ * piece (streaming prefill, sequence sharding across devices), each piece
+ * starting from the state its neighbours leave.  The calls below are
+ * la_forward / la_backward over one piece, with that state passed in and out
+ * as a RECORD:
+ *
+ *   record = [ M (D x D, row-major: M[a*D + b]) | x (D) | y (D) ],
+ *            fp32, one per head, layout [B, H, D*D + 2*D]
+ *            (la_record_size() bytes), device memory.
+ *
+ * Forward record (carry):      M = S = sum_j k_j v_j^T,  x = z = sum_j k_j,
+ *                              y = u = sum_j v_j
+ * Gradient record (gcarry):    M = sum_i q_i a_i^T,  x = sum_i c_i q_i,
+ *                              y = sum_i a_i,
+ *                              with a_i = dO_i / den_i, c_i = a_i . o_i of
+ *                              each row i, den_i and o_i of the whole sequence.
+ *
+ * carry_in stands for n_carry tokens outside the piece whose keys every row
+ * of the piece attends to: in the causal case the tokens before the piece,
+ * in the non-causal case all other tokens of the sequence.  gcarry_in stands
+ * for the rows outside the piece that attend to the piece's keys: causal,
+ * the rows after the piece; non-causal, all other rows.  The outputs are
+ * then exactly the piece's rows of the whole sequence's outputs.
+ *
+ * The records that come out are the ones that go in plus the piece's own:
+ * carry_out = carry_in + record of the piece's tokens, gcarry_out =
+ * gcarry_in + record of the piece's rows.  gcarry_out is also the gradient
+ * of L = sum dO . O (over the piece and the rows behind gcarry_in) with
+ * respect to the carried state: dL/dS = M, dL/dz = -x, dL/du = y.
+ *
+ * Use:
+ *   causal, streaming: forward the pieces in order, each taking the previous
+ *   carry_out (n_carry = tokens so far); backward in reverse order, each
+ *   taking the next piece's gcarry_out, with the same carry_in as its
+ *   forward (or the state_out its forward saved).
+ *   sharded (one piece per device): forward with O == NULL gives each
+ *   piece's own record; an exclusive scan (causal) or the sum over the other
+ *   pieces (non-causal) of those records is the carry_in of the real call.
+ *   The backward likewise: with dK == dV == NULL it gives dQ and the piece's
+ *   gcarry_out (with gcarry_in NULL: its own rows' record), whose reverse
+ *   exclusive scan or sum over the others is the gcarry_in of the full call.
+ */
+
+/* Bytes of one record per head for B x H heads of size D (0 if invalid). */
+size_t la_record_size(int64_t B, int64_t H, int64_t D);
+
+/*
+ * Forward pass over one piece of a longer sequence.  Arguments as for
+ * la_forward, plus:
+ *   carry_in  : record of the n_carry tokens outside the piece (see above),
+ *               or NULL (a zero record).
+ *   n_carry   : count of those tokens, 0 <= n_carry <= 2^40 (LA_ERR_SHAPE
+ *               otherwise); it enters every denominator.
+ *   carry_out : NULL, or receives carry_in + the piece's record.
+ *   O         : may be NULL when carry_out or state_out is given and
+ *               den_out is NULL: then only the records are computed.
+ *   state_out : as for la_forward; it then includes the carried state, and
+ *               la_backward_segment can take it as state_in.
+ * N == 0 copies carry_in (or zero) to carry_out.  carry_out must not
+ * overlap carry_in or any other argument (LA_ERR_ALIAS).
+ */
+int la_forward_segment(const void *Q, const void *K, const void *V, void *O,
+                       int64_t B, int64_t H, int64_t N, int64_t D, int causal,
+                       int dtype, const float *carry_in, int64_t n_carry,
+                       float *carry_out, float *den_out, void *state_out,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Backward pass over one piece.  Arguments as for la_backward, plus:
+ *   carry_in, n_carry : as given to la_forward_segment; carry_in is read only
+ *               when state_in is NULL (the state is then recomputed).
+ *   gcarry_in : gradient record of the rows outside the piece that attend to
+ *               its keys (see above), or NULL (a zero record).
+ *   gcarry_out: NULL, or receives gcarry_in + the piece's rows' record.
+ *   dK, dV    : both given, or both NULL: then only dQ and gcarry_out are
+ *               computed (dQ does not depend on gcarry_in).
+ * N == 0 copies gcarry_in (or zero) to gcarry_out.
+ */
+int la_backward_segment(const void *Q, const void *K, const void *V,
+                        const void *dO, void *dQ, void *dK, void *dV,
+                        int64_t B, int64_t H, int64_t N, int64_t D, int causal,
+                        int dtype, const float *carry_in, int64_t n_carry,
+                        const float *gcarry_in, float *gcarry_out,
+                        const void *state_in, void *ws, size_t ws_bytes,
+                        void *stream);
+
+/*
  * Kernel-level timing (benchmarks, profilers).  Same arguments and behaviour
  * as la_forward / la_backward, plus:
  *   events     : NULL, or n_events hipEvent_t handles created by the caller

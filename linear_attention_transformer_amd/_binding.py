@@ -55,6 +55,14 @@ def load_library():
     lib.la_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ci,
                                 ci, vp, vp, sz, vp]
     lib.la_backward.restype = ci
+    lib.la_record_size.argtypes = [i64, i64, i64]
+    lib.la_record_size.restype = sz
+    lib.la_forward_segment.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ci, ci, vp, i64,
+                                       vp, vp, vp, vp, sz, vp]
+    lib.la_forward_segment.restype = ci
+    lib.la_backward_segment.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ci,
+                                        ci, vp, i64, vp, vp, vp, vp, sz, vp]
+    lib.la_backward_segment.restype = ci
     ev, ip, cpp = ctypes.c_void_p, ctypes.POINTER(ci), ctypes.POINTER(ctypes.c_char_p)
     lib.la_forward_traced.argtypes = lib.la_forward.argtypes + [ev, ci, ip, cpp]
     lib.la_forward_traced.restype = ci
@@ -78,6 +86,10 @@ def state_size(B, H, N, D, causal=False) -> int:
 
 def num_segments(B, H, N, D, causal=False) -> int:
     return int(load_library().la_num_segments(B, H, N, D, int(bool(causal))))
+
+
+def record_size(B, H, D) -> int:
+    return int(load_library().la_record_size(B, H, D))
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -193,6 +205,90 @@ def backward(q, k, v, do, causal: bool = False, *, state=None, outs=None,
     if rc != 0:
         raise LAError(rc, "la_backward")
     return dq, dk, dv
+
+
+def _check_record(r, B, H, D, dev, what):
+    if r is None:
+        return
+    if (r.dtype != torch.float32 or not r.is_cuda or r.device != dev
+            or not r.is_contiguous() or r.shape != (B, H, D * D + 2 * D)):
+        raise ValueError("%s must be a contiguous float32 [B, H, D*D+2*D] tensor on %s"
+                         % (what, dev))
+
+
+def new_record(B, H, D, device) -> torch.Tensor:
+    """An uninitialised record tensor [B, H, D*D + 2*D] (float32)."""
+    return torch.empty((B, H, D * D + 2 * D), dtype=torch.float32, device=device)
+
+
+def forward_segment(q, k, v, causal: bool = False, *, carry_in=None, n_carry: int = 0,
+                    carry_out=True, compute_out: bool = True, return_den: bool = False,
+                    save_state: bool = False, out=None, state_out=None, workspace=None):
+    """Forward pass over one piece of a longer sequence (la_forward_segment).
+
+    carry_in: record [B, H, D*D+2D] of the n_carry tokens outside the piece
+    that its rows attend to (None = zero).  carry_out: True allocates the
+    outgoing record, a tensor receives it, None/False skips it.
+    compute_out=False computes only the records.
+    Returns (O or None, den or None, carry_out or None, state or None)."""
+    (B, H, N, D), dt = _check(q, k, v)
+    lib = load_library()
+    dev = q.device
+    _check_record(carry_in, B, H, D, dev, "carry_in")
+    if carry_out is True:
+        carry_out = new_record(B, H, D, dev)
+    elif carry_out is False:
+        carry_out = None
+    _check_record(carry_out, B, H, D, dev, "carry_out")
+    o = (torch.empty_like(q) if out is None else out) if compute_out else None
+    den = torch.empty((B, H, N), dtype=torch.float32, device=dev) if return_den else None
+    state = state_out
+    if state is None and save_state:
+        state = torch.empty(max(state_size(B, H, N, D, causal) // 4, 4),
+                            dtype=torch.float32, device=dev)
+    ws = alloc_workspace(B, H, N, D, causal, dev) if workspace is None else workspace
+    rc = lib.la_forward_segment(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, D,
+                                int(bool(causal)), dt, _ptr(carry_in), int(n_carry),
+                                _ptr(carry_out), _ptr(den), _ptr(state), _ptr(ws), ws.numel(),
+                                _stream(dev))
+    if rc != 0:
+        raise LAError(rc, "la_forward_segment")
+    return o, den, carry_out, state
+
+
+def backward_segment(q, k, v, do, causal: bool = False, *, carry_in=None, n_carry: int = 0,
+                     gcarry_in=None, gcarry_out=True, compute_kv: bool = True, state=None,
+                     outs=None, workspace=None):
+    """Backward pass over one piece (la_backward_segment).
+
+    carry_in / n_carry as given to forward_segment (carry_in is read only when
+    state is None); gcarry_in: gradient record of the rows outside the piece
+    that attend to its keys (None = zero); gcarry_out as carry_out of
+    forward_segment.  compute_kv=False computes only dQ and gcarry_out.
+    Returns (dQ, dK or None, dV or None, gcarry_out or None)."""
+    (B, H, N, D), dt = _check(q, k, v, do)
+    lib = load_library()
+    dev = q.device
+    _check_record(carry_in, B, H, D, dev, "carry_in")
+    _check_record(gcarry_in, B, H, D, dev, "gcarry_in")
+    if gcarry_out is True:
+        gcarry_out = new_record(B, H, D, dev)
+    elif gcarry_out is False:
+        gcarry_out = None
+    _check_record(gcarry_out, B, H, D, dev, "gcarry_out")
+    if outs is None:
+        dq = torch.empty_like(q)
+        dk, dv = (torch.empty_like(q), torch.empty_like(q)) if compute_kv else (None, None)
+    else:
+        dq, dk, dv = outs
+    ws = alloc_workspace(B, H, N, D, causal, dev) if workspace is None else workspace
+    rc = lib.la_backward_segment(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(dk),
+                                 _ptr(dv), B, H, N, D, int(bool(causal)), dt, _ptr(carry_in),
+                                 int(n_carry), _ptr(gcarry_in), _ptr(gcarry_out), _ptr(state),
+                                 _ptr(ws), ws.numel(), _stream(dev))
+    if rc != 0:
+        raise LAError(rc, "la_backward_segment")
+    return dq, dk, dv, gcarry_out
 
 
 class LinearAttention(torch.autograd.Function):

@@ -27,6 +27,7 @@ constexpr int64_t kTargetWorkgroups = 512;
 struct Plan {
     int64_t BH, N, D, PS, nseg, seg_len;
     int causal;
+    float n0;  // tokens carried in from outside the call, added to every row's count
 };
 
 bool supported_d(int64_t D)
@@ -42,6 +43,7 @@ Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int causal)
     p.D = D;
     p.PS = D * D + 2 * D;
     p.causal = causal;
+    p.n0 = 0.f;
     const int64_t nchunks = std::max<int64_t>((N + kSegAlign - 1) / kSegAlign, 1);
     const int64_t want =
         p.BH >= kTargetWorkgroups ? 1 : (kTargetWorkgroups + p.BH - 1) / std::max<int64_t>(p.BH, 1);
@@ -200,12 +202,16 @@ int traced(Tracer *t, hipStream_t s, const char *name, F &&launch)
     return rc;
 }
 
-int scan(float *part, float *out, const Plan &p, int mode, hipStream_t s, Tracer *t)
+// segment records -> head total (mode 0), exclusive prefixes (1) or
+// exclusive suffixes (2), starting from `init` and writing the inclusive
+// total to `total` when given
+int scan(float *part, float *out, const Plan &p, int mode, hipStream_t s, Tracer *t,
+         const float *init = nullptr, float *total = nullptr)
 {
     const int64_t bph = (p.PS / 4 + 255) / 256;  // 4 floats per thread
     return traced(t, s, "state_scan", [&] {
         k_state_scan<<<dim3((unsigned)(p.BH * bph)), dim3(256), 0, s>>>(
-            part, out, (int)p.nseg, p.PS, bph, mode);
+            part, out, (int)p.nseg, p.PS, bph, mode, init, total);
     });
 }
 
@@ -228,7 +234,7 @@ constexpr bool wide_path()
 
 template <class ST, int D>
 int state_of_kv(const void *K, const void *V, float *part, float *tot, const Plan &p,
-                hipStream_t s, Tracer *t)
+                hipStream_t s, Tracer *t, const float *init = nullptr, float *total = nullptr)
 {
     typedef Cfg<D, DefCS<D>::value> C;
     typedef typename ST::T T;
@@ -259,12 +265,17 @@ int state_of_kv(const void *K, const void *V, float *part, float *tot, const Pla
     }
     if (rc != LA_OK)
         return rc;
-    return p.causal ? scan(part, nullptr, p, 1, s, t) : scan(part, tot, p, 0, s, t);
+    return p.causal ? scan(part, nullptr, p, 1, s, t, init, total)
+                    : scan(part, tot, p, 0, s, t, init, total);
 }
 
+// Carry: `cin` (or null) is the record [S | z | u] of p.n0 tokens outside
+// the call that every row attends to; `cout` (or null) receives cin plus the
+// call's own record.  O == null computes the state only.
 template <class ST, int D>
 int run_forward(const void *Q, const void *K, const void *V, void *O, float *den_out,
-                void *state_out, float *ws, const Plan &p, hipStream_t s, Tracer *t)
+                void *state_out, float *ws, const Plan &p, hipStream_t s, Tracer *t,
+                const float *cin, float *cout)
 {
     typedef Cfg<D, DefCS<D>::value> C;
     typedef typename ST::T T;
@@ -273,12 +284,12 @@ int run_forward(const void *Q, const void *K, const void *V, void *O, float *den
     int rc;
     if (p.causal) {
         rec = state_out ? static_cast<float *>(state_out) : ws + l.part;
-        rc = state_of_kv<ST, D>(K, V, rec, nullptr, p, s, t);
+        rc = state_of_kv<ST, D>(K, V, rec, nullptr, p, s, t, cin, cout);
     } else {
         rec = state_out ? static_cast<float *>(state_out) : ws + l.tot;
-        rc = state_of_kv<ST, D>(K, V, ws + l.part, rec, p, s, t);
+        rc = state_of_kv<ST, D>(K, V, ws + l.part, rec, p, s, t, cin, cout);
     }
-    if (rc != LA_OK)
+    if (rc != LA_OK || O == nullptr)
         return rc;
     if constexpr (nc_path<D>()) {
         if (!p.causal)
@@ -287,12 +298,12 @@ int run_forward(const void *Q, const void *K, const void *V, void *O, float *den
                     bf::k_apply_bf<D, 0><<<dim3((unsigned)(p.nseg * p.BH)),
                                            dim3(bf::kApplyThreads), 0, s>>>(
                         static_cast<const T *>(Q), nullptr, static_cast<T *>(O), nullptr,
-                        den_out, nullptr, rec, p.N, p.seg_len, (int)p.nseg);
+                        den_out, nullptr, rec, p.N, p.seg_len, (int)p.nseg, p.n0);
                 else
                     nc::k_apply_nc<ST, D, 0><<<dim3((unsigned)(p.nseg * p.BH)),
                                                dim3(nc::kApplyThreads), 0, s>>>(
                         static_cast<const T *>(Q), nullptr, static_cast<T *>(O), nullptr,
-                        den_out, rec, p.N, p.seg_len, (int)p.nseg);
+                        den_out, rec, p.N, p.seg_len, (int)p.nseg, p.n0);
             });
         return traced(t, s, "forward", [&] {
             if constexpr (std::is_same<ST, StBF16>::value)
@@ -300,13 +311,13 @@ int run_forward(const void *Q, const void *K, const void *V, void *O, float *den
                                          dim3(cz::threads<D>()), 0, s>>>(
                     static_cast<const T *>(Q), static_cast<const T *>(K),
                     static_cast<const T *>(V), static_cast<T *>(O), den_out, rec, p.N, p.seg_len,
-                    (int)p.nseg);
+                    (int)p.nseg, p.n0);
             else
                 cz::k_fwd_causal<ST, D><<<dim3((unsigned)(p.nseg * p.BH)),
                                           dim3(cz::threads<D>()), 0, s>>>(
                     static_cast<const T *>(Q), static_cast<const T *>(K),
                     static_cast<const T *>(V), static_cast<T *>(O), den_out, rec, p.N, p.seg_len,
-                    (int)p.nseg);
+                    (int)p.nseg, p.n0);
         });
     }
     if constexpr (wide_path<ST, D>()) {
@@ -315,7 +326,7 @@ int run_forward(const void *Q, const void *K, const void *V, void *O, float *den
                 nc::k_apply_nc<ST, D, 0><<<dim3((unsigned)(p.nseg * p.BH)),
                                            dim3(nc::apply_threads<D>()), 0, s>>>(
                     static_cast<const T *>(Q), nullptr, static_cast<T *>(O), nullptr, den_out,
-                    rec, p.N, p.seg_len, (int)p.nseg);
+                    rec, p.N, p.seg_len, (int)p.nseg, p.n0);
             });
     }
     const dim3 grid((unsigned)(p.nseg * p.BH * C::CS));
@@ -324,19 +335,24 @@ int run_forward(const void *Q, const void *K, const void *V, void *O, float *den
             k_forward<ST, D, true><<<grid, dim3(C::NT), 0, s>>>(
                 static_cast<const T *>(Q), static_cast<const T *>(K),
                 static_cast<const T *>(V), static_cast<T *>(O), den_out, rec, p.N,
-                p.seg_len, (int)p.nseg);
+                p.seg_len, (int)p.nseg, p.n0);
         else
             k_forward<ST, D, false><<<grid, dim3(C::NT), 0, s>>>(
                 static_cast<const T *>(Q), static_cast<const T *>(K),
                 static_cast<const T *>(V), static_cast<T *>(O), den_out, rec, p.N,
-                p.seg_len, (int)p.nseg);
+                p.seg_len, (int)p.nseg, p.n0);
     });
 }
 
+// Carry: `cin` is the forward's carried-in record (read only when state_in
+// is null, to recompute the state); `gin` (or null) is the gradient record
+// [dS | r | t] of the rows outside the call that attend to its keys, and
+// `gout` (or null) receives gin plus the call's own gradient record.
+// dK == null skips the dK | dV pass.
 template <class ST, int D, bool CAUSAL>
 int run_backward_t(const void *Q, const void *K, const void *V, const void *G, void *dQ,
                    void *dK, void *dV, const void *state_in, float *ws, const Plan &p,
-                   hipStream_t s, Tracer *t)
+                   hipStream_t s, Tracer *t, const float *cin, const float *gin, float *gout)
 {
     typedef Cfg<D, DefCS<D>::value> C;
     typedef Cfg<D, 1> CQ;
@@ -348,7 +364,7 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
     if (state_in) {
         fstate = static_cast<const float *>(state_in);
     } else {
-        rc = state_of_kv<ST, D>(K, V, ws + l.part, ws + l.tot, p, s, t);
+        rc = state_of_kv<ST, D>(K, V, ws + l.part, ws + l.tot, p, s, t, cin);
         if (rc != LA_OK)
             return rc;
         fstate = CAUSAL ? ws + l.part : ws + l.tot;
@@ -363,11 +379,11 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
             if constexpr (std::is_same<ST, StBF16>::value)
                 bf::k_bwd_q_causal_bf<D><<<g1, nt, 0, s>>>(q, k, v, g, static_cast<T *>(dQ),
                                                            cbuf, fstate, p.N, p.seg_len,
-                                                           (int)p.nseg);
+                                                           (int)p.nseg, p.n0);
             else
                 cz::k_bwd_q_causal<ST, D><<<g1, nt, 0, s>>>(q, k, v, g, static_cast<T *>(dQ),
                                                             cbuf, fstate, p.N, p.seg_len,
-                                                            (int)p.nseg);
+                                                            (int)p.nseg, p.n0);
         });
         if (rc != LA_OK)
             return rc;
@@ -381,8 +397,10 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
         });
         if (rc != LA_OK)
             return rc;
-        if ((rc = scan(gpart, nullptr, p, 2, s, t)) != LA_OK)  // exclusive suffix
+        if ((rc = scan(gpart, nullptr, p, 2, s, t, gin, gout)) != LA_OK)  // exclusive suffix
             return rc;
+        if (dK == nullptr)
+            return LA_OK;
         return traced(t, s, "bwd_kv", [&] {
             if constexpr (std::is_same<ST, StBF16>::value)
                 bf::k_bwd_kv_causal_bf<D><<<dim3((unsigned)(2 * p.nseg * p.BH)), nt, 0, s>>>(
@@ -400,7 +418,7 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
         const dim3 g1((unsigned)(p.nseg * p.BH));
         rc = traced(t, s, "bwd_q", [&] {
             nc::k_bwd_q_nc<ST, D, false><<<g1, dim3(512), 0, s>>>(
-                g, q, static_cast<T *>(dQ), cbuf, fstate, p.N, p.seg_len, (int)p.nseg);
+                g, q, static_cast<T *>(dQ), cbuf, fstate, p.N, p.seg_len, (int)p.nseg, p.n0);
         });
         if (rc != LA_OK)
             return rc;
@@ -412,13 +430,15 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
         });
         if (rc != LA_OK)
             return rc;
-        if ((rc = scan(gpart, ws + l.gtot, p, 0, s, t)) != LA_OK)
+        if ((rc = scan(gpart, ws + l.gtot, p, 0, s, t, gin, gout)) != LA_OK)
             return rc;
+        if (dK == nullptr)
+            return LA_OK;
         return traced(t, s, "bwd_kv", [&] {
             nc::k_apply_nc<ST, D, 2><<<dim3((unsigned)(2 * p.nseg * p.BH)),
                                        dim3(nc::apply_threads<D>()), 0, s>>>(
                 v, k, static_cast<T *>(dK), static_cast<T *>(dV), nullptr, ws + l.gtot, p.N,
-                p.seg_len, (int)p.nseg);
+                p.seg_len, (int)p.nseg, p.n0);
         });
     }
     if constexpr (!CAUSAL && nc_path<D>()) {
@@ -429,7 +449,7 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
             rc = traced(t, s, "bwd_q", [&] {
                 bf::k_apply_bf<D, 1><<<g1, dim3(bf::kApplyThreads), 0, s>>>(
                     g, q, static_cast<T *>(dQ), nullptr, nullptr, cbuf, fstate, p.N, p.seg_len,
-                    (int)p.nseg);
+                    (int)p.nseg, p.n0);
             });
             if (rc != LA_OK)
                 return rc;
@@ -443,35 +463,38 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
             const Plan pq = one_batch(p, resident_wgs(nc::k_bwd_q_nc<ST, D>, 512));
             rc = traced(t, s, "bwd_q", [&] {
                 nc::k_bwd_q_nc<ST, D><<<dim3((unsigned)(pq.nseg * pq.BH)), dim3(512), 0, s>>>(
-                    g, q, static_cast<T *>(dQ), gpart, fstate, pq.N, pq.seg_len, (int)pq.nseg);
+                    g, q, static_cast<T *>(dQ), gpart, fstate, pq.N, pq.seg_len, (int)pq.nseg,
+                    pq.n0);
             });
             if (rc != LA_OK)
                 return rc;
-            if ((rc = scan(gpart, ws + l.gtot, pq, 0, s, t)) != LA_OK)
+            if ((rc = scan(gpart, ws + l.gtot, pq, 0, s, t, gin, gout)) != LA_OK)
                 return rc;
         }
         if (rc != LA_OK)
             return rc;
         if constexpr (std::is_same<ST, StBF16>::value)
-            if ((rc = scan(gpart, ws + l.gtot, p, 0, s, t)) != LA_OK)
+            if ((rc = scan(gpart, ws + l.gtot, p, 0, s, t, gin, gout)) != LA_OK)
                 return rc;
+        if (dK == nullptr)
+            return LA_OK;
         return traced(t, s, "bwd_kv", [&] {
             if constexpr (std::is_same<ST, StBF16>::value)
                 bf::k_apply_bf<D, 2><<<dim3((unsigned)(2 * p.nseg * p.BH)),
                                        dim3(bf::kApplyThreads), 0, s>>>(
                     v, k, static_cast<T *>(dK), static_cast<T *>(dV), nullptr, nullptr,
-                    ws + l.gtot, p.N, p.seg_len, (int)p.nseg);
+                    ws + l.gtot, p.N, p.seg_len, (int)p.nseg, p.n0);
             else
                 nc::k_apply_nc<ST, D, 2><<<dim3((unsigned)(2 * p.nseg * p.BH)),
                                            dim3(nc::kApplyThreads), 0, s>>>(
                     v, k, static_cast<T *>(dK), static_cast<T *>(dV), nullptr, ws + l.gtot, p.N,
-                    p.seg_len, (int)p.nseg);
+                    p.seg_len, (int)p.nseg, p.n0);
         });
     }
     rc = traced(t, s, "bwd_q", [&] {
         k_bwd_q<ST, D, CAUSAL, FUSE><<<dim3((unsigned)(p.nseg * p.BH)), dim3(CQ::NT), 0, s>>>(
             q, k, v, g, static_cast<T *>(dQ), fstate, gpart, cbuf, p.N, p.seg_len,
-            (int)p.nseg);
+            (int)p.nseg, p.n0);
     });
     if (rc != LA_OK)
         return rc;
@@ -486,14 +509,16 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
     }
     const float *gstate;
     if (CAUSAL) {
-        rc = scan(gpart, nullptr, p, 2, s, t);
+        rc = scan(gpart, nullptr, p, 2, s, t, gin, gout);
         gstate = gpart;
     } else {
-        rc = scan(gpart, ws + l.gtot, p, 0, s, t);
+        rc = scan(gpart, ws + l.gtot, p, 0, s, t, gin, gout);
         gstate = ws + l.gtot;
     }
     if (rc != LA_OK)
         return rc;
+    if (dK == nullptr)
+        return LA_OK;
     return traced(t, s, "bwd_kv", [&] {
         k_bwd_kv<ST, D, CAUSAL><<<grid, dim3(C::NT), 0, s>>>(
             q, k, v, g, static_cast<T *>(dK), static_cast<T *>(dV), gstate, cbuf, p.N,
@@ -504,23 +529,26 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
 template <class ST, int D>
 int run_backward(const void *Q, const void *K, const void *V, const void *G, void *dQ,
                  void *dK, void *dV, const void *state_in, float *ws, const Plan &p,
-                 hipStream_t s, Tracer *t)
+                 hipStream_t s, Tracer *t, const float *cin, const float *gin, float *gout)
 {
     if (p.causal)
-        return run_backward_t<ST, D, true>(Q, K, V, G, dQ, dK, dV, state_in, ws, p, s, t);
-    return run_backward_t<ST, D, false>(Q, K, V, G, dQ, dK, dV, state_in, ws, p, s, t);
+        return run_backward_t<ST, D, true>(Q, K, V, G, dQ, dK, dV, state_in, ws, p, s, t, cin,
+                                           gin, gout);
+    return run_backward_t<ST, D, false>(Q, K, V, G, dQ, dK, dV, state_in, ws, p, s, t, cin,
+                                        gin, gout);
 }
 
 template <class ST>
 int dispatch_forward(const void *Q, const void *K, const void *V, void *O, float *den,
-                     void *st, float *ws, const Plan &p, hipStream_t s, Tracer *t)
+                     void *st, float *ws, const Plan &p, hipStream_t s, Tracer *t,
+                     const float *cin, float *cout)
 {
     switch (p.D) {
-    case 16: return run_forward<ST, 16>(Q, K, V, O, den, st, ws, p, s, t);
-    case 32: return run_forward<ST, 32>(Q, K, V, O, den, st, ws, p, s, t);
-    case 64: return run_forward<ST, 64>(Q, K, V, O, den, st, ws, p, s, t);
-    case 128: return run_forward<ST, 128>(Q, K, V, O, den, st, ws, p, s, t);
-    case 256: return run_forward<ST, 256>(Q, K, V, O, den, st, ws, p, s, t);
+    case 16: return run_forward<ST, 16>(Q, K, V, O, den, st, ws, p, s, t, cin, cout);
+    case 32: return run_forward<ST, 32>(Q, K, V, O, den, st, ws, p, s, t, cin, cout);
+    case 64: return run_forward<ST, 64>(Q, K, V, O, den, st, ws, p, s, t, cin, cout);
+    case 128: return run_forward<ST, 128>(Q, K, V, O, den, st, ws, p, s, t, cin, cout);
+    case 256: return run_forward<ST, 256>(Q, K, V, O, den, st, ws, p, s, t, cin, cout);
     default: return LA_ERR_UNSUPPORTED;
     }
 }
@@ -528,19 +556,163 @@ int dispatch_forward(const void *Q, const void *K, const void *V, void *O, float
 template <class ST>
 int dispatch_backward(const void *Q, const void *K, const void *V, const void *G, void *dQ,
                       void *dK, void *dV, const void *st, float *ws, const Plan &p,
-                      hipStream_t s, Tracer *t)
+                      hipStream_t s, Tracer *t, const float *cin, const float *gin,
+                      float *gout)
 {
+#define LA_BWD(d)                                                                          \
+    run_backward<ST, d>(Q, K, V, G, dQ, dK, dV, st, ws, p, s, t, cin, gin, gout)
     switch (p.D) {
-    case 16: return run_backward<ST, 16>(Q, K, V, G, dQ, dK, dV, st, ws, p, s, t);
-    case 32: return run_backward<ST, 32>(Q, K, V, G, dQ, dK, dV, st, ws, p, s, t);
-    case 64: return run_backward<ST, 64>(Q, K, V, G, dQ, dK, dV, st, ws, p, s, t);
-    case 128: return run_backward<ST, 128>(Q, K, V, G, dQ, dK, dV, st, ws, p, s, t);
-    case 256: return run_backward<ST, 256>(Q, K, V, G, dQ, dK, dV, st, ws, p, s, t);
+    case 16: return LA_BWD(16);
+    case 32: return LA_BWD(32);
+    case 64: return LA_BWD(64);
+    case 128: return LA_BWD(128);
+    case 256: return LA_BWD(256);
     default: return LA_ERR_UNSUPPORTED;
     }
+#undef LA_BWD
 }
 
 size_t elem_size(int dtype) { return dtype == LA_BF16 ? 2 : 4; }
+
+// tokens a carried-in record may stand for (counts enter the kernels as fp32)
+constexpr int64_t kMaxCarry = (int64_t)1 << 40;
+
+// A call over zero tokens passes the carried record through: out = in, or
+// zero without one (the scan kernel over zero segments; no memset or copy
+// node, so the call stays capturable).
+int pass_record(const float *in, float *out, int64_t BH, int64_t D, hipStream_t s)
+{
+    if (out == nullptr)
+        return LA_OK;
+    const size_t rb = (size_t)(BH * (D * D + 2 * D)) * sizeof(float);
+    if (misaligned(out) || misaligned(in))
+        return LA_ERR_ALIGN;
+    if (overlap({(const char *)out, rb}, {(const char *)in, rb}))
+        return LA_ERR_ALIAS;
+    Plan p{};
+    p.BH = BH;
+    p.D = D;
+    p.PS = D * D + 2 * D;
+    p.nseg = 0;
+    return scan(out, out, p, 0, s, nullptr, in, nullptr);
+}
+
+int forward_impl(bool require_o, const void *Q, const void *K, const void *V, void *O,
+                 int64_t B, int64_t H, int64_t N, int64_t D, int causal, int dtype,
+                 const float *cin, int64_t n_carry, float *cout, float *den_out,
+                 void *state_out, void *ws, size_t ws_bytes, void *stream,
+                 void *const *events, int n_events, int *n_launched, const char **names)
+{
+    if (n_launched)
+        *n_launched = 0;
+    if (dtype != LA_FP32 && dtype != LA_BF16)
+        return LA_ERR_DTYPE;
+    int rc = check_sizes(B, H, N, D, causal);
+    if (rc != LA_OK)
+        return rc;
+    if (n_carry < 0 || n_carry > kMaxCarry)
+        return LA_ERR_SHAPE;
+    if (B * H == 0)
+        return LA_OK;
+    if (N == 0)
+        return pass_record(cin, cout, B * H, D, static_cast<hipStream_t>(stream));
+    // O == null asks for the state only: something must receive it
+    if (!Q || !K || !V || !ws || (!O && (require_o || den_out || (!cout && !state_out))))
+        return LA_ERR_NULL;
+    const size_t rb = (size_t)(B * H * (D * D + 2 * D)) * sizeof(float);
+    Plan p = make_plan(B, H, N, D, causal);
+    p.n0 = (float)n_carry;
+    const size_t need = (size_t)make_layout(p).total * sizeof(float);
+    if (ws_bytes < need)
+        return LA_ERR_WORKSPACE;
+    if (misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(O) ||
+        misaligned(den_out) || misaligned(state_out) || misaligned(ws) || misaligned(cin) ||
+        misaligned(cout))
+        return LA_ERR_ALIGN;
+    const size_t tb = (size_t)(B * H * N * D) * elem_size(dtype);
+    const Range ins[4] = {{(const char *)Q, tb},
+                          {(const char *)K, tb},
+                          {(const char *)V, tb},
+                          {(const char *)cin, rb}};
+    const Range outs[5] = {
+        {(const char *)O, tb},
+        {(const char *)den_out, (size_t)(B * H * N) * sizeof(float)},
+        {(const char *)state_out, (size_t)state_floats(p) * sizeof(float)},
+        {(const char *)ws, need},
+        {(const char *)cout, rb}};
+    if (aliased(outs, 5, ins, 4))
+        return LA_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float *w = static_cast<float *>(ws);
+    Tracer t{events, events ? n_events : 0, 0, names};
+    rc = (dtype == LA_FP32)
+             ? dispatch_forward<StF32>(Q, K, V, O, den_out, state_out, w, p, s, &t, cin, cout)
+             : dispatch_forward<StBF16>(Q, K, V, O, den_out, state_out, w, p, s, &t, cin, cout);
+    if (n_launched)
+        *n_launched = t.n;
+    return rc;
+}
+
+int backward_impl(bool require_kv, const void *Q, const void *K, const void *V,
+                  const void *dO, void *dQ, void *dK, void *dV, int64_t B, int64_t H,
+                  int64_t N, int64_t D, int causal, int dtype, const float *cin,
+                  int64_t n_carry, const float *gin, float *gout, const void *state_in,
+                  void *ws, size_t ws_bytes, void *stream, void *const *events, int n_events,
+                  int *n_launched, const char **names)
+{
+    if (n_launched)
+        *n_launched = 0;
+    if (dtype != LA_FP32 && dtype != LA_BF16)
+        return LA_ERR_DTYPE;
+    int rc = check_sizes(B, H, N, D, causal);
+    if (rc != LA_OK)
+        return rc;
+    if (n_carry < 0 || n_carry > kMaxCarry)
+        return LA_ERR_SHAPE;
+    if (B * H == 0)
+        return LA_OK;
+    if (N == 0)
+        return pass_record(gin, gout, B * H, D, static_cast<hipStream_t>(stream));
+    // dK and dV: both given, or (segment calls only) both null
+    if (!Q || !K || !V || !dO || !dQ || !ws || (dK == nullptr) != (dV == nullptr) ||
+        (require_kv && dK == nullptr))
+        return LA_ERR_NULL;
+    const size_t rb = (size_t)(B * H * (D * D + 2 * D)) * sizeof(float);
+    Plan p = make_plan(B, H, N, D, causal);
+    p.n0 = (float)n_carry;
+    const size_t need = (size_t)make_layout(p).total * sizeof(float);
+    if (ws_bytes < need)
+        return LA_ERR_WORKSPACE;
+    if (misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(dO) ||
+        misaligned(dQ) || misaligned(dK) || misaligned(dV) || misaligned(state_in) ||
+        misaligned(ws) || misaligned(cin) || misaligned(gin) || misaligned(gout))
+        return LA_ERR_ALIGN;
+    const size_t tb = (size_t)(B * H * N * D) * elem_size(dtype);
+    const Range ins[7] = {{(const char *)Q, tb},
+                          {(const char *)K, tb},
+                          {(const char *)V, tb},
+                          {(const char *)dO, tb},
+                          {(const char *)state_in, (size_t)state_floats(p) * sizeof(float)},
+                          {(const char *)cin, rb},
+                          {(const char *)gin, rb}};
+    const Range outs[5] = {{(const char *)dQ, tb},
+                           {(const char *)dK, tb},
+                           {(const char *)dV, tb},
+                           {(const char *)ws, need},
+                           {(const char *)gout, rb}};
+    if (aliased(outs, 5, ins, 7))
+        return LA_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float *w = static_cast<float *>(ws);
+    Tracer t{events, events ? n_events : 0, 0, names};
+    rc = (dtype == LA_FP32) ? dispatch_backward<StF32>(Q, K, V, dO, dQ, dK, dV, state_in, w, p,
+                                                       s, &t, cin, gin, gout)
+                            : dispatch_backward<StBF16>(Q, K, V, dO, dQ, dK, dV, state_in, w,
+                                                        p, s, &t, cin, gin, gout);
+    if (n_launched)
+        *n_launched = t.n;
+    return rc;
+}
 
 }  // namespace
 
@@ -584,47 +756,21 @@ size_t la_state_size(int64_t B, int64_t H, int64_t N, int64_t D, int causal)
     return (size_t)state_floats(make_plan(B, H, N, D, causal)) * sizeof(float);
 }
 
+size_t la_record_size(int64_t B, int64_t H, int64_t D)
+{
+    if (B < 0 || H < 0 || !supported_d(D) || B * H > (int64_t)1 << 22)
+        return 0;
+    return (size_t)(B * H * (D * D + 2 * D)) * sizeof(float);
+}
+
 int la_forward_traced(const void *Q, const void *K, const void *V, void *O, int64_t B,
                       int64_t H, int64_t N, int64_t D, int causal, int dtype, float *den_out,
                       void *state_out, void *ws, size_t ws_bytes, void *stream,
                       void *const *events, int n_events, int *n_launched, const char **names)
 {
-    if (n_launched)
-        *n_launched = 0;
-    if (dtype != LA_FP32 && dtype != LA_BF16)
-        return LA_ERR_DTYPE;
-    int rc = check_sizes(B, H, N, D, causal);
-    if (rc != LA_OK)
-        return rc;
-    if (B * H * N == 0)
-        return LA_OK;
-    if (!Q || !K || !V || !O || !ws)
-        return LA_ERR_NULL;
-    const Plan p = make_plan(B, H, N, D, causal);
-    const size_t need = (size_t)make_layout(p).total * sizeof(float);
-    if (ws_bytes < need)
-        return LA_ERR_WORKSPACE;
-    if (misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(O) ||
-        misaligned(den_out) || misaligned(state_out) || misaligned(ws))
-        return LA_ERR_ALIGN;
-    const size_t tb = (size_t)(B * H * N * D) * elem_size(dtype);
-    const Range ins[3] = {{(const char *)Q, tb}, {(const char *)K, tb}, {(const char *)V, tb}};
-    const Range outs[4] = {
-        {(const char *)O, tb},
-        {(const char *)den_out, (size_t)(B * H * N) * sizeof(float)},
-        {(const char *)state_out, (size_t)state_floats(p) * sizeof(float)},
-        {(const char *)ws, need}};
-    if (aliased(outs, 4, ins, 3))
-        return LA_ERR_ALIAS;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    float *w = static_cast<float *>(ws);
-    Tracer t{events, events ? n_events : 0, 0, names};
-    rc = (dtype == LA_FP32)
-             ? dispatch_forward<StF32>(Q, K, V, O, den_out, state_out, w, p, s, &t)
-             : dispatch_forward<StBF16>(Q, K, V, O, den_out, state_out, w, p, s, &t);
-    if (n_launched)
-        *n_launched = t.n;
-    return rc;
+    return forward_impl(true, Q, K, V, O, B, H, N, D, causal, dtype, nullptr, 0, nullptr,
+                        den_out, state_out, ws, ws_bytes, stream, events, n_events, n_launched,
+                        names);
 }
 
 int la_forward(const void *Q, const void *K, const void *V, void *O, int64_t B, int64_t H,
@@ -635,51 +781,26 @@ int la_forward(const void *Q, const void *K, const void *V, void *O, int64_t B, 
                              ws_bytes, stream, nullptr, 0, nullptr, nullptr);
 }
 
+int la_forward_segment(const void *Q, const void *K, const void *V, void *O, int64_t B,
+                       int64_t H, int64_t N, int64_t D, int causal, int dtype,
+                       const float *carry_in, int64_t n_carry, float *carry_out,
+                       float *den_out, void *state_out, void *ws, size_t ws_bytes,
+                       void *stream)
+{
+    return forward_impl(false, Q, K, V, O, B, H, N, D, causal, dtype, carry_in, n_carry,
+                        carry_out, den_out, state_out, ws, ws_bytes, stream, nullptr, 0, nullptr,
+                        nullptr);
+}
+
 int la_backward_traced(const void *Q, const void *K, const void *V, const void *dO, void *dQ,
                        void *dK, void *dV, int64_t B, int64_t H, int64_t N, int64_t D,
                        int causal, int dtype, const void *state_in, void *ws, size_t ws_bytes,
                        void *stream, void *const *events, int n_events, int *n_launched,
                        const char **names)
 {
-    if (n_launched)
-        *n_launched = 0;
-    if (dtype != LA_FP32 && dtype != LA_BF16)
-        return LA_ERR_DTYPE;
-    int rc = check_sizes(B, H, N, D, causal);
-    if (rc != LA_OK)
-        return rc;
-    if (B * H * N == 0)
-        return LA_OK;
-    if (!Q || !K || !V || !dO || !dQ || !dK || !dV || !ws)
-        return LA_ERR_NULL;
-    const Plan p = make_plan(B, H, N, D, causal);
-    const size_t need = (size_t)make_layout(p).total * sizeof(float);
-    if (ws_bytes < need)
-        return LA_ERR_WORKSPACE;
-    if (misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(dO) ||
-        misaligned(dQ) || misaligned(dK) || misaligned(dV) || misaligned(state_in) ||
-        misaligned(ws))
-        return LA_ERR_ALIGN;
-    const size_t tb = (size_t)(B * H * N * D) * elem_size(dtype);
-    const Range ins[5] = {{(const char *)Q, tb},
-                          {(const char *)K, tb},
-                          {(const char *)V, tb},
-                          {(const char *)dO, tb},
-                          {(const char *)state_in, (size_t)state_floats(p) * sizeof(float)}};
-    const Range outs[4] = {
-        {(const char *)dQ, tb}, {(const char *)dK, tb}, {(const char *)dV, tb},
-        {(const char *)ws, need}};
-    if (aliased(outs, 4, ins, 5))
-        return LA_ERR_ALIAS;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    float *w = static_cast<float *>(ws);
-    Tracer t{events, events ? n_events : 0, 0, names};
-    rc = (dtype == LA_FP32)
-             ? dispatch_backward<StF32>(Q, K, V, dO, dQ, dK, dV, state_in, w, p, s, &t)
-             : dispatch_backward<StBF16>(Q, K, V, dO, dQ, dK, dV, state_in, w, p, s, &t);
-    if (n_launched)
-        *n_launched = t.n;
-    return rc;
+    return backward_impl(true, Q, K, V, dO, dQ, dK, dV, B, H, N, D, causal, dtype, nullptr, 0,
+                         nullptr, nullptr, state_in, ws, ws_bytes, stream, events, n_events,
+                         n_launched, names);
 }
 
 int la_backward(const void *Q, const void *K, const void *V, const void *dO, void *dQ,
@@ -688,6 +809,17 @@ int la_backward(const void *Q, const void *K, const void *V, const void *dO, voi
 {
     return la_backward_traced(Q, K, V, dO, dQ, dK, dV, B, H, N, D, causal, dtype, state_in, ws,
                               ws_bytes, stream, nullptr, 0, nullptr, nullptr);
+}
+
+int la_backward_segment(const void *Q, const void *K, const void *V, const void *dO, void *dQ,
+                        void *dK, void *dV, int64_t B, int64_t H, int64_t N, int64_t D,
+                        int causal, int dtype, const float *carry_in, int64_t n_carry,
+                        const float *gcarry_in, float *gcarry_out, const void *state_in,
+                        void *ws, size_t ws_bytes, void *stream)
+{
+    return backward_impl(false, Q, K, V, dO, dQ, dK, dV, B, H, N, D, causal, dtype, carry_in,
+                         n_carry, gcarry_in, gcarry_out, state_in, ws, ws_bytes, stream, nullptr,
+                         0, nullptr, nullptr);
 }
 
 }  // extern "C"

@@ -503,17 +503,22 @@ __global__ __launch_bounds__(threads_for<D>()) void k_grad_state_local(
         out[D * D + tid] = csum;
 }
 
-// Combine the per-segment records of every head in a fixed order.
-//   mode 0: out[bh] = sum_s part[bh][s]
-//   mode 1: part[bh][s] <- sum_{s' < s} part[bh][s']   (in place)
-//   mode 2: part[bh][s] <- sum_{s' > s} part[bh][s']   (in place)
+// Combine the per-segment records of every head in a fixed order, starting
+// from init[bh] (a record carried in from outside the call; zero when init
+// is null):
+//   mode 0: out[bh] = init[bh] + sum_s part[bh][s]
+//   mode 1: part[bh][s] <- init[bh] + sum_{s' < s} part[bh][s']   (in place)
+//   mode 2: part[bh][s] <- init[bh] + sum_{s' > s} part[bh][s']   (in place)
+// and, when total is not null, total[bh] = init[bh] + sum_s part[bh][s]
+// (the record carried out of the call).
 // Each thread takes 4 consecutive floats of the record (records are PS =
 // D^2 + 2D floats, a multiple of 4, and 16-byte aligned); the segments'
 // loads of a batch are issued before any of them is added, in order.
 __global__ __launch_bounds__(256) void k_state_scan(float *__restrict__ part,
                                                     float *__restrict__ out, int nseg,
                                                     int64_t PS, int64_t blocks_per_head,
-                                                    int mode)
+                                                    int mode, const float *__restrict__ init,
+                                                    float *__restrict__ total)
 {
     constexpr int BATCH = 8;
     const int64_t bh = blockIdx.x / blocks_per_head;
@@ -523,6 +528,8 @@ __global__ __launch_bounds__(256) void k_state_scan(float *__restrict__ part,
     f4 *p = reinterpret_cast<f4 *>(part + bh * nseg * PS + e);
     const int64_t ps4 = PS / 4;
     f4 run = {0.f, 0.f, 0.f, 0.f};
+    if (init)
+        run = *reinterpret_cast<const f4 *>(init + bh * PS + e);
     if (mode == 0) {
         for (int s0 = 0; s0 < nseg; s0 += BATCH) {
             f4 v[BATCH];
@@ -549,6 +556,8 @@ __global__ __launch_bounds__(256) void k_state_scan(float *__restrict__ part,
             run += v;
         }
     }
+    if (total)
+        *reinterpret_cast<f4 *>(total + bh * PS + e) = run;
 }
 
 // Forward.  state: CAUSAL ? exclusive-prefix record per (head, segment)
@@ -558,7 +567,7 @@ __global__ __launch_bounds__(threads_for<D>()) void k_forward(
     const typename ST::T *__restrict__ Q, const typename ST::T *__restrict__ Kp,
     const typename ST::T *__restrict__ Vp, typename ST::T *__restrict__ O,
     float *__restrict__ den_out, const float *__restrict__ state, int64_t N,
-    int64_t seg_len, int nseg)
+    int64_t seg_len, int nseg, float n0)
 {
     typedef Cfg<D, DefCS<D>::value> C;
     constexpr int R = CAUSAL ? C::RC : C::RN;
@@ -617,7 +626,7 @@ __global__ __launch_bounds__(threads_for<D>()) void k_forward(
         if constexpr (CAUSAL) {
             build_w<C>(wl, pp, tid);
             if (tid < R) {
-                float s = (float)c0 + rowv[tid];
+                float s = (n0 + (float)c0) + rowv[tid];
                 for (int j = 0; j <= tid; ++j) {
                     float p = 0.f;
                     for (int ww = 0; ww < C::NW; ++ww)
@@ -628,7 +637,7 @@ __global__ __launch_bounds__(threads_for<D>()) void k_forward(
             }
         } else {
             for (int i = tid; i < R; i += C::NT)
-                denl[i] = (float)N + rowv[i];
+                denl[i] = (n0 + (float)N) + rowv[i];
         }
         __syncthreads();
 
@@ -679,7 +688,7 @@ __global__ __launch_bounds__(threads_for<D>()) void k_bwd_q(
     const typename ST::T *__restrict__ Vp, const typename ST::T *__restrict__ G,
     typename ST::T *__restrict__ dQ, const float *__restrict__ state,
     float *__restrict__ gpart, float *__restrict__ cbuf, int64_t N, int64_t seg_len,
-    int nseg)
+    int nseg, float n0)
 {
     typedef Cfg<D, 1> C;
     constexpr int R = CAUSAL ? C::RC : C::RN;
@@ -749,7 +758,7 @@ __global__ __launch_bounds__(threads_for<D>()) void k_bwd_q(
         if constexpr (CAUSAL) {
             build_w<C>(wl, pp, tid);
             if (tid < R) {
-                float s = (float)c0 + rowqz[tid];
+                float s = (n0 + (float)c0) + rowqz[tid];
                 for (int j = 0; j <= tid; ++j) {
                     float p = 0.f;
                     for (int ww = 0; ww < C::NW; ++ww)
@@ -760,7 +769,7 @@ __global__ __launch_bounds__(threads_for<D>()) void k_bwd_q(
             }
         } else {
             for (int i = tid; i < R; i += C::NT)
-                denl[i] = (float)N + rowqz[i];
+                denl[i] = (n0 + (float)N) + rowqz[i];
         }
         __syncthreads();
         // A = dO / den (rows past the end are zero)

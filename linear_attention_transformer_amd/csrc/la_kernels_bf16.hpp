@@ -104,7 +104,7 @@ template <int D, int KIND>
 __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
     const uint16_t *__restrict__ X, const uint16_t *__restrict__ X2, uint16_t *__restrict__ Out,
     uint16_t *__restrict__ Out2, float *__restrict__ den_out, float *__restrict__ cbuf,
-    const float *__restrict__ rec, int64_t N, int64_t seg_len, int nseg)
+    const float *__restrict__ rec, int64_t N, int64_t seg_len, int nseg, float n0)
 {
     static_assert(D >= 32 && D <= 128, "32-column output blocks");
     static_assert(KIND >= 0 && KIND <= 2, "forward, dQ or dK | dV");
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
 #pragma unroll
             for (int c2 = 0; c2 < NCB; ++c2)
                 qz += xch[buf][rg][c2][j][0];
-            const float den = (float)N + qz;
+            const float den = (n0 + (float)N) + qz;
             const float inv = 1.f / den;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -344,7 +344,7 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
                 sy += xch[buf][rg][c2][j][0];
                 qz += xch[buf][rg][c2][j][DQ ? 1 : 0];
             }
-            const float inv = 1.f / ((float)N + qz);
+            const float inv = 1.f / ((n0 + (float)N) + qz);
             const float c = sy * inv * inv;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -774,7 +774,7 @@ template <int D>
 __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal_bf(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ den_out,
-    const float *__restrict__ rec, int64_t N, int64_t seg_len, int nseg)
+    const float *__restrict__ rec, int64_t N, int64_t seg_len, int nseg, float n0)
 {
     typedef nc::IO<StBF16> io;
     static_assert(D >= 32 && D <= 128, "32-column blocks, state in registers");
@@ -919,7 +919,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal_bf(
         for (int c2 = 0; c2 < NCB; ++c2)
             qz += qzx[c2][j];
         // (4) normalised rows of the chunk, stored during the next product
-        const float den = (float)t0 + qz + rs;
+        const float den = (n0 + (float)t0) + qz + rs;
         const float inv = 1.f / den;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -960,7 +960,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ G, uint16_t *__restrict__ dQ,
     float *__restrict__ cbuf, const float *__restrict__ rec, int64_t N, int64_t seg_len,
-    int nseg)
+    int nseg, float n0)
 {
     typedef nc::IO<StBF16> io;
     static_assert(D >= 32 && D <= 128, "32-column blocks, state in registers");
@@ -1125,7 +1125,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
             qyu += xq[pp][j];
             qzs += xz[pp][j];
         }
-        const float den = (float)t0 + qzs + rs;
+        const float den = (n0 + (float)t0) + qzs + rs;
         const float inv = 1.f / den;
         const float c = (qyu + cw) * inv * inv;
         const float cden = c * den;

@@ -132,7 +132,7 @@ __global__ __launch_bounds__(threads<D>()) void k_fwd_causal(
     const typename ST::T *__restrict__ Q, const typename ST::T *__restrict__ K,
     const typename ST::T *__restrict__ V, typename ST::T *__restrict__ O,
     float *__restrict__ den_out, const float *__restrict__ rec, int64_t N, int64_t seg_len,
-    int nseg)
+    int nseg, float n0)
 {
     typedef typename ST::T T;
     typedef IO<ST> io;
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(threads<D>()) void k_fwd_causal(
         uc += __shfl_xor(uc, 32, 64);
         qz += __shfl_xor(qz, 32, 64);
         // (4) normalised rows of the chunk, stored during the next product
-        const float den = (float)t0 + qz + rs;
+        const float den = (n0 + (float)t0) + qz + rs;
         const float inv = 1.f / den;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(threads<D>()) void k_bwd_q_causal(
     const typename ST::T *__restrict__ Q, const typename ST::T *__restrict__ K,
     const typename ST::T *__restrict__ V, const typename ST::T *__restrict__ G,
     typename ST::T *__restrict__ dQ, float *__restrict__ cbuf, const float *__restrict__ rec,
-    int64_t N, int64_t seg_len, int nseg)
+    int64_t N, int64_t seg_len, int nseg, float n0)
 {
     typedef typename ST::T T;
     typedef IO<ST> io;
@@ -447,7 +447,7 @@ __global__ __launch_bounds__(threads<D>()) void k_bwd_q_causal(
 #pragma unroll
         for (int p = 0; p < NCB; ++p)
             qy += xq[p][j];
-        const float den = (float)t0 + qz + rs;
+        const float den = (n0 + (float)t0) + qz + rs;
         const float inv = 1.f / den;
         const float c = (gu + qy + cw) * inv * inv;
         const float cden = c * den;

@@ -421,7 +421,7 @@ __global__ __launch_bounds__(apply_threads<D>()) void k_apply_nc(
     const typename ST::T *__restrict__ X, const typename ST::T *__restrict__ X2,
     typename ST::T *__restrict__ Out, typename ST::T *__restrict__ Out2,
     float *__restrict__ den_out, const float *__restrict__ rec, int64_t N, int64_t seg_len,
-    int nseg)
+    int nseg, float n0)
 {
     typedef typename ST::T T;
     typedef IO<ST> io;
@@ -597,7 +597,7 @@ __global__ __launch_bounds__(apply_threads<D>()) void k_apply_nc(
 #pragma unroll
             for (int c2 = 0; c2 < NCB; ++c2)
                 qz += xch[buf][rg][c2][j];
-            const float den = (float)N + qz;
+            const float den = (n0 + (float)N) + qz;
             const float inv = 1.f / den;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -635,7 +635,7 @@ template <class ST, int D, bool DS = true>
 __global__ __launch_bounds__(512) void k_bwd_q_nc(
     const typename ST::T *__restrict__ G, const typename ST::T *__restrict__ Q,
     typename ST::T *__restrict__ dQ, float *__restrict__ part_out,
-    const float *__restrict__ rec, int64_t N, int64_t seg_len, int nseg)
+    const float *__restrict__ rec, int64_t N, int64_t seg_len, int nseg, float n0)
 {
     typedef typename ST::T T;
     typedef IO<ST> io;
@@ -723,7 +723,7 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
 #pragma unroll
             for (int o = 1; o < CPR; o <<= 1)
                 pz += __shfl_xor(pz, o, 64);
-            const float inv = 1.f / ((float)N + pz);
+            const float inv = 1.f / ((n0 + (float)N) + pz);
             if (c % CPR == 0)
                 ivx[buf][c / CPR] = inv;
             float gv[VEC];

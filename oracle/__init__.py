@@ -50,6 +50,13 @@ def _bind(lib):
         f.argtypes = [dp, dp, dp, dp, dp, dp, dp, i64, i64, i64, i64,
                       ctypes.c_int]
         f.restype = None
+    lib.la_oracle_forward_carry.argtypes = [dp, dp, dp, dp, dp, dp, ctypes.c_double,
+                                            dp, i64, i64, i64, i64, ctypes.c_int]
+    lib.la_oracle_forward_carry.restype = None
+    lib.la_oracle_backward_carry.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp,
+                                             ctypes.c_double, dp, dp, i64, i64,
+                                             i64, i64, ctypes.c_int]
+    lib.la_oracle_backward_carry.restype = None
     lib.la_oracle_max_threads.argtypes = []
     lib.la_oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -102,6 +109,47 @@ def _backward(name, q, k, v, g, causal, lib=None):
     return dq, dk, dv
 
 
+def _record(rec, B, H, D):
+    """A [B,H,D*D+2D] fp64 record, or None."""
+    if rec is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(rec, dtype=np.float64))
+    if a.shape != (B, H, D * D + 2 * D):
+        raise ValueError("expected a record of shape %r, got %r"
+                         % ((B, H, D * D + 2 * D), a.shape))
+    return a
+
+
+def _optr(a):
+    return None if a is None else _ptr(a)
+
+
+def _forward_carry(q, k, v, causal, rec_in, n0, lib=None):
+    q, k, v = _c64(q), _c64(k), _c64(v)
+    B, H, N, D = _check(q, k, v)
+    rec_in = _record(rec_in, B, H, D)
+    o = np.empty_like(q)
+    den = np.empty((B, H, N), dtype=np.float64)
+    rec_out = np.empty((B, H, D * D + 2 * D), dtype=np.float64)
+    (lib or _load()).la_oracle_forward_carry(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(den), _optr(rec_in), float(n0),
+        _ptr(rec_out), B, H, N, D, int(bool(causal)))
+    return o, den, rec_out
+
+
+def _backward_carry(q, k, v, g, causal, rec_in, n0, grec_in, lib=None):
+    q, k, v, g = _c64(q), _c64(k), _c64(v), _c64(g)
+    B, H, N, D = _check(q, k, v, g)
+    rec_in, grec_in = _record(rec_in, B, H, D), _record(grec_in, B, H, D)
+    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+    grec_out = np.empty((B, H, D * D + 2 * D), dtype=np.float64)
+    (lib or _load()).la_oracle_backward_carry(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(dq), _ptr(dk), _ptr(dv),
+        _optr(rec_in), float(n0), _optr(grec_in), _ptr(grec_out), B, H, N, D,
+        int(bool(causal)))
+    return dq, dk, dv, grec_out
+
+
 def forward_direct(q, k, v, causal=False):
     """O(N^2 D) definition: returns (O, den) as fp64 arrays."""
     return _forward("la_oracle_forward_direct", q, k, v, causal)
@@ -120,6 +168,24 @@ def backward_direct(q, k, v, g, causal=False):
 def backward_state(q, k, v, g, causal=False):
     """O(N D^2) gradients through the forward and gradient states."""
     return _backward("la_oracle_backward_state", q, k, v, g, causal)
+
+
+def forward_carry(q, k, v, causal=False, rec_in=None, n0=0):
+    """State form over one piece of a longer sequence.  rec_in is the record
+    [S | z | u] ([B,H,D*D+2D]) of n0 tokens outside the piece whose keys every
+    row of the piece sees (causal: the tokens before it; non-causal: the rest
+    of the sequence), or None.  Returns (O, den, rec_out) with rec_out the
+    record of those tokens plus the piece's own."""
+    return _forward_carry(q, k, v, causal, rec_in, n0)
+
+
+def backward_carry(q, k, v, g, causal=False, rec_in=None, n0=0, grec_in=None):
+    """Gradients of one piece.  rec_in, n0 as for forward_carry; grec_in is
+    the gradient record [R | r | t] of the rows outside the piece that see
+    its keys (causal: the rows after it; non-causal: the other rows), or
+    None.  Returns (dQ, dK, dV, grec_out) with grec_out = grec_in plus the
+    piece's own rows' record."""
+    return _backward_carry(q, k, v, g, causal, rec_in, n0, grec_in)
 
 
 def max_threads() -> int:
@@ -145,6 +211,12 @@ class Variant:
 
     def backward_state(self, q, k, v, g, causal=False):
         return _backward("la_oracle_backward_state", q, k, v, g, causal, self._lib)
+
+    def forward_carry(self, q, k, v, causal=False, rec_in=None, n0=0):
+        return _forward_carry(q, k, v, causal, rec_in, n0, self._lib)
+
+    def backward_carry(self, q, k, v, g, causal=False, rec_in=None, n0=0, grec_in=None):
+        return _backward_carry(q, k, v, g, causal, rec_in, n0, grec_in, self._lib)
 
 
 def build_variant(src_text: str, out_dir: str) -> "Variant":

@@ -43,6 +43,18 @@
  *              uses the matching states of the gradient (R = sum q a^T,
  *              r = sum c q, t = sum a), summed over the visible queries.
  *
+ * Carried state (a sequence processed in pieces; the state-update pseudocode
+ * of the cloud.baidu.com article grows one running state, so a piece can start
+ * from the state its predecessors left): the *_carry entry points take a
+ * record [S (D x D) | z (D) | u (D)] standing for n0 tokens outside the call
+ * whose keys every row of the call sees (causal: the tokens before it;
+ * non-causal: the rest of the sequence), and return the record of those
+ * tokens plus the call's own.  Their backward takes the matching gradient
+ * record [R | r | t] of the rows outside the call that see the call's keys
+ * (causal: the rows after it; non-causal: the other rows) and returns it
+ * plus the call's own rows' record.  With empty carries they are exactly the
+ * *_state evaluations.
+ *
  * Where the pages are silent (no epsilon in the denominator, no scaling of
  * q.k, identity feature map, causal mask includes the diagonal) the plainest
  * reading is taken; the denominator is divided as is (IEEE semantics).
@@ -201,30 +213,58 @@ static double state_apply(const double *S, const double *z, const double *u,
     return den;
 }
 
+/* record [S | z | u] <-> separate arrays (NULL record = zero state) */
+static void record_load(const double *rec, double *S, double *z, double *u,
+                        int64_t D)
+{
+    if (!rec)
+        return;
+    memcpy(S, rec, sizeof(double) * (size_t)(D * D));
+    memcpy(z, rec + D * D, sizeof(double) * (size_t)D);
+    memcpy(u, rec + D * D + D, sizeof(double) * (size_t)D);
+}
+
+static void record_store(double *rec, const double *S, const double *z,
+                         const double *u, int64_t D)
+{
+    if (!rec)
+        return;
+    memcpy(rec, S, sizeof(double) * (size_t)(D * D));
+    memcpy(rec + D * D, z, sizeof(double) * (size_t)D);
+    memcpy(rec + D * D + D, u, sizeof(double) * (size_t)D);
+}
+
+/* The state starts from rec_in (n0 tokens), or zero; rec_out gets the final
+ * state. */
 static void head_forward_state(const double *q, const double *k,
                                const double *v, double *o, double *den,
-                               int64_t N, int64_t D, int causal)
+                               int64_t N, int64_t D, int causal,
+                               const double *rec_in, double n0,
+                               double *rec_out)
 {
     double *S = (double *)calloc((size_t)(D * D), sizeof(double));
     double *z = (double *)calloc((size_t)D, sizeof(double));
     double *u = (double *)calloc((size_t)D, sizeof(double));
+    record_load(rec_in, S, z, u, D);
     if (!causal) {
         for (int64_t j = 0; j < N; ++j)
             state_add(S, z, u, k + j * D, v + j * D, D);
         for (int64_t i = 0; i < N; ++i) {
-            double di = state_apply(S, z, u, (double)N, q + i * D, o + i * D, D);
+            double di = state_apply(S, z, u, n0 + (double)N, q + i * D,
+                                    o + i * D, D);
             if (den)
                 den[i] = di;
         }
     } else {
         for (int64_t i = 0; i < N; ++i) {
             state_add(S, z, u, k + i * D, v + i * D, D);
-            double di = state_apply(S, z, u, (double)(i + 1), q + i * D,
+            double di = state_apply(S, z, u, n0 + (double)(i + 1), q + i * D,
                                     o + i * D, D);
             if (den)
                 den[i] = di;
         }
     }
+    record_store(rec_out, S, z, u, D);
     free(u);
     free(z);
     free(S);
@@ -240,7 +280,26 @@ void la_oracle_forward_state(const double *Q, const double *K,
     for (int64_t h = 0; h < heads; ++h) {
         int64_t off = h * N * D;
         head_forward_state(Q + off, K + off, V + off, O + off,
-                           den ? den + h * N : NULL, N, D, causal);
+                           den ? den + h * N : NULL, N, D, causal, NULL, 0.0,
+                           NULL);
+    }
+}
+
+/* records: [B,H,D*D+2D]; rec_in may be NULL (zero state) */
+void la_oracle_forward_carry(const double *Q, const double *K,
+                             const double *V, double *O, double *den,
+                             const double *rec_in, double n0, double *rec_out,
+                             int64_t B, int64_t H, int64_t N, int64_t D,
+                             int causal)
+{
+    int64_t heads = B * H, PS = D * D + 2 * D;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t h = 0; h < heads; ++h) {
+        int64_t off = h * N * D;
+        head_forward_state(Q + off, K + off, V + off, O + off,
+                           den ? den + h * N : NULL, N, D, causal,
+                           rec_in ? rec_in + h * PS : NULL, n0,
+                           rec_out + h * PS);
     }
 }
 
@@ -299,10 +358,13 @@ static void grad_state_apply(const double *R, const double *r,
     }
 }
 
+/* The forward state starts from rec_in (n0 tokens), the gradient state from
+ * grec_in; grec_out gets the final gradient state. */
 static void head_backward_state(const double *q, const double *k,
                                 const double *v, const double *g, double *dq,
                                 double *dk, double *dv, int64_t N, int64_t D,
-                                int causal)
+                                int causal, const double *rec_in, double n0,
+                                const double *grec_in, double *grec_out)
 {
     size_t DD = (size_t)(D * D);
     double *S = (double *)calloc(DD, sizeof(double));
@@ -314,13 +376,15 @@ static void head_backward_state(const double *q, const double *k,
     double *otmp = (double *)malloc(sizeof(double) * (size_t)D);
     double *A = (double *)malloc(sizeof(double) * (size_t)(N * D));
     double *C = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+    record_load(rec_in, S, z, u, D);
+    record_load(grec_in, R, r, t, D);
 
     if (!causal) {
         for (int64_t j = 0; j < N; ++j)
             state_add(S, z, u, k + j * D, v + j * D, D);
         for (int64_t i = 0; i < N; ++i)
-            C[i] = state_grad_query(S, z, u, (double)N, q + i * D, g + i * D,
-                                    A + i * D, dq + i * D, otmp, D);
+            C[i] = state_grad_query(S, z, u, n0 + (double)N, q + i * D,
+                                    g + i * D, A + i * D, dq + i * D, otmp, D);
         for (int64_t i = 0; i < N; ++i)
             grad_state_add(R, r, t, q + i * D, A + i * D, C[i], D);
         for (int64_t j = 0; j < N; ++j)
@@ -330,7 +394,7 @@ static void head_backward_state(const double *q, const double *k,
         /* forward sweep: prefix states (including token i) feed dq_i */
         for (int64_t i = 0; i < N; ++i) {
             state_add(S, z, u, k + i * D, v + i * D, D);
-            C[i] = state_grad_query(S, z, u, (double)(i + 1), q + i * D,
+            C[i] = state_grad_query(S, z, u, n0 + (double)(i + 1), q + i * D,
                                     g + i * D, A + i * D, dq + i * D, otmp, D);
         }
         /* reverse sweep: suffix states (queries i >= j) feed dk_j, dv_j */
@@ -340,6 +404,7 @@ static void head_backward_state(const double *q, const double *k,
                              dv + j * D, D);
         }
     }
+    record_store(grec_out, R, r, t, D);
     free(C);
     free(A);
     free(otmp);
@@ -361,6 +426,27 @@ void la_oracle_backward_state(const double *Q, const double *K,
     for (int64_t h = 0; h < heads; ++h) {
         int64_t off = h * N * D;
         head_backward_state(Q + off, K + off, V + off, dO + off, dQ + off,
-                            dK + off, dV + off, N, D, causal);
+                            dK + off, dV + off, N, D, causal, NULL, 0.0, NULL,
+                            NULL);
+    }
+}
+
+/* records: [B,H,D*D+2D]; rec_in and grec_in may be NULL (zero state) */
+void la_oracle_backward_carry(const double *Q, const double *K,
+                              const double *V, const double *dO, double *dQ,
+                              double *dK, double *dV, const double *rec_in,
+                              double n0, const double *grec_in,
+                              double *grec_out, int64_t B, int64_t H,
+                              int64_t N, int64_t D, int causal)
+{
+    int64_t heads = B * H, PS = D * D + 2 * D;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t h = 0; h < heads; ++h) {
+        int64_t off = h * N * D;
+        head_backward_state(Q + off, K + off, V + off, dO + off, dQ + off,
+                            dK + off, dV + off, N, D, causal,
+                            rec_in ? rec_in + h * PS : NULL, n0,
+                            grec_in ? grec_in + h * PS : NULL,
+                            grec_out + h * PS);
     }
 }

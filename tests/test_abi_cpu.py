@@ -110,6 +110,56 @@ def test_host_validation_rejects_before_launch():
              P(4 * tb), P(7 * tb), ws, None) == 6
     assert g(P(), P(tb), P(2 * tb), None, P(4 * tb), P(5 * tb), P(6 * tb), B, H, N, D, 0, 0,
              None, P(7 * tb), ws, None) == 1
+    # la_backward needs dK and dV
+    assert g(P(), P(tb), P(2 * tb), P(3 * tb), P(4 * tb), None, None, B, H, N, D, 0, 0,
+             None, P(7 * tb), ws, None) == 1
+
+
+@needs_no_gpu
+def test_host_validation_segment_calls():
+    """The carried-state calls reject bad records and counts before launch."""
+    lib = la.load_library()
+    buf = (ctypes.c_char * (1 << 21))()
+    a16 = (ctypes.addressof(buf) + 15) & ~15
+    P = lambda off=0: ctypes.c_void_p(a16 + off)
+    B, H, N, D = 1, 2, 8, 16
+    ws = la.workspace_size(B, H, N, D, True)
+    tb = B * H * N * D * 4
+    rb = la.record_size(B, H, D)
+    assert rb == B * H * (D * D + 2 * D) * 4
+    assert la.record_size(1, 1, 48) == 0 and la.record_size(-1, 1, 16) == 0
+    W, CI, CO = 4 * tb, 4 * tb + ws + 256, 4 * tb + ws + 256 + rb + 256
+    f = lib.la_forward_segment
+
+    def fa(o=P(3 * tb), cin=P(CI), n=5, cout=P(CO), den=None, st=None, N_=N):
+        return f(P(), P(tb), P(2 * tb), o, B, H, N_, D, 1, 0, cin, n, cout, den, st, P(W), ws,
+                 None)
+
+    assert fa(n=-1) == 2
+    assert fa(n=(1 << 40) + 1) == 2
+    assert fa(cout=P(CI + 16)) == 6              # carry_out overlaps carry_in
+    assert fa(cout=P(0)) == 6                    # carry_out overlaps Q
+    assert fa(cin=P(3 * tb)) == 6                # O overlaps carry_in
+    assert fa(cout=P(CO + 4)) == 7
+    assert fa(cin=P(CI + 8)) == 7
+    assert fa(o=None, cout=None) == 1            # nothing would receive a result
+    assert fa(o=None, den=P(CO + rb + 256)) == 1  # den needs O
+    assert fa(N_=0, cout=P(CI + 16)) == 6        # zero tokens: pass-through checks still apply
+    assert fa(N_=0, cout=P(CO + 4)) == 7
+    g = lib.la_backward_segment
+
+    def ga(dk=P(5 * tb), dv=P(6 * tb), gin=P(CI), gout=P(CO), n=5):
+        return g(P(), P(tb), P(2 * tb), P(3 * tb), P(4 * tb), dk, dv, B, H, N, D, 1, 0, None, n,
+                 gin, gout, None, P(7 * tb), ws, None)
+
+    ws_b = 7 * tb
+    CI, CO = ws_b + ws + 256, ws_b + ws + 256 + rb + 256
+    assert ga(gin=P(CI), gout=P(CO), n=-3) == 2
+    assert ga(dk=None, gin=P(CI), gout=P(CO)) == 1     # dK without dV
+    assert ga(dv=None, gin=P(CI), gout=P(CO)) == 1
+    assert ga(gin=P(CI), gout=P(CI + 32)) == 6         # gcarry_out overlaps gcarry_in
+    assert ga(gin=P(CI), gout=P(4 * tb)) == 6          # gcarry_out overlaps dQ
+    assert ga(gin=P(CI + 4), gout=P(CO)) == 7
 
 
 def test_python_side_refuses_cpu_tensors():

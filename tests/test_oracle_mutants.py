@@ -8,6 +8,7 @@ and at least one must fail.  The real oracle is never modified.
 import pytest
 
 import oracle
+from tests import test_oracle_carry as carry
 from tests import test_oracle_pins as pins
 
 # (name, text in la_oracle.c, replacement)
@@ -38,6 +39,12 @@ MUTANTS = [
      "double w = sim(q + j * D, k + i * D, D);\n            for (int64_t d = 0; d < D; ++d) {"),
     ("c_i uses g instead of a", "double c = dotv(a, o + i * D, D);",
      "double c = dotv(g + i * D, o + i * D, D);"),
+    ("carried count left out of the non-causal denominator",
+     "state_apply(S, z, u, n0 + (double)N,", "state_apply(S, z, u, (double)N,"),
+    ("gradient carry ignored", "record_load(grec_in, R, r, t, D);", ""),
+    ("carried record stored with z and u swapped",
+     "memcpy(rec + D * D + D, u, sizeof(double) * (size_t)D);",
+     "memcpy(rec + D * D + D, z, sizeof(double) * (size_t)D);"),
     ("causal count off by one", "(double)(i + 1), q + i * D,\n                                    o + i * D, D);",
      "(double)(i), q + i * D,\n                                    o + i * D, D);"),
 ]
@@ -58,6 +65,10 @@ def _pin_cases():
         cases.append((pins.test_autograd_gradients,
                       dict(shape=(1, 3, 7, 5), causal=causal)))
         cases.append((pins.test_first_order_agreement_with_softmax, dict(causal=causal)))
+        cases.append((carry.test_pieces_forward_match_whole_sequence, dict(causal=causal)))
+        cases.append((carry.test_pieces_backward_match_whole_sequence, dict(causal=causal)))
+        cases.append((carry.test_gradient_record_is_derivative_of_carried_state,
+                      dict(causal=causal)))
     return cases
 
 
