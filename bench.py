@@ -16,7 +16,10 @@ sustained load only after the first few tens of steps from idle).  `roofline`
 gives the dominant kernel's achieved rate from per-launch HIP events (a
 second timed pass in which the library records caller-owned events around
 every launch), against the MI355X fp32-MFMA or HBM peak.  `cpu_baseline`
-times the fp64 CPU oracle on the host.
+times the fp64 CPU oracle on the host.  `variants` times the other storage
+type and mask at the same shape; `pieces` times the causal step streamed as
+equal pieces through the carried-state calls (la_forward_segment /
+la_backward_segment).
 """
 from __future__ import annotations
 
@@ -211,6 +214,50 @@ def time_variant(la, make_inputs, dev, B, H, N, D, dtype, causal, steps, warmup)
     return e0.elapsed_time(e1) / steps
 
 
+def time_pieces(la, make_inputs, dev, B, H, N, D, dtype, pieces, steps, warmup):
+    """ms per causal fwd+bwd step of the same workload streamed as `pieces`
+    equal pieces through the carried-state calls: forward in order, each piece
+    taking the previous one's record; backward in reverse, each taking the
+    next piece's gradient record.  Inputs are split into per-piece tensors
+    before timing."""
+    import torch
+    q, k, v, g = make_inputs(B, H, N, D, dtype=dtype, seed=0, device=dev, draw_device=dev)
+    n = N // pieces
+    sl = [slice(i * n, N if i == pieces - 1 else (i + 1) * n) for i in range(pieces)]
+    parts = [[x[:, :, c].contiguous() for x in (q, k, v, g)] for c in sl]
+    del q, k, v, g
+    outs = [[torch.empty_like(p[0]) for _ in range(4)] for p in parts]
+    recs = [la.new_record(B, H, D, dev) for _ in range(pieces)]
+    grecs = [la.new_record(B, H, D, dev) for _ in range(pieces)]
+    ws = max((la.alloc_workspace(B, H, c.stop - c.start, D, True, dev) for c in sl),
+             key=lambda t: t.numel())
+    sts = [torch.empty(max(la.state_size(B, H, c.stop - c.start, D, True) // 4, 4),
+                       dtype=torch.float32, device=dev) for c in sl]
+
+    def step():
+        for i, (p, c) in enumerate(zip(parts, sl)):
+            la.forward_segment(p[0], p[1], p[2], True, carry_in=recs[i - 1] if i else None,
+                               n_carry=c.start, carry_out=recs[i], out=outs[i][0],
+                               state_out=sts[i], workspace=ws)
+        for i in reversed(range(pieces)):
+            p, c = parts[i], sl[i]
+            la.backward_segment(p[0], p[1], p[2], p[3], True, n_carry=c.start,
+                                gcarry_in=grecs[i + 1] if i + 1 < pieces else None,
+                                gcarry_out=grecs[i], state=sts[i], outs=outs[i][1:],
+                                workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def cpu_baseline(q, k, v, g, causal):
     import oracle
     from linear_attention_transformer_amd.inputs import as_f64_numpy
@@ -257,6 +304,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the other storage type / mask at the same shape")
+    ap.add_argument("--pieces", type=int, default=4,
+                    help="also time the causal step of this shape and storage streamed as "
+                         "this many pieces through the carried-state calls (0 = skip)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs of this script (FETCH_SIZE, "
                          "WRITE_SIZE) for the given workload into profiles/traffic.json; "
@@ -389,6 +439,21 @@ def main():
                 print("bench: variant %s %s: %.3f ms/step" % (vdt, "causal" if vc else
                       "non-causal", vms), file=sys.stderr, flush=True)
 
+    # the causal step streamed in pieces through the carried-state calls,
+    # against the same step over the whole sequence
+    pieces = None
+    if not args.no_variants and args.pieces > 1:
+        torch.cuda.empty_cache()
+        pms = time_pieces(la, make_inputs, dev, B, H, N, D, dt, args.pieces,
+                          max(args.steps // 2, 5), args.warmup)
+        whole = ms if causal else variants["%s causal" % args.dtype]["ms_per_step"]
+        pieces = {"pieces": args.pieces, "causal": True, "ms_per_step": round(pms, 4),
+                  "whole_sequence_ms_per_step": round(whole, 4),
+                  "tokens_per_s": round(B * N / (pms * 1e-3), 1),
+                  "vs_whole": round(whole / pms, 4)}
+        print("bench: causal %s in %d pieces: %.3f ms/step (whole sequence %.3f)"
+              % (args.dtype, args.pieces, pms, whole), file=sys.stderr, flush=True)
+
     # the copy reference runs after every timed region: a burst of streaming
     # traffic just before one would lower its clocks
     copy_gbs = copy_reference(dev)
@@ -425,6 +490,7 @@ def main():
         "hbm_copy_GBs": round(copy_gbs, 1),
         "memory_bytes": mem,
         "variants": variants,
+        "pieces": pieces,
     }
     print(json.dumps(line), flush=True)
 
