@@ -19,7 +19,8 @@ every launch), against the MI355X fp32-MFMA or HBM peak.  `cpu_baseline`
 times the fp64 CPU oracle on the host.  `variants` times the other storage
 type and mask at the same shape; `pieces` times the causal step streamed as
 equal pieces through the carried-state calls (la_forward_segment /
-la_backward_segment).
+la_backward_segment); `decode` times one recurrent decode step
+(la_decode_step) per head at the bench's B x H heads and at B = 64.
 """
 from __future__ import annotations
 
@@ -258,6 +259,52 @@ def time_pieces(la, make_inputs, dev, B, H, N, D, dtype, pieces, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
+def time_decode(la, make_inputs, dev, B, H, D, dtype, steps, warmup):
+    """One recurrent decode step (la_decode_step) per head of B x H heads,
+    the state alternating between two records.  Returns (us per step issued
+    from Python, us per step replayed from a captured HIP graph of 100 steps,
+    HBM bytes per step).  The graph removes the host's per-call cost, so its
+    time is the device's.  The algorithmic bytes are the record read and
+    written once per head plus the token's q, k, v in and o out."""
+    import torch
+    q, k, v, _ = make_inputs(B, H, 1, D, dtype=dtype, seed=0, device=dev)
+    q, k, v = (x[:, :, 0].contiguous() for x in (q, k, v))
+    o = torch.empty_like(q)
+    recs = [la.new_record(B, H, D, dev).zero_(), la.new_record(B, H, D, dev)]
+
+    def run(n):
+        for i in range(n):
+            la.decode_step(q, k, v, recs[i % 2], state_out=recs[(i + 1) % 2], n_prev=i,
+                           out=o)
+
+    def timed(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    run(warmup)
+    eager_us = 1e3 * timed(lambda: run(steps), 1) / steps
+    per_graph = 100
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        run(per_graph)                      # warm the side stream
+    torch.cuda.current_stream(dev).wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(per_graph)
+    reps = max(steps // per_graph, 1)
+    graph.replay()
+    graph_us = 1e3 * timed(graph.replay, reps) / (reps * per_graph)
+    nbytes = 2 * B * H * (D * D + 2 * D) * 4 + 4 * B * H * D * q.element_size()
+    return eager_us, graph_us, nbytes
+
+
 def cpu_baseline(q, k, v, g, causal):
     import oracle
     from linear_attention_transformer_amd.inputs import as_f64_numpy
@@ -454,6 +501,22 @@ def main():
         print("bench: causal %s in %d pieces: %.3f ms/step (whole sequence %.3f)"
               % (args.dtype, args.pieces, pms, whole), file=sys.stderr, flush=True)
 
+    # the recurrent decode step at the bench's heads and at a serving batch
+    decode = None
+    if not args.no_variants:
+        decode = {}
+        for db in (B, 64):
+            eus, us, nb = time_decode(la, make_inputs, dev, db, H, D, dt, 2000, args.warmup)
+            decode["B%d H%d" % (db, H)] = {
+                "us_per_step": round(us, 2), "us_per_step_eager": round(eus, 2),
+                "tokens_per_s": round(db / (us * 1e-6), 1),
+                "hbm_bytes_per_step": nb, "achieved_GBs": round(nb / (us * 1e-6) / 1e9, 1),
+                "frac_of_hbm_peak": round(nb / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+            print("bench: decode step B=%d H=%d D=%d %s: %.2f us in a graph (%.0f GB/s), "
+                  "%.2f us issued one by one" % (db, H, D, args.dtype, us,
+                                                 nb / (us * 1e-6) / 1e9, eus),
+                  file=sys.stderr, flush=True)
+
     # the copy reference runs after every timed region: a burst of streaming
     # traffic just before one would lower its clocks
     copy_gbs = copy_reference(dev)
@@ -491,6 +554,7 @@ def main():
         "memory_bytes": mem,
         "variants": variants,
         "pieces": pieces,
+        "decode": decode,
     }
     print(json.dumps(line), flush=True)
 

@@ -211,6 +211,40 @@ int la_backward_segment(const void *Q, const void *K, const void *V,
                         void *stream);
 
 /*
+ * One recurrent decode step (causal inference, one new token per head): the
+ * token-by-token state update of the state-update pseudocode in section 2
+ * of the cloud.baidu.com article, then the new token's normalised output
+ * (sciencestack.ai page, TL;DR):
+ *
+ *     S' = S + k v^T,  z' = z + k,  u' = u + v
+ *     den = n + 1 + q.z',  o = (u' + S'^T q) / den
+ *
+ * with n the number of tokens before this one.  Exactly the causal forward
+ * of a one-token piece (la_forward_segment with N = 1).
+ *   q, k, v   : inputs [B, H, D] of `dtype` (one token per head).
+ *   o         : output [B, H, D] of `dtype`.
+ *   state_in  : record [B, H, D*D + 2*D] fp32 (layout as for the carried-
+ *               state calls above: [S | z | u]) of the tokens before, or
+ *               NULL for none (an empty prefix).
+ *   state_out : output record, state_in plus this token.  It must not
+ *               overlap state_in (LA_ERR_ALIAS): callers alternate two
+ *               buffers.  The carry_out of la_forward_segment (a prefill)
+ *               can serve as the first state_in.
+ *   counts    : NULL, or device int64 [B]: tokens before this one for each
+ *               sequence of the batch (all its heads share it).
+ *   n_prev    : the count for every sequence when counts is NULL
+ *               (0 <= n_prev <= 2^40, LA_ERR_SHAPE otherwise).
+ *   den_out   : NULL, or output [B, H] fp32, the denominators.
+ * Validation and errors as for la_forward; D in {16, 32, 64, 128, 256}.
+ * One kernel launch; no workspace.
+ */
+int la_decode_step(const void *q, const void *k, const void *v, void *o,
+                   int64_t B, int64_t H, int64_t D, int dtype,
+                   const float *state_in, float *state_out,
+                   const int64_t *counts, int64_t n_prev, float *den_out,
+                   void *stream);
+
+/*
  * Kernel-level timing (benchmarks, profilers).  Same arguments and behaviour
  * as la_forward / la_backward, plus:
  *   events     : NULL, or n_events hipEvent_t handles created by the caller

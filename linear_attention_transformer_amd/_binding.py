@@ -63,6 +63,8 @@ def load_library():
     lib.la_backward_segment.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ci,
                                         ci, vp, i64, vp, vp, vp, vp, sz, vp]
     lib.la_backward_segment.restype = ci
+    lib.la_decode_step.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp, vp, vp, i64, vp, vp]
+    lib.la_decode_step.restype = ci
     ev, ip, cpp = ctypes.c_void_p, ctypes.POINTER(ci), ctypes.POINTER(ctypes.c_char_p)
     lib.la_forward_traced.argtypes = lib.la_forward.argtypes + [ev, ci, ip, cpp]
     lib.la_forward_traced.restype = ci
@@ -289,6 +291,34 @@ def backward_segment(q, k, v, do, causal: bool = False, *, carry_in=None, n_carr
     if rc != 0:
         raise LAError(rc, "la_backward_segment")
     return dq, dk, dv, gcarry_out
+
+
+def decode_step(q, k, v, state_in=None, *, state_out=None, counts=None, n_prev: int = 0,
+                out=None, return_den: bool = False):
+    """One causal decode step (la_decode_step): q, k, v are [B, H, D] (one
+    token per head).  state_in: record [B, H, D*D+2D] of the tokens before
+    (None = empty prefix); counts: None or a CUDA int64 [B] tensor of the
+    tokens before, per sequence (else n_prev for all).
+    Returns (o, den or None, state_out)."""
+    if q.dim() != 3:
+        raise ValueError("decode_step takes [B, H, D] tokens, got shape %s" % (tuple(q.shape),))
+    (B, H, _, D), dt = _check(*(t.unsqueeze(2) for t in (q, k, v)))
+    lib = load_library()
+    dev = q.device
+    _check_record(state_in, B, H, D, dev, "state_in")
+    if state_out is None:
+        state_out = new_record(B, H, D, dev)
+    _check_record(state_out, B, H, D, dev, "state_out")
+    if counts is not None and (counts.dtype != torch.int64 or counts.device != dev
+                               or counts.shape != (B,) or not counts.is_contiguous()):
+        raise ValueError("counts must be a contiguous int64 [B] tensor on %s" % dev)
+    o = torch.empty_like(q) if out is None else out
+    den = torch.empty((B, H), dtype=torch.float32, device=dev) if return_den else None
+    rc = lib.la_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, D, dt, _ptr(state_in),
+                            _ptr(state_out), _ptr(counts), int(n_prev), _ptr(den), _stream(dev))
+    if rc != 0:
+        raise LAError(rc, "la_decode_step")
+    return o, den, state_out
 
 
 class LinearAttention(torch.autograd.Function):

@@ -13,6 +13,7 @@
 #include "la_kernels_nc.hpp"
 #include "la_kernels_causal.hpp"
 #include "la_kernels_bf16.hpp"
+#include "la_kernels_decode.hpp"
 
 namespace {
 
@@ -714,9 +715,72 @@ int backward_impl(bool require_kv, const void *Q, const void *K, const void *V,
     return rc;
 }
 
+template <class ST>
+int launch_decode(const void *q, const void *k, const void *v, void *o, int64_t BH, int64_t H,
+                  int64_t D, const float *rin, float *rout, const int64_t *counts, float n_all,
+                  float *den, hipStream_t s)
+{
+    typedef typename ST::T T;
+#define LA_DEC(d)                                                                          \
+    dec::k_decode<ST, d><<<dim3((unsigned)(BH * dec::blocks_per_head<d>())),              \
+                           dim3(dec::kThreads), 0, s>>>(                                   \
+        static_cast<const T *>(q), static_cast<const T *>(k), static_cast<const T *>(v),   \
+        static_cast<T *>(o), den, rin, rout, counts, n_all, (int)H)
+    switch (D) {
+    case 16: LA_DEC(16); break;
+    case 32: LA_DEC(32); break;
+    case 64: LA_DEC(64); break;
+    case 128: LA_DEC(128); break;
+    case 256: LA_DEC(256); break;
+    default: return LA_ERR_UNSUPPORTED;
+    }
+#undef LA_DEC
+    return launched();
+}
+
 }  // namespace
 
 extern "C" {
+
+int la_decode_step(const void *q, const void *k, const void *v, void *o, int64_t B, int64_t H,
+                   int64_t D, int dtype, const float *state_in, float *state_out,
+                   const int64_t *counts, int64_t n_prev, float *den_out, void *stream)
+{
+    if (dtype != LA_FP32 && dtype != LA_BF16)
+        return LA_ERR_DTYPE;
+    int rc = check_sizes(B, H, 1, D, 1);
+    if (rc != LA_OK)
+        return rc;
+    if (n_prev < 0 || n_prev > kMaxCarry)
+        return LA_ERR_SHAPE;
+    if (B * H == 0)
+        return LA_OK;
+    if (!q || !k || !v || !o || !state_out)
+        return LA_ERR_NULL;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) ||
+        misaligned(state_in) || misaligned(state_out) || misaligned(counts) ||
+        misaligned(den_out))
+        return LA_ERR_ALIGN;
+    const size_t tb = (size_t)(B * H * D) * elem_size(dtype);
+    const size_t rb = (size_t)(B * H * (D * D + 2 * D)) * sizeof(float);
+    const Range ins[5] = {{(const char *)q, tb},
+                          {(const char *)k, tb},
+                          {(const char *)v, tb},
+                          {(const char *)state_in, rb},
+                          {(const char *)counts, (size_t)B * sizeof(int64_t)}};
+    const Range outs[3] = {{(const char *)o, tb},
+                           {(const char *)state_out, rb},
+                           {(const char *)den_out, (size_t)(B * H) * sizeof(float)}};
+    if (aliased(outs, 3, ins, 5))
+        return LA_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return dtype == LA_FP32 ? launch_decode<StF32>(q, k, v, o, B * H, H, D, state_in,
+                                                   state_out, counts, (float)n_prev, den_out, s)
+                            : launch_decode<StBF16>(q, k, v, o, B * H, H, D, state_in,
+                                                    state_out, counts, (float)n_prev, den_out,
+                                                    s);
+}
+
 
 const char *la_status_string(int status)
 {

@@ -162,6 +162,32 @@ def test_host_validation_segment_calls():
     assert ga(gin=P(CI + 4), gout=P(CO)) == 7
 
 
+@needs_no_gpu
+def test_host_validation_decode_step():
+    lib = la.load_library()
+    buf = (ctypes.c_char * (1 << 20))()
+    a16 = (ctypes.addressof(buf) + 15) & ~15
+    P = lambda off=0: ctypes.c_void_p(a16 + off)
+    B, H, D = 2, 2, 16
+    tb = B * H * D * 4
+    rb = la.record_size(B, H, D)
+    SI, SO = 4 * tb, 4 * tb + rb + 256
+    d = lib.la_decode_step
+
+    def da(q=P(0), o=P(3 * tb), si=P(SI), so=P(SO), counts=None, n=3, dt=0, D_=D):
+        return d(q, P(tb), P(2 * tb), o, B, H, D_, dt, si, so, counts, n, None, None)
+
+    assert da(dt=5) == 3
+    assert da(D_=48) == 4
+    assert da(n=-1) == 2
+    assert da(q=None) == 1
+    assert da(so=None) == 1
+    assert da(so=P(SI + 64)) == 6          # state_out overlaps state_in
+    assert da(o=P(tb)) == 6                # o overlaps k
+    assert da(so=P(SO + 8)) == 7
+    assert da(counts=P(SO + rb + 260)) == 7
+
+
 def test_python_side_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 4, 16)
     with pytest.raises(ValueError):

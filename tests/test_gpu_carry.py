@@ -203,3 +203,118 @@ def test_large_carried_count_and_state_only_call():
     o_r, den_r, _ = oracle.forward_carry(*a, False, None, n0)
     assert rel_l2(f64(o), o_r) <= 1e-5 and rel_l2(f64(den), den_r) <= 1e-6
     assert torch.equal(cout, cout2)
+
+
+# ------------------------------------------------------------ decode step
+@pytest.mark.parametrize("D", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_decode_step_parity(D, dtype):
+    """One decode step for B=3 sequences of different lengths (per-sequence
+    counts on the device) against the oracle's one-token causal piece."""
+    m = la()
+    B, H = 3, 2
+    lens = [0, 37, 190]
+    say("case decode B=%d H=%d D=%d %s prefixes=%s" % (B, H, D, dtype, lens))
+    q, k, v, _ = make_inputs(B, H, 1, D, dtype=dtype, seed=D + 3, device=DEV)
+    recs = []
+    for b, n in enumerate(lens):
+        qa, ka, va, _ = make_inputs(1, H, max(n, 1), D, dtype=dtype, seed=100 + b)
+        a = [as_f64_numpy(x)[:, :, :n] for x in (qa, ka, va)]
+        recs.append(oracle.forward_carry(*a, True)[2])
+    rin = torch.from_numpy(np.concatenate(recs, axis=0)).float().to(DEV)
+    counts = torch.tensor(lens, dtype=torch.int64, device=DEV)
+    o, den, rout = m.decode_step(q[:, :, 0].contiguous(), k[:, :, 0].contiguous(),
+                                 v[:, :, 0].contiguous(), rin, counts=counts, return_den=True)
+    torch.cuda.synchronize()
+    a = [as_f64_numpy(x) for x in (q, k, v)]
+    r64 = f64(rin)
+    errs = {"O": 0.0, "den": 0.0, "state_out": 0.0}
+    for b, n in enumerate(lens):
+        sb = slice(b, b + 1)
+        o_r, den_r, rec_r = oracle.forward_carry(a[0][sb], a[1][sb], a[2][sb], True, r64[sb], n)
+        errs["O"] = max(errs["O"], rel_l2(f64(o[sb]).reshape(o_r.shape), o_r))
+        errs["den"] = max(errs["den"], rel_l2(f64(den[sb]).reshape(den_r.shape), den_r))
+        errs["state_out"] = max(errs["state_out"], rel_l2(f64(rout[sb]), rec_r))
+    say("  rel-L2 " + " ".join("%s=%.2e" % kv for kv in errs.items()))
+    for name, e in errs.items():
+        assert e <= TOL[dtype], (name, e)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("prefill", [0, 300])
+def test_decode_chain_equals_causal_forward(dtype, prefill):
+    """A prefill through la_forward_segment (or none), then 40 decode steps
+    alternating two state buffers, gives the rows of one causal la_forward
+    over the whole sequence (B=2 H=8 D=128)."""
+    m = la()
+    B, H, D, T = 2, 8, 128, 40
+    N = prefill + T
+    say("case decode chain B=%d H=%d D=%d %s prefill=%d steps=%d" % (B, H, D, dtype, prefill, T))
+    q, k, v, _ = make_inputs(B, H, N, D, dtype=dtype, seed=21, device=DEV)
+    o_w, den_w, _ = m.forward(q, k, v, True, return_den=True)
+    bufs = [m.new_record(B, H, D, DEV), m.new_record(B, H, D, DEV)]
+    state = None
+    if prefill:
+        P = lambda x: x[:, :, :prefill].contiguous()  # noqa: E731
+        m.forward_segment(P(q), P(k), P(v), True, carry_out=bufs[0], compute_out=False)
+        state = bufs[0]
+    outs, dens = [], []
+    for t in range(T):
+        i = prefill + t
+        tok = lambda x: x[:, :, i].contiguous()  # noqa: E731
+        nxt = bufs[(t + 1) % 2] if prefill else bufs[t % 2]
+        o, den, state = m.decode_step(tok(q), tok(k), tok(v), state, state_out=nxt,
+                                      n_prev=i, return_den=True)
+        outs.append(o)
+        dens.append(den)
+    torch.cuda.synchronize()
+    got_o = torch.stack(outs, dim=2)
+    got_d = torch.stack(dens, dim=2)
+    eo = rel_l2(f64(got_o), f64(o_w[:, :, prefill:]))
+    ed = rel_l2(f64(got_d), f64(den_w[:, :, prefill:]))
+    say("  rel-L2 vs whole O=%.2e den=%.2e" % (eo, ed))
+    assert eo <= TOL[dtype] and ed <= 1e-5
+
+
+def test_decode_steps_replayed_from_a_graph():
+    """Six decode steps captured in a HIP graph (the call allocates nothing
+    and issues no memset) replay to the eager results, three times, with
+    eager work and synchronisation between the replays."""
+    m = la()
+    B, H, D, T = 2, 4, 64, 6
+    say("case decode graph B=%d H=%d D=%d steps=%d" % (B, H, D, T))
+    q, k, v, _ = make_inputs(B, H, T, D, dtype=torch.float32, seed=4, device=DEV)
+    toks = [[x[:, :, t].contiguous() for x in (q, k, v)] for t in range(T)]
+    start = torch.randn(B, H, D * D + 2 * D, device=DEV).abs_() * 0.01
+    recs = [m.new_record(B, H, D, DEV), m.new_record(B, H, D, DEV)]
+    outs = [torch.empty(B, H, D, device=DEV) for _ in range(T)]
+
+    def run():
+        for t in range(T):
+            m.decode_step(*toks[t], recs[t % 2], state_out=recs[(t + 1) % 2], n_prev=50 + t,
+                          out=outs[t])
+
+    recs[0].copy_(start)
+    run()
+    torch.cuda.synchronize()
+    ref_o = [x.clone() for x in outs]
+    ref_s = recs[T % 2].clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        recs[0].copy_(start)
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(3):
+        for x in outs:
+            x.zero_()
+        recs[0].copy_(start)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t in range(T):
+            assert torch.equal(outs[t], ref_o[t]), (rep, t)
+        assert torch.equal(recs[T % 2], ref_s), rep

@@ -143,3 +143,19 @@ def test_carry_edge_cases(oracle_mod, causal):
     assert np.array_equal(rec2, rec)
     *_, grec2 = oracle_mod.backward_carry(e, e, e, e, causal, rec, 21, grec)
     assert np.array_equal(grec2, grec)
+
+
+def test_token_by_token_matches_whole_sequence(oracle_mod):
+    """The recurrent decode reading: one-token causal pieces, each starting
+    from the record the previous token left, give the causal rows of the
+    pairwise definition.  Catches a decode step that counts the new token
+    twice or not at all, or applies the state before adding the token."""
+    q, k, v, _ = _inputs(B=1, H=2, D=4)
+    o_ref, den_ref = oracle_mod.forward_direct(q, k, v, True)
+    rec = None
+    for i in range(q.shape[2]):
+        c = slice(i, i + 1)
+        o, den, rec = oracle_mod.forward_carry(q[:, :, c], k[:, :, c], v[:, :, c], True,
+                                               rec, i)
+        assert _rel(o, o_ref[:, :, c]) < 1e-12
+        assert _rel(den, den_ref[:, :, c]) < 1e-12
