@@ -41,8 +41,8 @@ PEAK_BF16_MFMA_TFLOPS = 2516.6  # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 KERNEL_SOURCES = [os.path.join(ROOT, "linear_attention_transformer_amd", "csrc", f)
                   for f in ("la_kernels.hpp", "la_kernels_nc.hpp", "la_kernels_causal.hpp",
-                            "la_kernels_bf16.hpp",
-                            "la_api.hip")]
+                            "la_kernels_bf16.hpp", "la_kernels_decode.hpp",
+                            "la_kernels_stage.hpp", "la_api.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_MIB = 256                  # plain streaming kernel: reads and writes this much
 
@@ -55,6 +55,8 @@ KERNEL_NAMES = [
     (r"k_bwd_q_nc<|k_apply_bf<\d+, 1>|k_bwd_q_causal|k_bwd_q<", "bwd_q"),
     (r"k_apply_nc<[^>]*, 2>|k_apply_bf<\d+, 2>|k_bwd_kv_causal|k_bwd_kv<", "bwd_kv"),
     (r"k_state_scan", "state_scan"),
+    (r"k_stage", "stage"),
+    (r"k_decode", "decode"),
 ]
 
 
@@ -195,7 +197,7 @@ def time_variant(la, make_inputs, dev, B, H, N, D, dtype, causal, steps, warmup)
     import torch
     q, k, v, g = make_inputs(B, H, N, D, dtype=dtype, seed=0, device=dev, draw_device=dev)
     o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
-    ws = la.alloc_workspace(B, H, N, D, causal, dev)
+    ws = la.alloc_workspace(B, H, N, D, causal, dev, dtype)
     st = torch.empty(max(la.state_size(B, H, N, D, causal) // 4, 4), dtype=torch.float32,
                      device=dev)
 
@@ -230,7 +232,7 @@ def time_pieces(la, make_inputs, dev, B, H, N, D, dtype, pieces, steps, warmup):
     outs = [[torch.empty_like(p[0]) for _ in range(4)] for p in parts]
     recs = [la.new_record(B, H, D, dev) for _ in range(pieces)]
     grecs = [la.new_record(B, H, D, dev) for _ in range(pieces)]
-    ws = max((la.alloc_workspace(B, H, c.stop - c.start, D, True, dev) for c in sl),
+    ws = max((la.alloc_workspace(B, H, c.stop - c.start, D, True, dev, dtype) for c in sl),
              key=lambda t: t.numel())
     sts = [torch.empty(max(la.state_size(B, H, c.stop - c.start, D, True) // 4, 4),
                        dtype=torch.float32, device=dev) for c in sl]
@@ -341,8 +343,9 @@ def main():
     # (measured: ~0.8 ms/step over the first 20 fp32 steps, ~0.50 ms/step
     # from about step 60 on), so the untimed warm-up is long by default
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--dtype", choices=("fp32", "bf16"), default="fp32",
-                    help="storage dtype of Q, K, V, O and gradients (arithmetic is fp32)")
+    ap.add_argument("--dtype", choices=("fp32", "bf16", "fp16"), default="fp32",
+                    help="storage dtype of Q, K, V, O and gradients (arithmetic is fp32; "
+                         "fp16 storage is staged through fp32 buffers)")
     ap.add_argument("--causal", type=int, choices=(0, 1), default=0)
     ap.add_argument("--B", type=int, default=4)
     ap.add_argument("--H", type=int, default=16)
@@ -382,13 +385,13 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     B, H, N, D, causal = args.B, args.H, args.N, args.D, bool(args.causal)
-    dt = torch.float32 if args.dtype == "fp32" else torch.bfloat16
+    dt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[args.dtype]
     s = 4 if args.dtype == "fp32" else 2
     print("bench: B=%d H=%d N=%d D=%d %s causal=%d steps=%d warmup=%d"
           % (B, H, N, D, args.dtype, causal, args.steps, args.warmup), file=sys.stderr, flush=True)
     q, k, v, g = make_inputs(B, H, N, D, dtype=dt, seed=0, device=dev, draw_device=dev)
     o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
-    ws = la.alloc_workspace(B, H, N, D, causal, dev)
+    ws = la.alloc_workspace(B, H, N, D, causal, dev, dt)
     st = torch.empty(max(la.state_size(B, H, N, D, causal) // 4, 4), dtype=torch.float32,
                      device=dev)
 

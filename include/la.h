@@ -25,8 +25,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Tensors Q, K, V, O, dO, dQ, dK, dV are DEVICE pointers with layout
- *    [B, H, N, D], contiguous, element type `dtype` (fp32 or bf16).  All
- *    arithmetic is fp32; bf16 outputs are rounded to nearest even.
+ *    [B, H, N, D], contiguous, element type `dtype` (fp32, bf16 or fp16).
+ *    All arithmetic is fp32; bf16 and fp16 outputs are rounded to nearest
+ *    even.
  *  - The caller owns (allocates and frees) every buffer, including the
  *    workspace and the saved state.  The library never allocates memory.
  *  - Outputs are overwritten, never accumulated into.
@@ -34,7 +35,16 @@
  *  - Outputs must not overlap any input or each other (LA_ERR_ALIAS).
  *  - B, H, N >= 0, B*H <= 2^22, N <= 2^24 (LA_ERR_SHAPE otherwise).
  *    B*H*N == 0 is a no-op returning LA_OK.
- *    D must be one of 16, 32, 64, 128, 256 (LA_ERR_UNSUPPORTED otherwise).
+ *    1 <= D <= 256 (LA_ERR_UNSUPPORTED otherwise).  D = 32, 64, 128, 256
+ *    run as they are.  Other head sizes (the Figure 1 caption of the
+ *    sciencestack.ai page draws D = 6) are padded through the workspace
+ *    with zero columns to the next of those sizes, which is exact (the zero
+ *    columns add nothing to q.k and give zero output columns), and the
+ *    results are unpadded.  This costs extra passes over the data and room
+ *    for seven padded tensors (see la_workspace_size_for).
+ *  - fp16 storage runs on the fp32 matrix-core kernels (widened exactly on
+ *    load); bf16 storage runs on the bf16 matrix cores for D = 32..128 (with
+ *    fp32 factors split into two bf16 terms) and on the fp32 ones at 256.
  *  - All arguments are validated on the host before anything is enqueued;
  *    on any error nothing is launched.
  *  - Kernels are enqueued on `stream` (a hipStream_t; NULL = default
@@ -62,27 +72,34 @@ typedef enum {
     LA_OK = 0,
     LA_ERR_NULL = 1,        /* a required pointer is NULL */
     LA_ERR_SHAPE = 2,       /* negative size, or sizes overflow int64 */
-    LA_ERR_DTYPE = 3,       /* dtype is not LA_FP32 / LA_BF16 */
-    LA_ERR_UNSUPPORTED = 4, /* D not in {16,32,64,128,256}, or causal not 0/1 */
+    LA_ERR_DTYPE = 3,       /* dtype is not LA_FP32 / LA_BF16 / LA_FP16 */
+    LA_ERR_UNSUPPORTED = 4, /* D not in 1..256, or causal not 0/1 */
     LA_ERR_WORKSPACE = 5,   /* workspace smaller than la_workspace_size() */
     LA_ERR_ALIAS = 6,       /* an output overlaps an input or another output */
     LA_ERR_ALIGN = 7,       /* a device pointer is not 16-byte aligned */
     LA_ERR_HIP = 8          /* a HIP launch failed */
 } la_status;
 
-typedef enum { LA_FP32 = 0, LA_BF16 = 1 } la_dtype;
+typedef enum { LA_FP32 = 0, LA_BF16 = 1, LA_FP16 = 2 } la_dtype;
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *la_status_string(int status);
 
-/* Bytes of device workspace that la_forward and la_backward need for this
- * problem (the same bound covers both passes).  0 when B*H*N == 0. */
+/* Bytes of device workspace that la_forward and la_backward (and their
+ * segment forms) need for this problem with storage `dtype` (the same bound
+ * covers both passes).  0 when B*H*N == 0 or the arguments are invalid. */
+size_t la_workspace_size_for(int64_t B, int64_t H, int64_t N, int64_t D,
+                             int causal, int dtype);
+
+/* la_workspace_size_for with fp32 storage: enough for every storage type
+ * (padded tensors are largest in fp32). */
 size_t la_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D,
                          int causal);
 
 /* Bytes of the state the forward pass can save for the backward pass:
  * the reduced key-value state (S, z, u) of every head, and in the causal
- * case one exclusive prefix of it per sequence segment.  fp32. */
+ * case one exclusive prefix of it per sequence segment.  fp32, at the
+ * padded head size for padded calls; its layout is internal. */
 size_t la_state_size(int64_t B, int64_t H, int64_t N, int64_t D, int causal);
 
 /* Number of sequence segments each head is split into (diagnostic). */
@@ -235,8 +252,8 @@ int la_backward_segment(const void *Q, const void *K, const void *V,
  *   n_prev    : the count for every sequence when counts is NULL
  *               (0 <= n_prev <= 2^40, LA_ERR_SHAPE otherwise).
  *   den_out   : NULL, or output [B, H] fp32, the denominators.
- * Validation and errors as for la_forward; D in {16, 32, 64, 128, 256}.
- * One kernel launch; no workspace.
+ * Validation and errors as for la_forward; every 1 <= D <= 256 runs as it
+ * is here (no padding).  One kernel launch; no workspace.
  */
 int la_decode_step(const void *q, const void *k, const void *v, void *o,
                    int64_t B, int64_t H, int64_t D, int dtype,

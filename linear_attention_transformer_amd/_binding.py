@@ -15,11 +15,12 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "liblinattn.so")
 
-LA_FP32, LA_BF16 = 0, 1
+LA_FP32, LA_BF16, LA_FP16 = 0, 1, 2
 STATUS = {0: "LA_OK", 1: "LA_ERR_NULL", 2: "LA_ERR_SHAPE", 3: "LA_ERR_DTYPE",
           4: "LA_ERR_UNSUPPORTED", 5: "LA_ERR_WORKSPACE", 6: "LA_ERR_ALIAS",
           7: "LA_ERR_ALIGN", 8: "LA_ERR_HIP"}
-SUPPORTED_D = (16, 32, 64, 128, 256)
+SUPPORTED_D = tuple(range(1, 257))      # every head size the library takes
+NATIVE_D = (32, 64, 128, 256)            # run without padding
 
 _lib = None
 
@@ -45,6 +46,8 @@ def load_library():
     lib.la_status_string.restype = ctypes.c_char_p
     lib.la_workspace_size.argtypes = [i64, i64, i64, i64, ci]
     lib.la_workspace_size.restype = sz
+    lib.la_workspace_size_for.argtypes = [i64, i64, i64, i64, ci, ci]
+    lib.la_workspace_size_for.restype = sz
     lib.la_state_size.argtypes = [i64, i64, i64, i64, ci]
     lib.la_state_size.restype = sz
     lib.la_num_segments.argtypes = [i64, i64, i64, i64, ci]
@@ -78,8 +81,12 @@ def status_string(code: int) -> str:
     return load_library().la_status_string(int(code)).decode()
 
 
-def workspace_size(B, H, N, D, causal=False) -> int:
-    return int(load_library().la_workspace_size(B, H, N, D, int(bool(causal))))
+def workspace_size(B, H, N, D, causal=False, dtype=None) -> int:
+    """Workspace bytes; `dtype` (a torch dtype) matters for fp16 storage."""
+    if dtype is None:
+        return int(load_library().la_workspace_size(B, H, N, D, int(bool(causal))))
+    return int(load_library().la_workspace_size_for(B, H, N, D, int(bool(causal)),
+                                                    _dtype_of(dtype)))
 
 
 def state_size(B, H, N, D, causal=False) -> int:
@@ -94,13 +101,19 @@ def record_size(B, H, D) -> int:
     return int(load_library().la_record_size(B, H, D))
 
 
-def _dtype_code(t: torch.Tensor) -> int:
-    if t.dtype == torch.float32:
+def _dtype_of(dt) -> int:
+    if dt == torch.float32:
         return LA_FP32
-    if t.dtype == torch.bfloat16:
+    if dt == torch.bfloat16:
         return LA_BF16
-    raise TypeError("linear attention supports float32 and bfloat16 storage, got %s"
-                    % t.dtype)
+    if dt == torch.float16:
+        return LA_FP16
+    raise TypeError("linear attention supports float32, bfloat16 and float16 storage, got %s"
+                    % dt)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    return _dtype_of(t.dtype)
 
 
 def _check(*ts: torch.Tensor):
@@ -154,8 +167,9 @@ class KernelTrace:
                 for i in range(min(self._n.value, self.max_launches))]
 
 
-def alloc_workspace(B, H, N, D, causal, device) -> torch.Tensor:
-    return torch.empty(max(workspace_size(B, H, N, D, causal), 16), dtype=torch.uint8,
+def alloc_workspace(B, H, N, D, causal, device, dtype=torch.float32) -> torch.Tensor:
+    """Workspace for calls with storage `dtype` (fp32 covers bf16 as well)."""
+    return torch.empty(max(workspace_size(B, H, N, D, causal, dtype), 16), dtype=torch.uint8,
                        device=device)
 
 
@@ -175,7 +189,7 @@ def forward(q, k, v, causal: bool = False, *, return_den: bool = False,
     if state is None and save_state:
         state = torch.empty(max(state_size(B, H, N, D, causal) // 4, 4),
                             dtype=torch.float32, device=q.device)
-    ws = alloc_workspace(B, H, N, D, causal, q.device) if workspace is None else workspace
+    ws = alloc_workspace(B, H, N, D, causal, q.device, q.dtype) if workspace is None else workspace
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, D, c, dt, _ptr(den), _ptr(state),
             _ptr(ws), ws.numel(), _stream(q.device))
     if trace is None:
@@ -197,7 +211,7 @@ def backward(q, k, v, do, causal: bool = False, *, state=None, outs=None,
         dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     else:
         dq, dk, dv = outs
-    ws = alloc_workspace(B, H, N, D, causal, q.device) if workspace is None else workspace
+    ws = alloc_workspace(B, H, N, D, causal, q.device, q.dtype) if workspace is None else workspace
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, D,
             c, dt, _ptr(state), _ptr(ws), ws.numel(), _stream(q.device))
     if trace is None:
@@ -248,7 +262,7 @@ def forward_segment(q, k, v, causal: bool = False, *, carry_in=None, n_carry: in
     if state is None and save_state:
         state = torch.empty(max(state_size(B, H, N, D, causal) // 4, 4),
                             dtype=torch.float32, device=dev)
-    ws = alloc_workspace(B, H, N, D, causal, dev) if workspace is None else workspace
+    ws = alloc_workspace(B, H, N, D, causal, dev, q.dtype) if workspace is None else workspace
     rc = lib.la_forward_segment(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, D,
                                 int(bool(causal)), dt, _ptr(carry_in), int(n_carry),
                                 _ptr(carry_out), _ptr(den), _ptr(state), _ptr(ws), ws.numel(),
@@ -283,7 +297,7 @@ def backward_segment(q, k, v, do, causal: bool = False, *, carry_in=None, n_carr
         dk, dv = (torch.empty_like(q), torch.empty_like(q)) if compute_kv else (None, None)
     else:
         dq, dk, dv = outs
-    ws = alloc_workspace(B, H, N, D, causal, dev) if workspace is None else workspace
+    ws = alloc_workspace(B, H, N, D, causal, dev, q.dtype) if workspace is None else workspace
     rc = lib.la_backward_segment(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(dk),
                                  _ptr(dv), B, H, N, D, int(bool(causal)), dt, _ptr(carry_in),
                                  int(n_carry), _ptr(gcarry_in), _ptr(gcarry_out), _ptr(state),

@@ -14,6 +14,7 @@
 #include "la_kernels_causal.hpp"
 #include "la_kernels_bf16.hpp"
 #include "la_kernels_decode.hpp"
+#include "la_kernels_stage.hpp"
 
 namespace {
 
@@ -31,9 +32,10 @@ struct Plan {
     float n0;  // tokens carried in from outside the call, added to every row's count
 };
 
+// head sizes the kernels take as they are (others are padded to the next)
 bool supported_d(int64_t D)
 {
-    return D == 16 || D == 32 || D == 64 || D == 128 || D == 256;
+    return D == 32 || D == 64 || D == 128 || D == 256;
 }
 
 Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int causal)
@@ -126,17 +128,28 @@ Layout make_layout(const Plan &p)
 
 int64_t state_floats(const Plan &p) { return p.BH * (p.causal ? p.nseg : 1) * p.PS; }
 
+// the head size the kernels run: D itself, or the next native size above it
+// (the extra columns zero)
+int64_t padded_d(int64_t D)
+{
+    for (int64_t d : {32, 64, 128, 256})
+        if (D <= d)
+            return d;
+    return 0;
+}
+
 int check_sizes(int64_t B, int64_t H, int64_t N, int64_t D, int causal)
 {
     if (causal != 0 && causal != 1)
         return LA_ERR_UNSUPPORTED;
     if (B < 0 || H < 0 || N < 0)
         return LA_ERR_SHAPE;
-    if (!supported_d(D))
+    if (D < 1 || D > 256)
         return LA_ERR_UNSUPPORTED;
     int64_t t;
     if (__builtin_mul_overflow(B, H, &t) || __builtin_mul_overflow(t, N, &t) ||
-        __builtin_mul_overflow(t, D, &t) || __builtin_mul_overflow(t, (int64_t)16, &t))
+        __builtin_mul_overflow(t, padded_d(D), &t) ||
+        __builtin_mul_overflow(t, (int64_t)16, &t))
         return LA_ERR_SHAPE;
     // keeps every grid below 2^31 workgroups and row counts exact in fp32
     if (B * H > (int64_t)1 << 22 || N > (int64_t)1 << 24)
@@ -223,14 +236,14 @@ constexpr bool nc_path()
     return D >= 32 && D <= 128;
 }
 
-// fp32 storage at D = 256: the fast reduction (four 128 x 128 blocks per
+// fp32 or fp16 storage at D = 256: the fast reduction (four 128 x 128 blocks per
 // segment) for both masks, the fast non-causal apply kernels (eight waves)
 // and a dQ pass without the dS role (the gradient record then comes from
 // the reduction)
 template <class ST, int D>
 constexpr bool wide_path()
 {
-    return std::is_same<ST, StF32>::value && D == 256;
+    return !std::is_same<ST, StBF16>::value && D == 256;
 }
 
 template <class ST, int D>
@@ -545,7 +558,6 @@ int dispatch_forward(const void *Q, const void *K, const void *V, void *O, float
                      const float *cin, float *cout)
 {
     switch (p.D) {
-    case 16: return run_forward<ST, 16>(Q, K, V, O, den, st, ws, p, s, t, cin, cout);
     case 32: return run_forward<ST, 32>(Q, K, V, O, den, st, ws, p, s, t, cin, cout);
     case 64: return run_forward<ST, 64>(Q, K, V, O, den, st, ws, p, s, t, cin, cout);
     case 128: return run_forward<ST, 128>(Q, K, V, O, den, st, ws, p, s, t, cin, cout);
@@ -563,7 +575,6 @@ int dispatch_backward(const void *Q, const void *K, const void *V, const void *G
 #define LA_BWD(d)                                                                          \
     run_backward<ST, d>(Q, K, V, G, dQ, dK, dV, st, ws, p, s, t, cin, gin, gout)
     switch (p.D) {
-    case 16: return LA_BWD(16);
     case 32: return LA_BWD(32);
     case 64: return LA_BWD(64);
     case 128: return LA_BWD(128);
@@ -573,7 +584,12 @@ int dispatch_backward(const void *Q, const void *K, const void *V, const void *G
 #undef LA_BWD
 }
 
-size_t elem_size(int dtype) { return dtype == LA_BF16 ? 2 : 4; }
+size_t elem_size(int dtype) { return dtype == LA_FP32 ? 4 : 2; }
+
+bool valid_dtype(int dtype) { return dtype == LA_FP32 || dtype == LA_BF16 || dtype == LA_FP16; }
+
+// calls the matrix-core kernels take as they are; the others are padded
+bool native(int64_t D) { return supported_d(D); }
 
 // tokens a carried-in record may stand for (counts enter the kernels as fp32)
 constexpr int64_t kMaxCarry = (int64_t)1 << 40;
@@ -585,11 +601,6 @@ int pass_record(const float *in, float *out, int64_t BH, int64_t D, hipStream_t 
 {
     if (out == nullptr)
         return LA_OK;
-    const size_t rb = (size_t)(BH * (D * D + 2 * D)) * sizeof(float);
-    if (misaligned(out) || misaligned(in))
-        return LA_ERR_ALIGN;
-    if (overlap({(const char *)out, rb}, {(const char *)in, rb}))
-        return LA_ERR_ALIAS;
     Plan p{};
     p.BH = BH;
     p.D = D;
@@ -598,29 +609,36 @@ int pass_record(const float *in, float *out, int64_t BH, int64_t D, hipStream_t 
     return scan(out, out, p, 0, s, nullptr, in, nullptr);
 }
 
+size_t record_bytes(int64_t BH, int64_t D) { return (size_t)(BH * (D * D + 2 * D)) * sizeof(float); }
+
+// Native forward (supported D, fp32 or bf16).  Arguments are validated here.
 int forward_impl(bool require_o, const void *Q, const void *K, const void *V, void *O,
                  int64_t B, int64_t H, int64_t N, int64_t D, int causal, int dtype,
                  const float *cin, int64_t n_carry, float *cout, float *den_out,
-                 void *state_out, void *ws, size_t ws_bytes, void *stream,
-                 void *const *events, int n_events, int *n_launched, const char **names)
+                 void *state_out, void *ws, size_t ws_bytes, hipStream_t s, Tracer *t)
 {
-    if (n_launched)
-        *n_launched = 0;
-    if (dtype != LA_FP32 && dtype != LA_BF16)
+    if (!valid_dtype(dtype))
         return LA_ERR_DTYPE;
     int rc = check_sizes(B, H, N, D, causal);
     if (rc != LA_OK)
         return rc;
+    if (!supported_d(D))
+        return LA_ERR_UNSUPPORTED;
     if (n_carry < 0 || n_carry > kMaxCarry)
         return LA_ERR_SHAPE;
     if (B * H == 0)
         return LA_OK;
-    if (N == 0)
-        return pass_record(cin, cout, B * H, D, static_cast<hipStream_t>(stream));
+    const size_t rb = record_bytes(B * H, D);
+    if (N == 0) {
+        if (misaligned(cout) || misaligned(cin))
+            return LA_ERR_ALIGN;
+        if (overlap({(const char *)cout, rb}, {(const char *)cin, rb}))
+            return LA_ERR_ALIAS;
+        return pass_record(cin, cout, B * H, D, s);
+    }
     // O == null asks for the state only: something must receive it
     if (!Q || !K || !V || !ws || (!O && (require_o || den_out || (!cout && !state_out))))
         return LA_ERR_NULL;
-    const size_t rb = (size_t)(B * H * (D * D + 2 * D)) * sizeof(float);
     Plan p = make_plan(B, H, N, D, causal);
     p.n0 = (float)n_carry;
     const size_t need = (size_t)make_layout(p).total * sizeof(float);
@@ -643,42 +661,47 @@ int forward_impl(bool require_o, const void *Q, const void *K, const void *V, vo
         {(const char *)cout, rb}};
     if (aliased(outs, 5, ins, 4))
         return LA_ERR_ALIAS;
-    hipStream_t s = static_cast<hipStream_t>(stream);
     float *w = static_cast<float *>(ws);
-    Tracer t{events, events ? n_events : 0, 0, names};
-    rc = (dtype == LA_FP32)
-             ? dispatch_forward<StF32>(Q, K, V, O, den_out, state_out, w, p, s, &t, cin, cout)
-             : dispatch_forward<StBF16>(Q, K, V, O, den_out, state_out, w, p, s, &t, cin, cout);
-    if (n_launched)
-        *n_launched = t.n;
-    return rc;
+    switch (dtype) {
+    case LA_FP32:
+        return dispatch_forward<StF32>(Q, K, V, O, den_out, state_out, w, p, s, t, cin, cout);
+    case LA_BF16:
+        return dispatch_forward<StBF16>(Q, K, V, O, den_out, state_out, w, p, s, t, cin, cout);
+    default:
+        return dispatch_forward<StF16>(Q, K, V, O, den_out, state_out, w, p, s, t, cin, cout);
+    }
 }
 
+// Native backward (supported D, fp32 or bf16).  Arguments are validated here.
 int backward_impl(bool require_kv, const void *Q, const void *K, const void *V,
                   const void *dO, void *dQ, void *dK, void *dV, int64_t B, int64_t H,
                   int64_t N, int64_t D, int causal, int dtype, const float *cin,
                   int64_t n_carry, const float *gin, float *gout, const void *state_in,
-                  void *ws, size_t ws_bytes, void *stream, void *const *events, int n_events,
-                  int *n_launched, const char **names)
+                  void *ws, size_t ws_bytes, hipStream_t s, Tracer *t)
 {
-    if (n_launched)
-        *n_launched = 0;
-    if (dtype != LA_FP32 && dtype != LA_BF16)
+    if (!valid_dtype(dtype))
         return LA_ERR_DTYPE;
     int rc = check_sizes(B, H, N, D, causal);
     if (rc != LA_OK)
         return rc;
+    if (!supported_d(D))
+        return LA_ERR_UNSUPPORTED;
     if (n_carry < 0 || n_carry > kMaxCarry)
         return LA_ERR_SHAPE;
     if (B * H == 0)
         return LA_OK;
-    if (N == 0)
-        return pass_record(gin, gout, B * H, D, static_cast<hipStream_t>(stream));
+    const size_t rb = record_bytes(B * H, D);
+    if (N == 0) {
+        if (misaligned(gout) || misaligned(gin))
+            return LA_ERR_ALIGN;
+        if (overlap({(const char *)gout, rb}, {(const char *)gin, rb}))
+            return LA_ERR_ALIAS;
+        return pass_record(gin, gout, B * H, D, s);
+    }
     // dK and dV: both given, or (segment calls only) both null
     if (!Q || !K || !V || !dO || !dQ || !ws || (dK == nullptr) != (dV == nullptr) ||
         (require_kv && dK == nullptr))
         return LA_ERR_NULL;
-    const size_t rb = (size_t)(B * H * (D * D + 2 * D)) * sizeof(float);
     Plan p = make_plan(B, H, N, D, causal);
     p.n0 = (float)n_carry;
     const size_t need = (size_t)make_layout(p).total * sizeof(float);
@@ -703,16 +726,261 @@ int backward_impl(bool require_kv, const void *Q, const void *K, const void *V,
                            {(const char *)gout, rb}};
     if (aliased(outs, 5, ins, 7))
         return LA_ERR_ALIAS;
-    hipStream_t s = static_cast<hipStream_t>(stream);
     float *w = static_cast<float *>(ws);
-    Tracer t{events, events ? n_events : 0, 0, names};
-    rc = (dtype == LA_FP32) ? dispatch_backward<StF32>(Q, K, V, dO, dQ, dK, dV, state_in, w, p,
-                                                       s, &t, cin, gin, gout)
-                            : dispatch_backward<StBF16>(Q, K, V, dO, dQ, dK, dV, state_in, w,
-                                                        p, s, &t, cin, gin, gout);
-    if (n_launched)
-        *n_launched = t.n;
-    return rc;
+    switch (dtype) {
+    case LA_FP32:
+        return dispatch_backward<StF32>(Q, K, V, dO, dQ, dK, dV, state_in, w, p, s, t, cin, gin,
+                                        gout);
+    case LA_BF16:
+        return dispatch_backward<StBF16>(Q, K, V, dO, dQ, dK, dV, state_in, w, p, s, t, cin,
+                                         gin, gout);
+    default:
+        return dispatch_backward<StF16>(Q, K, V, dO, dQ, dK, dV, state_in, w, p, s, t, cin, gin,
+                                        gout);
+    }
+}
+
+// ------------------------------------------------------------ staging
+// Workspace of a padded call, in bytes: the native call's workspace at Dp,
+// then seven padded [B,H,N,Dp] tensors, then three padded records, each
+// region 256-byte aligned.
+struct Staging {
+    int64_t Dp;
+    size_t inner, tensor, record;
+    size_t off_inner, off_tensor[7], off_record[3], total;
+};
+
+size_t up256(size_t x) { return (x + 255) / 256 * 256; }
+
+Staging make_staging(int64_t B, int64_t H, int64_t N, int64_t D, int causal, int dtype)
+{
+    Staging g{};
+    g.Dp = padded_d(D);
+    g.inner = N > 0 ? (size_t)make_layout(make_plan(B, H, N, g.Dp, causal)).total * sizeof(float)
+                    : 0;
+    g.tensor = up256((size_t)(B * H * N * g.Dp) * elem_size(dtype));
+    g.record = up256(record_bytes(B * H, g.Dp));
+    size_t off = 0;
+    g.off_inner = off;
+    off += up256(g.inner);
+    for (int i = 0; i < 7; ++i) {
+        g.off_tensor[i] = off;
+        off += g.tensor;
+    }
+    for (int i = 0; i < 3; ++i) {
+        g.off_record[i] = off;
+        off += g.record;
+    }
+    g.total = off;
+    return g;
+}
+
+int grid_for(int64_t n)
+{
+    return (int)std::max<int64_t>(1, std::min<int64_t>((n + stg::kThreads - 1) / stg::kThreads,
+                                                       (int64_t)1 << 16));
+}
+
+// [rows, D] <-> [rows, Dp] in storage `dtype` (pad: to_padded, else unpad)
+int stage_tensor(const char *name, bool to_padded, const void *src, void *dst, int dtype,
+                 int64_t D, int64_t Dp, int64_t rows, hipStream_t s, Tracer *t)
+{
+    const int64_t chunks = rows * (Dp * (int64_t)elem_size(dtype) / 16);
+    const dim3 grid(grid_for(chunks)), blk(stg::kThreads);
+    return traced(t, s, name, [&] {
+        if (dtype == LA_FP32) {
+            if (to_padded)
+                stg::k_pad<StF32><<<grid, blk, 0, s>>>(static_cast<const float *>(src),
+                                                       static_cast<float *>(dst), rows, (int)D,
+                                                       (int)Dp);
+            else
+                stg::k_unpad<StF32><<<grid, blk, 0, s>>>(static_cast<const float *>(src),
+                                                         static_cast<float *>(dst), rows,
+                                                         (int)D, (int)Dp);
+        } else {
+            // bf16 and fp16 move as the same 16-bit words
+            if (to_padded)
+                stg::k_pad<StBF16><<<grid, blk, 0, s>>>(static_cast<const uint16_t *>(src),
+                                                        static_cast<uint16_t *>(dst), rows,
+                                                        (int)D, (int)Dp);
+            else
+                stg::k_unpad<StBF16><<<grid, blk, 0, s>>>(static_cast<const uint16_t *>(src),
+                                                          static_cast<uint16_t *>(dst), rows,
+                                                          (int)D, (int)Dp);
+        }
+    });
+}
+
+int stage_record(const char *name, const float *src, int64_t Ds, float *dst, int64_t Dd,
+                 int64_t BH, hipStream_t s, Tracer *t)
+{
+    return traced(t, s, name, [&] {
+        stg::k_stage_record<<<dim3(grid_for(BH * (Dd * Dd + 2 * Dd))), dim3(stg::kThreads), 0,
+                              s>>>(src, dst, BH, (int)Ds, (int)Dd);
+    });
+}
+
+// Forward of any supported call: native, or padded through the workspace.
+int forward_any(bool require_o, const void *Q, const void *K, const void *V, void *O,
+                int64_t B, int64_t H, int64_t N, int64_t D, int causal, int dtype,
+                const float *cin, int64_t n_carry, float *cout, float *den_out,
+                void *state_out, void *ws, size_t ws_bytes, hipStream_t s, Tracer *t)
+{
+    if (!valid_dtype(dtype))
+        return LA_ERR_DTYPE;
+    int rc = check_sizes(B, H, N, D, causal);
+    if (rc != LA_OK)
+        return rc;
+    if (native(D))
+        return forward_impl(require_o, Q, K, V, O, B, H, N, D, causal, dtype, cin, n_carry,
+                            cout, den_out, state_out, ws, ws_bytes, s, t);
+    if (n_carry < 0 || n_carry > kMaxCarry)
+        return LA_ERR_SHAPE;
+    if (B * H == 0)
+        return LA_OK;
+    const int64_t BH = B * H;
+    const size_t rb = record_bytes(BH, D);
+    if (misaligned(cin) || misaligned(cout))
+        return LA_ERR_ALIGN;
+    if (N == 0) {
+        if (overlap({(const char *)cout, rb}, {(const char *)cin, rb}))
+            return LA_ERR_ALIAS;
+        return cout ? stage_record("stage", cin, D, cout, D, BH, s, t) : LA_OK;
+    }
+    if (!Q || !K || !V || !ws || (!O && (require_o || den_out || (!cout && !state_out))))
+        return LA_ERR_NULL;
+    const Staging g = make_staging(B, H, N, D, causal, dtype);
+    if (ws_bytes < g.total)
+        return LA_ERR_WORKSPACE;
+    if (misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(O) ||
+        misaligned(den_out) || misaligned(state_out) || misaligned(ws))
+        return LA_ERR_ALIGN;
+    Plan pp = make_plan(B, H, N, g.Dp, causal);
+    const size_t tb = (size_t)(BH * N * D) * elem_size(dtype);
+    const Range ins[4] = {{(const char *)Q, tb},
+                          {(const char *)K, tb},
+                          {(const char *)V, tb},
+                          {(const char *)cin, rb}};
+    const Range outs[5] = {
+        {(const char *)O, tb},
+        {(const char *)den_out, (size_t)(BH * N) * sizeof(float)},
+        {(const char *)state_out, (size_t)state_floats(pp) * sizeof(float)},
+        {(const char *)ws, g.total},
+        {(const char *)cout, rb}};
+    if (aliased(outs, 5, ins, 4))
+        return LA_ERR_ALIAS;
+    char *w = static_cast<char *>(ws);
+    void *tq = w + g.off_tensor[0], *tk = w + g.off_tensor[1], *tv = w + g.off_tensor[2],
+         *to = w + g.off_tensor[3];
+    float *r_in = reinterpret_cast<float *>(w + g.off_record[0]);
+    float *r_out = reinterpret_cast<float *>(w + g.off_record[1]);
+    const int64_t rows = BH * N;
+    if ((rc = stage_tensor("stage", true, Q, tq, dtype, D, g.Dp, rows, s, t)) != LA_OK ||
+        (rc = stage_tensor("stage", true, K, tk, dtype, D, g.Dp, rows, s, t)) != LA_OK ||
+        (rc = stage_tensor("stage", true, V, tv, dtype, D, g.Dp, rows, s, t)) != LA_OK)
+        return rc;
+    if (cin && (rc = stage_record("stage", cin, D, r_in, g.Dp, BH, s, t)) != LA_OK)
+        return rc;
+    rc = forward_impl(require_o, tq, tk, tv, O ? to : nullptr, B, H, N, g.Dp, causal, dtype,
+                      cin ? r_in : nullptr, n_carry, cout ? r_out : nullptr, den_out,
+                      state_out, w + g.off_inner, g.inner, s, t);
+    if (rc != LA_OK)
+        return rc;
+    if (O && (rc = stage_tensor("unstage", false, to, O, dtype, D, g.Dp, rows, s, t)) != LA_OK)
+        return rc;
+    if (cout && (rc = stage_record("unstage", r_out, g.Dp, cout, D, BH, s, t)) != LA_OK)
+        return rc;
+    return LA_OK;
+}
+
+// Backward of any supported call: native, or padded through the workspace.
+int backward_any(bool require_kv, const void *Q, const void *K, const void *V,
+                 const void *dO, void *dQ, void *dK, void *dV, int64_t B, int64_t H,
+                 int64_t N, int64_t D, int causal, int dtype, const float *cin,
+                 int64_t n_carry, const float *gin, float *gout, const void *state_in,
+                 void *ws, size_t ws_bytes, hipStream_t s, Tracer *t)
+{
+    if (!valid_dtype(dtype))
+        return LA_ERR_DTYPE;
+    int rc = check_sizes(B, H, N, D, causal);
+    if (rc != LA_OK)
+        return rc;
+    if (native(D))
+        return backward_impl(require_kv, Q, K, V, dO, dQ, dK, dV, B, H, N, D, causal, dtype,
+                             cin, n_carry, gin, gout, state_in, ws, ws_bytes, s, t);
+    if (n_carry < 0 || n_carry > kMaxCarry)
+        return LA_ERR_SHAPE;
+    if (B * H == 0)
+        return LA_OK;
+    const int64_t BH = B * H;
+    const size_t rb = record_bytes(BH, D);
+    if (misaligned(gin) || misaligned(gout) || misaligned(cin))
+        return LA_ERR_ALIGN;
+    if (N == 0) {
+        if (overlap({(const char *)gout, rb}, {(const char *)gin, rb}))
+            return LA_ERR_ALIAS;
+        return gout ? stage_record("stage", gin, D, gout, D, BH, s, t) : LA_OK;
+    }
+    if (!Q || !K || !V || !dO || !dQ || !ws || (dK == nullptr) != (dV == nullptr) ||
+        (require_kv && dK == nullptr))
+        return LA_ERR_NULL;
+    const Staging g = make_staging(B, H, N, D, causal, dtype);
+    if (ws_bytes < g.total)
+        return LA_ERR_WORKSPACE;
+    if (misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(dO) ||
+        misaligned(dQ) || misaligned(dK) || misaligned(dV) || misaligned(state_in) ||
+        misaligned(ws))
+        return LA_ERR_ALIGN;
+    Plan pp = make_plan(B, H, N, g.Dp, causal);
+    const size_t tb = (size_t)(BH * N * D) * elem_size(dtype);
+    const Range ins[7] = {{(const char *)Q, tb},
+                          {(const char *)K, tb},
+                          {(const char *)V, tb},
+                          {(const char *)dO, tb},
+                          {(const char *)state_in, (size_t)state_floats(pp) * sizeof(float)},
+                          {(const char *)cin, rb},
+                          {(const char *)gin, rb}};
+    const Range outs[5] = {{(const char *)dQ, tb},
+                           {(const char *)dK, tb},
+                           {(const char *)dV, tb},
+                           {(const char *)ws, g.total},
+                           {(const char *)gout, rb}};
+    if (aliased(outs, 5, ins, 7))
+        return LA_ERR_ALIAS;
+    char *w = static_cast<char *>(ws);
+    void *T_[7];
+    for (int i = 0; i < 7; ++i)
+        T_[i] = w + g.off_tensor[i];
+    float *r_cin = reinterpret_cast<float *>(w + g.off_record[0]);
+    float *r_gin = reinterpret_cast<float *>(w + g.off_record[1]);
+    float *r_gout = reinterpret_cast<float *>(w + g.off_record[2]);
+    const int64_t rows = BH * N;
+    const void *src[4] = {Q, K, V, dO};
+    for (int i = 0; i < 4; ++i)
+        if ((rc = stage_tensor("stage", true, src[i], T_[i], dtype, D, g.Dp, rows, s, t)) !=
+            LA_OK)
+            return rc;
+    if (cin && !state_in && (rc = stage_record("stage", cin, D, r_cin, g.Dp, BH, s, t)) != LA_OK)
+        return rc;
+    if (gin && (rc = stage_record("stage", gin, D, r_gin, g.Dp, BH, s, t)) != LA_OK)
+        return rc;
+    const bool kv = dK != nullptr;
+    rc = backward_impl(require_kv, T_[0], T_[1], T_[2], T_[3], T_[4], kv ? T_[5] : nullptr,
+                       kv ? T_[6] : nullptr, B, H, N, g.Dp, causal, dtype,
+                       (cin && !state_in) ? r_cin : nullptr, n_carry, gin ? r_gin : nullptr,
+                       gout ? r_gout : nullptr, state_in, w + g.off_inner, g.inner, s, t);
+    if (rc != LA_OK)
+        return rc;
+    if ((rc = stage_tensor("unstage", false, T_[4], dQ, dtype, D, g.Dp, rows, s, t)) != LA_OK)
+        return rc;
+    if (kv && ((rc = stage_tensor("unstage", false, T_[5], dK, dtype, D, g.Dp, rows, s, t)) !=
+                   LA_OK ||
+               (rc = stage_tensor("unstage", false, T_[6], dV, dtype, D, g.Dp, rows, s, t)) !=
+                   LA_OK))
+        return rc;
+    if (gout && (rc = stage_record("unstage", r_gout, g.Dp, gout, D, BH, s, t)) != LA_OK)
+        return rc;
+    return LA_OK;
 }
 
 template <class ST>
@@ -721,20 +989,24 @@ int launch_decode(const void *q, const void *k, const void *v, void *o, int64_t 
                   float *den, hipStream_t s)
 {
     typedef typename ST::T T;
+    const T *qq = static_cast<const T *>(q), *kk = static_cast<const T *>(k),
+            *vv = static_cast<const T *>(v);
+    T *oo = static_cast<T *>(o);
 #define LA_DEC(d)                                                                          \
     dec::k_decode<ST, d><<<dim3((unsigned)(BH * dec::blocks_per_head<d>())),              \
-                           dim3(dec::kThreads), 0, s>>>(                                   \
-        static_cast<const T *>(q), static_cast<const T *>(k), static_cast<const T *>(v),   \
-        static_cast<T *>(o), den, rin, rout, counts, n_all, (int)H)
+                           dim3(dec::kThreads), 0, s>>>(qq, kk, vv, oo, den, rin, rout,    \
+                                                        counts, n_all, (int)H)
     switch (D) {
-    case 16: LA_DEC(16); break;
-    case 32: LA_DEC(32); break;
-    case 64: LA_DEC(64); break;
-    case 128: LA_DEC(128); break;
-    case 256: LA_DEC(256); break;
-    default: return LA_ERR_UNSUPPORTED;
+    case 16: LA_DEC(16); return launched();
+    case 32: LA_DEC(32); return launched();
+    case 64: LA_DEC(64); return launched();
+    case 128: LA_DEC(128); return launched();
+    case 256: LA_DEC(256); return launched();
+    default: break;
     }
 #undef LA_DEC
+    dec::k_decode_any<ST><<<dim3((unsigned)(BH * ((D + 31) / 32))), dim3(dec::kThreads), 0, s>>>(
+        qq, kk, vv, oo, den, rin, rout, counts, n_all, (int)H, (int)D);
     return launched();
 }
 
@@ -746,7 +1018,7 @@ int la_decode_step(const void *q, const void *k, const void *v, void *o, int64_t
                    int64_t D, int dtype, const float *state_in, float *state_out,
                    const int64_t *counts, int64_t n_prev, float *den_out, void *stream)
 {
-    if (dtype != LA_FP32 && dtype != LA_BF16)
+    if (!valid_dtype(dtype))
         return LA_ERR_DTYPE;
     int rc = check_sizes(B, H, 1, D, 1);
     if (rc != LA_OK)
@@ -762,7 +1034,7 @@ int la_decode_step(const void *q, const void *k, const void *v, void *o, int64_t
         misaligned(den_out))
         return LA_ERR_ALIGN;
     const size_t tb = (size_t)(B * H * D) * elem_size(dtype);
-    const size_t rb = (size_t)(B * H * (D * D + 2 * D)) * sizeof(float);
+    const size_t rb = record_bytes(B * H, D);
     const Range ins[5] = {{(const char *)q, tb},
                           {(const char *)k, tb},
                           {(const char *)v, tb},
@@ -774,13 +1046,18 @@ int la_decode_step(const void *q, const void *k, const void *v, void *o, int64_t
     if (aliased(outs, 3, ins, 5))
         return LA_ERR_ALIAS;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    return dtype == LA_FP32 ? launch_decode<StF32>(q, k, v, o, B * H, H, D, state_in,
-                                                   state_out, counts, (float)n_prev, den_out, s)
-                            : launch_decode<StBF16>(q, k, v, o, B * H, H, D, state_in,
-                                                    state_out, counts, (float)n_prev, den_out,
-                                                    s);
+    switch (dtype) {
+    case LA_FP32:
+        return launch_decode<StF32>(q, k, v, o, B * H, H, D, state_in, state_out, counts,
+                                    (float)n_prev, den_out, s);
+    case LA_BF16:
+        return launch_decode<StBF16>(q, k, v, o, B * H, H, D, state_in, state_out, counts,
+                                     (float)n_prev, den_out, s);
+    default:
+        return launch_decode<StF16>(q, k, v, o, B * H, H, D, state_in, state_out, counts,
+                                    (float)n_prev, den_out, s);
+    }
 }
-
 
 const char *la_status_string(int status)
 {
@@ -788,9 +1065,8 @@ const char *la_status_string(int status)
     case LA_OK: return "LA_OK";
     case LA_ERR_NULL: return "LA_ERR_NULL: a required pointer is NULL";
     case LA_ERR_SHAPE: return "LA_ERR_SHAPE: negative or too large size";
-    case LA_ERR_DTYPE: return "LA_ERR_DTYPE: dtype must be LA_FP32 or LA_BF16";
-    case LA_ERR_UNSUPPORTED:
-        return "LA_ERR_UNSUPPORTED: D must be 16, 32, 64, 128 or 256 and causal 0 or 1";
+    case LA_ERR_DTYPE: return "LA_ERR_DTYPE: dtype must be LA_FP32, LA_BF16 or LA_FP16";
+    case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED: D must be 1..256 and causal 0 or 1";
     case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE: workspace too small";
     case LA_ERR_ALIAS: return "LA_ERR_ALIAS: an output overlaps an input or another output";
     case LA_ERR_ALIGN: return "LA_ERR_ALIGN: device pointers must be 16-byte aligned";
@@ -803,28 +1079,38 @@ int64_t la_num_segments(int64_t B, int64_t H, int64_t N, int64_t D, int causal)
 {
     if (check_sizes(B, H, N, D, causal) != LA_OK)
         return 0;
-    return make_plan(B, H, N, D, causal).nseg;
+    return make_plan(B, H, N, padded_d(D), causal).nseg;
+}
+
+size_t la_workspace_size_for(int64_t B, int64_t H, int64_t N, int64_t D, int causal,
+                             int dtype)
+{
+    if (!valid_dtype(dtype) || check_sizes(B, H, N, D, causal) != LA_OK || B * H * N == 0)
+        return 0;
+    if (native(D))
+        return (size_t)make_layout(make_plan(B, H, N, D, causal)).total * sizeof(float);
+    return make_staging(B, H, N, D, causal, dtype).total;
 }
 
 size_t la_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D, int causal)
 {
-    if (check_sizes(B, H, N, D, causal) != LA_OK || B * H * N == 0)
-        return 0;
-    return (size_t)make_layout(make_plan(B, H, N, D, causal)).total * sizeof(float);
+    // padded fp32 tensors are the largest; native D needs the same for every
+    // storage type
+    return la_workspace_size_for(B, H, N, D, causal, LA_FP32);
 }
 
 size_t la_state_size(int64_t B, int64_t H, int64_t N, int64_t D, int causal)
 {
     if (check_sizes(B, H, N, D, causal) != LA_OK || B * H * N == 0)
         return 0;
-    return (size_t)state_floats(make_plan(B, H, N, D, causal)) * sizeof(float);
+    return (size_t)state_floats(make_plan(B, H, N, padded_d(D), causal)) * sizeof(float);
 }
 
 size_t la_record_size(int64_t B, int64_t H, int64_t D)
 {
-    if (B < 0 || H < 0 || !supported_d(D) || B * H > (int64_t)1 << 22)
+    if (B < 0 || H < 0 || D < 1 || D > 256 || B * H > (int64_t)1 << 22)
         return 0;
-    return (size_t)(B * H * (D * D + 2 * D)) * sizeof(float);
+    return record_bytes(B * H, D);
 }
 
 int la_forward_traced(const void *Q, const void *K, const void *V, void *O, int64_t B,
@@ -832,9 +1118,13 @@ int la_forward_traced(const void *Q, const void *K, const void *V, void *O, int6
                       void *state_out, void *ws, size_t ws_bytes, void *stream,
                       void *const *events, int n_events, int *n_launched, const char **names)
 {
-    return forward_impl(true, Q, K, V, O, B, H, N, D, causal, dtype, nullptr, 0, nullptr,
-                        den_out, state_out, ws, ws_bytes, stream, events, n_events, n_launched,
-                        names);
+    Tracer t{events, events ? n_events : 0, 0, names};
+    const int rc = forward_any(true, Q, K, V, O, B, H, N, D, causal, dtype, nullptr, 0, nullptr,
+                               den_out, state_out, ws, ws_bytes,
+                               static_cast<hipStream_t>(stream), &t);
+    if (n_launched)
+        *n_launched = t.n;
+    return rc;
 }
 
 int la_forward(const void *Q, const void *K, const void *V, void *O, int64_t B, int64_t H,
@@ -851,9 +1141,10 @@ int la_forward_segment(const void *Q, const void *K, const void *V, void *O, int
                        float *den_out, void *state_out, void *ws, size_t ws_bytes,
                        void *stream)
 {
-    return forward_impl(false, Q, K, V, O, B, H, N, D, causal, dtype, carry_in, n_carry,
-                        carry_out, den_out, state_out, ws, ws_bytes, stream, nullptr, 0, nullptr,
-                        nullptr);
+    Tracer t{nullptr, 0, 0, nullptr};
+    return forward_any(false, Q, K, V, O, B, H, N, D, causal, dtype, carry_in, n_carry,
+                       carry_out, den_out, state_out, ws, ws_bytes,
+                       static_cast<hipStream_t>(stream), &t);
 }
 
 int la_backward_traced(const void *Q, const void *K, const void *V, const void *dO, void *dQ,
@@ -862,9 +1153,13 @@ int la_backward_traced(const void *Q, const void *K, const void *V, const void *
                        void *stream, void *const *events, int n_events, int *n_launched,
                        const char **names)
 {
-    return backward_impl(true, Q, K, V, dO, dQ, dK, dV, B, H, N, D, causal, dtype, nullptr, 0,
-                         nullptr, nullptr, state_in, ws, ws_bytes, stream, events, n_events,
-                         n_launched, names);
+    Tracer t{events, events ? n_events : 0, 0, names};
+    const int rc = backward_any(true, Q, K, V, dO, dQ, dK, dV, B, H, N, D, causal, dtype,
+                                nullptr, 0, nullptr, nullptr, state_in, ws, ws_bytes,
+                                static_cast<hipStream_t>(stream), &t);
+    if (n_launched)
+        *n_launched = t.n;
+    return rc;
 }
 
 int la_backward(const void *Q, const void *K, const void *V, const void *dO, void *dQ,
@@ -881,9 +1176,10 @@ int la_backward_segment(const void *Q, const void *K, const void *V, const void 
                         const float *gcarry_in, float *gcarry_out, const void *state_in,
                         void *ws, size_t ws_bytes, void *stream)
 {
-    return backward_impl(false, Q, K, V, dO, dQ, dK, dV, B, H, N, D, causal, dtype, carry_in,
-                         n_carry, gcarry_in, gcarry_out, state_in, ws, ws_bytes, stream, nullptr,
-                         0, nullptr, nullptr);
+    Tracer t{nullptr, 0, 0, nullptr};
+    return backward_any(false, Q, K, V, dO, dQ, dK, dV, B, H, N, D, causal, dtype, carry_in,
+                        n_carry, gcarry_in, gcarry_out, state_in, ws, ws_bytes,
+                        static_cast<hipStream_t>(stream), &t);
 }
 
 }  // extern "C"

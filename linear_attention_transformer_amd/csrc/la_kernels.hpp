@@ -74,6 +74,7 @@ struct StF32 {
         o[3] = __uint_as_float(r.w);
     }
     __device__ static __forceinline__ T narrow(float x) { return x; }
+    __device__ static __forceinline__ float widen1(T x) { return x; }
 };
 
 struct StBF16 {
@@ -99,6 +100,48 @@ struct StBF16 {
     {
         typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
         const bf2 v = {(__bf16)a, (__bf16)b};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+    __device__ static __forceinline__ float widen1(T x) { return __uint_as_float((uint32_t)x << 16); }
+    // the two elements of a 32-bit word (low half first)
+    __device__ static __forceinline__ void widen2(uint32_t x, float *o)
+    {
+        o[0] = __uint_as_float(x << 16);
+        o[1] = __uint_as_float(x & 0xffff0000u);
+    }
+};
+
+// IEEE half storage: widened exactly to fp32 (v_cvt_f32_f16), narrowed with
+// round to nearest even (v_cvt_f16_f32 in the default rounding mode)
+struct StF16 {
+    typedef uint16_t T;
+    static constexpr int VEC = 8;
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    typedef float fl2 __attribute__((ext_vector_type(2)));
+    __device__ static __forceinline__ void widen2(uint32_t x, float *o)
+    {
+        const fl2 f = __builtin_convertvector(__builtin_bit_cast(h2, x), fl2);
+        o[0] = f.x;
+        o[1] = f.y;
+    }
+    __device__ static __forceinline__ void widen(const uint4 &r, float *o)
+    {
+        widen2(r.x, o);
+        widen2(r.y, o + 2);
+        widen2(r.z, o + 4);
+        widen2(r.w, o + 6);
+    }
+    __device__ static __forceinline__ float widen1(T x)
+    {
+        return (float)__builtin_bit_cast(_Float16, x);
+    }
+    __device__ static __forceinline__ T narrow(float x)
+    {
+        return __builtin_bit_cast(uint16_t, (_Float16)x);
+    }
+    __device__ static __forceinline__ uint32_t narrow2(float a, float b)
+    {
+        const h2 v = {(_Float16)a, (_Float16)b};
         return __builtin_bit_cast(uint32_t, v);
     }
 };

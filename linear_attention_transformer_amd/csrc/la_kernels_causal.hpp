@@ -87,10 +87,7 @@ struct Rows {
         for (int p = 0; p < PER; ++p) {
             const int c = tid + p * NT;
             float v[VEC];
-            if constexpr (VEC == 4)
-                StF32::widen(r[p], v);
-            else
-                StBF16::widen(r[p], v);
+            ST::widen(r[p], v);
             float *dst = lds + (c / CPR) * LDX + VEC * (c % CPR);
 #pragma unroll
             for (int x = 0; x < VEC; x += 4)

@@ -17,6 +17,8 @@
 // Thread (rg, cg) holds four consecutive columns (one 16-byte vector) and
 // walks its rows rg, rg + RG, ...; so the CB/4 threads of a row read one
 // contiguous run of the row.  The row partials of S'^T q meet in LDS.
+// k_decode_any takes any head size up to 256 (one column per thread, scalar
+// loads) and fp16 storage as well.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,6 +26,7 @@
 #include <cstdint>
 
 #include "la_kernels.hpp"
+#include "la_kernels_stage.hpp"
 
 namespace la {
 namespace dec {
@@ -45,10 +48,7 @@ constexpr int blocks_per_head()
 template <class ST>
 __device__ __forceinline__ float ld1(const typename ST::T *p)
 {
-    if constexpr (ST::VEC == 4)
-        return *p;
-    else
-        return __uint_as_float((uint32_t)*p << 16);
+    return ST::widen1(*p);
 }
 
 template <class ST, int D>
@@ -143,6 +143,87 @@ __global__ __launch_bounds__(kThreads) void k_decode(
         w[D * D + D + e] = u1;
         const float n = counts ? (float)counts[bh / H] : n_all;
         // den = (n + 1) + q.z' with q.z' = q.z + q.k
+        const float den = (n + 1.f) + (dots[1] + dots[0]);
+        O[io + e] = ST::narrow((u1 + num) / den);
+        if (den_out && cb == 0 && tid == 0)
+            den_out[bh] = den;
+    }
+}
+
+// Any head size D <= 256 (records of D*D + 2*D floats, no alignment beyond
+// 4 bytes).  A workgroup takes one head and 32 columns; thread (rg, c) holds
+// column c of the block and walks rows rg, rg + 8, ...
+template <class ST>
+__global__ __launch_bounds__(kThreads) void k_decode_any(
+    const typename ST::T *__restrict__ Q, const typename ST::T *__restrict__ K,
+    const typename ST::T *__restrict__ V, typename ST::T *__restrict__ O,
+    float *__restrict__ den_out, const float *__restrict__ rin, float *__restrict__ rout,
+    const int64_t *__restrict__ counts, float n_all, int H, int D)
+{
+    constexpr int CB = 32, RG = kThreads / CB;
+    __shared__ float qs[256], ks[256];
+    __shared__ float part[RG][CB];
+    __shared__ float dots[2];
+
+    const int nb = (D + CB - 1) / CB;
+    const int tid = threadIdx.x;
+    const int64_t bh = blockIdx.x / nb;
+    const int cb = blockIdx.x % nb;
+    const int64_t ps = (int64_t)D * D + 2 * D;
+    const int64_t io = bh * D;
+    const bool has_in = rin != nullptr;
+    const float *r = has_in ? rin + bh * ps : nullptr;
+    float *w = rout + bh * ps;
+
+    for (int d = tid; d < D; d += kThreads) {
+        qs[d] = ld1<ST>(Q + io + d);
+        ks[d] = ld1<ST>(K + io + d);
+    }
+    if (tid < 64) {
+        float qk = 0.f, qz = 0.f;
+        for (int d = tid; d < D; d += 64) {
+            const float q = ld1<ST>(Q + io + d);
+            qk += q * ld1<ST>(K + io + d);
+            qz += has_in ? q * r[(int64_t)D * D + d] : 0.f;
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            qk += __shfl_xor(qk, o, 64);
+            qz += __shfl_xor(qz, o, 64);
+        }
+        if (tid == 0) {
+            dots[0] = qk;
+            dots[1] = qz;
+        }
+    }
+    __syncthreads();
+
+    const int c = tid % CB, rg = tid / CB;
+    const int e = cb * CB + c;
+    float acc = 0.f;
+    if (e < D) {
+        const float ve = ld1<ST>(V + io + e);
+        for (int d = rg; d < D; d += RG) {
+            const int64_t x = (int64_t)d * D + e;
+            const float t = (has_in ? r[x] : 0.f) + ks[d] * ve;
+            w[x] = t;
+            acc += qs[d] * t;
+        }
+    }
+    part[rg][c] = acc;
+    if (cb == 0)
+        for (int d = tid; d < D; d += kThreads)
+            w[(int64_t)D * D + d] = (has_in ? r[(int64_t)D * D + d] : 0.f) + ks[d];
+    __syncthreads();
+
+    if (tid < CB && e < D) {
+        float num = 0.f;
+        for (int g = 0; g < RG; ++g)
+            num += part[g][tid];
+        const float v = ld1<ST>(V + io + e);
+        const float u1 = (has_in ? r[(int64_t)D * D + D + e] : 0.f) + v;
+        w[(int64_t)D * D + D + e] = u1;
+        const float n = counts ? (float)counts[bh / H] : n_all;
         const float den = (n + 1.f) + (dots[1] + dots[0]);
         O[io + e] = ST::narrow((u1 + num) / den);
         if (den_out && cb == 0 && tid == 0)

@@ -67,6 +67,26 @@ struct IO<StBF16> {
     }
 };
 
+template <>
+struct IO<StF16> {
+    __device__ static __forceinline__ float load1(const uint16_t *p) { return StF16::widen1(*p); }
+    __device__ static __forceinline__ f4 load4(const uint16_t *p)
+    {
+        const uint2 r = *reinterpret_cast<const uint2 *>(p);
+        float v[4];
+        StF16::widen2(r.x, v);
+        StF16::widen2(r.y, v + 2);
+        return f4{v[0], v[1], v[2], v[3]};
+    }
+    __device__ static __forceinline__ void store4(uint16_t *p, f4 v)
+    {
+        uint2 r;
+        r.x = StF16::narrow2(v[0], v[1]);
+        r.y = StF16::narrow2(v[2], v[3]);
+        *reinterpret_cast<uint2 *>(p) = r;
+    }
+};
+
 __device__ __forceinline__ float dot4(f4 a, f4 b)
 {
     return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
@@ -132,13 +152,10 @@ __device__ __forceinline__ void load_vec(const typename ST::T *p, float *o)
             o[0] = *reinterpret_cast<const float *>(p);
         }
     } else {
-        if constexpr (VW == 2) {
-            const uint32_t x = *reinterpret_cast<const uint32_t *>(p);
-            o[0] = __uint_as_float(x << 16);
-            o[1] = __uint_as_float(x & 0xffff0000u);
-        } else {
-            o[0] = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t *>(p) << 16);
-        }
+        if constexpr (VW == 2)
+            ST::widen2(*reinterpret_cast<const uint32_t *>(p), o);
+        else
+            o[0] = ST::widen1(*reinterpret_cast<const uint16_t *>(p));
     }
 }
 
@@ -156,14 +173,10 @@ __device__ __forceinline__ void buf_load_vec(__amdgpu_buffer_rsrc_t rs, int vo, 
             o[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, vo, so, 0));
         }
     } else {
-        if constexpr (VW == 2) {
-            const uint32_t x = __builtin_amdgcn_raw_buffer_load_b32(rs, vo, so, 0);
-            o[0] = __uint_as_float(x << 16);
-            o[1] = __uint_as_float(x & 0xffff0000u);
-        } else {
-            o[0] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, vo, so, 0)
-                                   << 16);
-        }
+        if constexpr (VW == 2)
+            ST::widen2(__builtin_amdgcn_raw_buffer_load_b32(rs, vo, so, 0), o);
+        else
+            o[0] = ST::widen1((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs, vo, so, 0));
     }
 }
 
@@ -483,10 +496,7 @@ __global__ __launch_bounds__(apply_threads<D>()) void k_apply_nc(
         for (int p = 0; p < PER; ++p) {
             const int c = tid + p * NT;
             float v[VEC];
-            if constexpr (VEC == 4)
-                StF32::widen(stg[p], v);
-            else
-                StBF16::widen(stg[p], v);
+            ST::widen(stg[p], v);
             float *dst = &xs[buf][(c / CPR) * LDX + VEC * (c % CPR)];
 #pragma unroll
             for (int x = 0; x < VEC; x += 4)
@@ -694,10 +704,7 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
     // widened chunk to LDS (rows past the segment end were loaded as zeros);
     // returns the values
     auto stage_one = [&](float *lds, const uint4 &src, int c, float (&v)[VEC]) {
-        if constexpr (VEC == 4)
-            StF32::widen(src, v);
-        else
-            StBF16::widen(src, v);
+        ST::widen(src, v);
         float *dst = lds + (c / CPR) * LDX + VEC * (c % CPR);
 #pragma unroll
         for (int x = 0; x < VEC; x += 4)
@@ -727,10 +734,7 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
             if (c % CPR == 0)
                 ivx[buf][c / CPR] = inv;
             float gv[VEC];
-            if constexpr (VEC == 4)
-                StF32::widen(sg[p], gv);
-            else
-                StBF16::widen(sg[p], gv);
+            ST::widen(sg[p], gv);
             float *dst = xs[buf] + (c / CPR) * LDX + VEC * (c % CPR);
 #pragma unroll
             for (int x = 0; x < VEC; x += 4)

@@ -59,7 +59,19 @@ def test_sizes():
     # once N >> D; here it must stay below the four fp32 inputs
     assert 0 < ws < 4 * B * H * N * D * 4
     assert la.workspace_size(0, 16, 4096, 128) == 0
-    assert la.workspace_size(4, 16, 4096, 48) == 0       # unsupported D
+    assert la.workspace_size(4, 16, 4096, 300) == 0      # unsupported D
+    assert la.workspace_size(4, 16, 4096, 0) == 0
+    # padded head sizes (between the native 32, 64, 128, 256) need room for
+    # seven padded tensors on top of the native workspace
+    nat = la.workspace_size(B, H, N, 64)
+    pad = B * H * N * 64
+    assert la.workspace_size(B, H, N, 48) >= nat + 7 * pad * 4
+    for dt in (torch.bfloat16, torch.float16):
+        assert la.workspace_size(B, H, N, 64, dtype=dt) == nat
+        assert nat + 7 * pad * 2 <= la.workspace_size(B, H, N, 48, dtype=dt) < \
+            la.workspace_size(B, H, N, 48)
+    assert la.state_size(B, H, N, 6, True) == la.state_size(B, H, N, 32, True)
+    assert la.state_size(B, H, N, 16, True) == la.state_size(B, H, N, 32, True)
     assert la.workspace_size(4, 16, -1, 128) == 0
     # segments grow with N, never exceed the 64-row chunks
     for n in (1, 63, 64, 65, 1000, 131072):
@@ -86,7 +98,13 @@ def test_host_validation_rejects_before_launch():
     assert f(P(), P(tb), P(2 * tb), P(3 * tb), B, H, N, D, 0, 7, None, None, P(4 * tb), ws, None) == 3
     assert f(P(), P(tb), P(2 * tb), P(3 * tb), B, H, N, D, 2, 0, None, None, P(4 * tb), ws, None) == 4
     assert f(P(), P(tb), P(2 * tb), P(3 * tb), B, H, -1, D, 0, 0, None, None, P(4 * tb), ws, None) == 2
-    assert f(P(), P(tb), P(2 * tb), P(3 * tb), B, H, N, 6, 0, 0, None, None, P(4 * tb), ws, None) == 4
+    assert f(P(), P(tb), P(2 * tb), P(3 * tb), B, H, N, 300, 0, 0, None, None, P(4 * tb), ws, None) == 4
+    assert f(P(), P(tb), P(2 * tb), P(3 * tb), B, H, N, 0, 0, 0, None, None, P(4 * tb), ws, None) == 4
+    # a padded head size (D = 6) with too small a workspace, in fp32 and fp16
+    assert f(P(), P(tb), P(2 * tb), P(3 * tb), B, H, N, 6, 0, 0, None, None, P(4 * tb), 4096,
+             None) == 5
+    assert f(P(), P(tb), P(2 * tb), P(3 * tb), B, H, N, 6, 0, 2, None, None, P(4 * tb), 4096,
+             None) == 5
     assert f(P(), P(tb), P(2 * tb), P(3 * tb), 1 << 40, 1 << 40, N, D, 0, 0, None, None,
              P(4 * tb), ws, None) == 2
     # empty problem is a no-op even with NULL pointers
@@ -127,7 +145,8 @@ def test_host_validation_segment_calls():
     tb = B * H * N * D * 4
     rb = la.record_size(B, H, D)
     assert rb == B * H * (D * D + 2 * D) * 4
-    assert la.record_size(1, 1, 48) == 0 and la.record_size(-1, 1, 16) == 0
+    assert la.record_size(1, 1, 300) == 0 and la.record_size(-1, 1, 16) == 0
+    assert la.record_size(1, 1, 6) == 48 * 4
     W, CI, CO = 4 * tb, 4 * tb + ws + 256, 4 * tb + ws + 256 + rb + 256
     f = lib.la_forward_segment
 
@@ -178,7 +197,8 @@ def test_host_validation_decode_step():
         return d(q, P(tb), P(2 * tb), o, B, H, D_, dt, si, so, counts, n, None, None)
 
     assert da(dt=5) == 3
-    assert da(D_=48) == 4
+    assert da(D_=300) == 4
+    assert da(D_=0) == 4
     assert da(n=-1) == 2
     assert da(q=None) == 1
     assert da(so=None) == 1

@@ -4,7 +4,9 @@ Every case draws seeded inputs from the shared generator, runs the forward
 and backward through the C ABI on cuda:0, and compares O, den, dQ, dK, dV
 element by element (relative L2 per tensor) with the oracle fed the same
 stored values.  Tolerances: fp32 storage 1e-5; bf16 storage (fp32
-arithmetic, bf16 outputs) 2e-2.
+arithmetic, bf16 outputs) 2e-2; fp16 storage (fp32 arithmetic, fp16
+outputs) 1e-3, from the fp16 rounding of the outputs (unit roundoff
+2^-11 = 4.9e-4, relative L2 about 3e-4 for uniformly spread rounding).
 """
 import sys
 
@@ -17,7 +19,7 @@ from linear_attention_transformer_amd.inputs import as_f64_numpy, make_inputs
 
 pytestmark = pytest.mark.gpu
 
-TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
+TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2, torch.float16: 1e-3}
 DEV = "cuda:0"
 
 
@@ -103,6 +105,23 @@ def test_ragged_bf16(D, causal):
     compare(2, 1, 777, D, torch.bfloat16, causal, seed=3)
 
 
+@pytest.mark.parametrize("D", [1, 6, 20, 48, 100, 200])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_generic_head_sizes(D, causal, dtype):
+    """Head sizes between the native ones (D = 6 is the Figure 1 shape),
+    padded to the next native size inside the library."""
+    compare(2, 2, 333, D, dtype, causal, seed=D + 40)
+
+
+@pytest.mark.parametrize("D", [6, 16, 32, 64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp16_storage(D, causal):
+    """fp16 storage on the fp32 matrix-core kernels (widened exactly on
+    load, outputs rounded to nearest even)."""
+    compare(2, 2, 333, D, torch.float16, causal, seed=D + 50)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_long_segments_d128(causal, dtype):
@@ -124,7 +143,7 @@ def test_multichunk_segments(causal, dtype):
 
 # ------------------------------------------------------------- full sizes
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
 def test_metric_shape_all_heads(causal, dtype):
     """B=4, H=16, N=4096, D=128, every element of every head."""
     compare(4, 16, 4096, 128, dtype, causal)
@@ -245,12 +264,16 @@ def test_validation_errors_on_device():
     with pytest.raises(m.LAError) as e:
         m.forward(mis, k, v)
     assert e.value.code == 7
-    q48 = torch.zeros(1, 2, 64, 48, device=DEV)
+    q300 = torch.zeros(1, 2, 64, 300, device=DEV)
     with pytest.raises(m.LAError) as e:
-        m.forward(q48, q48, q48)
+        m.forward(q300, q300, q300)               # head size above 256
     assert e.value.code == 4
     with pytest.raises(m.LAError) as e:
         m.forward(q, k, v, workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
     assert e.value.code == 5
     with pytest.raises(TypeError):
-        m.forward(q.half(), k.half(), v.half())
+        m.forward(q.double(), k.double(), v.double())
+    q48 = torch.zeros(1, 2, 64, 48, device=DEV, dtype=torch.float16)
+    with pytest.raises(m.LAError) as e:               # a padded size needs the larger workspace
+        m.forward(q48, q48, q48, workspace=m.alloc_workspace(1, 2, 64, 32, False, DEV))
+    assert e.value.code == 5
