@@ -20,7 +20,9 @@ times the fp64 CPU oracle on the host.  `variants` times the other storage
 type and mask at the same shape; `pieces` times the causal step streamed as
 equal pieces through the carried-state calls (la_forward_segment /
 la_backward_segment); `decode` times one recurrent decode step
-(la_decode_step) per head at the bench's B x H heads and at B = 64.
+(la_decode_step) per head at the bench's B x H heads and at B = 64; `layer`
+times one whole layer (projections, attention, their gradients) with
+C = H * D.
 """
 from __future__ import annotations
 
@@ -307,6 +309,40 @@ def time_decode(la, make_inputs, dev, B, H, D, dtype, steps, warmup):
     return eager_us, graph_us, nbytes
 
 
+def time_layer(la, dev, B, N, H, D, dtype, causal, steps, warmup):
+    """ms per forward + backward of one linear-attention layer with C = H*D
+    (la_layer_forward / la_layer_backward: QKV projection, attention, output
+    projection and their gradients), and its flops per step: the six
+    projection GEMMs (2*B*N*C*(3HD + HD) forward, twice that backward) plus
+    the attention's 12*B*H*N*D^2."""
+    import torch
+    from linear_attention_transformer_amd.inputs import make_layer_inputs
+    C = H * D
+    x, wqkv, wo, dy = make_layer_inputs(B, N, C, H, D, dtype=dtype, seed=0, device=dev)
+    sb, wb = la.layer_sizes(B, N, C, H, D, causal, dtype)
+    saved = torch.empty(sb, dtype=torch.uint8, device=dev)
+    ws = torch.empty(wb, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    outs = (torch.empty_like(x), torch.empty_like(wqkv), torch.empty_like(wo))
+
+    def step():
+        la.layer_forward(x, wqkv, wo, H, causal, saved=saved, out=y, workspace=ws)
+        la.layer_backward(x, wqkv, wo, dy, H, causal, saved=saved, outs=outs, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 3 * 2 * B * N * C * 4 * H * D + 12 * B * H * N * D * D
+    return ms, flops
+
+
 def cpu_baseline(q, k, v, g, causal):
     import oracle
     from linear_attention_transformer_amd.inputs import as_f64_numpy
@@ -505,6 +541,21 @@ def main():
         print("bench: causal %s in %d pieces: %.3f ms/step (whole sequence %.3f)"
               % (args.dtype, args.pieces, pms, whole), file=sys.stderr, flush=True)
 
+    # one whole layer around the attention (projections on rocBLAS)
+    layer = None
+    if not args.no_variants:
+        torch.cuda.empty_cache()
+        lms, lfl = time_layer(la, dev, B, N, H, D, dt, causal, max(args.steps // 4, 5),
+                              max(args.warmup // 10, 5))
+        lpeak = PEAK_FP32_MFMA_TFLOPS if args.dtype == "fp32" else PEAK_BF16_MFMA_TFLOPS
+        layer = {"C": H * D, "ms_per_step": round(lms, 4),
+                 "tokens_per_s": round(B * N / (lms * 1e-3), 1),
+                 "flops_per_step": lfl, "achieved_TFLOPs": round(lfl / (lms * 1e-3) / 1e12, 1),
+                 "peak_TFLOPs": lpeak, "frac": round(lfl / (lms * 1e-3) / 1e12 / lpeak, 4),
+                 "attention_ms_per_step": round(ms, 4)}
+        print("bench: layer (C=%d) fwd+bwd %.3f ms/step, %.0f TFLOP/s (attention alone %.3f ms)"
+              % (H * D, lms, lfl / (lms * 1e-3) / 1e12, ms), file=sys.stderr, flush=True)
+
     # the recurrent decode step at the bench's heads and at a serving batch
     decode = None
     if not args.no_variants:
@@ -559,6 +610,7 @@ def main():
         "variants": variants,
         "pieces": pieces,
         "decode": decode,
+        "layer": layer,
     }
     print(json.dumps(line), flush=True)
 

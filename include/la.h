@@ -55,8 +55,10 @@
  *    on every call (fixed-order reductions, no floating-point atomics).
  *  - The library keeps no mutable global state apart from device facts it
  *    caches on first use (the compute-unit count of each device and the
- *    occupancy of a kernel, which size some launches); concurrent calls on
- *    different streams must use different workspaces.
+ *    occupancy of a kernel, which size some launches) and, for the layer
+ *    calls, one rocBLAS handle per device (created on first use, guarded by
+ *    a lock); concurrent calls on different streams must use different
+ *    workspaces.
  */
 #ifndef LA_H
 #define LA_H
@@ -260,6 +262,49 @@ int la_decode_step(const void *q, const void *k, const void *v, void *o,
                    const float *state_in, float *state_out,
                    const int64_t *counts, int64_t n_prev, float *den_out,
                    void *stream);
+
+/*
+ * One linear-attention layer (the method outline of the cloud.baidu.com
+ * article: the input rows pass through a linear map, linear attention forms
+ * the context rows, which are processed further; here a second linear map).
+ * Per sequence, with X [N, C], Wqkv [C, 3*H*D], Wo [H*D, C]:
+ *
+ *     [Q | K | V] = X Wqkv      column j*H*D + h*D + d of Wqkv feeds element d
+ *                               of head h of Q (j = 0), K (j = 1), V (j = 2)
+ *     O_h = linear attention of (Q_h, K_h, V_h)   (la_forward, each head)
+ *     Y = [O_1 ... O_H] Wo      (heads side by side: column h*D + d)
+ *
+ * No biases and no scaling beyond the weights.  All matrices are DEVICE,
+ * row-major, contiguous, of `dtype` (fp32, bf16 or fp16): X, Y, dY, dX are
+ * [B, N, C].  The two projections and their gradients are GEMMs on rocBLAS
+ * (fp32 accumulation, results rounded to `dtype`); the head split and merge
+ * and the attention are this library's kernels.  Sizes: B*N, C and 3*H*D
+ * below 2^31, and the attention's own limits (1 <= D <= 256; B*H, N as for
+ * la_forward).
+ *
+ *   saved : la_layer_saved_size() bytes, written by the forward and read by
+ *           the backward (Q, K, V, the merged O and the attention state), or
+ *           NULL in a forward that needs no backward (they then go to `ws`).
+ *   ws    : la_layer_workspace_size() bytes of device scratch (it covers
+ *           both passes and the no-saved forward; rocBLAS takes its scratch
+ *           from here too, so the calls allocate nothing).
+ * Errors as for la_forward.  B*N == 0 or C == 0 is a no-op; H == 0 with
+ * C > 0 is LA_ERR_SHAPE.
+ */
+size_t la_layer_saved_size(int64_t B, int64_t N, int64_t C, int64_t H,
+                           int64_t D, int causal, int dtype);
+size_t la_layer_workspace_size(int64_t B, int64_t N, int64_t C, int64_t H,
+                               int64_t D, int causal, int dtype);
+int la_layer_forward(const void *X, const void *Wqkv, const void *Wo, void *Y,
+                     int64_t B, int64_t N, int64_t C, int64_t H, int64_t D,
+                     int causal, int dtype, void *saved, void *ws,
+                     size_t ws_bytes, void *stream);
+/* dX, dWqkv, dWo: gradients of L = sum dY . Y (overwritten). */
+int la_layer_backward(const void *X, const void *Wqkv, const void *Wo,
+                      const void *dY, void *dX, void *dWqkv, void *dWo,
+                      int64_t B, int64_t N, int64_t C, int64_t H, int64_t D,
+                      int causal, int dtype, const void *saved, void *ws,
+                      size_t ws_bytes, void *stream);
 
 /*
  * Kernel-level timing (benchmarks, profilers).  Same arguments and behaviour

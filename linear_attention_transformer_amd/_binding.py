@@ -66,6 +66,16 @@ def load_library():
     lib.la_backward_segment.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ci,
                                         ci, vp, i64, vp, vp, vp, vp, sz, vp]
     lib.la_backward_segment.restype = ci
+    lib.la_layer_saved_size.argtypes = [i64, i64, i64, i64, i64, ci, ci]
+    lib.la_layer_saved_size.restype = sz
+    lib.la_layer_workspace_size.argtypes = [i64, i64, i64, i64, i64, ci, ci]
+    lib.la_layer_workspace_size.restype = sz
+    lib.la_layer_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ci, ci, vp, vp,
+                                     sz, vp]
+    lib.la_layer_forward.restype = ci
+    lib.la_layer_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ci,
+                                      ci, vp, vp, sz, vp]
+    lib.la_layer_backward.restype = ci
     lib.la_decode_step.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp, vp, vp, i64, vp, vp]
     lib.la_decode_step.restype = ci
     ev, ip, cpp = ctypes.c_void_p, ctypes.POINTER(ci), ctypes.POINTER(ctypes.c_char_p)
@@ -333,6 +343,69 @@ def decode_step(q, k, v, state_in=None, *, state_out=None, counts=None, n_prev: 
     if rc != 0:
         raise LAError(rc, "la_decode_step")
     return o, den, state_out
+
+
+def _layer_dims(x, wqkv, wo, H):
+    for t in (x, wqkv, wo):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != x.dtype or t.device != x.device:
+            raise ValueError("layer tensors must be contiguous, on one GPU, of one dtype")
+    if x.dim() != 3:
+        raise ValueError("x must be [B, N, C]")
+    B, N, C = x.shape
+    if wqkv.dim() != 2 or wqkv.shape[0] != C or wqkv.shape[1] % (3 * H) != 0:
+        raise ValueError("wqkv must be [C, 3*H*D]")
+    D = wqkv.shape[1] // (3 * H)
+    if tuple(wo.shape) != (H * D, C):
+        raise ValueError("wo must be [H*D, C]")
+    return B, N, C, D, _dtype_code(x)
+
+
+def layer_sizes(B, N, C, H, D, causal=False, dtype=torch.float32):
+    """(saved bytes, workspace bytes) of the layer calls."""
+    lib = load_library()
+    dt, c = _dtype_of(dtype), int(bool(causal))
+    return (int(lib.la_layer_saved_size(B, N, C, H, D, c, dt)),
+            int(lib.la_layer_workspace_size(B, N, C, H, D, c, dt)))
+
+
+def layer_forward(x, wqkv, wo, H: int, causal: bool = False, *, saved=None, out=None,
+                  workspace=None, save: bool = True):
+    """Y = one linear-attention layer (la_layer_forward).  Returns (Y, saved)
+    with `saved` the buffer the backward needs (None when save=False)."""
+    B, N, C, D, dt = _layer_dims(x, wqkv, wo, H)
+    lib = load_library()
+    sb, wb = layer_sizes(B, N, C, H, D, causal, x.dtype)
+    if saved is None and save:
+        saved = torch.empty(max(sb, 16), dtype=torch.uint8, device=x.device)
+    ws = torch.empty(max(wb, 16), dtype=torch.uint8, device=x.device) if workspace is None \
+        else workspace
+    y = torch.empty_like(x) if out is None else out
+    rc = lib.la_layer_forward(_ptr(x), _ptr(wqkv), _ptr(wo), _ptr(y), B, N, C, H, D,
+                              int(bool(causal)), dt, _ptr(saved), _ptr(ws), ws.numel(),
+                              _stream(x.device))
+    if rc != 0:
+        raise LAError(rc, "la_layer_forward")
+    return y, saved
+
+
+def layer_backward(x, wqkv, wo, dy, H: int, causal: bool = False, *, saved, outs=None,
+                   workspace=None):
+    """(dX, dWqkv, dWo) of L = sum dY . Y (la_layer_backward)."""
+    B, N, C, D, dt = _layer_dims(x, wqkv, wo, H)
+    if dy.shape != x.shape or dy.dtype != x.dtype or not dy.is_contiguous():
+        raise ValueError("dy must match x")
+    lib = load_library()
+    _, wb = layer_sizes(B, N, C, H, D, causal, x.dtype)
+    ws = torch.empty(max(wb, 16), dtype=torch.uint8, device=x.device) if workspace is None \
+        else workspace
+    dx, dwqkv, dwo = (torch.empty_like(x), torch.empty_like(wqkv), torch.empty_like(wo)) \
+        if outs is None else outs
+    rc = lib.la_layer_backward(_ptr(x), _ptr(wqkv), _ptr(wo), _ptr(dy), _ptr(dx), _ptr(dwqkv),
+                               _ptr(dwo), B, N, C, H, D, int(bool(causal)), dt, _ptr(saved),
+                               _ptr(ws), ws.numel(), _stream(x.device))
+    if rc != 0:
+        raise LAError(rc, "la_layer_backward")
+    return dx, dwqkv, dwo
 
 
 class LinearAttention(torch.autograd.Function):

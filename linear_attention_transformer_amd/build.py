@@ -1,6 +1,7 @@
 """Build the HIP library in-tree: linear_attention_transformer_amd/liblinattn.so.
 
-Compiles csrc/la_api.hip (which includes the kernels) for gfx950 with hipcc.
+Compiles csrc/la_api.hip (which includes the kernels) and csrc/la_layer.hip
+(the layer around them; its projections call rocBLAS) for gfx950 with hipcc.
 Packed fp32 VALU instructions are disabled for the device code.
 """
 from __future__ import annotations
@@ -11,7 +12,7 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "la_api.hip")
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("la_api.hip", "la_layer.hip")]
 LIB = os.path.join(PKG, "liblinattn.so")
 ARCH = "gfx950"
 
@@ -32,7 +33,7 @@ def build(verbose: bool = False) -> str:
            # kernels are both accumulators and A operands, and the AGPR form
            # would keep a copy of them in each register file
            "-mllvm", "-amdgpu-mfma-vgpr-form",
-           "-o", tmp, SRC]
+           "-o", tmp] + SRCS + ["-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass warns that it does not know the device feature; drop that
     noise = "-packed-fp32-ops' is not a recognized feature"

@@ -49,3 +49,27 @@ def make_inputs(B: int, H: int, N: int, D: int, *, dtype=torch.float32,
 def as_f64_numpy(t: torch.Tensor):
     """Exact fp64 copy of a stored tensor, as a numpy array."""
     return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def make_layer_inputs(B: int, N: int, C: int, H: int, D: int, *, dtype=torch.float32,
+                      seed: int = 0, device="cpu"):
+    """Return (x, wqkv, wo, dy) for one attention layer, drawn in that order
+    from one CPU generator seeded with ``seed`` (fp32 randn, then scaled):
+
+    * x [B, N, C] and dy [B, N, C]: standard normal;
+    * wqkv [C, 3*H*D]: the query and key columns scaled by 1/sqrt(C*D), so
+      that queries and keys have the N(0, 1/D) entries of the head-batch
+      recipe above; the value columns by 1/sqrt(C);
+    * wo [H*D, C]: scaled by 1/sqrt(H*D);
+
+    then ``.to(dtype)`` (round to nearest even) on ``device``."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    HD = H * D
+    x = torch.randn((B, N, C), generator=gen)
+    wqkv = torch.randn((C, 3 * HD), generator=gen)
+    wqkv[:, :2 * HD] /= math.sqrt(C * D)
+    wqkv[:, 2 * HD:] /= math.sqrt(C)
+    wo = torch.randn((HD, C), generator=gen) / math.sqrt(HD)
+    dy = torch.randn((B, N, C), generator=gen)
+    return tuple(t.to(device=device, dtype=dtype).contiguous() for t in (x, wqkv, wo, dy))

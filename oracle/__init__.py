@@ -4,8 +4,10 @@ TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
 CPU-baseline leg may import this package; the product path (the HIP library
 and its Python binding) never does.  It shares no code with the HIP path.
 
-The arithmetic lives in ``la_oracle.c`` (plain C, fp64).  This module only
-builds it with gcc, loads it with ctypes and marshals numpy arrays.  See the
+The attention arithmetic lives in ``la_oracle.c`` (plain C, fp64).  This
+module builds it with gcc, loads it with ctypes and marshals numpy arrays; the
+only arithmetic here is the layer around the attention (``layer_forward`` /
+``layer_backward``), whose projections are fp64 numpy matrix products.  See the
 header of ``la_oracle.c`` for what is computed and which passage of the pages
 each step follows ("Transformer Based Linear Attention with Optimized GPU
 Kernel Implementation": TL;DR and Figure 1 caption on the sciencestack.ai page;
@@ -186,6 +188,51 @@ def backward_carry(q, k, v, g, causal=False, rec_in=None, n0=0, grec_in=None):
     None.  Returns (dQ, dK, dV, grec_out) with grec_out = grec_in plus the
     piece's own rows' record."""
     return _backward_carry(q, k, v, g, causal, rec_in, n0, grec_in)
+
+
+def _split_heads(t, H, D):
+    B, N, _ = t.shape
+    return np.ascontiguousarray(t.reshape(B, N, H, D).transpose(0, 2, 1, 3))
+
+
+def _merge_heads(t):
+    B, H, N, D = t.shape
+    return np.ascontiguousarray(t.transpose(0, 2, 1, 3).reshape(B, N, H * D))
+
+
+def layer_forward(x, wqkv, wo, H, D, causal=False):
+    """One linear-attention layer (cloud.baidu.com article, method outline:
+    the input rows pass through a linear map, linear attention forms the
+    context rows, a further map follows; the plainest reading is a query /
+    key / value projection and an output projection without biases):
+    [Q | K | V] = X Wqkv, O_h = LA(Q_h, K_h, V_h), Y = [O_1 .. O_H] Wo.
+    x [B, N, C], wqkv [C, 3HD], wo [HD, C]; returns Y [B, N, C] in fp64."""
+    x, wqkv, wo = (np.asarray(a, dtype=np.float64) for a in (x, wqkv, wo))
+    HD = H * D
+    qkv = np.matmul(x, wqkv)
+    q, k, v = (_split_heads(qkv[..., j * HD:(j + 1) * HD], H, D) for j in range(3))
+    o, _ = forward_state(q, k, v, causal)
+    return np.matmul(_merge_heads(o), wo)
+
+
+def layer_backward(x, wqkv, wo, dy, H, D, causal=False):
+    """Gradients of L = sum dY . Y for layer_forward, by the chain rule
+    through the two products and the attention's own backward:
+    dWo = O^T dY, dO = dY Wo^T, (dQ, dK, dV) = LA backward, dWqkv = X^T dQKV,
+    dX = dQKV Wqkv^T (sums over the batch).  Returns (dX, dWqkv, dWo)."""
+    x, wqkv, wo, dy = (np.asarray(a, dtype=np.float64) for a in (x, wqkv, wo, dy))
+    HD = H * D
+    qkv = np.matmul(x, wqkv)
+    q, k, v = (_split_heads(qkv[..., j * HD:(j + 1) * HD], H, D) for j in range(3))
+    o, _ = forward_state(q, k, v, causal)
+    orows = _merge_heads(o)
+    dwo = np.einsum("bni,bnc->ic", orows, dy)
+    do = _split_heads(np.matmul(dy, wo.T), H, D)
+    dq, dk, dv = backward_state(q, k, v, do, causal)
+    dqkv = np.concatenate([_merge_heads(t) for t in (dq, dk, dv)], axis=-1)
+    dwqkv = np.einsum("bnc,bnj->cj", x, dqkv)
+    dx = np.matmul(dqkv, wqkv.T)
+    return dx, dwqkv, dwo
 
 
 def max_threads() -> int:
