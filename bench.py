@@ -157,6 +157,53 @@ def pmc_summary(fetch_dir, write_dir, args):
         json.dump(doc, f, indent=1, sort_keys=True)
 
 
+COUNTERS = ("SQ_BUSY_CU_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F32 "
+            "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU "
+            "GRBM_GUI_ACTIVE")
+
+
+def counter_summary(pmc_dir, args):
+    """Per-launch matrix-core and instruction counts of the library's kernels
+    from one rocprofv3 --pmc run of this script with COUNTERS (no GPU work).
+    MOPS count MFMA work in units of 512 flops; the MFMA busy fraction is
+    SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE (summed over the 8 XCDs)
+    times the 1024 SIMDs."""
+    import collections
+    import csv
+    import glob
+    import statistics as st
+    f = glob.glob(os.path.join(pmc_dir, "*counter_collection.csv"))[0]
+    by = collections.defaultdict(lambda: collections.defaultdict(list))
+    dur = collections.defaultdict(dict)
+    for r in csv.DictReader(open(f)):
+        n = r["Kernel_Name"]
+        if "la::" not in n:
+            continue
+        name = launch_name(n.split("(")[0].replace("void ", ""))
+        by[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        dur[name][r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    s = 4 if args.dtype == "fp32" else 2
+    B, H, N, D = args.B, args.H, args.N, args.D
+    fused = "grad_state_local" not in by
+    print("| kernel | us | MFMA instr | MOPS x 512 / algorithmic flops | MFMA busy | "
+          "VALU (non-MFMA) / MFMA | LDS / MFMA | SALU / MFMA | TFLOP/s |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for name, c in by.items():
+        m = {k: st.mean(v) for k, v in c.items()}
+        t = st.mean(dur[name].values()) * 1e-9
+        mops = m.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0) + m.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0)
+        flops, _ = algorithmic(name, B * H, N, D, s, fused)
+        mf = m.get("SQ_INSTS_MFMA", 0)
+        g = m.get("GRBM_GUI_ACTIVE", 0) / 8
+        per = lambda k: (m.get(k, 0) / mf) if mf else float("nan")  # noqa: E731
+        print("| %s | %.1f | %.3g | %s | %s | %.2f | %.2f | %.2f | %s |" % (
+            name, t * 1e6, mf, "%.3f" % (mops * 512 / flops) if flops else "-",
+            "%.3f" % (m.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) / (g * 1024)) if g else "-",
+            (m.get("SQ_INSTS_VALU", 0) - mf) / mf if mf else float("nan"),
+            per("SQ_INSTS_LDS"), per("SQ_INSTS_SALU"),
+            "%.1f" % (mops * 512 / t / 1e12) if t else "-"))
+
+
 def copy_reference(dev):
     """Bandwidth of a plain streaming kernel (torch.neg over COPY_MIB fp32,
     read once and written once): the achievable-HBM reference, and the
@@ -394,6 +441,10 @@ def main():
     ap.add_argument("--pieces", type=int, default=4,
                     help="also time the causal step of this shape and storage streamed as "
                          "this many pieces through the carried-state calls (0 = skip)")
+    ap.add_argument("--counter-summary", metavar="PMC_DIR",
+                    help="summarise one rocprofv3 --pmc run of this script with the counters "
+                         "of COUNTERS (matrix-core work and busy cycles, VALU, LDS and SALU "
+                         "instructions per kernel) as a markdown table; no GPU work")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs of this script (FETCH_SIZE, "
                          "WRITE_SIZE) for the given workload into profiles/traffic.json; "
@@ -401,6 +452,9 @@ def main():
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary, args)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
