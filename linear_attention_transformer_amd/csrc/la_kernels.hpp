@@ -45,22 +45,57 @@ __device__ __forceinline__ f4 mma(float a, float b, f4 c)
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float wave_sum(float v)
+// Lane-group sums without the LDS crossbar: DPP moves within rows of 16
+// lanes (quad_perm [1,0,3,2] and [2,3,0,1], then the half-row and row
+// mirrors), v_permlane16_swap between rows 2r and 2r+1, v_permlane32_swap
+// between the wave's halves.  group_sum<N> sums aligned groups of N lanes
+// (N = 1..64, a power of two) and leaves the sum in every lane of the group.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        v += __shfl_xor(v, o, 64);
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// v + (the same register of lane l ^ 16), i.e. the sum of rows 2r, 2r+1
+__device__ __forceinline__ float swap16_sum(float v)
+{
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// v + (the same register of lane l ^ 32)
+__device__ __forceinline__ float swap32_sum(float v)
+{
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+template <int N>
+__device__ __forceinline__ float group_sum(float v)
+{
+    static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "power-of-two group");
+    if constexpr (N >= 2)
+        v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+    if constexpr (N >= 4)
+        v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+    if constexpr (N >= 8)
+        v += dpp_mov<0x141>(v);  // row_half_mirror
+    if constexpr (N >= 16)
+        v += dpp_mov<0x140>(v);  // row_mirror
+    if constexpr (N >= 32)
+        v = swap16_sum(v);
+    if constexpr (N >= 64)
+        v = swap32_sum(v);
     return v;
 }
 
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
+
 // sum over the 16 lanes that share l/16
-__device__ __forceinline__ float group16_sum(float v)
-{
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1)
-        v += __shfl_xor(v, o, 64);
-    return v;
-}
+__device__ __forceinline__ float group16_sum(float v) { return group_sum<16>(v); }
 
 // ------------------------------------------------------------ storage types
 struct StF32 {

@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
                 p += dot4(f4{af[0], af[1], af[2], af[3]}, *reinterpret_cast<const f4 *>(br)) +
                      dot4(f4{af[4], af[5], af[6], af[7]}, *reinterpret_cast<const f4 *>(br + 4));
             }
-            return p + __shfl_xor(p, 32, 64);
+            return swap32_sum(p);
         };
         if constexpr (KIND == 0) {
             const float p = rowdot(&xs[buf][(32 * rg + j) * LDX], vz);  // q.z
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
                      __uint_as_float(u.y << 16) * acc[4 * q + 2] +
                      __uint_as_float(u.y & 0xffff0000u) * acc[4 * q + 3];
             }
-            p += __shfl_xor(p, 32, 64);
+            p = swap32_sum(p);
             p += rowdot(&xs[buf][(32 * rg + j) * LDX], vu);               // g.u
             const float pz = rowdot(&qs[buf][(32 * rg + j) * LDX], vz);  // q.z
             if (h == 0) {
@@ -573,11 +573,8 @@ __global__ __launch_bounds__(256) void k_reduce_bf(
         const int q = tid + p * NT;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-#pragma unroll
-            for (int o = 1; o < TT / 2; o <<= 1) {
-                cx[p][s] += __shfl_xor(cx[p][s], o, 64);
-                cy[p][s] += __shfl_xor(cy[p][s], o, 64);
-            }
+            cx[p][s] = group_sum<TT / 2>(cx[p][s]);
+            cy[p][s] = group_sum<TT / 2>(cy[p][s]);
         }
         if ((PC % NT == 0 || q < PC) && q % (TT / 2) == 0) {
             const int chunk = q / (TT / 2);
@@ -847,7 +844,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal_bf(
                 p += dot4(f4{xf[0], xf[1], xf[2], xf[3]}, *reinterpret_cast<const f4 *>(zr)) +
                      dot4(f4{xf[4], xf[5], xf[6], xf[7]}, *reinterpret_cast<const f4 *>(zr + 4));
             }
-            p += __shfl_xor(p, 32, 64);
+            p = swap32_sum(p);
             if (h == 0)
                 qzx[cb][j] = p;
 #pragma unroll
@@ -911,9 +908,9 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal_bf(
             uc = sum8(vcol, uc);
             __builtin_amdgcn_sched_barrier(0);
         }
-        rs += __shfl_xor(rs, 32, 64);
-        zc += __shfl_xor(zc, 32, 64);
-        uc += __shfl_xor(uc, 32, 64);
+        rs = swap32_sum(rs);
+        zc = swap32_sum(zc);
+        uc = swap32_sum(uc);
         float qz = 0.f;
 #pragma unroll
         for (int c2 = 0; c2 < NCB; ++c2)
@@ -1087,8 +1084,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
                       __uint_as_float(u.y & 0xffff0000u) * acc[4 * q + 3];
             }
             pq += gu;
-            pq += __shfl_xor(pq, 32, 64);
-            qz += __shfl_xor(qz, 32, 64);
+            pq = swap32_sum(pq);
+            qz = swap32_sum(qz);
             if (h == 0) {
                 xq[cb][j] = pq;
                 xz[cb][j] = qz;
@@ -1117,8 +1114,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
                 cw += wm * gv;
                 gvk[kk][s2] = m ? gv : 0.f;
             }
-        rs += __shfl_xor(rs, 32, 64);
-        cw += __shfl_xor(cw, 32, 64);
+        rs = swap32_sum(rs);
+        cw = swap32_sum(cw);
         float qyu = 0.f, qzs = 0.f;  // q.y + g.u and q.z over all columns
 #pragma unroll
         for (int pp = 0; pp < NCB; ++pp) {
@@ -1154,8 +1151,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
             zc = sum8(kcol, zc);
             __builtin_amdgcn_sched_barrier(0);
         }
-        zc += __shfl_xor(zc, 32, 64);
-        uc += __shfl_xor(uc, 32, 64);
+        zc = swap32_sum(zc);
+        uc = swap32_sum(uc);
         // (4) dq rows (z of the rows before the chunk)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1348,7 +1345,7 @@ __device__ __forceinline__ void kv_pass_bf(
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        vc += __shfl_xor(vc, 32, 64);
+        vc = swap32_sum(vc);
         // (4) rows of dK (- r) or dV (+ t) with the vector of the rows after
         // the chunk
         const float sg = (PAR == 0) ? -1.f : 1.f;

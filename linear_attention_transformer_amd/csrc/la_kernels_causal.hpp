@@ -246,10 +246,10 @@ __global__ __launch_bounds__(threads<D>()) void k_fwd_causal(
             uc += vb;
             __builtin_amdgcn_sched_barrier(0);
         }
-        rs += __shfl_xor(rs, 32, 64);
-        zc += __shfl_xor(zc, 32, 64);
-        uc += __shfl_xor(uc, 32, 64);
-        qz += __shfl_xor(qz, 32, 64);
+        rs = swap32_sum(rs);
+        zc = swap32_sum(zc);
+        uc = swap32_sum(uc);
+        qz = swap32_sum(qz);
         // (4) normalised rows of the chunk, stored during the next product
         const float den = (n0 + (float)t0) + qz + rs;
         const float inv = 1.f / den;
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(threads<D>()) void k_bwd_q_causal(
                 p += qv[0] * acc[4 * q] + qv[1] * acc[4 * q + 1] + qv[2] * acc[4 * q + 2] +
                      qv[3] * acc[4 * q + 3];
             }
-            p += __shfl_xor(p, 32, 64);
+            p = swap32_sum(p);
             if (h == 0)
                 xq[cb][j] = p;
         }
@@ -436,10 +436,10 @@ __global__ __launch_bounds__(threads<D>()) void k_bwd_q_causal(
             cw += wm * gv;
             gvk[kk] = m ? gv : 0.f;
         }
-        rs += __shfl_xor(rs, 32, 64);
-        cw += __shfl_xor(cw, 32, 64);
-        gu += __shfl_xor(gu, 32, 64);
-        qz += __shfl_xor(qz, 32, 64);
+        rs = swap32_sum(rs);
+        cw = swap32_sum(cw);
+        gu = swap32_sum(gu);
+        qz = swap32_sum(qz);
         float qy = 0.f;
 #pragma unroll
         for (int p = 0; p < NCB; ++p)
@@ -465,8 +465,8 @@ __global__ __launch_bounds__(threads<D>()) void k_bwd_q_causal(
             zc += kv;
             __builtin_amdgcn_sched_barrier(0);
         }
-        zc += __shfl_xor(zc, 32, 64);
-        uc += __shfl_xor(uc, 32, 64);
+        zc = swap32_sum(zc);
+        uc = swap32_sum(uc);
         // (4) dq rows (z of the rows before the chunk), stored during the next
         // product
 #pragma unroll
@@ -661,7 +661,7 @@ __device__ __forceinline__ void kv_pass(
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        vc += __shfl_xor(vc, 32, 64);
+        vc = swap32_sum(vc);
         // (4) rows of dK (- r) or dV (+ t) with the vector of the rows after
         // the chunk (stored here: the next chunk's product covers them)
         const float sg = (PAR == 0) ? -1.f : 1.f;

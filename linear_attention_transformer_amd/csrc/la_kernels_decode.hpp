@@ -90,11 +90,8 @@ __global__ __launch_bounds__(kThreads) void k_decode(
             qk += q * ld1<ST>(K + io + d);
             qz += has_in ? q * r[D * D + d] : 0.f;
         }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            qk += __shfl_xor(qk, o, 64);
-            qz += __shfl_xor(qz, o, 64);
-        }
+        qk = wave_sum(qk);
+        qz = wave_sum(qz);
         if (tid == 0) {
             dots[0] = qk;
             dots[1] = qz;
@@ -186,11 +183,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_any(
             qk += q * ld1<ST>(K + io + d);
             qz += has_in ? q * r[(int64_t)D * D + d] : 0.f;
         }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            qk += __shfl_xor(qk, o, 64);
-            qz += __shfl_xor(qz, o, 64);
-        }
+        qk = wave_sum(qk);
+        qz = wave_sum(qz);
         if (tid == 0) {
             dots[0] = qk;
             dots[1] = qz;

@@ -95,9 +95,7 @@ __device__ __forceinline__ float dot4(f4 a, f4 b)
 // sum over the four lane groups (lanes with equal l % 16)
 __device__ __forceinline__ float lg_sum(float v)
 {
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    return v;
+    return swap32_sum(swap16_sum(v));
 }
 
 constexpr int kReduceThreads = 256;
@@ -338,8 +336,8 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce_nc(
     }
 #pragma unroll
     for (int a = 0; a < VW; ++a) {
-        csx[a] += __shfl_xor(csx[a], 32, 64);
-        csy[a] += __shfl_xor(csy[a], 32, 64);
+        csx[a] = swap32_sum(csx[a]);
+        csy[a] = swap32_sum(csy[a]);
     }
 
     if constexpr (TS > 1) {
@@ -583,7 +581,7 @@ __global__ __launch_bounds__(apply_threads<D>()) void k_apply_nc(
 #pragma unroll
             for (int e = 0; e < 16; e += 4)
                 p += dot4(*reinterpret_cast<const f4 *>(qr + e), *reinterpret_cast<const f4 *>(zr + e));
-            p += __shfl_xor(p, 32, 64);
+            p = swap32_sum(p);
             if (h == 0)
                 xch[buf][rg][cb][j] = p;
         } else {
@@ -727,9 +725,7 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
             for (int x = 0; x < VEC; x += 4)
                 pz += dot4(f4{qv[x], qv[x + 1], qv[x + 2], qv[x + 3]},
                            *reinterpret_cast<const f4 *>(zc + x));
-#pragma unroll
-            for (int o = 1; o < CPR; o <<= 1)
-                pz += __shfl_xor(pz, o, 64);
+            pz = group_sum<CPR>(pz);
             const float inv = 1.f / ((n0 + (float)N) + pz);
             if (c % CPR == 0)
                 ivx[buf][c / CPR] = inv;
@@ -799,8 +795,8 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
                     p2 += qv[0] * acc[4 * q] + qv[1] * acc[4 * q + 1] + qv[2] * acc[4 * q + 2] +
                           qv[3] * acc[4 * q + 3];
                 }
-                p0 += __shfl_xor(p0, 32, 64);
-                p2 += __shfl_xor(p2, 32, 64);
+                p0 = swap32_sum(p0);
+                p2 = swap32_sum(p2);
                 if (h == 0) {
                     xch[buf][rg][cb][j][0] = p0;
                     xch[buf][rg][cb][j][1] = p2;
@@ -900,8 +896,8 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
             for (int kk = 0; kk < 16; ++kk)
                 racc += cx[lb][rg][2 * kk + h] * qprev[kk];
         }
-        racc += __shfl_xor(racc, 32, 64);
-        tacc += __shfl_xor(tacc, 32, 64);
+        racc = swap32_sum(racc);
+        tacc = swap32_sum(tacc);
         if (NRG > 1 && rg > 0) {
             float *dst = red + ((rg - 1) * NCB + cb) * PW;
 #pragma unroll
