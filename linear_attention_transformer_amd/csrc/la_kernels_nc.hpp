@@ -258,14 +258,40 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce_nc(
     for (int a = 0; a < VW; ++a)
         csx[a] = csy[a] = 0.f;
 
-    float ra[U][VW], rb[U][VW], rc[U], rs[U];
+    // The ring holds the loaded words as they are (fp32 values, or pairs of
+    // 16-bit elements widened only when consumed, so that no load is waited
+    // for before its slot comes round).
+    constexpr bool WIDE = sizeof(T) == 4;
+    constexpr int RW = WIDE ? VW : 1;
+    typedef typename std::conditional<WIDE, float, uint32_t>::type RT;
+    RT ra[U][RW], rb[U][RW];
+    float rc[U], rs[U];
+    auto raw_load = [&](__amdgpu_buffer_rsrc_t r, int vo, int so, RT *o) {
+        if constexpr (WIDE)
+            buf_load_vec<ST, VW>(r, vo, so, o);
+        else if constexpr (VW == 2)
+            o[0] = __builtin_amdgcn_raw_buffer_load_b32(r, vo, so, 0);
+        else
+            o[0] = __builtin_amdgcn_raw_buffer_load_b16(r, vo, so, 0);
+    };
+    auto widen_slot = [&](const RT *r, float *o) {
+        if constexpr (WIDE) {
+#pragma unroll
+            for (int a = 0; a < VW; ++a)
+                o[a] = r[a];
+        } else if constexpr (VW == 2) {
+            ST::widen2(r[0], o);
+        } else {
+            o[0] = ST::widen1((uint16_t)r[0]);
+        }
+    };
     // Prefetch ring over this wave's complete 2-token steps.  Slots past the
     // last step are fetched (as zeros) but never consumed, so nothing waits on
     // a load before its use.  An odd last token is handled after the loop.
     auto fetch = [&](int u, int s) {
         const int so = __builtin_amdgcn_readfirstlane(s) * (int)(2 * D * sizeof(T));
-        buf_load_vec<ST, VW>(rx, ox, so, ra[u]);
-        buf_load_vec<ST, VW>(ry, oy, so, rb[u]);
+        raw_load(rx, ox, so, ra[u]);
+        raw_load(ry, oy, so, rb[u]);
         if constexpr (GRAD) {
             const float2 cs = __builtin_bit_cast(
                 float2, __builtin_amdgcn_raw_buffer_load_b64(
@@ -303,7 +329,10 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce_nc(
     for (int it = 0; it < full; ++it) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            consume(ra[u], rb[u], GRAD ? rc[u] : 1.f, GRAD ? rs[u] : 1.f);
+            float xa[VW], yb[VW];
+            widen_slot(ra[u], xa);
+            widen_slot(rb[u], yb);
+            consume(xa, yb, GRAD ? rc[u] : 1.f, GRAD ? rs[u] : 1.f);
             fetch(u, tsi + ((it + 1) * U + u) * TS);
             // keep step u's work and its refill together: the scheduler would
             // otherwise sink the refills to the end of the body and hoist the
@@ -313,8 +342,12 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce_nc(
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
-        if (u < mine - full * U)
-            consume(ra[u], rb[u], GRAD ? rc[u] : 1.f, GRAD ? rs[u] : 1.f);
+        if (u < mine - full * U) {
+            float xa[VW], yb[VW];
+            widen_slot(ra[u], xa);
+            widen_slot(rb[u], yb);
+            consume(xa, yb, GRAD ? rc[u] : 1.f, GRAD ? rs[u] : 1.f);
+        }
     if (((end - beg) & 1) && tsi == (int)(npairs % TS)) {
         // last, unpaired token: lane half h = 1 contributes zeros
         const int64_t t = end - 1;
