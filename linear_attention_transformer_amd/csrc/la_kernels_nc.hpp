@@ -667,9 +667,11 @@ __global__ __launch_bounds__(apply_threads<D>()) void k_apply_nc(
 //   role 1 (waves 4-7): dS[:, 32*cb ..] over the round's rows, with
 //                       a_i = g_i / den_i; r needs c_i, which role 0 hands
 //                       over through LDS one round later.
-// Both roles stage the rows (Q and dO, fp32, double-buffered) together,
-// forming 1/den_i of each staged row on the way, and meet at one barrier per
-// round.  With DS = false (D = 256, where a wave of either role needs 128
+// Both roles stage the rows (Q and dO, fp32, double-buffered), forming
+// 1/den_i of each staged row on the way, and meet at one barrier per round:
+// role 1 stages its half of the next round's rows before its MFMA chain and
+// role 0 its half after its own, so that each role's staging runs beside the
+// other role's chain on the SIMD they share.  With DS = false (D = 256, where a wave of either role needs 128
 // registers of state) the workgroup is eight dQ waves only, and it writes
 // (c_i, 1/den_i) to part_out (as cbuf) for k_reduce_nc<GRAD = true>.
 template <class ST, int D, bool DS = true>
@@ -871,6 +873,14 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
             gacc[t] = zero16();
         for (int64_t round = 0; round < nrounds; ++round) {
             const int buf = (int)(round & 1);
+            // this role's half of the next round's rows first (buffer
+            // buf ^ 1 was last read before the previous barrier), while
+            // role 0 runs its chain; role 0 stages its half after its chain
+            if (round + 1 < nrounds) {
+                stage_round(buf ^ 1);
+                if (round + 2 < nrounds)
+                    fetch_round(beg + (round + 2) * TR);
+            }
             // dS[:, block cb] += Q^T A over the tile's rows (k = row; rows
             // 2kk + h per MFMA step), operands one step ahead.  Lane j reads
             // NCB consecutive columns NCB j .. of its q row as one vector:
@@ -896,11 +906,6 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
                     gacc[t] = mma32(a[t], bv, gacc[t]);
                 qcur[kk] = qc[2 * kk * LDX];
                 __builtin_amdgcn_sched_barrier(0);
-            }
-            if (round + 1 < nrounds) {
-                stage_round(buf ^ 1);
-                if (round + 2 < nrounds)
-                    fetch_round(beg + (round + 2) * TR);
             }
             __syncthreads();
             // r += c_i q_i over the previous round's rows (c_i arrived in LDS
