@@ -57,7 +57,7 @@ KERNEL_NAMES = [
     (r"k_bwd_q_nc<|k_apply_bf<\d+, 1>|k_bwd_q_causal|k_bwd_q<", "bwd_q"),
     (r"k_apply_nc<[^>]*, 2>|k_apply_bf<\d+, 2>|k_bwd_kv_causal|k_bwd_kv<", "bwd_kv"),
     (r"k_state_scan", "state_scan"),
-    (r"k_stage", "stage"),
+    (r"k_pad<|k_unpad<|k_stage_record", "stage"),
     (r"k_decode", "decode"),
 ]
 
