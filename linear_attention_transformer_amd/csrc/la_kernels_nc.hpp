@@ -24,6 +24,8 @@
 // MFMA: v_mfma_f32_32x32x2_f32 throughout (layout below).
 #pragma once
 
+#include <type_traits>
+
 #include "la_kernels.hpp"
 
 namespace la {
@@ -433,6 +435,48 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce_nc(
     }
 }
 
+// ============================================================ split products
+// An fp32 value is the exact sum of three bf16 terms, x = hi + mid + lo, each
+// rounded to nearest from what the previous ones leave (8 + 8 + 8 bits of
+// the 24-bit significand; the differences are exact in fp32).  A product of
+// two such values on the bf16 matrix cores keeps the six term products down
+// to 2^-16 of the leading one (hi.hi, hi.mid, mid.hi, hi.lo, lo.hi, mid.mid)
+// and drops the rest, which lie near 2^-24 relative, below fp32 rounding;
+// every term product is exact in the fp32 accumulator.
+typedef __bf16 bf8x __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f16v mma_bf16(bf8x a, bf8x b, f16v c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void split3(const float *x, bf8x &hi, bf8x &mid, bf8x &lo)
+{
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const __bf16 a = (__bf16)x[e];
+        const float r = x[e] - (float)a;
+        const __bf16 b = (__bf16)r;
+        hi[e] = a;
+        mid[e] = b;
+        lo[e] = (__bf16)(r - (float)b);
+    }
+}
+
+// the six term products of a (three planes) and b (three planes), smallest
+// first
+__device__ __forceinline__ f16v mma_split3(const bf8x &a1, const bf8x &a2, const bf8x &a3,
+                                           const bf8x &b1, const bf8x &b2, const bf8x &b3,
+                                           f16v acc)
+{
+    acc = mma_bf16(a2, b2, acc);
+    acc = mma_bf16(a1, b3, acc);
+    acc = mma_bf16(a3, b1, acc);
+    acc = mma_bf16(a1, b2, acc);
+    acc = mma_bf16(a2, b1, acc);
+    return mma_bf16(a1, b1, acc);
+}
+
 // ============================================================ apply
 // A is the MFMA left operand applied to each row x_i of X:
 // KIND 0 forward : A = S^T;  o_i = (u + A q_i) / (N + q_i.z);
@@ -538,21 +582,46 @@ __global__ __launch_bounds__(apply_threads<D>()) void k_apply_nc(
     const int64_t nrounds = (end - beg + TR - 1) / TR;
     fetch_round(beg);
 
-    // this wave's block of A: am[kb][r] = A[32*cb + j][kb*8 + 4*h + r]
-    float am[KB][4];
-    if (colread) {
+    // fp16 storage at D = 128: the products run as split products on the
+    // bf16 matrix cores (the block of A in three bf16 planes: a1[ks][e] + a2
+    // + a3 = A[32*cb + j][16*ks + 8*h + e]), 8% faster per step than on the
+    // fp32 matrix cores.  fp32 storage stays on the fp32 matrix cores: there
+    // the same change gained 2%, and the extra power slowed the neighbouring
+    // fp32 launches.  At D = 256 the planes would not fit in registers; at
+    // D <= 64 the fp32 matrix cores were as fast.
+    constexpr bool X3 = std::is_same<ST, StF16>::value && D == 128;
+    constexpr int KS = D / 16;
+    bf8x a1[X3 ? KS : 1], a2[X3 ? KS : 1], a3[X3 ? KS : 1];
+    if constexpr (X3) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int ks = 0; ks < KS; ++ks) {
+            float v[8];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                am[kb][r] = st[(kb * 8 + 4 * h + r) * D + 32 * cb + j];
-    } else {
+            for (int e = 0; e < 8; ++e) {
+                const int k = 16 * ks + 8 * h + e;
+                v[e] = colread ? st[k * D + 32 * cb + j] : st[(32 * cb + j) * D + k];
+            }
+            split3(v, a1[ks], a2[ks], a3[ks]);
+        }
+    }
+    // else this wave's block of A in fp32: am[kb][r] = A[32*cb + j][kb*8 + 4*h + r]
+    float am[X3 ? 1 : KB][4];
+    if constexpr (!X3) {
+        if (colread) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const f4 v = *reinterpret_cast<const f4 *>(st + (32 * cb + j) * D + kb * 8 + 4 * h);
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                am[kb][r] = v[r];
+                for (int r = 0; r < 4; ++r)
+                    am[kb][r] = st[(kb * 8 + 4 * h + r) * D + 32 * cb + j];
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const f4 v =
+                    *reinterpret_cast<const f4 *>(st + (32 * cb + j) * D + kb * 8 + 4 * h);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    am[kb][r] = v[r];
+            }
         }
     }
     // epilogue vector at the lane's output columns 32*cb + 8*q + 4*h + (0..3):
@@ -585,24 +654,50 @@ __global__ __launch_bounds__(apply_threads<D>()) void k_apply_nc(
 
     for (int64_t round = 0; round < nrounds; ++round) {
         const int buf = (int)(round & 1);
-        const float *xt = &xs[buf][(32 * rg + j) * LDX + 4 * h];
         f16v acc = zero16();
-        // LDS operands one k-block ahead of the MFMAs; the scheduling barrier
-        // per k-block stops the compiler from hoisting every read of the tile
-        f4 xn = *reinterpret_cast<const f4 *>(xt);
+        if constexpr (X3) {
+            // B operand: the tile row's 8 consecutive values 16*ks + 8*h ..,
+            // split into three bf16 planes, one k-step ahead of the MFMAs
+            const float *xt = &xs[buf][(32 * rg + j) * LDX + 8 * h];
+            f4 xn0 = *reinterpret_cast<const f4 *>(xt);
+            f4 xn1 = *reinterpret_cast<const f4 *>(xt + 4);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const f4 x = xn;
-            if (kb + 1 < KB)
-                xn = *reinterpret_cast<const f4 *>(xt + (kb + 1) * 8);
+            for (int ks = 0; ks < KS; ++ks) {
+                const float xv[8] = {xn0[0], xn0[1], xn0[2], xn0[3],
+                                     xn1[0], xn1[1], xn1[2], xn1[3]};
+                if (ks + 1 < KS) {
+                    xn0 = *reinterpret_cast<const f4 *>(xt + (ks + 1) * 16);
+                    xn1 = *reinterpret_cast<const f4 *>(xt + (ks + 1) * 16 + 4);
+                }
+                bf8x b1, b2, b3;
+                split3(xv, b1, b2, b3);
+                acc = mma_split3(a1[ks], a2[ks], a3[ks], b1, b2, b3, acc);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                acc = mma32(am[kb][r], x[r], acc);
+                for (int q = 0; q < 4; ++q)
+                    if (ks == q * (KS / 4))
+                        store_pending(q);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            const float *xt = &xs[buf][(32 * rg + j) * LDX + 4 * h];
+            // LDS operands one k-block ahead of the MFMAs; the scheduling
+            // barrier per k-block stops the compiler from hoisting every read
+            // of the tile
+            f4 xn = *reinterpret_cast<const f4 *>(xt);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if (kb == q * (KB / 4))
-                    store_pending(q);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int kb = 0; kb < KB; ++kb) {
+                const f4 x = xn;
+                if (kb + 1 < KB)
+                    xn = *reinterpret_cast<const f4 *>(xt + (kb + 1) * 8);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc = mma32(am[kb][r], x[r], acc);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (kb == q * (KB / 4))
+                        store_pending(q);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
 
         const int64_t row = beg + round * TR + 32 * rg + j;
@@ -671,9 +766,10 @@ __global__ __launch_bounds__(apply_threads<D>()) void k_apply_nc(
 // 1/den_i of each staged row on the way, and meet at one barrier per round:
 // role 1 stages its half of the next round's rows before its MFMA chain and
 // role 0 its half after its own, so that each role's staging runs beside the
-// other role's chain on the SIMD they share.  With DS = false (D = 256, where a wave of either role needs 128
-// registers of state) the workgroup is eight dQ waves only, and it writes
-// (c_i, 1/den_i) to part_out (as cbuf) for k_reduce_nc<GRAD = true>.
+// other role's chain on the SIMD they share.  With DS = false (D = 256,
+// where a wave of either role needs 128 registers of state) the workgroup is
+// eight dQ waves only, and it writes (c_i, 1/den_i) to part_out (as cbuf)
+// for k_reduce_nc<GRAD = true>.
 template <class ST, int D, bool DS = true>
 __global__ __launch_bounds__(512) void k_bwd_q_nc(
     const typename ST::T *__restrict__ G, const typename ST::T *__restrict__ Q,
@@ -777,16 +873,31 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
     fetch_round(beg);
     for (int e = tid; e < 2 * D; e += NT)
         vl[e] = st[D * D + e];
-    // role 0's block of S: am[kb][r] = S[32*cb + j][kb*8 + 4*h + r] (loaded
-    // by every wave so that the registers are set on every path; dead in
-    // role 1)
-    float am[KB][4];
+    // Role 0's block of S (loaded by every wave so that the registers are
+    // set on every path; dead in role 1).  For fp16 storage at D = 128 (as
+    // in k_apply_nc) its product y = S a runs as split products on the bf16
+    // matrix cores: s1[ks][e] + s2 + s3 = S[32*cb + j][16*ks + 8*h + e];
+    // else in fp32: am[kb][r] = S[32*cb + j][kb*8 + 4*h + r].
+    constexpr bool X3 = DS && std::is_same<ST, StF16>::value && D == 128;
+    constexpr int KS = D / 16;
+    bf8x s1[X3 ? KS : 1], s2[X3 ? KS : 1], s3[X3 ? KS : 1];
+    float am[X3 ? 1 : KB][4];
+    if constexpr (X3) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-        const f4 v = *reinterpret_cast<const f4 *>(st + (32 * cb + j) * D + kb * 8 + 4 * h);
+        for (int ks = 0; ks < KS; ++ks) {
+            const float *p = st + (32 * cb + j) * D + 16 * ks + 8 * h;
+            const f4 v0 = *reinterpret_cast<const f4 *>(p), v1 = *reinterpret_cast<const f4 *>(p + 4);
+            const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+            split3(v, s1[ks], s2[ks], s3[ks]);
+        }
+    } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            am[kb][r] = v[r];
+        for (int kb = 0; kb < KB; ++kb) {
+            const f4 v = *reinterpret_cast<const f4 *>(st + (32 * cb + j) * D + kb * 8 + 4 * h);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                am[kb][r] = v[r];
+        }
     }
     __syncthreads();  // z in LDS before the first staging reads it
     stage_round(0);
@@ -804,18 +915,39 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
             const int64_t row = beg + round * TR + 32 * rg + j;
             // (read before the barrier: the slot is restaged one round later)
             const float inv = ivx[buf][32 * rg + j];
-            const float *xt = &xs[buf][(32 * rg + j) * LDX + 4 * h];
             f16v acc = zero16();
-            f4 xn = *reinterpret_cast<const f4 *>(xt);
+            if constexpr (X3) {
+                // the row of a, 8 values 16*ks + 8*h .. per k-step, split
+                // into three bf16 planes one k-step ahead of the MFMAs
+                const float *xt = &xs[buf][(32 * rg + j) * LDX + 8 * h];
+                f4 xn0 = *reinterpret_cast<const f4 *>(xt);
+                f4 xn1 = *reinterpret_cast<const f4 *>(xt + 4);
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const f4 x = xn;
-                if (kb + 1 < KB)
-                    xn = *reinterpret_cast<const f4 *>(xt + (kb + 1) * 8);
+                for (int ks = 0; ks < KS; ++ks) {
+                    const float xv[8] = {xn0[0], xn0[1], xn0[2], xn0[3],
+                                         xn1[0], xn1[1], xn1[2], xn1[3]};
+                    if (ks + 1 < KS) {
+                        xn0 = *reinterpret_cast<const f4 *>(xt + (ks + 1) * 16);
+                        xn1 = *reinterpret_cast<const f4 *>(xt + (ks + 1) * 16 + 4);
+                    }
+                    bf8x b1, b2, b3;
+                    split3(xv, b1, b2, b3);
+                    acc = mma_split3(s1[ks], s2[ks], s3[ks], b1, b2, b3, acc);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+                const float *xt = &xs[buf][(32 * rg + j) * LDX + 4 * h];
+                f4 xn = *reinterpret_cast<const f4 *>(xt);
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc = mma32(am[kb][r], x[r], acc);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int kb = 0; kb < KB; ++kb) {
+                    const f4 x = xn;
+                    if (kb + 1 < KB)
+                        xn = *reinterpret_cast<const f4 *>(xt + (kb + 1) * 8);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc = mma32(am[kb][r], x[r], acc);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
             // y' = S a in acc; partial a.u and q.y' over this block's columns
             {
