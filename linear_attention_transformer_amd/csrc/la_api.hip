@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <cstring>
 #include <type_traits>
@@ -60,27 +61,28 @@ Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int causal)
 // Workgroups of `kern` (`threads` each) resident on the current device at
 // once: compute units x workgroups per unit.  Both factors are cached (the
 // compute-unit count per device, the occupancy per kernel); 0 if unknown.
+// (Concurrent first calls may both query; they store the same values.)
 template <class K>
 int64_t resident_wgs(K kern, int threads)
 {
-    static int cus[64];
-    static int per_cu = -1;
+    static std::atomic<int> cus[64];
+    static std::atomic<int> per_cu{-1};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return 0;
-    if (cus[dev] == 0) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    int c = cus[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return 0;
-        cus[dev] = v;
+        cus[dev].store(c, std::memory_order_relaxed);
     }
-    if (per_cu < 0) {
-        int v = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kern, threads, 0) != hipSuccess)
+    int o = per_cu.load(std::memory_order_relaxed);
+    if (o < 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, threads, 0) != hipSuccess)
             return 0;
-        per_cu = v;
+        per_cu.store(o, std::memory_order_relaxed);
     }
-    return (int64_t)per_cu * cus[dev];
+    return (int64_t)o * c;
 }
 
 // The plan re-segmented so that one pass of the kernel is a single batch of
