@@ -212,3 +212,48 @@ def test_python_side_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 4, 16)
     with pytest.raises(ValueError):
         la.forward(q, q, q)
+
+
+@needs_no_gpu
+def test_host_validation_layer_calls():
+    """The layer calls reject bad shapes, pointers and workspaces before
+    touching rocBLAS or launching anything."""
+    lib = la.load_library()
+    B, N, C, H, D = 1, 8, 16, 2, 8
+    sb = lib.la_layer_saved_size(B, N, C, H, D, 0, 0)
+    wb = lib.la_layer_workspace_size(B, N, C, H, D, 0, 0)
+    assert sb > 0 and wb > sb
+    assert lib.la_layer_workspace_size(B, N, C, H, 300, 0, 0) == 0
+    assert lib.la_layer_saved_size(B, N, C, H, D, 0, 9) == 0
+    # bf16 needs half the fp32 tensors (plus the fixed rocBLAS scratch)
+    assert lib.la_layer_workspace_size(B, N, C, H, D, 0, 1) < wb
+    buf = (ctypes.c_char * (wb + sb + (1 << 20)))()
+    a16 = (ctypes.addressof(buf) + 255) & ~255
+    P = lambda off=0: ctypes.c_void_p(a16 + off)
+    xb, wq, wo = B * N * C * 4, C * 3 * H * D * 4, H * D * C * 4
+    X, WQ, WO, Y = 0, 4096, 8192, 12288
+    SV, WS = 16384, 16384 + ((sb + 255) // 256) * 256
+    f = lib.la_layer_forward
+
+    def fa(x=P(X), y=P(Y), b=B, n=N, c=C, h=H, d=D, causal=0, dt=0, sv=P(SV), ws=P(WS), wsb=wb):
+        return f(x, P(WQ), P(WO), y, b, n, c, h, d, causal, dt, sv, ws, wsb, None)
+
+    assert fa(dt=7) == 3
+    assert fa(causal=2) == 4 and fa(d=0) == 4 and fa(d=300) == 4
+    assert fa(b=-1) == 2
+    assert fa(h=0) == 2
+    assert fa(x=None) == 1 and fa(ws=None) == 1
+    assert fa(wsb=wb - sb - 1) == 5                 # with a saved buffer
+    assert fa(x=P(X + 4)) == 7
+    assert fa(y=P(X + 16)) == 6                     # Y overlaps X
+    assert fa(b=0) == 0 and fa(c=0) == 0            # empty: nothing to do
+    g = lib.la_layer_backward
+
+    def ga(dx=P(X + xb + 1024), sv=P(SV), wsb=wb):
+        return g(P(X), P(WQ), P(WO), P(Y), dx, P(WS + wb), P(WS + wb + wq + 256), B, N, C, H, D,
+                 0, 0, sv, P(WS), wsb, None)
+
+    assert ga(sv=None) == 1
+    assert ga(wsb=1024) == 5
+    assert ga(dx=P(Y)) == 6                         # dX overlaps dY
+    assert xb <= 4096 and wq <= 4096 and wo <= 4096
