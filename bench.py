@@ -459,7 +459,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures the linear-attention hot path on one GPU "
+        print("bench.py: the library measures the linear-attention hot path on one GPU "
               "(heads shard across GPUs with no communication); --gpus %d is not "
               "supported" % max(args.gpus, world), file=sys.stderr)
         sys.exit(2)
