@@ -204,6 +204,49 @@ def counter_summary(pmc_dir, args):
             "%.1f" % (mops * 512 / t / 1e12) if t else "-"))
 
 
+LDS_COUNTERS = ("SQ_LDS_BANK_CONFLICT SQ_LDS_ADDR_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS "
+                "SQ_WAIT_INST_LDS SQ_LDS_MEM_VIOLATIONS SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE")
+
+
+def lds_summary(pmc_dir, args):
+    """Per-launch LDS counters of the library's kernels from one rocprofv3
+    --pmc run of this script with LDS_COUNTERS (no GPU work): bank-conflict
+    stall cycles over the cycles the LDS did useful indexed work
+    (SQ_LDS_BANK_CONFLICT / (SQ_LDS_IDX_ACTIVE - SQ_LDS_BANK_CONFLICT)), the
+    LDS busy fraction (SQ_LDS_IDX_ACTIVE over GRBM_GUI_ACTIVE / 8 cycles of
+    one XCD times 256 compute units), address-conflict cycles, issue-wait
+    cycles per LDS instruction (SQ_WAIT_INST_LDS counts 4-cycle units) and
+    the LDS memory violations (0 when every access is in range)."""
+    import collections
+    import csv
+    import glob
+    import statistics as st
+    f = glob.glob(os.path.join(pmc_dir, "*counter_collection.csv"))[0]
+    by = collections.defaultdict(lambda: collections.defaultdict(list))
+    dur = collections.defaultdict(dict)
+    for r in csv.DictReader(open(f)):
+        n = r["Kernel_Name"]
+        if "la::" not in n:
+            continue
+        name = launch_name(n.split("(")[0].replace("void ", ""))
+        by[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        dur[name][r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    print("| kernel | us | LDS instr | bank-conflict / useful LDS cycles | LDS busy | "
+          "address-conflict cycles | wait cycles per LDS instr | LDS violations |")
+    print("|---|---|---|---|---|---|---|---|")
+    for name, c in by.items():
+        m = {k: st.mean(v) for k, v in c.items()}
+        t = st.mean(dur[name].values()) * 1e-9
+        bank, idx = m.get("SQ_LDS_BANK_CONFLICT", 0), m.get("SQ_LDS_IDX_ACTIVE", 0)
+        g = m.get("GRBM_GUI_ACTIVE", 0) / 8
+        ni = m.get("SQ_INSTS_LDS", 0)
+        print("| %s | %.1f | %.3g | %s | %s | %.3g | %s | %d |" % (
+            name, t * 1e6, ni, "%.3f" % (bank / (idx - bank)) if idx > bank else "-",
+            "%.3f" % (idx / (g * 256)) if g else "-", m.get("SQ_LDS_ADDR_CONFLICT", 0),
+            "%.2f" % (4 * m.get("SQ_WAIT_INST_LDS", 0) / ni) if ni else "-",
+            int(sum(c.get("SQ_LDS_MEM_VIOLATIONS", [0])))))
+
+
 def copy_reference(dev):
     """Bandwidth of a plain streaming kernel (torch.neg over COPY_MIB fp32,
     read once and written once): the achievable-HBM reference, and the
@@ -445,6 +488,10 @@ def main():
                     help="summarise one rocprofv3 --pmc run of this script with the counters "
                          "of COUNTERS (matrix-core work and busy cycles, VALU, LDS and SALU "
                          "instructions per kernel) as a markdown table; no GPU work")
+    ap.add_argument("--lds-summary", metavar="PMC_DIR",
+                    help="summarise one rocprofv3 --pmc run of this script with the counters "
+                         "of LDS_COUNTERS (bank and address conflicts, LDS busy, issue waits) "
+                         "as a markdown table; no GPU work")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs of this script (FETCH_SIZE, "
                          "WRITE_SIZE) for the given workload into profiles/traffic.json; "
@@ -455,6 +502,9 @@ def main():
         return
     if args.counter_summary:
         counter_summary(args.counter_summary, args)
+        return
+    if args.lds_summary:
+        lds_summary(args.lds_summary, args)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

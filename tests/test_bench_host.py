@@ -112,3 +112,21 @@ def test_counter_summary_ratios(tmp_path, capsys):
     assert cells[3] == "1.000"                 # matrix work = algorithmic
     assert cells[4] == "0.500"                 # busy half of the SIMD cycles
     assert cells[5] == "2.00" and cells[6] == "0.50" and cells[7] == "0.25"
+
+
+def test_lds_summary_ratios(tmp_path, capsys):
+    """Bank-conflict cycles over the useful LDS cycles, LDS busy over the
+    cycles of one XCD times 256 compute units, wait cycles per LDS
+    instruction in 4-cycle units."""
+    k = "void la::nc::k_bwd_q_nc<la::StF32, 128, true>(float const*)"
+    vals = {"SQ_LDS_BANK_CONFLICT": 100.0, "SQ_LDS_ADDR_CONFLICT": 7.0,
+            "SQ_LDS_IDX_ACTIVE": 500.0, "SQ_INSTS_LDS": 50.0, "SQ_WAIT_INST_LDS": 25.0,
+            "SQ_LDS_MEM_VIOLATIONS": 0.0, "SQ_BUSY_CU_CYCLES": 1.0,
+            "GRBM_GUI_ACTIVE": 8 * 1000 / 256 * 4}
+    _write_counters(str(tmp_path / "l"), [(k, c, v, 0, 100_000) for c, v in vals.items()])
+    bench.lds_summary(str(tmp_path / "l"), _args())
+    row = [l for l in capsys.readouterr().out.splitlines() if l.startswith("| bwd_q")][0]
+    cells = [c.strip() for c in row.strip("|").split("|")]
+    assert cells[3] == "0.250"                 # 100 / (500 - 100)
+    assert cells[4] == "0.125"                 # 500 / (1000 / 256 * 4 * 256)
+    assert cells[6] == "2.00" and cells[7] == "0"
