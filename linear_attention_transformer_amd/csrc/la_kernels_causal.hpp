@@ -11,10 +11,10 @@
 // suffix of the gradient records).  For every chunk:
 //   - the running state is applied to the chunk's rows (an MFMA product
 //     over D, as in the non-causal kernels);
-//   - the masked in-chunk block is formed densely: each wave contributes the
-//     share of a C x C product (Q K^T or dO V^T) over its 32 columns of D,
-//     the shares meet in LDS, and the block is applied with one more MFMA
-//     over the chunk's rows;
+//   - the masked in-chunk block is formed densely: the C x C product (Q K^T
+//     or dO V^T) is split into 16 x 16 tiles over all of D, spread over the
+//     waves, written once to LDS, and applied with one more MFMA over the
+//     chunk's rows;
 //   - the running state is updated by the chunk (an MFMA over its rows).
 //
 // Wave cb of a workgroup owns output columns 32 cb .. 32 cb + 31 and the
@@ -27,7 +27,7 @@
 // state is applied and updated in place without leaving the registers.
 //
 // Rows are staged in LDS as fp32 from a register prefetch of the next chunk.
-// Three barriers per chunk: after the shares are written (B1), after the
+// Three barriers per chunk: after the product tiles are written (B1), after the
 // last read of the chunk's rows (B2) and after the next chunk is staged
 // (B3).  Tensors read only before B1 are restaged right after it, so at most
 // two tensors' prefetch registers are live at a time.
@@ -96,27 +96,90 @@ struct Rows {
     }
 };
 
-// this wave's share of X_c Y_c^T over columns 32 cb .. 32 cb + 31 of D,
-// written to sh[i * WP + jj] (i: row of X, jj: row of Y)
+// Q_c K_c^T into wx and G_c V_c^T into gx (sh[i * WP + jj]; i: row of the
+// first factor, jj: row of the second), each whole over the D columns, as
+// eight 16 x 16 tiles (v_mfma_f32_16x16x4_f32) spread over the NCB waves:
+// one copy of each product in LDS.  Lane
+// (g = lane / 16, r = lane % 16) reads columns 16 s + 4 g .. + 3 of row r of
+// a tile as one vector and supplies component c at MFMA step 4 s + c; both
+// factors use the same order of the columns, so their sum is unchanged.
+// Output element v of the lane sits at tile row 4 g + v, tile column r.
 template <int D>
-__device__ __forceinline__ void share_xyT(const float *xs, const float *ys, float *sh, int cb,
-                                          int j, int h)
+__device__ __forceinline__ void tiles_xyT(const float *qs, const float *ks, const float *gs,
+                                          const float *vs, float *wx, float *gx, int cb,
+                                          int lane)
 {
-    constexpr int LDX = D + 4, WP = kC + 1;
-    f16v a = zero16();
-    const float *xa = xs + j * LDX + 32 * cb + 4 * h;
-    const float *ya = ys + j * LDX + 32 * cb + 4 * h;
+    constexpr int NCB = D / 32, LDX = D + 4, WP = kC + 1, PER = 8 / NCB;
+    static_assert(PER % 2 == 0 || PER == 1, "tiles per wave");
+    constexpr int GRP = PER >= 2 ? 2 : 1;  // tiles in flight together
+    const int r = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        const f4 x = *reinterpret_cast<const f4 *>(xa + 8 * kb);
-        const f4 y = *reinterpret_cast<const f4 *>(ya + 8 * kb);
+    for (int k0 = 0; k0 < PER; k0 += GRP) {
+        const float *xa[GRP], *ya[GRP];
+        float *dst[GRP];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            a = mma32(x[r], y[r], a);
+        for (int u = 0; u < GRP; ++u) {
+            const int tt = cb * PER + k0 + u;  // 0..3: Q K^T tiles, 4..7: G V^T
+            const int ti = (tt >> 1) & 1, tj = tt & 1;
+            xa[u] = (tt < 4 ? qs : gs) + (16 * ti + r) * LDX + 4 * g;
+            ya[u] = (tt < 4 ? ks : vs) + (16 * tj + r) * LDX + 4 * g;
+            dst[u] = (tt < 4 ? wx : gx) + (16 * ti + 4 * g) * WP + 16 * tj + r;
+        }
+        f4 a[GRP];
+#pragma unroll
+        for (int u = 0; u < GRP; ++u)
+            a[u] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) {
+            f4 x[GRP], y[GRP];
+#pragma unroll
+            for (int u = 0; u < GRP; ++u) {
+                x[u] = *reinterpret_cast<const f4 *>(xa[u] + 16 * st);
+                y[u] = *reinterpret_cast<const f4 *>(ya[u] + 16 * st);
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int u = 0; u < GRP; ++u)
+                    a[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[u][c], y[u][c], a[u], 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < GRP; ++u)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                dst[u][v * WP] = a[u][v];
     }
+}
+
+// X_c Y_c^T into sh (as above, one product): its four 16 x 16 tiles spread
+// over the NCB waves; a wave with a single tile runs its k-steps as two
+// independent chains (even and odd column groups) and adds them at the end.
+template <int D>
+__device__ __forceinline__ void tile_xyT(const float *xs, const float *ys, float *sh, int cb,
+                                         int lane)
+{
+    constexpr int NCB = D / 32, LDX = D + 4, WP = kC + 1, PER = 4 / NCB, NST = D / 16;
+    const int r = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-        sh[(8 * (e / 4) + 4 * h + (e % 4)) * WP + j] = a[e];
+    for (int k = 0; k < PER; ++k) {
+        const int tt = cb * PER + k;
+        const int ti = tt >> 1, tj = tt & 1;
+        const float *xa = xs + (16 * ti + r) * LDX + 4 * g;
+        const float *ya = ys + (16 * tj + r) * LDX + 4 * g;
+        f4 a[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+            const f4 x = *reinterpret_cast<const f4 *>(xa + 16 * st);
+            const f4 y = *reinterpret_cast<const f4 *>(ya + 16 * st);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                a[st & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[c], y[c], a[st & 1], 0, 0, 0);
+        }
+        float *dst = sh + (16 * ti + 4 * g) * WP + 16 * tj + r;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            dst[v * WP] = a[0][v] + a[1][v];
+    }
 }
 
 // ============================================================ forward
@@ -138,7 +201,7 @@ __global__ __launch_bounds__(threads<D>()) void k_fwd_causal(
     __shared__ __attribute__((aligned(16))) float qs[kC * LDX];
     __shared__ __attribute__((aligned(16))) float ks[kC * LDX];
     __shared__ __attribute__((aligned(16))) float vs[kC * LDX];
-    __shared__ float wx[NCB][kC * WP];
+    __shared__ float wx[kC * WP];  // Q_c K_c^T
     __shared__ __attribute__((aligned(16))) float vz[D];
     __shared__ __attribute__((aligned(16))) float vu[D];
 
@@ -214,8 +277,8 @@ __global__ __launch_bounds__(threads<D>()) void k_fwd_causal(
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // (2) this wave's share of Q_c K_c^T
-        share_xyT<D>(qs, ks, wx[cb], cb, j, h);
+        // (2) this wave's tiles of Q_c K_c^T
+        tile_xyT<D>(qs, ks, wx, cb, lane);
         __syncthreads();  // B1
         if (more) {
             rq.stage(qs, tid);
@@ -229,10 +292,7 @@ __global__ __launch_bounds__(threads<D>()) void k_fwd_causal(
         for (int kk = 0; kk < kC / 2; ++kk) {
             const int jr = 2 * kk + h;
             const float vb = vs[jr * LDX + 32 * cb + j];
-            float wsum = 0.f;
-#pragma unroll
-            for (int p = 0; p < NCB; ++p)
-                wsum += wx[p][j * WP + jr];
+            const float wsum = wx[j * WP + jr];
             const float wm = (jr <= j) ? 1.f + wsum : 0.f;
             rs += wm;
             acc = mma32(vb, wm, acc);
@@ -305,8 +365,8 @@ __global__ __launch_bounds__(threads<D>()) void k_bwd_q_causal(
     __shared__ __attribute__((aligned(16))) float ks[kC * LDX];
     __shared__ __attribute__((aligned(16))) float vs[kC * LDX];
     __shared__ __attribute__((aligned(16))) float gs[kC * LDX];
-    __shared__ float wx[NCB][kC * WP];  // shares of Q_c K_c^T
-    __shared__ float gx[NCB][kC * WP];  // shares of G_c V_c^T
+    __shared__ float wx[kC * WP];       // Q_c K_c^T
+    __shared__ float gx[kC * WP];       // G_c V_c^T
     __shared__ float xq[NCB][kC];       // shares of q_i.y_i
     __shared__ __attribute__((aligned(16))) float vz[D];
     __shared__ __attribute__((aligned(16))) float vu[D];
@@ -395,9 +455,9 @@ __global__ __launch_bounds__(threads<D>()) void k_bwd_q_causal(
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // (2) shares of Q_c K_c^T, G_c V_c^T and q.y over this wave's columns
-        share_xyT<D>(qs, ks, wx[cb], cb, j, h);
-        share_xyT<D>(gs, vs, gx[cb], cb, j, h);
+        // (2) Q_c K_c^T and G_c V_c^T (whole tiles), q.y over this wave's
+        // columns
+        tiles_xyT<D>(qs, ks, gs, vs, wx, gx, cb, lane);
         {
             float p = 0.f;
 #pragma unroll
@@ -424,12 +484,7 @@ __global__ __launch_bounds__(threads<D>()) void k_bwd_q_causal(
 #pragma unroll
         for (int kk = 0; kk < kC / 2; ++kk) {
             const int jr = 2 * kk + h;
-            float w = 0.f, gv = 0.f;
-#pragma unroll
-            for (int p = 0; p < NCB; ++p) {
-                w += wx[p][j * WP + jr];
-                gv += gx[p][j * WP + jr];
-            }
+            const float w = wx[j * WP + jr], gv = gx[j * WP + jr];
             const bool m = jr <= j;
             const float wm = m ? 1.f + w : 0.f;
             rs += wm;
@@ -506,8 +561,7 @@ __global__ __launch_bounds__(threads<D>()) void k_bwd_q_causal(
 //   dv_j = t + R^T k_j + sum_i (1 + q_i.k_j) a_i,
 // a_i = g_i / den_i and (c_i, 1 / den_i) from cbuf; then (R, r, t) += the
 // chunk's rows.  Workgroup parity 0 computes dK (st[t] = R^T[32t.., 32cb..],
-// shares of G_c V_c^T), parity 1 computes dV (st[t] = R[32t.., 32cb..],
-// shares of Q_c K_c^T).
+// G_c V_c^T), parity 1 computes dV (st[t] = R[32t.., 32cb..], Q_c K_c^T).
 // LDS of the dK | dV pass
 template <int D>
 struct KvLds {
@@ -515,7 +569,7 @@ struct KvLds {
     float xs[kC * LDX];    // V (dK) or K (dV)
     float qs[kC * LDX];
     float gs[kC * LDX];
-    float sh[NCB][kC * WP];
+    float sh[kC * WP];     // G_c V_c^T (dK) or Q_c K_c^T (dV)
     float cs[kC], is[kC];  // c_i, 1/den_i of the chunk's rows
     float vr[D];           // r (dK) or t (dV)
 };
@@ -610,11 +664,11 @@ __device__ __forceinline__ void kv_pass(
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // (2) shares: G_c V_c^T (dK; xs holds V) or Q_c K_c^T (dV; xs holds K)
+        // (2) G_c V_c^T (dK; xs holds V) or Q_c K_c^T (dV; xs holds K)
         if constexpr (PAR == 0)
-            share_xyT<D>(gs, xs, sh[cb], cb, j, h);
+            tile_xyT<D>(gs, xs, sh, cb, lane);
         else
-            share_xyT<D>(qs, xs, sh[cb], cb, j, h);
+            tile_xyT<D>(qs, xs, sh, cb, lane);
         __syncthreads();  // B1
         if (more) {
             rx.stage(xs, tid);
@@ -629,10 +683,7 @@ __device__ __forceinline__ void kv_pass(
 #pragma unroll
             for (int kk = 0; kk < kC / 2; ++kk) {
                 const int ir = 2 * kk + h;
-                float s = 0.f;
-#pragma unroll
-                for (int p = 0; p < NCB; ++p)
-                    s += sh[p][ir * WP + j];
+                const float s = sh[ir * WP + j];
                 const float ci = cs[ir], ii = is[ir];
                 const float pm = (ir >= j) ? s * ii - ci : 0.f;
                 const float qb = qs[ir * LDX + 32 * cb + j];
@@ -647,10 +698,7 @@ __device__ __forceinline__ void kv_pass(
 #pragma unroll
             for (int kk = 0; kk < kC / 2; ++kk) {
                 const int ir = 2 * kk + h;
-                float s = 0.f;
-#pragma unroll
-                for (int p = 0; p < NCB; ++p)
-                    s += sh[p][ir * WP + j];
+                const float s = sh[ir * WP + j];
                 const float wm = (ir >= j) ? 1.f + s : 0.f;
                 const float ab = gs[ir * LDX + 32 * cb + j] * is[ir];
                 acc = mma32(ab, wm, acc);
