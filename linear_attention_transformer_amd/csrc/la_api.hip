@@ -58,12 +58,13 @@ Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int causal)
     return p;
 }
 
-// Workgroups of `kern` (`threads` each) resident on the current device at
-// once: compute units x workgroups per unit.  Both factors are cached (the
-// compute-unit count per device, the occupancy per kernel); 0 if unknown.
-// (Concurrent first calls may both query; they store the same values.)
-template <class K>
-int64_t resident_wgs(K kern, int threads)
+// Workgroups of kernel KERN (`threads` each) resident on the current device
+// at once: compute units x workgroups per unit.  Both factors are cached (the
+// compute-unit count per device, the occupancy per kernel: one cache per
+// instantiation, i.e. per kernel); 0 if unknown.  (Concurrent first calls
+// may both query; they store the same values.)
+template <auto KERN>
+int64_t resident_wgs(int threads)
 {
     static std::atomic<int> cus[64];
     static std::atomic<int> per_cu{-1};
@@ -78,7 +79,7 @@ int64_t resident_wgs(K kern, int threads)
     }
     int o = per_cu.load(std::memory_order_relaxed);
     if (o < 0) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, threads, 0) != hipSuccess)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, KERN, threads, 0) != hipSuccess)
             return 0;
         per_cu.store(o, std::memory_order_relaxed);
     }
@@ -99,6 +100,24 @@ Plan one_batch(const Plan &p, int64_t resident)
     const int64_t nchunks = std::max<int64_t>((p.N + kSegAlign - 1) / kSegAlign, 1);
     const int64_t per = (nchunks + want - 1) / want;
     q.seg_len = per * kSegAlign;
+    q.nseg = std::max<int64_t>((p.N + q.seg_len - 1) / q.seg_len, 1);
+    return q;
+}
+
+// The plan re-segmented so that a launch of `per` workgroups per segment and
+// head fills `resident` slots in one batch, for a kernel whose workgroups
+// read only the head's total state (no record per segment): more or fewer
+// segments than the plan's are both fine.
+Plan rows_plan(const Plan &p, int64_t resident, int64_t per)
+{
+    if (resident <= 0)
+        return p;
+    Plan q = p;
+    const int64_t want = std::max<int64_t>(resident / (per * std::max<int64_t>(p.BH, 1)), 1);
+    const int64_t nchunks = std::max<int64_t>((p.N + kSegAlign - 1) / kSegAlign, 1);
+    const int64_t ns = std::min(want, nchunks);
+    const int64_t each = (nchunks + ns - 1) / ns;
+    q.seg_len = each * kSegAlign;
     q.nseg = std::max<int64_t>((p.N + q.seg_len - 1) / q.seg_len, 1);
     return q;
 }
@@ -315,11 +334,14 @@ int run_forward(const void *Q, const void *K, const void *V, void *O, float *den
                                            dim3(bf::kApplyThreads), 0, s>>>(
                         static_cast<const T *>(Q), nullptr, static_cast<T *>(O), nullptr,
                         den_out, nullptr, rec, p.N, p.seg_len, (int)p.nseg, p.n0);
-                else
-                    nc::k_apply_nc<ST, D, 0><<<dim3((unsigned)(p.nseg * p.BH)),
+                else {
+                    const Plan pf = rows_plan(
+                        p, resident_wgs<nc::k_apply_nc<ST, D, 0>>(nc::kApplyThreads), 1);
+                    nc::k_apply_nc<ST, D, 0><<<dim3((unsigned)(pf.nseg * pf.BH)),
                                                dim3(nc::kApplyThreads), 0, s>>>(
                         static_cast<const T *>(Q), nullptr, static_cast<T *>(O), nullptr,
-                        den_out, rec, p.N, p.seg_len, (int)p.nseg, p.n0);
+                        den_out, rec, pf.N, pf.seg_len, (int)pf.nseg, pf.n0);
+                }
             });
         return traced(t, s, "forward", [&] {
             if constexpr (std::is_same<ST, StBF16>::value)
@@ -476,7 +498,7 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
         } else {
             // dQ and the segment's gradient record in one pass over Q and dO,
             // its segments sized for one batch of resident workgroups
-            const Plan pq = one_batch(p, resident_wgs(nc::k_bwd_q_nc<ST, D>, 512));
+            const Plan pq = one_batch(p, resident_wgs<nc::k_bwd_q_nc<ST, D>>(512));
             rc = traced(t, s, "bwd_q", [&] {
                 nc::k_bwd_q_nc<ST, D><<<dim3((unsigned)(pq.nseg * pq.BH)), dim3(512), 0, s>>>(
                     g, q, static_cast<T *>(dQ), gpart, fstate, pq.N, pq.seg_len, (int)pq.nseg,
@@ -500,11 +522,14 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
                                        dim3(bf::kApplyThreads), 0, s>>>(
                     v, k, static_cast<T *>(dK), static_cast<T *>(dV), nullptr, nullptr,
                     ws + l.gtot, p.N, p.seg_len, (int)p.nseg, p.n0);
-            else
-                nc::k_apply_nc<ST, D, 2><<<dim3((unsigned)(2 * p.nseg * p.BH)),
+            else {
+                const Plan pk =
+                    rows_plan(p, resident_wgs<nc::k_apply_nc<ST, D, 2>>(nc::kApplyThreads), 2);
+                nc::k_apply_nc<ST, D, 2><<<dim3((unsigned)(2 * pk.nseg * pk.BH)),
                                            dim3(nc::kApplyThreads), 0, s>>>(
-                    v, k, static_cast<T *>(dK), static_cast<T *>(dV), nullptr, ws + l.gtot, p.N,
-                    p.seg_len, (int)p.nseg, p.n0);
+                    v, k, static_cast<T *>(dK), static_cast<T *>(dV), nullptr, ws + l.gtot, pk.N,
+                    pk.seg_len, (int)pk.nseg, pk.n0);
+            }
         });
     }
     rc = traced(t, s, "bwd_q", [&] {
