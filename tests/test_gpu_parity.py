@@ -141,6 +141,18 @@ def test_multichunk_segments(causal, dtype):
     compare(1, 4, 9000, 64, dtype, causal, seed=5)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("D", [32, 128])
+def test_many_heads_one_segment_each(D, dtype, causal):
+    """640 heads, more than the 512 workgroups a launch aims at: every head
+    is one segment, and so are the launches sized to the resident
+    workgroups.  A ragged N; heads at both ends and in the middle checked."""
+    m = la()
+    assert m.num_segments(8, 80, 300, D) == 1
+    compare(8, 80, 300, D, dtype, causal, heads=[0, 1, 319, 638, 639], seed=D + 7)
+
+
 # ------------------------------------------------------------- full sizes
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
