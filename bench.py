@@ -283,9 +283,69 @@ def step_floor_us(B, H, N, D, s, bf16_mfma):
     return 1e6 * max(flops / (peak * 1e12), nbytes / (PEAK_HBM_GBS * 1e9))
 
 
+FLUSH_MIB = 512                 # scratch written between flushed steps (> 256 MB MALL)
+
+
+def measure(fn, steps, warmup, flush=None):
+    """Time `steps` calls of fn.  Unflushed: the calls back to back between
+    two device synchronisations, with an event before each call and after
+    the last, so one region gives the mean (total / steps) and the median of
+    the per-call times.  Flushed (when `flush`, a device buffer, is given):
+    each call preceded by a write of the whole buffer, which evicts the
+    inputs from the L2 caches and the MALL, and timed between its own two
+    events.  Returns a dict of ms."""
+    import statistics
+    import torch
+    for _ in range(warmup):
+        fn()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(steps):
+        fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    out = {"mean": ev[0].elapsed_time(ev[-1]) / steps, "median": statistics.median(per)}
+    if flush is not None:
+        a = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        b = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            flush.fill_(float(i & 7))
+            a[i].record()
+            fn()
+            b[i].record()
+        torch.cuda.synchronize()
+        per = [a[i].elapsed_time(b[i]) for i in range(steps)]
+        out["flushed_mean"] = sum(per) / steps
+        out["flushed_median"] = statistics.median(per)
+    return out
+
+
+def pass_floor_us(kind, B, H, N, D, s, bf16_mfma):
+    """Roofline time of the forward (4ND^2 flops, 4ND*s bytes per head) or
+    the backward (8ND^2, 7ND*s) alone."""
+    f, b = {"forward": (4, 4), "backward": (8, 7)}[kind]
+    flops, nbytes = f * B * H * N * D * D, b * B * H * N * D * s
+    peak = PEAK_BF16_MFMA_TFLOPS if bf16_mfma else PEAK_FP32_MFMA_TFLOPS
+    return 1e6 * max(flops / (peak * 1e12), nbytes / (PEAK_HBM_GBS * 1e9))
+
+
+def fp16_step_floor_us(B, H, N, D):
+    """Roofline time of the fp16-storage step at 32 <= D <= 128 non-causal,
+    priced on the arithmetic it runs: the two segment reductions (S and dS,
+    2ND^2 each) on the fp32 matrix cores; the forward apply, the dQ role and
+    dK | dV (8ND^2 in all) as split products, six bf16 matrix products per
+    fp32 product; against 11ND*2 bytes at the HBM peak."""
+    nd2 = B * H * N * D * D
+    t_mfma = 4 * nd2 / (PEAK_FP32_MFMA_TFLOPS * 1e12) + 6 * 8 * nd2 / (PEAK_BF16_MFMA_TFLOPS * 1e12)
+    return 1e6 * max(t_mfma, 11 * B * H * N * D * 2 / (PEAK_HBM_GBS * 1e9))
+
+
 def time_variant(la, make_inputs, dev, B, H, N, D, dtype, causal, steps, warmup):
     """ms per fwd+bwd step of another storage type / mask at the same shape
-    (same protocol as the headline: warm-up, then steps between two events)."""
+    (same protocol as the headline: warm-up, then the steps back to back)."""
     import torch
     q, k, v, g = make_inputs(B, H, N, D, dtype=dtype, seed=0, device=dev, draw_device=dev)
     o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
@@ -297,16 +357,7 @@ def time_variant(la, make_inputs, dev, B, H, N, D, dtype, causal, steps, warmup)
         la.forward(q, k, v, causal, out=o, state_out=st, workspace=ws)
         la.backward(q, k, v, g, causal, state=st, outs=(dq, dk, dv), workspace=ws)
 
-    for _ in range(warmup):
-        step()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    return measure(step, steps, warmup)
 
 
 def time_pieces(la, make_inputs, dev, B, H, N, D, dtype, pieces, steps, warmup):
@@ -433,6 +484,18 @@ def time_layer(la, dev, B, N, H, D, dtype, causal, steps, warmup):
     return ms, flops
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (as lscpu reports it)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(q, k, v, g, causal):
     import oracle
     from linear_attention_transformer_amd.inputs import as_f64_numpy
@@ -454,6 +517,7 @@ def cpu_baseline(q, k, v, g, causal):
     dt = sorted(times)[len(times) // 2]
     tokens = B * N * heads / BH
     return {"value": tokens / dt, "unit": "tokens/s", "cores": oracle.max_threads(),
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
             "kind": "oracle",
             "sample": "fp64 C oracle (state form, OpenMP over heads), forward+backward "
                       "of %d of the %d heads at N=%d D=%d; median of %d runs, %.2f s "
@@ -470,6 +534,9 @@ def main():
     # (measured: ~0.8 ms/step over the first 20 fp32 steps, ~0.50 ms/step
     # from about step 60 on), so the untimed warm-up is long by default
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--settle-s", type=float, default=0.5,
+                    help="before the warm-up steps, run steps untimed for this long so the "
+                         "GPU reaches its loaded clocks (reported as clock_settle)")
     ap.add_argument("--dtype", choices=("fp32", "bf16", "fp16"), default="fp32",
                     help="storage dtype of Q, K, V, O and gradients (arithmetic is fp32; "
                          "fp16 storage is staged through fp32 buffers)")
@@ -540,8 +607,15 @@ def main():
         la.forward(q, k, v, causal, out=o, state_out=st, workspace=ws, trace=tf)
         la.backward(q, k, v, g, causal, state=st, outs=(dq, dk, dv), workspace=ws, trace=tb)
 
-    for _ in range(args.warmup):
+    # clock settle: untimed steps for a fixed wall time (synchronised every
+    # 16 steps, so the host does not run far ahead), then the warm-up steps
+    settle_steps = 0
+    t_end = time.perf_counter() + max(args.settle_s, 0.0)
+    while time.perf_counter() < t_end:
         step()
+        settle_steps += 1
+        if settle_steps % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     # device memory of the step: the 8 I/O tensors plus the library's
     # workspace and saved state (everything the caller allocates for it)
@@ -549,20 +623,21 @@ def main():
            "io_tensors": 8 * q.numel() * q.element_size(),
            "workspace": ws.numel(), "saved_state": st.numel() * 4}
 
-    # timed region 1: the headline, nothing but the K steps
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    # timed region 1: the headline, nothing but the K steps (after the W
+    # warm-up steps), back to back between two synchronisations
     w0 = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
+    head = measure(step, args.steps, args.warmup)
     wall = time.perf_counter() - w0
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = head["mean"]
     tokens_per_s = B * N / (ms * 1e-3)
-    print("bench: %.3f ms/step (wall %.3f ms/step), %.1f M tokens/s"
-          % (ms, wall * 1e3 / args.steps, tokens_per_s / 1e6), file=sys.stderr, flush=True)
+    print("bench: %.3f ms/step (median %.3f; wall incl. warm-up %.3f ms/step), %.1f M tokens/s"
+          % (ms, head["median"], wall * 1e3 / (args.steps + args.warmup), tokens_per_s / 1e6),
+          file=sys.stderr, flush=True)
+    # the same steps with the L2 caches and the MALL flushed before each
+    flush = torch.empty((FLUSH_MIB << 20) // 4, dtype=torch.float32, device=dev)
+    fl = measure(step, args.steps, 0, flush=flush)
+    print("bench: flushed %.3f ms/step (median %.3f)" % (fl["flushed_mean"], fl["flushed_median"]),
+          file=sys.stderr, flush=True)
 
     # timed region 2: the same K steps with per-launch events
     traces = [(la.KernelTrace(dev), la.KernelTrace(dev)) for _ in range(args.steps)]
@@ -606,8 +681,38 @@ def main():
                 "kernel_avg_us": round(avg_us[dom], 2),
                 "algorithmic_per_launch": {"flops": flops, "bytes": nbytes}}
     floor_us = step_floor_us(B, H, N, D, s, bf16_mfma)
+    if args.dtype == "fp16" and 32 <= D <= 128 and not causal:
+        floor_us = fp16_step_floor_us(B, H, N, D)
+    # the step's own fraction beside the dominant kernel's
+    roofline["step"] = {"floor_us": round(floor_us, 1), "frac": round(floor_us / (ms * 1e3), 4)}
     print("bench: per-kernel us/launch " + ", ".join("%s=%.1f" % kv for kv in avg_us.items()),
           file=sys.stderr, flush=True)
+
+    # the forward and the backward alone, both masks, same storage; each
+    # against its own floor, unflushed and flushed
+    passes = {}
+    if not args.no_variants:
+        for pc in (False, True):
+            pws = la.alloc_workspace(B, H, N, D, pc, dev, dt)
+            pst = torch.empty(max(la.state_size(B, H, N, D, pc) // 4, 4), dtype=torch.float32,
+                              device=dev)
+            la.forward(q, k, v, pc, out=o, state_out=pst, workspace=pws)
+            fns = {"forward": lambda: la.forward(q, k, v, pc, out=o, state_out=pst,
+                                                 workspace=pws),
+                   "backward": lambda: la.backward(q, k, v, g, pc, state=pst,
+                                                   outs=(dq, dk, dv), workspace=pws)}
+            for kind, fn in fns.items():
+                r = measure(fn, args.steps, args.warmup, flush=flush)
+                pf = pass_floor_us(kind, B, H, N, D, s, bf16_mfma)
+                passes["%s %s" % (kind, "causal" if pc else "non-causal")] = {
+                    "ms": round(r["mean"], 4), "ms_median": round(r["median"], 4),
+                    "ms_flushed_median": round(r["flushed_median"], 4),
+                    "tokens_per_s": round(B * N / (r["mean"] * 1e-3), 1),
+                    "floor_us": round(pf, 1), "frac": round(pf / (r["mean"] * 1e3), 4)}
+                print("bench: %s %s alone: %.3f ms (flushed %.3f), %.2f of its floor"
+                      % (kind, "causal" if pc else "non-causal", r["mean"], r["flushed_median"],
+                         pf / (r["mean"] * 1e3)), file=sys.stderr, flush=True)
+            del pws, pst
 
     # the other storage type and mask at the same shape, each timed like the
     # headline (bf16 storage runs on the bf16 matrix cores for 32 <= D <= 128)
@@ -615,20 +720,29 @@ def main():
     if not args.no_variants:
         del o, dq, dk, dv, ws, st
         torch.cuda.empty_cache()
-        for vdt in ("fp32", "bf16"):
-            for vc in (False, True):
-                if vdt == args.dtype and vc == causal:
-                    continue
-                tdt = torch.float32 if vdt == "fp32" else torch.bfloat16
-                vms = time_variant(la, make_inputs, dev, B, H, N, D, tdt, vc,
-                                   max(args.steps // 2, 5), args.warmup)
-                vs = 4 if vdt == "fp32" else 2
-                fl = step_floor_us(B, H, N, D, vs, uses_bf16_mfma(vdt, D, vc))
-                variants["%s %s" % (vdt, "causal" if vc else "non-causal")] = {
-                    "ms_per_step": round(vms, 4), "tokens_per_s": round(B * N / (vms * 1e-3), 1),
-                    "step_floor_us": round(fl, 1), "step_frac": round(fl / (vms * 1e3), 4)}
-                print("bench: variant %s %s: %.3f ms/step" % (vdt, "causal" if vc else
-                      "non-causal", vms), file=sys.stderr, flush=True)
+        combos = [(vdt, vc) for vdt in ("fp32", "bf16") for vc in (False, True)]
+        combos.append(("fp16", False))
+        for vdt, vc in combos:
+            if vdt == args.dtype and vc == causal:
+                continue
+            tdt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[vdt]
+            r = time_variant(la, make_inputs, dev, B, H, N, D, tdt, vc, args.steps,
+                             args.warmup)
+            vms = r["mean"]
+            vs = 4 if vdt == "fp32" else 2
+            if vdt == "fp16" and 32 <= D <= 128 and not vc:
+                vfl, basis = fp16_step_floor_us(B, H, N, D), "fp32 + split-bf16 matrix cores"
+            else:
+                bm = uses_bf16_mfma(vdt, D, vc)
+                vfl = step_floor_us(B, H, N, D, vs, bm)
+                basis = "bf16 matrix cores / HBM" if bm else "fp32 matrix cores / HBM"
+            variants["%s %s" % (vdt, "causal" if vc else "non-causal")] = {
+                "ms_per_step": round(vms, 4), "ms_median": round(r["median"], 4),
+                "tokens_per_s": round(B * N / (vms * 1e-3), 1),
+                "step_floor_us": round(vfl, 1), "step_frac": round(vfl / (vms * 1e3), 4),
+                "floor_basis": basis}
+            print("bench: variant %s %s: %.3f ms/step" % (vdt, "causal" if vc else
+                  "non-causal", vms), file=sys.stderr, flush=True)
 
     # the causal step streamed in pieces through the carried-state calls,
     # against the same step over the whole sequence
@@ -637,12 +751,12 @@ def main():
         torch.cuda.empty_cache()
         pms = time_pieces(la, make_inputs, dev, B, H, N, D, dt, args.pieces,
                           max(args.steps // 2, 5), args.warmup)
-        whole = ms if causal else variants["%s causal" % args.dtype]["ms_per_step"]
+        whole = ms if causal else variants.get("%s causal" % args.dtype, {}).get("ms_per_step")
         pieces = {"pieces": args.pieces, "causal": True, "ms_per_step": round(pms, 4),
-                  "whole_sequence_ms_per_step": round(whole, 4),
+                  "whole_sequence_ms_per_step": None if whole is None else round(whole, 4),
                   "tokens_per_s": round(B * N / (pms * 1e-3), 1),
-                  "vs_whole": round(whole / pms, 4)}
-        print("bench: causal %s in %d pieces: %.3f ms/step (whole sequence %.3f)"
+                  "vs_whole": None if whole is None else round(whole / pms, 4)}
+        print("bench: causal %s in %d pieces: %.3f ms/step (whole sequence %s)"
               % (args.dtype, args.pieces, pms, whole), file=sys.stderr, flush=True)
 
     # one whole layer around the attention (projections on rocBLAS)
@@ -707,6 +821,12 @@ def main():
         "cpu_baseline": cpu,
         "step_roofline": {"floor_us": round(floor_us, 1),
                           "frac": round(floor_us / (ms * 1e3), 4)},
+        "ms_per_step_median": round(head["median"], 4),
+        "flushed": {"ms_per_step": round(fl["flushed_mean"], 4),
+                    "ms_per_step_median": round(fl["flushed_median"], 4),
+                    "scratch_written_MiB": FLUSH_MIB},
+        "clock_settle": {"seconds": args.settle_s, "steps": settle_steps},
+        "passes": passes,
         "kernels_us_per_launch": {n: round(t, 2) for n, t in avg_us.items()},
         "traced_ms_per_step": round(traced_ms, 4),
         "hbm_copy_GBs": round(copy_gbs, 1),

@@ -50,7 +50,9 @@
  *  - Kernels are enqueued on `stream` (a hipStream_t; NULL = default
  *    stream).  The call does not synchronise.  A failed launch returns
  *    LA_ERR_HIP; faults inside kernels surface at the caller's next
- *    synchronisation.
+ *    synchronisation.  An error that earlier HIP calls on the thread left
+ *    pending (hipPeekAtLastError) is not taken for the call's own: the call
+ *    launches nothing and returns LA_ERR_HIP_PENDING, leaving it pending.
  *  - Results are deterministic: the same inputs give bit-identical outputs
  *    on every call (fixed-order reductions, no floating-point atomics).
  *  - The library keeps no mutable global state apart from device facts it
@@ -79,7 +81,11 @@ typedef enum {
     LA_ERR_WORKSPACE = 5,   /* workspace smaller than la_workspace_size() */
     LA_ERR_ALIAS = 6,       /* an output overlaps an input or another output */
     LA_ERR_ALIGN = 7,       /* a device pointer is not 16-byte aligned */
-    LA_ERR_HIP = 8          /* a HIP launch failed */
+    LA_ERR_HIP = 8,         /* a HIP launch failed */
+    LA_ERR_HIP_PENDING = 9  /* an error from earlier HIP work on this thread
+                               was pending at the first launch: nothing was
+                               launched, and that error is left pending for
+                               the code that caused it */
 } la_status;
 
 typedef enum { LA_FP32 = 0, LA_BF16 = 1, LA_FP16 = 2 } la_dtype;
@@ -264,9 +270,10 @@ int la_decode_step(const void *q, const void *k, const void *v, void *o,
                    void *stream);
 
 /*
- * One linear-attention layer (the method outline of the cloud.baidu.com
- * article: the input rows pass through a linear map, linear attention forms
- * the context rows, which are processed further; here a second linear map).
+ * One linear-attention layer (the technical-framework paragraph, 技术框架, of
+ * the shd-paper.top digest: the input rows pass through a linear map, linear
+ * attention forms the context rows, which are processed further; here a
+ * second linear map).
  * Per sequence, with X [N, C], Wqkv [C, 3*H*D], Wo [H*D, C]:
  *
  *     [Q | K | V] = X Wqkv      column j*H*D + h*D + d of Wqkv feeds element d

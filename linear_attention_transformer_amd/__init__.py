@@ -11,6 +11,7 @@ from ._binding import (KernelTrace, LA_BF16, LA_FP16, LA_FP32, LIB_PATH, NATIVE_
 
 __all__ = ["KernelTrace", "LA_BF16", "LA_FP16", "LA_FP32", "LIB_PATH", "NATIVE_D", "STATUS",
            "SUPPORTED_D", "LAError", "LinearAttention", "alloc_workspace", "backward",
-           "backward_segment", "decode_step", "forward", "forward_segment", "layer_backward",
+           "backward_segment", "decode_step", "forward", "forward_segment",
+           "layer_backward",
            "layer_forward", "layer_sizes", "linear_attention", "load_library", "new_record",
            "num_segments", "record_size", "state_size", "status_string", "workspace_size"]

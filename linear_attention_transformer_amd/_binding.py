@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "liblinattn.so")
 LA_FP32, LA_BF16, LA_FP16 = 0, 1, 2
 STATUS = {0: "LA_OK", 1: "LA_ERR_NULL", 2: "LA_ERR_SHAPE", 3: "LA_ERR_DTYPE",
           4: "LA_ERR_UNSUPPORTED", 5: "LA_ERR_WORKSPACE", 6: "LA_ERR_ALIAS",
-          7: "LA_ERR_ALIGN", 8: "LA_ERR_HIP"}
+          7: "LA_ERR_ALIGN", 8: "LA_ERR_HIP", 9: "LA_ERR_HIP_PENDING"}
 SUPPORTED_D = tuple(range(1, 257))      # every head size the library takes
 NATIVE_D = (32, 64, 128, 256)            # run without padding
 
@@ -127,18 +127,54 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def _check(*ts: torch.Tensor):
+    """Inputs q, k, v (and dO): one shape [B, H, N, D], dtype and device,
+    contiguous.  (The GPU check comes last, in _on_gpu, after every buffer
+    has been checked.)"""
     t0 = ts[0]
     if t0.dim() != 4:
         raise ValueError("expected [B, H, N, D] tensors, got shape %s" % (tuple(t0.shape),))
     for t in ts:
-        if not t.is_cuda:
-            raise ValueError("linear attention runs on the GPU only; got a %s tensor"
-                             % t.device)
         if t.shape != t0.shape or t.dtype != t0.dtype or t.device != t0.device:
             raise ValueError("q, k, v (and dO) must share shape, dtype and device")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous [B, H, N, D]")
     return tuple(t0.shape), _dtype_code(t0)
+
+
+def _on_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("linear attention runs on the GPU only; got a %s tensor"
+                             % t.device)
+
+
+def _check_like(t, like, what):
+    """A caller-supplied output must be exactly like `like`: the library
+    writes as many elements of that dtype as `like` holds."""
+    if t is None:
+        return
+    if (not isinstance(t, torch.Tensor) or t.shape != like.shape or t.dtype != like.dtype
+            or t.device != like.device or not t.is_contiguous()):
+        raise ValueError("%s must be a contiguous %s tensor of shape %s on %s"
+                         % (what, like.dtype, tuple(like.shape), like.device))
+
+
+def _check_bytes(t, nbytes, dev, what, dtype=None):
+    """A caller-supplied buffer of at least `nbytes` bytes on `dev`
+    (contiguous; of `dtype` when given)."""
+    if t is None:
+        return
+    if (not isinstance(t, torch.Tensor) or t.device != dev or not t.is_contiguous()
+            or (dtype is not None and t.dtype != dtype)):
+        raise ValueError("%s must be a contiguous %stensor on %s"
+                         % (what, "" if dtype is None else "%s " % dtype, dev))
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError("%s holds %d bytes; this call needs %d"
+                         % (what, t.numel() * t.element_size(), nbytes))
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
 
 
 def _ptr(t):
@@ -193,15 +229,20 @@ def forward(q, k, v, causal: bool = False, *, return_den: bool = False,
     (B, H, N, D), dt = _check(q, k, v)
     lib = load_library()
     c = int(bool(causal))
+    dev = q.device
+    _check_like(out, q, "out")
+    _check_bytes(state_out, state_size(B, H, N, D, causal), dev, "state_out", torch.float32)
+    _check_bytes(workspace, 0, dev, "workspace")
+    _on_gpu(q, out, state_out, workspace)
     o = torch.empty_like(q) if out is None else out
-    den = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_den else None
+    den = torch.empty((B, H, N), dtype=torch.float32, device=dev) if return_den else None
     state = state_out
     if state is None and save_state:
         state = torch.empty(max(state_size(B, H, N, D, causal) // 4, 4),
-                            dtype=torch.float32, device=q.device)
-    ws = alloc_workspace(B, H, N, D, causal, q.device, q.dtype) if workspace is None else workspace
+                            dtype=torch.float32, device=dev)
+    ws = alloc_workspace(B, H, N, D, causal, dev, q.dtype) if workspace is None else workspace
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, D, c, dt, _ptr(den), _ptr(state),
-            _ptr(ws), ws.numel(), _stream(q.device))
+            _ptr(ws), _nbytes(ws), _stream(dev))
     if trace is None:
         rc = lib.la_forward(*args)
     else:
@@ -217,13 +258,26 @@ def backward(q, k, v, do, causal: bool = False, *, state=None, outs=None,
     (B, H, N, D), dt = _check(q, k, v, do)
     lib = load_library()
     c = int(bool(causal))
+    dev = q.device
+    if outs is not None:
+        if len(outs) != 3:
+            raise ValueError("outs must be (dQ, dK, dV)")
+        for t, name in zip(outs, ("dQ", "dK", "dV")):
+            if t is None:
+                raise ValueError("outs: %s is None" % name)
+            _check_like(t, q, name)
+    # a saved state must be the one the forward wrote for these sizes and
+    # this mask (a causal one holds a record per segment)
+    _check_bytes(state, state_size(B, H, N, D, causal), dev, "state", torch.float32)
+    _check_bytes(workspace, 0, dev, "workspace")
+    _on_gpu(q, state, workspace, *(outs or ()))
     if outs is None:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     else:
         dq, dk, dv = outs
-    ws = alloc_workspace(B, H, N, D, causal, q.device, q.dtype) if workspace is None else workspace
+    ws = alloc_workspace(B, H, N, D, causal, dev, q.dtype) if workspace is None else workspace
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, D,
-            c, dt, _ptr(state), _ptr(ws), ws.numel(), _stream(q.device))
+            c, dt, _ptr(state), _ptr(ws), _nbytes(ws), _stream(dev))
     if trace is None:
         rc = lib.la_backward(*args)
     else:
@@ -236,7 +290,7 @@ def backward(q, k, v, do, causal: bool = False, *, state=None, outs=None,
 def _check_record(r, B, H, D, dev, what):
     if r is None:
         return
-    if (r.dtype != torch.float32 or not r.is_cuda or r.device != dev
+    if (not isinstance(r, torch.Tensor) or r.dtype != torch.float32 or r.device != dev
             or not r.is_contiguous() or r.shape != (B, H, D * D + 2 * D)):
         raise ValueError("%s must be a contiguous float32 [B, H, D*D+2*D] tensor on %s"
                          % (what, dev))
@@ -266,6 +320,10 @@ def forward_segment(q, k, v, causal: bool = False, *, carry_in=None, n_carry: in
     elif carry_out is False:
         carry_out = None
     _check_record(carry_out, B, H, D, dev, "carry_out")
+    _check_like(out, q, "out")
+    _check_bytes(state_out, state_size(B, H, N, D, causal), dev, "state_out", torch.float32)
+    _check_bytes(workspace, 0, dev, "workspace")
+    _on_gpu(q, carry_in, carry_out, out, state_out, workspace)
     o = (torch.empty_like(q) if out is None else out) if compute_out else None
     den = torch.empty((B, H, N), dtype=torch.float32, device=dev) if return_den else None
     state = state_out
@@ -275,7 +333,7 @@ def forward_segment(q, k, v, causal: bool = False, *, carry_in=None, n_carry: in
     ws = alloc_workspace(B, H, N, D, causal, dev, q.dtype) if workspace is None else workspace
     rc = lib.la_forward_segment(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, D,
                                 int(bool(causal)), dt, _ptr(carry_in), int(n_carry),
-                                _ptr(carry_out), _ptr(den), _ptr(state), _ptr(ws), ws.numel(),
+                                _ptr(carry_out), _ptr(den), _ptr(state), _ptr(ws), _nbytes(ws),
                                 _stream(dev))
     if rc != 0:
         raise LAError(rc, "la_forward_segment")
@@ -302,6 +360,14 @@ def backward_segment(q, k, v, do, causal: bool = False, *, carry_in=None, n_carr
     elif gcarry_out is False:
         gcarry_out = None
     _check_record(gcarry_out, B, H, D, dev, "gcarry_out")
+    if outs is not None:
+        if len(outs) != 3 or outs[0] is None or (outs[1] is None) != (outs[2] is None):
+            raise ValueError("outs must be (dQ, dK, dV), with dK and dV both given or both None")
+        for t, name in zip(outs, ("dQ", "dK", "dV")):
+            _check_like(t, q, name)
+    _check_bytes(state, state_size(B, H, N, D, causal), dev, "state", torch.float32)
+    _check_bytes(workspace, 0, dev, "workspace")
+    _on_gpu(q, carry_in, gcarry_in, gcarry_out, state, workspace, *(outs or ()))
     if outs is None:
         dq = torch.empty_like(q)
         dk, dv = (torch.empty_like(q), torch.empty_like(q)) if compute_kv else (None, None)
@@ -311,7 +377,7 @@ def backward_segment(q, k, v, do, causal: bool = False, *, carry_in=None, n_carr
     rc = lib.la_backward_segment(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(dk),
                                  _ptr(dv), B, H, N, D, int(bool(causal)), dt, _ptr(carry_in),
                                  int(n_carry), _ptr(gcarry_in), _ptr(gcarry_out), _ptr(state),
-                                 _ptr(ws), ws.numel(), _stream(dev))
+                                 _ptr(ws), _nbytes(ws), _stream(dev))
     if rc != 0:
         raise LAError(rc, "la_backward_segment")
     return dq, dk, dv, gcarry_out
@@ -336,6 +402,8 @@ def decode_step(q, k, v, state_in=None, *, state_out=None, counts=None, n_prev: 
     if counts is not None and (counts.dtype != torch.int64 or counts.device != dev
                                or counts.shape != (B,) or not counts.is_contiguous()):
         raise ValueError("counts must be a contiguous int64 [B] tensor on %s" % dev)
+    _check_like(out, q, "out")
+    _on_gpu(q, state_in, state_out, counts, out)
     o = torch.empty_like(q) if out is None else out
     den = torch.empty((B, H), dtype=torch.float32, device=dev) if return_den else None
     rc = lib.la_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, D, dt, _ptr(state_in),
@@ -347,7 +415,7 @@ def decode_step(q, k, v, state_in=None, *, state_out=None, counts=None, n_prev: 
 
 def _layer_dims(x, wqkv, wo, H):
     for t in (x, wqkv, wo):
-        if not t.is_cuda or not t.is_contiguous() or t.dtype != x.dtype or t.device != x.device:
+        if not t.is_contiguous() or t.dtype != x.dtype or t.device != x.device:
             raise ValueError("layer tensors must be contiguous, on one GPU, of one dtype")
     if x.dim() != 3:
         raise ValueError("x must be [B, N, C]")
@@ -375,13 +443,17 @@ def layer_forward(x, wqkv, wo, H: int, causal: bool = False, *, saved=None, out=
     B, N, C, D, dt = _layer_dims(x, wqkv, wo, H)
     lib = load_library()
     sb, wb = layer_sizes(B, N, C, H, D, causal, x.dtype)
+    _check_like(out, x, "out")
+    _check_bytes(saved, sb, x.device, "saved")
+    _check_bytes(workspace, 0, x.device, "workspace")
+    _on_gpu(x, out, saved, workspace)
     if saved is None and save:
         saved = torch.empty(max(sb, 16), dtype=torch.uint8, device=x.device)
     ws = torch.empty(max(wb, 16), dtype=torch.uint8, device=x.device) if workspace is None \
         else workspace
     y = torch.empty_like(x) if out is None else out
     rc = lib.la_layer_forward(_ptr(x), _ptr(wqkv), _ptr(wo), _ptr(y), B, N, C, H, D,
-                              int(bool(causal)), dt, _ptr(saved), _ptr(ws), ws.numel(),
+                              int(bool(causal)), dt, _ptr(saved), _ptr(ws), _nbytes(ws),
                               _stream(x.device))
     if rc != 0:
         raise LAError(rc, "la_layer_forward")
@@ -395,14 +467,26 @@ def layer_backward(x, wqkv, wo, dy, H: int, causal: bool = False, *, saved, outs
     if dy.shape != x.shape or dy.dtype != x.dtype or not dy.is_contiguous():
         raise ValueError("dy must match x")
     lib = load_library()
-    _, wb = layer_sizes(B, N, C, H, D, causal, x.dtype)
+    sb, wb = layer_sizes(B, N, C, H, D, causal, x.dtype)
+    if saved is None:
+        raise ValueError("layer_backward needs the saved buffer of layer_forward")
+    _check_bytes(saved, sb, x.device, "saved")
+    _check_bytes(workspace, 0, x.device, "workspace")
+    if outs is not None:
+        if len(outs) != 3:
+            raise ValueError("outs must be (dX, dWqkv, dWo)")
+        for t, like, name in zip(outs, (x, wqkv, wo), ("dX", "dWqkv", "dWo")):
+            if t is None:
+                raise ValueError("outs: %s is None" % name)
+            _check_like(t, like, name)
+    _on_gpu(x, dy, saved, workspace, *(outs or ()))
     ws = torch.empty(max(wb, 16), dtype=torch.uint8, device=x.device) if workspace is None \
         else workspace
     dx, dwqkv, dwo = (torch.empty_like(x), torch.empty_like(wqkv), torch.empty_like(wo)) \
         if outs is None else outs
     rc = lib.la_layer_backward(_ptr(x), _ptr(wqkv), _ptr(wo), _ptr(dy), _ptr(dx), _ptr(dwqkv),
                                _ptr(dwo), B, N, C, H, D, int(bool(causal)), dt, _ptr(saved),
-                               _ptr(ws), ws.numel(), _stream(x.device))
+                               _ptr(ws), _nbytes(ws), _stream(x.device))
     if rc != 0:
         raise LAError(rc, "la_layer_backward")
     return dx, dwqkv, dwo

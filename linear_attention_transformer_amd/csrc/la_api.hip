@@ -210,6 +210,24 @@ int launched()
     return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
+// Checked once per call before its first launch: an error that earlier HIP
+// calls on this thread left pending is not this call's to report or to
+// clear.  The call then launches nothing, leaves that error pending and
+// returns LA_ERR_HIP_PENDING; with none pending, every error launched()
+// reads afterwards is this call's own.  hipErrorNotReady (the answer of an
+// earlier query, not a failure) is cleared.
+int no_pending_error()
+{
+    const hipError_t e = hipPeekAtLastError();
+    if (e == hipSuccess)
+        return LA_OK;
+    if (e == hipErrorNotReady) {
+        (void)hipGetLastError();
+        return LA_OK;
+    }
+    return LA_ERR_HIP_PENDING;
+}
+
 // Optional per-launch timing: caller-owned hipEvents recorded around each
 // kernel launch (events[2i] before, events[2i+1] after launch i).
 struct Tracer {
@@ -222,6 +240,12 @@ struct Tracer {
 template <class F>
 int traced(Tracer *t, hipStream_t s, const char *name, F &&launch)
 {
+    // the first launch of a call (a call without a tracer makes one launch)
+    if (t == nullptr || t->n == 0) {
+        const int pend = no_pending_error();
+        if (pend != LA_OK)
+            return pend;
+    }
     const bool rec = t != nullptr && t->ev != nullptr && 2 * t->n + 1 < t->nev;
     if (rec && hipEventRecord(static_cast<hipEvent_t>(t->ev[2 * t->n]), s) != hipSuccess)
         return LA_ERR_HIP;
@@ -1019,6 +1043,9 @@ int launch_decode(const void *q, const void *k, const void *v, void *o, int64_t 
     const T *qq = static_cast<const T *>(q), *kk = static_cast<const T *>(k),
             *vv = static_cast<const T *>(v);
     T *oo = static_cast<T *>(o);
+    const int pend = no_pending_error();
+    if (pend != LA_OK)
+        return pend;
 #define LA_DEC(d)                                                                          \
     dec::k_decode<ST, d><<<dim3((unsigned)(BH * dec::blocks_per_head<d>())),              \
                            dim3(dec::kThreads), 0, s>>>(qq, kk, vv, oo, den, rin, rout,    \
@@ -1098,6 +1125,9 @@ const char *la_status_string(int status)
     case LA_ERR_ALIAS: return "LA_ERR_ALIAS: an output overlaps an input or another output";
     case LA_ERR_ALIGN: return "LA_ERR_ALIGN: device pointers must be 16-byte aligned";
     case LA_ERR_HIP: return "LA_ERR_HIP: a HIP launch failed";
+    case LA_ERR_HIP_PENDING:
+        return "LA_ERR_HIP_PENDING: a HIP error from earlier work was pending; nothing was "
+               "launched and the error was left pending";
     default: return "unknown la_status";
     }
 }

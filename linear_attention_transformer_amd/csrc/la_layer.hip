@@ -1,8 +1,8 @@
 // la_layer.hip -- one linear-attention layer around the head-batch passes:
 // the input rows go through a linear map to queries, keys and values, linear
 // attention gives the context rows, and a second linear map gives the output
-// (the method outline, "technical framework", of the cloud.baidu.com article
-// on "Transformer Based Linear Attention with Optimized GPU Kernel
+// (the technical-framework paragraph, 技术框架, of the shd-paper.top digest
+// of "Transformer Based Linear Attention with Optimized GPU Kernel
 // Implementation").  Per sequence b, with X_b [N, C], Wqkv [C, 3 H D] and
 // Wo [H D, C]:
 //
@@ -98,6 +98,21 @@ int heads(bool to_heads, void *rows_, void *t0, void *t1, void *t2, int64_t BN, 
                 (int)D);
     }
     return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+// An error that earlier HIP calls on this thread left pending is not this
+// call's: it launches nothing and leaves the error pending (as the head-batch
+// calls do; hipErrorNotReady, a query's answer, is cleared).
+int pending_error()
+{
+    const hipError_t e = hipPeekAtLastError();
+    if (e == hipSuccess)
+        return LA_OK;
+    if (e == hipErrorNotReady) {
+        (void)hipGetLastError();
+        return LA_OK;
+    }
+    return LA_ERR_HIP_PENDING;
 }
 
 // ------------------------------------------------------------ rocBLAS
@@ -279,6 +294,8 @@ int la_layer_forward(const void *X, const void *Wqkv, const void *Wo, void *Y, i
     void *bw = w + z.rows3 + z.head + z.la_ws;
     const int64_t BN = B * N;
 
+    if ((rc = pending_error()) != LA_OK)
+        return rc;
     Blas *bl = blas_for_current_device();
     if (!bl)
         return LA_ERR_HIP;
@@ -349,6 +366,8 @@ int la_layer_backward(const void *X, const void *Wqkv, const void *Wo, const voi
     void *bw = w + z.rows1 + 4 * z.head + z.rows3 + z.la_ws;
     const int64_t BN = B * N;
 
+    if ((rc = pending_error()) != LA_OK)
+        return rc;
     Blas *bl = blas_for_current_device();
     if (!bl)
         return LA_ERR_HIP;

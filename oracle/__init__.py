@@ -201,7 +201,8 @@ def _merge_heads(t):
 
 
 def layer_forward(x, wqkv, wo, H, D, causal=False):
-    """One linear-attention layer (cloud.baidu.com article, method outline:
+    """One linear-attention layer (shd-paper.top digest, technical-framework
+    paragraph 技术框架:
     the input rows pass through a linear map, linear attention forms the
     context rows, a further map follows; the plainest reading is a query /
     key / value projection and an output projection without biases):

@@ -4,9 +4,10 @@ la_backward_segment) against the fp64 oracle (marked gpu).
 The carried records are formed by the oracle from seeded tokens outside the
 piece (so their magnitudes are those of real prefixes and suffixes), rounded
 to fp32, and given to both sides.  O, den, dQ, dK, dV and the outgoing
-records are compared element by element (relative L2 per tensor) at the same
-tolerances as the plain calls: fp32 storage 1e-5, bf16 storage 2e-2, fp16
-storage 1e-3.
+records are compared element by element at the same tolerances as the plain
+calls (fp32 storage 1e-5, bf16 storage 2e-2, fp16 storage 1e-3): tensor-wide,
+head by head and row by row (tests/parity_checks.py; a record's rows are the
+D rows of its matrix and its two vectors).
 """
 import sys
 
@@ -16,6 +17,7 @@ import torch
 
 import oracle
 from linear_attention_transformer_amd.inputs import as_f64_numpy, make_inputs
+from tests import parity_checks as pc
 
 pytestmark = pytest.mark.gpu
 
@@ -56,10 +58,14 @@ def carries(B, H, D, dtype, causal, n_before, n_after, seed):
     return t(rec), t(grec)
 
 
-def check(name, got, ref, tol, errs):
+def check(name, got, ref, D, heads, errs, tol):
+    """Append the error measures of one output (den: per element, against
+    its own value; everything else: rows of D values)."""
     x = f64(got).reshape(ref.shape)
     assert np.all(np.isfinite(x)), name
-    errs[name] = rel_l2(x, ref)
+    den = name.startswith("den")
+    errs.append((name, pc.metrics(x, ref, 1 if den else D, heads,
+                                  floor=0.0 if den else pc.row_floor(tol))))
 
 
 @pytest.mark.parametrize("D", [6, 16, 32, 64, 128, 256])
@@ -86,14 +92,12 @@ def test_segment_parity(D, causal, dtype):
     rin, grin = f64(cin), f64(gin)
     o_r, den_r, cout_r = oracle.forward_carry(a[0], a[1], a[2], causal, rin, nb)
     dq_r, dk_r, dv_r, gout_r = oracle.backward_carry(*a, causal, rin, nb, grin)
-    errs = {}
+    errs = []
     for name, x, r in (("O", o, o_r), ("den", den, den_r), ("carry_out", cout, cout_r),
                        ("dQ", dq, dq_r), ("dK", dk, dk_r), ("dV", dv, dv_r),
                        ("gcarry_out", gout, gout_r)):
-        check(name, x, r, TOL[dtype], errs)
-    say("  rel-L2 " + " ".join("%s=%.2e" % kv for kv in errs.items()))
-    for name, e in errs.items():
-        assert e <= TOL[dtype], (name, e)
+        check(name, x, r, D, B * H, errs, TOL[dtype])
+    pc.check_all(errs, TOL[dtype], say)
     for x, y in ((dq, dq2), (dk, dk2), (dv, dv2), (gout, gout2)):
         assert torch.equal(x, y)
 
@@ -164,13 +168,12 @@ def test_pieces_equal_whole_sequence(causal, dtype):
             outs[c.start] += [dq, dk, dv]
     torch.cuda.synchronize()
     whole = (o_w, den_w, dq_w, dk_w, dv_w)
-    errs = {}
+    errs = []
     for i, name in enumerate(("O", "den", "dQ", "dK", "dV")):
         got = torch.cat([outs[c.start][i] for c in cuts], dim=2)
-        errs[name] = rel_l2(f64(got), f64(whole[i]))
-    say("  rel-L2 vs whole " + " ".join("%s=%.2e" % kv for kv in errs.items()))
-    for name, e in errs.items():
-        assert e <= TOL[dtype], (name, e)
+        check(name, got, f64(whole[i]), D, B * H, errs, TOL[dtype])
+    say("  against the whole sequence:")
+    pc.check_all(errs, TOL[dtype], say)
 
 
 def test_zero_length_piece_passes_records_through():
@@ -229,16 +232,14 @@ def test_decode_step_parity(D, dtype):
     torch.cuda.synchronize()
     a = [as_f64_numpy(x) for x in (q, k, v)]
     r64 = f64(rin)
-    errs = {"O": 0.0, "den": 0.0, "state_out": 0.0}
+    errs = []
     for b, n in enumerate(lens):
         sb = slice(b, b + 1)
         o_r, den_r, rec_r = oracle.forward_carry(a[0][sb], a[1][sb], a[2][sb], True, r64[sb], n)
-        errs["O"] = max(errs["O"], rel_l2(f64(o[sb]).reshape(o_r.shape), o_r))
-        errs["den"] = max(errs["den"], rel_l2(f64(den[sb]).reshape(den_r.shape), den_r))
-        errs["state_out"] = max(errs["state_out"], rel_l2(f64(rout[sb]), rec_r))
-    say("  rel-L2 " + " ".join("%s=%.2e" % kv for kv in errs.items()))
-    for name, e in errs.items():
-        assert e <= TOL[dtype], (name, e)
+        check("O[%d]" % b, o[sb], o_r, D, H, errs, TOL[dtype])
+        check("den[%d]" % b, den[sb], den_r, D, H, errs, TOL[dtype])
+        check("state_out[%d]" % b, rout[sb], rec_r, D, H, errs, TOL[dtype])
+    pc.check_all(errs, TOL[dtype], say)
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
