@@ -145,6 +145,34 @@ int la_backward(const void *Q, const void *K, const void *V, const void *dO,
                 void *stream);
 
 /*
+ * Forward pass without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Arguments and results as for
+ * la_forward (the caller still provides the inputs, O and the optional
+ * den_out / state_out); the call allocates nothing.
+ *
+ * Its workspace is a static array in device memory, LA_SCRATCH_BYTES
+ * (64 MiB) on every device the library runs on, held until the process
+ * ends; its address is looked up on the first call on each device.  Calls
+ * whose workspace would exceed it return LA_ERR_WORKSPACE and launch
+ * nothing.  At D = 32, 64, 128, 256 a forward needs two regions of
+ * B*H*S and B*H records of (D*D + 2*D) floats, each rounded up to 256
+ * bytes, with S = la_num_segments(); other head sizes need
+ * la_workspace_size_for().  So B=4 H=16 N=4096 at D = 128 (38.3 MB) fits,
+ * and the same at D = 256 (152 MB) does not; la_forward takes any size.
+ * Every call on one device shares that
+ * device's array and leaves its last contents there (nothing in it needs to
+ * start at zero: each kernel writes what it reads): calls that overlap in
+ * time on one device, from two streams or two host threads, race on it and
+ * must not be made.
+ */
+#define LA_SCRATCH_BYTES (64u << 20)
+int la_forward_noalloc(const void *Q, const void *K, const void *V, void *O,
+                       int64_t B, int64_t H, int64_t N, int64_t D, int causal,
+                       int dtype, float *den_out, void *state_out,
+                       void *stream);
+
+/*
  * Sequences in pieces: carried state
  * ----------------------------------
  * The method keeps one running state (S, z, u) and a token count, grown

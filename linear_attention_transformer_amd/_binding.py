@@ -78,6 +78,8 @@ def load_library():
     lib.la_layer_backward.restype = ci
     lib.la_decode_step.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp, vp, vp, i64, vp, vp]
     lib.la_decode_step.restype = ci
+    lib.la_forward_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ci, ci, vp, vp, vp]
+    lib.la_forward_noalloc.restype = ci
     ev, ip, cpp = ctypes.c_void_p, ctypes.POINTER(ci), ctypes.POINTER(ctypes.c_char_p)
     lib.la_forward_traced.argtypes = lib.la_forward.argtypes + [ev, ci, ip, cpp]
     lib.la_forward_traced.restype = ci
@@ -250,6 +252,34 @@ def forward(q, k, v, causal: bool = False, *, return_den: bool = False,
     if rc != 0:
         raise LAError(rc, "la_forward")
     return o, den, state
+
+
+SCRATCH_BYTES = 64 << 20   # LA_SCRATCH_BYTES: the static workspace of la_forward_noalloc
+
+
+def forward_noalloc(q, k, v, causal: bool = False, *, out, den_out=None, state_out=None):
+    """la_forward_noalloc: the forward pass on the library's static device
+    workspace, for callers that cannot allocate (graph capture, serving
+    loops).  Every output is the caller's: ``out`` (like q), and optionally
+    ``den_out`` (float32 [B, H, N]) and ``state_out`` (state_size() bytes).
+    Returns (out, den_out, state_out)."""
+    (B, H, N, D), dt = _check(q, k, v)
+    lib = load_library()
+    dev = q.device
+    if out is None:
+        raise ValueError("forward_noalloc writes into the caller's out")
+    _check_like(out, q, "out")
+    if den_out is not None and (den_out.dtype != torch.float32 or den_out.shape != (B, H, N)
+                                or den_out.device != dev or not den_out.is_contiguous()):
+        raise ValueError("den_out must be a contiguous float32 [B, H, N] tensor on %s" % dev)
+    _check_bytes(state_out, state_size(B, H, N, D, causal), dev, "state_out", torch.float32)
+    _on_gpu(q, out, den_out, state_out)
+    rc = lib.la_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, D,
+                                int(bool(causal)), dt, _ptr(den_out), _ptr(state_out),
+                                _stream(dev))
+    if rc != 0:
+        raise LAError(rc, "la_forward_noalloc")
+    return out, den_out, state_out
 
 
 def backward(q, k, v, do, causal: bool = False, *, state=None, outs=None,

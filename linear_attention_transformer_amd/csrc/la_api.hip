@@ -7,6 +7,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "la.h"
@@ -692,7 +693,8 @@ int forward_impl(bool require_o, const void *Q, const void *K, const void *V, vo
         return LA_ERR_NULL;
     Plan p = make_plan(B, H, N, D, causal);
     p.n0 = (float)n_carry;
-    const size_t need = (size_t)make_layout(p).total * sizeof(float);
+    // the forward uses the first two workspace regions (records, totals)
+    const size_t need = (size_t)make_layout(p).gpart * sizeof(float);
     if (ws_bytes < need)
         return LA_ERR_WORKSPACE;
     if (misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(O) ||
@@ -1064,9 +1066,77 @@ int launch_decode(const void *q, const void *k, const void *v, void *o, int64_t 
     return launched();
 }
 
+// Workspace bytes of a forward call: the records and totals at a native
+// head size, the whole staging layout for a padded one; 0 when there is
+// nothing to do.  Arguments already validated.
+size_t forward_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int causal, int dtype)
+{
+    if (B * H * N == 0)
+        return 0;
+    if (native(D))
+        return (size_t)make_layout(make_plan(B, H, N, D, causal)).gpart * sizeof(float);
+    return make_staging(B, H, N, D, causal, dtype).total;
+}
+
+}  // namespace
+
+// ------------------------------------------------- forward without a workspace
+// The workspace of la_forward_noalloc: a static array in device memory, one
+// copy on every device the library runs on, held until the process ends.  Host
+// code never passes this name to a kernel or a copy (on the host it is only a
+// stand-in for the symbol): the device address of each device's copy comes
+// from hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[LA_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_lock;
+void *g_scratch_addr[64];
+
+int scratch_on_current_device(void **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return LA_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_scratch_lock);
+    if (g_scratch_addr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return LA_ERR_HIP;
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
+    return LA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int la_forward_noalloc(const void *Q, const void *K, const void *V, void *O, int64_t B,
+                       int64_t H, int64_t N, int64_t D, int causal, int dtype, float *den_out,
+                       void *state_out, void *stream)
+{
+    if (!valid_dtype(dtype))
+        return LA_ERR_DTYPE;
+    int rc = check_sizes(B, H, N, D, causal);
+    if (rc != LA_OK)
+        return rc;
+    const size_t need = forward_ws_bytes(B, H, N, D, causal, dtype);
+    if (need > (size_t)LA_SCRATCH_BYTES)
+        return LA_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (need > 0) {
+        if ((rc = no_pending_error()) != LA_OK)
+            return rc;
+        if ((rc = scratch_on_current_device(&ws)) != LA_OK)
+            return rc;
+    }
+    Tracer t{nullptr, 0, 0, nullptr};
+    return forward_any(true, Q, K, V, O, B, H, N, D, causal, dtype, nullptr, 0, nullptr,
+                       den_out, state_out, ws, (size_t)LA_SCRATCH_BYTES,
+                       static_cast<hipStream_t>(stream), &t);
+}
 
 int la_decode_step(const void *q, const void *k, const void *v, void *o, int64_t B, int64_t H,
                    int64_t D, int dtype, const float *state_in, float *state_out,
