@@ -766,11 +766,19 @@ def main():
         lms, lfl = time_layer(la, dev, B, N, H, D, dt, causal, max(args.steps // 4, 5),
                               max(args.warmup // 10, 5))
         lpeak = PEAK_FP32_MFMA_TFLOPS if args.dtype == "fp32" else PEAK_BF16_MFMA_TFLOPS
+        gemm_fl = lfl - 12 * B * H * N * D * D
         layer = {"C": H * D, "ms_per_step": round(lms, 4),
                  "tokens_per_s": round(B * N / (lms * 1e-3), 1),
                  "flops_per_step": lfl, "achieved_TFLOPs": round(lfl / (lms * 1e-3) / 1e12, 1),
                  "peak_TFLOPs": lpeak, "frac": round(lfl / (lms * 1e-3) / 1e12 / lpeak, 4),
-                 "attention_ms_per_step": round(ms, 4)}
+                 "attention_ms_per_step": round(ms, 4),
+                 # the step split: the attention timed alone on the same
+                 # shapes, the projections' GEMMs the rest; no pass moves rows
+                 # between layouts
+                 "breakdown_ms": {"attention": round(ms, 4), "gemms": round(lms - ms, 4),
+                                  "layout_passes": 0.0},
+                 "gemm_TFLOPs": round(gemm_fl / ((lms - ms) * 1e-3) / 1e12, 1)
+                 if lms > ms else None}
         print("bench: layer (C=%d) fwd+bwd %.3f ms/step, %.0f TFLOP/s (attention alone %.3f ms)"
               % (H * D, lms, lfl / (lms * 1e-3) / 1e12, ms), file=sys.stderr, flush=True)
 

@@ -312,8 +312,12 @@ int la_decode_step(const void *q, const void *k, const void *v, void *o,
  * No biases and no scaling beyond the weights.  All matrices are DEVICE,
  * row-major, contiguous, of `dtype` (fp32, bf16 or fp16): X, Y, dY, dX are
  * [B, N, C].  The two projections and their gradients are GEMMs on rocBLAS
- * (fp32 accumulation, results rounded to `dtype`); the head split and merge
- * and the attention are this library's kernels.  Sizes: B*N, C and 3*H*D
+ * (fp32 accumulation, results rounded to `dtype`), and the attention is this
+ * library's kernels.  No pass moves rows between layouts: the QKV projection
+ * writes each head's block straight into the attention's [B, H, N, D]
+ * inputs (strided-batched over the heads), and the attention writes O (and,
+ * backward, dQ | dK | dV) straight into the row layout that the output
+ * projection and the weight gradients take.  Sizes: B*N, C and 3*H*D
  * below 2^31, and the attention's own limits (1 <= D <= 256; B*H, N as for
  * la_forward).
  *

@@ -11,6 +11,7 @@
 #include <type_traits>
 
 #include "la.h"
+#include "la_internal.hpp"
 #include "la_kernels.hpp"
 #include "la_kernels_nc.hpp"
 #include "la_kernels_causal.hpp"
@@ -32,7 +33,14 @@ struct Plan {
     int64_t BH, N, D, PS, nseg, seg_len;
     int causal;
     float n0;  // tokens carried in from outside the call, added to every row's count
+    OutLay ol; // where the outputs go (default: [B, H, N, D] contiguous)
 };
+
+// the plain [B, H, N, D] layout
+OutLay plain_layout(int64_t H, int64_t N, int64_t D)
+{
+    return OutLay{std::max<int64_t>(H, 1) * N * D, N * D, D, std::max<int64_t>(H, 1)};
+}
 
 // head sizes the kernels take as they are (others are padded to the next)
 bool supported_d(int64_t D)
@@ -49,6 +57,7 @@ Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int causal)
     p.PS = D * D + 2 * D;
     p.causal = causal;
     p.n0 = 0.f;
+    p.ol = plain_layout(H, N, D);
     const int64_t nchunks = std::max<int64_t>((N + kSegAlign - 1) / kSegAlign, 1);
     const int64_t want =
         p.BH >= kTargetWorkgroups ? 1 : (kTargetWorkgroups + p.BH - 1) / std::max<int64_t>(p.BH, 1);
@@ -191,20 +200,42 @@ bool overlap(const Range &a, const Range &b)
     return a.p < b.p + b.n && b.p < a.p + a.n;
 }
 
-bool aliased(const Range *outs, int nout, const Range *ins, int nin)
+// outputs against inputs, and against each other unless `outs_checked`
+// (outputs of a row layout that interleave by design, e.g. dQ, dK and dV
+// side by side in each row: their spans overlap, their elements do not)
+bool aliased(const Range *outs, int nout, const Range *ins, int nin, bool outs_checked = false)
 {
     for (int i = 0; i < nout; ++i) {
         for (int j = 0; j < nin; ++j)
             if (overlap(outs[i], ins[j]))
                 return true;
-        for (int j = i + 1; j < nout; ++j)
-            if (overlap(outs[i], outs[j]))
-                return true;
+        if (!outs_checked)
+            for (int j = i + 1; j < nout; ++j)
+                if (overlap(outs[i], outs[j]))
+                    return true;
     }
     return false;
 }
 
 bool misaligned(const void *p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u); }
+
+// elements an output of layout ol spans, from its pointer to one past its
+// last element
+int64_t out_extent(const OutLay &ol, int64_t B, int64_t H, int64_t N, int64_t D)
+{
+    return (B - 1) * ol.sb + (H - 1) * ol.sh + (N - 1) * ol.sn + D;
+}
+
+// An output layout the kernels can write: positive strides, rows of D
+// elements that do not overlap (sn >= D), and, where the kernels store
+// 16-byte pieces (every native head size), strides in whole 16 bytes.
+bool layout_ok(const OutLay &ol, int64_t D, size_t esz, bool native_d)
+{
+    if (ol.sb <= 0 || ol.sh <= 0 || ol.sn < D || ol.H <= 0)
+        return false;
+    const int64_t v = (int64_t)(16 / esz);
+    return !native_d || (ol.sb % v == 0 && ol.sh % v == 0 && ol.sn % v == 0);
+}
 
 int launched()
 {
@@ -358,14 +389,14 @@ int run_forward(const void *Q, const void *K, const void *V, void *O, float *den
                     bf::k_apply_bf<D, 0><<<dim3((unsigned)(p.nseg * p.BH)),
                                            dim3(bf::kApplyThreads), 0, s>>>(
                         static_cast<const T *>(Q), nullptr, static_cast<T *>(O), nullptr,
-                        den_out, nullptr, rec, p.N, p.seg_len, (int)p.nseg, p.n0);
+                        den_out, nullptr, rec, p.N, p.seg_len, (int)p.nseg, p.n0, p.ol);
                 else {
                     const Plan pf = rows_plan(
                         p, resident_wgs<nc::k_apply_nc<ST, D, 0>>(nc::kApplyThreads), 1);
                     nc::k_apply_nc<ST, D, 0><<<dim3((unsigned)(pf.nseg * pf.BH)),
                                                dim3(nc::kApplyThreads), 0, s>>>(
                         static_cast<const T *>(Q), nullptr, static_cast<T *>(O), nullptr,
-                        den_out, rec, pf.N, pf.seg_len, (int)pf.nseg, pf.n0);
+                        den_out, rec, pf.N, pf.seg_len, (int)pf.nseg, pf.n0, pf.ol);
                 }
             });
         return traced(t, s, "forward", [&] {
@@ -374,13 +405,13 @@ int run_forward(const void *Q, const void *K, const void *V, void *O, float *den
                                          dim3(cz::threads<D>()), 0, s>>>(
                     static_cast<const T *>(Q), static_cast<const T *>(K),
                     static_cast<const T *>(V), static_cast<T *>(O), den_out, rec, p.N, p.seg_len,
-                    (int)p.nseg, p.n0);
+                    (int)p.nseg, p.n0, p.ol);
             else
                 cz::k_fwd_causal<ST, D><<<dim3((unsigned)(p.nseg * p.BH)),
                                           dim3(cz::threads<D>()), 0, s>>>(
                     static_cast<const T *>(Q), static_cast<const T *>(K),
                     static_cast<const T *>(V), static_cast<T *>(O), den_out, rec, p.N, p.seg_len,
-                    (int)p.nseg, p.n0);
+                    (int)p.nseg, p.n0, p.ol);
         });
     }
     if constexpr (wide_path<ST, D>()) {
@@ -389,7 +420,7 @@ int run_forward(const void *Q, const void *K, const void *V, void *O, float *den
                 nc::k_apply_nc<ST, D, 0><<<dim3((unsigned)(p.nseg * p.BH)),
                                            dim3(nc::apply_threads<D>()), 0, s>>>(
                     static_cast<const T *>(Q), nullptr, static_cast<T *>(O), nullptr, den_out,
-                    rec, p.N, p.seg_len, (int)p.nseg, p.n0);
+                    rec, p.N, p.seg_len, (int)p.nseg, p.n0, p.ol);
             });
     }
     const dim3 grid((unsigned)(p.nseg * p.BH * C::CS));
@@ -398,12 +429,12 @@ int run_forward(const void *Q, const void *K, const void *V, void *O, float *den
             k_forward<ST, D, true><<<grid, dim3(C::NT), 0, s>>>(
                 static_cast<const T *>(Q), static_cast<const T *>(K),
                 static_cast<const T *>(V), static_cast<T *>(O), den_out, rec, p.N,
-                p.seg_len, (int)p.nseg, p.n0);
+                p.seg_len, (int)p.nseg, p.n0, p.ol);
         else
             k_forward<ST, D, false><<<grid, dim3(C::NT), 0, s>>>(
                 static_cast<const T *>(Q), static_cast<const T *>(K),
                 static_cast<const T *>(V), static_cast<T *>(O), den_out, rec, p.N,
-                p.seg_len, (int)p.nseg, p.n0);
+                p.seg_len, (int)p.nseg, p.n0, p.ol);
     });
 }
 
@@ -442,11 +473,11 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
             if constexpr (std::is_same<ST, StBF16>::value)
                 bf::k_bwd_q_causal_bf<D><<<g1, nt, 0, s>>>(q, k, v, g, static_cast<T *>(dQ),
                                                            cbuf, fstate, p.N, p.seg_len,
-                                                           (int)p.nseg, p.n0);
+                                                           (int)p.nseg, p.n0, p.ol);
             else
                 cz::k_bwd_q_causal<ST, D><<<g1, nt, 0, s>>>(q, k, v, g, static_cast<T *>(dQ),
                                                             cbuf, fstate, p.N, p.seg_len,
-                                                            (int)p.nseg, p.n0);
+                                                            (int)p.nseg, p.n0, p.ol);
         });
         if (rc != LA_OK)
             return rc;
@@ -468,11 +499,11 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
             if constexpr (std::is_same<ST, StBF16>::value)
                 bf::k_bwd_kv_causal_bf<D><<<dim3((unsigned)(2 * p.nseg * p.BH)), nt, 0, s>>>(
                     q, k, v, g, static_cast<T *>(dK), static_cast<T *>(dV), cbuf, gpart, p.N,
-                    p.seg_len, (int)p.nseg);
+                    p.seg_len, (int)p.nseg, p.ol);
             else
                 cz::k_bwd_kv_causal<ST, D><<<dim3((unsigned)(2 * p.nseg * p.BH)), nt, 0, s>>>(
                     q, k, v, g, static_cast<T *>(dK), static_cast<T *>(dV), cbuf, gpart, p.N,
-                    p.seg_len, (int)p.nseg);
+                    p.seg_len, (int)p.nseg, p.ol);
         });
     }
     if constexpr (!CAUSAL && wide_path<ST, D>()) {
@@ -481,7 +512,7 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
         const dim3 g1((unsigned)(p.nseg * p.BH));
         rc = traced(t, s, "bwd_q", [&] {
             nc::k_bwd_q_nc<ST, D, false><<<g1, dim3(512), 0, s>>>(
-                g, q, static_cast<T *>(dQ), cbuf, fstate, p.N, p.seg_len, (int)p.nseg, p.n0);
+                g, q, static_cast<T *>(dQ), cbuf, fstate, p.N, p.seg_len, (int)p.nseg, p.n0, p.ol);
         });
         if (rc != LA_OK)
             return rc;
@@ -501,7 +532,7 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
             nc::k_apply_nc<ST, D, 2><<<dim3((unsigned)(2 * p.nseg * p.BH)),
                                        dim3(nc::apply_threads<D>()), 0, s>>>(
                 v, k, static_cast<T *>(dK), static_cast<T *>(dV), nullptr, ws + l.gtot, p.N,
-                p.seg_len, (int)p.nseg, p.n0);
+                p.seg_len, (int)p.nseg, p.n0, p.ol);
         });
     }
     if constexpr (!CAUSAL && nc_path<D>()) {
@@ -512,7 +543,7 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
             rc = traced(t, s, "bwd_q", [&] {
                 bf::k_apply_bf<D, 1><<<g1, dim3(bf::kApplyThreads), 0, s>>>(
                     g, q, static_cast<T *>(dQ), nullptr, nullptr, cbuf, fstate, p.N, p.seg_len,
-                    (int)p.nseg, p.n0);
+                    (int)p.nseg, p.n0, p.ol);
             });
             if (rc != LA_OK)
                 return rc;
@@ -527,7 +558,7 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
             rc = traced(t, s, "bwd_q", [&] {
                 nc::k_bwd_q_nc<ST, D><<<dim3((unsigned)(pq.nseg * pq.BH)), dim3(512), 0, s>>>(
                     g, q, static_cast<T *>(dQ), gpart, fstate, pq.N, pq.seg_len, (int)pq.nseg,
-                    pq.n0);
+                    pq.n0, pq.ol);
             });
             if (rc != LA_OK)
                 return rc;
@@ -546,21 +577,21 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
                 bf::k_apply_bf<D, 2><<<dim3((unsigned)(2 * p.nseg * p.BH)),
                                        dim3(bf::kApplyThreads), 0, s>>>(
                     v, k, static_cast<T *>(dK), static_cast<T *>(dV), nullptr, nullptr,
-                    ws + l.gtot, p.N, p.seg_len, (int)p.nseg, p.n0);
+                    ws + l.gtot, p.N, p.seg_len, (int)p.nseg, p.n0, p.ol);
             else {
                 const Plan pk =
                     rows_plan(p, resident_wgs<nc::k_apply_nc<ST, D, 2>>(nc::kApplyThreads), 2);
                 nc::k_apply_nc<ST, D, 2><<<dim3((unsigned)(2 * pk.nseg * pk.BH)),
                                            dim3(nc::kApplyThreads), 0, s>>>(
                     v, k, static_cast<T *>(dK), static_cast<T *>(dV), nullptr, ws + l.gtot, pk.N,
-                    pk.seg_len, (int)pk.nseg, pk.n0);
+                    pk.seg_len, (int)pk.nseg, pk.n0, pk.ol);
             }
         });
     }
     rc = traced(t, s, "bwd_q", [&] {
         k_bwd_q<ST, D, CAUSAL, FUSE><<<dim3((unsigned)(p.nseg * p.BH)), dim3(CQ::NT), 0, s>>>(
             q, k, v, g, static_cast<T *>(dQ), fstate, gpart, cbuf, p.N, p.seg_len,
-            (int)p.nseg, p.n0);
+            (int)p.nseg, p.n0, p.ol);
     });
     if (rc != LA_OK)
         return rc;
@@ -588,7 +619,7 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
     return traced(t, s, "bwd_kv", [&] {
         k_bwd_kv<ST, D, CAUSAL><<<grid, dim3(C::NT), 0, s>>>(
             q, k, v, g, static_cast<T *>(dK), static_cast<T *>(dV), gstate, cbuf, p.N,
-            p.seg_len, (int)p.nseg);
+            p.seg_len, (int)p.nseg, p.ol);
     });
 }
 
@@ -667,7 +698,8 @@ size_t record_bytes(int64_t BH, int64_t D) { return (size_t)(BH * (D * D + 2 * D
 int forward_impl(bool require_o, const void *Q, const void *K, const void *V, void *O,
                  int64_t B, int64_t H, int64_t N, int64_t D, int causal, int dtype,
                  const float *cin, int64_t n_carry, float *cout, float *den_out,
-                 void *state_out, void *ws, size_t ws_bytes, hipStream_t s, Tracer *t)
+                 void *state_out, void *ws, size_t ws_bytes, hipStream_t s, Tracer *t,
+                 const OutLay *ol = nullptr)
 {
     if (!valid_dtype(dtype))
         return LA_ERR_DTYPE;
@@ -693,6 +725,11 @@ int forward_impl(bool require_o, const void *Q, const void *K, const void *V, vo
         return LA_ERR_NULL;
     Plan p = make_plan(B, H, N, D, causal);
     p.n0 = (float)n_carry;
+    if (ol != nullptr) {
+        if (!layout_ok(*ol, D, elem_size(dtype), true))
+            return LA_ERR_ALIGN;
+        p.ol = *ol;
+    }
     // the forward uses the first two workspace regions (records, totals)
     const size_t need = (size_t)make_layout(p).gpart * sizeof(float);
     if (ws_bytes < need)
@@ -702,12 +739,13 @@ int forward_impl(bool require_o, const void *Q, const void *K, const void *V, vo
         misaligned(cout))
         return LA_ERR_ALIGN;
     const size_t tb = (size_t)(B * H * N * D) * elem_size(dtype);
+    const size_t ob = (size_t)out_extent(p.ol, B, H, N, D) * elem_size(dtype);
     const Range ins[4] = {{(const char *)Q, tb},
                           {(const char *)K, tb},
                           {(const char *)V, tb},
                           {(const char *)cin, rb}};
     const Range outs[5] = {
-        {(const char *)O, tb},
+        {(const char *)O, ob},
         {(const char *)den_out, (size_t)(B * H * N) * sizeof(float)},
         {(const char *)state_out, (size_t)state_floats(p) * sizeof(float)},
         {(const char *)ws, need},
@@ -730,7 +768,8 @@ int backward_impl(bool require_kv, const void *Q, const void *K, const void *V,
                   const void *dO, void *dQ, void *dK, void *dV, int64_t B, int64_t H,
                   int64_t N, int64_t D, int causal, int dtype, const float *cin,
                   int64_t n_carry, const float *gin, float *gout, const void *state_in,
-                  void *ws, size_t ws_bytes, hipStream_t s, Tracer *t)
+                  void *ws, size_t ws_bytes, hipStream_t s, Tracer *t,
+                  const OutLay *ol = nullptr)
 {
     if (!valid_dtype(dtype))
         return LA_ERR_DTYPE;
@@ -757,6 +796,11 @@ int backward_impl(bool require_kv, const void *Q, const void *K, const void *V,
         return LA_ERR_NULL;
     Plan p = make_plan(B, H, N, D, causal);
     p.n0 = (float)n_carry;
+    if (ol != nullptr) {
+        if (!layout_ok(*ol, D, elem_size(dtype), true))
+            return LA_ERR_ALIGN;
+        p.ol = *ol;
+    }
     const size_t need = (size_t)make_layout(p).total * sizeof(float);
     if (ws_bytes < need)
         return LA_ERR_WORKSPACE;
@@ -765,6 +809,7 @@ int backward_impl(bool require_kv, const void *Q, const void *K, const void *V,
         misaligned(ws) || misaligned(cin) || misaligned(gin) || misaligned(gout))
         return LA_ERR_ALIGN;
     const size_t tb = (size_t)(B * H * N * D) * elem_size(dtype);
+    const size_t ob = (size_t)out_extent(p.ol, B, H, N, D) * elem_size(dtype);
     const Range ins[7] = {{(const char *)Q, tb},
                           {(const char *)K, tb},
                           {(const char *)V, tb},
@@ -772,12 +817,13 @@ int backward_impl(bool require_kv, const void *Q, const void *K, const void *V,
                           {(const char *)state_in, (size_t)state_floats(p) * sizeof(float)},
                           {(const char *)cin, rb},
                           {(const char *)gin, rb}};
-    const Range outs[5] = {{(const char *)dQ, tb},
-                           {(const char *)dK, tb},
-                           {(const char *)dV, tb},
+    const Range outs[5] = {{(const char *)dQ, ob},
+                           {(const char *)dK, ob},
+                           {(const char *)dV, ob},
                            {(const char *)ws, need},
                            {(const char *)gout, rb}};
-    if (aliased(outs, 5, ins, 7))
+    if (aliased(outs, 5, ins, 7, ol != nullptr) ||
+        (ol != nullptr && (aliased(outs + 3, 2, outs, 3) || overlap(outs[3], outs[4]))))
         return LA_ERR_ALIAS;
     float *w = static_cast<float *>(ws);
     switch (dtype) {
@@ -835,11 +881,15 @@ int grid_for(int64_t n)
 }
 
 // [rows, D] <-> [rows, Dp] in storage `dtype` (pad: to_padded, else unpad)
+// (unpad: rows r = bh * N + n go to row n of head bh in the layout `ol`, or
+// to row r of a plain [rows, D] tensor)
 int stage_tensor(const char *name, bool to_padded, const void *src, void *dst, int dtype,
-                 int64_t D, int64_t Dp, int64_t rows, hipStream_t s, Tracer *t)
+                 int64_t D, int64_t Dp, int64_t rows, hipStream_t s, Tracer *t, int64_t N = 1,
+                 const OutLay *ol = nullptr)
 {
     const int64_t chunks = rows * (Dp * (int64_t)elem_size(dtype) / 16);
     const dim3 grid(grid_for(chunks)), blk(stg::kThreads);
+    const OutLay lay = ol ? *ol : OutLay{N * D, N * D, D, 1};
     return traced(t, s, name, [&] {
         if (dtype == LA_FP32) {
             if (to_padded)
@@ -849,7 +899,7 @@ int stage_tensor(const char *name, bool to_padded, const void *src, void *dst, i
             else
                 stg::k_unpad<StF32><<<grid, blk, 0, s>>>(static_cast<const float *>(src),
                                                          static_cast<float *>(dst), rows,
-                                                         (int)D, (int)Dp);
+                                                         (int)D, (int)Dp, N, lay);
         } else {
             // bf16 and fp16 move as the same 16-bit words
             if (to_padded)
@@ -859,7 +909,7 @@ int stage_tensor(const char *name, bool to_padded, const void *src, void *dst, i
             else
                 stg::k_unpad<StBF16><<<grid, blk, 0, s>>>(static_cast<const uint16_t *>(src),
                                                           static_cast<uint16_t *>(dst), rows,
-                                                          (int)D, (int)Dp);
+                                                          (int)D, (int)Dp, N, lay);
         }
     });
 }
@@ -877,7 +927,8 @@ int stage_record(const char *name, const float *src, int64_t Ds, float *dst, int
 int forward_any(bool require_o, const void *Q, const void *K, const void *V, void *O,
                 int64_t B, int64_t H, int64_t N, int64_t D, int causal, int dtype,
                 const float *cin, int64_t n_carry, float *cout, float *den_out,
-                void *state_out, void *ws, size_t ws_bytes, hipStream_t s, Tracer *t)
+                void *state_out, void *ws, size_t ws_bytes, hipStream_t s, Tracer *t,
+                const OutLay *ol = nullptr)
 {
     if (!valid_dtype(dtype))
         return LA_ERR_DTYPE;
@@ -886,7 +937,7 @@ int forward_any(bool require_o, const void *Q, const void *K, const void *V, voi
         return rc;
     if (native(D))
         return forward_impl(require_o, Q, K, V, O, B, H, N, D, causal, dtype, cin, n_carry,
-                            cout, den_out, state_out, ws, ws_bytes, s, t);
+                            cout, den_out, state_out, ws, ws_bytes, s, t, ol);
     if (n_carry < 0 || n_carry > kMaxCarry)
         return LA_ERR_SHAPE;
     if (B * H == 0)
@@ -909,13 +960,17 @@ int forward_any(bool require_o, const void *Q, const void *K, const void *V, voi
         misaligned(den_out) || misaligned(state_out) || misaligned(ws))
         return LA_ERR_ALIGN;
     Plan pp = make_plan(B, H, N, g.Dp, causal);
+    if (ol != nullptr && !layout_ok(*ol, D, elem_size(dtype), false))
+        return LA_ERR_ALIGN;
     const size_t tb = (size_t)(BH * N * D) * elem_size(dtype);
+    const size_t ob =
+        (size_t)out_extent(ol ? *ol : plain_layout(H, N, D), B, H, N, D) * elem_size(dtype);
     const Range ins[4] = {{(const char *)Q, tb},
                           {(const char *)K, tb},
                           {(const char *)V, tb},
                           {(const char *)cin, rb}};
     const Range outs[5] = {
-        {(const char *)O, tb},
+        {(const char *)O, ob},
         {(const char *)den_out, (size_t)(BH * N) * sizeof(float)},
         {(const char *)state_out, (size_t)state_floats(pp) * sizeof(float)},
         {(const char *)ws, g.total},
@@ -939,7 +994,8 @@ int forward_any(bool require_o, const void *Q, const void *K, const void *V, voi
                       state_out, w + g.off_inner, g.inner, s, t);
     if (rc != LA_OK)
         return rc;
-    if (O && (rc = stage_tensor("unstage", false, to, O, dtype, D, g.Dp, rows, s, t)) != LA_OK)
+    if (O && (rc = stage_tensor("unstage", false, to, O, dtype, D, g.Dp, rows, s, t, N, ol)) !=
+                 LA_OK)
         return rc;
     if (cout && (rc = stage_record("unstage", r_out, g.Dp, cout, D, BH, s, t)) != LA_OK)
         return rc;
@@ -951,7 +1007,8 @@ int backward_any(bool require_kv, const void *Q, const void *K, const void *V,
                  const void *dO, void *dQ, void *dK, void *dV, int64_t B, int64_t H,
                  int64_t N, int64_t D, int causal, int dtype, const float *cin,
                  int64_t n_carry, const float *gin, float *gout, const void *state_in,
-                 void *ws, size_t ws_bytes, hipStream_t s, Tracer *t)
+                 void *ws, size_t ws_bytes, hipStream_t s, Tracer *t,
+                 const OutLay *ol = nullptr)
 {
     if (!valid_dtype(dtype))
         return LA_ERR_DTYPE;
@@ -960,7 +1017,7 @@ int backward_any(bool require_kv, const void *Q, const void *K, const void *V,
         return rc;
     if (native(D))
         return backward_impl(require_kv, Q, K, V, dO, dQ, dK, dV, B, H, N, D, causal, dtype,
-                             cin, n_carry, gin, gout, state_in, ws, ws_bytes, s, t);
+                             cin, n_carry, gin, gout, state_in, ws, ws_bytes, s, t, ol);
     if (n_carry < 0 || n_carry > kMaxCarry)
         return LA_ERR_SHAPE;
     if (B * H == 0)
@@ -985,7 +1042,11 @@ int backward_any(bool require_kv, const void *Q, const void *K, const void *V,
         misaligned(ws))
         return LA_ERR_ALIGN;
     Plan pp = make_plan(B, H, N, g.Dp, causal);
+    if (ol != nullptr && !layout_ok(*ol, D, elem_size(dtype), false))
+        return LA_ERR_ALIGN;
     const size_t tb = (size_t)(BH * N * D) * elem_size(dtype);
+    const size_t ob =
+        (size_t)out_extent(ol ? *ol : plain_layout(H, N, D), B, H, N, D) * elem_size(dtype);
     const Range ins[7] = {{(const char *)Q, tb},
                           {(const char *)K, tb},
                           {(const char *)V, tb},
@@ -993,12 +1054,13 @@ int backward_any(bool require_kv, const void *Q, const void *K, const void *V,
                           {(const char *)state_in, (size_t)state_floats(pp) * sizeof(float)},
                           {(const char *)cin, rb},
                           {(const char *)gin, rb}};
-    const Range outs[5] = {{(const char *)dQ, tb},
-                           {(const char *)dK, tb},
-                           {(const char *)dV, tb},
+    const Range outs[5] = {{(const char *)dQ, ob},
+                           {(const char *)dK, ob},
+                           {(const char *)dV, ob},
                            {(const char *)ws, g.total},
                            {(const char *)gout, rb}};
-    if (aliased(outs, 5, ins, 7))
+    if (aliased(outs, 5, ins, 7, ol != nullptr) ||
+        (ol != nullptr && (aliased(outs + 3, 2, outs, 3) || overlap(outs[3], outs[4]))))
         return LA_ERR_ALIAS;
     char *w = static_cast<char *>(ws);
     void *T_[7];
@@ -1024,12 +1086,14 @@ int backward_any(bool require_kv, const void *Q, const void *K, const void *V,
                        gout ? r_gout : nullptr, state_in, w + g.off_inner, g.inner, s, t);
     if (rc != LA_OK)
         return rc;
-    if ((rc = stage_tensor("unstage", false, T_[4], dQ, dtype, D, g.Dp, rows, s, t)) != LA_OK)
+    if ((rc = stage_tensor("unstage", false, T_[4], dQ, dtype, D, g.Dp, rows, s, t, N, ol)) !=
+        LA_OK)
         return rc;
-    if (kv && ((rc = stage_tensor("unstage", false, T_[5], dK, dtype, D, g.Dp, rows, s, t)) !=
-                   LA_OK ||
-               (rc = stage_tensor("unstage", false, T_[6], dV, dtype, D, g.Dp, rows, s, t)) !=
-                   LA_OK))
+    if (kv &&
+        ((rc = stage_tensor("unstage", false, T_[5], dK, dtype, D, g.Dp, rows, s, t, N, ol)) !=
+             LA_OK ||
+         (rc = stage_tensor("unstage", false, T_[6], dV, dtype, D, g.Dp, rows, s, t, N, ol)) !=
+             LA_OK))
         return rc;
     if (gout && (rc = stage_record("unstage", r_gout, g.Dp, gout, D, BH, s, t)) != LA_OK)
         return rc;
@@ -1079,6 +1143,34 @@ size_t forward_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int causal, 
 }
 
 }  // namespace
+
+// ------------------------------------------------- outputs in a given layout
+namespace la_internal {
+
+int forward_to(const void *Q, const void *K, const void *V, void *O, int64_t B, int64_t H,
+               int64_t N, int64_t D, int causal, int dtype, void *state_out, void *ws,
+               size_t ws_bytes, void *stream, OutStrides o)
+{
+    const la::OutLay ol{o.sb, o.sh, o.sn, std::max<int64_t>(H, 1)};
+    Tracer t{nullptr, 0, 0, nullptr};
+    return forward_any(true, Q, K, V, O, B, H, N, D, causal, dtype, nullptr, 0, nullptr,
+                       nullptr, state_out, ws, ws_bytes, static_cast<hipStream_t>(stream), &t,
+                       &ol);
+}
+
+int backward_to(const void *Q, const void *K, const void *V, const void *dO, void *dQ,
+                void *dK, void *dV, int64_t B, int64_t H, int64_t N, int64_t D, int causal,
+                int dtype, const void *state_in, void *ws, size_t ws_bytes, void *stream,
+                OutStrides o)
+{
+    const la::OutLay ol{o.sb, o.sh, o.sn, std::max<int64_t>(H, 1)};
+    Tracer t{nullptr, 0, 0, nullptr};
+    return backward_any(true, Q, K, V, dO, dQ, dK, dV, B, H, N, D, causal, dtype, nullptr, 0,
+                        nullptr, nullptr, state_in, ws, ws_bytes,
+                        static_cast<hipStream_t>(stream), &t, &ol);
+}
+
+}  // namespace la_internal
 
 // ------------------------------------------------- forward without a workspace
 // The workspace of la_forward_noalloc: a static array in device memory, one

@@ -40,6 +40,21 @@ namespace la {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
+// Where a kernel writes a [B, H, N, D] output: element d of row n of head
+// bh = b * H + h at (b * sb + h * sh + n * sn + d) elements from the output
+// pointer.  The plain layout is {H N D, N D, D, H}; a row layout puts the
+// heads of one token side by side ([B, N, H, D]: {N H D, D, H D, H}).  Row
+// strides and head offsets keep 16-byte alignment wherever the kernels store
+// 16-byte pieces (checked on the host).
+struct OutLay {
+    int64_t sb, sh, sn;
+    int64_t H;
+    __device__ __forceinline__ int64_t head(int64_t bh) const
+    {
+        return (bh / H) * sb + (bh % H) * sh;
+    }
+};
+
 __device__ __forceinline__ f4 mma(float a, float b, f4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -645,7 +660,7 @@ __global__ __launch_bounds__(threads_for<D>()) void k_forward(
     const typename ST::T *__restrict__ Q, const typename ST::T *__restrict__ Kp,
     const typename ST::T *__restrict__ Vp, typename ST::T *__restrict__ O,
     float *__restrict__ den_out, const float *__restrict__ state, int64_t N,
-    int64_t seg_len, int nseg, float n0)
+    int64_t seg_len, int nseg, float n0, OutLay ol)
 {
     typedef Cfg<D, DefCS<D>::value> C;
     constexpr int R = CAUSAL ? C::RC : C::RN;
@@ -738,7 +753,7 @@ __global__ __launch_bounds__(threads_for<D>()) void k_forward(
                 for (int r = 0; r < 4; ++r) {
                     const int row = tb * 16 + 4 * lg + r;
                     if (c0 + row < end)
-                        O[hoff + (c0 + row) * D + ncol<C>(g.cs, w, nb) + lr] =
+                        O[ol.head(g.bh) + (c0 + row) * ol.sn + ncol<C>(g.cs, w, nb) + lr] =
                             ST::narrow(out[tb][nb][r] / denl[row]);
                 }
         if (den_out != nullptr && g.cs == 0)
@@ -766,7 +781,7 @@ __global__ __launch_bounds__(threads_for<D>()) void k_bwd_q(
     const typename ST::T *__restrict__ Vp, const typename ST::T *__restrict__ G,
     typename ST::T *__restrict__ dQ, const float *__restrict__ state,
     float *__restrict__ gpart, float *__restrict__ cbuf, int64_t N, int64_t seg_len,
-    int nseg, float n0)
+    int nseg, float n0, OutLay ol)
 {
     typedef Cfg<D, 1> C;
     constexpr int R = CAUSAL ? C::RC : C::RN;
@@ -937,7 +952,7 @@ __global__ __launch_bounds__(threads_for<D>()) void k_bwd_q(
                 for (int r = 0; r < 4; ++r) {
                     const int row = tb * 16 + 4 * lg + r;
                     if (c0 + row < end)
-                        dQ[hoff + (c0 + row) * D + ncol<C>(0, w, nb) + lr] =
+                        dQ[ol.head(g.bh) + (c0 + row) * ol.sn + ncol<C>(0, w, nb) + lr] =
                             ST::narrow(y[tb][nb][r]);
                 }
         if constexpr (FUSE) {
@@ -974,7 +989,7 @@ __global__ __launch_bounds__(threads_for<D>()) void k_bwd_kv(
     const typename ST::T *__restrict__ Vp, const typename ST::T *__restrict__ G,
     typename ST::T *__restrict__ dK, typename ST::T *__restrict__ dV,
     const float *__restrict__ gstate, const float *__restrict__ cbuf, int64_t N,
-    int64_t seg_len, int nseg)
+    int64_t seg_len, int nseg, OutLay ol)
 {
     typedef Cfg<D, DefCS<D>::value> C;
     constexpr int R = CAUSAL ? C::RC : C::RN;
@@ -1090,7 +1105,8 @@ __global__ __launch_bounds__(threads_for<D>()) void k_bwd_kv(
                 for (int r = 0; r < 4; ++r) {
                     const int row = tb * 16 + 4 * lg + r;
                     if (c0 + row < end) {
-                        const int64_t o = hoff + (c0 + row) * D + ncol<C>(g.cs, w, nb) + lr;
+                        const int64_t o =
+                            ol.head(g.bh) + (c0 + row) * ol.sn + ncol<C>(g.cs, w, nb) + lr;
                         dK[o] = ST::narrow(dk[tb][nb][r]);
                         dV[o] = ST::narrow(dv[tb][nb][r]);
                     }

@@ -104,7 +104,7 @@ template <int D, int KIND>
 __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
     const uint16_t *__restrict__ X, const uint16_t *__restrict__ X2, uint16_t *__restrict__ Out,
     uint16_t *__restrict__ Out2, float *__restrict__ den_out, float *__restrict__ cbuf,
-    const float *__restrict__ rec, int64_t N, int64_t seg_len, int nseg, float n0)
+    const float *__restrict__ rec, int64_t N, int64_t seg_len, int nseg, float n0, OutLay ol)
 {
     static_assert(D >= 32 && D <= 128, "32-column output blocks");
     static_assert(KIND >= 0 && KIND <= 2, "forward, dQ or dK | dV");
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
     const bool colread = (KIND == 0) || (KIND == 2 && sub == 1);
     const uint16_t *xh = ((KIND == 2 && sub == 1) ? X2 : X) + hoff;
     const uint16_t *qh = DQ ? X2 + hoff : nullptr;
-    uint16_t *oh = ((KIND == 2 && sub == 1) ? Out2 : Out) + hoff;
+    uint16_t *oh = ((KIND == 2 && sub == 1) ? Out2 : Out) + ol.head(bh);
 
     uint4 stg[PER], stq[DQ ? PER : 1];
     auto fetch_round = [&](int64_t r0) {
@@ -246,7 +246,7 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
         const int c = tid + p * kApplyThreads;
         const int64_t grow = beg + rr * TR + c / CPR;
         if (grow < end)
-            *reinterpret_cast<uint4 *>(oh + grow * D + 8 * (c % CPR)) =
+            *reinterpret_cast<uint4 *>(oh + grow * ol.sn + 8 * (c % CPR)) =
                 *reinterpret_cast<const uint4 *>(&ot[(int)(rr & 1)][(c / CPR) * LDX + 8 * (c % CPR)]);
     };
 
@@ -771,7 +771,7 @@ template <int D>
 __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal_bf(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ den_out,
-    const float *__restrict__ rec, int64_t N, int64_t seg_len, int nseg, float n0)
+    const float *__restrict__ rec, int64_t N, int64_t seg_len, int nseg, float n0, OutLay ol)
 {
     typedef nc::IO<StBF16> io;
     static_assert(D >= 32 && D <= 128, "32-column blocks, state in registers");
@@ -793,7 +793,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal_bf(
     const int64_t hoff = bh * N * D;
     const float *st = rec + (bh * nseg + seg) * (int64_t)(D * D + 2 * D);
     const uint16_t *qh = Q + hoff, *kh = K + hoff, *vh = V + hoff;
-    uint16_t *oh = O + hoff;
+    uint16_t *oh = O + ol.head(bh);
 
     ChunkRows<D, NT> rq, rk, rv;
     const int64_t nrounds = (end - beg + kCc - 1) / kCc;
@@ -824,7 +824,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal_bf(
     bool pok = false;
     auto store_pending = [&](int q) {
         if (pok)
-            io::store4(oh + prow * D + 32 * cb + 8 * q + 4 * h, pend[q]);
+            io::store4(oh + prow * ol.sn + 32 * cb + 8 * q + 4 * h, pend[q]);
     };
 
     for (int64_t round = 0; round < nrounds; ++round) {
@@ -957,7 +957,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ G, uint16_t *__restrict__ dQ,
     float *__restrict__ cbuf, const float *__restrict__ rec, int64_t N, int64_t seg_len,
-    int nseg, float n0)
+    int nseg, float n0, OutLay ol)
 {
     typedef nc::IO<StBF16> io;
     static_assert(D >= 32 && D <= 128, "32-column blocks, state in registers");
@@ -983,7 +983,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
     const int64_t hoff = bh * N * D;
     const float *st = rec + (bh * nseg + seg) * (int64_t)(D * D + 2 * D);
     const uint16_t *qh = Q + hoff, *kh = K + hoff, *vh = V + hoff, *gh = G + hoff;
-    uint16_t *oh = dQ + hoff;
+    uint16_t *oh = dQ + ol.head(bh);
 
     ChunkRows<D, NT> rq, rg, rk, rv;
     const int64_t nrounds = (end - beg + kCc - 1) / kCc;
@@ -1025,7 +1025,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
     bool pok = false;
     auto store_pending = [&](int q) {
         if (pok)
-            io::store4(oh + prow * D + 32 * cb + 8 * q + 4 * h, pend[q]);
+            io::store4(oh + prow * ol.sn + 32 * cb + 8 * q + 4 * h, pend[q]);
     };
 
     for (int64_t round = 0; round < nrounds; ++round) {
@@ -1210,7 +1210,7 @@ __device__ __forceinline__ void kv_pass_bf(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ G, uint16_t *__restrict__ dK,
     uint16_t *__restrict__ dV, const float *__restrict__ cbuf, const float *__restrict__ rec,
-    int64_t N, int64_t seg_len, int nseg, KvBfLds<D> &L)
+    int64_t N, int64_t seg_len, int nseg, OutLay ol, KvBfLds<D> &L)
 {
     typedef nc::IO<StBF16> io;
     constexpr int NCB = D / 32, NT = 64 * NCB, LDX = D + 8, WP = kCc + 1;
@@ -1223,7 +1223,7 @@ __device__ __forceinline__ void kv_pass_bf(
     const int64_t hoff = bh * N * D;
     const float *st = rec + (bh * nseg + seg) * (int64_t)(D * D + 2 * D);
     const uint16_t *xh = (PAR == 0 ? V : K) + hoff, *qh = Q + hoff, *gh = G + hoff;
-    uint16_t *oh = (PAR == 0 ? dK : dV) + hoff;
+    uint16_t *oh = (PAR == 0 ? dK : dV) + ol.head(bh);
     const float2 *ch = reinterpret_cast<const float2 *>(cbuf) + bh * N;
 
     ChunkRows<D, NT> rx, rq, rg;
@@ -1353,7 +1353,7 @@ __device__ __forceinline__ void kv_pass_bf(
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const f4 v = *reinterpret_cast<const f4 *>(&L.vr[32 * cb + 8 * q + 4 * h]);
-                io::store4(oh + (t0 + j) * D + 32 * cb + 8 * q + 4 * h,
+                io::store4(oh + (t0 + j) * ol.sn + 32 * cb + 8 * q + 4 * h,
                            f4{acc[4 * q] + sg * v[0], acc[4 * q + 1] + sg * v[1],
                               acc[4 * q + 2] + sg * v[2], acc[4 * q + 3] + sg * v[3]});
             }
@@ -1374,13 +1374,13 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_kv_causal_bf(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ G, uint16_t *__restrict__ dK,
     uint16_t *__restrict__ dV, const float *__restrict__ cbuf, const float *__restrict__ rec,
-    int64_t N, int64_t seg_len, int nseg)
+    int64_t N, int64_t seg_len, int nseg, OutLay ol)
 {
     __shared__ __attribute__((aligned(16))) KvBfLds<D> lds;
     if (blockIdx.x & 1)
-        kv_pass_bf<D, 1>(Q, K, V, G, dK, dV, cbuf, rec, N, seg_len, nseg, lds);
+        kv_pass_bf<D, 1>(Q, K, V, G, dK, dV, cbuf, rec, N, seg_len, nseg, ol, lds);
     else
-        kv_pass_bf<D, 0>(Q, K, V, G, dK, dV, cbuf, rec, N, seg_len, nseg, lds);
+        kv_pass_bf<D, 0>(Q, K, V, G, dK, dV, cbuf, rec, N, seg_len, nseg, ol, lds);
 }
 
 }  // namespace bf

@@ -192,7 +192,7 @@ __global__ __launch_bounds__(threads<D>()) void k_fwd_causal(
     const typename ST::T *__restrict__ Q, const typename ST::T *__restrict__ K,
     const typename ST::T *__restrict__ V, typename ST::T *__restrict__ O,
     float *__restrict__ den_out, const float *__restrict__ rec, int64_t N, int64_t seg_len,
-    int nseg, float n0)
+    int nseg, float n0, OutLay ol)
 {
     typedef typename ST::T T;
     typedef IO<ST> io;
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(threads<D>()) void k_fwd_causal(
     const int64_t hoff = bh * N * D;
     const float *st = rec + (bh * nseg + seg) * (int64_t)(D * D + 2 * D);
     const T *qh = Q + hoff, *kh = K + hoff, *vh = V + hoff;
-    T *oh = O + hoff;
+    T *oh = O + ol.head(bh);
 
     Rows<ST, D, NT> rq, rk, rv;
     const int64_t nrounds = (end - beg + kC - 1) / kC;
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(threads<D>()) void k_fwd_causal(
     bool pok = false;
     auto store_pending = [&](int q) {
         if (pok)
-            io::store4(oh + prow * D + 32 * cb + 8 * q + 4 * h, pend[q]);
+            io::store4(oh + prow * ol.sn + 32 * cb + 8 * q + 4 * h, pend[q]);
     };
 
     for (int64_t round = 0; round < nrounds; ++round) {
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(threads<D>()) void k_bwd_q_causal(
     const typename ST::T *__restrict__ Q, const typename ST::T *__restrict__ K,
     const typename ST::T *__restrict__ V, const typename ST::T *__restrict__ G,
     typename ST::T *__restrict__ dQ, float *__restrict__ cbuf, const float *__restrict__ rec,
-    int64_t N, int64_t seg_len, int nseg, float n0)
+    int64_t N, int64_t seg_len, int nseg, float n0, OutLay ol)
 {
     typedef typename ST::T T;
     typedef IO<ST> io;
@@ -379,7 +379,7 @@ __global__ __launch_bounds__(threads<D>()) void k_bwd_q_causal(
     const int64_t hoff = bh * N * D;
     const float *st = rec + (bh * nseg + seg) * (int64_t)(D * D + 2 * D);
     const T *qh = Q + hoff, *kh = K + hoff, *vh = V + hoff, *gh = G + hoff;
-    T *oh = dQ + hoff;
+    T *oh = dQ + ol.head(bh);
 
     Rows<ST, D, NT> rq, rk, rv, rg;
     const int64_t nrounds = (end - beg + kC - 1) / kC;
@@ -419,7 +419,7 @@ __global__ __launch_bounds__(threads<D>()) void k_bwd_q_causal(
     bool pok = false;
     auto store_pending = [&](int q) {
         if (pok)
-            io::store4(oh + prow * D + 32 * cb + 8 * q + 4 * h, pend[q]);
+            io::store4(oh + prow * ol.sn + 32 * cb + 8 * q + 4 * h, pend[q]);
     };
 
     for (int64_t round = 0; round < nrounds; ++round) {
@@ -580,7 +580,7 @@ __device__ __forceinline__ void kv_pass(
     const typename ST::T *__restrict__ V, const typename ST::T *__restrict__ G,
     typename ST::T *__restrict__ dK, typename ST::T *__restrict__ dV,
     const float *__restrict__ cbuf, const float *__restrict__ rec, int64_t N, int64_t seg_len,
-    int nseg, KvLds<D> &L)
+    int nseg, OutLay ol, KvLds<D> &L)
 {
     typedef typename ST::T T;
     typedef IO<ST> io;
@@ -598,7 +598,7 @@ __device__ __forceinline__ void kv_pass(
     const int64_t hoff = bh * N * D;
     const float *st = rec + (bh * nseg + seg) * (int64_t)(D * D + 2 * D);
     const T *xh = (PAR == 0 ? V : K) + hoff, *qh = Q + hoff, *gh = G + hoff;
-    T *oh = (PAR == 0 ? dK : dV) + hoff;
+    T *oh = (PAR == 0 ? dK : dV) + ol.head(bh);
     const float2 *ch = reinterpret_cast<const float2 *>(cbuf) + bh * N;
 
     Rows<ST, D, NT> rx, rq, rg;
@@ -717,7 +717,7 @@ __device__ __forceinline__ void kv_pass(
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const f4 v = *reinterpret_cast<const f4 *>(&vr[32 * cb + 8 * q + 4 * h]);
-                io::store4(oh + (t0 + j) * D + 32 * cb + 8 * q + 4 * h,
+                io::store4(oh + (t0 + j) * ol.sn + 32 * cb + 8 * q + 4 * h,
                            f4{acc[4 * q] + sg * v[0], acc[4 * q + 1] + sg * v[1],
                               acc[4 * q + 2] + sg * v[2], acc[4 * q + 3] + sg * v[3]});
             }
@@ -742,13 +742,13 @@ __global__ __launch_bounds__(threads<D>()) __attribute__((amdgpu_waves_per_eu(2)
     const typename ST::T *__restrict__ V, const typename ST::T *__restrict__ G,
     typename ST::T *__restrict__ dK, typename ST::T *__restrict__ dV,
     const float *__restrict__ cbuf, const float *__restrict__ rec, int64_t N, int64_t seg_len,
-    int nseg)
+    int nseg, OutLay ol)
 {
     __shared__ __attribute__((aligned(16))) KvLds<D> lds;
     if (blockIdx.x & 1)
-        kv_pass<ST, D, 1>(Q, K, V, G, dK, dV, cbuf, rec, N, seg_len, nseg, lds);
+        kv_pass<ST, D, 1>(Q, K, V, G, dK, dV, cbuf, rec, N, seg_len, nseg, ol, lds);
     else
-        kv_pass<ST, D, 0>(Q, K, V, G, dK, dV, cbuf, rec, N, seg_len, nseg, lds);
+        kv_pass<ST, D, 0>(Q, K, V, G, dK, dV, cbuf, rec, N, seg_len, nseg, ol, lds);
 }
 
 }  // namespace cz

@@ -509,7 +509,7 @@ __global__ __launch_bounds__(apply_threads<D>()) void k_apply_nc(
     const typename ST::T *__restrict__ X, const typename ST::T *__restrict__ X2,
     typename ST::T *__restrict__ Out, typename ST::T *__restrict__ Out2,
     float *__restrict__ den_out, const float *__restrict__ rec, int64_t N, int64_t seg_len,
-    int nseg, float n0)
+    int nseg, float n0, OutLay ol)
 {
     typedef typename ST::T T;
     typedef IO<ST> io;
@@ -546,7 +546,7 @@ __global__ __launch_bounds__(apply_threads<D>()) void k_apply_nc(
     const bool colread = (KIND == 0) || (KIND == 2 && sub == 1);
 
     const T *xh = ((KIND == 2 && sub == 1) ? X2 : X) + hoff;
-    T *oh = ((KIND == 2 && sub == 1) ? Out2 : Out) + hoff;
+    T *oh = ((KIND == 2 && sub == 1) ? Out2 : Out) + ol.head(bh);
 
     // staging: thread's chunk p of a round covers row (tid + p*NT) / CPR,
     // columns VEC*((tid + p*NT) % CPR) ..
@@ -649,7 +649,7 @@ __global__ __launch_bounds__(apply_threads<D>()) void k_apply_nc(
     bool pok = false;
     auto store_pending = [&](int q) {
         if (pok)
-            io::store4(oh + prow * D + 32 * cb + 8 * q + 4 * h, pend[q]);
+            io::store4(oh + prow * ol.sn + 32 * cb + 8 * q + 4 * h, pend[q]);
     };
 
     for (int64_t round = 0; round < nrounds; ++round) {
@@ -774,7 +774,7 @@ template <class ST, int D, bool DS = true>
 __global__ __launch_bounds__(512) void k_bwd_q_nc(
     const typename ST::T *__restrict__ G, const typename ST::T *__restrict__ Q,
     typename ST::T *__restrict__ dQ, float *__restrict__ part_out,
-    const float *__restrict__ rec, int64_t N, int64_t seg_len, int nseg, float n0)
+    const float *__restrict__ rec, int64_t N, int64_t seg_len, int nseg, float n0, OutLay ol)
 {
     typedef typename ST::T T;
     typedef IO<ST> io;
@@ -810,7 +810,7 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
     const int64_t hoff = bh * N * D;
     const float *st = rec + bh * (int64_t)(D * D + 2 * D);
     const T *gh = G + hoff, *qh = Q + hoff;
-    T *oh = dQ + hoff;
+    T *oh = dQ + ol.head(bh);
 
     // rows load through descriptors over the segment (rows past its end read
     // zeros); the lane's offsets are fixed, the round's is a scalar
@@ -988,7 +988,7 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
                 const f4 o = {acc[4 * q] - c * z[0], acc[4 * q + 1] - c * z[1],
                               acc[4 * q + 2] - c * z[2], acc[4 * q + 3] - c * z[3]};
                 if (row < end)
-                    io::store4(oh + row * D + 32 * cb + 8 * q + 4 * h, o);
+                    io::store4(oh + row * ol.sn + 32 * cb + 8 * q + 4 * h, o);
             }
             if constexpr (DS) {
                 if (cb == 0 && h == 0)

@@ -52,31 +52,37 @@ __global__ __launch_bounds__(kThreads) void k_pad(const typename ST::T *__restri
     }
 }
 
-// [rows, Dp] -> [rows, D]: the first D columns of each padded row.  A thread
-// reads one 16-byte chunk of a padded row and writes its part below D.
+// [rows, Dp] -> the first D columns of each padded row, written to row n of
+// head bh (r = bh * N + n) in the output layout ol.  A thread reads one
+// 16-byte chunk of a padded row and writes its part below D, as one 16-byte
+// store when the columns and every stride of the layout allow it.
 template <class ST>
 __global__ __launch_bounds__(kThreads) void k_unpad(const typename ST::T *__restrict__ src,
                                                     typename ST::T *__restrict__ dst,
-                                                    int64_t rows, int D, int Dp)
+                                                    int64_t rows, int D, int Dp, int64_t N,
+                                                    OutLay ol)
 {
     typedef typename ST::T T;
     constexpr int V = 16 / sizeof(T);
     const int cpr = (D + V - 1) / V;          // chunks holding real columns
     const int64_t total = rows * cpr;
+    const bool vec = D % V == 0 && ol.sn % V == 0 && ol.sh % V == 0 && ol.sb % V == 0;
     for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < total;
          i += (int64_t)gridDim.x * kThreads) {
         const int64_t r = i / cpr;
         const int c0 = (int)(i - r * cpr) * V;
         const uint4 in = *reinterpret_cast<const uint4 *>(src + r * Dp + c0);
-        if (D % V == 0) {
-            *reinterpret_cast<uint4 *>(dst + r * D + c0) = in;
+        const int64_t bh = r / N;
+        T *drow = dst + ol.head(bh) + (r - bh * N) * ol.sn;
+        if (vec) {
+            *reinterpret_cast<uint4 *>(drow + c0) = in;
         } else {
             T e[V];
             *reinterpret_cast<uint4 *>(e) = in;
 #pragma unroll
             for (int x = 0; x < V; ++x)
                 if (c0 + x < D)
-                    dst[r * D + c0 + x] = e[x];
+                    drow[c0 + x] = e[x];
         }
     }
 }

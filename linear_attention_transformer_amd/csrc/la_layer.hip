@@ -7,14 +7,20 @@
 // Wo [H D, C]:
 //
 //     [Q | K | V] = X Wqkv        (columns: H heads of D for each of Q, K, V)
-//     O_h = LA(Q_h, K_h, V_h)     (la_forward, every head h)
+//     O_h = LA(Q_h, K_h, V_h)     (the library's attention, every head h)
 //     Y = [O_1 .. O_H] Wo
 //
-// The projections are plain GEMMs and run on rocBLAS (gemm_ex, fp32
-// accumulation, storage-type inputs and outputs); the head split and merge
-// between the row layout [B, N, T, H, D] and the head layout [B, H, N, D] of
-// the attention passes is a kernel of this file; the attention is the
-// library's own la_forward / la_backward.
+// The projections are GEMMs on rocBLAS (fp32 accumulation, storage-type
+// inputs and outputs) arranged so that no pass moves rows between layouts:
+//   - the QKV projection is one strided-batched GEMM per (sequence, Q|K|V)
+//     over the heads, writing each head's [N, D] block straight into the
+//     [B, H, N, D] tensors the attention reads;
+//   - the attention writes O in the row layout [B, N, H, D], which the output
+//     projection and its weight gradient take as a plain [B N, H D] matrix;
+//   - backward, dO is formed per (sequence) by one strided-batched GEMM over
+//     the heads in the [B, H, N, D] layout, and the attention writes dQ, dK,
+//     dV side by side in the row layout [B, N, 3, H, D], which the two
+//     gradient GEMMs of the projection take as a plain [B N, 3 H D] matrix.
 #include <hip/hip_runtime.h>
 #include <rocblas/rocblas.h>
 
@@ -23,82 +29,15 @@
 #include <mutex>
 
 #include "la.h"
+#include "la_internal.hpp"
 
 namespace {
 
-constexpr int kThreads = 256;
 constexpr size_t kBlasWorkspace = (size_t)64 << 20;   // rocBLAS scratch, from the caller's workspace
 
 size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 
 size_t esize(int dtype) { return dtype == LA_FP32 ? 4 : 2; }
-
-// Rows of the [B, N, T*H*D] row layout <-> T tensors [B, H, N, D].  A
-// workgroup walks whole rows (b, n); its threads take consecutive chunks of
-// the row (16 bytes when D allows, else one element), so both sides move
-// contiguous runs.
-template <class E, bool TO_HEADS>
-__global__ __launch_bounds__(kThreads) void k_heads(E *__restrict__ rows_, E *__restrict__ t0,
-                                                    E *__restrict__ t1, E *__restrict__ t2,
-                                                    int64_t BN, int64_t N, int T, int H, int D)
-{
-    constexpr int V = 16 / sizeof(E);
-    const bool vec = D % V == 0;
-    const int W = vec ? V : 1;                       // elements per chunk
-    const int row_len = T * H * D;
-    const int chunks = row_len / W;
-    for (int64_t r = blockIdx.x; r < BN; r += gridDim.x) {
-        const int64_t b = r / N, n = r - b * N;
-        E *row = rows_ + r * row_len;
-        for (int ch = threadIdx.x; ch < chunks; ch += kThreads) {
-            const int e = ch * W;
-            const int c = e % D, th = e / D;
-            const int h = th % H, t = th / H;
-            E *tens = t == 0 ? t0 : (t == 1 ? t1 : t2);
-            E *hp = tens + ((b * H + h) * N + n) * (int64_t)D + c;
-            E *rp = row + e;
-            if (vec) {
-                if (TO_HEADS)
-                    *reinterpret_cast<uint4 *>(hp) = *reinterpret_cast<const uint4 *>(rp);
-                else
-                    *reinterpret_cast<uint4 *>(rp) = *reinterpret_cast<const uint4 *>(hp);
-            } else {
-                if (TO_HEADS)
-                    *hp = *rp;
-                else
-                    *rp = *hp;
-            }
-        }
-    }
-}
-
-int heads(bool to_heads, void *rows_, void *t0, void *t1, void *t2, int64_t BN, int64_t N,
-          int T, int64_t H, int64_t D, int dtype, hipStream_t s)
-{
-    const dim3 grid((unsigned)std::min<int64_t>(BN, 8192)), blk(kThreads);
-    if (dtype == LA_FP32) {
-        if (to_heads)
-            k_heads<float, true><<<grid, blk, 0, s>>>(
-                static_cast<float *>(rows_), static_cast<float *>(t0), static_cast<float *>(t1),
-                static_cast<float *>(t2), BN, N, T, (int)H, (int)D);
-        else
-            k_heads<float, false><<<grid, blk, 0, s>>>(
-                static_cast<float *>(rows_), static_cast<float *>(t0), static_cast<float *>(t1),
-                static_cast<float *>(t2), BN, N, T, (int)H, (int)D);
-    } else {
-        if (to_heads)
-            k_heads<uint16_t, true><<<grid, blk, 0, s>>>(
-                static_cast<uint16_t *>(rows_), static_cast<uint16_t *>(t0),
-                static_cast<uint16_t *>(t1), static_cast<uint16_t *>(t2), BN, N, T, (int)H,
-                (int)D);
-        else
-            k_heads<uint16_t, false><<<grid, blk, 0, s>>>(
-                static_cast<uint16_t *>(rows_), static_cast<uint16_t *>(t0),
-                static_cast<uint16_t *>(t1), static_cast<uint16_t *>(t2), BN, N, T, (int)H,
-                (int)D);
-    }
-    return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
-}
 
 // An error that earlier HIP calls on this thread left pending is not this
 // call's: it launches nothing and leaves the error pending (as the head-batch
@@ -160,12 +99,31 @@ int gemm(rocblas_handle h, bool ta, bool tb, int64_t M, int64_t Nc, int64_t K, c
     return st == rocblas_status_success ? LA_OK : LA_ERR_HIP;
 }
 
+// The same for `count` products C_i = op(A_i) op(B_i), A_i = A + i * sa,
+// B_i = B + i * sb, C_i = C + i * sc (elements; a stride of 0 reuses one
+// matrix for every product).
+int gemm_batched(rocblas_handle h, bool ta, bool tb, int64_t M, int64_t Nc, int64_t K,
+                 const void *A, int64_t lda, int64_t sa, const void *B, int64_t ldb, int64_t sb,
+                 void *C, int64_t ldc, int64_t sc, int64_t count, int dtype)
+{
+    const float one = 1.f, zero = 0.f;
+    const rocblas_datatype t = blas_type(dtype);
+    const rocblas_status st = rocblas_gemm_strided_batched_ex(
+        h, tb ? rocblas_operation_transpose : rocblas_operation_none,
+        ta ? rocblas_operation_transpose : rocblas_operation_none, (rocblas_int)Nc,
+        (rocblas_int)M, (rocblas_int)K, &one, B, t, (rocblas_int)ldb, (rocblas_stride)sb, A, t,
+        (rocblas_int)lda, (rocblas_stride)sa, &zero, C, t, (rocblas_int)ldc, (rocblas_stride)sc,
+        C, t, (rocblas_int)ldc, (rocblas_stride)sc, (rocblas_int)count, rocblas_datatype_f32_r,
+        rocblas_gemm_algo_standard, 0, 0);
+    return st == rocblas_status_success ? LA_OK : LA_ERR_HIP;
+}
+
 // ------------------------------------------------------------ layout
 // saved (forward -> backward): Q, K, V [B,H,N,D], O in rows [B,N,H*D], the
-// attention state.  Forward workspace: QKV rows [B,N,3HD], O [B,H,N,D], the
-// attention workspace, rocBLAS scratch (+ the saved tensors when no saved
-// buffer is given).  Backward workspace: dO rows, dO, dQ, dK, dV, dQKV rows,
-// the attention workspace, rocBLAS scratch.
+// attention state.  Forward workspace: the attention workspace and rocBLAS
+// scratch (+ the saved tensors when no saved buffer is given).  Backward
+// workspace: dO [B,H,N,D], dQKV rows [B,N,3HD], the attention workspace,
+// rocBLAS scratch.
 struct Sizes {
     size_t head, rows1, rows3, state, la_ws;
     size_t saved;        // Q K V O-rows state
@@ -182,8 +140,8 @@ Sizes sizes(int64_t B, int64_t N, int64_t C, int64_t H, int64_t D, int causal, i
     z.state = up256(la_state_size(B, H, N, D, causal));
     z.la_ws = up256(la_workspace_size_for(B, H, N, D, causal, dtype));
     z.saved = 3 * z.head + z.rows1 + z.state;
-    z.fwd = z.rows3 + z.head + z.la_ws + kBlasWorkspace + z.saved;
-    z.bwd = z.rows1 + 4 * z.head + z.rows3 + z.la_ws + kBlasWorkspace;
+    z.fwd = z.la_ws + kBlasWorkspace + z.saved;
+    z.bwd = z.head + z.rows3 + z.la_ws + kBlasWorkspace;
     (void)C;
     return z;
 }
@@ -276,10 +234,10 @@ int la_layer_forward(const void *X, const void *Wqkv, const void *Wo, void *Y, i
     if (misaligned(X) || misaligned(Wqkv) || misaligned(Wo) || misaligned(Y) ||
         misaligned(saved) || misaligned(ws))
         return LA_ERR_ALIGN;
-    const size_t s = esize(dtype), HD = (size_t)(H * D);
+    const size_t s = esize(dtype), hd = (size_t)(H * D);
     const Range ins[3] = {{(const char *)X, (size_t)(B * N * C) * s},
-                          {(const char *)Wqkv, (size_t)C * 3 * HD * s},
-                          {(const char *)Wo, HD * (size_t)C * s}};
+                          {(const char *)Wqkv, (size_t)C * 3 * hd * s},
+                          {(const char *)Wo, hd * (size_t)C * s}};
     const Range outs[3] = {{(const char *)Y, (size_t)(B * N * C) * s},
                            {(const char *)saved, saved ? z.saved : 0},
                            {(const char *)ws, need}};
@@ -290,9 +248,9 @@ int la_layer_forward(const void *X, const void *Wqkv, const void *Wo, void *Y, i
     char *sv = saved ? static_cast<char *>(saved) : w + (z.fwd - z.saved);
     void *q = sv, *k = sv + z.head, *v = sv + 2 * z.head, *orows = sv + 3 * z.head;
     void *state = sv + 3 * z.head + z.rows1;
-    void *qkv = w, *o = w + z.rows3, *law = w + z.rows3 + z.head;
-    void *bw = w + z.rows3 + z.head + z.la_ws;
-    const int64_t BN = B * N;
+    void *law = w, *bw = w + z.la_ws;
+    const int64_t BN = B * N, HD = H * D;
+    const size_t es = esize(dtype);
 
     if ((rc = pending_error()) != LA_OK)
         return rc;
@@ -304,22 +262,28 @@ int la_layer_forward(const void *X, const void *Wqkv, const void *Wo, void *Y, i
         if (rocblas_set_stream(bl->h, st) != rocblas_status_success ||
             rocblas_set_workspace(bl->h, bw, kBlasWorkspace) != rocblas_status_success)
             return LA_ERR_HIP;
-        if ((rc = gemm(bl->h, false, false, BN, 3 * H * D, C, X, C, Wqkv, 3 * H * D, qkv,
-                       3 * H * D, dtype)) != LA_OK)
-            return rc;
+        // head h of Q (j = 0), K (1), V (2) of sequence b:
+        // X_b [N, C] . Wqkv[:, j HD + h D ..] [C, D] -> [N, D] at (b H + h) N D
+        void *dst[3] = {q, k, v};
+        for (int64_t b = 0; b < B; ++b)
+            for (int j = 0; j < 3; ++j)
+                if ((rc = gemm_batched(bl->h, false, false, N, D, C,
+                                       static_cast<const char *>(X) + (size_t)(b * N * C) * es, C,
+                                       0, static_cast<const char *>(Wqkv) + (size_t)(j * HD) * es,
+                                       3 * HD, D,
+                                       static_cast<char *>(dst[j]) + (size_t)(b * H * N * D) * es,
+                                       D, N * D, H, dtype)) != LA_OK)
+                    return rc;
     }
-    if ((rc = heads(true, qkv, q, k, v, BN, N, 3, H, D, dtype, st)) != LA_OK)
-        return rc;
-    if ((rc = la_forward(q, k, v, o, B, H, N, D, causal, dtype, nullptr, state, law, z.la_ws,
-                         stream)) != LA_OK)
-        return rc;
-    if ((rc = heads(false, orows, o, nullptr, nullptr, BN, N, 1, H, D, dtype, st)) != LA_OK)
+    // O straight into the rows [B, N, H, D]
+    if ((rc = la_internal::forward_to(q, k, v, orows, B, H, N, D, causal, dtype, state, law,
+                                      z.la_ws, stream, {N * HD, D, HD})) != LA_OK)
         return rc;
     std::lock_guard<std::mutex> lk(bl->m);
     if (rocblas_set_stream(bl->h, st) != rocblas_status_success ||
         rocblas_set_workspace(bl->h, bw, kBlasWorkspace) != rocblas_status_success)
         return LA_ERR_HIP;
-    return gemm(bl->h, false, false, BN, C, H * D, orows, H * D, Wo, C, Y, C, dtype);
+    return gemm(bl->h, false, false, BN, C, HD, orows, HD, Wo, C, Y, C, dtype);
 }
 
 int la_layer_backward(const void *X, const void *Wqkv, const void *Wo, const void *dY,
@@ -343,15 +307,15 @@ int la_layer_backward(const void *X, const void *Wqkv, const void *Wo, const voi
         misaligned(dX) || misaligned(dWqkv) || misaligned(dWo) || misaligned(saved) ||
         misaligned(ws))
         return LA_ERR_ALIGN;
-    const size_t s = esize(dtype), HD = (size_t)(H * D);
+    const size_t s = esize(dtype), hd = (size_t)(H * D);
     const Range ins[5] = {{(const char *)X, (size_t)(B * N * C) * s},
-                          {(const char *)Wqkv, (size_t)C * 3 * HD * s},
-                          {(const char *)Wo, HD * (size_t)C * s},
+                          {(const char *)Wqkv, (size_t)C * 3 * hd * s},
+                          {(const char *)Wo, hd * (size_t)C * s},
                           {(const char *)dY, (size_t)(B * N * C) * s},
                           {(const char *)saved, z.saved}};
     const Range outs[4] = {{(const char *)dX, (size_t)(B * N * C) * s},
-                           {(const char *)dWqkv, (size_t)C * 3 * HD * s},
-                           {(const char *)dWo, HD * (size_t)C * s},
+                           {(const char *)dWqkv, (size_t)C * 3 * hd * s},
+                           {(const char *)dWo, hd * (size_t)C * s},
                            {(const char *)ws, z.bwd}};
     if (aliased(outs, 4, ins, 5))
         return LA_ERR_ALIAS;
@@ -360,11 +324,10 @@ int la_layer_backward(const void *X, const void *Wqkv, const void *Wo, const voi
     const void *q = sv, *k = sv + z.head, *v = sv + 2 * z.head, *orows = sv + 3 * z.head;
     const void *state = sv + 3 * z.head + z.rows1;
     char *w = static_cast<char *>(ws);
-    void *dorows = w, *dO = w + z.rows1, *dq = w + z.rows1 + z.head,
-         *dk = w + z.rows1 + 2 * z.head, *dv = w + z.rows1 + 3 * z.head,
-         *dqkv = w + z.rows1 + 4 * z.head, *law = w + z.rows1 + 4 * z.head + z.rows3;
-    void *bw = w + z.rows1 + 4 * z.head + z.rows3 + z.la_ws;
-    const int64_t BN = B * N;
+    void *dO = w, *dqkv = w + z.head, *law = w + z.head + z.rows3;
+    void *bw = w + z.head + z.rows3 + z.la_ws;
+    const int64_t BN = B * N, HD = H * D;
+    const size_t es = esize(dtype);
 
     if ((rc = pending_error()) != LA_OK)
         return rc;
@@ -376,30 +339,34 @@ int la_layer_backward(const void *X, const void *Wqkv, const void *Wo, const voi
         if (rocblas_set_stream(bl->h, st) != rocblas_status_success ||
             rocblas_set_workspace(bl->h, bw, kBlasWorkspace) != rocblas_status_success)
             return LA_ERR_HIP;
-        // dWo = O_rows^T dY ; dO_rows = dY Wo^T
-        if ((rc = gemm(bl->h, true, false, H * D, C, BN, orows, H * D, dY, C, dWo, C, dtype)) !=
-                LA_OK ||
-            (rc = gemm(bl->h, false, true, BN, H * D, C, dY, C, Wo, C, dorows, H * D, dtype)) !=
-                LA_OK)
+        // dWo = O_rows^T dY
+        if ((rc = gemm(bl->h, true, false, HD, C, BN, orows, HD, dY, C, dWo, C, dtype)) != LA_OK)
             return rc;
+        // head h of dO of sequence b: dY_b [N, C] . (rows h D .. of Wo)^T [C, D]
+        for (int64_t b = 0; b < B; ++b)
+            if ((rc = gemm_batched(bl->h, false, true, N, D, C,
+                                   static_cast<const char *>(dY) + (size_t)(b * N * C) * es, C, 0,
+                                   Wo, C, D * C,
+                                   static_cast<char *>(dO) + (size_t)(b * H * N * D) * es, D,
+                                   N * D, H, dtype)) != LA_OK)
+                return rc;
     }
-    if ((rc = heads(true, dorows, dO, nullptr, nullptr, BN, N, 1, H, D, dtype, st)) != LA_OK)
-        return rc;
-    if ((rc = la_backward(q, k, v, dO, dq, dk, dv, B, H, N, D, causal, dtype, state, law,
-                          z.la_ws, stream)) != LA_OK)
-        return rc;
-    if ((rc = heads(false, dqkv, dq, dk, dv, BN, N, 3, H, D, dtype, st)) != LA_OK)
+    // dQ, dK, dV side by side in the rows [B, N, 3, H, D]
+    char *dq = static_cast<char *>(dqkv);
+    if ((rc = la_internal::backward_to(q, k, v, dO, dq, dq + (size_t)HD * es,
+                                       dq + (size_t)(2 * HD) * es, B, H, N, D, causal, dtype,
+                                       state, law, z.la_ws, stream, {N * 3 * HD, D, 3 * HD})) !=
+        LA_OK)
         return rc;
     std::lock_guard<std::mutex> lk(bl->m);
     if (rocblas_set_stream(bl->h, st) != rocblas_status_success ||
         rocblas_set_workspace(bl->h, bw, kBlasWorkspace) != rocblas_status_success)
         return LA_ERR_HIP;
     // dWqkv = X^T dQKV ; dX = dQKV Wqkv^T
-    if ((rc = gemm(bl->h, true, false, C, 3 * H * D, BN, X, C, dqkv, 3 * H * D, dWqkv,
-                   3 * H * D, dtype)) != LA_OK)
+    if ((rc = gemm(bl->h, true, false, C, 3 * HD, BN, X, C, dqkv, 3 * HD, dWqkv, 3 * HD,
+                   dtype)) != LA_OK)
         return rc;
-    return gemm(bl->h, false, true, BN, C, 3 * H * D, dqkv, 3 * H * D, Wqkv, 3 * H * D, dX, C,
-                dtype);
+    return gemm(bl->h, false, true, BN, C, 3 * HD, dqkv, 3 * HD, Wqkv, 3 * HD, dX, C, dtype);
 }
 
 }  // extern "C"
