@@ -496,7 +496,12 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
         if (dK == nullptr)
             return LA_OK;
         return traced(t, s, "bwd_kv", [&] {
-            if constexpr (std::is_same<ST, StBF16>::value)
+            if constexpr (std::is_same<ST, StBF16>::value && D >= 64)
+                bf::k_bwd_kv_causal_bf2<D><<<dim3((unsigned)(p.nseg * p.BH)), dim3(128 * (D / 32)),
+                                             0, s>>>(q, k, v, g, static_cast<T *>(dK),
+                                                     static_cast<T *>(dV), cbuf, gpart, p.N,
+                                                     p.seg_len, (int)p.nseg, p.ol);
+            else if constexpr (std::is_same<ST, StBF16>::value)
                 bf::k_bwd_kv_causal_bf<D><<<dim3((unsigned)(2 * p.nseg * p.BH)), nt, 0, s>>>(
                     q, k, v, g, static_cast<T *>(dK), static_cast<T *>(dV), cbuf, gpart, p.N,
                     p.seg_len, (int)p.nseg, p.ol);

@@ -1383,5 +1383,330 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_kv_causal_bf(
         kv_pass_bf<D, 0>(Q, K, V, G, dK, dV, cbuf, rec, N, seg_len, nseg, ol, lds);
 }
 
+// ============================================================ causal dK | dV, one pass
+// The causal dK | dV pass of one segment in a single workgroup (D = 64, 128):
+// waves 0 .. NCB-1 form the 32-column blocks of dK, waves NCB .. 2 NCB - 1
+// those of dV, over the segment's chunks in reverse order.  The suffix state R
+// (sum over the rows after the chunk of q_i a_i^T) is kept once: every wave
+// owns NCB/2 of its 32 x 32 tiles as fp32 MFMA accumulators, updates them by
+// the chunk (R += Q_c^T A_c) and writes them after each chunk as hi and lo
+// bf16 planes in LDS, laid out [b][a] (column-major R), from which both
+// products read their operand: dK = V_c R^T - r (8 consecutive b of a row of
+// R, gathered by the LDS transpose read) and dV = K_c R + t (contiguous runs
+// of 8 a).  The chunk's rows of Q, K, V and A = dO / den (hi and lo) are
+// staged once, as natural rows; the in-chunk blocks P = M o (A V^T - c) and
+// W = M o (1 + Q K^T) are formed by one wave each and stored [j][i] as hi /
+// lo planes.  Products over the chunk's tokens (R's update, P^T Q, W^T A)
+// read 8 consecutive tokens of a column with two ds_read_b64_tr_b16.  The
+// column sums r = sum c_i q_i and t = sum a_i run in registers of D threads.
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16 on gfx950: within each group of 16 lanes, lane p = 4e + f
+// points at row r0 + e, columns c0 + 4f .. + 3 of a row-major bf16 tile;
+// lane i of the group then receives rows r0 .. r0 + 3 of column c0 + i.
+__device__ __forceinline__ v4s tr4(const uint16_t *tile, int pitch, int r0, int c0, int p)
+{
+    const uint16_t *a = tile + (r0 + (p >> 2)) * pitch + c0 + 4 * (p & 3);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(a));
+}
+
+// the MFMA operand of lane (j, h) = 32 h + j: rows rb + 8 h .. + 7 of column
+// cb0 + j (8 consecutive tokens of one column)
+__device__ __forceinline__ bf8 col8(const uint16_t *tile, int pitch, int rb, int cb0, int lane)
+{
+    const int g = lane >> 4, p = lane & 15;
+    const int r0 = rb + 8 * (g >> 1), c0 = cb0 + 16 * (g & 1);
+    const v4s x = tr4(tile, pitch, r0, c0, p);
+    const v4s y = tr4(tile, pitch, r0 + 4, c0, p);
+    const uint2 ux = __builtin_bit_cast(uint2, x), uy = __builtin_bit_cast(uint2, y);
+    return __builtin_bit_cast(bf8, uint4{ux.x, ux.y, uy.x, uy.y});
+}
+
+// the MFMA operand of lane (j, h): row rb + j, columns c + 8 h .. + 7
+__device__ __forceinline__ bf8 row8(const uint16_t *tile, int pitch, int rb, int c, int j, int h)
+{
+    return *reinterpret_cast<const bf8 *>(tile + (rb + j) * pitch + c + 8 * h);
+}
+
+// two fp32 as hi and lo bf16 pairs (a in the low halves): one paired
+// round-to-nearest conversion for hi, the residuals, one for lo
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo)
+{
+    hi = StBF16::narrow2(a, b);
+    lo = StBF16::narrow2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+
+// four fp32 as hi and lo bf16 (two 8-byte words)
+__device__ __forceinline__ void split4(float a, float b, float c, float d, uint2 &hi, uint2 &lo)
+{
+    split2(a, b, hi.x, lo.x);
+    split2(c, d, hi.y, lo.y);
+}
+
+template <int D>
+struct KvBf2Lds {
+    static constexpr int LDX = D + 8;    // natural row pitch (bf16)
+    static constexpr int RP = D + 8;     // R planes: element (a, b) at b * RP + a
+    static constexpr int PP = kCc + 8;   // P, W planes: element (i, j) at j * PP + i
+    uint16_t q[kCc * LDX], k[kCc * LDX], v[kCc * LDX], ahi[kCc * LDX], alo[kCc * LDX];
+    uint16_t rhi[D * RP], rlo[D * RP];
+    uint16_t phi[kCc * PP], plo[kCc * PP], whi[kCc * PP], wlo[kCc * PP];
+    float cs[kCc];
+    float vr[D], vt[D];
+};
+
+template <int D>
+__global__ __launch_bounds__(128 * (D / 32)) void k_bwd_kv_causal_bf2(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const uint16_t *__restrict__ G, uint16_t *__restrict__ dK,
+    uint16_t *__restrict__ dV, const float *__restrict__ cbuf, const float *__restrict__ rec,
+    int64_t N, int64_t seg_len, int nseg, OutLay ol)
+{
+    typedef nc::IO<StBF16> io;
+    static_assert(D == 64 || D == 128, "two or four 32-column blocks");
+    constexpr int NCB = D / 32, NW = 2 * NCB, NT = 64 * NW, KS = D / 16, CPR = D / 8;
+    constexpr int TPW = NCB * NCB / NW;  // R tiles per wave
+    constexpr int LDX = KvBf2Lds<D>::LDX, RP = KvBf2Lds<D>::RP, PP = KvBf2Lds<D>::PP;
+    static_assert(NT == kCc * CPR, "one staging item per thread");
+    __shared__ __attribute__((aligned(16))) KvBf2Lds<D> L;
+
+    const int64_t bh = blockIdx.x / nseg;
+    const int seg = (int)(blockIdx.x % nseg);
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, j = lane & 31, h = lane >> 5;
+    const bool isk = w < NCB;
+    const int cb = isk ? w : w - NCB;
+    const int64_t beg = (int64_t)seg * seg_len;
+    const int64_t end = (beg + seg_len < N) ? beg + seg_len : N;
+    const int64_t hoff = bh * N * D;
+    const float *st = rec + (bh * nseg + seg) * (int64_t)(D * D + 2 * D);
+    const uint16_t *qh = Q + hoff, *kh = K + hoff, *vh = V + hoff, *gh = G + hoff;
+    uint16_t *oh = (isk ? dK : dV) + ol.head(bh);
+    const float2 *ch = reinterpret_cast<const float2 *>(cbuf) + bh * N;
+
+    // staging item of this thread: row it of the chunk, 8-column piece ic;
+    // two register sets (set x & 1 holds chunk x of the walk), so the loads
+    // of the next two chunks are in flight while one is computed
+    const int it = tid / CPR, ic = tid % CPR;
+    uint4 pq[2], pk[2], pv[2], pg[2];
+    float2 pc[2];
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    auto fetch = [&](int64_t r0, auto set_) {
+        constexpr int X = decltype(set_)::value;
+        const int rows = (int)(end - r0 < kCc ? end - r0 : kCc);
+        const int off = it * D * 2 + 16 * ic;
+        auto rs = [&](const uint16_t *x) {
+            return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(x + r0 * D), (short)0,
+                                                     rows * D * 2, kBufferWord3);
+        };
+        pq[X] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs(qh), off, 0, 0));
+        pk[X] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs(kh), off, 0, 0));
+        pv[X] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs(vh), off, 0, 0));
+        pg[X] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs(gh), off, 0, 0));
+        const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float2 *>(ch + r0), (short)0, rows * 8, kBufferWord3);
+        pc[X] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rc, it * 8, 0, 0));
+    };
+    auto stage = [&](auto set_) {
+        constexpr int X = decltype(set_)::value;
+        const int o = it * LDX + 8 * ic;
+        *reinterpret_cast<uint4 *>(&L.q[o]) = pq[X];
+        *reinterpret_cast<uint4 *>(&L.k[o]) = pk[X];
+        *reinterpret_cast<uint4 *>(&L.v[o]) = pv[X];
+        float gf[8];
+        StBF16::widen(pg[X], gf);
+        const float inv = pc[X].y;
+        uint2 h0, l0, h1, l1;
+        split4(gf[0] * inv, gf[1] * inv, gf[2] * inv, gf[3] * inv, h0, l0);
+        split4(gf[4] * inv, gf[5] * inv, gf[6] * inv, gf[7] * inv, h1, l1);
+        *reinterpret_cast<uint4 *>(&L.ahi[o]) = uint4{h0.x, h0.y, h1.x, h1.y};
+        *reinterpret_cast<uint4 *>(&L.alo[o]) = uint4{l0.x, l0.y, l1.x, l1.y};
+        if (ic == 0)
+            L.cs[it] = pc[X].x;
+    };
+
+    // this wave's tiles of R: tile u <-> R[32 ta .., 32 tb ..], accumulator
+    // element i of lane (j, h) at a = 32 ta + 8 (i / 4) + 4 h + i % 4, b = 32 tb + j
+    f16v racc[TPW];
+    auto write_r = [&]() {
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const int tau = w * TPW + u, ta = tau / NCB, tb = tau % NCB;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint2 hi, lo;
+                split4(racc[u][4 * q], racc[u][4 * q + 1], racc[u][4 * q + 2], racc[u][4 * q + 3],
+                       hi, lo);
+                const int o = (32 * tb + j) * RP + 32 * ta + 8 * q + 4 * h;
+                *reinterpret_cast<uint2 *>(&L.rhi[o]) = hi;
+                *reinterpret_cast<uint2 *>(&L.rlo[o]) = lo;
+            }
+        }
+    };
+
+    const int64_t nrounds = (end - beg + kCc - 1) / kCc;
+    const int64_t last = beg + (nrounds - 1) * kCc;
+    fetch(last, S0{});
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int tau = w * TPW + u, ta = tau / NCB, tb = tau % NCB;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            racc[u][i] = st[(32 * ta + 8 * (i / 4) + 4 * h + (i % 4)) * D + 32 * tb + j];
+    }
+    // the column-sum threads: the last D of the workgroup, one column each
+    const bool csum = tid >= NT - D;
+    const int cd = tid - (NT - D);
+    float rr = 0.f, tt = 0.f;  // r and t of the rows after the chunk
+    if (csum) {
+        rr = st[D * D + cd];
+        tt = st[D * D + D + cd];
+    }
+    write_r();
+    stage(S0{});
+    drain_loads();
+    if (nrounds > 1)
+        fetch(last - kCc, S1{});
+    if (nrounds > 2)
+        fetch(last - 2 * kCc, S0{});
+    __syncthreads();
+
+    // one chunk; set_ holds the next chunk's rows (round + 1 = set_ mod 2)
+    auto round_body = [&](int64_t round, auto set_) {
+        const int64_t t0 = last - round * kCc;
+        // (1) the suffix state applied to the chunk's rows: dK^T block
+        // C[a][t] = sum_b R[a][b] V[t][b], or dV^T block C[b][t] = sum_a
+        // R[a][b] K[t][a]
+        // (the role tests stay outside the k-loops: a branch inside one would
+        // split it into blocks and keep the LDS reads from running ahead)
+        f16v acc = zero16();
+        if (isk) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf8 x = row8(L.v, LDX, 0, 16 * ks, j, h);
+                acc = mma16(col8(L.rhi, RP, 16 * ks, 32 * cb, lane), x, acc);
+                acc = mma16(col8(L.rlo, RP, 16 * ks, 32 * cb, lane), x, acc);
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf8 x = row8(L.k, LDX, 0, 16 * ks, j, h);
+                acc = mma16(row8(L.rhi, RP, 32 * cb, 16 * ks, j, h), x, acc);
+                acc = mma16(row8(L.rlo, RP, 32 * cb, 16 * ks, j, h), x, acc);
+            }
+        }
+        // the in-chunk blocks, [j][i] planes: P = A V^T - c (wave 0) and
+        // W = 1 + Q K^T (wave NCB), masked to i >= j
+        if (w == 0 || w == NCB) {
+            f16v pa = zero16();
+            if (w == 0) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf8 vj = row8(L.v, LDX, 0, 16 * ks, j, h);
+                    pa = mma16(row8(L.ahi, LDX, 0, 16 * ks, j, h), vj, pa);
+                    pa = mma16(row8(L.alo, LDX, 0, 16 * ks, j, h), vj, pa);
+                }
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    pa = mma16(row8(L.q, LDX, 0, 16 * ks, j, h), row8(L.k, LDX, 0, 16 * ks, j, h),
+                               pa);
+            }
+            uint16_t *ph = (w == 0) ? L.phi : L.whi;
+            uint16_t *pl = (w == 0) ? L.plo : L.wlo;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float x4[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 8 * q + 4 * h + r;
+                    const float e = pa[4 * q + r];
+                    x4[r] = (i >= j) ? ((w == 0) ? e - L.cs[i] : 1.f + e) : 0.f;
+                }
+                uint2 hi, lo;
+                split4(x4[0], x4[1], x4[2], x4[3], hi, lo);
+                *reinterpret_cast<uint2 *>(&ph[j * PP + 8 * q + 4 * h]) = hi;
+                *reinterpret_cast<uint2 *>(&pl[j * PP + 8 * q + 4 * h]) = lo;
+            }
+        }
+        // column sums of the chunk; the vectors of the rows after it go to
+        // LDS for the epilogue
+        if (csum) {
+            L.vr[cd] = rr;
+            L.vt[cd] = tt;
+            float rc = 0.f, tc = 0.f;
+#pragma unroll 8
+            for (int i = 0; i < kCc; ++i) {
+                rc += L.cs[i] * __uint_as_float((uint32_t)L.q[i * LDX + cd] << 16);
+                tc += __uint_as_float((uint32_t)L.ahi[i * LDX + cd] << 16) +
+                      __uint_as_float((uint32_t)L.alo[i * LDX + cd] << 16);
+            }
+            rr += rc;
+            tt += tc;
+        }
+        __syncthreads();  // B1
+        // (2) in-chunk terms: dK^T += Q^T P (C[a][j] += sum_i Q[i][a] P[i][j]),
+        // dV^T += A^T W (C[b][j] += sum_i A[i][b] W[i][j])
+        if (isk) {
+#pragma unroll
+            for (int kk = 0; kk < kCc / 16; ++kk) {
+                const bf8 qa = col8(L.q, LDX, 16 * kk, 32 * cb, lane);
+                acc = mma16(qa, row8(L.phi, PP, 0, 16 * kk, j, h), acc);
+                acc = mma16(qa, row8(L.plo, PP, 0, 16 * kk, j, h), acc);
+            }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < kCc / 16; ++kk) {
+                const bf8 ah = col8(L.ahi, LDX, 16 * kk, 32 * cb, lane);
+                const bf8 al = col8(L.alo, LDX, 16 * kk, 32 * cb, lane);
+                const bf8 wh = row8(L.whi, PP, 0, 16 * kk, j, h);
+                acc = mma16(ah, wh, acc);
+                acc = mma16(ah, row8(L.wlo, PP, 0, 16 * kk, j, h), acc);
+                acc = mma16(al, wh, acc);
+            }
+        }
+        // rows of dK (- r) or dV (+ t) with the vectors of the rows after the chunk
+        {
+            const float sg = isk ? -1.f : 1.f;
+            const float *vec = isk ? L.vr : L.vt;
+            if (t0 + j < end)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f4 v = *reinterpret_cast<const f4 *>(&vec[32 * cb + 8 * q + 4 * h]);
+                    io::store4(oh + (t0 + j) * ol.sn + 32 * cb + 8 * q + 4 * h,
+                               f4{acc[4 * q] + sg * v[0], acc[4 * q + 1] + sg * v[1],
+                                  acc[4 * q + 2] + sg * v[2], acc[4 * q + 3] + sg * v[3]});
+                }
+        }
+        // the suffix state takes the chunk in: R += Q_c^T A_c
+        if (round + 1 < nrounds) {
+#pragma unroll
+            for (int u = 0; u < TPW; ++u) {
+                const int tau = w * TPW + u, ta = tau / NCB, tb = tau % NCB;
+#pragma unroll
+                for (int kk = 0; kk < kCc / 16; ++kk) {
+                    const bf8 qa = col8(L.q, LDX, 16 * kk, 32 * ta, lane);
+                    racc[u] = mma16(qa, col8(L.ahi, LDX, 16 * kk, 32 * tb, lane), racc[u]);
+                    racc[u] = mma16(qa, col8(L.alo, LDX, 16 * kk, 32 * tb, lane), racc[u]);
+                }
+            }
+            write_r();
+        }
+        __syncthreads();  // B2
+        if (round + 1 < nrounds) {
+            stage(set_);
+            if (round + 3 < nrounds)
+                fetch(t0 - 3 * kCc, set_);
+        }
+        __syncthreads();  // B3
+    };
+    for (int64_t round = 0; round < nrounds; round += 2) {
+        round_body(round, S1{});
+        if (round + 1 < nrounds)
+            round_body(round + 1, S0{});
+    }
+}
+
 }  // namespace bf
 }  // namespace la
