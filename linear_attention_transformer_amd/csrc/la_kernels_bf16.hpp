@@ -79,6 +79,50 @@ __device__ __forceinline__ float sum8(bf8 b, float c)
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.w), ones, c, false);
 }
 
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16 on gfx950: within each group of 16 lanes, lane p = 4e + f
+// points at row r0 + e, columns c0 + 4f .. + 3 of a row-major bf16 tile;
+// lane i of the group then receives rows r0 .. r0 + 3 of column c0 + i.
+__device__ __forceinline__ v4s tr4(const uint16_t *tile, int pitch, int r0, int c0, int p)
+{
+    const uint16_t *a = tile + (r0 + (p >> 2)) * pitch + c0 + 4 * (p & 3);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(a));
+}
+
+// the MFMA operand of lane (j, h) = 32 h + j: rows rb + 8 h .. + 7 of column
+// cb0 + j (8 consecutive tokens of one column)
+__device__ __forceinline__ bf8 col8(const uint16_t *tile, int pitch, int rb, int cb0, int lane)
+{
+    const int g = lane >> 4, p = lane & 15;
+    const int r0 = rb + 8 * (g >> 1), c0 = cb0 + 16 * (g & 1);
+    const v4s x = tr4(tile, pitch, r0, c0, p);
+    const v4s y = tr4(tile, pitch, r0 + 4, c0, p);
+    const uint2 ux = __builtin_bit_cast(uint2, x), uy = __builtin_bit_cast(uint2, y);
+    return __builtin_bit_cast(bf8, uint4{ux.x, ux.y, uy.x, uy.y});
+}
+
+// the MFMA operand of lane (j, h): row rb + j, columns c + 8 h .. + 7
+__device__ __forceinline__ bf8 row8(const uint16_t *tile, int pitch, int rb, int c, int j, int h)
+{
+    return *reinterpret_cast<const bf8 *>(tile + (rb + j) * pitch + c + 8 * h);
+}
+
+// two fp32 as hi and lo bf16 pairs (a in the low halves): one paired
+// round-to-nearest conversion for hi, the residuals, one for lo
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo)
+{
+    hi = StBF16::narrow2(a, b);
+    lo = StBF16::narrow2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+
+// four fp32 as hi and lo bf16 (two 8-byte words)
+__device__ __forceinline__ void split4(float a, float b, float c, float d, uint2 &hi, uint2 &lo)
+{
+    split2(a, b, hi.x, lo.x);
+    split2(c, d, hi.y, lo.y);
+}
+
 constexpr int kApplyThreads = 256;
 
 // ============================================================ apply
@@ -368,15 +412,16 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
 // cx = sum_t w_t X[t], cy = sum_t Y'[t] over the segment's rows, with
 //   forward  (GRAD = false): X = K, Y' = V, w = 1        -> S, z, u
 //   backward (GRAD = true) : X = Q, Y' = dO / den, w = c -> dS, r, t
-// and (c_t, 1/den_t) from cbuf.  The contraction runs over tokens, so both
-// MFMA operands need 8 consecutive tokens of one column per lane: each
-// round of TT = 64 rows is staged transposed in LDS (column-major, tokens
-// contiguous), each staging lane packing a pair of tokens into 32-bit
-// writes.  Y' of the backward is an fp32 product, kept as hi and lo bf16
-// planes (two MFMAs per step).  The column sums are accumulated by the
-// staging lanes across rounds and reduced across lanes once at the end.
-// Waves own 32x32 output tiles (D = 128: a 2 x 2 block each); for D = 32
-// the four waves split the k-steps of the single tile and add up in LDS.
+// and (c_t, 1/den_t) from cbuf.  Each round of TT = 64 rows is loaded as
+// whole rows (consecutive lanes take consecutive 16-byte pieces of a row)
+// and staged as natural rows in LDS, one 16-byte write per piece; the
+// contraction runs over tokens, and both MFMA operands (8 consecutive tokens
+// of one column per lane) are read with the LDS transpose read.  Y' of the
+// backward is an fp32 product, kept as hi and lo planes (two MFMAs per
+// step).  The column sums are accumulated by the staging lanes (each keeps
+// the same 8 columns in every round) and reduced once at the end.  Waves own
+// 32x32 output tiles (D = 128: a 2 x 2 block each); for D = 32 the four
+// waves split the k-steps of the single tile and add up in LDS.
 template <int D, bool GRAD>
 __global__ __launch_bounds__(256) void k_reduce_bf(
     const uint16_t *__restrict__ X, const uint16_t *__restrict__ Y,
@@ -384,25 +429,24 @@ __global__ __launch_bounds__(256) void k_reduce_bf(
     int nseg)
 {
     static_assert(D >= 32 && D <= 128, "32x32 tiles");
-    // rows per round: 64, or 32 for the backward, whose staging also carries
-    // (c, 1/den) and the hi/lo planes (registers for one wave per SIMD more)
-    constexpr int NT = 256, TT = GRAD ? 32 : 64;
-    constexpr int R2 = TT + 8;              // bf16 pitch of a transposed column
+    constexpr int NT = 256, TT = 64;
+    constexpr int LDP = D + 16;             // row pitch: 16-lane transpose reads conflict-free
     constexpr int NTILE1 = D / 32;          // tiles per dimension
     constexpr int NTILE = NTILE1 * NTILE1;
     constexpr int TPW1 = NTILE >= 4 ? NTILE1 / 2 : 1;  // tiles per wave per dimension
     constexpr int WPT = NTILE >= 4 ? 1 : 4;           // waves sharing a tile (k split)
-    constexpr int CH = D / 8;               // 8-column chunks per row
-    constexpr int PC = (TT / 2) * CH;       // (token pair, chunk) items per round
-    constexpr int PER = (PC + NT - 1) / NT;
+    constexpr int CPR = D / 8;              // 16-byte pieces per row
+    constexpr int PER = TT * CPR / NT;      // pieces per thread per round
+    static_assert(PER >= 1 && TT * CPR % NT == 0 && NT % CPR == 0, "staging split");
     constexpr int NYP = GRAD ? 2 : 1;       // planes of Y'
-    __shared__ __attribute__((aligned(16))) uint16_t xT[D * R2];
-    __shared__ __attribute__((aligned(16))) uint16_t yT[NYP][D * R2];
+    __shared__ __attribute__((aligned(16))) uint16_t xs[TT * LDP];
+    __shared__ __attribute__((aligned(16))) uint16_t ys[NYP][TT * LDP];
     __shared__ float red[WPT > 1 ? (WPT - 1) * 16 * 64 : 1];
+    __shared__ float csx[NT / 64][CPR][8], csy[NT / 64][CPR][8];
 
     const int64_t bh = blockIdx.x / nseg;
     const int seg = (int)(blockIdx.x % nseg);
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, j = lane & 31, h = lane >> 5;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int64_t beg = (int64_t)seg * seg_len;
     const int64_t end = (beg + seg_len < N) ? beg + seg_len : N;
     const int64_t hoff = bh * N * D;
@@ -413,15 +457,14 @@ __global__ __launch_bounds__(256) void k_reduce_bf(
     const int n0 = (NTILE >= 4) ? (w % 2) * 32 * TPW1 : 0;
     const int ksplit = (NTILE >= 4) ? 0 : w;  // D = 32: this wave's k-step
 
-    // staging items: q = tid + p * NT -> chunk q / (TT/2), token pair q % (TT/2)
-    uint4 sx[PER][2], sy[PER][2];
-    float2 scb[PER][2];
-    float cx[PER][8], cy[PER][8];
+    // staging pieces: q = tid + p * NT -> row q / CPR, columns 8 (q % CPR) ..
+    // (the same 8 columns, tid % CPR, for every piece of the thread)
+    uint4 sx[PER], sy[PER];
+    float2 scb[PER];
+    float cx[8], cy[8];
 #pragma unroll
-    for (int p = 0; p < PER; ++p)
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-            cx[p][s] = cy[p][s] = 0.f;
+    for (int s = 0; s < 8; ++s)
+        cx[s] = cy[s] = 0.f;
 
     auto fetch = [&](int64_t r0) {
         const int rows = (int)(end - r0 < TT ? end - r0 : TT);
@@ -436,69 +479,43 @@ __global__ __launch_bounds__(256) void k_reduce_bf(
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
             const int q = tid + p * NT;
-            if (PC % NT == 0 || q < PC) {
-                const int chunk = q / (TT / 2), pr = q % (TT / 2);
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int off = (2 * pr + u) * D * 2 + 16 * chunk;
-                    sx[p][u] = __builtin_bit_cast(uint4,
-                                                  __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
-                    sy[p][u] = __builtin_bit_cast(uint4,
-                                                  __builtin_amdgcn_raw_buffer_load_b128(ry, off, 0, 0));
-                    if constexpr (GRAD)
-                        scb[p][u] = __builtin_bit_cast(
-                            float2, __builtin_amdgcn_raw_buffer_load_b64(rc, (2 * pr + u) * 8, 0, 0));
-                }
-            }
+            const int off = (q / CPR) * D * 2 + 16 * (q % CPR);
+            sx[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+            sy[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ry, off, 0, 0));
+            if constexpr (GRAD)
+                scb[p] = __builtin_bit_cast(
+                    float2, __builtin_amdgcn_raw_buffer_load_b64(rc, (q / CPR) * 8, 0, 0));
         }
     };
     auto stage = [&]() {
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
             const int q = tid + p * NT;
-            if (PC % NT == 0 || q < PC) {
-                const int chunk = q / (TT / 2), pr = q % (TT / 2);
-                // tokens 2 pr, 2 pr + 1 of column 8 chunk + s as one bf16 pair
+            const int o = (q / CPR) * LDP + 8 * (q % CPR);
+            *reinterpret_cast<uint4 *>(&xs[o]) = sx[p];
+            float xv[8], yv[8];
+            StBF16::widen(sx[p], xv);
+            StBF16::widen(sy[p], yv);
+            if constexpr (!GRAD) {
+                *reinterpret_cast<uint4 *>(&ys[0][o]) = sy[p];
 #pragma unroll
-                for (int s = 0; s < 8; ++s)
-                    *reinterpret_cast<uint32_t *>(&xT[(8 * chunk + s) * R2 + 2 * pr]) =
-                        pair_bf16(sx[p][0], sx[p][1], s);
-                if constexpr (!GRAD) {
-                    // column sums from the same pairs: a two-term bf16 dot
-                    // product with (1, 1), exact products summed in fp32
-                    const bf2 ones = {(__bf16)1.f, (__bf16)1.f};
+                for (int s = 0; s < 8; ++s) {
+                    cx[s] += xv[s];
+                    cy[s] += yv[s];
+                }
+            } else {
+                const float c = scb[p].x, inv = scb[p].y;
+                uint4 hi, lo;
+                split2(yv[0] * inv, yv[1] * inv, hi.x, lo.x);
+                split2(yv[2] * inv, yv[3] * inv, hi.y, lo.y);
+                split2(yv[4] * inv, yv[5] * inv, hi.z, lo.z);
+                split2(yv[6] * inv, yv[7] * inv, hi.w, lo.w);
+                *reinterpret_cast<uint4 *>(&ys[0][o]) = hi;
+                *reinterpret_cast<uint4 *>(&ys[1][o]) = lo;
 #pragma unroll
-                    for (int s = 0; s < 8; ++s) {
-                        const uint32_t px = pair_bf16(sx[p][0], sx[p][1], s);
-                        const uint32_t py = pair_bf16(sy[p][0], sy[p][1], s);
-                        *reinterpret_cast<uint32_t *>(&yT[0][(8 * chunk + s) * R2 + 2 * pr]) = py;
-                        cx[p][s] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, px), ones,
-                                                                   cx[p][s], false);
-                        cy[p][s] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, py), ones,
-                                                                   cy[p][s], false);
-                    }
-                } else {
-                    float xv[2][8], yv[2][8];
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        StBF16::widen(sx[p][u], xv[u]);
-                        StBF16::widen(sy[p][u], yv[u]);
-                    }
-#pragma unroll
-                    for (int s = 0; s < 8; ++s) {
-                        __bf16 h0, l0, h1, l1;
-                        const float a0 = yv[0][s] * scb[p][0].y, a1 = yv[1][s] * scb[p][1].y;
-                        split_bf16(a0, h0, l0);
-                        split_bf16(a1, h1, l1);
-                        *reinterpret_cast<uint32_t *>(&yT[0][(8 * chunk + s) * R2 + 2 * pr]) =
-                            (uint32_t)__builtin_bit_cast(uint16_t, h0) |
-                            ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-                        *reinterpret_cast<uint32_t *>(&yT[1][(8 * chunk + s) * R2 + 2 * pr]) =
-                            (uint32_t)__builtin_bit_cast(uint16_t, l0) |
-                            ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
-                        cx[p][s] += scb[p][0].x * xv[0][s] + scb[p][1].x * xv[1][s];
-                        cy[p][s] += a0 + a1;
-                    }
+                for (int s = 0; s < 8; ++s) {
+                    cx[s] += c * xv[s];
+                    cy[s] += yv[s] * inv;
                 }
             }
         }
@@ -526,13 +543,12 @@ __global__ __launch_bounds__(256) void k_reduce_bf(
             bf8 av[TPW1], bv[TPW1][NYP];
 #pragma unroll
             for (int a = 0; a < TPW1; ++a)
-                av[a] = *reinterpret_cast<const bf8 *>(&xT[(m0 + 32 * a + j) * R2 + 16 * kk + 8 * h]);
+                av[a] = col8(xs, LDP, 16 * kk, m0 + 32 * a, lane);
 #pragma unroll
             for (int b = 0; b < TPW1; ++b)
 #pragma unroll
                 for (int y = 0; y < NYP; ++y)
-                    bv[b][y] = *reinterpret_cast<const bf8 *>(
-                        &yT[y][(n0 + 32 * b + j) * R2 + 16 * kk + 8 * h]);
+                    bv[b][y] = col8(ys[y], LDP, 16 * kk, n0 + 32 * b, lane);
 #pragma unroll
             for (int a = 0; a < TPW1; ++a)
 #pragma unroll
@@ -543,6 +559,7 @@ __global__ __launch_bounds__(256) void k_reduce_bf(
         }
     }
 
+    const int j = lane & 31, h = lane >> 5;
     float *out = part + (bh * nseg + seg) * (int64_t)(D * D + 2 * D);
     if constexpr (WPT > 1) {
         // D = 32: waves 1..3 hand their k-split partials to wave 0
@@ -567,23 +584,41 @@ __global__ __launch_bounds__(256) void k_reduce_bf(
                     out[(m0 + 32 * a + 8 * (i / 4) + 4 * h + (i % 4)) * D + n0 + 32 * b + j] =
                         acc[a][b][i];
     }
-    // column sums: the TT/2 consecutive lanes of a chunk hold its 8 columns
+    // column sums: the lanes l + k CPR of a wave hold the same 8 columns;
+    // sum them (rotations within rows of 16 lanes, then the swaps across
+    // rows), then the waves' sums meet in LDS
 #pragma unroll
-    for (int p = 0; p < PER; ++p) {
-        const int q = tid + p * NT;
+    for (int s = 0; s < 8; ++s) {
+        float a = cx[s], b = cy[s];
+        if constexpr (CPR <= 4) {
+            a += dpp_mov<0x124>(a);  // row_ror:4
+            b += dpp_mov<0x124>(b);
+        }
+        if constexpr (CPR <= 8) {
+            a += dpp_mov<0x128>(a);  // row_ror:8
+            b += dpp_mov<0x128>(b);
+        }
+        cx[s] = swap32_sum(swap16_sum(a));
+        cy[s] = swap32_sum(swap16_sum(b));
+    }
+    if (lane < CPR) {
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            cx[p][s] = group_sum<TT / 2>(cx[p][s]);
-            cy[p][s] = group_sum<TT / 2>(cy[p][s]);
+            csx[w][lane][s] = cx[s];
+            csy[w][lane][s] = cy[s];
         }
-        if ((PC % NT == 0 || q < PC) && q % (TT / 2) == 0) {
-            const int chunk = q / (TT / 2);
+    }
+    __syncthreads();
+    if (tid < D) {
+        const int pc2 = tid / 8, s2 = tid % 8;
+        float a = 0.f, b = 0.f;
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                out[D * D + 8 * chunk + s] = cx[p][s];
-                out[D * D + D + 8 * chunk + s] = cy[p][s];
-            }
+        for (int v = 0; v < NT / 64; ++v) {
+            a += csx[v][pc2][s2];
+            b += csy[v][pc2][s2];
         }
+        out[D * D + tid] = a;
+        out[D * D + D + tid] = b;
     }
 }
 
@@ -1399,50 +1434,6 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_kv_causal_bf(
 // lo planes.  Products over the chunk's tokens (R's update, P^T Q, W^T A)
 // read 8 consecutive tokens of a column with two ds_read_b64_tr_b16.  The
 // column sums r = sum c_i q_i and t = sum a_i run in registers of D threads.
-
-typedef short v4s __attribute__((ext_vector_type(4)));
-
-// ds_read_b64_tr_b16 on gfx950: within each group of 16 lanes, lane p = 4e + f
-// points at row r0 + e, columns c0 + 4f .. + 3 of a row-major bf16 tile;
-// lane i of the group then receives rows r0 .. r0 + 3 of column c0 + i.
-__device__ __forceinline__ v4s tr4(const uint16_t *tile, int pitch, int r0, int c0, int p)
-{
-    const uint16_t *a = tile + (r0 + (p >> 2)) * pitch + c0 + 4 * (p & 3);
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(a));
-}
-
-// the MFMA operand of lane (j, h) = 32 h + j: rows rb + 8 h .. + 7 of column
-// cb0 + j (8 consecutive tokens of one column)
-__device__ __forceinline__ bf8 col8(const uint16_t *tile, int pitch, int rb, int cb0, int lane)
-{
-    const int g = lane >> 4, p = lane & 15;
-    const int r0 = rb + 8 * (g >> 1), c0 = cb0 + 16 * (g & 1);
-    const v4s x = tr4(tile, pitch, r0, c0, p);
-    const v4s y = tr4(tile, pitch, r0 + 4, c0, p);
-    const uint2 ux = __builtin_bit_cast(uint2, x), uy = __builtin_bit_cast(uint2, y);
-    return __builtin_bit_cast(bf8, uint4{ux.x, ux.y, uy.x, uy.y});
-}
-
-// the MFMA operand of lane (j, h): row rb + j, columns c + 8 h .. + 7
-__device__ __forceinline__ bf8 row8(const uint16_t *tile, int pitch, int rb, int c, int j, int h)
-{
-    return *reinterpret_cast<const bf8 *>(tile + (rb + j) * pitch + c + 8 * h);
-}
-
-// two fp32 as hi and lo bf16 pairs (a in the low halves): one paired
-// round-to-nearest conversion for hi, the residuals, one for lo
-__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo)
-{
-    hi = StBF16::narrow2(a, b);
-    lo = StBF16::narrow2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
-}
-
-// four fp32 as hi and lo bf16 (two 8-byte words)
-__device__ __forceinline__ void split4(float a, float b, float c, float d, uint2 &hi, uint2 &lo)
-{
-    split2(a, b, hi.x, lo.x);
-    split2(c, d, hi.y, lo.y);
-}
 
 template <int D>
 struct KvBf2Lds {
