@@ -542,7 +542,21 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
     }
     if constexpr (!CAUSAL && nc_path<D>()) {
         const dim3 g1((unsigned)(p.nseg * p.BH));
-        if constexpr (std::is_same<ST, StBF16>::value) {
+        if constexpr (std::is_same<ST, StBF16>::value && D >= 64) {
+            // bf16 matrix cores: dQ and the segment's gradient record in one
+            // pass over Q and dO, segments sized for one batch of resident
+            // workgroups
+            const Plan pq = one_batch(p, resident_wgs<bf::k_bwd_q_bf<D>>(512));
+            rc = traced(t, s, "bwd_q", [&] {
+                bf::k_bwd_q_bf<D><<<dim3((unsigned)(pq.nseg * pq.BH)), dim3(512), 0, s>>>(
+                    g, q, static_cast<T *>(dQ), gpart, fstate, pq.N, pq.seg_len, (int)pq.nseg,
+                    pq.n0, pq.ol);
+            });
+            if (rc != LA_OK)
+                return rc;
+            if ((rc = scan(gpart, ws + l.gtot, pq, 0, s, t, gin, gout)) != LA_OK)
+                return rc;
+        } else if constexpr (std::is_same<ST, StBF16>::value) {
             // bf16 matrix cores: dQ with (c_i, 1/den_i), then the gradient
             // records from a second (bf16, half-size) read of Q and dO
             rc = traced(t, s, "bwd_q", [&] {
@@ -556,6 +570,10 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
                 bf::k_reduce_bf<D, true><<<g1, dim3(256), 0, s>>>(q, g, cbuf, gpart, p.N,
                                                                 p.seg_len, (int)p.nseg);
             });
+            if (rc != LA_OK)
+                return rc;
+            if ((rc = scan(gpart, ws + l.gtot, p, 0, s, t, gin, gout)) != LA_OK)
+                return rc;
         } else {
             // dQ and the segment's gradient record in one pass over Q and dO,
             // its segments sized for one batch of resident workgroups
@@ -572,9 +590,6 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
         }
         if (rc != LA_OK)
             return rc;
-        if constexpr (std::is_same<ST, StBF16>::value)
-            if ((rc = scan(gpart, ws + l.gtot, p, 0, s, t, gin, gout)) != LA_OK)
-                return rc;
         if (dK == nullptr)
             return LA_OK;
         return traced(t, s, "bwd_kv", [&] {

@@ -622,6 +622,333 @@ __global__ __launch_bounds__(256) void k_reduce_bf(
     }
 }
 
+// ============================================================ fused dQ + dS (non-causal)
+// dQ and the segment's gradient record [dS | r | t] in one pass over Q and
+// dO (D = 64, 128), eight waves in two roles over rounds of TR rows:
+//   - staging (by the dS waves, two 16-byte pieces of Q and of dO per thread
+//     and round, loaded three rounds ahead):
+//     den_t = n0 + N + q_t.z from a 16-lane (D / 8-lane) row sum, then
+//     a_t = dO_t / den_t as hi / lo planes; Q, dO, a staged as natural rows;
+//   - waves 0..3 (dQ role): y_t = S dO_t as in k_apply_bf<D, 1> (S as hi /
+//     lo operand registers), c_t = (dO_t.u + q_t.y_t) / den_t^2, dq_t =
+//     y_t / den_t - c_t z; they also sum r = sum c_t q_t and t = sum a_t at
+//     their output columns, from values kept in registers;
+//   - waves 4..7 (dS role): dS += Q^T A over the round's tokens, both
+//     operands read with the LDS transpose read (a: hi and lo).
+// One barrier per round.  A round's staged rows are read before its barrier
+// only (the epilogue after it works from registers and the exchange), so
+// staging the next round into the other buffers never overwrites a value
+// still to be read.  Rows read whole (dO, the dQ tile) have a pitch of D + 8
+// (conflict-free 16-byte row reads), rows read by the transpose read a pitch
+// of D + 16 (32 bytes mod 128: conflict-free 16-lane transpose reads).
+template <int D>
+struct BqBfLds {
+    static constexpr int NCB = D / 32, NRG = 4 / NCB, TR = 32 * NRG, LDX = D + 8, LDT = D + 16;
+    uint16_t xs[2][TR * LDX];   // dO rows
+    uint16_t qs[2][TR * LDT];   // Q rows
+    uint16_t ah[2][TR * LDT];   // a = dO / den, hi
+    uint16_t al[2][TR * LDT];   // a, lo
+    uint16_t ot[2][TR * LDX];   // dQ rows of a round, stored as whole rows
+    float ivx[2][TR];           // 1 / den of the round's rows
+    float xch[2][NRG][NCB][32]; // per column block: dO.u + q.y
+    float vu[D];
+    float csr[NRG][D], cst[NRG][D];  // r, t of each row group
+};
+
+template <int D>
+__global__ __launch_bounds__(512) void k_bwd_q_bf(
+    const uint16_t *__restrict__ G, const uint16_t *__restrict__ Q, uint16_t *__restrict__ dQ,
+    float *__restrict__ part, const float *__restrict__ rec, int64_t N, int64_t seg_len,
+    int nseg, float n0, OutLay ol)
+{
+    static_assert(D == 64 || D == 128, "two or four column blocks");
+    typedef BqBfLds<D> Lt;
+    constexpr int NT = 512, KS = D / 16, NCB = Lt::NCB, NRG = Lt::NRG, TR = Lt::TR;
+    constexpr int LDX = Lt::LDX, LDT = Lt::LDT, CPR = D / 8;
+    static_assert(TR * CPR == NT, "two staging pieces per staging thread and tensor");
+    constexpr int TPW1 = NCB / 2;  // dS tiles per wave and dimension
+    __shared__ __attribute__((aligned(16))) Lt L;
+
+    const int64_t bh = blockIdx.x / nseg;
+    const int seg = (int)(blockIdx.x % nseg);
+    const int tid = threadIdx.x, lane = tid & 63, j = lane & 31, h = lane >> 5;
+    // the wave index as a scalar: the role branches below are uniform per
+    // wave, and each role's loop passes the same barriers
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int w4 = w & 3;
+    const int cb = w4 % NCB, rg = w4 / NCB;
+    const int64_t beg = (int64_t)seg * seg_len;
+    const int len = (int)((beg + seg_len < N ? beg + seg_len : N) - beg);  // rows of the segment
+    const int64_t hoff = bh * N * D + beg * D;
+    const float *st = rec + bh * (int64_t)(D * D + 2 * D);
+    const uint16_t *gh = G + hoff, *qh = Q + hoff;
+    uint16_t *oh = dQ + ol.head(bh) + beg * ol.sn;
+    const float ntot = n0 + (float)N;
+
+    // store piece of this thread (dQ rows): row it, columns 8 ic .. 8 ic + 7
+    const int it = tid / CPR, ic = tid % CPR;
+    // staging pieces of the dS waves' threads: rows sr + (0, NT / 2 / CPR),
+    // columns 8 ic .. (the same columns for both: NT / 2 is a multiple of CPR)
+    const int sr = (tid - NT / 2) / CPR;
+    constexpr int SR2 = NT / 2 / CPR;
+    float zp[8];  // z at the pieces' columns (loaded by the dS waves)
+    // three register sets (set x mod 3 holds round x's pieces): the loads of
+    // a round are issued three rounds before it is staged
+    uint4 pg[3][2], pq[3][2];
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    // round r's pieces (rounds past the end read nothing: their pieces are zero)
+    auto fetch = [&](int r, auto set_) {
+        constexpr int X = decltype(set_)::value;
+        const int rb = r * TR < len ? r * TR : len;
+        const int rows = len - rb < TR ? len - rb : TR;
+        const int off = sr * D * 2 + 16 * ic;
+        const __amdgpu_buffer_rsrc_t rgs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(gh + (int64_t)rb * D), (short)0, rows * D * 2, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rqs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(qh + (int64_t)rb * D), (short)0, rows * D * 2, kBufferWord3);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            pg[X][p] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(rgs, off + p * SR2 * D * 2, 0, 0));
+            pq[X][p] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(rqs, off + p * SR2 * D * 2, 0, 0));
+        }
+    };
+    // the fetched pieces into LDS: dO and Q as they are, 1 / den of their
+    // rows, a = dO / den as hi and lo (rows past the end are zero: a = 0)
+    auto stage = [&](int buf, auto set_) {
+        constexpr int X = decltype(set_)::value;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int row = sr + p * SR2;
+            const int o = row * LDT + 8 * ic;
+            *reinterpret_cast<uint4 *>(&L.xs[buf][row * LDX + 8 * ic]) = pg[X][p];
+            *reinterpret_cast<uint4 *>(&L.qs[buf][o]) = pq[X][p];
+            float qf[8], gf[8];
+            StBF16::widen(pq[X][p], qf);
+            StBF16::widen(pg[X][p], gf);
+            float qz = 0.f;
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                qz += qf[s] * zp[s];
+            qz = group_sum<CPR>(qz);
+            const float inv = 1.f / (ntot + qz);
+            if (ic == 0)
+                L.ivx[buf][row] = inv;
+            uint4 hi, lo;
+            split2(gf[0] * inv, gf[1] * inv, hi.x, lo.x);
+            split2(gf[2] * inv, gf[3] * inv, hi.y, lo.y);
+            split2(gf[4] * inv, gf[5] * inv, hi.z, lo.z);
+            split2(gf[6] * inv, gf[7] * inv, hi.w, lo.w);
+            *reinterpret_cast<uint4 *>(&L.ah[buf][o]) = hi;
+            *reinterpret_cast<uint4 *>(&L.al[buf][o]) = lo;
+        }
+    };
+    // round rr's dQ rows to global memory (one 16-byte piece per thread;
+    // none for rr < 0 or rows past the end)
+    auto store_tile = [&](int rr) {
+        const int lr = rr * TR + it;
+        if (rr >= 0 && lr < len)
+            *reinterpret_cast<uint4 *>(oh + lr * ol.sn + 8 * ic) =
+                *reinterpret_cast<const uint4 *>(&L.ot[(int)(rr & 1)][it * LDX + 8 * ic]);
+    };
+    for (int e = tid; e < D; e += NT)
+        L.vu[e] = st[D * D + D + e];
+
+    // The rounds are padded to a multiple of three: the padding rounds are
+    // past the end (zero rows: no dQ rows, nothing added to dS, r, t).  The
+    // loop body is then three rounds of straight-line code, with every load
+    // and stage unconditional, so that each stage waits for its own loads
+    // only (a branch around a load makes the compiler wait for all of them).
+    const int nrounds = (len + TR - 1) / TR;
+    const int nr3 = (nrounds + 2) / 3 * 3;
+    // (dS waves) the next round into the other buffers from its register
+    // set, whose loads are reissued for the round three later
+    auto next = [&](int round, auto set_) {
+        stage((round + 1) & 1, set_);
+        fetch(round + 4, set_);
+    };
+
+    float *out = part + (bh * nseg + seg) * (int64_t)(D * D + 2 * D);
+    if (w < 4) {
+        // ---- dQ role: S's block as hi / lo operands,
+        // s?[ks][s] = S[32 cb + j][16 ks + 8 h + s]
+        bf8 shi[KS], slo[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const f4 v0 = *reinterpret_cast<const f4 *>(st + (32 * cb + j) * D + 16 * ks + 8 * h);
+            const f4 v1 =
+                *reinterpret_cast<const f4 *>(st + (32 * cb + j) * D + 16 * ks + 8 * h + 4);
+            uint4 hi, lo;
+            split2(v0[0], v0[1], hi.x, lo.x);
+            split2(v0[2], v0[3], hi.y, lo.y);
+            split2(v1[0], v1[1], hi.z, lo.z);
+            split2(v1[2], v1[3], hi.w, lo.w);
+            shi[ks] = __builtin_bit_cast(bf8, hi);
+            slo[ks] = __builtin_bit_cast(bf8, lo);
+        }
+        f4 ez[4];  // z at the lane's output columns 32 cb + 8 q + 4 h ..
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            ez[q] = *reinterpret_cast<const f4 *>(st + D * D + 32 * cb + 8 * q + 4 * h);
+        // r and t at the lane's output columns, summed over its rows
+        float rsum[16], tsum[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            rsum[e] = tsum[e] = 0.f;
+        __syncthreads();  // the first round staged
+
+        for (int round = 0; round < nr3; ++round) {
+            const int buf = round & 1;
+            store_tile(round - 2);
+            const uint16_t *xr = &L.xs[buf][(32 * rg + j) * LDX];
+            f16v acc = zero16();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf8 x = *reinterpret_cast<const bf8 *>(xr + 16 * ks + 8 * h);
+                acc = mma16(shi[ks], x, acc);
+                acc = mma16(slo[ks], x, acc);
+            }
+            // q.y over this block's output columns, dO.u over the same columns
+            const uint16_t *qr = &L.qs[buf][(32 * rg + j) * LDT + 32 * cb + 4 * h];
+            const uint16_t *gr = xr + 32 * cb + 4 * h;
+            uint2 qv[4], gv[4];
+            float p = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                qv[q] = *reinterpret_cast<const uint2 *>(qr + 8 * q);
+                gv[q] = *reinterpret_cast<const uint2 *>(gr + 8 * q);
+                float qf[4], gf[4];
+                StBF16::widen2(qv[q].x, qf);
+                StBF16::widen2(qv[q].y, qf + 2);
+                StBF16::widen2(gv[q].x, gf);
+                StBF16::widen2(gv[q].y, gf + 2);
+                const f4 u = *reinterpret_cast<const f4 *>(&L.vu[32 * cb + 8 * q + 4 * h]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    p += qf[r] * acc[4 * q + r] + gf[r] * u[r];
+            }
+            p = swap32_sum(p);
+            if (h == 0)
+                L.xch[buf][rg][cb][j] = p;
+            const float inv = L.ivx[buf][32 * rg + j];
+            __syncthreads();
+            float sy = 0.f;
+#pragma unroll
+            for (int c2 = 0; c2 < NCB; ++c2)
+                sy += L.xch[buf][rg][c2][j];
+            const float c = sy * inv * inv;
+            const float cv = (round * TR + 32 * rg + j < len) ? c : 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f4 o = {acc[4 * q] * inv - c * ez[q][0], acc[4 * q + 1] * inv - c * ez[q][1],
+                              acc[4 * q + 2] * inv - c * ez[q][2],
+                              acc[4 * q + 3] * inv - c * ez[q][3]};
+                uint2 r2;
+                r2.x = StBF16::narrow2(o[0], o[1]);
+                r2.y = StBF16::narrow2(o[2], o[3]);
+                *reinterpret_cast<uint2 *>(
+                    &L.ot[buf][(32 * rg + j) * LDX + 32 * cb + 8 * q + 4 * h]) = r2;
+                float qf[4], gf[4];
+                StBF16::widen2(qv[q].x, qf);
+                StBF16::widen2(qv[q].y, qf + 2);
+                StBF16::widen2(gv[q].x, gf);
+                StBF16::widen2(gv[q].y, gf + 2);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    rsum[4 * q + r] += cv * qf[r];
+                    tsum[4 * q + r] += gf[r] * inv;
+                }
+            }
+        }
+        // r and t over the wave's rows (the 32 lanes of each half)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const float a = group_sum<32>(rsum[e]), b = group_sum<32>(tsum[e]);
+            if (j == 0) {
+                const int col = 32 * cb + 8 * (e / 4) + 4 * h + (e % 4);
+                L.csr[rg][col] = a;
+                L.cst[rg][col] = b;
+            }
+        }
+    } else {
+        // ---- dS role (and the staging): the first rounds in flight, the
+        // first staged; everything any wave loads before the loops is loaded
+        // in its own branch, so the loop's waits cover its own loads only
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            zp[s] = st[D * D + 8 * ic + s];
+        fetch(0, S0{});
+        fetch(1, S1{});
+        fetch(2, S2{});
+        stage(0, S0{});
+        fetch(3, S0{});
+        __syncthreads();  // the first round staged
+        // tiles dS[tm0 + 32 a ..][tn0 + 32 b ..]
+        const int tm0 = (w4 / 2) * 32 * TPW1, tn0 = (w4 % 2) * 32 * TPW1;
+        f16v dacc[TPW1][TPW1];
+#pragma unroll
+        for (int a = 0; a < TPW1; ++a)
+#pragma unroll
+            for (int b = 0; b < TPW1; ++b)
+                dacc[a][b] = zero16();
+        // body(round, set of round + 1), unrolled over the three sets
+        auto body = [&](int round, auto set_) {
+            const int buf = round & 1;
+            store_tile(round - 2);
+#pragma unroll
+            for (int kk = 0; kk < TR / 16; ++kk) {
+                bf8 av[TPW1], bvh[TPW1], bvl[TPW1];
+#pragma unroll
+                for (int a = 0; a < TPW1; ++a)
+                    av[a] = col8(L.qs[buf], LDT, 16 * kk, tm0 + 32 * a, lane);
+#pragma unroll
+                for (int b = 0; b < TPW1; ++b) {
+                    bvh[b] = col8(L.ah[buf], LDT, 16 * kk, tn0 + 32 * b, lane);
+                    bvl[b] = col8(L.al[buf], LDT, 16 * kk, tn0 + 32 * b, lane);
+                }
+#pragma unroll
+                for (int a = 0; a < TPW1; ++a)
+#pragma unroll
+                    for (int b = 0; b < TPW1; ++b) {
+                        dacc[a][b] = mma16(av[a], bvh[b], dacc[a][b]);
+                        dacc[a][b] = mma16(av[a], bvl[b], dacc[a][b]);
+                    }
+            }
+            next(round, set_);
+            __syncthreads();
+        };
+        for (int round = 0; round < nr3; round += 3) {
+            body(round, S1{});
+            body(round + 1, S2{});
+            body(round + 2, S0{});
+        }
+#pragma unroll
+        for (int a = 0; a < TPW1; ++a)
+#pragma unroll
+            for (int b = 0; b < TPW1; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    out[(tm0 + 32 * a + 8 * (i / 4) + 4 * h + (i % 4)) * D + tn0 + 32 * b + j] =
+                        dacc[a][b][i];
+    }
+    __syncthreads();  // the last tiles, r and t
+    store_tile(nr3 - 2);
+    store_tile(nr3 - 1);
+    if (tid < D) {
+        float a = 0.f, b = 0.f;
+#pragma unroll
+        for (int g2 = 0; g2 < NRG; ++g2) {
+            a += L.csr[g2][tid];
+            b += L.cst[g2][tid];
+        }
+        out[D * D + tid] = a;
+        out[D * D + D + tid] = b;
+    }
+}
+
 // ============================================================ causal
 // The causal kernels of la_kernels_causal.hpp on the bf16 matrix cores, same
 // chunking (C = 32 rows) and state layout: wave cb holds its D x 32 slice of
