@@ -123,6 +123,18 @@ __device__ __forceinline__ void split4(float a, float b, float c, float d, uint2
     split2(c, d, hi.y, lo.y);
 }
 
+// eight fp32 as hi and lo bf16 MFMA operands (paired conversions)
+__device__ __forceinline__ void split8v(const float *x, bf8 &hi, bf8 &lo)
+{
+    uint4 h, l;
+    split2(x[0], x[1], h.x, l.x);
+    split2(x[2], x[3], h.y, l.y);
+    split2(x[4], x[5], h.z, l.z);
+    split2(x[6], x[7], h.w, l.w);
+    hi = __builtin_bit_cast(bf8, h);
+    lo = __builtin_bit_cast(bf8, l);
+}
+
 constexpr int kApplyThreads = 256;
 
 // ============================================================ apply
@@ -975,13 +987,11 @@ __device__ __forceinline__ bf8 row_at(const uint16_t *row, int d0)
 // hi/lo bf16 operands of accumulator elements 8p .. 8p + 7 of a
 __device__ __forceinline__ void split8(const f16v &a, int p, bf8 &hi, bf8 &lo)
 {
+    float x[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        __bf16 x, y;
-        split_bf16(a[8 * p + s], x, y);
-        hi[s] = x;
-        lo[s] = y;
-    }
+    for (int s = 0; s < 8; ++s)
+        x[s] = a[8 * p + s];
+    split8v(x, hi, lo);
 }
 
 // Staging of one chunk: item q = tid (+ NT) covers token pair pr = q % 16
@@ -1250,13 +1260,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal_bf(
                 rs += wm[s];
             }
             bf8 whi, wlo;
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                __bf16 x, y;
-                split_bf16(wm[s], x, y);
-                whi[s] = x;
-                wlo[s] = y;
-            }
+            split8v(wm, whi, wlo);
             const bf8 vcol = col_at(vT, 32 * cb + j, kk, h);  // V[16kk+8h..][32cb+j]
             acc = mma16(vcol, whi, acc);
             acc = mma16(vcol, wlo, acc);
@@ -1492,14 +1496,13 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
 #pragma unroll
         for (int kk = 0; kk < kCc / 16; ++kk) {
             bf8 phi, plo;
+            float pm[8];
 #pragma unroll
             for (int s2 = 0; s2 < 8; ++s2) {
                 const int jr = 16 * kk + 8 * h + s2;
-                __bf16 x, y;
-                split_bf16((jr <= j) ? gvk[kk][s2] - cden : 0.f, x, y);
-                phi[s2] = x;
-                plo[s2] = y;
+                pm[s2] = (jr <= j) ? gvk[kk][s2] - cden : 0.f;
             }
+            split8v(pm, phi, plo);
             const bf8 kcol = col_at(kT, 32 * cb + j, kk, h);  // K[16kk+8h..][32cb+j]
             acc = mma16(kcol, phi, acc);
             acc = mma16(kcol, plo, acc);
@@ -1670,13 +1673,7 @@ __device__ __forceinline__ void kv_pass_bf(
                     bm[s2] = (ir >= j) ? 1.f + sv : 0.f;
             }
             bf8 bhi, blo;
-#pragma unroll
-            for (int s2 = 0; s2 < 8; ++s2) {
-                __bf16 x, y;
-                split_bf16(bm[s2], x, y);
-                bhi[s2] = x;
-                blo[s2] = y;
-            }
+            split8v(bm, bhi, blo);
             if constexpr (PAR == 0) {
                 const bf8 qcol = col_at(L.qT, 32 * cb + j, kk, h);  // Q[ir][32cb+j]
                 acc = mma16(qcol, bhi, acc);
@@ -1764,10 +1761,16 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_kv_causal_bf(
 
 template <int D>
 struct KvBf2Lds {
-    static constexpr int LDX = D + 8;    // natural row pitch (bf16)
-    static constexpr int RP = D + 8;     // R planes: element (a, b) at b * RP + a
+    // Row pitches (bf16): D + 8 (16 mod 128 bytes) for the rows read whole
+    // only (K, V: conflict-free 16-byte row reads), D + 16 (32 mod 128 bytes)
+    // for the planes read mostly with the transpose read (Q, a and R:
+    // conflict-free 16-lane transpose reads).  D = 64 keeps D + 8 throughout:
+    // the wider planes would cost it a third resident workgroup per CU.
+    static constexpr int LDX = D + 8;
+    static constexpr int LDT = D == 64 ? D + 8 : D + 16;
+    static constexpr int RP = LDT;       // R planes: element (a, b) at b * RP + a
     static constexpr int PP = kCc + 8;   // P, W planes: element (i, j) at j * PP + i
-    uint16_t q[kCc * LDX], k[kCc * LDX], v[kCc * LDX], ahi[kCc * LDX], alo[kCc * LDX];
+    uint16_t q[kCc * LDT], k[kCc * LDX], v[kCc * LDX], ahi[kCc * LDT], alo[kCc * LDT];
     uint16_t rhi[D * RP], rlo[D * RP];
     uint16_t phi[kCc * PP], plo[kCc * PP], whi[kCc * PP], wlo[kCc * PP];
     float cs[kCc];
@@ -1785,7 +1788,8 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_bwd_kv_causal_bf2(
     static_assert(D == 64 || D == 128, "two or four 32-column blocks");
     constexpr int NCB = D / 32, NW = 2 * NCB, NT = 64 * NW, KS = D / 16, CPR = D / 8;
     constexpr int TPW = NCB * NCB / NW;  // R tiles per wave
-    constexpr int LDX = KvBf2Lds<D>::LDX, RP = KvBf2Lds<D>::RP, PP = KvBf2Lds<D>::PP;
+    constexpr int LDX = KvBf2Lds<D>::LDX, LDT = KvBf2Lds<D>::LDT, RP = KvBf2Lds<D>::RP,
+                  PP = KvBf2Lds<D>::PP;
     static_assert(NT == kCc * CPR, "one staging item per thread");
     __shared__ __attribute__((aligned(16))) KvBf2Lds<D> L;
 
@@ -1810,12 +1814,14 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_bwd_kv_causal_bf2(
     float2 pc[2];
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
+    // (chunks before the segment, the walk's padding, read nothing: zero rows)
     auto fetch = [&](int64_t r0, auto set_) {
         constexpr int X = decltype(set_)::value;
-        const int rows = (int)(end - r0 < kCc ? end - r0 : kCc);
+        const int rows = r0 < beg ? 0 : (int)(end - r0 < kCc ? end - r0 : kCc);
+        const int64_t rb = r0 < beg ? beg : r0;
         const int off = it * D * 2 + 16 * ic;
         auto rs = [&](const uint16_t *x) {
-            return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(x + r0 * D), (short)0,
+            return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(x + rb * D), (short)0,
                                                      rows * D * 2, kBufferWord3);
         };
         pq[X] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs(qh), off, 0, 0));
@@ -1823,15 +1829,15 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_bwd_kv_causal_bf2(
         pv[X] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs(vh), off, 0, 0));
         pg[X] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs(gh), off, 0, 0));
         const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<float2 *>(ch + r0), (short)0, rows * 8, kBufferWord3);
+            const_cast<float2 *>(ch + rb), (short)0, rows * 8, kBufferWord3);
         pc[X] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rc, it * 8, 0, 0));
     };
     auto stage = [&](auto set_) {
         constexpr int X = decltype(set_)::value;
-        const int o = it * LDX + 8 * ic;
+        const int o = it * LDT + 8 * ic, ox = it * LDX + 8 * ic;
         *reinterpret_cast<uint4 *>(&L.q[o]) = pq[X];
-        *reinterpret_cast<uint4 *>(&L.k[o]) = pk[X];
-        *reinterpret_cast<uint4 *>(&L.v[o]) = pv[X];
+        *reinterpret_cast<uint4 *>(&L.k[ox]) = pk[X];
+        *reinterpret_cast<uint4 *>(&L.v[ox]) = pv[X];
         float gf[8];
         StBF16::widen(pg[X], gf);
         const float inv = pc[X].y;
@@ -1863,7 +1869,13 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_bwd_kv_causal_bf2(
         }
     };
 
+    // The walk is padded to an even number of chunks (a padding chunk lies
+    // before the segment: zero rows, no output rows, nothing added to the
+    // state), so that its loop body is two chunks of straight-line code with
+    // every load and stage unconditional: each stage then waits for its own
+    // loads only (a branch around a load makes the compiler wait for all).
     const int64_t nrounds = (end - beg + kCc - 1) / kCc;
+    const int64_t nr2 = (nrounds + 1) / 2 * 2;
     const int64_t last = beg + (nrounds - 1) * kCc;
     fetch(last, S0{});
 #pragma unroll
@@ -1884,10 +1896,8 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_bwd_kv_causal_bf2(
     write_r();
     stage(S0{});
     drain_loads();
-    if (nrounds > 1)
-        fetch(last - kCc, S1{});
-    if (nrounds > 2)
-        fetch(last - 2 * kCc, S0{});
+    fetch(last - kCc, S1{});
+    fetch(last - 2 * kCc, S0{});
     __syncthreads();
 
     // one chunk; set_ holds the next chunk's rows (round + 1 = set_ mod 2)
@@ -1922,13 +1932,13 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_bwd_kv_causal_bf2(
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const bf8 vj = row8(L.v, LDX, 0, 16 * ks, j, h);
-                    pa = mma16(row8(L.ahi, LDX, 0, 16 * ks, j, h), vj, pa);
-                    pa = mma16(row8(L.alo, LDX, 0, 16 * ks, j, h), vj, pa);
+                    pa = mma16(row8(L.ahi, LDT, 0, 16 * ks, j, h), vj, pa);
+                    pa = mma16(row8(L.alo, LDT, 0, 16 * ks, j, h), vj, pa);
                 }
             } else {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
-                    pa = mma16(row8(L.q, LDX, 0, 16 * ks, j, h), row8(L.k, LDX, 0, 16 * ks, j, h),
+                    pa = mma16(row8(L.q, LDT, 0, 16 * ks, j, h), row8(L.k, LDX, 0, 16 * ks, j, h),
                                pa);
             }
             uint16_t *ph = (w == 0) ? L.phi : L.whi;
@@ -1956,9 +1966,9 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_bwd_kv_causal_bf2(
             float rc = 0.f, tc = 0.f;
 #pragma unroll 8
             for (int i = 0; i < kCc; ++i) {
-                rc += L.cs[i] * __uint_as_float((uint32_t)L.q[i * LDX + cd] << 16);
-                tc += __uint_as_float((uint32_t)L.ahi[i * LDX + cd] << 16) +
-                      __uint_as_float((uint32_t)L.alo[i * LDX + cd] << 16);
+                rc += L.cs[i] * __uint_as_float((uint32_t)L.q[i * LDT + cd] << 16);
+                tc += __uint_as_float((uint32_t)L.ahi[i * LDT + cd] << 16) +
+                      __uint_as_float((uint32_t)L.alo[i * LDT + cd] << 16);
             }
             rr += rc;
             tt += tc;
@@ -1969,15 +1979,15 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_bwd_kv_causal_bf2(
         if (isk) {
 #pragma unroll
             for (int kk = 0; kk < kCc / 16; ++kk) {
-                const bf8 qa = col8(L.q, LDX, 16 * kk, 32 * cb, lane);
+                const bf8 qa = col8(L.q, LDT, 16 * kk, 32 * cb, lane);
                 acc = mma16(qa, row8(L.phi, PP, 0, 16 * kk, j, h), acc);
                 acc = mma16(qa, row8(L.plo, PP, 0, 16 * kk, j, h), acc);
             }
         } else {
 #pragma unroll
             for (int kk = 0; kk < kCc / 16; ++kk) {
-                const bf8 ah = col8(L.ahi, LDX, 16 * kk, 32 * cb, lane);
-                const bf8 al = col8(L.alo, LDX, 16 * kk, 32 * cb, lane);
+                const bf8 ah = col8(L.ahi, LDT, 16 * kk, 32 * cb, lane);
+                const bf8 al = col8(L.alo, LDT, 16 * kk, 32 * cb, lane);
                 const bf8 wh = row8(L.whi, PP, 0, 16 * kk, j, h);
                 acc = mma16(ah, wh, acc);
                 acc = mma16(ah, row8(L.wlo, PP, 0, 16 * kk, j, h), acc);
@@ -1988,7 +1998,7 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_bwd_kv_causal_bf2(
         {
             const float sg = isk ? -1.f : 1.f;
             const float *vec = isk ? L.vr : L.vt;
-            if (t0 + j < end)
+            if (t0 + j >= beg && t0 + j < end)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const f4 v = *reinterpret_cast<const f4 *>(&vec[32 * cb + 8 * q + 4 * h]);
@@ -1997,32 +2007,29 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_bwd_kv_causal_bf2(
                                   acc[4 * q + 2] + sg * v[2], acc[4 * q + 3] + sg * v[3]});
                 }
         }
-        // the suffix state takes the chunk in: R += Q_c^T A_c
-        if (round + 1 < nrounds) {
+        // the suffix state takes the chunk in: R += Q_c^T A_c (also after the
+        // last chunk, where it is not read again)
+        {
 #pragma unroll
             for (int u = 0; u < TPW; ++u) {
                 const int tau = w * TPW + u, ta = tau / NCB, tb = tau % NCB;
 #pragma unroll
                 for (int kk = 0; kk < kCc / 16; ++kk) {
-                    const bf8 qa = col8(L.q, LDX, 16 * kk, 32 * ta, lane);
-                    racc[u] = mma16(qa, col8(L.ahi, LDX, 16 * kk, 32 * tb, lane), racc[u]);
-                    racc[u] = mma16(qa, col8(L.alo, LDX, 16 * kk, 32 * tb, lane), racc[u]);
+                    const bf8 qa = col8(L.q, LDT, 16 * kk, 32 * ta, lane);
+                    racc[u] = mma16(qa, col8(L.ahi, LDT, 16 * kk, 32 * tb, lane), racc[u]);
+                    racc[u] = mma16(qa, col8(L.alo, LDT, 16 * kk, 32 * tb, lane), racc[u]);
                 }
             }
             write_r();
         }
         __syncthreads();  // B2
-        if (round + 1 < nrounds) {
-            stage(set_);
-            if (round + 3 < nrounds)
-                fetch(t0 - 3 * kCc, set_);
-        }
+        stage(set_);
+        fetch(t0 - 3 * kCc, set_);
         __syncthreads();  // B3
     };
-    for (int64_t round = 0; round < nrounds; round += 2) {
+    for (int64_t round = 0; round < nr2; round += 2) {
         round_body(round, S1{});
-        if (round + 1 < nrounds)
-            round_body(round + 1, S0{});
+        round_body(round + 1, S0{});
     }
 }
 
