@@ -505,6 +505,11 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
                 bf::k_bwd_kv_causal_bf<D><<<dim3((unsigned)(2 * p.nseg * p.BH)), nt, 0, s>>>(
                     q, k, v, g, static_cast<T *>(dK), static_cast<T *>(dV), cbuf, gpart, p.N,
                     p.seg_len, (int)p.nseg, p.ol);
+            else if constexpr (D >= 64)
+                cz::k_bwd_kv_causal2<ST, D><<<dim3((unsigned)(p.nseg * p.BH)), dim3(128 * (D / 32)),
+                                              0, s>>>(q, k, v, g, static_cast<T *>(dK),
+                                                      static_cast<T *>(dV), cbuf, gpart, p.N,
+                                                      p.seg_len, (int)p.nseg, p.ol);
             else
                 cz::k_bwd_kv_causal<ST, D><<<dim3((unsigned)(2 * p.nseg * p.BH)), nt, 0, s>>>(
                     q, k, v, g, static_cast<T *>(dK), static_cast<T *>(dV), cbuf, gpart, p.N,

@@ -751,5 +751,261 @@ __global__ __launch_bounds__(threads<D>()) __attribute__((amdgpu_waves_per_eu(2)
         kv_pass<ST, D, 0>(Q, K, V, G, dK, dV, cbuf, rec, N, seg_len, nseg, ol, lds);
 }
 
+// ============================================================ dK | dV, one workgroup
+// The recurrences of kv_pass, with dK and dV of a segment formed by one
+// workgroup of 2 NCB waves that holds the suffix state R once, so that R is
+// updated once per chunk instead of once per output:
+//   - R (fp32) lives in LDS as R[a][b] (a: column of Q, b: column of a);
+//     each wave keeps NCB / 2 of its 32 x 32 tiles as MFMA accumulators,
+//     adds the chunk (R += Q_c^T A_c) and writes them back after the
+//     chunk's last read of R;
+//   - waves 0 .. NCB - 1 form dK columns 32 w .. (dk_j = R v_j - r + in-chunk
+//     terms, R read by rows), waves NCB .. 2 NCB - 1 form dV columns
+//     (dv_j = R^T k_j + t + in-chunk terms, R read by columns);
+//   - the products Q_c K_c^T and G_c V_c^T are split into 16 x 16 tiles over
+//     all waves.
+// Three barriers per chunk, as in kv_pass: after the product tiles (B1),
+// after the chunk's last reads (B2), after the next chunk is staged (B3).
+// K and V are read only before B1 and are restaged right after it.
+template <int D>
+struct Kv2Lds {
+    static constexpr int LDX = D + 4, RP = D + 4, WP = kC + 1;
+    float qs[kC * LDX], ks[kC * LDX], vs[kC * LDX], gs[kC * LDX];
+    float rs[D * RP];                // R[a][b] at a * RP + b
+    float wx[kC * WP], gx[kC * WP];  // Q_c K_c^T, G_c V_c^T ([i][j] at i * WP + j)
+    float cs[kC], is[kC];            // c_i, 1 / den_i of the chunk's rows
+    float vr[D], vt[D];              // r, t of the rows after the chunk
+};
+
+// Q_c K_c^T into wx and G_c V_c^T into gx as eight 16 x 16 tiles spread over
+// NW waves (as tiles_xyT; a wave with a single tile runs its k-steps as two
+// chains and adds them at the end)
+template <int D, int NW>
+__device__ __forceinline__ void tiles8_xyT(const float *qs, const float *ks, const float *gs,
+                                           const float *vs, float *wx, float *gx, int w, int lane)
+{
+    constexpr int LDX = D + 4, WP = kC + 1, PER = 8 / NW, NST = D / 16;
+    static_assert(PER * NW == 8, "tiles per wave");
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int tt = w * PER + k;  // 0..3: Q K^T tiles, 4..7: G V^T
+        const int ti = (tt >> 1) & 1, tj = tt & 1;
+        const float *xa = (tt < 4 ? qs : gs) + (16 * ti + r) * LDX + 4 * g;
+        const float *ya = (tt < 4 ? ks : vs) + (16 * tj + r) * LDX + 4 * g;
+        f4 a[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+            const f4 x = *reinterpret_cast<const f4 *>(xa + 16 * st);
+            const f4 y = *reinterpret_cast<const f4 *>(ya + 16 * st);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                a[st & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[c], y[c], a[st & 1], 0, 0, 0);
+        }
+        float *dst = (tt < 4 ? wx : gx) + (16 * ti + 4 * g) * WP + 16 * tj + r;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            dst[v * WP] = a[0][v] + a[1][v];
+    }
+}
+
+template <class ST, int D>
+__global__ __launch_bounds__(128 * (D / 32)) void k_bwd_kv_causal2(
+    const typename ST::T *__restrict__ Q, const typename ST::T *__restrict__ K,
+    const typename ST::T *__restrict__ V, const typename ST::T *__restrict__ G,
+    typename ST::T *__restrict__ dK, typename ST::T *__restrict__ dV,
+    const float *__restrict__ cbuf, const float *__restrict__ rec, int64_t N, int64_t seg_len,
+    int nseg, OutLay ol)
+{
+    typedef typename ST::T T;
+    typedef IO<ST> io;
+    static_assert(D == 64 || D == 128, "two or four 32-column blocks");
+    constexpr int NCB = D / 32, NW = 2 * NCB, NT = 64 * NW, KB = D / 8;
+    constexpr int LDX = Kv2Lds<D>::LDX, RP = Kv2Lds<D>::RP, WP = Kv2Lds<D>::WP;
+    constexpr int TPW = NCB / 2;  // R tiles per wave
+    __shared__ __attribute__((aligned(16))) Kv2Lds<D> L;
+
+    const int64_t bh = blockIdx.x / nseg;
+    const int seg = (int)(blockIdx.x % nseg);
+    const int tid = threadIdx.x, lane = tid & 63, j = lane & 31, h = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool isk = w < NCB;
+    const int cb = isk ? w : w - NCB;
+    const int64_t beg = (int64_t)seg * seg_len;
+    const int64_t end = (beg + seg_len < N) ? beg + seg_len : N;
+    const int64_t hoff = bh * N * D;
+    const float *st = rec + (bh * nseg + seg) * (int64_t)(D * D + 2 * D);
+    const T *qh = Q + hoff, *kh = K + hoff, *vh = V + hoff, *gh = G + hoff;
+    T *oh = (isk ? dK : dV) + ol.head(bh);
+    const float2 *ch = reinterpret_cast<const float2 *>(cbuf) + bh * N;
+
+    // chunk rows from registers: a chunk outside [beg, end) reads nothing
+    // (its rows are zero), so the fetches past the walk need no branch
+    Rows<ST, D, NT> rq, rk, rv, rg;
+    float2 pc = float2{0.f, 0.f};
+    auto fetch_kv = [&](int64_t r0) {
+        const int64_t rb = r0 < beg ? end : r0;
+        rk.fetch(kh, rb, end, tid);
+        rv.fetch(vh, rb, end, tid);
+    };
+    auto fetch_qg = [&](int64_t r0) {
+        const int64_t rb = r0 < beg ? end : r0;
+        rq.fetch(qh, rb, end, tid);
+        rg.fetch(gh, rb, end, tid);
+        const int rows = (int)(end - rb < kC ? end - rb : kC);
+        const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float2 *>(ch + rb), (short)0, rows * 8, kBufferWord3);
+        pc = __builtin_bit_cast(float2,
+                                __builtin_amdgcn_raw_buffer_load_b64(rc, (tid & (kC - 1)) * 8, 0, 0));
+    };
+    auto stage_kv = [&]() {
+        rk.stage(L.ks, tid);
+        rv.stage(L.vs, tid);
+    };
+    auto stage_qg = [&]() {
+        rq.stage(L.qs, tid);
+        rg.stage(L.gs, tid);
+        if (tid < kC) {
+            L.cs[tid] = pc.x;
+            L.is[tid] = pc.y;
+        }
+    };
+
+    // this wave's R tiles: tile u <-> R[32 ta .., 32 tb ..], accumulator
+    // element i of lane (j, h) at a = 32 ta + 8 (i / 4) + 4 h + i % 4, b = 32 tb + j
+    f16v racc[TPW];
+    auto tile_of = [&](int u, int &ta, int &tb) {
+        const int tau = w * TPW + u;
+        ta = tau / NCB;
+        tb = tau % NCB;
+    };
+    auto write_r = [&]() {
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            int ta, tb;
+            tile_of(u, ta, tb);
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                L.rs[(32 * ta + 8 * (i / 4) + 4 * h + (i % 4)) * RP + 32 * tb + j] = racc[u][i];
+        }
+    };
+
+    const int64_t nrounds = (end - beg + kC - 1) / kC;
+    const int64_t last = beg + (nrounds - 1) * kC;  // first row of the last chunk
+    fetch_kv(last);
+    fetch_qg(last);
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        int ta, tb;
+        tile_of(u, ta, tb);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            racc[u][i] = st[(32 * ta + 8 * (i / 4) + 4 * h + (i % 4)) * D + 32 * tb + j];
+    }
+    for (int e = tid; e < D; e += NT) {
+        L.vr[e] = st[D * D + e];
+        L.vt[e] = st[D * D + D + e];
+    }
+    write_r();
+    stage_kv();
+    stage_qg();
+    drain_loads();
+    fetch_kv(last - kC);
+    fetch_qg(last - kC);
+    __syncthreads();
+
+    for (int64_t round = 0; round < nrounds; ++round) {
+        const int64_t t0 = last - round * kC;
+        // (1) the suffix state applied to the chunk's rows: dK^T block
+        // C[a][t] = sum_b R[a][b] V[t][b] (R by rows) or dV^T block
+        // C[b][t] = sum_a R[a][b] K[t][a] (R by columns); k-slot of lane
+        // (j, h) at k-block kb, step r: column 8 kb + 4 h + r
+        f16v acc = zero16();
+        if (isk) {
+            const float *xt = &L.vs[j * LDX + 4 * h];
+            const float *rt = &L.rs[(32 * cb + j) * RP + 4 * h];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const f4 x = *reinterpret_cast<const f4 *>(xt + 8 * kb);
+                const f4 a = *reinterpret_cast<const f4 *>(rt + 8 * kb);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc = mma32(a[r], x[r], acc);
+            }
+        } else {
+            const float *xt = &L.ks[j * LDX + 4 * h];
+            const float *rt = &L.rs[(4 * h) * RP + 32 * cb + j];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const f4 x = *reinterpret_cast<const f4 *>(xt + 8 * kb);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc = mma32(rt[(8 * kb + r) * RP], x[r], acc);
+            }
+        }
+        // (2) Q_c K_c^T and G_c V_c^T, tiles over all waves
+        tiles8_xyT<D, NW>(L.qs, L.ks, L.gs, L.vs, L.wx, L.gx, w, lane);
+        __syncthreads();  // B1
+        stage_kv();  // K, V are read only before B1
+        fetch_kv(t0 - 2 * kC);
+        // (3) in-chunk terms over rows ir = 2 kk + h >= j:
+        // dK^T[a][j] += sum_i Q[i][a] (a_i.v_j - c_i), dV^T[b][j] += sum_i A[i][b] (1 + q_i.k_j)
+        float vc = 0.f;
+        if (isk) {
+#pragma unroll
+            for (int kk = 0; kk < kC / 2; ++kk) {
+                const int ir = 2 * kk + h;
+                const float ci = L.cs[ir];
+                const float pm = (ir >= j) ? L.gx[ir * WP + j] * L.is[ir] - ci : 0.f;
+                const float qb = L.qs[ir * LDX + 32 * cb + j];
+                acc = mma32(qb, pm, acc);
+                vc += ci * qb;
+            }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < kC / 2; ++kk) {
+                const int ir = 2 * kk + h;
+                const float wm = (ir >= j) ? 1.f + L.wx[ir * WP + j] : 0.f;
+                const float ab = L.gs[ir * LDX + 32 * cb + j] * L.is[ir];
+                acc = mma32(ab, wm, acc);
+                vc += ab;
+            }
+        }
+        vc = swap32_sum(vc);
+        // (4) rows of dK (- r) or dV (+ t) with the vectors of the rows after the chunk
+        {
+            const float sg = isk ? -1.f : 1.f;
+            const float *vec = isk ? L.vr : L.vt;
+            if (t0 + j < end)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f4 v = *reinterpret_cast<const f4 *>(&vec[32 * cb + 8 * q + 4 * h]);
+                    io::store4(oh + (t0 + j) * ol.sn + 32 * cb + 8 * q + 4 * h,
+                               f4{acc[4 * q] + sg * v[0], acc[4 * q + 1] + sg * v[1],
+                                  acc[4 * q + 2] + sg * v[2], acc[4 * q + 3] + sg * v[3]});
+                }
+        }
+        // (5) the suffix state takes the chunk in: R += Q_c^T A_c, tile by tile
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            int ta, tb;
+            tile_of(u, ta, tb);
+#pragma unroll
+            for (int kk = 0; kk < kC / 2; ++kk) {
+                const int ir = 2 * kk + h;
+                racc[u] = mma32(L.qs[ir * LDX + 32 * ta + j],
+                                L.gs[ir * LDX + 32 * tb + j] * L.is[ir], racc[u]);
+            }
+        }
+        write_r();  // every read of R for this chunk was before B1
+        __syncthreads();  // B2
+        if (h == 0)
+            (isk ? L.vr : L.vt)[32 * cb + j] += vc;
+        stage_qg();
+        fetch_qg(t0 - 2 * kC);
+        __syncthreads();  // B3
+    }
+}
+
 }  // namespace cz
 }  // namespace la
