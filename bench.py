@@ -54,7 +54,7 @@ KERNEL_NAMES = [
      "grad_state_local"),
     (r"k_reduce_nc<|k_reduce_bf<|k_state_local<", "state_local"),
     (r"k_apply_nc<[^>]*, 0>|k_apply_bf<\d+, 0>|k_fwd_causal|k_forward<", "forward"),
-    (r"k_bwd_q_nc<|k_apply_bf<\d+, 1>|k_bwd_q_causal|k_bwd_q<", "bwd_q"),
+    (r"k_bwd_q_nc<|k_bwd_q_bf<|k_apply_bf<\d+, 1>|k_bwd_q_causal|k_bwd_q<", "bwd_q"),
     (r"k_apply_nc<[^>]*, 2>|k_apply_bf<\d+, 2>|k_bwd_kv_causal|k_bwd_kv<", "bwd_kv"),
     (r"k_state_scan", "state_scan"),
     (r"k_pad<|k_unpad<|k_stage_record", "stage"),

@@ -109,6 +109,25 @@ __device__ __forceinline__ float group_sum(float v)
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 
+// Workgroup b of a launch of `units` workgroups per head: its head bh and
+// its unit u (0 <= u < units).  The dispatcher deals workgroups to the eight
+// XCDs in turn (b mod 8); when the number of heads is a multiple of 8, the
+// units of one head are all given workgroups on one XCD, so that the head's
+// state record, which each of them reads, is fetched into one L2 instead of
+// eight.  Otherwise the plain order (bh = b / units).
+__device__ __forceinline__ void xcd_unit(int64_t b, int units, int64_t &bh, int &u)
+{
+    const int64_t heads = gridDim.x / units;
+    if ((heads & 7) == 0) {
+        const int64_t l = b >> 3;
+        bh = (l / units) * 8 + (b & 7);
+        u = (int)(l % units);
+    } else {
+        bh = b / units;
+        u = (int)(b % units);
+    }
+}
+
 // sum over the 16 lanes that share l/16
 __device__ __forceinline__ float group16_sum(float v) { return group_sum<16>(v); }
 

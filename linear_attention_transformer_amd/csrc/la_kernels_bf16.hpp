@@ -189,10 +189,12 @@ __global__ __launch_bounds__(kApplyThreads) void k_apply_bf(
     constexpr int OCH = TR * CPR / kApplyThreads;  // 16-byte output chunks per thread
     __shared__ __attribute__((aligned(16))) uint16_t ot[2][TR * LDX];
 
-    const int sub = (KIND == 2) ? (int)(blockIdx.x & 1) : 0;
-    const int64_t b = (KIND == 2) ? (blockIdx.x >> 1) : blockIdx.x;
-    const int64_t bh = b / nseg;
-    const int seg = (int)(b % nseg);
+    // unit = segment (forward, dQ) or 2 segment + parity (dK | dV)
+    int64_t bh;
+    int unit;
+    xcd_unit(blockIdx.x, KIND == 2 ? 2 * nseg : nseg, bh, unit);
+    const int sub = (KIND == 2) ? (unit & 1) : 0;
+    const int seg = (KIND == 2) ? (unit >> 1) : unit;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, j = lane & 31, h = lane >> 5;
     const int cb = w % NCB, rg = w / NCB;
     const int64_t beg = (int64_t)seg * seg_len;
@@ -681,8 +683,9 @@ __global__ __launch_bounds__(512) void k_bwd_q_bf(
     constexpr int TPW1 = NCB / 2;  // dS tiles per wave and dimension
     __shared__ __attribute__((aligned(16))) Lt L;
 
-    const int64_t bh = blockIdx.x / nseg;
-    const int seg = (int)(blockIdx.x % nseg);
+    int64_t bh;
+    int seg;
+    xcd_unit(blockIdx.x, nseg, bh, seg);
     const int tid = threadIdx.x, lane = tid & 63, j = lane & 31, h = lane >> 5;
     // the wave index as a scalar: the role branches below are uniform per
     // wave, and each role's loop passes the same barriers

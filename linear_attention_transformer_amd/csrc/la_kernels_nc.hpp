@@ -533,10 +533,12 @@ __global__ __launch_bounds__(apply_threads<D>()) void k_apply_nc(
     // the round's barrier)
     __shared__ float xch[KIND == 0 ? 2 : 1][NRG][NCB][32];
 
-    const int sub = (KIND == 2) ? (int)(blockIdx.x & 1) : 0;
-    const int64_t b = (KIND == 2) ? (blockIdx.x >> 1) : blockIdx.x;
-    const int64_t bh = b / nseg;
-    const int seg = (int)(b % nseg);
+    // unit = segment (forward, dQ) or 2 segment + parity (dK | dV)
+    int64_t bh;
+    int unit;
+    xcd_unit(blockIdx.x, KIND == 2 ? 2 * nseg : nseg, bh, unit);
+    const int sub = (KIND == 2) ? (unit & 1) : 0;
+    const int seg = (KIND == 2) ? (unit >> 1) : unit;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, j = lane & 31, h = lane >> 5;
     const int cb = w % NCB, rg = w / NCB;
     const int64_t beg = (int64_t)seg * seg_len;
@@ -800,8 +802,9 @@ __global__ __launch_bounds__(512) void k_bwd_q_nc(
     __shared__ float cx[2][NRG][32];           // c_i of the round's rows
     __shared__ float ivx[2][TR];               // 1/den_i of the round's rows
 
-    const int64_t bh = blockIdx.x / nseg;
-    const int seg = (int)(blockIdx.x % nseg);
+    int64_t bh;
+    int seg;
+    xcd_unit(blockIdx.x, nseg, bh, seg);
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, j = lane & 31, h = lane >> 5;
     const int role = DS ? (w >> 2) : 0, w0 = DS ? (w & 3) : w;
     const int cb = w0 % NCB, rg = w0 / NCB;
