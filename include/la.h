@@ -36,12 +36,15 @@
  *  - B, H, N >= 0, B*H <= 2^22, N <= 2^24 (LA_ERR_SHAPE otherwise).
  *    B*H*N == 0 is a no-op returning LA_OK.
  *    1 <= D <= 256 (LA_ERR_UNSUPPORTED otherwise).  D = 32, 64, 128, 256
- *    run as they are.  Other head sizes (the Figure 1 caption of the
- *    sciencestack.ai page draws D = 6) are padded through the workspace
- *    with zero columns to the next of those sizes, which is exact (the zero
- *    columns add nothing to q.k and give zero output columns), and the
- *    results are unpadded.  This costs extra passes over the data and room
- *    for seven padded tensors (see la_workspace_size_for).
+ *    run as they are.  D <= 16 (the Figure 1 caption of the sciencestack.ai
+ *    page draws D = 6) runs at width 16 on the caller's own rows: the
+ *    kernels read D columns per row and take the others as zero, and write
+ *    D columns, which is exact (zero columns add nothing to q.k and give
+ *    zero output columns); only the carried records change width.  Other
+ *    head sizes are padded through the workspace with zero columns to the
+ *    next native size and the results unpadded, which costs extra passes
+ *    over the data and room for seven padded tensors (see
+ *    la_workspace_size_for).
  *  - fp16 storage runs on the fp32 matrix-core kernels (widened exactly on
  *    load); bf16 storage runs on the bf16 matrix cores for D = 32..128 (with
  *    fp32 factors split into two bf16 terms) and on the fp32 ones at 256.
@@ -107,7 +110,8 @@ size_t la_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D,
 /* Bytes of the state the forward pass can save for the backward pass:
  * the reduced key-value state (S, z, u) of every head, and in the causal
  * case one exclusive prefix of it per sequence segment.  fp32, at the
- * padded head size for padded calls; its layout is internal. */
+ * width the kernels run at (16 for D <= 16, the padded size for padded
+ * calls); its layout is internal. */
 size_t la_state_size(int64_t B, int64_t H, int64_t N, int64_t D, int causal);
 
 /* Number of sequence segments each head is split into (diagnostic). */
@@ -356,7 +360,9 @@ int la_layer_backward(const void *X, const void *Wqkv, const void *Wo,
  *   names      : optional out array of n_events/2 entries; names[i] is set
  *                to a static string naming the i-th kernel ("state_local",
  *                "state_scan", "forward", "bwd_q", "grad_state_local",
- *                "bwd_kv").
+ *                "bwd_kv"; for padded head sizes also "stage" and
+ *                "unstage", the tensor passes, and for carried records of
+ *                another width "stage_record" and "unstage_record").
  * Events are recorded only when all arguments are valid.  The library
  * never creates, synchronises or destroys the events.
  */

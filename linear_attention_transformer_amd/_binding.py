@@ -20,7 +20,8 @@ STATUS = {0: "LA_OK", 1: "LA_ERR_NULL", 2: "LA_ERR_SHAPE", 3: "LA_ERR_DTYPE",
           4: "LA_ERR_UNSUPPORTED", 5: "LA_ERR_WORKSPACE", 6: "LA_ERR_ALIAS",
           7: "LA_ERR_ALIGN", 8: "LA_ERR_HIP", 9: "LA_ERR_HIP_PENDING"}
 SUPPORTED_D = tuple(range(1, 257))      # every head size the library takes
-NATIVE_D = (32, 64, 128, 256)            # run without padding
+NATIVE_D = (32, 64, 128, 256)            # run at their own width
+NARROW_D = tuple(range(1, 17))           # run at width 16 on the caller's rows (no padded copies)
 
 _lib = None
 

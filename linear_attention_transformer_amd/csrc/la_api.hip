@@ -31,6 +31,7 @@ constexpr int64_t kTargetWorkgroups = 512;
 
 struct Plan {
     int64_t BH, N, D, PS, nseg, seg_len;
+    int64_t dl;  // columns of the caller's rows (D unless a narrow head runs at width D)
     int causal;
     float n0;  // tokens carried in from outside the call, added to every row's count
     OutLay ol; // where the outputs go (default: [B, H, N, D] contiguous)
@@ -58,6 +59,7 @@ Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int causal)
     p.causal = causal;
     p.n0 = 0.f;
     p.ol = plain_layout(H, N, D);
+    p.dl = D;
     const int64_t nchunks = std::max<int64_t>((N + kSegAlign - 1) / kSegAlign, 1);
     const int64_t want =
         p.BH >= kTargetWorkgroups ? 1 : (kTargetWorkgroups + p.BH - 1) / std::max<int64_t>(p.BH, 1);
@@ -163,7 +165,7 @@ int64_t state_floats(const Plan &p) { return p.BH * (p.causal ? p.nseg : 1) * p.
 // (the extra columns zero)
 int64_t padded_d(int64_t D)
 {
-    for (int64_t d : {32, 64, 128, 256})
+    for (int64_t d : {16, 32, 64, 128, 256})
         if (D <= d)
             return d;
     return 0;
@@ -351,7 +353,7 @@ int state_of_kv(const void *K, const void *V, float *part, float *tot, const Pla
         rc = traced(t, s, "state_local", [&] {
             k_state_local<ST, D><<<grid, dim3(C::NT), 0, s>>>(
                 static_cast<const T *>(K), static_cast<const T *>(V), part, p.N, p.seg_len,
-                (int)p.nseg);
+                (int)p.nseg, (int)p.dl);
         });
     }
     if (rc != LA_OK)
@@ -429,12 +431,12 @@ int run_forward(const void *Q, const void *K, const void *V, void *O, float *den
             k_forward<ST, D, true><<<grid, dim3(C::NT), 0, s>>>(
                 static_cast<const T *>(Q), static_cast<const T *>(K),
                 static_cast<const T *>(V), static_cast<T *>(O), den_out, rec, p.N,
-                p.seg_len, (int)p.nseg, p.n0, p.ol);
+                p.seg_len, (int)p.nseg, p.n0, p.ol, (int)p.dl);
         else
             k_forward<ST, D, false><<<grid, dim3(C::NT), 0, s>>>(
                 static_cast<const T *>(Q), static_cast<const T *>(K),
                 static_cast<const T *>(V), static_cast<T *>(O), den_out, rec, p.N,
-                p.seg_len, (int)p.nseg, p.n0, p.ol);
+                p.seg_len, (int)p.nseg, p.n0, p.ol, (int)p.dl);
     });
 }
 
@@ -616,15 +618,15 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
     rc = traced(t, s, "bwd_q", [&] {
         k_bwd_q<ST, D, CAUSAL, FUSE><<<dim3((unsigned)(p.nseg * p.BH)), dim3(CQ::NT), 0, s>>>(
             q, k, v, g, static_cast<T *>(dQ), fstate, gpart, cbuf, p.N, p.seg_len,
-            (int)p.nseg, p.n0, p.ol);
+            (int)p.nseg, p.n0, p.ol, (int)p.dl);
     });
     if (rc != LA_OK)
         return rc;
     const dim3 grid((unsigned)(p.nseg * p.BH * C::CS));
     if constexpr (!FUSE) {
         rc = traced(t, s, "grad_state_local", [&] {
-            k_grad_state_local<ST, D><<<grid, dim3(C::NT), 0, s>>>(q, g, cbuf, gpart, p.N,
-                                                                   p.seg_len, (int)p.nseg);
+            k_grad_state_local<ST, D><<<grid, dim3(C::NT), 0, s>>>(
+                q, g, cbuf, gpart, p.N, p.seg_len, (int)p.nseg, (int)p.dl);
         });
         if (rc != LA_OK)
             return rc;
@@ -644,7 +646,7 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
     return traced(t, s, "bwd_kv", [&] {
         k_bwd_kv<ST, D, CAUSAL><<<grid, dim3(C::NT), 0, s>>>(
             q, k, v, g, static_cast<T *>(dK), static_cast<T *>(dV), gstate, cbuf, p.N,
-            p.seg_len, (int)p.nseg, p.ol);
+            p.seg_len, (int)p.nseg, p.ol, (int)p.dl);
     });
 }
 
@@ -666,6 +668,7 @@ int dispatch_forward(const void *Q, const void *K, const void *V, void *O, float
                      const float *cin, float *cout)
 {
     switch (p.D) {
+    case 16: return run_forward<ST, 16>(Q, K, V, O, den, st, ws, p, s, t, cin, cout);
     case 32: return run_forward<ST, 32>(Q, K, V, O, den, st, ws, p, s, t, cin, cout);
     case 64: return run_forward<ST, 64>(Q, K, V, O, den, st, ws, p, s, t, cin, cout);
     case 128: return run_forward<ST, 128>(Q, K, V, O, den, st, ws, p, s, t, cin, cout);
@@ -683,6 +686,7 @@ int dispatch_backward(const void *Q, const void *K, const void *V, const void *G
 #define LA_BWD(d)                                                                          \
     run_backward<ST, d>(Q, K, V, G, dQ, dK, dV, st, ws, p, s, t, cin, gin, gout)
     switch (p.D) {
+    case 16: return LA_BWD(16);
     case 32: return LA_BWD(32);
     case 64: return LA_BWD(64);
     case 128: return LA_BWD(128);
@@ -724,14 +728,16 @@ int forward_impl(bool require_o, const void *Q, const void *K, const void *V, vo
                  int64_t B, int64_t H, int64_t N, int64_t D, int causal, int dtype,
                  const float *cin, int64_t n_carry, float *cout, float *den_out,
                  void *state_out, void *ws, size_t ws_bytes, hipStream_t s, Tracer *t,
-                 const OutLay *ol = nullptr)
+                 const OutLay *ol = nullptr, int64_t dl = 0)
 {
     if (!valid_dtype(dtype))
         return LA_ERR_DTYPE;
     int rc = check_sizes(B, H, N, D, causal);
     if (rc != LA_OK)
         return rc;
-    if (!supported_d(D))
+    // dl > 0: heads of dl <= 16 columns run at width D = 16 on the caller's
+    // rows (dl elements apart); the records stay at width D
+    if (!(supported_d(D) || (D == 16 && dl > 0 && dl <= 16)))
         return LA_ERR_UNSUPPORTED;
     if (n_carry < 0 || n_carry > kMaxCarry)
         return LA_ERR_SHAPE;
@@ -750,8 +756,12 @@ int forward_impl(bool require_o, const void *Q, const void *K, const void *V, vo
         return LA_ERR_NULL;
     Plan p = make_plan(B, H, N, D, causal);
     p.n0 = (float)n_carry;
+    if (dl > 0) {
+        p.dl = dl;
+        p.ol = plain_layout(H, N, dl);
+    }
     if (ol != nullptr) {
-        if (!layout_ok(*ol, D, elem_size(dtype), true))
+        if (!layout_ok(*ol, p.dl, elem_size(dtype), p.dl == D))
             return LA_ERR_ALIGN;
         p.ol = *ol;
     }
@@ -763,8 +773,8 @@ int forward_impl(bool require_o, const void *Q, const void *K, const void *V, vo
         misaligned(den_out) || misaligned(state_out) || misaligned(ws) || misaligned(cin) ||
         misaligned(cout))
         return LA_ERR_ALIGN;
-    const size_t tb = (size_t)(B * H * N * D) * elem_size(dtype);
-    const size_t ob = (size_t)out_extent(p.ol, B, H, N, D) * elem_size(dtype);
+    const size_t tb = (size_t)(B * H * N * p.dl) * elem_size(dtype);
+    const size_t ob = (size_t)out_extent(p.ol, B, H, N, p.dl) * elem_size(dtype);
     const Range ins[4] = {{(const char *)Q, tb},
                           {(const char *)K, tb},
                           {(const char *)V, tb},
@@ -794,14 +804,16 @@ int backward_impl(bool require_kv, const void *Q, const void *K, const void *V,
                   int64_t N, int64_t D, int causal, int dtype, const float *cin,
                   int64_t n_carry, const float *gin, float *gout, const void *state_in,
                   void *ws, size_t ws_bytes, hipStream_t s, Tracer *t,
-                  const OutLay *ol = nullptr)
+                  const OutLay *ol = nullptr, int64_t dl = 0)
 {
     if (!valid_dtype(dtype))
         return LA_ERR_DTYPE;
     int rc = check_sizes(B, H, N, D, causal);
     if (rc != LA_OK)
         return rc;
-    if (!supported_d(D))
+    // dl > 0: heads of dl <= 16 columns run at width D = 16 on the caller's
+    // rows (dl elements apart); the records stay at width D
+    if (!(supported_d(D) || (D == 16 && dl > 0 && dl <= 16)))
         return LA_ERR_UNSUPPORTED;
     if (n_carry < 0 || n_carry > kMaxCarry)
         return LA_ERR_SHAPE;
@@ -821,8 +833,12 @@ int backward_impl(bool require_kv, const void *Q, const void *K, const void *V,
         return LA_ERR_NULL;
     Plan p = make_plan(B, H, N, D, causal);
     p.n0 = (float)n_carry;
+    if (dl > 0) {
+        p.dl = dl;
+        p.ol = plain_layout(H, N, dl);
+    }
     if (ol != nullptr) {
-        if (!layout_ok(*ol, D, elem_size(dtype), true))
+        if (!layout_ok(*ol, p.dl, elem_size(dtype), p.dl == D))
             return LA_ERR_ALIGN;
         p.ol = *ol;
     }
@@ -833,8 +849,8 @@ int backward_impl(bool require_kv, const void *Q, const void *K, const void *V,
         misaligned(dQ) || misaligned(dK) || misaligned(dV) || misaligned(state_in) ||
         misaligned(ws) || misaligned(cin) || misaligned(gin) || misaligned(gout))
         return LA_ERR_ALIGN;
-    const size_t tb = (size_t)(B * H * N * D) * elem_size(dtype);
-    const size_t ob = (size_t)out_extent(p.ol, B, H, N, D) * elem_size(dtype);
+    const size_t tb = (size_t)(B * H * N * p.dl) * elem_size(dtype);
+    const size_t ob = (size_t)out_extent(p.ol, B, H, N, p.dl) * elem_size(dtype);
     const Range ins[7] = {{(const char *)Q, tb},
                           {(const char *)K, tb},
                           {(const char *)V, tb},
@@ -867,7 +883,8 @@ int backward_impl(bool require_kv, const void *Q, const void *K, const void *V,
 // ------------------------------------------------------------ staging
 // Workspace of a padded call, in bytes: the native call's workspace at Dp,
 // then seven padded [B,H,N,Dp] tensors, then three padded records, each
-// region 256-byte aligned.
+// region 256-byte aligned.  Heads of D <= 16 run at width Dp = 16 on the
+// caller's own rows: no padded tensors, only the records.
 struct Staging {
     int64_t Dp;
     size_t inner, tensor, record;
@@ -882,7 +899,7 @@ Staging make_staging(int64_t B, int64_t H, int64_t N, int64_t D, int causal, int
     g.Dp = padded_d(D);
     g.inner = N > 0 ? (size_t)make_layout(make_plan(B, H, N, g.Dp, causal)).total * sizeof(float)
                     : 0;
-    g.tensor = up256((size_t)(B * H * N * g.Dp) * elem_size(dtype));
+    g.tensor = g.Dp == 16 ? 0 : up256((size_t)(B * H * N * g.Dp) * elem_size(dtype));
     g.record = up256(record_bytes(B * H, g.Dp));
     size_t off = 0;
     g.off_inner = off;
@@ -939,10 +956,12 @@ int stage_tensor(const char *name, bool to_padded, const void *src, void *dst, i
     });
 }
 
-int stage_record(const char *name, const float *src, int64_t Ds, float *dst, int64_t Dd,
-                 int64_t BH, hipStream_t s, Tracer *t)
+// a record of width Ds as one of width Dd (zero where Dd > Ds); `to` names
+// the direction for the tracer
+int stage_record(bool to, const float *src, int64_t Ds, float *dst, int64_t Dd, int64_t BH,
+                 hipStream_t s, Tracer *t)
 {
-    return traced(t, s, name, [&] {
+    return traced(t, s, to ? "stage_record" : "unstage_record", [&] {
         stg::k_stage_record<<<dim3(grid_for(BH * (Dd * Dd + 2 * Dd))), dim3(stg::kThreads), 0,
                               s>>>(src, dst, BH, (int)Ds, (int)Dd);
     });
@@ -974,7 +993,7 @@ int forward_any(bool require_o, const void *Q, const void *K, const void *V, voi
     if (N == 0) {
         if (overlap({(const char *)cout, rb}, {(const char *)cin, rb}))
             return LA_ERR_ALIAS;
-        return cout ? stage_record("stage", cin, D, cout, D, BH, s, t) : LA_OK;
+        return cout ? stage_record(true, cin, D, cout, D, BH, s, t) : LA_OK;
     }
     if (!Q || !K || !V || !ws || (!O && (require_o || den_out || (!cout && !state_out))))
         return LA_ERR_NULL;
@@ -1007,12 +1026,24 @@ int forward_any(bool require_o, const void *Q, const void *K, const void *V, voi
          *to = w + g.off_tensor[3];
     float *r_in = reinterpret_cast<float *>(w + g.off_record[0]);
     float *r_out = reinterpret_cast<float *>(w + g.off_record[1]);
+    if (g.Dp == 16) {
+        // D <= 16: the kernels read and write the caller's rows directly;
+        // only the carried records change width
+        if (cin && (rc = stage_record(true, cin, D, r_in, g.Dp, BH, s, t)) != LA_OK)
+            return rc;
+        rc = forward_impl(require_o, Q, K, V, O, B, H, N, g.Dp, causal, dtype,
+                          cin ? r_in : nullptr, n_carry, cout ? r_out : nullptr, den_out,
+                          state_out, w + g.off_inner, g.inner, s, t, ol, D);
+        if (rc != LA_OK)
+            return rc;
+        return cout ? stage_record(false, r_out, g.Dp, cout, D, BH, s, t) : LA_OK;
+    }
     const int64_t rows = BH * N;
     if ((rc = stage_tensor("stage", true, Q, tq, dtype, D, g.Dp, rows, s, t)) != LA_OK ||
         (rc = stage_tensor("stage", true, K, tk, dtype, D, g.Dp, rows, s, t)) != LA_OK ||
         (rc = stage_tensor("stage", true, V, tv, dtype, D, g.Dp, rows, s, t)) != LA_OK)
         return rc;
-    if (cin && (rc = stage_record("stage", cin, D, r_in, g.Dp, BH, s, t)) != LA_OK)
+    if (cin && (rc = stage_record(true, cin, D, r_in, g.Dp, BH, s, t)) != LA_OK)
         return rc;
     rc = forward_impl(require_o, tq, tk, tv, O ? to : nullptr, B, H, N, g.Dp, causal, dtype,
                       cin ? r_in : nullptr, n_carry, cout ? r_out : nullptr, den_out,
@@ -1022,7 +1053,7 @@ int forward_any(bool require_o, const void *Q, const void *K, const void *V, voi
     if (O && (rc = stage_tensor("unstage", false, to, O, dtype, D, g.Dp, rows, s, t, N, ol)) !=
                  LA_OK)
         return rc;
-    if (cout && (rc = stage_record("unstage", r_out, g.Dp, cout, D, BH, s, t)) != LA_OK)
+    if (cout && (rc = stage_record(false, r_out, g.Dp, cout, D, BH, s, t)) != LA_OK)
         return rc;
     return LA_OK;
 }
@@ -1054,7 +1085,7 @@ int backward_any(bool require_kv, const void *Q, const void *K, const void *V,
     if (N == 0) {
         if (overlap({(const char *)gout, rb}, {(const char *)gin, rb}))
             return LA_ERR_ALIAS;
-        return gout ? stage_record("stage", gin, D, gout, D, BH, s, t) : LA_OK;
+        return gout ? stage_record(true, gin, D, gout, D, BH, s, t) : LA_OK;
     }
     if (!Q || !K || !V || !dO || !dQ || !ws || (dK == nullptr) != (dV == nullptr) ||
         (require_kv && dK == nullptr))
@@ -1094,15 +1125,30 @@ int backward_any(bool require_kv, const void *Q, const void *K, const void *V,
     float *r_cin = reinterpret_cast<float *>(w + g.off_record[0]);
     float *r_gin = reinterpret_cast<float *>(w + g.off_record[1]);
     float *r_gout = reinterpret_cast<float *>(w + g.off_record[2]);
+    if (g.Dp == 16) {
+        // D <= 16: the kernels read and write the caller's rows directly;
+        // only the carried records change width
+        if (cin && !state_in && (rc = stage_record(true, cin, D, r_cin, g.Dp, BH, s, t)) != LA_OK)
+            return rc;
+        if (gin && (rc = stage_record(true, gin, D, r_gin, g.Dp, BH, s, t)) != LA_OK)
+            return rc;
+        rc = backward_impl(require_kv, Q, K, V, dO, dQ, dK, dV, B, H, N, g.Dp, causal, dtype,
+                           (cin && !state_in) ? r_cin : nullptr, n_carry, gin ? r_gin : nullptr,
+                           gout ? r_gout : nullptr, state_in, w + g.off_inner, g.inner, s, t, ol,
+                           D);
+        if (rc != LA_OK)
+            return rc;
+        return gout ? stage_record(false, r_gout, g.Dp, gout, D, BH, s, t) : LA_OK;
+    }
     const int64_t rows = BH * N;
     const void *src[4] = {Q, K, V, dO};
     for (int i = 0; i < 4; ++i)
         if ((rc = stage_tensor("stage", true, src[i], T_[i], dtype, D, g.Dp, rows, s, t)) !=
             LA_OK)
             return rc;
-    if (cin && !state_in && (rc = stage_record("stage", cin, D, r_cin, g.Dp, BH, s, t)) != LA_OK)
+    if (cin && !state_in && (rc = stage_record(true, cin, D, r_cin, g.Dp, BH, s, t)) != LA_OK)
         return rc;
-    if (gin && (rc = stage_record("stage", gin, D, r_gin, g.Dp, BH, s, t)) != LA_OK)
+    if (gin && (rc = stage_record(true, gin, D, r_gin, g.Dp, BH, s, t)) != LA_OK)
         return rc;
     const bool kv = dK != nullptr;
     rc = backward_impl(require_kv, T_[0], T_[1], T_[2], T_[3], T_[4], kv ? T_[5] : nullptr,
@@ -1120,7 +1166,7 @@ int backward_any(bool require_kv, const void *Q, const void *K, const void *V,
          (rc = stage_tensor("unstage", false, T_[6], dV, dtype, D, g.Dp, rows, s, t, N, ol)) !=
              LA_OK))
         return rc;
-    if (gout && (rc = stage_record("unstage", r_gout, g.Dp, gout, D, BH, s, t)) != LA_OK)
+    if (gout && (rc = stage_record(false, r_gout, g.Dp, gout, D, BH, s, t)) != LA_OK)
         return rc;
     return LA_OK;
 }

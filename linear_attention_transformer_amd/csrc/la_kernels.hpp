@@ -262,7 +262,8 @@ __device__ __forceinline__ int ncol(int cs, int w, int nb)
 // ---------------------------------------------------------------- tile I/O
 // ROWS x D tile of one head, fetched with 16-byte loads into registers and
 // committed to LDS as fp32 (row stride D + 4).  Rows at or beyond `lim` read
-// as zero.
+// as zero.  A head of dl < D columns (rows dl elements apart in memory) is
+// read element by element, its columns dl .. D - 1 as zero.
 template <class ST, class C, int ROWS>
 struct Tile {
     typedef typename ST::T T;
@@ -273,7 +274,7 @@ struct Tile {
     uint4 r[PER];
 
     __device__ __forceinline__ void fetch(const T *__restrict__ head, int64_t row0,
-                                          int64_t lim)
+                                          int64_t lim, int dl = D)
     {
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
@@ -281,9 +282,20 @@ struct Tile {
             r[p] = make_uint4(0u, 0u, 0u, 0u);
             if (NV % C::NT == 0 || idx < NV) {
                 const int row = idx / VPR, cv = idx % VPR;
-                if (row0 + row < lim)
-                    r[p] = *reinterpret_cast<const uint4 *>(
-                        head + (row0 + row) * (int64_t)D + cv * ST::VEC);
+                if (row0 + row < lim) {
+                    if (dl == D) {
+                        r[p] = *reinterpret_cast<const uint4 *>(
+                            head + (row0 + row) * (int64_t)D + cv * ST::VEC);
+                    } else {
+                        T v[ST::VEC];
+#pragma unroll
+                        for (int x = 0; x < ST::VEC; ++x) {
+                            const int col = cv * ST::VEC + x;
+                            v[x] = col < dl ? head[(row0 + row) * (int64_t)dl + col] : T(0);
+                        }
+                        r[p] = __builtin_bit_cast(uint4, v);
+                    }
+                }
             }
         }
     }
@@ -517,7 +529,7 @@ __device__ __forceinline__ Where decode(int nseg)
 template <class ST, int D>
 __global__ __launch_bounds__(threads_for<D>()) void k_state_local(
     const typename ST::T *__restrict__ Kp, const typename ST::T *__restrict__ Vp,
-    float *__restrict__ part, int64_t N, int64_t seg_len, int nseg)
+    float *__restrict__ part, int64_t N, int64_t seg_len, int nseg, int dl)
 {
     typedef Cfg<D, DefCS<D>::value> C;
     constexpr int R = C::RN;
@@ -528,23 +540,23 @@ __global__ __launch_bounds__(threads_for<D>()) void k_state_local(
               lg = lane >> 4;
     const int64_t beg = g.seg * seg_len;
     const int64_t end = (beg + seg_len < N) ? beg + seg_len : N;
-    const typename ST::T *xh = Kp + g.bh * N * D;
-    const typename ST::T *yh = Vp + g.bh * N * D;
+    const typename ST::T *xh = Kp + g.bh * N * dl;
+    const typename ST::T *yh = Vp + g.bh * N * dl;
 
     Acc<C> acc;
     acc.zero();
     float csum = 0.f;
 
     Tile<ST, C, R> tx, ty;
-    tx.fetch(xh, beg, end);
-    ty.fetch(yh, beg, end);
+    tx.fetch(xh, beg, end, dl);
+    ty.fetch(yh, beg, end, dl);
     for (int64_t c0 = beg; c0 < end; c0 += R) {
         __syncthreads();
         tx.commit(xs);
         ty.commit(ys);
         if (c0 + R < end) {
-            tx.fetch(xh, c0 + R, end);
-            ty.fetch(yh, c0 + R, end);
+            tx.fetch(xh, c0 + R, end, dl);
+            ty.fetch(yh, c0 + R, end, dl);
         }
         __syncthreads();
         reduce_rows<C, R>(acc, xs, ys, g.cs, w, lr, lg);
@@ -564,7 +576,7 @@ template <class ST, int D>
 __global__ __launch_bounds__(threads_for<D>()) void k_grad_state_local(
     const typename ST::T *__restrict__ Q, const typename ST::T *__restrict__ G,
     const float *__restrict__ cbuf, float *__restrict__ gpart, int64_t N,
-    int64_t seg_len, int nseg)
+    int64_t seg_len, int nseg, int dl)
 {
     typedef Cfg<D, DefCS<D>::value> C;
     constexpr int R = C::RN;
@@ -576,21 +588,21 @@ __global__ __launch_bounds__(threads_for<D>()) void k_grad_state_local(
               lg = lane >> 4;
     const int64_t beg = g.seg * seg_len;
     const int64_t end = (beg + seg_len < N) ? beg + seg_len : N;
-    const int64_t hoff = g.bh * N * D;
+    const int64_t hoff = g.bh * N * dl;
 
     Acc<C> acc;
     acc.zero();
     float csum = 0.f;
     Tile<ST, C, R> tq, tg;
-    tq.fetch(Q + hoff, beg, end);
-    tg.fetch(G + hoff, beg, end);
+    tq.fetch(Q + hoff, beg, end, dl);
+    tg.fetch(G + hoff, beg, end, dl);
     for (int64_t c0 = beg; c0 < end; c0 += R) {
         __syncthreads();
         tq.commit(qs);
         tg.commit(gs);
         if (c0 + R < end) {
-            tq.fetch(Q + hoff, c0 + R, end);
-            tg.fetch(G + hoff, c0 + R, end);
+            tq.fetch(Q + hoff, c0 + R, end, dl);
+            tg.fetch(G + hoff, c0 + R, end, dl);
         }
         for (int i = tid; i < R; i += C::NT) {
             const bool ok = c0 + i < end;
@@ -679,7 +691,7 @@ __global__ __launch_bounds__(threads_for<D>()) void k_forward(
     const typename ST::T *__restrict__ Q, const typename ST::T *__restrict__ Kp,
     const typename ST::T *__restrict__ Vp, typename ST::T *__restrict__ O,
     float *__restrict__ den_out, const float *__restrict__ state, int64_t N,
-    int64_t seg_len, int nseg, float n0, OutLay ol)
+    int64_t seg_len, int nseg, float n0, OutLay ol, int dl)
 {
     typedef Cfg<D, DefCS<D>::value> C;
     constexpr int R = CAUSAL ? C::RC : C::RN;
@@ -698,7 +710,7 @@ __global__ __launch_bounds__(threads_for<D>()) void k_forward(
               lg = lane >> 4;
     const int64_t beg = g.seg * seg_len;
     const int64_t end = (beg + seg_len < N) ? beg + seg_len : N;
-    const int64_t hoff = g.bh * N * D;
+    const int64_t hoff = g.bh * N * dl;
     const float *st = state + (CAUSAL ? (g.bh * nseg + g.seg) : g.bh) * (int64_t)C::PS;
 
     Acc<C> S;  // Mat[k=d][n=e] = S
@@ -711,10 +723,10 @@ __global__ __launch_bounds__(threads_for<D>()) void k_forward(
 
     Tile<ST, C, R> tq;
     Tile<ST, C, RK> tk, tv;
-    tq.fetch(Q + hoff, beg, end);
+    tq.fetch(Q + hoff, beg, end, dl);
     if constexpr (CAUSAL) {
-        tk.fetch(Kp + hoff, beg, end);
-        tv.fetch(Vp + hoff, beg, end);
+        tk.fetch(Kp + hoff, beg, end, dl);
+        tv.fetch(Vp + hoff, beg, end, dl);
     }
     for (int64_t c0 = beg; c0 < end; c0 += R) {
         __syncthreads();
@@ -724,10 +736,10 @@ __global__ __launch_bounds__(threads_for<D>()) void k_forward(
             tv.commit(vs);
         }
         if (c0 + R < end) {
-            tq.fetch(Q + hoff, c0 + R, end);
+            tq.fetch(Q + hoff, c0 + R, end, dl);
             if constexpr (CAUSAL) {
-                tk.fetch(Kp + hoff, c0 + R, end);
-                tv.fetch(Vp + hoff, c0 + R, end);
+                tk.fetch(Kp + hoff, c0 + R, end, dl);
+                tv.fetch(Vp + hoff, c0 + R, end, dl);
             }
         }
         __syncthreads();
@@ -771,8 +783,9 @@ __global__ __launch_bounds__(threads_for<D>()) void k_forward(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = tb * 16 + 4 * lg + r;
-                    if (c0 + row < end)
-                        O[ol.head(g.bh) + (c0 + row) * ol.sn + ncol<C>(g.cs, w, nb) + lr] =
+                    const int col = ncol<C>(g.cs, w, nb) + lr;
+                    if (c0 + row < end && col < dl)
+                        O[ol.head(g.bh) + (c0 + row) * ol.sn + col] =
                             ST::narrow(out[tb][nb][r] / denl[row]);
                 }
         if (den_out != nullptr && g.cs == 0)
@@ -800,7 +813,7 @@ __global__ __launch_bounds__(threads_for<D>()) void k_bwd_q(
     const typename ST::T *__restrict__ Vp, const typename ST::T *__restrict__ G,
     typename ST::T *__restrict__ dQ, const float *__restrict__ state,
     float *__restrict__ gpart, float *__restrict__ cbuf, int64_t N, int64_t seg_len,
-    int nseg, float n0, OutLay ol)
+    int nseg, float n0, OutLay ol, int dl)
 {
     typedef Cfg<D, 1> C;
     constexpr int R = CAUSAL ? C::RC : C::RN;
@@ -823,7 +836,7 @@ __global__ __launch_bounds__(threads_for<D>()) void k_bwd_q(
               lg = lane >> 4;
     const int64_t beg = g.seg * seg_len;
     const int64_t end = (beg + seg_len < N) ? beg + seg_len : N;
-    const int64_t hoff = g.bh * N * D;
+    const int64_t hoff = g.bh * N * dl;
     const float *st = state + (CAUSAL ? (g.bh * nseg + g.seg) : g.bh) * (int64_t)C::PS;
 
     Acc<C> ST_;  // Mat[k=e][n=d] = S^T
@@ -840,11 +853,11 @@ __global__ __launch_bounds__(threads_for<D>()) void k_bwd_q(
 
     Tile<ST, C, R> tq, tg;
     Tile<ST, C, RK> tk, tv;
-    tq.fetch(Q + hoff, beg, end);
-    tg.fetch(G + hoff, beg, end);
+    tq.fetch(Q + hoff, beg, end, dl);
+    tg.fetch(G + hoff, beg, end, dl);
     if constexpr (CAUSAL) {
-        tk.fetch(Kp + hoff, beg, end);
-        tv.fetch(Vp + hoff, beg, end);
+        tk.fetch(Kp + hoff, beg, end, dl);
+        tv.fetch(Vp + hoff, beg, end, dl);
     }
     for (int64_t c0 = beg; c0 < end; c0 += R) {
         __syncthreads();
@@ -855,11 +868,11 @@ __global__ __launch_bounds__(threads_for<D>()) void k_bwd_q(
             tv.commit(vs);
         }
         if (c0 + R < end) {
-            tq.fetch(Q + hoff, c0 + R, end);
-            tg.fetch(G + hoff, c0 + R, end);
+            tq.fetch(Q + hoff, c0 + R, end, dl);
+            tg.fetch(G + hoff, c0 + R, end, dl);
             if constexpr (CAUSAL) {
-                tk.fetch(Kp + hoff, c0 + R, end);
-                tv.fetch(Vp + hoff, c0 + R, end);
+                tk.fetch(Kp + hoff, c0 + R, end, dl);
+                tv.fetch(Vp + hoff, c0 + R, end, dl);
             }
         }
         __syncthreads();
@@ -970,9 +983,9 @@ __global__ __launch_bounds__(threads_for<D>()) void k_bwd_q(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = tb * 16 + 4 * lg + r;
-                    if (c0 + row < end)
-                        dQ[ol.head(g.bh) + (c0 + row) * ol.sn + ncol<C>(0, w, nb) + lr] =
-                            ST::narrow(y[tb][nb][r]);
+                    const int col = ncol<C>(0, w, nb) + lr;
+                    if (c0 + row < end && col < dl)
+                        dQ[ol.head(g.bh) + (c0 + row) * ol.sn + col] = ST::narrow(y[tb][nb][r]);
                 }
         if constexpr (FUSE) {
             reduce_rows<C, R>(dS, qs, gs, 0, w, lr, lg);
@@ -1008,7 +1021,7 @@ __global__ __launch_bounds__(threads_for<D>()) void k_bwd_kv(
     const typename ST::T *__restrict__ Vp, const typename ST::T *__restrict__ G,
     typename ST::T *__restrict__ dK, typename ST::T *__restrict__ dV,
     const float *__restrict__ gstate, const float *__restrict__ cbuf, int64_t N,
-    int64_t seg_len, int nseg, OutLay ol)
+    int64_t seg_len, int nseg, OutLay ol, int dl)
 {
     typedef Cfg<D, DefCS<D>::value> C;
     constexpr int R = CAUSAL ? C::RC : C::RN;
@@ -1029,7 +1042,7 @@ __global__ __launch_bounds__(threads_for<D>()) void k_bwd_kv(
               lg = lane >> 4;
     const int64_t beg = g.seg * seg_len;
     const int64_t end = (beg + seg_len < N) ? beg + seg_len : N;
-    const int64_t hoff = g.bh * N * D;
+    const int64_t hoff = g.bh * N * dl;
     const float *st = gstate + (CAUSAL ? (g.bh * nseg + g.seg) : g.bh) * (int64_t)C::PS;
 
     Acc<C> dST, dSN;  // Mat[k=e][n=d] = dS^T (for dK);  Mat[k=d][n=e] = dS (for dV)
@@ -1047,11 +1060,11 @@ __global__ __launch_bounds__(threads_for<D>()) void k_bwd_kv(
     Tile<ST, C, RQ> tq, tg;
     {
         const int64_t c = CAUSAL ? beg + (nch - 1) * R : beg;
-        tk.fetch(Kp + hoff, c, end);
-        tv.fetch(Vp + hoff, c, end);
+        tk.fetch(Kp + hoff, c, end, dl);
+        tv.fetch(Vp + hoff, c, end, dl);
         if constexpr (CAUSAL) {
-            tq.fetch(Q + hoff, c, end);
-            tg.fetch(G + hoff, c, end);
+            tq.fetch(Q + hoff, c, end, dl);
+            tg.fetch(G + hoff, c, end, dl);
         }
     }
     for (int64_t ci = 0; ci < nch; ++ci) {
@@ -1065,11 +1078,11 @@ __global__ __launch_bounds__(threads_for<D>()) void k_bwd_kv(
         }
         if (ci + 1 < nch) {
             const int64_t c1 = CAUSAL ? c0 - R : c0 + R;
-            tk.fetch(Kp + hoff, c1, end);
-            tv.fetch(Vp + hoff, c1, end);
+            tk.fetch(Kp + hoff, c1, end, dl);
+            tv.fetch(Vp + hoff, c1, end, dl);
             if constexpr (CAUSAL) {
-                tq.fetch(Q + hoff, c1, end);
-                tg.fetch(G + hoff, c1, end);
+                tq.fetch(Q + hoff, c1, end, dl);
+                tg.fetch(G + hoff, c1, end, dl);
             }
         }
         if constexpr (CAUSAL) {
@@ -1123,9 +1136,9 @@ __global__ __launch_bounds__(threads_for<D>()) void k_bwd_kv(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = tb * 16 + 4 * lg + r;
-                    if (c0 + row < end) {
-                        const int64_t o =
-                            ol.head(g.bh) + (c0 + row) * ol.sn + ncol<C>(g.cs, w, nb) + lr;
+                    const int col = ncol<C>(g.cs, w, nb) + lr;
+                    if (c0 + row < end && col < dl) {
+                        const int64_t o = ol.head(g.bh) + (c0 + row) * ol.sn + col;
                         dK[o] = ST::narrow(dk[tb][nb][r]);
                         dV[o] = ST::narrow(dv[tb][nb][r]);
                     }
