@@ -315,14 +315,14 @@ constexpr bool nc_path()
     return D >= 32 && D <= 128;
 }
 
-// fp32 or fp16 storage at D = 256: the fast reduction (four 128 x 128 blocks per
-// segment) for both masks, the fast non-causal apply kernels (eight waves)
-// and a dQ pass without the dS role (the gradient record then comes from
-// the reduction)
+// D = 256, every storage type (2-byte rows widened exactly to fp32): the
+// fast reduction (four 128 x 128 blocks per segment) for both masks, the
+// fast non-causal apply kernels (eight waves) and a dQ pass without the dS
+// role (the gradient record then comes from the reduction)
 template <class ST, int D>
 constexpr bool wide_path()
 {
-    return !std::is_same<ST, StBF16>::value && D == 256;
+    return D == 256;
 }
 
 template <class ST, int D>
@@ -335,7 +335,7 @@ int state_of_kv(const void *K, const void *V, float *part, float *tot, const Pla
     bool done = false;
     if constexpr (nc_path<D>() || wide_path<ST, D>()) {
         rc = traced(t, s, "state_local", [&] {
-            if constexpr (std::is_same<ST, StBF16>::value)
+            if constexpr (std::is_same<ST, StBF16>::value && D <= 128)
                 bf::k_reduce_bf<D, false><<<dim3((unsigned)(p.nseg * p.BH)), dim3(256), 0, s>>>(
                     static_cast<const T *>(K), static_cast<const T *>(V), nullptr, part, p.N,
                     p.seg_len, (int)p.nseg);
