@@ -61,8 +61,10 @@ Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int causal)
     p.ol = plain_layout(H, N, D);
     p.dl = D;
     const int64_t nchunks = std::max<int64_t>((N + kSegAlign - 1) / kSegAlign, 1);
+    // width 16 runs one-wave workgroups: four times as many fill the chip
+    const int64_t target = D <= 16 ? 8 * kTargetWorkgroups : kTargetWorkgroups;
     const int64_t want =
-        p.BH >= kTargetWorkgroups ? 1 : (kTargetWorkgroups + p.BH - 1) / std::max<int64_t>(p.BH, 1);
+        p.BH >= target ? 1 : (target + p.BH - 1) / std::max<int64_t>(p.BH, 1);
     const int64_t ns = std::min(want, nchunks);
     const int64_t per = (nchunks + ns - 1) / ns;
     p.seg_len = per * kSegAlign;
