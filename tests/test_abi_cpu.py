@@ -72,8 +72,11 @@ def test_sizes():
             la.workspace_size(B, H, N, 48)
     # heads of D <= 16 run at width 16 on the caller's rows: records of width
     # 16, and a workspace without padded tensors (below one [B,H,N,16] fp32)
-    assert la.state_size(B, H, N, 6, True) == la.state_size(B, H, N, 16, True) < \
-        la.state_size(B, H, N, 32, True)
+    ns16 = la.num_segments(B, H, N, 6)
+    for d in (1, 6, 16):
+        assert la.num_segments(B, H, N, d) == ns16
+        assert la.state_size(B, H, N, d, False) == B * H * (16 * 16 + 2 * 16) * 4
+        assert la.state_size(B, H, N, d, True) == B * H * ns16 * (16 * 16 + 2 * 16) * 4
     for d in (1, 6, 16):
         assert 0 < la.workspace_size(B, H, N, d) < B * H * N * 16 * 4
     assert la.workspace_size(4, 16, -1, 128) == 0
