@@ -389,12 +389,14 @@ int run_forward(const void *Q, const void *K, const void *V, void *O, float *den
     if constexpr (nc_path<D>()) {
         if (!p.causal)
             return traced(t, s, "forward", [&] {
-                if constexpr (std::is_same<ST, StBF16>::value)
-                    bf::k_apply_bf<D, 0><<<dim3((unsigned)(p.nseg * p.BH)),
+                if constexpr (std::is_same<ST, StBF16>::value) {
+                    const Plan pf = rows_plan(
+                        p, resident_wgs<bf::k_apply_bf<D, 0>>(bf::kApplyThreads), 1);
+                    bf::k_apply_bf<D, 0><<<dim3((unsigned)(pf.nseg * pf.BH)),
                                            dim3(bf::kApplyThreads), 0, s>>>(
                         static_cast<const T *>(Q), nullptr, static_cast<T *>(O), nullptr,
-                        den_out, nullptr, rec, p.N, p.seg_len, (int)p.nseg, p.n0, p.ol);
-                else {
+                        den_out, nullptr, rec, pf.N, pf.seg_len, (int)pf.nseg, pf.n0, pf.ol);
+                } else {
                     const Plan pf = rows_plan(
                         p, resident_wgs<nc::k_apply_nc<ST, D, 0>>(nc::kApplyThreads), 1);
                     nc::k_apply_nc<ST, D, 0><<<dim3((unsigned)(pf.nseg * pf.BH)),
@@ -602,12 +604,14 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
         if (dK == nullptr)
             return LA_OK;
         return traced(t, s, "bwd_kv", [&] {
-            if constexpr (std::is_same<ST, StBF16>::value)
-                bf::k_apply_bf<D, 2><<<dim3((unsigned)(2 * p.nseg * p.BH)),
+            if constexpr (std::is_same<ST, StBF16>::value) {
+                const Plan pk =
+                    rows_plan(p, resident_wgs<bf::k_apply_bf<D, 2>>(bf::kApplyThreads), 2);
+                bf::k_apply_bf<D, 2><<<dim3((unsigned)(2 * pk.nseg * pk.BH)),
                                        dim3(bf::kApplyThreads), 0, s>>>(
                     v, k, static_cast<T *>(dK), static_cast<T *>(dV), nullptr, nullptr,
-                    ws + l.gtot, p.N, p.seg_len, (int)p.nseg, p.n0, p.ol);
-            else {
+                    ws + l.gtot, pk.N, pk.seg_len, (int)pk.nseg, pk.n0, pk.ol);
+            } else {
                 const Plan pk =
                     rows_plan(p, resident_wgs<nc::k_apply_nc<ST, D, 2>>(nc::kApplyThreads), 2);
                 nc::k_apply_nc<ST, D, 2><<<dim3((unsigned)(2 * pk.nseg * pk.BH)),
