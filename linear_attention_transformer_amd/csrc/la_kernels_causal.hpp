@@ -822,7 +822,6 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_bwd_kv_causal2(
     static_assert(D == 64 || D == 128, "two or four 32-column blocks");
     constexpr int NCB = D / 32, NW = 2 * NCB, NT = 64 * NW, KB = D / 8;
     constexpr int LDX = Kv2Lds<D>::LDX, RP = Kv2Lds<D>::RP, WP = Kv2Lds<D>::WP;
-    constexpr int TPW = NCB / 2;  // R tiles per wave
     __shared__ __attribute__((aligned(16))) Kv2Lds<D> L;
 
     const int64_t bh = blockIdx.x / nseg;
@@ -871,42 +870,36 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_bwd_kv_causal2(
         }
     };
 
-    // this wave's R tiles: tile u <-> R[32 ta .., 32 tb ..], accumulator
-    // element i of lane (j, h) at a = 32 ta + 8 (i / 4) + 4 h + i % 4, b = 32 tb + j
-    f16v racc[TPW];
-    auto tile_of = [&](int u, int &ta, int &tb) {
-        const int tau = w * TPW + u;
-        ta = tau / NCB;
-        tb = tau % NCB;
-    };
+    // dV waves: their D x 32 column slab of R as MFMA accumulators,
+    // sacc[t][i] <-> R[32 t + 8 (i / 4) + 4 h + i % 4][32 cb + j], which is
+    // also the A operand of R^T k at k-block kb, step r: sacc[kb / 4][4 (kb %
+    // 4) + r].  They add each chunk to it and publish it in LDS for the dK
+    // waves, which read R by rows.
+    f16v sacc[NCB];
     auto write_r = [&]() {
 #pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-            int ta, tb;
-            tile_of(u, ta, tb);
+        for (int t = 0; t < NCB; ++t)
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                L.rs[(32 * ta + 8 * (i / 4) + 4 * h + (i % 4)) * RP + 32 * tb + j] = racc[u][i];
-        }
+                L.rs[(32 * t + 8 * (i / 4) + 4 * h + (i % 4)) * RP + 32 * cb + j] = sacc[t][i];
     };
 
     const int64_t nrounds = (end - beg + kC - 1) / kC;
     const int64_t last = beg + (nrounds - 1) * kC;  // first row of the last chunk
     fetch_kv(last);
     fetch_qg(last);
+    if (!isk) {
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-        int ta, tb;
-        tile_of(u, ta, tb);
+        for (int t = 0; t < NCB; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            racc[u][i] = st[(32 * ta + 8 * (i / 4) + 4 * h + (i % 4)) * D + 32 * tb + j];
+            for (int i = 0; i < 16; ++i)
+                sacc[t][i] = st[(32 * t + 8 * (i / 4) + 4 * h + (i % 4)) * D + 32 * cb + j];
+        write_r();
     }
     for (int e = tid; e < D; e += NT) {
         L.vr[e] = st[D * D + e];
         L.vt[e] = st[D * D + D + e];
     }
-    write_r();
     stage_kv();
     stage_qg();
     drain_loads();
@@ -914,97 +907,101 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_bwd_kv_causal2(
     fetch_qg(last - kC);
     __syncthreads();
 
-    for (int64_t round = 0; round < nrounds; ++round) {
-        const int64_t t0 = last - round * kC;
-        // (1) the suffix state applied to the chunk's rows: dK^T block
-        // C[a][t] = sum_b R[a][b] V[t][b] (R by rows) or dV^T block
-        // C[b][t] = sum_a R[a][b] K[t][a] (R by columns); k-slot of lane
-        // (j, h) at k-block kb, step r: column 8 kb + 4 h + r
-        f16v acc = zero16();
-        if (isk) {
-            const float *xt = &L.vs[j * LDX + 4 * h];
-            const float *rt = &L.rs[(32 * cb + j) * RP + 4 * h];
+    // one loop per role (a scalar branch: each role's registers are
+    // allocated apart), both through the same three barriers per chunk
+    auto walk = [&](auto role) {
+        constexpr bool DK = decltype(role)::value;
+        for (int64_t round = 0; round < nrounds; ++round) {
+            const int64_t t0 = last - round * kC;
+            // (1) the suffix state applied to the chunk's rows: dK^T block
+            // C[a][t] = sum_b R[a][b] V[t][b] (R by rows, from LDS) or dV^T
+            // block C[b][t] = sum_a R[a][b] K[t][a] (the wave's own slab);
+            // k-slot of lane (j, h) at k-block kb, step r: column 8 kb + 4 h + r
+            f16v acc = zero16();
+            if constexpr (DK) {
+                const float *xt = &L.vs[j * LDX + 4 * h];
+                const float *rt = &L.rs[(32 * cb + j) * RP + 4 * h];
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const f4 x = *reinterpret_cast<const f4 *>(xt + 8 * kb);
-                const f4 a = *reinterpret_cast<const f4 *>(rt + 8 * kb);
+                for (int kb = 0; kb < KB; ++kb) {
+                    const f4 x = *reinterpret_cast<const f4 *>(xt + 8 * kb);
+                    const f4 a = *reinterpret_cast<const f4 *>(rt + 8 * kb);
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc = mma32(a[r], x[r], acc);
-            }
-        } else {
-            const float *xt = &L.ks[j * LDX + 4 * h];
-            const float *rt = &L.rs[(4 * h) * RP + 32 * cb + j];
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const f4 x = *reinterpret_cast<const f4 *>(xt + 8 * kb);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc = mma32(rt[(8 * kb + r) * RP], x[r], acc);
-            }
-        }
-        // (2) Q_c K_c^T and G_c V_c^T, tiles over all waves
-        tiles8_xyT<D, NW>(L.qs, L.ks, L.gs, L.vs, L.wx, L.gx, w, lane);
-        __syncthreads();  // B1
-        stage_kv();  // K, V are read only before B1
-        fetch_kv(t0 - 2 * kC);
-        // (3) in-chunk terms over rows ir = 2 kk + h >= j:
-        // dK^T[a][j] += sum_i Q[i][a] (a_i.v_j - c_i), dV^T[b][j] += sum_i A[i][b] (1 + q_i.k_j)
-        float vc = 0.f;
-        if (isk) {
-#pragma unroll
-            for (int kk = 0; kk < kC / 2; ++kk) {
-                const int ir = 2 * kk + h;
-                const float ci = L.cs[ir];
-                const float pm = (ir >= j) ? L.gx[ir * WP + j] * L.is[ir] - ci : 0.f;
-                const float qb = L.qs[ir * LDX + 32 * cb + j];
-                acc = mma32(qb, pm, acc);
-                vc += ci * qb;
-            }
-        } else {
-#pragma unroll
-            for (int kk = 0; kk < kC / 2; ++kk) {
-                const int ir = 2 * kk + h;
-                const float wm = (ir >= j) ? 1.f + L.wx[ir * WP + j] : 0.f;
-                const float ab = L.gs[ir * LDX + 32 * cb + j] * L.is[ir];
-                acc = mma32(ab, wm, acc);
-                vc += ab;
-            }
-        }
-        vc = swap32_sum(vc);
-        // (4) rows of dK (- r) or dV (+ t) with the vectors of the rows after the chunk
-        {
-            const float sg = isk ? -1.f : 1.f;
-            const float *vec = isk ? L.vr : L.vt;
-            if (t0 + j < end)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const f4 v = *reinterpret_cast<const f4 *>(&vec[32 * cb + 8 * q + 4 * h]);
-                    io::store4(oh + (t0 + j) * ol.sn + 32 * cb + 8 * q + 4 * h,
-                               f4{acc[4 * q] + sg * v[0], acc[4 * q + 1] + sg * v[1],
-                                  acc[4 * q + 2] + sg * v[2], acc[4 * q + 3] + sg * v[3]});
+                    for (int r = 0; r < 4; ++r)
+                        acc = mma32(a[r], x[r], acc);
                 }
-        }
-        // (5) the suffix state takes the chunk in: R += Q_c^T A_c, tile by tile
+                // (2) Q_c K_c^T and G_c V_c^T, tiles over the dK waves (the dV
+                // waves update R after B1)
+                tiles8_xyT<D, NCB>(L.qs, L.ks, L.gs, L.vs, L.wx, L.gx, cb, lane);
+            } else {
+                const float *xt = &L.ks[j * LDX + 4 * h];
 #pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-            int ta, tb;
-            tile_of(u, ta, tb);
+                for (int kb = 0; kb < KB; ++kb) {
+                    const f4 x = *reinterpret_cast<const f4 *>(xt + 8 * kb);
 #pragma unroll
-            for (int kk = 0; kk < kC / 2; ++kk) {
-                const int ir = 2 * kk + h;
-                racc[u] = mma32(L.qs[ir * LDX + 32 * ta + j],
-                                L.gs[ir * LDX + 32 * tb + j] * L.is[ir], racc[u]);
+                    for (int r = 0; r < 4; ++r)
+                        acc = mma32(sacc[kb / 4][4 * (kb % 4) + r], x[r], acc);
+                }
             }
+            __syncthreads();  // B1
+            stage_kv();  // K, V are read only before B1
+            fetch_kv(t0 - 2 * kC);
+            // (3) in-chunk terms over rows ir = 2 kk + h >= j: dK^T[a][j] +=
+            // sum_i Q[i][a] (a_i.v_j - c_i), dV^T[b][j] += sum_i A[i][b] (1 + q_i.k_j)
+            float vc = 0.f;
+            if constexpr (DK) {
+#pragma unroll
+                for (int kk = 0; kk < kC / 2; ++kk) {
+                    const int ir = 2 * kk + h;
+                    const float ci = L.cs[ir];
+                    const float pm = (ir >= j) ? L.gx[ir * WP + j] * L.is[ir] - ci : 0.f;
+                    const float qb = L.qs[ir * LDX + 32 * cb + j];
+                    acc = mma32(qb, pm, acc);
+                    vc += ci * qb;
+                }
+            } else {
+                // and the slab of R takes the chunk in: R[a][32 cb ..] += Q_c^T A_c
+#pragma unroll
+                for (int kk = 0; kk < kC / 2; ++kk) {
+                    const int ir = 2 * kk + h;
+                    const float wm = (ir >= j) ? 1.f + L.wx[ir * WP + j] : 0.f;
+                    const float ab = L.gs[ir * LDX + 32 * cb + j] * L.is[ir];
+                    acc = mma32(ab, wm, acc);
+#pragma unroll
+                    for (int t = 0; t < NCB; ++t)
+                        sacc[t] = mma32(L.qs[ir * LDX + 32 * t + j], ab, sacc[t]);
+                    vc += ab;
+                }
+            }
+            vc = swap32_sum(vc);
+            // (4) rows of dK (- r) or dV (+ t) with the vectors of the rows after the chunk
+            {
+                constexpr float sg = DK ? -1.f : 1.f;
+                const float *vec = DK ? L.vr : L.vt;
+                if (t0 + j < end)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f4 v = *reinterpret_cast<const f4 *>(&vec[32 * cb + 8 * q + 4 * h]);
+                        io::store4(oh + (t0 + j) * ol.sn + 32 * cb + 8 * q + 4 * h,
+                                   f4{acc[4 * q] + sg * v[0], acc[4 * q + 1] + sg * v[1],
+                                      acc[4 * q + 2] + sg * v[2], acc[4 * q + 3] + sg * v[3]});
+                    }
+            }
+            // (5) the dV waves publish the updated R (every read of R for this
+            // chunk was before B1)
+            if constexpr (!DK)
+                write_r();
+            __syncthreads();  // B2
+            if (h == 0)
+                (DK ? L.vr : L.vt)[32 * cb + j] += vc;
+            stage_qg();
+            fetch_qg(t0 - 2 * kC);
+            __syncthreads();  // B3
         }
-        write_r();  // every read of R for this chunk was before B1
-        __syncthreads();  // B2
-        if (h == 0)
-            (isk ? L.vr : L.vt)[32 * cb + j] += vc;
-        stage_qg();
-        fetch_qg(t0 - 2 * kC);
-        __syncthreads();  // B3
-    }
+    };
+    if (isk)
+        walk(std::true_type{});
+    else
+        walk(std::false_type{});
 }
 
 }  // namespace cz
