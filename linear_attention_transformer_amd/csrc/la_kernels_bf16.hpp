@@ -1138,10 +1138,51 @@ __device__ __forceinline__ void full_bf(const uint16_t *xs, const uint16_t *ys, 
         sh[(8 * (e / 4) + 4 * h + (e % 4)) * WP + j] = a[e];
 }
 
+constexpr int kWP = kCc + 8;  // bf16 pitch of a [row][key] plane of a chunk
+
+// W = M o (1 + Q_c K_c^T) of a chunk, quarter qd (rows 16 (qd / 2) ..,
+// keys 16 (qd % 2) ..), as hi / lo bf16 planes [row][key] (pitch kWP) and
+// its row sums over the quarter's keys (rsx[(qd % 2) kCc + row]).  The
+// quarter is one product K_blk Q_blk^T on v_mfma_f32_16x16x32_bf16 (lane l
+// supplies key / row l % 16 and columns 8 (l / 16) .. + 7 of each 32-column
+// step, and receives keys 4 (l / 16) + 0..3 of row l % 16); the quarter
+// above the diagonal is all zero and skips the product.
+template <int D>
+__device__ __forceinline__ void w_quarter(const uint16_t *qs, const uint16_t *ks, uint16_t *whi,
+                                          uint16_t *wlo, float *rsx, int qd, int lane)
+{
+    constexpr int LDX = D + 8;
+    const int rb0 = 16 * (qd >> 1), kb0 = 16 * (qd & 1);
+    const int r = lane & 15, g = lane >> 4;
+    f4 t = {0.f, 0.f, 0.f, 0.f};
+    if (kb0 <= rb0) {
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) {
+            const bf8 a = *reinterpret_cast<const bf8 *>(&ks[(kb0 + r) * LDX + 32 * s + 8 * g]);
+            const bf8 b = *reinterpret_cast<const bf8 *>(&qs[(rb0 + r) * LDX + 32 * s + 8 * g]);
+            t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, t, 0, 0, 0);
+        }
+    }
+    const int row = rb0 + r, k0 = kb0 + 4 * g;
+    float w[4], sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        w[i] = (k0 + i <= row) ? 1.f + t[i] : 0.f;
+        sum += w[i];
+    }
+    uint2 hi, lo;
+    split4(w[0], w[1], w[2], w[3], hi, lo);
+    *reinterpret_cast<uint2 *>(&whi[row * kWP + k0]) = hi;
+    *reinterpret_cast<uint2 *>(&wlo[row * kWP + k0]) = lo;
+    sum = swap32_sum(swap16_sum(sum));
+    if (g == 0)
+        rsx[(qd & 1) * kCc + row] = sum;
+}
+
 // Forward (as cz::k_fwd_causal): per chunk (1) acc = S^T-block . Q_c^T and
-// q.z; (2) share of Q_c K_c^T; barrier; (3) acc += V_c-block^T . W^T with W
-// masked and the constant added (its row sums go to den), st += K_c^T .
-// V_c-block; (4) normalised rows.
+// q.z; (2) the waves' quarters of W = M o (1 + Q_c K_c^T) as hi / lo planes,
+// with their row sums; barrier; (3) acc += V_c-block^T . W^T (the row sums
+// go to den), st += K_c^T . V_c-block; (4) normalised rows.
 template <int D>
 __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal_bf(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
@@ -1150,12 +1191,14 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal_bf(
 {
     typedef nc::IO<StBF16> io;
     static_assert(D >= 32 && D <= 128, "32-column blocks, state in registers");
-    constexpr int NCB = D / 32, NT = 64 * NCB, LDX = D + 8, WP = kCc + 1;
+    constexpr int NCB = D / 32, NT = 64 * NCB, LDX = D + 8;
     __shared__ __attribute__((aligned(16))) uint16_t qs[kCc * LDX];
     __shared__ __attribute__((aligned(16))) uint16_t ks[kCc * LDX];
     __shared__ __attribute__((aligned(16))) uint16_t kT[D * kRT];
     __shared__ __attribute__((aligned(16))) uint16_t vT[D * kRT];
-    __shared__ float wx[kCc * WP];  // Q_c K_c^T
+    __shared__ __attribute__((aligned(16))) uint16_t whi[kCc * kWP];  // W, [row][key]
+    __shared__ __attribute__((aligned(16))) uint16_t wlo[kCc * kWP];
+    __shared__ float rsx[2 * kCc];   // row sums of W by key half
     __shared__ float qzx[NCB][kCc];  // q.z over each wave's 32 columns
     __shared__ __attribute__((aligned(16))) float vz[D];
     __shared__ __attribute__((aligned(16))) float vu[D];
@@ -1240,9 +1283,9 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal_bf(
                     __builtin_amdgcn_sched_barrier(0);
                 }
         }
-        // (2) Q_c K_c^T (one wave)
-        if (cb == 0)
-            full_bf<D>(qs, ks, wx, j, h);
+        // (2) this wave's quarters of W
+        for (int qd = cb; qd < 4; qd += NCB)
+            w_quarter<D>(qs, ks, whi, wlo, rsx, qd, lane);
         __syncthreads();  // B1
         if (more)
             rq.stage_nat(qs, tid);  // Q is read only before B1
@@ -1251,22 +1294,15 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal_bf(
             rv.fetch(vh, t0 + kCc, end, tid);
         }
         // (3) in-chunk term over key rows 16 kk + 8 h .. and the state update
-        float rs = 0.f, zc = 0.f, uc = 0.f;
+        float zc = 0.f, uc = 0.f;
 #pragma unroll
         for (int kk = 0; kk < kCc / 16; ++kk) {
-            // W[j][16 kk + 8 h + s], masked, + 1
-            float wm[8];
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const int jr = 16 * kk + 8 * h + s;
-                wm[s] = (jr <= j) ? 1.f + wx[j * WP + jr] : 0.f;
-                rs += wm[s];
-            }
-            bf8 whi, wlo;
-            split8v(wm, whi, wlo);
+            // W[j][16 kk + 8 h ..]
+            const bf8 wh = *reinterpret_cast<const bf8 *>(&whi[j * kWP + 16 * kk + 8 * h]);
+            const bf8 wl = *reinterpret_cast<const bf8 *>(&wlo[j * kWP + 16 * kk + 8 * h]);
             const bf8 vcol = col_at(vT, 32 * cb + j, kk, h);  // V[16kk+8h..][32cb+j]
-            acc = mma16(vcol, whi, acc);
-            acc = mma16(vcol, wlo, acc);
+            acc = mma16(vcol, wh, acc);
+            acc = mma16(vcol, wl, acc);
 #pragma unroll
             for (int t = 0; t < NCB; ++t) {
                 const bf8 kcol = col_at(kT, 32 * t + j, kk, h);
@@ -1277,9 +1313,9 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal_bf(
             uc = sum8(vcol, uc);
             __builtin_amdgcn_sched_barrier(0);
         }
-        rs = swap32_sum(rs);
         zc = swap32_sum(zc);
         uc = swap32_sum(uc);
+        const float rs = rsx[j] + rsx[kCc + j];
         float qz = 0.f;
 #pragma unroll
         for (int c2 = 0; c2 < NCB; ++c2)
@@ -1752,7 +1788,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_kv_causal_bf(
 // (sum over the rows after the chunk of q_i a_i^T) is kept once: every wave
 // owns NCB/2 of its 32 x 32 tiles as fp32 MFMA accumulators, updates them by
 // the chunk (R += Q_c^T A_c) and writes them after each chunk as hi and lo
-// bf16 planes in LDS, laid out [b][a] (column-major R), from which both
+// bf16 planes in LDS, laid out [b][a] (column-major R, columns swizzled by
+// rsw), from which both
 // products read their operand: dK = V_c R^T - r (8 consecutive b of a row of
 // R, gathered by the LDS transpose read) and dV = K_c R + t (contiguous runs
 // of 8 a).  The chunk's rows of Q, K, V and A = dO / den (hi and lo) are
@@ -1762,6 +1799,35 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_kv_causal_bf(
 // read 8 consecutive tokens of a column with two ds_read_b64_tr_b16.  The
 // column sums r = sum c_i q_i and t = sum a_i run in registers of D threads.
 
+// Column of element (row r, column c) of an R plane: 4-element granule c / 4
+// XOR sig(r), sig(r) = 4 (r & 3) + 2 ((r >> 2) & 1).  With rows a multiple of
+// 32 banks apart, the 2-dword bank slot of a granule is its index mod 16, and
+//   - the transpose read (16 lanes: rows r0 + 0..3, granules 4m + 0..3, r0 a
+//     multiple of 4) hits 4 ((m ^ e) & 3) + (f ^ 2 s): 16 distinct slots;
+//   - a 16-byte row read by 8 lanes (rows j = 0..7, one even granule pair)
+//     hits 8 distinct even slots and their odd neighbours (sig is even, so
+//     a pair stays whole and in order);
+//   - an 8-byte write by 16 lanes (rows j = 0..15, one granule) hits 8
+//     slots, twice each (4 times without the swizzle at pitch D + 16).
+__device__ __forceinline__ int rsw(int r, int c)
+{
+    return c ^ (((r & 3) << 4) | ((r & 4) << 1));
+}
+
+// col8 on an R plane (swizzled columns)
+__device__ __forceinline__ bf8 col8_rsw(const uint16_t *tile, int pitch, int rb, int cb0,
+                                        int lane)
+{
+    const int g = lane >> 4, p = lane & 15;
+    const int ra = rb + 8 * (g >> 1) + (p >> 2), c = cb0 + 16 * (g & 1) + 4 * (p & 3);
+    typedef __attribute__((address_space(3))) v4s *lp;
+    const v4s x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(tile + ra * pitch + rsw(ra, c)));
+    const v4s y = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lp)(tile + (ra + 4) * pitch + rsw(ra + 4, c)));
+    const uint2 ux = __builtin_bit_cast(uint2, x), uy = __builtin_bit_cast(uint2, y);
+    return __builtin_bit_cast(bf8, uint4{ux.x, ux.y, uy.x, uy.y});
+}
+
 template <int D>
 struct KvBf2Lds {
     // Row pitches (bf16): D + 8 (16 mod 128 bytes) for the rows read whole
@@ -1769,9 +1835,12 @@ struct KvBf2Lds {
     // for the planes read mostly with the transpose read (Q, a and R:
     // conflict-free 16-lane transpose reads).  D = 64 keeps D + 8 throughout:
     // the wider planes would cost it a third resident workgroup per CU.
+    // The R planes are written by columns as well (8 bytes per lane, one row
+    // per lane), so they take pitch D (a multiple of 128 bytes) and an XOR
+    // swizzle instead (rsw below).
     static constexpr int LDX = D + 8;
     static constexpr int LDT = D == 64 ? D + 8 : D + 16;
-    static constexpr int RP = LDT;       // R planes: element (a, b) at b * RP + a
+    static constexpr int RP = D;         // R planes: element (a, b) at b * RP + rsw(b, a)
     static constexpr int PP = kCc + 8;   // P, W planes: element (i, j) at j * PP + i
     uint16_t q[kCc * LDT], k[kCc * LDX], v[kCc * LDX], ahi[kCc * LDT], alo[kCc * LDT];
     uint16_t rhi[D * RP], rlo[D * RP];
@@ -1865,7 +1934,7 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_bwd_kv_causal_bf2(
                 uint2 hi, lo;
                 split4(racc[u][4 * q], racc[u][4 * q + 1], racc[u][4 * q + 2], racc[u][4 * q + 3],
                        hi, lo);
-                const int o = (32 * tb + j) * RP + 32 * ta + 8 * q + 4 * h;
+                const int o = (32 * tb + j) * RP + rsw(j, 32 * ta + 8 * q + 4 * h);
                 *reinterpret_cast<uint2 *>(&L.rhi[o]) = hi;
                 *reinterpret_cast<uint2 *>(&L.rlo[o]) = lo;
             }
@@ -1916,20 +1985,23 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_bwd_kv_causal_bf2(
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const bf8 x = row8(L.v, LDX, 0, 16 * ks, j, h);
-                acc = mma16(col8(L.rhi, RP, 16 * ks, 32 * cb, lane), x, acc);
-                acc = mma16(col8(L.rlo, RP, 16 * ks, 32 * cb, lane), x, acc);
+                acc = mma16(col8_rsw(L.rhi, RP, 16 * ks, 32 * cb, lane), x, acc);
+                acc = mma16(col8_rsw(L.rlo, RP, 16 * ks, 32 * cb, lane), x, acc);
             }
         } else {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const bf8 x = row8(L.k, LDX, 0, 16 * ks, j, h);
-                acc = mma16(row8(L.rhi, RP, 32 * cb, 16 * ks, j, h), x, acc);
-                acc = mma16(row8(L.rlo, RP, 32 * cb, 16 * ks, j, h), x, acc);
+                const int o = (32 * cb + j) * RP + rsw(j, 16 * ks + 8 * h);
+                acc = mma16(*reinterpret_cast<const bf8 *>(&L.rhi[o]), x, acc);
+                acc = mma16(*reinterpret_cast<const bf8 *>(&L.rlo[o]), x, acc);
             }
         }
         // the in-chunk blocks, [j][i] planes: P = A V^T - c (wave 0) and
-        // W = 1 + Q K^T (wave NCB), masked to i >= j
-        if (w == 0 || w == NCB) {
+        // W = 1 + Q K^T (wave 1), masked to i >= j.  Waves w and w + 4 share
+        // a SIMD, and the column-sum waves are the last two: the extra
+        // products go to the first two SIMDs, one each.
+        if (w < 2) {
             f16v pa = zero16();
             if (w == 0) {
 #pragma unroll

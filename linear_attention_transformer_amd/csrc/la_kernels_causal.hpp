@@ -755,15 +755,16 @@ __global__ __launch_bounds__(threads<D>()) __attribute__((amdgpu_waves_per_eu(2)
 // The recurrences of kv_pass, with dK and dV of a segment formed by one
 // workgroup of 2 NCB waves that holds the suffix state R once, so that R is
 // updated once per chunk instead of once per output:
-//   - R (fp32) lives in LDS as R[a][b] (a: column of Q, b: column of a);
-//     each wave keeps NCB / 2 of its 32 x 32 tiles as MFMA accumulators,
-//     adds the chunk (R += Q_c^T A_c) and writes them back after the
-//     chunk's last read of R;
+//   - waves NCB .. 2 NCB - 1 form dV columns 32 (w - NCB) .. (dv_j = R^T k_j
+//     + t + in-chunk terms); each keeps its D x 32 column slab of R as MFMA
+//     accumulators (the A operand of R^T k), adds the chunk to it in place
+//     (R += Q_c^T A_c) and, after the chunk's last read of R, publishes it in
+//     LDS as R[a][b] (a: column of Q, b: column of a);
 //   - waves 0 .. NCB - 1 form dK columns 32 w .. (dk_j = R v_j - r + in-chunk
-//     terms, R read by rows), waves NCB .. 2 NCB - 1 form dV columns
-//     (dv_j = R^T k_j + t + in-chunk terms, R read by columns);
-//   - the products Q_c K_c^T and G_c V_c^T are split into 16 x 16 tiles over
-//     all waves.
+//     terms), reading R by rows from LDS, and the products Q_c K_c^T and
+//     G_c V_c^T as 16 x 16 tiles;
+//   - one loop per role, behind a scalar branch on the wave index, so that
+//     each role's registers are allocated apart.
 // Three barriers per chunk, as in kv_pass: after the product tiles (B1),
 // after the chunk's last reads (B2), after the next chunk is staged (B3).
 // K and V are read only before B1 and are restaged right after it.
@@ -776,38 +777,6 @@ struct Kv2Lds {
     float cs[kC], is[kC];            // c_i, 1 / den_i of the chunk's rows
     float vr[D], vt[D];              // r, t of the rows after the chunk
 };
-
-// Q_c K_c^T into wx and G_c V_c^T into gx as eight 16 x 16 tiles spread over
-// NW waves (as tiles_xyT; a wave with a single tile runs its k-steps as two
-// chains and adds them at the end)
-template <int D, int NW>
-__device__ __forceinline__ void tiles8_xyT(const float *qs, const float *ks, const float *gs,
-                                           const float *vs, float *wx, float *gx, int w, int lane)
-{
-    constexpr int LDX = D + 4, WP = kC + 1, PER = 8 / NW, NST = D / 16;
-    static_assert(PER * NW == 8, "tiles per wave");
-    const int r = lane & 15, g = lane >> 4;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-        const int tt = w * PER + k;  // 0..3: Q K^T tiles, 4..7: G V^T
-        const int ti = (tt >> 1) & 1, tj = tt & 1;
-        const float *xa = (tt < 4 ? qs : gs) + (16 * ti + r) * LDX + 4 * g;
-        const float *ya = (tt < 4 ? ks : vs) + (16 * tj + r) * LDX + 4 * g;
-        f4 a[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int st = 0; st < NST; ++st) {
-            const f4 x = *reinterpret_cast<const f4 *>(xa + 16 * st);
-            const f4 y = *reinterpret_cast<const f4 *>(ya + 16 * st);
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-                a[st & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[c], y[c], a[st & 1], 0, 0, 0);
-        }
-        float *dst = (tt < 4 ? wx : gx) + (16 * ti + 4 * g) * WP + 16 * tj + r;
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-            dst[v * WP] = a[0][v] + a[1][v];
-    }
-}
 
 template <class ST, int D>
 __global__ __launch_bounds__(128 * (D / 32)) void k_bwd_kv_causal2(
@@ -931,7 +900,7 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_bwd_kv_causal2(
                 }
                 // (2) Q_c K_c^T and G_c V_c^T, tiles over the dK waves (the dV
                 // waves update R after B1)
-                tiles8_xyT<D, NCB>(L.qs, L.ks, L.gs, L.vs, L.wx, L.gx, cb, lane);
+                tiles_xyT<D>(L.qs, L.ks, L.gs, L.vs, L.wx, L.gx, cb, lane);
             } else {
                 const float *xt = &L.ks[j * LDX + 4 * h];
 #pragma unroll
