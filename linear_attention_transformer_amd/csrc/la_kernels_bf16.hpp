@@ -1304,12 +1304,11 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal_bf(
             acc = mma16(vcol, wh, acc);
             acc = mma16(vcol, wl, acc);
 #pragma unroll
-            for (int t = 0; t < NCB; ++t) {
-                const bf8 kcol = col_at(kT, 32 * t + j, kk, h);
-                sacc[t] = mma16(kcol, vcol, sacc[t]);
-                if (t == cb)
-                    zc = sum8(kcol, zc);
-            }
+            for (int t = 0; t < NCB; ++t)
+                sacc[t] = mma16(col_at(kT, 32 * t + j, kk, h), vcol, sacc[t]);
+            // (this wave's K column read again: selecting it among the
+            // unrolled operands would cost a sum per block)
+            zc = sum8(col_at(kT, 32 * cb + j, kk, h), zc);
             uc = sum8(vcol, uc);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -1352,11 +1351,60 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal_bf(
         store_pending(q);
 }
 
+// The dQ pass's in-chunk blocks, quarter qd (as w_quarter): W = 1 + Q_c K_c^T
+// and GV = G_c V_c^T under the mask M, the masked GV as hi / lo planes
+// [row][key], and the row sums over the quarter's keys of W (rsx) and of
+// W o GV (cwx), both at [(qd % 2) kCc + row].
+template <int D>
+__device__ __forceinline__ void wg_quarter(const uint16_t *qs, const uint16_t *ks,
+                                           const uint16_t *gs, const uint16_t *vs, uint16_t *ghi,
+                                           uint16_t *glo, float *rsx, float *cwx, int qd,
+                                           int lane)
+{
+    constexpr int LDX = D + 8;
+    const int rb0 = 16 * (qd >> 1), kb0 = 16 * (qd & 1);
+    const int r = lane & 15, g = lane >> 4;
+    f4 tw = {0.f, 0.f, 0.f, 0.f}, tg = {0.f, 0.f, 0.f, 0.f};
+    if (kb0 <= rb0) {
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) {
+            const int ok = (kb0 + r) * LDX + 32 * s + 8 * g, orw = (rb0 + r) * LDX + 32 * s + 8 * g;
+            tw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf8 *>(&ks[ok]),
+                                                         *reinterpret_cast<const bf8 *>(&qs[orw]),
+                                                         tw, 0, 0, 0);
+            tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf8 *>(&vs[ok]),
+                                                         *reinterpret_cast<const bf8 *>(&gs[orw]),
+                                                         tg, 0, 0, 0);
+        }
+    }
+    const int row = rb0 + r, k0 = kb0 + 4 * g;
+    float gm[4], rs = 0.f, cw = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bool m = k0 + i <= row;
+        const float w = m ? 1.f + tw[i] : 0.f;
+        gm[i] = m ? tg[i] : 0.f;
+        rs += w;
+        cw += w * gm[i];
+    }
+    uint2 hi, lo;
+    split4(gm[0], gm[1], gm[2], gm[3], hi, lo);
+    *reinterpret_cast<uint2 *>(&ghi[row * kWP + k0]) = hi;
+    *reinterpret_cast<uint2 *>(&glo[row * kWP + k0]) = lo;
+    rs = swap32_sum(swap16_sum(rs));
+    cw = swap32_sum(swap16_sum(cw));
+    if (g == 0) {
+        rsx[(qd & 1) * kCc + row] = rs;
+        cwx[(qd & 1) * kCc + row] = cw;
+    }
+}
+
 // dQ (as cz::k_bwd_q_causal): st[t] = S^T[32t.., 32cb..]; per chunk
-// (1) acc = S-block . G_c^T with g.u and q.z; (2) shares of Q_c K_c^T and
-// G_c V_c^T, q.y over the wave's columns; barrier; (3) den, c, then acc +=
-// K_c-block^T . P^T (P = GV - c den, masked) and st += V_c^T . K_c-block;
-// (4) dq rows and cbuf = (c, 1/den).
+// (1) acc = S-block . G_c^T with g.u and q.z; (2) the waves' quarters of the
+// in-chunk blocks (wg_quarter), q.y over the wave's columns; barrier; (3)
+// den, c, then acc += K_c-block^T . P^T with P = M o GV - c den M, formed as
+// two products, K^T (M o GV)^T - c den K^T M^T (M exact in bf16), and st +=
+// V_c^T . K_c-block; (4) dq rows and cbuf = (c, 1/den).
 template <int D>
 __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
@@ -1366,15 +1414,17 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
 {
     typedef nc::IO<StBF16> io;
     static_assert(D >= 32 && D <= 128, "32-column blocks, state in registers");
-    constexpr int NCB = D / 32, NT = 64 * NCB, LDX = D + 8, WP = kCc + 1;
+    constexpr int NCB = D / 32, NT = 64 * NCB, LDX = D + 8;
     __shared__ __attribute__((aligned(16))) uint16_t qs[kCc * LDX];
     __shared__ __attribute__((aligned(16))) uint16_t gs[kCc * LDX];
     __shared__ __attribute__((aligned(16))) uint16_t ks[kCc * LDX];
     __shared__ __attribute__((aligned(16))) uint16_t vs[kCc * LDX];
     __shared__ __attribute__((aligned(16))) uint16_t kT[D * kRT];
     __shared__ __attribute__((aligned(16))) uint16_t vT[D * kRT];
-    __shared__ float wx[kCc * WP];       // Q_c K_c^T
-    __shared__ float gx[kCc * WP];       // G_c V_c^T
+    __shared__ __attribute__((aligned(16))) uint16_t ghi[kCc * kWP];  // M o GV, [row][key]
+    __shared__ __attribute__((aligned(16))) uint16_t glo[kCc * kWP];
+    __shared__ float rsx[2 * kCc];       // row sums of W by key half
+    __shared__ float cwx[2 * kCc];       // row sums of W o GV by key half
     __shared__ float xq[NCB][kCc];       // shares of q_i.y_i + g_i.u
     __shared__ float xz[NCB][kCc];       // shares of q_i.z
     __shared__ __attribute__((aligned(16))) float vz[D];
@@ -1471,12 +1521,10 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
                     __builtin_amdgcn_sched_barrier(0);
                 }
         }
-        // (2) Q_c K_c^T and G_c V_c^T (one wave each), q.y over this wave's
-        // columns
-        if (cb == 0)
-            full_bf<D>(qs, ks, wx, j, h);
-        if (cb == NCB - 1)
-            full_bf<D>(gs, vs, gx, j, h);
+        // (2) this wave's quarters of the in-chunk blocks, q.y over this
+        // wave's columns
+        for (int qd = cb; qd < 4; qd += NCB)
+            wg_quarter<D>(qs, ks, gs, vs, ghi, glo, rsx, cwx, qd, lane);
         {
             const uint16_t *qr = &qs[j * LDX + 32 * cb + 4 * h];
             float pq = 0.f;
@@ -1505,22 +1553,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
         }
         // (3) den and c of row j, then the in-chunk term and the update over
         // key rows 16 kk + 8 h + s
-        float gvk[kCc / 16][8];
-        float rs = 0.f, cw = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < kCc / 16; ++kk)
-#pragma unroll
-            for (int s2 = 0; s2 < 8; ++s2) {
-                const int jr = 16 * kk + 8 * h + s2;
-                const float w = wx[j * WP + jr], gv = gx[j * WP + jr];
-                const bool m = jr <= j;
-                const float wm = m ? 1.f + w : 0.f;
-                rs += wm;
-                cw += wm * gv;
-                gvk[kk][s2] = m ? gv : 0.f;
-            }
-        rs = swap32_sum(rs);
-        cw = swap32_sum(cw);
+        const float rs = rsx[j] + rsx[kCc + j], cw = cwx[j] + cwx[kCc + j];
         float qyu = 0.f, qzs = 0.f;  // q.y + g.u and q.z over all columns
 #pragma unroll
         for (int pp = 0; pp < NCB; ++pp) {
@@ -1532,26 +1565,23 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
         const float c = (qyu + cw) * inv * inv;
         const float cden = c * den;
         float zc = 0.f, uc = 0.f;
+        f16v kcum = zero16();  // K^T M^T: sums of K over the keys up to row j
 #pragma unroll
         for (int kk = 0; kk < kCc / 16; ++kk) {
-            bf8 phi, plo;
-            float pm[8];
+            const bf8 gh = *reinterpret_cast<const bf8 *>(&ghi[j * kWP + 16 * kk + 8 * h]);
+            const bf8 gl = *reinterpret_cast<const bf8 *>(&glo[j * kWP + 16 * kk + 8 * h]);
+            bf8 mk;
 #pragma unroll
-            for (int s2 = 0; s2 < 8; ++s2) {
-                const int jr = 16 * kk + 8 * h + s2;
-                pm[s2] = (jr <= j) ? gvk[kk][s2] - cden : 0.f;
-            }
-            split8v(pm, phi, plo);
+            for (int s2 = 0; s2 < 8; ++s2)
+                mk[s2] = (16 * kk + 8 * h + s2 <= j) ? (__bf16)1.f : (__bf16)0.f;
             const bf8 kcol = col_at(kT, 32 * cb + j, kk, h);  // K[16kk+8h..][32cb+j]
-            acc = mma16(kcol, phi, acc);
-            acc = mma16(kcol, plo, acc);
+            acc = mma16(kcol, gh, acc);
+            acc = mma16(kcol, gl, acc);
+            kcum = mma16(kcol, mk, kcum);
 #pragma unroll
-            for (int t = 0; t < NCB; ++t) {
-                const bf8 vcol = col_at(vT, 32 * t + j, kk, h);
-                sacc[t] = mma16(vcol, kcol, sacc[t]);
-                if (t == cb)
-                    uc = sum8(vcol, uc);
-            }
+            for (int t = 0; t < NCB; ++t)
+                sacc[t] = mma16(col_at(vT, 32 * t + j, kk, h), kcol, sacc[t]);
+            uc = sum8(col_at(vT, 32 * cb + j, kk, h), uc);  // (as in the forward)
             zc = sum8(kcol, zc);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -1561,8 +1591,11 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const f4 z = *reinterpret_cast<const f4 *>(&vz[32 * cb + 8 * q + 4 * h]);
-            pend[q] = f4{acc[4 * q] * inv - c * z[0], acc[4 * q + 1] * inv - c * z[1],
-                         acc[4 * q + 2] * inv - c * z[2], acc[4 * q + 3] * inv - c * z[3]};
+            f4 o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                o[r] = (acc[4 * q + r] - cden * kcum[4 * q + r]) * inv - c * z[r];
+            pend[q] = o;
         }
         prow = t0 + j;
         pok = prow < end;

@@ -297,12 +297,11 @@ __global__ __launch_bounds__(threads<D>()) void k_fwd_causal(
             rs += wm;
             acc = mma32(vb, wm, acc);
 #pragma unroll
-            for (int t = 0; t < NCB; ++t) {
-                const float kt = ks[jr * LDX + 32 * t + j];
-                sacc[t] = mma32(kt, vb, sacc[t]);
-                if (t == cb)
-                    zc += kt;
-            }
+            for (int t = 0; t < NCB; ++t)
+                sacc[t] = mma32(ks[jr * LDX + 32 * t + j], vb, sacc[t]);
+            // (this wave's K column read again: selecting it among the
+            // unrolled operands would cost a select per block)
+            zc += ks[jr * LDX + 32 * cb + j];
             uc += vb;
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -351,7 +350,7 @@ __global__ __launch_bounds__(threads<D>()) void k_fwd_causal(
 // cbuf[i] = (c_i, 1 / den_i) for the gradient record and the dK | dV pass.
 // The product runs over S's rows: st[t] = S^T[32t.., 32cb..].
 template <class ST, int D>
-__global__ __launch_bounds__(threads<D>()) void k_bwd_q_causal(
+__global__ __launch_bounds__(threads<D>()) __attribute__((amdgpu_waves_per_eu(2))) void k_bwd_q_causal(
     const typename ST::T *__restrict__ Q, const typename ST::T *__restrict__ K,
     const typename ST::T *__restrict__ V, const typename ST::T *__restrict__ G,
     typename ST::T *__restrict__ dQ, float *__restrict__ cbuf, const float *__restrict__ rec,
@@ -511,12 +510,9 @@ __global__ __launch_bounds__(threads<D>()) void k_bwd_q_causal(
             const float pm = (jr <= j) ? gvk[kk] - cden : 0.f;
             acc = mma32(kv, pm, acc);
 #pragma unroll
-            for (int t = 0; t < NCB; ++t) {
-                const float vt = vs[jr * LDX + 32 * t + j];
-                sacc[t] = mma32(vt, kv, sacc[t]);
-                if (t == cb)
-                    uc += vt;
-            }
+            for (int t = 0; t < NCB; ++t)
+                sacc[t] = mma32(vs[jr * LDX + 32 * t + j], kv, sacc[t]);
+            uc += vs[jr * LDX + 32 * cb + j];  // (as in the forward)
             zc += kv;
             __builtin_amdgcn_sched_barrier(0);
         }
