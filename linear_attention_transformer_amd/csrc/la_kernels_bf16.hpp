@@ -1827,8 +1827,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_kv_causal_bf(
 // R, gathered by the LDS transpose read) and dV = K_c R + t (contiguous runs
 // of 8 a).  The chunk's rows of Q, K, V and A = dO / den (hi and lo) are
 // staged once, as natural rows; the in-chunk blocks P = M o (A V^T - c) and
-// W = M o (1 + Q K^T) are formed by one wave each and stored [j][i] as hi /
-// lo planes.  Products over the chunk's tokens (R's update, P^T Q, W^T A)
+// W = M o (1 + Q K^T) are formed by 16 x 16 quarters over the waves and
+// stored [j][i] as hi / lo planes.  Products over the chunk's tokens (R's update, P^T Q, W^T A)
 // read 8 consecutive tokens of a column with two ds_read_b64_tr_b16.  The
 // column sums r = sum c_i q_i and t = sum a_i run in registers of D threads.
 
@@ -2030,41 +2030,47 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_bwd_kv_causal_bf2(
                 acc = mma16(*reinterpret_cast<const bf8 *>(&L.rlo[o]), x, acc);
             }
         }
-        // the in-chunk blocks, [j][i] planes: P = A V^T - c (wave 0) and
-        // W = 1 + Q K^T (wave 1), masked to i >= j.  Waves w and w + 4 share
-        // a SIMD, and the column-sum waves are the last two: the extra
-        // products go to the first two SIMDs, one each.
-        if (w < 2) {
-            f16v pa = zero16();
-            if (w == 0) {
+        // the in-chunk blocks, [j][i] planes: P = A V^T - c and W = 1 + Q K^T,
+        // masked to i >= j, by 16 x 16 quarters (i block 16 (qd / 2), j block
+        // 16 (qd % 2)) on v_mfma_f32_16x16x32_bf16: lane l supplies row l % 16
+        // of each block and columns 8 (l / 16) .. + 7 of a 32-column step, and
+        // receives i = 4 (l / 16) + 0..3 of j = l % 16.  Wave w forms quarter
+        // w % 4 of P (w < 4) or of W; with four waves, both.  The quarter
+        // above the diagonal is all zero and skips the product.
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const bf8 vj = row8(L.v, LDX, 0, 16 * ks, j, h);
-                    pa = mma16(row8(L.ahi, LDT, 0, 16 * ks, j, h), vj, pa);
-                    pa = mma16(row8(L.alo, LDT, 0, 16 * ks, j, h), vj, pa);
+        for (int pw = 0; pw < 2; ++pw) {
+            if (NW == 8 && pw != (w >> 2))
+                continue;
+            const int qd = w & 3, ib0 = 16 * (qd >> 1), jb0 = 16 * (qd & 1);
+            const int r16 = lane & 15, g4 = lane >> 4;
+            f4 t = {0.f, 0.f, 0.f, 0.f};
+            if (jb0 <= ib0) {
+#pragma unroll
+                for (int ks = 0; ks < D / 32; ++ks) {
+                    const int oi = (ib0 + r16) * LDT + 32 * ks + 8 * g4;
+                    const int oj = (jb0 + r16) * LDX + 32 * ks + 8 * g4;
+                    if (pw == 0) {
+                        const bf8 vj = *reinterpret_cast<const bf8 *>(&L.v[oj]);
+                        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            *reinterpret_cast<const bf8 *>(&L.ahi[oi]), vj, t, 0, 0, 0);
+                        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            *reinterpret_cast<const bf8 *>(&L.alo[oi]), vj, t, 0, 0, 0);
+                    } else {
+                        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            *reinterpret_cast<const bf8 *>(&L.q[oi]),
+                            *reinterpret_cast<const bf8 *>(&L.k[oj]), t, 0, 0, 0);
+                    }
                 }
-            } else {
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    pa = mma16(row8(L.q, LDT, 0, 16 * ks, j, h), row8(L.k, LDX, 0, 16 * ks, j, h),
-                               pa);
             }
-            uint16_t *ph = (w == 0) ? L.phi : L.whi;
-            uint16_t *pl = (w == 0) ? L.plo : L.wlo;
+            const int jj = jb0 + r16, i0 = ib0 + 4 * g4;
+            float x4[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float x4[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 8 * q + 4 * h + r;
-                    const float e = pa[4 * q + r];
-                    x4[r] = (i >= j) ? ((w == 0) ? e - L.cs[i] : 1.f + e) : 0.f;
-                }
-                uint2 hi, lo;
-                split4(x4[0], x4[1], x4[2], x4[3], hi, lo);
-                *reinterpret_cast<uint2 *>(&ph[j * PP + 8 * q + 4 * h]) = hi;
-                *reinterpret_cast<uint2 *>(&pl[j * PP + 8 * q + 4 * h]) = lo;
-            }
+            for (int r = 0; r < 4; ++r)
+                x4[r] = (i0 + r >= jj) ? ((pw == 0) ? t[r] - L.cs[i0 + r] : 1.f + t[r]) : 0.f;
+            uint2 hi, lo;
+            split4(x4[0], x4[1], x4[2], x4[3], hi, lo);
+            *reinterpret_cast<uint2 *>(&(pw == 0 ? L.phi : L.whi)[jj * PP + i0]) = hi;
+            *reinterpret_cast<uint2 *>(&(pw == 0 ? L.plo : L.wlo)[jj * PP + i0]) = lo;
         }
         // column sums of the chunk; the vectors of the rows after it go to
         // LDS for the epilogue
