@@ -1112,6 +1112,36 @@ __device__ __forceinline__ void stage_a_tr(const ChunkRows<D, NT> &rg, const Chu
     }
 }
 
+// One row's 32 output columns held by lanes (j, 0) and (j, 1) (lane h:
+// columns 8 q + 4 h + 0..3 in v[q]) stored as bf16 in two 16-byte pieces per
+// lane: a permlane32 swap per dword pair (q = 2 s, 2 s + 1) leaves lane h
+// with columns 16 s + 8 h .. + 7 (h = 0: its own q = 2 s and the partner's;
+// h = 1: the partner's q = 2 s + 1 and its own).  Every lane runs the swaps;
+// ok guards the stores.
+__device__ __forceinline__ void store_row32(uint16_t *p, const f4 *v, int h, bool ok)
+{
+    uint32_t w[4][2];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        w[q][0] = StBF16::narrow2(v[q][0], v[q][1]);
+        w[q][1] = StBF16::narrow2(v[q][2], v[q][3]);
+    }
+    uint32_t o[2][4];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const auto r = __builtin_amdgcn_permlane32_swap(w[2 * s2][e], w[2 * s2 + 1][e], false,
+                                                            false);
+            o[s2][e] = (uint32_t)r[0];
+            o[s2][2 + e] = (uint32_t)r[1];
+        }
+    if (ok) {
+        *reinterpret_cast<uint4 *>(p + 8 * h) = uint4{o[0][0], o[0][1], o[0][2], o[0][3]};
+        *reinterpret_cast<uint4 *>(p + 16 + 8 * h) = uint4{o[1][0], o[1][1], o[1][2], o[1][3]};
+    }
+}
+
 // 8 consecutive tokens (16 kk + 8 h ..) of column c of a transposed tile
 __device__ __forceinline__ bf8 col_at(const uint16_t *ldsT, int c, int kk, int h)
 {
@@ -1240,10 +1270,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal_bf(
     f4 pend[4];
     int64_t prow = 0;
     bool pok = false;
-    auto store_pending = [&](int q) {
-        if (pok)
-            io::store4(oh + prow * ol.sn + 32 * cb + 8 * q + 4 * h, pend[q]);
-    };
+    auto store_pending = [&]() { store_row32(oh + prow * ol.sn + 32 * cb, pend, h, pok); };
 
     for (int64_t round = 0; round < nrounds; ++round) {
         const int64_t t0 = beg + round * kCc;
@@ -1275,11 +1302,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal_bf(
                     split8(sacc[t], p, ahi, alo);
                     acc = mma16(ahi, x, acc);
                     acc = mma16(alo, x, acc);
-                    if (t == 0 && p == 0) {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            store_pending(q);
-                    }
+                    if (t == 0 && p == 0)
+                        store_pending();
                     __builtin_amdgcn_sched_barrier(0);
                 }
         }
@@ -1346,9 +1370,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_causal_bf(
         }
         __syncthreads();  // B3
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        store_pending(q);
+    store_pending();
 }
 
 // The dQ pass's in-chunk blocks, quarter qd (as w_quarter): W = 1 + Q_c K_c^T
@@ -1478,10 +1500,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
     f4 pend[4];
     int64_t prow = 0;
     bool pok = false;
-    auto store_pending = [&](int q) {
-        if (pok)
-            io::store4(oh + prow * ol.sn + 32 * cb + 8 * q + 4 * h, pend[q]);
-    };
+    auto store_pending = [&]() { store_row32(oh + prow * ol.sn + 32 * cb, pend, h, pok); };
 
     for (int64_t round = 0; round < nrounds; ++round) {
         const int64_t t0 = beg + round * kCc;
@@ -1513,11 +1532,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
                     split8(sacc[t], p, ahi, alo);
                     acc = mma16(ahi, x, acc);
                     acc = mma16(alo, x, acc);
-                    if (t == 0 && p == 0) {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            store_pending(q);
-                    }
+                    if (t == 0 && p == 0)
+                        store_pending();
                     __builtin_amdgcn_sched_barrier(0);
                 }
         }
@@ -1618,9 +1634,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_q_causal_bf(
         }
         __syncthreads();  // B3
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        store_pending(q);
+    store_pending();
 }
 
 // dK | dV (as cz::k_bwd_kv_causal), chunks in reverse order with the running
@@ -2112,14 +2126,14 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_bwd_kv_causal_bf2(
         {
             const float sg = isk ? -1.f : 1.f;
             const float *vec = isk ? L.vr : L.vt;
-            if (t0 + j >= beg && t0 + j < end)
+            f4 o[4];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const f4 v = *reinterpret_cast<const f4 *>(&vec[32 * cb + 8 * q + 4 * h]);
-                    io::store4(oh + (t0 + j) * ol.sn + 32 * cb + 8 * q + 4 * h,
-                               f4{acc[4 * q] + sg * v[0], acc[4 * q + 1] + sg * v[1],
-                                  acc[4 * q + 2] + sg * v[2], acc[4 * q + 3] + sg * v[3]});
-                }
+            for (int q = 0; q < 4; ++q) {
+                const f4 v = *reinterpret_cast<const f4 *>(&vec[32 * cb + 8 * q + 4 * h]);
+                o[q] = f4{acc[4 * q] + sg * v[0], acc[4 * q + 1] + sg * v[1],
+                          acc[4 * q + 2] + sg * v[2], acc[4 * q + 3] + sg * v[3]};
+            }
+            store_row32(oh + (t0 + j) * ol.sn + 32 * cb, o, h, t0 + j >= beg && t0 + j < end);
         }
         // the suffix state takes the chunk in: R += Q_c^T A_c (also after the
         // last chunk, where it is not read again)
