@@ -987,14 +987,53 @@ __device__ __forceinline__ bf8 row_at(const uint16_t *row, int d0)
     return __builtin_bit_cast(bf8, uint4{a.x, a.y, b.x, b.y});
 }
 
-// hi/lo bf16 operands of accumulator elements 8p .. 8p + 7 of a
+// hi/lo bf16 operands of accumulator elements 8p .. 8p + 7 of a running
+// state.  The residual x - hi of each element is one v_dot2_f32_bf16,
+// x + (-1) hi.x + 0 hi.y (or the mirror): the products are exact and the
+// residual of a round-to-nearest bf16 is representable in fp32, so it is
+// exact, and it replaces an unpack and a subtraction.  Written as one asm
+// block because the compiler neither selects this form (it uses the dot2c
+// form plus a copy) nor encodes the (-1, 0) operand correctly as a constant
+// (its inline constant -1.0 is read as the fp32 pattern, i.e. (0, -1)), and
+// because a dot2 result needs three wait states before a VALU reads it,
+// which the compiler does not insert after inline asm: the order below
+// leaves at least three instructions between every dot2 and its reader,
+// and two wait states after the last conversion (an MFMA may read it next).
+// The inputs must not be fresh MFMA results (the compiler does not insert
+// the MFMA-to-VALU wait states before inline asm either): here they are
+// state accumulators last updated a whole chunk earlier.
 __device__ __forceinline__ void split8(const f16v &a, int p, bf8 &hi, bf8 &lo)
 {
-    float x[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-        x[s] = a[8 * p + s];
-    split8v(x, hi, lo);
+    uint32_t m0, m1;
+    asm("v_mov_b32 %0, 0xbf80" : "=v"(m0));      // (-1, 0)
+    asm("v_mov_b32 %0, 0xbf800000" : "=v"(m1));  // (0, -1)
+    uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+    float r0, r1, r2, r3, r4, r5, r6, r7;
+    asm("v_cvt_pk_bf16_f32 %0, %16, %17\n\t"
+        "v_cvt_pk_bf16_f32 %1, %18, %19\n\t"
+        "v_cvt_pk_bf16_f32 %2, %20, %21\n\t"
+        "v_cvt_pk_bf16_f32 %3, %22, %23\n\t"
+        "v_dot2_f32_bf16 %8, %0, %24, %16\n\t"
+        "v_dot2_f32_bf16 %9, %0, %25, %17\n\t"
+        "v_dot2_f32_bf16 %10, %1, %24, %18\n\t"
+        "v_dot2_f32_bf16 %11, %1, %25, %19\n\t"
+        "v_dot2_f32_bf16 %12, %2, %24, %20\n\t"
+        "v_dot2_f32_bf16 %13, %2, %25, %21\n\t"
+        "v_dot2_f32_bf16 %14, %3, %24, %22\n\t"
+        "v_dot2_f32_bf16 %15, %3, %25, %23\n\t"
+        "v_cvt_pk_bf16_f32 %4, %8, %9\n\t"
+        "v_cvt_pk_bf16_f32 %5, %10, %11\n\t"
+        "v_cvt_pk_bf16_f32 %6, %12, %13\n\t"
+        "v_cvt_pk_bf16_f32 %7, %14, %15\n\t"
+        "s_nop 1"
+        : "=&v"(h0), "=&v"(h1), "=&v"(h2), "=&v"(h3), "=&v"(l0), "=&v"(l1), "=&v"(l2),
+          "=&v"(l3), "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5),
+          "=&v"(r6), "=&v"(r7)
+        : "v"(a[8 * p]), "v"(a[8 * p + 1]), "v"(a[8 * p + 2]), "v"(a[8 * p + 3]),
+          "v"(a[8 * p + 4]), "v"(a[8 * p + 5]), "v"(a[8 * p + 6]), "v"(a[8 * p + 7]), "v"(m0),
+          "v"(m1));
+    hi = __builtin_bit_cast(bf8, uint4{h0, h1, h2, h3});
+    lo = __builtin_bit_cast(bf8, uint4{l0, l1, l2, l3});
 }
 
 // Staging of one chunk: item q = tid (+ NT) covers token pair pr = q % 16
