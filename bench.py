@@ -17,7 +17,8 @@ gives the dominant kernel's achieved rate from per-launch HIP events (a
 second timed pass in which the library records caller-owned events around
 every launch), against the MI355X fp32-MFMA or HBM peak.  `cpu_baseline`
 times the fp64 CPU oracle on the host.  `variants` times the other storage
-type and mask at the same shape; `pieces` times the causal step streamed as
+type and mask at the same shape, each after its own clock-settle phase;
+`pieces` times the causal step streamed as
 equal pieces through the carried-state calls (la_forward_segment /
 la_backward_segment); `decode` times one recurrent decode step
 (la_decode_step) per head at the bench's B x H heads and at B = 64; `layer`
@@ -343,9 +344,25 @@ def fp16_step_floor_us(B, H, N, D):
     return 1e6 * max(t_mfma, 11 * B * H * N * D * 2 / (PEAK_HBM_GBS * 1e9))
 
 
-def time_variant(la, make_inputs, dev, B, H, N, D, dtype, causal, steps, warmup):
+def settle(step, seconds):
+    """Clock settle: untimed calls of step for a fixed wall time (synchronised
+    every 16 calls, so the host does not run far ahead).  Returns the count."""
+    import torch
+    n = 0
+    t_end = time.perf_counter() + max(seconds, 0.0)
+    while time.perf_counter() < t_end:
+        step()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
+def time_variant(la, make_inputs, dev, B, H, N, D, dtype, causal, steps, warmup, settle_s):
     """ms per fwd+bwd step of another storage type / mask at the same shape
-    (same protocol as the headline: warm-up, then the steps back to back)."""
+    (same protocol as the headline: clock settle, warm-up, then the steps back
+    to back)."""
     import torch
     q, k, v, g = make_inputs(B, H, N, D, dtype=dtype, seed=0, device=dev, draw_device=dev)
     o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
@@ -357,6 +374,7 @@ def time_variant(la, make_inputs, dev, B, H, N, D, dtype, causal, steps, warmup)
         la.forward(q, k, v, causal, out=o, state_out=st, workspace=ws)
         la.backward(q, k, v, g, causal, state=st, outs=(dq, dk, dv), workspace=ws)
 
+    settle(step, settle_s)
     return measure(step, steps, warmup)
 
 
@@ -535,8 +553,9 @@ def main():
     # from about step 60 on), so the untimed warm-up is long by default
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--settle-s", type=float, default=0.5,
-                    help="before the warm-up steps, run steps untimed for this long so the "
-                         "GPU reaches its loaded clocks (reported as clock_settle)")
+                    help="before the warm-up steps (of the headline and of each variant), "
+                         "run steps untimed for this long so the GPU reaches its loaded "
+                         "clocks (reported as clock_settle)")
     ap.add_argument("--dtype", choices=("fp32", "bf16", "fp16"), default="fp32",
                     help="storage dtype of Q, K, V, O and gradients (arithmetic is fp32; "
                          "fp16 storage is staged through fp32 buffers)")
@@ -607,16 +626,8 @@ def main():
         la.forward(q, k, v, causal, out=o, state_out=st, workspace=ws, trace=tf)
         la.backward(q, k, v, g, causal, state=st, outs=(dq, dk, dv), workspace=ws, trace=tb)
 
-    # clock settle: untimed steps for a fixed wall time (synchronised every
-    # 16 steps, so the host does not run far ahead), then the warm-up steps
-    settle_steps = 0
-    t_end = time.perf_counter() + max(args.settle_s, 0.0)
-    while time.perf_counter() < t_end:
-        step()
-        settle_steps += 1
-        if settle_steps % 16 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
+    # clock settle (untimed steps for a fixed wall time), then the warm-up steps
+    settle_steps = settle(step, args.settle_s)
     # device memory of the step: the 8 I/O tensors plus the library's
     # workspace and saved state (everything the caller allocates for it)
     mem = {"peak_allocated": torch.cuda.max_memory_allocated(dev),
@@ -727,7 +738,7 @@ def main():
                 continue
             tdt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[vdt]
             r = time_variant(la, make_inputs, dev, B, H, N, D, tdt, vc, args.steps,
-                             args.warmup)
+                             args.warmup, args.settle_s)
             vms = r["mean"]
             vs = 4 if vdt == "fp32" else 2
             if vdt == "fp16" and 32 <= D <= 128 and not vc:
