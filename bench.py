@@ -374,8 +374,10 @@ def time_variant(la, make_inputs, dev, B, H, N, D, dtype, causal, steps, warmup,
         la.forward(q, k, v, causal, out=o, state_out=st, workspace=ws)
         la.backward(q, k, v, g, causal, state=st, outs=(dq, dk, dv), workspace=ws)
 
-    settle(step, settle_s)
-    return measure(step, steps, warmup)
+    n = settle(step, settle_s)
+    r = measure(step, steps, warmup)
+    r["settle_steps"] = n
+    return r
 
 
 def time_pieces(la, make_inputs, dev, B, H, N, D, dtype, pieces, steps, warmup):
@@ -751,7 +753,8 @@ def main():
                 "ms_per_step": round(vms, 4), "ms_median": round(r["median"], 4),
                 "tokens_per_s": round(B * N / (vms * 1e-3), 1),
                 "step_floor_us": round(vfl, 1), "step_frac": round(vfl / (vms * 1e3), 4),
-                "floor_basis": basis}
+                "floor_basis": basis,
+                "clock_settle": {"seconds": args.settle_s, "steps": r["settle_steps"]}}
             print("bench: variant %s %s: %.3f ms/step" % (vdt, "causal" if vc else
                   "non-causal", vms), file=sys.stderr, flush=True)
 
