@@ -428,6 +428,15 @@ int run_forward(const void *Q, const void *K, const void *V, void *O, float *den
                     static_cast<const T *>(Q), nullptr, static_cast<T *>(O), nullptr, den_out,
                     rec, p.N, p.seg_len, (int)p.nseg, p.n0, p.ol);
             });
+        // causal: the chunk walk of la_kernels_causal.hpp with eight waves,
+        // each holding a 256 x 32 slab of the running state (rows widened to
+        // fp32 for every storage type)
+        return traced(t, s, "forward", [&] {
+            cz::k_fwd_causal<ST, D><<<dim3((unsigned)(p.nseg * p.BH)), dim3(cz::threads<D>()),
+                                      0, s>>>(
+                static_cast<const T *>(Q), static_cast<const T *>(K), static_cast<const T *>(V),
+                static_cast<T *>(O), den_out, rec, p.N, p.seg_len, (int)p.nseg, p.n0, p.ol);
+        });
     }
     const dim3 grid((unsigned)(p.nseg * p.BH * C::CS));
     return traced(t, s, "forward", [&] {
@@ -520,6 +529,37 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
                 cz::k_bwd_kv_causal<ST, D><<<dim3((unsigned)(2 * p.nseg * p.BH)), nt, 0, s>>>(
                     q, k, v, g, static_cast<T *>(dK), static_cast<T *>(dV), cbuf, gpart, p.N,
                     p.seg_len, (int)p.nseg, p.ol);
+        });
+    }
+    if constexpr (CAUSAL && wide_path<ST, D>()) {
+        // the causal walks with eight waves (a 256 x 32 state slab each), the
+        // gradient records by the fast reduction, dK | dV by the two-parity
+        // walk (the one-workgroup form would need the whole fp32 suffix state,
+        // 256 KB, in LDS)
+        const dim3 g1((unsigned)(p.nseg * p.BH)), nt(cz::threads<D>());
+        rc = traced(t, s, "bwd_q", [&] {
+            cz::k_bwd_q_causal<ST, D><<<g1, nt, 0, s>>>(q, k, v, g, static_cast<T *>(dQ), cbuf,
+                                                        fstate, p.N, p.seg_len, (int)p.nseg,
+                                                        p.n0, p.ol);
+        });
+        if (rc != LA_OK)
+            return rc;
+        rc = traced(t, s, "grad_state_local", [&] {
+            nc::k_reduce_nc<ST, D, true>
+                <<<dim3((unsigned)(p.nseg * p.BH * nc::reduce_blocks<D>())),
+                   dim3(nc::kReduceThreads), 0, s>>>(q, g, cbuf, gpart, p.N, p.seg_len,
+                                                     (int)p.nseg);
+        });
+        if (rc != LA_OK)
+            return rc;
+        if ((rc = scan(gpart, nullptr, p, 2, s, t, gin, gout)) != LA_OK)  // exclusive suffix
+            return rc;
+        if (dK == nullptr)
+            return LA_OK;
+        return traced(t, s, "bwd_kv", [&] {
+            cz::k_bwd_kv_causal<ST, D><<<dim3((unsigned)(2 * p.nseg * p.BH)), nt, 0, s>>>(
+                q, k, v, g, static_cast<T *>(dK), static_cast<T *>(dV), cbuf, gpart, p.N,
+                p.seg_len, (int)p.nseg, p.ol);
         });
     }
     if constexpr (!CAUSAL && wide_path<ST, D>()) {

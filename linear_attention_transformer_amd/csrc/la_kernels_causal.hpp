@@ -152,17 +152,21 @@ __device__ __forceinline__ void tiles_xyT(const float *qs, const float *ks, cons
 }
 
 // X_c Y_c^T into sh (as above, one product): its four 16 x 16 tiles spread
-// over the NCB waves; a wave with a single tile runs its k-steps as two
-// independent chains (even and odd column groups) and adds them at the end.
+// over the NCB waves (D = 256: waves 0..3, one each; the others have none);
+// a wave with a single tile runs its k-steps as two independent chains (even
+// and odd column groups) and adds them at the end.
 template <int D>
 __device__ __forceinline__ void tile_xyT(const float *xs, const float *ys, float *sh, int cb,
                                          int lane)
 {
-    constexpr int NCB = D / 32, LDX = D + 4, WP = kC + 1, PER = 4 / NCB, NST = D / 16;
+    constexpr int NCB = D / 32, LDX = D + 4, WP = kC + 1, PER = NCB >= 4 ? 1 : 4 / NCB,
+                  NST = D / 16;
     const int r = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
         const int tt = cb * PER + k;
+        if (tt >= 4)
+            break;
         const int ti = tt >> 1, tj = tt & 1;
         const float *xa = xs + (16 * ti + r) * LDX + 4 * g;
         const float *ya = ys + (16 * tj + r) * LDX + 4 * g;
@@ -196,7 +200,7 @@ __global__ __launch_bounds__(threads<D>()) void k_fwd_causal(
 {
     typedef typename ST::T T;
     typedef IO<ST> io;
-    static_assert(D >= 32 && D <= 128, "32-column blocks, state in registers");
+    static_assert(D >= 32 && D <= 256, "32-column blocks, state in registers");
     constexpr int NCB = D / 32, NT = threads<D>(), KB = D / 8, LDX = D + 4, WP = kC + 1;
     __shared__ __attribute__((aligned(16))) float qs[kC * LDX];
     __shared__ __attribute__((aligned(16))) float ks[kC * LDX];
@@ -358,7 +362,7 @@ __global__ __launch_bounds__(threads<D>()) __attribute__((amdgpu_waves_per_eu(2)
 {
     typedef typename ST::T T;
     typedef IO<ST> io;
-    static_assert(D >= 32 && D <= 128, "32-column blocks, state in registers");
+    static_assert(D >= 32 && D <= 256, "32-column blocks, state in registers");
     constexpr int NCB = D / 32, NT = threads<D>(), KB = D / 8, LDX = D + 4, WP = kC + 1;
     __shared__ __attribute__((aligned(16))) float qs[kC * LDX];
     __shared__ __attribute__((aligned(16))) float ks[kC * LDX];
@@ -580,7 +584,7 @@ __device__ __forceinline__ void kv_pass(
 {
     typedef typename ST::T T;
     typedef IO<ST> io;
-    static_assert(D >= 32 && D <= 128, "32-column blocks, state in registers");
+    static_assert(D >= 32 && D <= 256, "32-column blocks, state in registers");
     constexpr int NCB = D / 32, NT = threads<D>(), KB = D / 8, LDX = D + 4, WP = kC + 1;
     float *xs = L.xs, *qs = L.qs, *gs = L.gs, *cs = L.cs, *is = L.is, *vr = L.vr;
     auto &sh = L.sh;
