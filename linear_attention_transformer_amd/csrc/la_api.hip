@@ -350,14 +350,18 @@ int state_of_kv(const void *K, const void *V, float *part, float *tot, const Pla
         });
         done = true;
     }
-    if (!done) {
+    if constexpr (D <= 16) {
+        // width 16: the first-version kernels
         const dim3 grid((unsigned)(p.nseg * p.BH * C::CS));
         rc = traced(t, s, "state_local", [&] {
             k_state_local<ST, D><<<grid, dim3(C::NT), 0, s>>>(
                 static_cast<const T *>(K), static_cast<const T *>(V), part, p.N, p.seg_len,
                 (int)p.nseg, (int)p.dl);
         });
+        done = true;
     }
+    if (!done)
+        return LA_ERR_UNSUPPORTED;
     if (rc != LA_OK)
         return rc;
     return p.causal ? scan(part, nullptr, p, 1, s, t, init, total)
@@ -438,19 +442,24 @@ int run_forward(const void *Q, const void *K, const void *V, void *O, float *den
                 static_cast<T *>(O), den_out, rec, p.N, p.seg_len, (int)p.nseg, p.n0, p.ol);
         });
     }
-    const dim3 grid((unsigned)(p.nseg * p.BH * C::CS));
-    return traced(t, s, "forward", [&] {
-        if (p.causal)
-            k_forward<ST, D, true><<<grid, dim3(C::NT), 0, s>>>(
-                static_cast<const T *>(Q), static_cast<const T *>(K),
-                static_cast<const T *>(V), static_cast<T *>(O), den_out, rec, p.N,
-                p.seg_len, (int)p.nseg, p.n0, p.ol, (int)p.dl);
-        else
-            k_forward<ST, D, false><<<grid, dim3(C::NT), 0, s>>>(
-                static_cast<const T *>(Q), static_cast<const T *>(K),
-                static_cast<const T *>(V), static_cast<T *>(O), den_out, rec, p.N,
-                p.seg_len, (int)p.nseg, p.n0, p.ol, (int)p.dl);
-    });
+    if constexpr (D > 16) {
+        return LA_ERR_UNSUPPORTED;  // every D from 32 up returned above
+    } else {
+        // width 16: the first-version kernels
+        const dim3 grid((unsigned)(p.nseg * p.BH * C::CS));
+        return traced(t, s, "forward", [&] {
+            if (p.causal)
+                k_forward<ST, D, true><<<grid, dim3(C::NT), 0, s>>>(
+                    static_cast<const T *>(Q), static_cast<const T *>(K),
+                    static_cast<const T *>(V), static_cast<T *>(O), den_out, rec, p.N,
+                    p.seg_len, (int)p.nseg, p.n0, p.ol, (int)p.dl);
+            else
+                k_forward<ST, D, false><<<grid, dim3(C::NT), 0, s>>>(
+                    static_cast<const T *>(Q), static_cast<const T *>(K),
+                    static_cast<const T *>(V), static_cast<T *>(O), den_out, rec, p.N,
+                    p.seg_len, (int)p.nseg, p.n0, p.ol, (int)p.dl);
+        });
+    }
 }
 
 // Carry: `cin` is the forward's carried-in record (read only when state_in
@@ -466,7 +475,6 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
     typedef Cfg<D, DefCS<D>::value> C;
     typedef Cfg<D, 1> CQ;
     typedef typename ST::T T;
-    constexpr bool FUSE = (D != 256);
     const Layout l = make_layout(p);
     const float *fstate;
     int rc;
@@ -661,39 +669,36 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
             }
         });
     }
-    rc = traced(t, s, "bwd_q", [&] {
-        k_bwd_q<ST, D, CAUSAL, FUSE><<<dim3((unsigned)(p.nseg * p.BH)), dim3(CQ::NT), 0, s>>>(
-            q, k, v, g, static_cast<T *>(dQ), fstate, gpart, cbuf, p.N, p.seg_len,
-            (int)p.nseg, p.n0, p.ol, (int)p.dl);
-    });
-    if (rc != LA_OK)
-        return rc;
-    const dim3 grid((unsigned)(p.nseg * p.BH * C::CS));
-    if constexpr (!FUSE) {
-        rc = traced(t, s, "grad_state_local", [&] {
-            k_grad_state_local<ST, D><<<grid, dim3(C::NT), 0, s>>>(
-                q, g, cbuf, gpart, p.N, p.seg_len, (int)p.nseg, (int)p.dl);
+    if constexpr (D > 16) {
+        return LA_ERR_UNSUPPORTED;  // every D from 32 up returned above
+    } else {
+        // width 16: the first-version kernels (dQ fused with the gradient record)
+        rc = traced(t, s, "bwd_q", [&] {
+            k_bwd_q<ST, D, CAUSAL><<<dim3((unsigned)(p.nseg * p.BH)), dim3(CQ::NT), 0, s>>>(
+                q, k, v, g, static_cast<T *>(dQ), fstate, gpart, cbuf, p.N, p.seg_len,
+                (int)p.nseg, p.n0, p.ol, (int)p.dl);
         });
         if (rc != LA_OK)
             return rc;
+        const dim3 grid((unsigned)(p.nseg * p.BH * C::CS));
+        const float *gstate;
+        if (CAUSAL) {
+            rc = scan(gpart, nullptr, p, 2, s, t, gin, gout);
+            gstate = gpart;
+        } else {
+            rc = scan(gpart, ws + l.gtot, p, 0, s, t, gin, gout);
+            gstate = ws + l.gtot;
+        }
+        if (rc != LA_OK)
+            return rc;
+        if (dK == nullptr)
+            return LA_OK;
+        return traced(t, s, "bwd_kv", [&] {
+            k_bwd_kv<ST, D, CAUSAL><<<grid, dim3(C::NT), 0, s>>>(
+                q, k, v, g, static_cast<T *>(dK), static_cast<T *>(dV), gstate, cbuf, p.N,
+                p.seg_len, (int)p.nseg, p.ol, (int)p.dl);
+        });
     }
-    const float *gstate;
-    if (CAUSAL) {
-        rc = scan(gpart, nullptr, p, 2, s, t, gin, gout);
-        gstate = gpart;
-    } else {
-        rc = scan(gpart, ws + l.gtot, p, 0, s, t, gin, gout);
-        gstate = ws + l.gtot;
-    }
-    if (rc != LA_OK)
-        return rc;
-    if (dK == nullptr)
-        return LA_OK;
-    return traced(t, s, "bwd_kv", [&] {
-        k_bwd_kv<ST, D, CAUSAL><<<grid, dim3(C::NT), 0, s>>>(
-            q, k, v, g, static_cast<T *>(dK), static_cast<T *>(dV), gstate, cbuf, p.N,
-            p.seg_len, (int)p.nseg, p.ol, (int)p.dl);
-    });
 }
 
 template <class ST, int D>

@@ -569,64 +569,6 @@ __global__ __launch_bounds__(threads_for<D>()) void k_state_local(
         out[D * D + tid] = csum;
 }
 
-// Segment-local gradient state from stored (c_i, den_i): with a_i = g_i/den_i,
-// Mat = Q^T A (dS), r = sum c_i q_i, t = sum a_i.  Used when the query-side
-// kernel cannot keep dS in registers next to S (D = 256).
-template <class ST, int D>
-__global__ __launch_bounds__(threads_for<D>()) void k_grad_state_local(
-    const typename ST::T *__restrict__ Q, const typename ST::T *__restrict__ G,
-    const float *__restrict__ cbuf, float *__restrict__ gpart, int64_t N,
-    int64_t seg_len, int nseg, int dl)
-{
-    typedef Cfg<D, DefCS<D>::value> C;
-    constexpr int R = C::RN;
-    __shared__ __attribute__((aligned(16))) float qs[R * C::LD];
-    __shared__ __attribute__((aligned(16))) float gs[R * C::LD];
-    __shared__ float cl[R], denl[R];
-    const Where g = decode<C::CS>(nseg);
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lr = lane & 15,
-              lg = lane >> 4;
-    const int64_t beg = g.seg * seg_len;
-    const int64_t end = (beg + seg_len < N) ? beg + seg_len : N;
-    const int64_t hoff = g.bh * N * dl;
-
-    Acc<C> acc;
-    acc.zero();
-    float csum = 0.f;
-    Tile<ST, C, R> tq, tg;
-    tq.fetch(Q + hoff, beg, end, dl);
-    tg.fetch(G + hoff, beg, end, dl);
-    for (int64_t c0 = beg; c0 < end; c0 += R) {
-        __syncthreads();
-        tq.commit(qs);
-        tg.commit(gs);
-        if (c0 + R < end) {
-            tq.fetch(Q + hoff, c0 + R, end, dl);
-            tg.fetch(G + hoff, c0 + R, end, dl);
-        }
-        for (int i = tid; i < R; i += C::NT) {
-            const bool ok = c0 + i < end;
-            cl[i] = ok ? cbuf[(g.bh * N + c0 + i) * 2 + 0] : 0.f;
-            denl[i] = ok ? cbuf[(g.bh * N + c0 + i) * 2 + 1] : 1.f;
-        }
-        __syncthreads();
-        for (int x = tid; x < R * D; x += C::NT) {
-            const int i = x / D, d = x % D;
-            gs[i * C::LD + d] = (c0 + i < end) ? gs[i * C::LD + d] / denl[i] : 0.f;
-        }
-        __syncthreads();
-        reduce_rows<C, R>(acc, qs, gs, g.cs, w, lr, lg);
-        if (tid < D)
-            csum += col_wsum<C, R>(qs, cl, tid);
-        else if (tid < 2 * D)
-            csum += col_sum<C, R>(gs, tid - D);
-    }
-    float *out = gpart + (g.bh * nseg + g.seg) * (int64_t)C::PS;
-    acc.store(out, g.cs, w, lr, lg);
-    if (g.cs == 0 && tid < 2 * D)
-        out[D * D + tid] = csum;
-}
-
 // Combine the per-segment records of every head in a fixed order, starting
 // from init[bh] (a record carried in from outside the call; zero when init
 // is null):
@@ -803,11 +745,11 @@ __global__ __launch_bounds__(threads_for<D>()) void k_forward(
     }
 }
 
-// Backward, query side: dQ.  FUSE: also accumulate the segment-local
-// gradient record (dS = Q^T A, r = sum c q, t = sum a) into gpart.  Stores
-// (c_i, den_i) per token into cbuf when CAUSAL or !FUSE.  The workgroup
-// holds all of S (one column slice), since c_i needs q_i.(S a_i) in full.
-template <class ST, int D, bool CAUSAL, bool FUSE>
+// Backward, query side: dQ, and the segment-local gradient record (dS =
+// Q^T A, r = sum c q, t = sum a) into gpart.  Stores (c_i, den_i) per token
+// into cbuf when CAUSAL.  The workgroup holds all of S (one column slice),
+// since c_i needs q_i.(S a_i) in full.
+template <class ST, int D, bool CAUSAL>
 __global__ __launch_bounds__(threads_for<D>()) void k_bwd_q(
     const typename ST::T *__restrict__ Q, const typename ST::T *__restrict__ Kp,
     const typename ST::T *__restrict__ Vp, const typename ST::T *__restrict__ G,
@@ -842,8 +784,7 @@ __global__ __launch_bounds__(threads_for<D>()) void k_bwd_q(
     Acc<C> ST_;  // Mat[k=e][n=d] = S^T
     ST_.load_t(st, 0, w, lr, lg);
     Acc<C> dS;   // Mat[k=d][n=e] = sum q a^T over the segment
-    if constexpr (FUSE)
-        dS.zero();
+    dS.zero();
     if (tid < D) {
         zl[0][tid] = st[D * D + tid];
         ul[0][tid] = st[D * D + D + tid];
@@ -955,7 +896,7 @@ __global__ __launch_bounds__(threads_for<D>()) void k_bwd_q(
                 pml[i * 20 + j] = (j <= i) ? e - cl[i] : 0.f;
             }
         }
-        if constexpr (CAUSAL || !FUSE) {
+        if constexpr (CAUSAL) {
             for (int i = tid; i < R; i += C::NT)
                 if (c0 + i < end) {
                     cbuf[(g.bh * N + c0 + i) * 2 + 0] = cl[i];
@@ -987,13 +928,11 @@ __global__ __launch_bounds__(threads_for<D>()) void k_bwd_q(
                     if (c0 + row < end && col < dl)
                         dQ[ol.head(g.bh) + (c0 + row) * ol.sn + col] = ST::narrow(y[tb][nb][r]);
                 }
-        if constexpr (FUSE) {
-            reduce_rows<C, R>(dS, qs, gs, 0, w, lr, lg);
-            if (tid < D)
-                colacc += col_wsum<C, R>(qs, cl, tid);
-            else if (tid < 2 * D)
-                colacc += col_sum<C, R>(gs, tid - D);
-        }
+        reduce_rows<C, R>(dS, qs, gs, 0, w, lr, lg);
+        if (tid < D)
+            colacc += col_wsum<C, R>(qs, cl, tid);
+        else if (tid < 2 * D)
+            colacc += col_sum<C, R>(gs, tid - D);
         if constexpr (CAUSAL) {
             // S^T += V^T K ; z += sum k ; u += sum v
             reduce_rows<C, RK>(ST_, vs, ks, 0, w, lr, lg);
@@ -1004,12 +943,10 @@ __global__ __launch_bounds__(threads_for<D>()) void k_bwd_q(
             cur ^= 1;
         }
     }
-    if constexpr (FUSE) {
-        float *out = gpart + (g.bh * nseg + g.seg) * (int64_t)C::PS;
-        dS.store(out, 0, w, lr, lg);
-        if (tid < 2 * D)
-            out[D * D + tid] = colacc;
-    }
+    float *out = gpart + (g.bh * nseg + g.seg) * (int64_t)C::PS;
+    dS.store(out, 0, w, lr, lg);
+    if (tid < 2 * D)
+        out[D * D + tid] = colacc;
 }
 
 // Backward, key/value side: dK = V dS^T - r (+ Pm^T Q), dV = K dS + t
