@@ -229,6 +229,14 @@ def test_metric_shape_all_heads(causal, dtype):
     compare(4, 16, 4096, 128, dtype, causal)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+def test_causal_d256_full_size(dtype):
+    """B=4, H=16, N=4096, D=256 causal: the eight-wave chunk walks over
+    512-row segments (a 256 x 32 state slab per wave); heads at both ends and
+    in the middle, head by head and row by row."""
+    compare(4, 16, 4096, 256, dtype, True, heads=[0, 1, 31, 62, 63], seed=9)
+
+
 @pytest.mark.parametrize("D", [32, 64, 256])
 def test_d_sweep(D):
     """D sweep at B=4, H=16, N=4096 fp32 (non-causal); every head checked,
