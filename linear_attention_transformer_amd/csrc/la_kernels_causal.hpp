@@ -417,14 +417,6 @@ __global__ __launch_bounds__(threads<D>()) __attribute__((amdgpu_waves_per_eu(2)
     }
     __syncthreads();
 
-    f4 pend[4];
-    int64_t prow = 0;
-    bool pok = false;
-    auto store_pending = [&](int q) {
-        if (pok)
-            io::store4(oh + prow * ol.sn + 32 * cb + 8 * q + 4 * h, pend[q]);
-    };
-
     for (int64_t round = 0; round < nrounds; ++round) {
         const int64_t t0 = beg + round * kC;
         const bool more = round + 1 < nrounds;
@@ -451,10 +443,6 @@ __global__ __launch_bounds__(threads<D>()) __attribute__((amdgpu_waves_per_eu(2)
                 gu += dot4(x, u);
                 qz += dot4(qv, z);
                 asm volatile("" : "+v"(gu), "+v"(qz));
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (kb == q * (KB / 4))
-                        store_pending(q);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -522,18 +510,21 @@ __global__ __launch_bounds__(threads<D>()) __attribute__((amdgpu_waves_per_eu(2)
         }
         zc = swap32_sum(zc);
         uc = swap32_sum(uc);
-        // (4) dq rows (z of the rows before the chunk), stored during the next
-        // product
+        // (4) dq rows (z of the rows before the chunk), stored right away
+        // (held to be stored during the next product, they cost registers
+        // that the product's operands then spilled)
+        const int64_t row = t0 + j;
+        if (row < end) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const f4 z = *reinterpret_cast<const f4 *>(&vz[32 * cb + 8 * q + 4 * h]);
-            pend[q] = f4{acc[4 * q] * inv - c * z[0], acc[4 * q + 1] * inv - c * z[1],
-                         acc[4 * q + 2] * inv - c * z[2], acc[4 * q + 3] * inv - c * z[3]};
+            for (int q = 0; q < 4; ++q) {
+                const f4 z = *reinterpret_cast<const f4 *>(&vz[32 * cb + 8 * q + 4 * h]);
+                io::store4(oh + row * ol.sn + 32 * cb + 8 * q + 4 * h,
+                           f4{acc[4 * q] * inv - c * z[0], acc[4 * q + 1] * inv - c * z[1],
+                              acc[4 * q + 2] * inv - c * z[2], acc[4 * q + 3] * inv - c * z[3]});
+            }
+            if (h == 0 && cb == 0)
+                reinterpret_cast<float2 *>(cbuf)[bh * N + row] = float2{c, inv};
         }
-        prow = t0 + j;
-        pok = prow < end;
-        if (pok && h == 0 && cb == 0)
-            reinterpret_cast<float2 *>(cbuf)[bh * N + prow] = float2{c, inv};
         __syncthreads();  // B2
         if (h == 0) {
             vz[32 * cb + j] += zc;
@@ -549,9 +540,6 @@ __global__ __launch_bounds__(threads<D>()) __attribute__((amdgpu_waves_per_eu(2)
         }
         __syncthreads();  // B3
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        store_pending(q);
 }
 
 // ============================================================ dK | dV
