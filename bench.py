@@ -64,10 +64,17 @@ KERNEL_NAMES = [
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code: comments and whitespace are left
+    out, so that an edit of a comment keeps the traffic entries measured on
+    the same code."""
+    import re
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1918,12 +1918,12 @@ template <int D>
 struct KvBf2Lds {
     // Row pitches (bf16): D + 8 (16 mod 128 bytes) for the rows read whole
     // only (K, V: conflict-free 16-byte row reads), D + 16 (32 mod 128 bytes)
-    // for the planes read mostly with the transpose read (Q, a and R:
-    // conflict-free 16-lane transpose reads).  D = 64 keeps D + 8 throughout:
-    // the wider planes would cost it a third resident workgroup per CU.
-    // The R planes are written by columns as well (8 bytes per lane, one row
-    // per lane), so they take pitch D (a multiple of 128 bytes) and an XOR
-    // swizzle instead (rsw below).
+    // for the planes read mostly with the transpose read (Q and a:
+    // conflict-free 16-lane transpose reads).  D = 64 keeps D + 8 there: the
+    // wider planes would cost it a third resident workgroup per CU.  The R
+    // planes are read both ways and written by columns (8 bytes per lane, one
+    // row per lane), so they take pitch D (a multiple of 128 bytes) and the
+    // XOR swizzle of rsw instead.
     static constexpr int LDX = D + 8;
     static constexpr int LDT = D == 64 ? D + 8 : D + 16;
     static constexpr int RP = D;         // R planes: element (a, b) at b * RP + rsw(b, a)

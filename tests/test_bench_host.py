@@ -130,3 +130,16 @@ def test_lds_summary_ratios(tmp_path, capsys):
     assert cells[3] == "0.250"                 # 100 / (500 - 100)
     assert cells[4] == "0.125"                 # 500 / (1000 / 256 * 4 * 256)
     assert cells[6] == "2.00" and cells[7] == "0"
+
+
+def test_kernel_source_hash_ignores_comments(tmp_path, monkeypatch):
+    """The traffic entries stay valid across comment edits of the kernel
+    sources and become stale on a code edit."""
+    src = tmp_path / "k.hpp"
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", [str(src)])
+    src.write_text("// a\nint f(int x) { return x + 1; }  /* b */\n")
+    h0 = bench.kernel_source_hash()
+    src.write_text("// another comment\n/* a\n block */ int f(int x)  {\n return x + 1; }\n")
+    assert bench.kernel_source_hash() == h0
+    src.write_text("int f(int x) { return x + 2; }\n")
+    assert bench.kernel_source_hash() != h0
