@@ -51,7 +51,7 @@ COPY_MIB = 256                  # plain streaming kernel: reads and writes this 
 
 # device kernel (demangled name) -> launch name the library's tracer reports
 KERNEL_NAMES = [
-    (r"k_reduce_nc<[^>]*, (true|1)>|k_reduce_bf<\d+, true>|k_grad_state_local<",
+    (r"k_reduce_nc<[^>]*, (true|1)>|k_reduce_bf<\d+, true>",
      "grad_state_local"),
     (r"k_reduce_nc<|k_reduce_bf<|k_state_local<", "state_local"),
     (r"k_apply_nc<[^>]*, 0>|k_apply_bf<\d+, 0>|k_fwd_causal|k_forward<", "forward"),
