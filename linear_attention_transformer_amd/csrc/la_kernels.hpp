@@ -88,6 +88,25 @@ __device__ __forceinline__ float swap32_sum(float v)
     return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
+// Two sums for one exchange: a + (a of lane l ^ 16) in rows 0 and 2 of
+// the wave, b + (b of lane l ^ 16) in rows 1 and 3 (v_permlane16_swap moves
+// the odd rows of its first register and the even rows of its second)
+__device__ __forceinline__ float pair16_sum(float a, float b)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a),
+                                                    __builtin_bit_cast(unsigned, b), false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// a + (a of lane l ^ 32) in the lower half, b + (b of lane l ^ 32) in the
+// upper half
+__device__ __forceinline__ float pair32_sum(float a, float b)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a),
+                                                    __builtin_bit_cast(unsigned, b), false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
 template <int N>
 __device__ __forceinline__ float group_sum(float v)
 {

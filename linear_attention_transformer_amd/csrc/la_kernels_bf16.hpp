@@ -1933,6 +1933,7 @@ struct KvBf2Lds {
     uint16_t phi[kCc * PP], plo[kCc * PP], whi[kCc * PP], wlo[kCc * PP];
     float cs[kCc];
     float vr[D], vt[D];
+    float csp[D / 16][2][D];  // each wave's column sums of c q and a over its rows
 };
 
 template <int D>
@@ -1996,16 +1997,46 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_bwd_kv_causal_bf2(
         *reinterpret_cast<uint4 *>(&L.q[o]) = pq[X];
         *reinterpret_cast<uint4 *>(&L.k[ox]) = pk[X];
         *reinterpret_cast<uint4 *>(&L.v[ox]) = pv[X];
-        float gf[8];
+        float gf[8], qf[8];
         StBF16::widen(pg[X], gf);
-        const float inv = pc[X].y;
+        StBF16::widen(pq[X], qf);
+        const float c = pc[X].x, inv = pc[X].y;
+        float v[16];  // c q and a at the item's 8 columns
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            v[s] = c * qf[s];
+            v[8 + s] = gf[s] * inv;
+        }
         uint2 h0, l0, h1, l1;
-        split4(gf[0] * inv, gf[1] * inv, gf[2] * inv, gf[3] * inv, h0, l0);
-        split4(gf[4] * inv, gf[5] * inv, gf[6] * inv, gf[7] * inv, h1, l1);
+        split4(v[8], v[9], v[10], v[11], h0, l0);
+        split4(v[12], v[13], v[14], v[15], h1, l1);
         *reinterpret_cast<uint4 *>(&L.ahi[o]) = uint4{h0.x, h0.y, h1.x, h1.y};
         *reinterpret_cast<uint4 *>(&L.alo[o]) = uint4{l0.x, l0.y, l1.x, l1.y};
         if (ic == 0)
-            L.cs[it] = pc[X].x;
+            L.cs[it] = c;
+        // the sums of v over the wave's rows of the chunk: (D = 64: the two
+        // rows of each 16-lane row first), then pairwise exchanges across
+        // rows 2r, 2r + 1 and across the halves, each of which sums two
+        // values at once; lane (g = lane / 16, ic) ends with v[4 n + g]
+        if constexpr (CPR == 8) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                v[e] += dpp_mov<0x128>(v[e]);  // row_ror:8
+        }
+        float u[8], x[4];
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            u[m] = pair16_sum(v[2 * m], v[2 * m + 1]);
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+            x[n] = pair32_sum(u[2 * n], u[2 * n + 1]);
+        if ((lane & 15) < CPR) {
+            const int g = lane >> 4;
+            L.csp[w][0][8 * ic + g] = x[0];
+            L.csp[w][0][8 * ic + 4 + g] = x[1];
+            L.csp[w][1][8 * ic + g] = x[2];
+            L.csp[w][1][8 * ic + 4 + g] = x[3];
+        }
     };
 
     // this wave's tiles of R: tile u <-> R[32 ta .., 32 tb ..], accumulator
@@ -2043,14 +2074,10 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_bwd_kv_causal_bf2(
         for (int i = 0; i < 16; ++i)
             racc[u][i] = st[(32 * ta + 8 * (i / 4) + 4 * h + (i % 4)) * D + 32 * tb + j];
     }
-    // the column-sum threads: the last D of the workgroup, one column each
-    const bool csum = tid >= NT - D;
-    const int cd = tid - (NT - D);
-    float rr = 0.f, tt = 0.f;  // r and t of the rows after the chunk
-    if (csum) {
-        rr = st[D * D + cd];
-        tt = st[D * D + D + cd];
-    }
+    // the vector threads: the first 2 D of the workgroup, thread e holds
+    // element e of [r | t] of the rows after the chunk
+    const bool vth = tid < 2 * D;
+    float rt = vth ? st[D * D + tid] : 0.f;
     write_r();
     stage(S0{});
     drain_loads();
@@ -2125,20 +2152,17 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_bwd_kv_causal_bf2(
             *reinterpret_cast<uint2 *>(&(pw == 0 ? L.phi : L.whi)[jj * PP + i0]) = hi;
             *reinterpret_cast<uint2 *>(&(pw == 0 ? L.plo : L.wlo)[jj * PP + i0]) = lo;
         }
-        // column sums of the chunk; the vectors of the rows after it go to
-        // LDS for the epilogue
-        if (csum) {
-            L.vr[cd] = rr;
-            L.vt[cd] = tt;
-            float rc = 0.f, tc = 0.f;
-#pragma unroll 8
-            for (int i = 0; i < kCc; ++i) {
-                rc += L.cs[i] * __uint_as_float((uint32_t)L.q[i * LDT + cd] << 16);
-                tc += __uint_as_float((uint32_t)L.ahi[i * LDT + cd] << 16) +
-                      __uint_as_float((uint32_t)L.alo[i * LDT + cd] << 16);
-            }
-            rr += rc;
-            tt += tc;
+        // the vectors of the rows after the chunk go to LDS for the
+        // epilogue; then the chunk's column sums (the waves' partials from
+        // its staging) join them
+        if (vth) {
+            const int vi = tid / D, cd = tid % D;
+            (vi ? L.vt : L.vr)[cd] = rt;
+            float sc = 0.f;
+#pragma unroll
+            for (int u = 0; u < NW; ++u)
+                sc += L.csp[u][vi][cd];
+            rt += sc;
         }
         __syncthreads();  // B1
         // (2) in-chunk terms: dK^T += Q^T P (C[a][j] += sum_i Q[i][a] P[i][j]),
