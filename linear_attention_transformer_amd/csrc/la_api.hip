@@ -118,6 +118,21 @@ Plan one_batch(const Plan &p, int64_t resident)
     return q;
 }
 
+// Segments per workgroup for a walk over the suffix (or prefix) records of
+// the plan: the smallest count that fits the launch into one batch of
+// `resident` workgroups (the plan's segments when even one per head does
+// not fit; 1 if the residency is unknown).  Records stay the plan's: a
+// merged walk starts from the record of its last segment.
+int merge_factor(const Plan &p, int64_t resident)
+{
+    if (resident <= 0)
+        return 1;
+    for (int64_t m = 1; m < p.nseg; ++m)
+        if ((p.nseg + m - 1) / m * p.BH <= resident)
+            return (int)m;
+    return (int)std::max<int64_t>(p.nseg, 1);
+}
+
 // The plan re-segmented so that a launch of `per` workgroups per segment and
 // head fills `resident` slots in one batch, for a kernel whose workgroups
 // read only the head's total state (no record per segment): more or fewer
@@ -519,21 +534,27 @@ int run_backward_t(const void *Q, const void *K, const void *V, const void *G, v
         if (dK == nullptr)
             return LA_OK;
         return traced(t, s, "bwd_kv", [&] {
-            if constexpr (std::is_same<ST, StBF16>::value && D >= 64)
-                bf::k_bwd_kv_causal_bf2<D><<<dim3((unsigned)(p.nseg * p.BH)), dim3(128 * (D / 32)),
-                                             0, s>>>(q, k, v, g, static_cast<T *>(dK),
-                                                     static_cast<T *>(dV), cbuf, gpart, p.N,
-                                                     p.seg_len, (int)p.nseg, p.ol);
-            else if constexpr (std::is_same<ST, StBF16>::value)
+            // one workgroup per CU: segments are merged so that the walk is
+            // one batch of resident workgroups
+            if constexpr (std::is_same<ST, StBF16>::value && D >= 64) {
+                const int m = merge_factor(
+                    p, resident_wgs<bf::k_bwd_kv_causal_bf2<D>>(128 * (D / 32)));
+                bf::k_bwd_kv_causal_bf2<D>
+                    <<<dim3((unsigned)((p.nseg + m - 1) / m * p.BH)), dim3(128 * (D / 32)), 0,
+                       s>>>(q, k, v, g, static_cast<T *>(dK), static_cast<T *>(dV), cbuf, gpart,
+                            p.N, p.seg_len, (int)p.nseg, m, p.ol);
+            } else if constexpr (std::is_same<ST, StBF16>::value)
                 bf::k_bwd_kv_causal_bf<D><<<dim3((unsigned)(2 * p.nseg * p.BH)), nt, 0, s>>>(
                     q, k, v, g, static_cast<T *>(dK), static_cast<T *>(dV), cbuf, gpart, p.N,
                     p.seg_len, (int)p.nseg, p.ol);
-            else if constexpr (D >= 64)
-                cz::k_bwd_kv_causal2<ST, D><<<dim3((unsigned)(p.nseg * p.BH)), dim3(128 * (D / 32)),
-                                              0, s>>>(q, k, v, g, static_cast<T *>(dK),
-                                                      static_cast<T *>(dV), cbuf, gpart, p.N,
-                                                      p.seg_len, (int)p.nseg, p.ol);
-            else
+            else if constexpr (D >= 64) {
+                const int m = merge_factor(
+                    p, resident_wgs<cz::k_bwd_kv_causal2<ST, D>>(128 * (D / 32)));
+                cz::k_bwd_kv_causal2<ST, D>
+                    <<<dim3((unsigned)((p.nseg + m - 1) / m * p.BH)), dim3(128 * (D / 32)), 0,
+                       s>>>(q, k, v, g, static_cast<T *>(dK), static_cast<T *>(dV), cbuf, gpart,
+                            p.N, p.seg_len, (int)p.nseg, m, p.ol);
+            } else
                 cz::k_bwd_kv_causal<ST, D><<<dim3((unsigned)(2 * p.nseg * p.BH)), nt, 0, s>>>(
                     q, k, v, g, static_cast<T *>(dK), static_cast<T *>(dV), cbuf, gpart, p.N,
                     p.seg_len, (int)p.nseg, p.ol);

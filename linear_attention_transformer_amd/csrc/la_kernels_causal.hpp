@@ -772,7 +772,7 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_bwd_kv_causal2(
     const typename ST::T *__restrict__ V, const typename ST::T *__restrict__ G,
     typename ST::T *__restrict__ dK, typename ST::T *__restrict__ dV,
     const float *__restrict__ cbuf, const float *__restrict__ rec, int64_t N, int64_t seg_len,
-    int nseg, OutLay ol)
+    int nseg, int merge, OutLay ol)
 {
     typedef typename ST::T T;
     typedef IO<ST> io;
@@ -781,14 +781,18 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_bwd_kv_causal2(
     constexpr int LDX = Kv2Lds<D>::LDX, RP = Kv2Lds<D>::RP, WP = Kv2Lds<D>::WP;
     __shared__ __attribute__((aligned(16))) Kv2Lds<D> L;
 
-    const int64_t bh = blockIdx.x / nseg;
-    const int seg = (int)(blockIdx.x % nseg);
+    // a workgroup walks `merge` consecutive segments of the plan, starting
+    // from the suffix record of the last of them
+    const int nsm = (nseg + merge - 1) / merge;
+    const int64_t bh = blockIdx.x / nsm;
+    const int sm = (int)(blockIdx.x % nsm);
+    const int seg = (sm + 1) * merge - 1 < nseg ? (sm + 1) * merge - 1 : nseg - 1;
     const int tid = threadIdx.x, lane = tid & 63, j = lane & 31, h = lane >> 5;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool isk = w < NCB;
     const int cb = isk ? w : w - NCB;
-    const int64_t beg = (int64_t)seg * seg_len;
-    const int64_t end = (beg + seg_len < N) ? beg + seg_len : N;
+    const int64_t beg = (int64_t)sm * merge * seg_len;
+    const int64_t end = (beg + merge * seg_len < N) ? beg + merge * seg_len : N;
     const int64_t hoff = bh * N * D;
     const float *st = rec + (bh * nseg + seg) * (int64_t)(D * D + 2 * D);
     const T *qh = Q + hoff, *kh = K + hoff, *vh = V + hoff, *gh = G + hoff;

@@ -237,6 +237,15 @@ def test_causal_d256_full_size(dtype):
     compare(4, 16, 4096, 256, dtype, True, heads=[0, 1, 31, 62, 63], seed=9)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_causal_merged_walk_odd_segments(dtype):
+    """B=4, H=16, N=640, D=128 causal: five 128-row segments per head, more
+    workgroups than one batch of the one-workgroup dK | dV walk holds, so its
+    workgroups walk two segments each and the last one walks a single
+    segment; every head, head by head and row by row."""
+    compare(4, 16, 640, 128, dtype, True, seed=11)
+
+
 @pytest.mark.parametrize("D", [32, 64, 256])
 def test_d_sweep(D):
     """D sweep at B=4, H=16, N=4096 fp32 (non-causal); every head checked,
