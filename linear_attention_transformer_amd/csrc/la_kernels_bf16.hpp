@@ -1881,9 +1881,14 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_kv_causal_bf(
 // of 8 a).  The chunk's rows of Q, K, V and A = dO / den (hi and lo) are
 // staged once, as natural rows; the in-chunk blocks P = M o (A V^T - c) and
 // W = M o (1 + Q K^T) are formed by 16 x 16 quarters over the waves and
-// stored [j][i] as hi / lo planes.  Products over the chunk's tokens (R's update, P^T Q, W^T A)
-// read 8 consecutive tokens of a column with two ds_read_b64_tr_b16.  The
-// column sums r = sum c_i q_i and t = sum a_i run in registers of D threads.
+// stored [j][i] as hi / lo planes.  Products over the chunk's tokens (R's
+// update, P^T Q, W^T A) read 8 consecutive tokens of a column with two
+// ds_read_b64_tr_b16.  The column sums r = sum c_i q_i and t = sum a_i of a
+// chunk are formed at its staging, per wave by lane exchanges, and added
+// over the waves by the 2 D threads that carry the running vectors.  When
+// the launch has more workgroups than one batch holds (one workgroup per CU
+// at D = 128), a workgroup walks several consecutive segments, starting
+// from the suffix record of the last of them.
 
 // Column of element (row r, column c) of an R plane: 4-element granule c / 4
 // XOR sig(r), sig(r) = 4 (r & 3) + 2 ((r >> 2) & 1).  With rows a multiple of

@@ -755,7 +755,9 @@ __global__ __launch_bounds__(threads<D>()) __attribute__((amdgpu_waves_per_eu(2)
 //     each role's registers are allocated apart.
 // Three barriers per chunk, as in kv_pass: after the product tiles (B1),
 // after the chunk's last reads (B2), after the next chunk is staged (B3).
-// K and V are read only before B1 and are restaged right after it.
+// K and V are read only before B1 and are restaged right after it.  When the
+// launch has more workgroups than one batch holds, a workgroup walks several
+// consecutive segments, starting from the suffix record of the last of them.
 template <int D>
 struct Kv2Lds {
     static constexpr int LDX = D + 4, RP = D + 4, WP = kC + 1;
