@@ -237,7 +237,7 @@ def test_causal_d256_full_size(dtype):
     compare(4, 16, 4096, 256, dtype, True, heads=[0, 1, 31, 62, 63], seed=9)
 
 
-@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
 def test_causal_merged_walk_odd_segments(dtype):
     """B=4, H=16, N=640, D=128 causal: five 128-row segments per head, more
     workgroups than one batch of the one-workgroup dK | dV walk holds, so its
