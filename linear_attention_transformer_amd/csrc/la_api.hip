@@ -28,6 +28,7 @@ using namespace la;
 // splitting each head's sequence into segments.
 constexpr int64_t kSegAlign = 64;
 constexpr int64_t kTargetWorkgroups = 512;
+constexpr int64_t kMinSegChunks = 4;
 
 struct Plan {
     int64_t BH, N, D, PS, nseg, seg_len;
@@ -66,7 +67,14 @@ Plan make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int causal)
     const int64_t want =
         p.BH >= target ? 1 : (target + p.BH - 1) / std::max<int64_t>(p.BH, 1);
     const int64_t ns = std::min(want, nchunks);
-    const int64_t per = (nchunks + ns - 1) / ns;
+    // Segments of at least kMinSegChunks chunks when that still gives one
+    // workgroup per CU: shorter segments cost more in their 4(D^2 + 2D)-byte
+    // records (written, scanned, read by the walks) than they gain in
+    // parallelism.  (B4 H16 N1024: 8 segments of 128 rows -> 4 of 256, bf16
+    // causal step 0.127 -> 0.117 ms; with 4 heads the short segments stay.)
+    const int64_t at_min = (nchunks + kMinSegChunks - 1) / kMinSegChunks;
+    const int64_t pmin = (D > 16 && p.BH * at_min >= kTargetWorkgroups / 2) ? kMinSegChunks : 1;
+    const int64_t per = std::max<int64_t>((nchunks + ns - 1) / ns, pmin);
     p.seg_len = per * kSegAlign;
     p.nseg = std::max<int64_t>((N + p.seg_len - 1) / p.seg_len, 1);
     return p;

@@ -80,6 +80,11 @@ def test_sizes():
     for d in (1, 6, 16):
         assert 0 < la.workspace_size(B, H, N, d) < B * H * N * 16 * 4
     assert la.workspace_size(4, 16, -1, 128) == 0
+    # short sequences: segments of at least 256 rows where that still leaves
+    # one workgroup per CU (64 heads), else the plan's shorter segments
+    assert la.num_segments(4, 16, 1024, 128) == 4
+    assert la.num_segments(4, 16, 640, 128) == 5
+    assert la.num_segments(1, 4, 1024, 128) == 16
     # segments grow with N, never exceed the 64-row chunks
     for n in (1, 63, 64, 65, 1000, 131072):
         s = la.num_segments(1, 1, n, 64)

@@ -243,6 +243,7 @@ def test_causal_merged_walk_odd_segments(dtype):
     workgroups than one batch of the one-workgroup dK | dV walk holds, so its
     workgroups walk two segments each and the last one walks a single
     segment; every head, head by head and row by row."""
+    assert la().num_segments(4, 16, 640, 128) == 5
     compare(4, 16, 640, 128, dtype, True, seed=11)
 
 
