@@ -532,6 +532,18 @@ __global__ __launch_bounds__(apply_threads<D>()) void k_apply_nc(
     // forward: q.z of each row over each wave's 32 columns (added up after
     // the round's barrier)
     __shared__ float xch[KIND == 0 ? 2 : 1][NRG][NCB][32];
+    // D = 64 (few matrix steps per row, the output stores weigh most): a
+    // round's output rows go to an LDS tile and the workgroup stores them as
+    // whole 16-byte row pieces LAG rounds later (the dK | dV tile is complete
+    // at the round's barrier, the forward's, normalised after it, at the
+    // next one).  In the MFMA layout a lane's own stores cover 32 bytes of
+    // each of 32 rows per instruction.  (fp32 step at B4 H16 N4096 D64:
+    // 0.195 -> 0.182 ms, at two workgroups per CU instead of four; D = 32
+    // measured the same either way, D = 128 spends its time on the products.)
+    constexpr bool OT = D == 64;
+    constexpr int LDO = D + VEC;  // tile row pitch (elements)
+    constexpr int LAG = KIND == 0 ? 2 : 1;
+    __shared__ __attribute__((aligned(16))) T ot[OT ? 2 : 1][OT ? TR * LDO : VEC];
 
     // unit = segment (forward, dQ) or 2 segment + parity (dK | dV)
     int64_t bh;
@@ -645,13 +657,28 @@ __global__ __launch_bounds__(apply_threads<D>()) void k_apply_nc(
         fetch_round(beg + TR);
     __syncthreads();
 
-    // the previous round's output rows, stored during the next round
+    // the previous round's output rows, stored during the next round (or,
+    // with the LDS tile, the round's values put into the tile)
     f4 pend[4];
     int64_t prow = 0;
     bool pok = false;
     auto store_pending = [&](int q) {
         if (pok)
             io::store4(oh + prow * ol.sn + 32 * cb + 8 * q + 4 * h, pend[q]);
+    };
+    auto put_tile = [&](int tb) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            io::store4(&ot[tb][(32 * rg + j) * LDO + 32 * cb + 8 * q + 4 * h], pend[q]);
+    };
+    // 16-byte piece p of round rr's tile to global memory (consecutive lanes
+    // take consecutive pieces of a row)
+    auto store_tile = [&](int64_t rr, int p) {
+        const int c = tid + p * NT;
+        const int64_t grow = beg + rr * TR + c / CPR;
+        if (grow < end)
+            *reinterpret_cast<uint4 *>(oh + grow * ol.sn + VEC * (c % CPR)) =
+                *reinterpret_cast<const uint4 *>(&ot[(int)(rr & 1)][(c / CPR) * LDO + VEC * (c % CPR)]);
     };
 
     for (int64_t round = 0; round < nrounds; ++round) {
@@ -694,10 +721,17 @@ __global__ __launch_bounds__(apply_threads<D>()) void k_apply_nc(
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     acc = mma32(am[kb][r], x[r], acc);
+                if constexpr (OT) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (kb == q * (KB / 4))
-                        store_pending(q);
+                    for (int p = 0; p < PER; ++p)
+                        if (round >= LAG && kb == (p * KB) / PER)
+                            store_tile(round - LAG, p);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (kb == q * (KB / 4))
+                            store_pending(q);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -719,6 +753,8 @@ __global__ __launch_bounds__(apply_threads<D>()) void k_apply_nc(
             for (int q = 0; q < 4; ++q)
                 pend[q] = f4{acc[4 * q] + ev[q][0], acc[4 * q + 1] + ev[q][1],
                              acc[4 * q + 2] + ev[q][2], acc[4 * q + 3] + ev[q][3]};
+            if constexpr (OT)
+                put_tile(buf);
         }
         prow = row;
         pok = row < end;
@@ -743,11 +779,21 @@ __global__ __launch_bounds__(apply_threads<D>()) void k_apply_nc(
                              (acc[4 * q + 2] + ev[q][2]) * inv, (acc[4 * q + 3] + ev[q][3]) * inv};
             if (den_out != nullptr && row < end && h == 0 && cb == 0)
                 den_out[bh * N + row] = den;
+            if constexpr (OT)
+                put_tile(buf);
         }
     }
+    if constexpr (OT) {
+        __syncthreads();
+        for (int64_t rr = nrounds - LAG < 0 ? 0 : nrounds - LAG; rr < nrounds; ++rr)
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-        store_pending(q);
+            for (int p = 0; p < PER; ++p)
+                store_tile(rr, p);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            store_pending(q);
+    }
 }
 
 // ============================================================ dQ + gradient record
